@@ -1,0 +1,338 @@
+"""Plain fp64 CPU oracle for the Online KL Shampoo / Shampoo preconditioner step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code, tables or helpers
+with the HIP library; the two meet only at seeded inputs.
+
+Every function below follows a passage of the source pages, cited by page
+title and section.  Short names used in the citations:
+
+  [OKLS]     "Online KL Shampoo" (project README page), sections "How it works",
+             "Hyperparameters", "Batched matrices", "Learning-rate schedule".
+  [SHAMPOO]  "Shampoo: 그래디언트 행렬 하나로 두 조각을" (optim-book chapter),
+             sections "2 × 3 그래디언트 하나로 손계산" (worked example) and
+             "문제 14" (problem 14, exponent and scale).
+  [CLEAN]    "Clean: Second-order LLM Training at Linear Memory Cost via
+             Nyström Sketching", section 2, equations (2)-(3).
+
+Where the pages leave a step open, the reading taken is named in the
+docstring as R1..R12; the list of readings lives with the project's design
+notes.  All arithmetic is numpy float64; eigendecompositions use LAPACK
+(numpy.linalg.eigh).  Nothing here is blocked, fused or reordered beyond the
+definitions.
+
+Parity status of each function (what pins it in the CPU test-suite):
+  c_shape ...................... closed forms (square case 1/(2 sqrt n))
+  nesterov_scale / momentum .... t=1 gives N=G exactly; Monte-Carlo RMS of N = 1
+  factor_update_okls ........... white-Gaussian expectation, equivariance, transpose
+  factor_update_shampoo ........ worked example L = G G^T = [[10,3],[3,5]]
+  inv_root_exact ............... P S P = I, 2x2 closed form, scipy sqrtm on 3x3,
+                                 worked example and problem 14 singular values
+  ns_coefficients .............. classical Newton-Schulz limit (3/2, -1/2),
+                                 equioscillation, grid-search optimality
+  ns_inv_sqrt / ns_inv_quarter . diagonal S reduces to scalar recurrences,
+                                 eigen closed form, worked example through NS
+  whiten / update_weights ...... G=0 step gives W' = (1 - lr wd) W exactly
+  okls_step / shampoo_step ..... orthogonal equivariance, transpose identity,
+                                 3-D batch = per-matrix results
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Hyperparameters  ([OKLS] "Hyperparameters": defaults lr 0.09434,
+# beta1 0.9684, beta2 0.9482, eps 1e-9, weight_decay 0.0303)
+# ---------------------------------------------------------------------------
+@dataclass
+class Hyper:
+    lr: float = 0.09434
+    beta1: float = 0.9684
+    beta2: float = 0.9482
+    eps: float = 1e-9
+    weight_decay: float = 0.0303
+    lr_peak: float | None = None        # [OKLS] "Learning-rate schedule": the initial lr is kept as lr_peak
+    nesterov_var_corr: bool = True      # R5
+    ns_steps: int = 10                  # [OKLS] intro: 10-step inverse-root method
+    ns_floor: float = 1e-3              # R4: lower end of the design interval for sqrt(lambda / ||S||_F)
+
+    def peak(self) -> float:
+        return self.lr if self.lr_peak is None else self.lr_peak
+
+
+# ---------------------------------------------------------------------------
+# [OKLS] "How it works": muP shape multiplier c_shape = sqrt(m/n) / (sqrt(m) + sqrt(n)),
+# with G in R^{m x n}; m is the number of rows (R3).
+# ---------------------------------------------------------------------------
+def c_shape(m: int, n: int) -> float:
+    return math.sqrt(m / n) / (math.sqrt(m) + math.sqrt(n))
+
+
+# ---------------------------------------------------------------------------
+# [OKLS] intro + "Hyperparameters": Nesterov momentum with variance correction,
+# beta1 the momentum EMA coefficient.  The pages give no formula (R5).
+# Reading: M_t = beta1 M_{t-1} + (1-beta1) G_t;  N_t = s_t (beta1 M_t + (1-beta1) G_t),
+# with s_t = v_t^{-1/2} and v_t the variance of beta1 M_t + (1-beta1) G_t when the
+# G_s are independent with unit variance and M_0 = 0.
+# ---------------------------------------------------------------------------
+def nesterov_scale(beta1: float, t: int, enabled: bool = True) -> float:
+    if not enabled:
+        return 1.0
+    if t < 1:
+        raise ValueError("t is 1-based")
+    # weight on G_t: beta1 (1-beta1) + (1-beta1) = (1-beta1)(1+beta1)
+    v = ((1.0 - beta1) * (1.0 + beta1)) ** 2
+    # weights on G_s, s<t: beta1 * (1-beta1) * beta1^(t-s)
+    for s in range(1, t):
+        v += (beta1 * (1.0 - beta1) * beta1 ** (t - s)) ** 2
+    return 1.0 / math.sqrt(v)
+
+
+def momentum(M: np.ndarray, G: np.ndarray, beta1: float, t: int, var_corr: bool = True):
+    """Returns (M_t, N_t) for one step; see nesterov_scale for the reading."""
+    M_new = beta1 * M + (1.0 - beta1) * G
+    N = nesterov_scale(beta1, t, var_corr) * (beta1 * M_new + (1.0 - beta1) * G)
+    return M_new, N
+
+
+# ---------------------------------------------------------------------------
+# [OKLS] "How it works": two-sided KL factor updates using the previous
+# preconditioners,
+#   S_a <- beta2 S_a + (1-beta2)/n (G P_b)(G P_b)^T
+#   S_b <- beta2 S_b + (1-beta2)/m (P_a G)^T (P_a G)
+# [OKLS] "Hyperparameters": eps is added during factor initialisation and
+# updates (R1: + eps I after every update).
+# ---------------------------------------------------------------------------
+def factor_update_okls(Sa, Sb, Pa, Pb, G, beta2: float, eps: float):
+    m, n = G.shape
+    Xa = G @ Pb
+    Xb = Pa @ G
+    Sa_new = beta2 * Sa + ((1.0 - beta2) / n) * (Xa @ Xa.T) + eps * np.eye(m)
+    Sb_new = beta2 * Sb + ((1.0 - beta2) / m) * (Xb.T @ Xb) + eps * np.eye(n)
+    return _sym(Sa_new), _sym(Sb_new)
+
+
+# ---------------------------------------------------------------------------
+# [CLEAN] eq (2) and [SHAMPOO] worked example: L = sum G G^T, R = sum G^T G.
+# R7: the accumulators start at eps I and get + eps I per update (R1).
+# ---------------------------------------------------------------------------
+def factor_update_shampoo(Sa, Sb, G, eps: float):
+    m, n = G.shape
+    Sa_new = Sa + G @ G.T + eps * np.eye(m)
+    Sb_new = Sb + G.T @ G + eps * np.eye(n)
+    return _sym(Sa_new), _sym(Sb_new)
+
+
+def _sym(S):
+    return 0.5 * (S + S.T)
+
+
+# ---------------------------------------------------------------------------
+# Exact inverse p-th roots ([OKLS] "How it works": P = S^{-1/2};
+# [CLEAN] eq (3) / [SHAMPOO]: L^{-1/4}, R^{-1/4}).  Principal root of an SPD
+# matrix via the symmetric eigendecomposition.
+# ---------------------------------------------------------------------------
+def inv_root_exact(S: np.ndarray, p: int):
+    """Returns (S^{-1/p}, condition number lambda_max / lambda_min)."""
+    lam, V = np.linalg.eigh(_sym(S))
+    if lam[0] <= 0.0:
+        raise np.linalg.LinAlgError("factor is not positive definite")
+    P = (V * lam ** (-1.0 / p)) @ V.T
+    return _sym(P), float(lam[-1] / lam[0])
+
+
+# ---------------------------------------------------------------------------
+# Coupled Newton-Schulz coefficients (R4).  [OKLS] intro and "How it works":
+# a 10-step inverse-root iteration with Chebyshev-optimised coefficients and
+# deterministic per-step scales that keep the fp16 inputs in range.  The
+# coefficients themselves are not printed; the reading is the per-step minimax
+# odd cubic:
+#   step k acts on each eigen-direction as  sigma -> sigma (a_k + b_k sigma^2),
+#   (a_k, b_k) minimise max |sigma (a + b sigma^2) - 1| over sigma in [l_k, u_k],
+#   the minimax error E_k is attained with alternating sign at l_k, at the
+#   interior maximum x_k and at u_k (equioscillation of a 2-parameter family).
+# Every step but the last is divided by (1 + E_k) so the mapped interval is
+# [(1-E_k)/(1+E_k), 1] and no iterate exceeds 1; the last step is left as is so
+# the output is centred on 1.
+# ---------------------------------------------------------------------------
+def _minimax_cubic(lo: float, hi: float):
+    # p(x) = a x + b x^3, p(lo) = p(hi) = 1 - E, p(x*) = 1 + E, p'(x*) = 0.
+    # p(lo) = p(hi)  =>  a = -b (hi^2 + hi lo + lo^2);  x*^2 = (hi^2 + hi lo + lo^2) / 3
+    # p(x*) = -2 b x*^3,  p(lo) = -b lo hi (lo + hi);  p(x*) + p(lo) = 2.
+    q = hi * hi + hi * lo + lo * lo
+    xs = math.sqrt(q / 3.0)
+    b = -2.0 / (2.0 * xs ** 3 + lo * hi * (lo + hi))
+    a = -b * q
+    err = -2.0 * b * xs ** 3 - 1.0
+    return a, b, err
+
+
+def ns_coefficients(floor: float = 1e-3, steps: int = 10):
+    """List of (a_k, b_k) for k = 0..steps-1 and the final interval half-width."""
+    lo, hi = floor, 1.0
+    coeffs = []
+    err = 0.0
+    for k in range(steps):
+        a, b, err = _minimax_cubic(lo, hi)
+        if k < steps - 1:
+            a, b = a / (1.0 + err), b / (1.0 + err)
+            lo, hi = (1.0 - err) / (1.0 + err), 1.0
+        coeffs.append((a, b))
+    return coeffs, err
+
+
+# ---------------------------------------------------------------------------
+# Coupled Newton-Schulz inverse square root in fp64 ([OKLS] "How it works":
+# roots evaluated by the coupled iteration; intro: 10 steps, 27 GEMMs).
+#   Y_0 = S / c with c = ||S||_F (so the spectrum lies in (0, 1]), Z_0 = I,
+#   T_k = a_k I + b_k Z_k Y_k,  Y_{k+1} = Y_k T_k,  Z_{k+1} = T_k Z_k.
+#   Z_K -> (S/c)^{-1/2}, Y_K -> (S/c)^{1/2};  P = Z_K / sqrt(c).
+# This is the iteration itself (the GPU's algorithm in exact-ish arithmetic);
+# the exact eigh root above is the method's target.
+# ---------------------------------------------------------------------------
+def ns_inv_sqrt(S: np.ndarray, coeffs):
+    """Returns (S^{-1/2} estimate, S^{1/2} estimate) after len(coeffs) steps."""
+    d = S.shape[0]
+    eye = np.eye(d)
+    c = float(np.linalg.norm(S))
+    Y = S / c
+    Z = eye.copy()
+    for a, b in coeffs:
+        T = a * eye + b * (Z @ Y)
+        Y, Z = Y @ T, T @ Z
+    return Z / math.sqrt(c), Y * math.sqrt(c)
+
+
+def ns_inv_quarter(S: np.ndarray, coeffs):
+    """S^{-1/4} as two chained inverse-square-root iterations (R8):
+    R = S^{1/2} from the first chain's Y output, then P = R^{-1/2}."""
+    _, R = ns_inv_sqrt(S, coeffs)
+    P, _ = ns_inv_sqrt(_sym(R), coeffs)
+    return P
+
+
+def ns_eigen_closed_form(S: np.ndarray, coeffs, p: int = 2):
+    """Exact-arithmetic output of ns_inv_sqrt through the eigen-decomposition:
+    on each eigen-direction the coupled iteration keeps Z_k Y_k = sigma_k^2 with
+    sigma_0 = sqrt(lambda / c) and sigma_{k+1} = sigma_k (a_k + b_k sigma_k^2),
+    so P = V diag(sigma_K / sqrt(lambda)) V^T.  Used as a diagnostic and a pin."""
+    lam, V = np.linalg.eigh(_sym(S))
+    c = float(np.linalg.norm(S))
+    s = np.sqrt(lam / c)
+    for a, b in coeffs:
+        s = s * (a + b * s * s)
+    if p == 2:
+        return (V * (s / np.sqrt(lam))) @ V.T
+    raise ValueError("closed form only for p=2")
+
+
+# ---------------------------------------------------------------------------
+# [OKLS] "How it works": U = P_a N P_b; c_shape scaling.
+# R6 (AdamC, [OKLS] "Learning-rate schedule"/"Hyperparameters"): decoupled decay
+# with the factor lr / lr_peak, applied to the previous weights.
+# ---------------------------------------------------------------------------
+def whiten(Pa, N, Pb):
+    return Pa @ N @ Pb
+
+
+def update_weights(W, U, lr: float, lr_peak: float, wd: float):
+    m, n = W.shape
+    decay = 1.0 - lr * wd * (lr / lr_peak)
+    return decay * W - lr * c_shape(m, n) * U
+
+
+# ---------------------------------------------------------------------------
+# State and full steps.
+# ---------------------------------------------------------------------------
+@dataclass
+class MatState:
+    W: np.ndarray
+    M: np.ndarray
+    Sa: np.ndarray
+    Sb: np.ndarray
+    Pa: np.ndarray
+    Pb: np.ndarray
+
+
+def init_state(W: np.ndarray, eps: float) -> MatState:
+    """[OKLS] "Hyperparameters": eps added at factor initialisation (S_0 = eps I);
+    R2: P_0 = I; momentum starts at zero."""
+    m, n = W.shape
+    return MatState(W=np.array(W, dtype=np.float64), M=np.zeros((m, n)),
+                    Sa=eps * np.eye(m), Sb=eps * np.eye(n), Pa=np.eye(m), Pb=np.eye(n))
+
+
+@dataclass
+class StepResult:
+    state: MatState
+    N: np.ndarray
+    U: np.ndarray
+    Pa_ns: np.ndarray | None = None
+    Pb_ns: np.ndarray | None = None
+    kappa_a: float = 0.0
+    kappa_b: float = 0.0
+    extra: dict = field(default_factory=dict)
+
+
+def okls_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "exact") -> StepResult:
+    """One OKLS step for one matrix ([OKLS] "How it works", in its order):
+    factors with the previous P, fresh roots, Nesterov momentum, two-sided
+    whitening, c_shape-scaled update with AdamC decay.
+    root='exact' uses eigh roots (the method's target); root='ns' uses the
+    coupled Newton-Schulz iteration in fp64.  Both are always reported."""
+    G = np.asarray(G, dtype=np.float64)
+    Sa, Sb = factor_update_okls(st.Sa, st.Sb, st.Pa, st.Pb, G, hp.beta2, hp.eps)
+    Pa_ex, ka = inv_root_exact(Sa, 2)
+    Pb_ex, kb = inv_root_exact(Sb, 2)
+    coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+    Pa_ns, _ = ns_inv_sqrt(Sa, coeffs)
+    Pb_ns, _ = ns_inv_sqrt(Sb, coeffs)
+    Pa, Pb = (Pa_ex, Pb_ex) if root == "exact" else (_sym(Pa_ns), _sym(Pb_ns))
+    M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
+    U = whiten(Pa, N, Pb)
+    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
+    return StepResult(MatState(W, M, Sa, Sb, Pa, Pb), N, U, Pa_ns, Pb_ns, ka, kb)
+
+
+def shampoo_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "exact") -> StepResult:
+    """Classic Shampoo mode (R7): sums G G^T and G^T G, P = S^{-1/4}
+    ([CLEAN] eq (2)-(3), [SHAMPOO] worked example); momentum, c_shape and
+    decoupled decay as in OKLS."""
+    G = np.asarray(G, dtype=np.float64)
+    Sa, Sb = factor_update_shampoo(st.Sa, st.Sb, G, hp.eps)
+    Pa_ex, ka = inv_root_exact(Sa, 4)
+    Pb_ex, kb = inv_root_exact(Sb, 4)
+    coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+    Pa_ns = _sym(ns_inv_quarter(Sa, coeffs))
+    Pb_ns = _sym(ns_inv_quarter(Sb, coeffs))
+    Pa, Pb = (Pa_ex, Pb_ex) if root == "exact" else (Pa_ns, Pb_ns)
+    M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
+    U = whiten(Pa, N, Pb)
+    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
+    return StepResult(MatState(W, M, Sa, Sb, Pa, Pb), N, U, Pa_ns, Pb_ns, ka, kb)
+
+
+def step(st: MatState, G, hp: Hyper, t: int, mode: str = "okls", root: str = "exact") -> StepResult:
+    if mode == "okls":
+        return okls_step(st, G, hp, t, root)
+    if mode == "shampoo":
+        return shampoo_step(st, G, hp, t, root)
+    raise ValueError(mode)
+
+
+def step_batched(states, Gs, hp: Hyper, t: int, mode: str = "okls", root: str = "exact"):
+    """[OKLS] "Batched matrices": a 3-D parameter (N, m, n) is N independent
+    matrices sharing the hyperparameters."""
+    return [step(s, g, hp, t, mode, root) for s, g in zip(states, Gs)]
+
+
+def rel_frob(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
