@@ -1,0 +1,158 @@
+/*
+ * okls.h - C ABI of the MI355X (gfx950) batched Online KL Shampoo / Shampoo
+ * preconditioner step.
+ *
+ * What one okls_step computes, for every matrix parameter G in R^{m x n}
+ * of every group ("Online KL Shampoo" project README, section "How it works",
+ * and its intro list):
+ *   1. two-sided factor updates with the previous preconditioners
+ *        S_a <- beta2 S_a + (1-beta2)/n (G P_b)(G P_b)^T + eps I
+ *        S_b <- beta2 S_b + (1-beta2)/m (P_a G)^T (P_a G) + eps I
+ *      or, in Shampoo mode, the sums S_a += G G^T, S_b += G^T G (+ eps I)
+ *      ("Clean: Second-order LLM Training at Linear Memory Cost via Nystrom
+ *      Sketching", section 2, eq. (2); the optim-book Shampoo chapter's
+ *      worked example);
+ *   2. fresh inverse roots P = S^{-1/2} (Shampoo: S^{-1/4}, the Clean paper's
+ *      eq. (3)) from a coupled Newton-Schulz iteration made of GEMMs only
+ *      (10 steps, 27 GEMMs per root, fp16 GEMM inputs with fp32 accumulation);
+ *   3. Nesterov momentum with variance correction, M <- beta1 M + (1-beta1) G,
+ *      N = s_t (beta1 M + (1-beta1) G), whitened U = P_a N P_b;
+ *   4. W <- (1 - lr wd lr/lr_peak) W - lr c_shape U,
+ *      c_shape = sqrt(m/n) / (sqrt(m) + sqrt(n))  (README "How it works";
+ *      AdamC decay per "Learning-rate schedule" and "Hyperparameters").
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     row-major and contiguous, at least 16-byte aligned.  A group of N
+ *     same-shaped matrices is one (N, rows, cols) tensor ("Batched matrices"
+ *     section: a 3-D parameter is N independent matrices that share the
+ *     hyperparameters).
+ *   - The caller owns every tensor and the workspace.  The library never
+ *     allocates device memory; the handle owns host memory only.
+ *   - All device work is enqueued on the given stream (a hipStream_t passed
+ *     as void*; NULL is the default stream).  okls_init and okls_init_state
+ *     synchronise that stream once (init uploads descriptor tables);
+ *     okls_step never synchronises.  Device faults surface at the caller's
+ *     next synchronisation.
+ *   - Errors are returned as okls_status; no exception crosses the ABI.
+ *     Argument errors are detected on the host before any launch.
+ *   - A handle may be used by one host thread at a time.  Two steps that
+ *     share a workspace must be ordered on one stream.
+ */
+#ifndef OKLS_H_
+#define OKLS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OKLS_OK = 0,
+    OKLS_ERR_INVALID_ARG = -1,   /* null pointer, bad enum, bad hyperparameter */
+    OKLS_ERR_SHAPE = -2,         /* non-positive or too large dimensions, too many groups */
+    OKLS_ERR_DTYPE = -3,         /* unsupported gradient dtype */
+    OKLS_ERR_WORKSPACE = -4,     /* workspace null, misaligned or smaller than okls_workspace_size */
+    OKLS_ERR_HIP = -5,           /* a HIP runtime call or launch failed */
+    OKLS_ERR_NONFINITE = -6,     /* okls_check_finite found Inf/NaN in the state */
+    OKLS_ERR_UNSUPPORTED = -7    /* a combination this build does not implement */
+} okls_status;
+
+typedef enum { OKLS_F32 = 0, OKLS_BF16 = 1 } okls_dtype;
+
+typedef enum {
+    OKLS_MODE_OKLS = 0,      /* KL factor EMAs, P = S^{-1/2} */
+    OKLS_MODE_SHAMPOO = 1    /* plain sums, P = S^{-1/4} via two chained roots */
+} okls_mode;
+
+typedef struct {
+    int32_t mode;              /* okls_mode */
+    int32_t ns_steps;          /* Newton-Schulz steps, 2..16 (pages: 10) */
+    int32_t ns_split_steps;    /* first k NS steps use split-fp16 (hi*hi + hi*lo + lo*hi)
+                                  GEMMs; 0 = every NS GEMM plain fp16 (the pages' FP16
+                                  path), ns_steps = every NS GEMM fp32-accurate */
+    int32_t factor_split;      /* 1: factor, cross-preconditioning and whitening GEMMs
+                                  also use split-fp16 (the fp32-accurate path) */
+    int32_t nesterov_var_corr; /* 1: N scaled by s_t = 1/sqrt(var) (reading of "variance
+                                  correction"); 0: s_t = 1 */
+    int32_t chunk_matrices;    /* 0: all matrices in one pass; k > 0: at most k matrices
+                                  per pass (bounds the workspace) */
+    float beta1;               /* Nesterov momentum EMA coefficient (default 0.9684) */
+    float beta2;               /* factor EMA coefficient (default 0.9482); ignored in Shampoo mode */
+    float eps;                 /* added at factor init and after every update (default 1e-9) */
+    float weight_decay;        /* AdamC decoupled decay coefficient (default 0.0303) */
+    float lr_peak;             /* initial learning rate kept for the AdamC correction */
+    float ns_floor;            /* lower end l_0 of the interval the NS coefficients are
+                                  optimised on, for sqrt(lambda / ||S||_F); default 1e-3 */
+    float ns_damping;          /* nu: the root is taken of S + (nu / sqrt(d)) ||S||_F I, which
+                                  keeps the rounded iteration positive definite; default
+                                  5e-3 for the fp16 path, 4e-4 suits the split-fp16 path */
+} okls_config;
+
+typedef struct {
+    int32_t batch;     /* N >= 1 matrices of this shape */
+    int32_t m, n;      /* rows (fan-out) and columns of each matrix, 1..32768 */
+    int32_t g_dtype;   /* okls_dtype of the gradient; W, M, S, P are fp32 */
+} okls_group_desc;
+
+typedef struct {
+    float* W;          /* (N, m, n) weights, updated in place */
+    const void* G;     /* (N, m, n) gradient, read only, fp32 or bf16 */
+    float* M;          /* (N, m, n) momentum, updated in place */
+    float* Sa;         /* (N, m, m) left factor, symmetric, updated in place */
+    float* Sb;         /* (N, n, n) right factor */
+    float* Pa;         /* (N, m, m) left preconditioner S_a^{-1/2} (Shampoo S_a^{-1/4}) */
+    float* Pb;         /* (N, n, n) right preconditioner */
+} okls_group_tensors;
+
+typedef struct okls_handle okls_handle;
+
+/* Fills cfg with the pages' defaults ("Hyperparameters" table of the README;
+ * 10 NS steps) and the fp16 path. */
+void okls_default_config(okls_config* cfg);
+
+/* Bytes of device workspace that okls_init needs for these groups.  Pure
+ * host function.  Returns 0 if the arguments are invalid. */
+size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups);
+
+/* Validates the groups, plans the launches and uploads descriptor tables into
+ * the caller's workspace (ws_bytes >= okls_workspace_size, 256-byte aligned).
+ * The workspace must stay valid and unused by others until okls_destroy.
+ * Synchronises `stream` once.  *out is NULL on error. */
+okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups,
+                      const okls_group_desc* groups, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* Fills the state for a fresh start (README "Hyperparameters": eps at factor
+ * initialisation): S = eps I, P = I, M = 0.  W and G are not touched (may be
+ * NULL).  `tensors` points to n_groups entries.  Asynchronous on `stream`. */
+okls_status okls_init_state(okls_handle* h, const okls_group_tensors* tensors, void* stream);
+
+/* One optimizer step (1-based step counter t, current learning rate lr) for
+ * every matrix of every group: steps 1-4 in the header comment.  G is read
+ * only; W, M, S_a, S_b, P_a, P_b are updated in place.  S must be symmetric
+ * on entry (only its upper triangle is read).  Asynchronous on `stream`. */
+okls_status okls_step(okls_handle* h, const okls_group_tensors* tensors, int64_t t, float lr,
+                      void* stream);
+
+/* Scans W, M, S and P of every group for Inf/NaN; synchronises `stream`.
+ * Returns OKLS_OK or OKLS_ERR_NONFINITE. */
+okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* tensors, void* stream);
+
+/* The Newton-Schulz coefficient table the handle uses: a[k], b[k] for
+ * k < ns_steps (T_k = a_k I + b_k Z_k Y_k), written to caller host arrays of
+ * length >= max_steps.  Returns the number of steps, or -1 on bad arguments. */
+int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_steps);
+
+/* Frees the handle's host memory.  Does not touch device memory. */
+okls_status okls_destroy(okls_handle* h);
+
+/* Static string describing a status code. */
+const char* okls_status_string(okls_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OKLS_H_ */

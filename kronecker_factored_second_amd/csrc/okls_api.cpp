@@ -1,0 +1,1130 @@
+// Host side of the batched OKLS / Shampoo preconditioner step: argument
+// validation, workspace layout, launch planning and the C ABI of okls.h.
+//
+// One okls_step enqueues, per chunk of matrices, this fixed sequence
+// (all launches grouped over every matrix / factor of the chunk):
+//   stats(G, N, P_old)  -> cast(G16, G16^T, N16 [+ M update], P16_old)
+//   GEMM  X_a = G P_b, X_b^T = G^T P_a          (OKLS only)
+//   stats -> cast(X16)                          (OKLS only)
+//   GEMM  S <- c0 S + c1 X X^T + eps I          (upper tiles, mirrored)
+//   stats(S) -> cast(Y_0 = S/c, Z_1 = a_0 I + b_0 S/c)
+//   GEMM  Newton-Schulz: 1 + 3*(K-2) + 2 GEMMs per root in 2K-1 launches
+//         (Shampoo: a second chain on the first chain's square root)
+//   GEMM  V^T = P_b N^T -> stats -> cast
+//   GEMM  U = P_a V with the fused update W <- decay W - lr c_shape U
+// The order is the "Online KL Shampoo" README's "How it works": factors
+// with the previous preconditioners, fresh roots, whitening, update.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/okls.h"
+#include "okls_kernels.h"
+
+using namespace okls;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDim = 32768;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int pad_tile(int x) { return (x + kTile - 1) / kTile * kTile; }
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz coefficients.  The README ("How it works" and the intro
+// list) names Chebyshev-optimised coefficients with deterministic per-step
+// scales for a 10-step coupled iteration but prints no values.  Reading
+// taken here: each step k applies sigma -> sigma (a_k + b_k sigma^2) to every
+// eigen-direction of Z_k Y_k = sigma^2; (a_k, b_k) is the odd cubic with the
+// least maximum deviation from 1 on the current interval [lo, hi].  With
+// equal deviation E at lo, at the interior maximum x* and at hi:
+//   a = -b (hi^2 + hi lo + lo^2),  x*^2 = (hi^2 + hi lo + lo^2) / 3,
+//   b = -2 / (2 x*^3 + lo hi (lo + hi)),  E = -2 b x*^3 - 1.
+// Every step except the last is divided by (1 + E) so the next interval is
+// [(1 - E)/(1 + E), 1] and no iterate's spectrum exceeds 1 (the fp16 range
+// guard); the last is left unscaled so the result is centred on 1.
+// ---------------------------------------------------------------------------
+void ns_table(double floor, int steps, std::vector<double>& a, std::vector<double>& b, double* final_err) {
+  a.assign(steps, 0.0);
+  b.assign(steps, 0.0);
+  double lo = floor, hi = 1.0, err = 0.0;
+  for (int k = 0; k < steps; ++k) {
+    const double q = hi * hi + hi * lo + lo * lo;
+    const double xs = std::sqrt(q / 3.0);
+    double bk = -2.0 / (2.0 * xs * xs * xs + lo * hi * (lo + hi));
+    double ak = -bk * q;
+    err = -2.0 * bk * xs * xs * xs - 1.0;
+    if (k < steps - 1) {
+      ak /= (1.0 + err);
+      bk /= (1.0 + err);
+      lo = (1.0 - err) / (1.0 + err);
+      hi = 1.0;
+    }
+    a[k] = ak;
+    b[k] = bk;
+  }
+  if (final_err) *final_err = err;
+}
+
+float pow2_for_bound(double bound) {   // largest 2^e with bound * 2^e <= 2^kScaleExp
+  const int e = kScaleExp - static_cast<int>(std::ceil(std::log2(std::max(bound, 1e-30))));
+  return std::ldexp(1.0f, e);
+}
+
+struct FacBufs {
+  int d = 0, dp = 0, ld = 0;
+  size_t Y[2] = {0, 0}, Z[2] = {0, 0}, T = 0, R32 = 0;
+  int s_pold = 0, s_cinv = 0, s_rho = 0, s_sqrtc = 0, s_p16 = 0;
+  int s_cinv2 = 0, s_rho2 = 0, s_sqrtc2 = 0;
+};
+
+struct MatBufs {
+  int group = 0, index = 0, m = 0, n = 0, mp = 0, np = 0, ldm = 0, ldn = 0;
+  size_t G16 = 0, G16T = 0, N16 = 0, Xa32 = 0, XbT32 = 0, Xa16 = 0, XbT16 = 0, VT32 = 0, VT16 = 0;
+  int s_g = 0, s_n = 0, s_xa = 0, s_xb = 0, s_vt = 0;
+  FacBufs fa, fb;
+};
+
+enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2 };
+
+struct LaunchRec {
+  int type = L_STAT;
+  int first = 0, count = 0;     // jobs (stat/cast) or tiles (gemm)
+  int nblocks = 0;
+  int blk_offset = 0;
+  int prob_base = 0;
+  int split_in = 0, write_lo = 0;
+  float ka = 0.f, kb = 0.f;
+};
+
+// Global scale slots
+enum { SL_ONE = 0, SL_Y = 1, SL_Z = 2, SL_T = 3, SL_FIRST_DYN = 4 };
+
+Ref ws_ref(size_t off) { return Ref{REF_WS, 0, static_cast<int64_t>(off)}; }
+Ref user_ref(int kind, int group, size_t byte_off) { return Ref{kind, group, static_cast<int64_t>(byte_off)}; }
+Ref no_ref() { return Ref{REF_NONE, 0, 0}; }
+
+bool env_fault(const char* call) {
+  const char* f = std::getenv("OKLS_FAULT");
+  return f != nullptr && std::strcmp(f, call) == 0;
+}
+
+}  // namespace
+
+struct okls_handle {
+  okls_config cfg{};
+  std::vector<okls_group_desc> groups;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_scal = 0, off_part = 0, off_flag = 0;
+  std::vector<std::vector<LaunchRec>> chunks;
+  std::vector<double> na, nb;
+};
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Validation
+// ---------------------------------------------------------------------------
+okls_status check_config(const okls_config* c) {
+  if (c == nullptr) return OKLS_ERR_INVALID_ARG;
+  if (c->mode != OKLS_MODE_OKLS && c->mode != OKLS_MODE_SHAMPOO) return OKLS_ERR_INVALID_ARG;
+  if (c->ns_steps < 2 || c->ns_steps > 16) return OKLS_ERR_INVALID_ARG;
+  if (c->ns_split_steps < 0 || c->ns_split_steps > c->ns_steps) return OKLS_ERR_INVALID_ARG;
+  if (c->factor_split != 0 && c->factor_split != 1) return OKLS_ERR_INVALID_ARG;
+  if (c->nesterov_var_corr != 0 && c->nesterov_var_corr != 1) return OKLS_ERR_INVALID_ARG;
+  if (c->chunk_matrices < 0) return OKLS_ERR_INVALID_ARG;
+  if (!(c->beta1 >= 0.f && c->beta1 < 1.f)) return OKLS_ERR_INVALID_ARG;
+  if (c->mode == OKLS_MODE_OKLS && !(c->beta2 >= 0.f && c->beta2 < 1.f)) return OKLS_ERR_INVALID_ARG;
+  if (!(c->eps >= 0.f && std::isfinite(c->eps))) return OKLS_ERR_INVALID_ARG;
+  if (!(c->weight_decay >= 0.f && std::isfinite(c->weight_decay))) return OKLS_ERR_INVALID_ARG;
+  if (!(c->lr_peak > 0.f && std::isfinite(c->lr_peak))) return OKLS_ERR_INVALID_ARG;
+  if (!(c->ns_floor > 0.f && c->ns_floor < 1.f)) return OKLS_ERR_INVALID_ARG;
+  if (!(c->ns_damping >= 0.f && c->ns_damping < 1.f)) return OKLS_ERR_INVALID_ARG;
+  return OKLS_OK;
+}
+
+okls_status check_groups(int n_groups, const okls_group_desc* g) {
+  if (g == nullptr) return OKLS_ERR_INVALID_ARG;
+  if (n_groups < 1 || n_groups > kMaxGroups) return OKLS_ERR_SHAPE;
+  for (int i = 0; i < n_groups; ++i) {
+    if (g[i].batch < 1 || g[i].m < 1 || g[i].n < 1 || g[i].m > kMaxDim || g[i].n > kMaxDim) return OKLS_ERR_SHAPE;
+    if (g[i].g_dtype != OKLS_F32 && g[i].g_dtype != OKLS_BF16) return OKLS_ERR_DTYPE;
+  }
+  return OKLS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Planner
+// ---------------------------------------------------------------------------
+struct Planner {
+  const okls_config& cfg;
+  const std::vector<okls_group_desc>& groups;
+  bool okls_mode;
+  bool lo_layout;
+  std::vector<double> na, nb;
+  float sY = 0, sZ = 0, sT = 0;
+
+  // tables
+  std::vector<GemmProb> probs;
+  std::vector<TileRef> tiles;
+  std::vector<StatJob> stat_jobs;
+  std::vector<CastJob> cast_jobs;
+  std::vector<std::vector<LaunchRec>> chunks;
+  std::map<std::string, std::pair<int, int>> tile_cache;
+
+  std::vector<std::map<size_t, size_t>> ws_bufs;   // per chunk: workspace buffer offset -> bytes
+  size_t chunk_bytes = 0;     // per-chunk buffer region size (max over chunks)
+  int n_slots = SL_FIRST_DYN; // max over chunks
+  int max_partials = 1;
+
+  Planner(const okls_config& c, const std::vector<okls_group_desc>& g)
+      : cfg(c), groups(g), okls_mode(c.mode == OKLS_MODE_OKLS),
+        lo_layout(c.factor_split != 0 || c.ns_split_steps > 0) {
+    ns_table(cfg.ns_floor, cfg.ns_steps, na, nb, nullptr);
+    double prod = 1.0, amax = 0.0;
+    for (int k = 0; k < cfg.ns_steps; ++k) {
+      prod *= std::max(std::fabs(na[k]), std::fabs(na[k] + nb[k]));
+      amax = std::max(amax, std::max(std::fabs(na[k]), std::fabs(na[k] + nb[k])));
+    }
+    sY = pow2_for_bound(1.0);
+    sZ = pow2_for_bound(prod);
+    sT = pow2_for_bound(amax);
+  }
+
+  int ld_for(int dp) const { return lo_layout ? 2 * dp : dp; }
+  // relative shift of the rooted matrix: delta = nu / sqrt(d)
+  float damping(int d) const { return static_cast<float>(cfg.ns_damping / std::sqrt(static_cast<double>(d))); }
+
+  // lays out one chunk's buffers from offset 0 (relative); returns size
+  std::vector<std::pair<size_t, size_t>> pending;   // chunk-relative buffers of the chunk being laid out
+  size_t layout_chunk(std::vector<MatBufs>& mats, int& slot) {
+    size_t off = 0;
+    pending.clear();
+    auto take = [&](size_t bytes) {
+      size_t o = off;
+      off = align_up(off + bytes, kAlign);
+      pending.push_back({o, bytes});
+      return o;
+    };
+    auto fac = [&](FacBufs& f, int d) {
+      f.d = d; f.dp = pad_tile(d); f.ld = ld_for(f.dp);
+      const size_t b16 = static_cast<size_t>(f.dp) * f.ld * 2;
+      f.Y[0] = take(b16); f.Y[1] = take(b16); f.Z[0] = take(b16); f.Z[1] = take(b16); f.T = take(b16);
+      if (!okls_mode) f.R32 = take(static_cast<size_t>(d) * d * 4);
+      f.s_pold = slot++; f.s_cinv = slot++; f.s_rho = slot++; f.s_sqrtc = slot++; f.s_p16 = slot++;
+      f.s_cinv2 = slot++; f.s_rho2 = slot++; f.s_sqrtc2 = slot++;
+    };
+    for (MatBufs& mb : mats) {
+      const okls_group_desc& g = groups[mb.group];
+      mb.m = g.m; mb.n = g.n; mb.mp = pad_tile(g.m); mb.np = pad_tile(g.n);
+      mb.ldm = ld_for(mb.mp); mb.ldn = ld_for(mb.np);
+      mb.G16 = take(static_cast<size_t>(mb.mp) * mb.ldn * 2);
+      mb.G16T = take(static_cast<size_t>(mb.np) * mb.ldm * 2);
+      mb.N16 = take(static_cast<size_t>(mb.mp) * mb.ldn * 2);
+      if (okls_mode) {
+        mb.Xa32 = take(static_cast<size_t>(mb.m) * mb.n * 4);
+        mb.XbT32 = take(static_cast<size_t>(mb.n) * mb.m * 4);
+        mb.Xa16 = take(static_cast<size_t>(mb.mp) * mb.ldn * 2);
+        mb.XbT16 = take(static_cast<size_t>(mb.np) * mb.ldm * 2);
+      }
+      mb.VT32 = take(static_cast<size_t>(mb.n) * mb.m * 4);
+      mb.VT16 = take(static_cast<size_t>(mb.np) * mb.ldm * 2);
+      mb.s_g = slot++; mb.s_n = slot++; mb.s_xa = slot++; mb.s_xb = slot++; mb.s_vt = slot++;
+      fac(mb.fa, g.m);
+      fac(mb.fb, g.n);
+    }
+    return off;
+  }
+
+  // ---- tiles
+  std::pair<int, int> tiles_for(const std::vector<GemmProb>& ps, bool upper) {
+    std::string key = upper ? "U" : "F";
+    for (const GemmProb& p : ps) key += ":" + std::to_string(p.Mp) + "x" + std::to_string(p.Np);
+    auto it = tile_cache.find(key);
+    if (it != tile_cache.end()) return it->second;
+    const int first = static_cast<int>(tiles.size());
+    for (size_t q = 0; q < ps.size(); ++q) {
+      const int tm = ps[q].Mp / kTile, tn = ps[q].Np / kTile;
+      for (int i = 0; i < tm; ++i)
+        for (int j = upper ? i : 0; j < tn; ++j)
+          tiles.push_back(TileRef{static_cast<int32_t>(q), (i << 16) | j});
+    }
+    const std::pair<int, int> r{first, static_cast<int>(tiles.size()) - first};
+    tile_cache[key] = r;
+    return r;
+  }
+
+  void add_gemm(std::vector<LaunchRec>& L, const std::vector<GemmProb>& ps, bool upper, int split_in,
+                int write_lo, float ka = 0.f, float kb = 0.f) {
+    if (ps.empty()) return;
+    LaunchRec r;
+    r.type = L_GEMM;
+    r.prob_base = static_cast<int>(probs.size());
+    probs.insert(probs.end(), ps.begin(), ps.end());
+    const std::pair<int, int> t = tiles_for(ps, upper);
+    r.first = t.first;
+    r.count = t.second;
+    r.split_in = split_in;
+    r.write_lo = write_lo;
+    r.ka = ka;
+    r.kb = kb;
+    L.push_back(r);
+  }
+
+  // ---- statistics: returns (part_begin, part_count) per job appended
+  struct StatSpec { int kind; Ref src; int ld; Ref src2; int g_bf16; int rows, cols; };
+  std::vector<std::pair<int, int>> add_stats(std::vector<LaunchRec>& L, const std::vector<StatSpec>& specs) {
+    std::vector<std::pair<int, int>> parts;
+    LaunchRec r;
+    r.type = L_STAT;
+    r.first = static_cast<int>(stat_jobs.size());
+    int blk = 0, part = 0;
+    for (const StatSpec& s : specs) {
+      StatJob j{};
+      j.kind = s.kind; j.src = s.src; j.src_ld = s.ld; j.src2 = s.src2; j.g_bf16 = s.g_bf16;
+      j.rows = s.rows; j.cols = s.cols;
+      j.rows_per_blk = std::max(1, std::min(s.rows, 32768 / std::max(1, s.cols)));
+      const int nb = (s.rows + j.rows_per_blk - 1) / j.rows_per_blk;
+      j.part_begin = part;
+      j.blk_begin = blk;
+      parts.push_back({part, nb});
+      part += nb;
+      blk += nb;
+      stat_jobs.push_back(j);
+    }
+    r.count = static_cast<int>(specs.size());
+    r.nblocks = blk;
+    max_partials = std::max(max_partials, part);
+    if (!specs.empty()) L.push_back(r);
+    return parts;
+  }
+
+  struct CastSpec {
+    int kind; Ref src; int src_ld; Ref src2; int g_bf16; int write_m; int transpose;
+    int rows, cols, dst_rows_p, dst_cols_p; Ref dst; int dst_ld; int dst_lo;
+    std::pair<int, int> parts; int scale_mode; int scale_slot;
+    int cinv_slot, rho_slot, sqrtc_slot, p16_slot; int write_lo; float damp;
+  };
+  CastSpec cast_spec() {
+    CastSpec c{};
+    c.src2 = no_ref();
+    c.dst = no_ref();
+    c.cinv_slot = c.rho_slot = c.sqrtc_slot = c.p16_slot = -1;
+    return c;
+  }
+  void add_cast(std::vector<LaunchRec>& L, const std::vector<CastSpec>& specs, float ka = 0.f, float kb = 0.f) {
+    if (specs.empty()) return;
+    LaunchRec r;
+    r.type = L_CAST;
+    r.first = static_cast<int>(cast_jobs.size());
+    int blk = 0;
+    for (const CastSpec& s : specs) {
+      CastJob j{};
+      j.kind = s.kind; j.src = s.src; j.src_ld = s.src_ld; j.src2 = s.src2; j.g_bf16 = s.g_bf16;
+      j.write_m = s.write_m; j.transpose = s.transpose; j.rows = s.rows; j.cols = s.cols;
+      j.dst_rows_p = s.dst_rows_p; j.dst_cols_p = s.dst_cols_p; j.dst = s.dst; j.dst_ld = s.dst_ld;
+      j.dst_lo = s.dst_lo; j.part_begin = s.parts.first; j.part_count = s.parts.second;
+      j.scale_mode = s.scale_mode; j.scale_slot = s.scale_slot; j.cinv_slot = s.cinv_slot;
+      j.rho_slot = s.rho_slot; j.sqrtc_slot = s.sqrtc_slot; j.p16_slot = s.p16_slot;
+      j.p16_static = sZ; j.write_lo = s.write_lo; j.damp = s.damp;
+      j.tiles_x = s.dst_cols_p / kCastTile;
+      j.blk_begin = blk;
+      blk += j.tiles_x * (s.dst_rows_p / kCastTile);
+      cast_jobs.push_back(j);
+    }
+    r.count = static_cast<int>(specs.size());
+    r.nblocks = blk;
+    r.ka = ka;
+    r.kb = kb;
+    L.push_back(r);
+  }
+
+  GemmProb prob() {
+    GemmProb p{};
+    p.A = p.B = p.out32 = p.out16 = p.aux = no_ref();
+    p.s_out = -1;
+    p.cslot = -1;
+    return p;
+  }
+
+  // ---- Newton-Schulz chain for a list of factors.  src(f) is the fp32
+  // matrix being rooted (d x d, ld d); returns launches appended to L.
+  // final_mode 0: inverse root into the caller P (+ fp16 copy in Z[K%2]);
+  // final_mode 1: square root into fac.R32 (the first Shampoo chain).
+  void ns_chain(std::vector<LaunchRec>& L, std::vector<FacBufs*>& facs, std::vector<Ref>& src,
+                std::vector<Ref>& pdst, int final_mode, int chain) {
+    const int K = cfg.ns_steps;
+    const int ks = cfg.ns_split_steps;
+    const size_t nf = facs.size();
+    // statistics (sum of squares) of the rooted matrix
+    std::vector<StatSpec> st;
+    for (size_t f = 0; f < nf; ++f)
+      st.push_back(StatSpec{ST_F32, src[f], facs[f]->d, no_ref(), 0, facs[f]->d, facs[f]->d});
+    std::vector<std::pair<int, int>> parts = add_stats(L, st);
+    // Y_0 = S/c and Z_1 = a_0 I + b_0 S/c
+    std::vector<CastSpec> cs;
+    for (size_t f = 0; f < nf; ++f) {
+      FacBufs& F = *facs[f];
+      CastSpec y = cast_spec();
+      y.kind = CA_NS_Y0; y.src = src[f]; y.src_ld = F.d; y.rows = F.d; y.cols = F.d;
+      y.dst_rows_p = F.dp; y.dst_cols_p = F.dp; y.dst = ws_ref(F.Y[0]); y.dst_ld = F.ld; y.dst_lo = F.dp;
+      y.parts = parts[f]; y.scale_mode = SC_STATIC; y.scale_slot = SL_Y;
+      y.cinv_slot = chain == 0 ? F.s_cinv : F.s_cinv2;
+      y.rho_slot = chain == 0 ? F.s_rho : F.s_rho2;
+      y.sqrtc_slot = chain == 0 ? F.s_sqrtc : F.s_sqrtc2;
+      y.p16_slot = (final_mode == 0) ? F.s_p16 : -1;
+      y.write_lo = ks > 0;
+      y.damp = damping(F.d);
+      cs.push_back(y);
+      CastSpec z = y;
+      z.kind = CA_NS_Z1; z.dst = ws_ref(F.Z[1]); z.scale_slot = SL_Z;
+      z.cinv_slot = z.rho_slot = z.sqrtc_slot = z.p16_slot = -1;
+      z.write_lo = ks > 1;
+      cs.push_back(z);
+    }
+    add_cast(L, cs, static_cast<float>(na[0]), static_cast<float>(nb[0]));
+    // step 0: Y_1 = a_0 Y_0 + b_0 Y_0 Y_0
+    {
+      std::vector<GemmProb> ps;
+      for (size_t f = 0; f < nf; ++f) {
+        FacBufs& F = *facs[f];
+        GemmProb p = prob();
+        p.A = p.B = ws_ref(F.Y[0]); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp; p.Mp = p.Np = F.dp;
+        p.epi = EPI_NS_Y1; p.aux = src[f]; p.ldaux = F.d; p.cslot = chain == 0 ? F.s_cinv : F.s_cinv2;
+        p.c2 = damping(F.d) / (1.0f + damping(F.d));
+        p.out16 = ws_ref(F.Y[1]); p.ld16 = F.ld; p.lo16 = F.dp; p.s_out = SL_Y; p.sA = p.sB = SL_Y;
+        ps.push_back(p);
+      }
+      add_gemm(L, ps, false, 0 < ks, 1 < ks, static_cast<float>(na[0]), static_cast<float>(nb[0]));
+    }
+    for (int k = 1; k < K; ++k) {
+      const int cb = k & 1, nbuf = (k + 1) & 1;
+      const float ka = static_cast<float>(na[k]), kb = static_cast<float>(nb[k]);
+      // T_k = a_k I + b_k Z_k Y_k
+      std::vector<GemmProb> pt;
+      for (size_t f = 0; f < nf; ++f) {
+        FacBufs& F = *facs[f];
+        GemmProb p = prob();
+        p.A = ws_ref(F.Z[cb]); p.B = ws_ref(F.Y[cb]); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
+        p.Mp = p.Np = F.dp; p.epi = EPI_NS_T; p.out16 = ws_ref(F.T); p.ld16 = F.ld; p.lo16 = F.dp;
+        p.s_out = SL_T; p.sA = SL_Z; p.sB = SL_Y;
+        pt.push_back(p);
+      }
+      add_gemm(L, pt, false, k < ks, k < ks, ka, kb);
+      std::vector<GemmProb> pu;
+      if (k < K - 1) {
+        for (size_t f = 0; f < nf; ++f) {   // Y_{k+1} = Y_k T_k
+          FacBufs& F = *facs[f];
+          GemmProb p = prob();
+          p.A = ws_ref(F.Y[cb]); p.B = ws_ref(F.T); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
+          p.Mp = p.Np = F.dp; p.epi = EPI_STORE16; p.out16 = ws_ref(F.Y[nbuf]); p.ld16 = F.ld; p.lo16 = F.dp;
+          p.s_out = SL_Y; p.sA = SL_Y; p.sB = SL_T;
+          pu.push_back(p);
+        }
+        for (size_t f = 0; f < nf; ++f) {   // Z_{k+1} = T_k Z_k
+          FacBufs& F = *facs[f];
+          GemmProb p = prob();
+          p.A = ws_ref(F.T); p.B = ws_ref(F.Z[cb]); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
+          p.Mp = p.Np = F.dp; p.epi = EPI_STORE16; p.out16 = ws_ref(F.Z[nbuf]); p.ld16 = F.ld; p.lo16 = F.dp;
+          p.s_out = SL_Z; p.sA = SL_T; p.sB = SL_Z;
+          pu.push_back(p);
+        }
+        add_gemm(L, pu, false, k < ks, k + 1 < ks);
+      } else {
+        for (size_t f = 0; f < nf; ++f) {
+          FacBufs& F = *facs[f];
+          GemmProb p = prob();
+          p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp; p.Mp = p.Np = F.dp; p.epi = EPI_NS_FINAL;
+          if (final_mode == 0) {      // P = Z_K / sqrt(c), fp16 copy Z_K * s_Z
+            p.A = ws_ref(F.T); p.B = ws_ref(F.Z[cb]); p.sA = SL_T; p.sB = SL_Z;
+            p.out32 = pdst[f]; p.ld32 = F.d; p.cslot = chain == 0 ? F.s_rho : F.s_rho2;
+            p.out16 = ws_ref(F.Z[nbuf]); p.ld16 = F.ld; p.lo16 = F.dp; p.s_out = SL_Z;
+          } else {                    // R = Y_K sqrt(c)
+            p.A = ws_ref(F.Y[cb]); p.B = ws_ref(F.T); p.sA = SL_Y; p.sB = SL_T;
+            p.out32 = ws_ref(F.R32); p.ld32 = F.d; p.cslot = F.s_sqrtc;
+          }
+          pu.push_back(p);
+        }
+        add_gemm(L, pu, false, k < ks, cfg.factor_split);
+      }
+    }
+  }
+
+  // P16 produced by the chain of this factor, in Z[K % 2]
+  size_t p16_of(const FacBufs& F) const { return F.Z[cfg.ns_steps & 1]; }
+
+  void plan_chunk(std::vector<MatBufs>& mats, size_t base) {
+    // rebase offsets
+    for (MatBufs& mb : mats) {
+      size_t* offs[] = {&mb.G16, &mb.G16T, &mb.N16, &mb.Xa32, &mb.XbT32, &mb.Xa16, &mb.XbT16, &mb.VT32, &mb.VT16};
+      for (size_t* o : offs) *o += base;
+      for (FacBufs* f : {&mb.fa, &mb.fb}) {
+        f->Y[0] += base; f->Y[1] += base; f->Z[0] += base; f->Z[1] += base; f->T += base; f->R32 += base;
+      }
+    }
+    ws_bufs.emplace_back();
+    for (const std::pair<size_t, size_t>& b : pending) ws_bufs.back()[b.first + base] = b.second;
+    std::vector<LaunchRec> L;
+    const int fs = cfg.factor_split;
+    auto gdt = [&](const MatBufs& mb) { return groups[mb.group].g_dtype; };
+    auto goff = [&](const MatBufs& mb) {
+      return static_cast<size_t>(mb.index) * mb.m * mb.n * (gdt(mb) == OKLS_BF16 ? 2 : 4);
+    };
+    auto moff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.n * 4; };
+    auto aoff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.m * 4; };
+    auto boff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.n * mb.n * 4; };
+
+    // 1. statistics of G, N and the previous preconditioners
+    std::vector<StatSpec> st;
+    for (const MatBufs& mb : mats) {
+      const int gk = gdt(mb) == OKLS_BF16 ? ST_BF16 : ST_F32;
+      st.push_back(StatSpec{gk, user_ref(REF_G, mb.group, goff(mb)), mb.n, no_ref(), 0, mb.m, mb.n});
+      st.push_back(StatSpec{ST_NESTEROV, user_ref(REF_G, mb.group, goff(mb)), mb.n,
+                            user_ref(REF_M, mb.group, moff(mb)), gdt(mb) == OKLS_BF16, mb.m, mb.n});
+      if (okls_mode) {
+        st.push_back(StatSpec{ST_F32, user_ref(REF_PA, mb.group, aoff(mb)), mb.m, no_ref(), 0, mb.m, mb.m});
+        st.push_back(StatSpec{ST_F32, user_ref(REF_PB, mb.group, boff(mb)), mb.n, no_ref(), 0, mb.n, mb.n});
+      }
+    }
+    std::vector<std::pair<int, int>> parts = add_stats(L, st);
+    // 2. casts
+    std::vector<CastSpec> cs;
+    const int per = okls_mode ? 4 : 2;
+    for (size_t q = 0; q < mats.size(); ++q) {
+      const MatBufs& mb = mats[q];
+      const bool bf = gdt(mb) == OKLS_BF16;
+      CastSpec g = cast_spec();
+      g.kind = bf ? CA_BF16 : CA_F32; g.src = user_ref(REF_G, mb.group, goff(mb)); g.src_ld = mb.n;
+      g.rows = mb.m; g.cols = mb.n; g.dst_rows_p = mb.mp; g.dst_cols_p = mb.np; g.dst = ws_ref(mb.G16);
+      g.dst_ld = mb.ldn; g.dst_lo = mb.np; g.parts = parts[per * q]; g.scale_mode = SC_ABSMAX;
+      g.scale_slot = mb.s_g; g.write_lo = fs;
+      cs.push_back(g);
+      CastSpec gt = g;
+      gt.transpose = 1; gt.dst_rows_p = mb.np; gt.dst_cols_p = mb.mp; gt.dst = ws_ref(mb.G16T);
+      gt.dst_ld = mb.ldm; gt.dst_lo = mb.mp;
+      cs.push_back(gt);
+      CastSpec nn = cast_spec();
+      nn.kind = CA_NESTEROV; nn.src = user_ref(REF_M, mb.group, moff(mb)); nn.src_ld = mb.n;
+      nn.src2 = user_ref(REF_G, mb.group, goff(mb)); nn.g_bf16 = bf; nn.write_m = 1;
+      nn.rows = mb.m; nn.cols = mb.n; nn.dst_rows_p = mb.mp; nn.dst_cols_p = mb.np; nn.dst = ws_ref(mb.N16);
+      nn.dst_ld = mb.ldn; nn.dst_lo = mb.np; nn.parts = parts[per * q + 1]; nn.scale_mode = SC_ABSMAX;
+      nn.scale_slot = mb.s_n; nn.write_lo = fs;
+      cs.push_back(nn);
+      if (okls_mode) {
+        const FacBufs* fl[2] = {&mb.fa, &mb.fb};
+        const int kinds[2] = {REF_PA, REF_PB};
+        const size_t offs[2] = {aoff(mb), boff(mb)};
+        for (int s = 0; s < 2; ++s) {
+          const FacBufs& F = *fl[s];
+          CastSpec p = cast_spec();
+          p.kind = CA_F32; p.src = user_ref(kinds[s], mb.group, offs[s]); p.src_ld = F.d;
+          p.rows = p.cols = F.d; p.dst_rows_p = p.dst_cols_p = F.dp; p.dst = ws_ref(F.T);
+          p.dst_ld = F.ld; p.dst_lo = F.dp; p.parts = parts[per * q + 2 + s]; p.scale_mode = SC_ABSMAX;
+          p.scale_slot = F.s_pold; p.write_lo = fs;
+          cs.push_back(p);
+        }
+      }
+    }
+    add_cast(L, cs);
+
+    if (okls_mode) {
+      // 3. X_a = G P_b (m x n), X_b^T = G^T P_a (n x m)
+      std::vector<GemmProb> px;
+      for (const MatBufs& mb : mats) {
+        GemmProb p = prob();
+        p.A = ws_ref(mb.G16); p.lda = mb.ldn; p.B = ws_ref(mb.fb.T); p.ldb = mb.fb.ld;
+        p.M = mb.m; p.N = mb.n; p.Kp = mb.np; p.Mp = mb.mp; p.Np = mb.np; p.epi = EPI_STORE32;
+        p.out32 = ws_ref(mb.Xa32); p.ld32 = mb.n; p.sA = mb.s_g; p.sB = mb.fb.s_pold;
+        px.push_back(p);
+        GemmProb r = prob();
+        r.A = ws_ref(mb.G16T); r.lda = mb.ldm; r.B = ws_ref(mb.fa.T); r.ldb = mb.fa.ld;
+        r.M = mb.n; r.N = mb.m; r.Kp = mb.mp; r.Mp = mb.np; r.Np = mb.mp; r.epi = EPI_STORE32;
+        r.out32 = ws_ref(mb.XbT32); r.ld32 = mb.m; r.sA = mb.s_g; r.sB = mb.fa.s_pold;
+        px.push_back(r);
+      }
+      add_gemm(L, px, false, fs, 0);
+      std::vector<StatSpec> sx;
+      for (const MatBufs& mb : mats) {
+        sx.push_back(StatSpec{ST_F32, ws_ref(mb.Xa32), mb.n, no_ref(), 0, mb.m, mb.n});
+        sx.push_back(StatSpec{ST_F32, ws_ref(mb.XbT32), mb.m, no_ref(), 0, mb.n, mb.m});
+      }
+      std::vector<std::pair<int, int>> px_parts = add_stats(L, sx);
+      std::vector<CastSpec> cx;
+      for (size_t q = 0; q < mats.size(); ++q) {
+        const MatBufs& mb = mats[q];
+        CastSpec a = cast_spec();
+        a.kind = CA_F32; a.src = ws_ref(mb.Xa32); a.src_ld = mb.n; a.rows = mb.m; a.cols = mb.n;
+        a.dst_rows_p = mb.mp; a.dst_cols_p = mb.np; a.dst = ws_ref(mb.Xa16); a.dst_ld = mb.ldn; a.dst_lo = mb.np;
+        a.parts = px_parts[2 * q]; a.scale_mode = SC_ABSMAX; a.scale_slot = mb.s_xa; a.write_lo = fs;
+        cx.push_back(a);
+        CastSpec b = cast_spec();
+        b.kind = CA_F32; b.src = ws_ref(mb.XbT32); b.src_ld = mb.m; b.rows = mb.n; b.cols = mb.m;
+        b.dst_rows_p = mb.np; b.dst_cols_p = mb.mp; b.dst = ws_ref(mb.XbT16); b.dst_ld = mb.ldm; b.dst_lo = mb.mp;
+        b.parts = px_parts[2 * q + 1]; b.scale_mode = SC_ABSMAX; b.scale_slot = mb.s_xb; b.write_lo = fs;
+        cx.push_back(b);
+      }
+      add_cast(L, cx);
+    }
+
+    // 4. factor update (upper tiles, mirrored)
+    {
+      std::vector<GemmProb> ps;
+      for (const MatBufs& mb : mats) {
+        GemmProb a = prob();
+        a.A = a.B = ws_ref(okls_mode ? mb.Xa16 : mb.G16); a.lda = a.ldb = mb.ldn;
+        a.M = a.N = mb.m; a.Kp = mb.np; a.Mp = a.Np = mb.mp; a.epi = EPI_SYRK;
+        a.out32 = user_ref(REF_SA, mb.group, aoff(mb)); a.ld32 = mb.m;
+        a.sA = a.sB = okls_mode ? mb.s_xa : mb.s_g;
+        a.c0 = okls_mode ? cfg.beta2 : 1.0f;
+        a.c1 = okls_mode ? static_cast<float>((1.0 - cfg.beta2) / mb.n) : 1.0f;
+        a.c2 = cfg.eps;
+        ps.push_back(a);
+        GemmProb b = prob();
+        b.A = b.B = ws_ref(okls_mode ? mb.XbT16 : mb.G16T); b.lda = b.ldb = mb.ldm;
+        b.M = b.N = mb.n; b.Kp = mb.mp; b.Mp = b.Np = mb.np; b.epi = EPI_SYRK;
+        b.out32 = user_ref(REF_SB, mb.group, boff(mb)); b.ld32 = mb.n;
+        b.sA = b.sB = okls_mode ? mb.s_xb : mb.s_g;
+        b.c0 = okls_mode ? cfg.beta2 : 1.0f;
+        b.c1 = okls_mode ? static_cast<float>((1.0 - cfg.beta2) / mb.m) : 1.0f;
+        b.c2 = cfg.eps;
+        ps.push_back(b);
+      }
+      add_gemm(L, ps, true, fs, 0);
+    }
+
+    // 5. inverse roots
+    std::vector<FacBufs*> facs;
+    std::vector<Ref> src, pdst;
+    for (MatBufs& mb : mats) {
+      facs.push_back(&mb.fa);
+      src.push_back(user_ref(REF_SA, mb.group, aoff(mb)));
+      pdst.push_back(user_ref(REF_PA, mb.group, aoff(mb)));
+      facs.push_back(&mb.fb);
+      src.push_back(user_ref(REF_SB, mb.group, boff(mb)));
+      pdst.push_back(user_ref(REF_PB, mb.group, boff(mb)));
+    }
+    if (okls_mode) {
+      ns_chain(L, facs, src, pdst, 0, 0);
+    } else {
+      ns_chain(L, facs, src, pdst, 1, 0);
+      std::vector<Ref> rsrc;
+      for (FacBufs* f : facs) rsrc.push_back(ws_ref(f->R32));
+      ns_chain(L, facs, rsrc, pdst, 0, 1);
+    }
+
+    // 6. whitening: V^T = P_b N^T (n x m), then U = P_a V fused with the update
+    {
+      std::vector<GemmProb> pv;
+      for (const MatBufs& mb : mats) {
+        GemmProb p = prob();
+        p.A = ws_ref(p16_of(mb.fb)); p.lda = mb.fb.ld; p.B = ws_ref(mb.N16); p.ldb = mb.ldn;
+        p.M = mb.n; p.N = mb.m; p.Kp = mb.np; p.Mp = mb.np; p.Np = mb.mp; p.epi = EPI_STORE32;
+        p.out32 = ws_ref(mb.VT32); p.ld32 = mb.m; p.sA = mb.fb.s_p16; p.sB = mb.s_n;
+        pv.push_back(p);
+      }
+      add_gemm(L, pv, false, fs, 0);
+      std::vector<StatSpec> sv;
+      for (const MatBufs& mb : mats) sv.push_back(StatSpec{ST_F32, ws_ref(mb.VT32), mb.m, no_ref(), 0, mb.n, mb.m});
+      std::vector<std::pair<int, int>> pvp = add_stats(L, sv);
+      std::vector<CastSpec> cv;
+      for (size_t q = 0; q < mats.size(); ++q) {
+        const MatBufs& mb = mats[q];
+        CastSpec c = cast_spec();
+        c.kind = CA_F32; c.src = ws_ref(mb.VT32); c.src_ld = mb.m; c.rows = mb.n; c.cols = mb.m;
+        c.dst_rows_p = mb.np; c.dst_cols_p = mb.mp; c.dst = ws_ref(mb.VT16); c.dst_ld = mb.ldm; c.dst_lo = mb.mp;
+        c.parts = pvp[q]; c.scale_mode = SC_ABSMAX; c.scale_slot = mb.s_vt; c.write_lo = fs;
+        cv.push_back(c);
+      }
+      add_cast(L, cv);
+      std::vector<GemmProb> pu;
+      for (const MatBufs& mb : mats) {
+        GemmProb p = prob();
+        p.A = ws_ref(p16_of(mb.fa)); p.lda = mb.fa.ld; p.B = ws_ref(mb.VT16); p.ldb = mb.ldm;
+        p.M = mb.m; p.N = mb.n; p.Kp = mb.mp; p.Mp = mb.mp; p.Np = mb.np; p.epi = EPI_UPDATE;
+        p.out32 = user_ref(REF_W, mb.group, moff(mb)); p.ld32 = mb.n; p.sA = mb.fa.s_p16; p.sB = mb.s_vt;
+        p.c0 = static_cast<float>(std::sqrt(static_cast<double>(mb.m) / mb.n) /
+                                  (std::sqrt(static_cast<double>(mb.m)) + std::sqrt(static_cast<double>(mb.n))));
+        pu.push_back(p);
+      }
+      add_gemm(L, pu, false, fs, 0);
+    }
+    chunks.push_back(std::move(L));
+  }
+
+  // ---- host-side extent checks of every descriptor against the buffer it
+  // points into; a failure is a planning error and nothing is launched.
+  const std::map<size_t, size_t>* cur_bufs = nullptr;
+  bool fits_ws(const Ref& r, size_t bytes) const {
+    auto it = cur_bufs->upper_bound(static_cast<size_t>(r.off));
+    if (it == cur_bufs->begin()) return false;
+    --it;
+    return static_cast<size_t>(r.off) >= it->first && static_cast<size_t>(r.off) + bytes <= it->first + it->second;
+  }
+  size_t user_bytes(int kind, int group) const {
+    const okls_group_desc& g = groups[group];
+    const size_t b = static_cast<size_t>(g.batch);
+    switch (kind) {
+      case REF_W: case REF_M: return b * g.m * g.n * 4;
+      case REF_G: return b * g.m * g.n * (g.g_dtype == OKLS_BF16 ? 2 : 4);
+      case REF_SA: case REF_PA: return b * g.m * g.m * 4;
+      case REF_SB: case REF_PB: return b * g.n * g.n * 4;
+    }
+    return 0;
+  }
+  bool fits(const Ref& r, size_t bytes) const {
+    if (r.kind == REF_WS) return fits_ws(r, bytes);
+    if (r.kind < REF_W || r.kind > REF_PB || r.group < 0 || r.group >= static_cast<int>(groups.size())) return false;
+    return r.off >= 0 && static_cast<size_t>(r.off) + bytes <= user_bytes(r.kind, r.group);
+  }
+  bool slot_ok(int s) const { return s >= 0 && s < n_slots; }
+
+  bool validate() {
+    if (ws_bufs.size() != chunks.size()) return false;
+    for (size_t ci = 0; ci < chunks.size(); ++ci) {
+      cur_bufs = &ws_bufs[ci];
+      for (const LaunchRec& r : chunks[ci]) {
+        if (r.type == L_GEMM) {
+          if (r.first < 0 || r.first + r.count > static_cast<int>(tiles.size())) return false;
+          const int segs = r.split_in ? 2 : 1;
+          for (int t = r.first; t < r.first + r.count; ++t) {
+            const TileRef tr = tiles[t];
+            const int q = r.prob_base + tr.prob;
+            if (tr.prob < 0 || q >= static_cast<int>(probs.size())) return false;
+            const GemmProb& p = probs[q];
+            const int ti = tr.ij >> 16, tj = tr.ij & 0xffff;
+            if (p.Mp % kTile || p.Np % kTile || p.Kp % kTile || p.Kp <= 0) return false;
+            if (ti < 0 || tj < 0 || ti >= p.Mp / kTile || tj >= p.Np / kTile) return false;
+            if (p.M > p.Mp || p.N > p.Np || p.M < 1 || p.N < 1) return false;
+            if (p.lda < segs * p.Kp || p.ldb < segs * p.Kp) return false;
+            if (!fits(p.A, static_cast<size_t>(p.Mp) * p.lda * 2) || !fits(p.B, static_cast<size_t>(p.Np) * p.ldb * 2))
+              return false;
+            if (!slot_ok(p.sA) || !slot_ok(p.sB)) return false;
+            if (p.s_out >= 0 && !slot_ok(p.s_out)) return false;
+            if (p.cslot >= 0 && !slot_ok(p.cslot)) return false;
+            const bool need32 = p.epi == EPI_STORE32 || p.epi == EPI_SYRK || p.epi == EPI_UPDATE ||
+                                (p.epi == EPI_NS_FINAL && p.out32.kind != REF_NONE);
+            if (need32) {
+              if (p.out32.kind == REF_NONE || p.ld32 < p.N) return false;
+              if (!fits(p.out32, (static_cast<size_t>(p.M - 1) * p.ld32 + p.N) * 4)) return false;
+              if (p.epi == EPI_SYRK && p.M != p.N) return false;
+            }
+            const bool need16 = p.epi == EPI_NS_T || p.epi == EPI_NS_Y1 || p.epi == EPI_STORE16 ||
+                                (p.epi == EPI_NS_FINAL && p.out16.kind != REF_NONE);
+            if (need16) {
+              if (p.out16.kind == REF_NONE || !slot_ok(p.s_out)) return false;
+              const int need_ld = r.write_lo ? p.lo16 + p.Np : p.Np;
+              if (p.ld16 < need_ld || (r.write_lo && p.lo16 < p.Np)) return false;
+              if (!fits(p.out16, static_cast<size_t>(p.Mp) * p.ld16 * 2)) return false;
+            }
+            if (p.epi == EPI_NS_Y1) {
+              if (p.aux.kind == REF_NONE || p.ldaux < p.N || !slot_ok(p.cslot)) return false;
+              if (!fits(p.aux, (static_cast<size_t>(p.M - 1) * p.ldaux + p.N) * 4)) return false;
+            }
+          }
+        } else if (r.type == L_STAT) {
+          int blk = 0;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const StatJob& s = stat_jobs[j];
+            if (s.blk_begin != blk || s.rows < 1 || s.cols < 1 || s.src_ld < s.cols || s.rows_per_blk < 1) return false;
+            const int nb = (s.rows + s.rows_per_blk - 1) / s.rows_per_blk;
+            blk += nb;
+            if (s.part_begin < 0 || s.part_begin + nb > max_partials) return false;
+            const size_t esz = (s.kind == ST_BF16 || (s.kind == ST_NESTEROV && s.g_bf16)) ? 2 : 4;
+            if (!fits(s.src, (static_cast<size_t>(s.rows - 1) * s.src_ld + s.cols) * esz)) return false;
+            if (s.kind == ST_NESTEROV && !fits(s.src2, (static_cast<size_t>(s.rows - 1) * s.src_ld + s.cols) * 4))
+              return false;
+          }
+          if (blk != r.nblocks) return false;
+        } else {
+          int blk = 0;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const CastJob& c = cast_jobs[j];
+            if (c.blk_begin != blk) return false;
+            if (c.dst_rows_p % kCastTile || c.dst_cols_p % kCastTile || c.tiles_x != c.dst_cols_p / kCastTile) return false;
+            blk += c.tiles_x * (c.dst_rows_p / kCastTile);
+            const int drows = c.transpose ? c.cols : c.rows, dcols = c.transpose ? c.rows : c.cols;
+            if (drows > c.dst_rows_p || dcols > c.dst_cols_p || c.src_ld < c.cols || c.rows < 1 || c.cols < 1) return false;
+            const int need_ld = c.write_lo ? c.dst_lo + c.dst_cols_p : c.dst_cols_p;
+            if (c.dst_ld < need_ld || (c.write_lo && c.dst_lo < c.dst_cols_p)) return false;
+            if (!fits(c.dst, static_cast<size_t>(c.dst_rows_p) * c.dst_ld * 2)) return false;
+            const size_t esz = (c.kind == CA_BF16) ? 2 : 4;
+            if (!fits(c.src, (static_cast<size_t>(c.rows - 1) * c.src_ld + c.cols) * esz)) return false;
+            if (c.kind == CA_NESTEROV) {
+              if (c.transpose) return false;
+              if (!fits(c.src2, (static_cast<size_t>(c.rows - 1) * c.src_ld + c.cols) * (c.g_bf16 ? 2 : 4))) return false;
+            }
+            if ((c.kind == CA_NS_Y0 || c.kind == CA_NS_Z1) && c.rows != c.cols) return false;
+            if (c.part_begin < 0 || c.part_count < 1 || c.part_begin + c.part_count > max_partials) return false;
+            if (!slot_ok(c.scale_slot)) return false;
+            for (int s : {c.cinv_slot, c.rho_slot, c.sqrtc_slot, c.p16_slot})
+              if (s >= 0 && !slot_ok(s)) return false;
+          }
+          if (blk != r.nblocks) return false;
+        }
+      }
+    }
+    return true;
+  }
+
+  // Plans every chunk; chunk buffers start at `base` (identical across chunks).
+  void plan(size_t base) {
+    std::vector<std::vector<MatBufs>> all;
+    std::vector<MatBufs> cur;
+    const int cap = cfg.chunk_matrices > 0 ? cfg.chunk_matrices : (1 << 30);
+    for (size_t g = 0; g < groups.size(); ++g)
+      for (int i = 0; i < groups[g].batch; ++i) {
+        MatBufs mb;
+        mb.group = static_cast<int>(g);
+        mb.index = i;
+        cur.push_back(mb);
+        if (static_cast<int>(cur.size()) == cap) { all.push_back(cur); cur.clear(); }
+      }
+    if (!cur.empty()) all.push_back(cur);
+    chunk_bytes = 0;
+    for (std::vector<MatBufs>& c : all) {
+      int slot = SL_FIRST_DYN;
+      chunk_bytes = std::max(chunk_bytes, layout_chunk(c, slot));
+      n_slots = std::max(n_slots, slot);
+      plan_chunk(c, base);
+    }
+  }
+};
+
+struct WsLayout {
+  size_t probs = 0, tiles = 0, stat = 0, cast = 0, scal = 0, part = 0, flag = 0, chunk = 0, total = 0;
+};
+
+WsLayout ws_layout(Planner& P) {
+  // tables depend on the chunk base only through offsets; plan with base 0 to size them
+  P.plan(0);
+  WsLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1), kAlign); return o; };
+  w.probs = take(P.probs.size() * sizeof(GemmProb));
+  w.tiles = take(P.tiles.size() * sizeof(TileRef));
+  w.stat = take(P.stat_jobs.size() * sizeof(StatJob));
+  w.cast = take(P.cast_jobs.size() * sizeof(CastJob));
+  w.scal = take(static_cast<size_t>(P.n_slots) * sizeof(float));
+  w.part = take(static_cast<size_t>(P.max_partials) * 2 * sizeof(float));
+  w.flag = take(sizeof(int));
+  w.chunk = off;
+  w.total = off + P.chunk_bytes;
+  return w;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+UserPtrs user_ptrs(const okls_handle* h, const okls_group_tensors* t) {
+  UserPtrs u;
+  std::memset(&u, 0, sizeof(u));
+  for (size_t g = 0; g < h->groups.size(); ++g) {
+    u.p[g][REF_W] = t[g].W;
+    u.p[g][REF_G] = const_cast<void*>(t[g].G);
+    u.p[g][REF_M] = t[g].M;
+    u.p[g][REF_SA] = t[g].Sa;
+    u.p[g][REF_SB] = t[g].Sb;
+    u.p[g][REF_PA] = t[g].Pa;
+    u.p[g][REF_PB] = t[g].Pb;
+  }
+  return u;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+void okls_default_config(okls_config* c) {
+  if (c == nullptr) return;
+  std::memset(c, 0, sizeof(*c));
+  c->mode = OKLS_MODE_OKLS;
+  c->ns_steps = 10;
+  c->ns_split_steps = 0;
+  c->factor_split = 0;
+  c->nesterov_var_corr = 1;
+  c->chunk_matrices = 0;
+  c->beta1 = 0.9684f;
+  c->beta2 = 0.9482f;
+  c->eps = 1e-9f;
+  c->weight_decay = 0.0303f;
+  c->lr_peak = 0.09434f;
+  c->ns_floor = 1e-3f;
+  c->ns_damping = 5e-3f;
+}
+
+size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups) {
+  if (check_config(cfg) != OKLS_OK || check_groups(n_groups, groups) != OKLS_OK) return 0;
+  std::vector<okls_group_desc> g(groups, groups + n_groups);
+  Planner P(*cfg, g);
+  const WsLayout w = ws_layout(P);
+  if (!P.validate()) return 0;
+  return w.total;
+}
+
+int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_steps) {
+  if (check_config(cfg) != OKLS_OK || a == nullptr || b == nullptr || max_steps < cfg->ns_steps) return -1;
+  std::vector<double> na, nb;
+  ns_table(cfg->ns_floor, cfg->ns_steps, na, nb, nullptr);
+  for (int k = 0; k < cfg->ns_steps; ++k) {
+    a[k] = na[k];
+    b[k] = nb[k];
+  }
+  return cfg->ns_steps;
+}
+
+okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, const okls_group_desc* groups,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  if (out == nullptr) return OKLS_ERR_INVALID_ARG;
+  *out = nullptr;
+  okls_status st = check_config(cfg);
+  if (st != OKLS_OK) return st;
+  st = check_groups(n_groups, groups);
+  if (st != OKLS_OK) return st;
+  if (workspace == nullptr || !aligned(workspace, kAlign)) return OKLS_ERR_WORKSPACE;
+  if (env_fault("okls_init")) return OKLS_ERR_HIP;
+
+  std::vector<okls_group_desc> g(groups, groups + n_groups);
+  Planner sizing(*cfg, g);
+  const WsLayout w = ws_layout(sizing);
+  if (ws_bytes < w.total) return OKLS_ERR_WORKSPACE;
+
+  // plan again with the real chunk base
+  Planner P(*cfg, g);
+  P.plan(w.chunk);
+  if (!P.validate() || P.probs.size() != sizing.probs.size() || P.chunk_bytes != sizing.chunk_bytes)
+    return OKLS_ERR_UNSUPPORTED;
+  // the regions the tables and slots occupy must end before the chunk buffers
+  if (w.flag + sizeof(int) > w.chunk) return OKLS_ERR_UNSUPPORTED;
+
+  okls_handle* h = new (std::nothrow) okls_handle();
+  if (h == nullptr) return OKLS_ERR_INVALID_ARG;
+  h->cfg = *cfg;
+  h->groups = g;
+  h->ws = static_cast<char*>(workspace);
+  h->ws_bytes = ws_bytes;
+  h->off_probs = w.probs;
+  h->off_tiles = w.tiles;
+  h->off_stat = w.stat;
+  h->off_cast = w.cast;
+  h->off_scal = w.scal;
+  h->off_part = w.part;
+  h->off_flag = w.flag;
+  h->chunks = P.chunks;
+  h->na = P.na;
+  h->nb = P.nb;
+
+  std::vector<float> scal(static_cast<size_t>(P.n_slots), 1.0f);
+  scal[SL_ONE] = 1.0f;
+  scal[SL_Y] = P.sY;
+  scal[SL_Z] = P.sZ;
+  scal[SL_T] = P.sT;
+
+  hipStream_t s = as_stream(stream);
+  hipError_t e = hipSuccess;
+  auto up = [&](size_t off, const void* src, size_t bytes) {
+    if (e == hipSuccess && bytes > 0) e = hipMemcpyAsync(h->ws + off, src, bytes, hipMemcpyHostToDevice, s);
+  };
+  up(w.probs, P.probs.data(), P.probs.size() * sizeof(GemmProb));
+  up(w.tiles, P.tiles.data(), P.tiles.size() * sizeof(TileRef));
+  up(w.stat, P.stat_jobs.data(), P.stat_jobs.size() * sizeof(StatJob));
+  up(w.cast, P.cast_jobs.data(), P.cast_jobs.size() * sizeof(CastJob));
+  up(w.scal, scal.data(), scal.size() * sizeof(float));
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete h;
+    return OKLS_ERR_HIP;
+  }
+  *out = h;
+  return OKLS_OK;
+}
+
+static okls_status check_tensors(const okls_handle* h, const okls_group_tensors* t, bool need_wg) {
+  if (t == nullptr) return OKLS_ERR_INVALID_ARG;
+  for (size_t g = 0; g < h->groups.size(); ++g) {
+    const okls_group_tensors& x = t[g];
+    if (x.M == nullptr || x.Sa == nullptr || x.Sb == nullptr || x.Pa == nullptr || x.Pb == nullptr)
+      return OKLS_ERR_INVALID_ARG;
+    if (!aligned(x.M, 4) || !aligned(x.Sa, 4) || !aligned(x.Sb, 4) || !aligned(x.Pa, 4) || !aligned(x.Pb, 4))
+      return OKLS_ERR_INVALID_ARG;
+    if (need_wg) {
+      if (x.W == nullptr || x.G == nullptr) return OKLS_ERR_INVALID_ARG;
+      if (!aligned(x.W, 4) || !aligned(x.G, h->groups[g].g_dtype == OKLS_BF16 ? 2 : 4)) return OKLS_ERR_INVALID_ARG;
+    }
+  }
+  return OKLS_OK;
+}
+
+okls_status okls_init_state(okls_handle* h, const okls_group_tensors* t, void* stream) {
+  if (h == nullptr) return OKLS_ERR_INVALID_ARG;
+  okls_status st = check_tensors(h, t, false);
+  if (st != OKLS_OK) return st;
+  if (env_fault("okls_init_state")) return OKLS_ERR_HIP;
+  InitArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.user = user_ptrs(h, t);
+  int n = 0;
+  for (size_t g = 0; g < h->groups.size(); ++g) {
+    const okls_group_desc& d = h->groups[g];
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, h->cfg.eps};
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, h->cfg.eps};
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, d.m, 1.0f};
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, d.n, 1.0f};
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_M, d.batch, d.m, d.n, 0.0f};
+  }
+  hipStream_t s = as_stream(stream);
+  if (launch_init_state(a, n, s) != hipSuccess) return OKLS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return OKLS_ERR_HIP;
+  return OKLS_OK;
+}
+
+okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step, float lr, void* stream) {
+  if (h == nullptr) return OKLS_ERR_INVALID_ARG;
+  if (step < 1 || !(lr >= 0.f && std::isfinite(lr))) return OKLS_ERR_INVALID_ARG;
+  okls_status st = check_tensors(h, t, true);
+  if (st != OKLS_OK) return st;
+  if (env_fault("okls_step")) return OKLS_ERR_HIP;
+
+  // host scalars of this step
+  const double b1 = h->cfg.beta1;
+  double s_t = 1.0;
+  if (h->cfg.nesterov_var_corr) {
+    // variance of beta1 M_t + (1-beta1) G_t for independent unit-variance G and M_0 = 0
+    const double w0 = (1.0 - b1) * (1.0 + b1);
+    double v = w0 * w0;
+    const double q = b1 * b1;
+    const double tail = (1.0 - b1) * (1.0 - b1) * q * q;     // weight^2 of G_{t-1}
+    if (step > 1) {
+      // sum_{j=0}^{t-2} q^j = (1 - q^(t-1)) / (1 - q)
+      v += tail * (1.0 - std::pow(q, static_cast<double>(step - 1))) / (1.0 - q);
+    }
+    s_t = 1.0 / std::sqrt(v);
+  }
+  const double decay = 1.0 - static_cast<double>(lr) * h->cfg.weight_decay * (static_cast<double>(lr) / h->cfg.lr_peak);
+
+  const UserPtrs user = user_ptrs(h, t);
+  hipStream_t s = as_stream(stream);
+  char* ws = h->ws;
+  float* scal = reinterpret_cast<float*>(ws + h->off_scal);
+  float* part = reinterpret_cast<float*>(ws + h->off_part);
+
+  for (const std::vector<LaunchRec>& L : h->chunks) {
+    for (const LaunchRec& r : L) {
+      hipError_t e = hipSuccess;
+      if (r.type == L_STAT) {
+        StatArgs a;
+        a.jobs = reinterpret_cast<const StatJob*>(ws + h->off_stat) + r.first;
+        a.n_jobs = r.count;
+        a.blk_offset = 0;
+        a.partials = part;
+        a.beta1 = static_cast<float>(b1);
+        a.s_t = static_cast<float>(s_t);
+        a.ws = ws;
+        a.user = user;
+        e = launch_stats(a, r.nblocks, s);
+      } else if (r.type == L_CAST) {
+        CastArgs a;
+        a.jobs = reinterpret_cast<const CastJob*>(ws + h->off_cast) + r.first;
+        a.n_jobs = r.count;
+        a.blk_offset = 0;
+        a.partials = part;
+        a.scal = scal;
+        a.beta1 = static_cast<float>(b1);
+        a.s_t = static_cast<float>(s_t);
+        a.ka = r.ka;
+        a.kb = r.kb;
+        a.ws = ws;
+        a.user = user;
+        e = launch_cast(a, r.nblocks, s);
+      } else {
+        GemmArgs a;
+        a.probs = reinterpret_cast<const GemmProb*>(ws + h->off_probs);
+        a.tiles = reinterpret_cast<const TileRef*>(ws + h->off_tiles);
+        a.tile_begin = r.first;
+        a.prob_base = r.prob_base;
+        a.split_in = r.split_in;
+        a.write_lo = r.write_lo;
+        a.ka = r.ka;
+        a.kb = r.kb;
+        a.lr = lr;
+        a.decay = static_cast<float>(decay);
+        a.ws = ws;
+        a.scal = scal;
+        a.user = user;
+        e = launch_gemm(a, r.count, s);
+      }
+      if (e != hipSuccess) return OKLS_ERR_HIP;
+    }
+  }
+  return OKLS_OK;
+}
+
+okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* t, void* stream) {
+  if (h == nullptr) return OKLS_ERR_INVALID_ARG;
+  okls_status st = check_tensors(h, t, true);
+  if (st != OKLS_OK) return st;
+  InitArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.user = user_ptrs(h, t);
+  int n = 0;
+  for (size_t g = 0; g < h->groups.size(); ++g) {
+    const okls_group_desc& d = h->groups[g];
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, 0.f};
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, 0.f};
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, d.m, 0.f};
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, d.n, 0.f};
+    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_M, d.batch, d.m, d.n, 0.f};
+  }
+  hipStream_t s = as_stream(stream);
+  int* flag = reinterpret_cast<int*>(h->ws + h->off_flag);
+  if (launch_check_finite(a, n, flag, s) != hipSuccess) return OKLS_ERR_HIP;
+  // W too
+  InitArgs w = a;
+  int nw = 0;
+  for (size_t g = 0; g < h->groups.size(); ++g) {
+    const okls_group_desc& d = h->groups[g];
+    w.jobs[nw++] = InitJob{static_cast<int32_t>(g), REF_W, d.batch, d.m, d.n, 0.f};
+  }
+  int host_flag = 0;
+  if (hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return OKLS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return OKLS_ERR_HIP;
+  if (host_flag) return OKLS_ERR_NONFINITE;
+  if (launch_check_finite(w, nw, flag, s) != hipSuccess) return OKLS_ERR_HIP;
+  if (hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return OKLS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return OKLS_ERR_HIP;
+  return host_flag ? OKLS_ERR_NONFINITE : OKLS_OK;
+}
+
+okls_status okls_destroy(okls_handle* h) {
+  if (h == nullptr) return OKLS_ERR_INVALID_ARG;
+  delete h;
+  return OKLS_OK;
+}
+
+const char* okls_status_string(okls_status s) {
+  switch (s) {
+    case OKLS_OK: return "ok";
+    case OKLS_ERR_INVALID_ARG: return "invalid argument";
+    case OKLS_ERR_SHAPE: return "invalid shape";
+    case OKLS_ERR_DTYPE: return "unsupported dtype";
+    case OKLS_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case OKLS_ERR_HIP: return "HIP runtime error";
+    case OKLS_ERR_NONFINITE: return "non-finite values in the optimizer state";
+    case OKLS_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Host-side launchers of the gfx950 kernels (okls_kernels.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "okls_types.h"
+
+namespace okls {
+
+constexpr int kMaxInitJobs = 5 * kMaxGroups;
+
+// One caller tensor of one group: batch x rows x cols fp32, filled with
+// `diag` on each matrix's diagonal and zero elsewhere (init), or scanned
+// for Inf/NaN (finiteness check).
+struct InitJob {
+  int32_t group;
+  int32_t kind;     // RefKind of the tensor
+  int32_t batch, rows, cols;
+  float diag;
+};
+
+struct InitArgs {
+  InitJob jobs[kMaxInitJobs];
+  UserPtrs user;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, int n_tiles, hipStream_t s);
+hipError_t launch_stats(const StatArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_cast(const CastArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_init_state(const InitArgs& a, int n_jobs, hipStream_t s);
+hipError_t launch_check_finite(const InitArgs& a, int n_jobs, int* flag_dev, hipStream_t s);
+
+}  // namespace okls

@@ -1,0 +1,488 @@
+// gfx950 kernels of the batched OKLS / Shampoo preconditioner step.
+//
+//  gemm_nt_kernel   grouped fp16 MFMA GEMM, C = alpha A B^T, fp32 accumulation,
+//                   128x128 output tiles, LDS double-buffered K loop, optional
+//                   split-fp16 (hi*hi + hi*lo + lo*hi) as a 3-segment K loop,
+//                   fused epilogues (factor EMA with mirrored store, the
+//                   Newton-Schulz step polynomial, the weight update).
+//  stats_kernel     per-block absmax / sum of squares partials.
+//  cast_kernel      fp32/bf16 -> padded fp16 (hi, lo) with a power-of-two
+//                   scale derived from the partials, optional transpose; also
+//                   the Nesterov momentum update and the Newton-Schulz start.
+//  init_state_kernel, finite_kernel.
+//
+// The operation each epilogue performs is documented on okls::Epi; the
+// mathematics follows the "Online KL Shampoo" README, section "How it works".
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "okls_kernels.h"
+
+namespace okls {
+
+typedef _Float16 half_t;
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ char* resolve(const Ref& r, char* ws, const UserPtrs& u) {
+  if (r.kind == REF_WS) return ws + r.off;
+  return static_cast<char*>(u.p[r.group][r.kind]) + r.off;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM
+// ---------------------------------------------------------------------------
+constexpr int kLdsStride = kBK + 8;   // halves per LDS row: 144 B, breaks the 128 B row aliasing
+constexpr int kGemmThreads = 256;
+
+__device__ __forceinline__ void store16(half_t* p, int lo_off, bool write_lo, const float (&x)[4], float s) {
+  half4_t hi, lo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float y = x[e] * s;
+    half_t h = static_cast<half_t>(y);
+    hi[e] = h;
+    lo[e] = static_cast<half_t>(y - static_cast<float>(h));
+  }
+  *reinterpret_cast<half4_t*>(p) = hi;
+  if (write_lo) *reinterpret_cast<half4_t*>(p + lo_off) = lo;
+}
+
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args) {
+  __shared__ half_t sA[2][kTile * kLdsStride];
+  __shared__ half_t sB[2][kTile * kLdsStride];
+
+  const TileRef tr = args.tiles[args.tile_begin + blockIdx.x];
+  const GemmProb& P = args.probs[args.prob_base + tr.prob];
+  const int ti = tr.ij >> 16;
+  const int tj = tr.ij & 0xffff;
+  const int lda = P.lda, ldb = P.ldb, Kp = P.Kp;
+
+  const half_t* A = reinterpret_cast<const half_t*>(resolve(P.A, args.ws, args.user)) +
+                    static_cast<size_t>(ti) * kTile * lda;
+  const half_t* B = reinterpret_cast<const half_t*>(resolve(P.B, args.ws, args.user)) +
+                    static_cast<size_t>(tj) * kTile * ldb;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = tid >> 3;          // 0..31
+  const int lk = (tid & 7) * 8;       // 0..56
+
+  const int kt_per_seg = Kp / kBK;
+  const int niter = (args.split_in ? 3 : 1) * kt_per_seg;
+
+  half8_t ra[4], rb[4];
+  auto gload = [&](int it) {
+    const int seg = it / kt_per_seg;
+    const int k0 = (it - seg * kt_per_seg) * kBK + lk;
+    const int offA = (seg == 2 ? Kp : 0) + k0;
+    const int offB = (seg == 1 ? Kp : 0) + k0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      ra[p] = *reinterpret_cast<const half8_t*>(A + static_cast<size_t>(lrow + 32 * p) * lda + offA);
+      rb[p] = *reinterpret_cast<const half8_t*>(B + static_cast<size_t>(lrow + 32 * p) * ldb + offB);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      *reinterpret_cast<half8_t*>(&sA[buf][(lrow + 32 * p) * kLdsStride + lk]) = ra[p];
+      *reinterpret_cast<half8_t*>(&sB[buf][(lrow + 32 * p) * kLdsStride + lk]) = rb[p];
+    }
+  };
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  int cur = 0;
+  const int frow = lane & 15;
+  const int fk = (lane >> 4) * 8;
+  for (int it = 0; it < niter; ++it) {
+    if (it + 1 < niter) gload(it + 1);
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 32) {
+      half8_t fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const half8_t*>(&sA[cur][(wm * 64 + i * 16 + frow) * kLdsStride + kk + fk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const half8_t*>(&sB[cur][(wn * 64 + j * 16 + frow) * kLdsStride + kk + fk]);
+      // Operands swapped (B rows as the MFMA's A) so that each lane ends with
+      // four consecutive output columns of one output row.
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (it + 1 < niter) sstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // ---------------- epilogue ----------------
+  const float alpha = 1.0f / (args.scal[P.sA] * args.scal[P.sB]);
+  const int epi = P.epi;
+  const int M = P.M, N = P.N;
+  const bool write_lo = args.write_lo != 0;
+  float* out32 = P.out32.kind != REF_NONE ? reinterpret_cast<float*>(resolve(P.out32, args.ws, args.user)) : nullptr;
+  half_t* out16 = P.out16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16, args.ws, args.user)) : nullptr;
+  const float* aux = P.aux.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(P.aux, args.ws, args.user)) : nullptr;
+  const float s_out = P.s_out >= 0 ? args.scal[P.s_out] : 1.0f;
+  const float cval = P.cslot >= 0 ? args.scal[P.cslot] : 1.0f;
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ti * kTile + wm * 64 + i * 16 + frow;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c0 = tj * kTile + wn * 64 + j * 16 + (lane >> 4) * 4;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] * alpha;
+
+      if (epi == EPI_STORE32) {
+        if (r < M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c0 + e < N) out32[static_cast<size_t>(r) * P.ld32 + c0 + e] = v[e];
+        }
+      } else if (epi == EPI_SYRK) {
+        // S <- c0*S + c1*v + c2*I on the upper triangle, mirrored below.
+        if (r < M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = c0 + e;
+            if (c < N && (ti != tj || r <= c)) {
+              const size_t up = static_cast<size_t>(r) * P.ld32 + c;
+              float s = P.c0 * out32[up] + P.c1 * v[e] + (r == c ? P.c2 : 0.0f);
+              out32[up] = s;
+              if (r != c) out32[static_cast<size_t>(c) * P.ld32 + r] = s;
+            }
+          }
+        }
+      } else if (epi == EPI_UPDATE) {
+        if (r < M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = c0 + e;
+            if (c < N) {
+              const size_t o = static_cast<size_t>(r) * P.ld32 + c;
+              out32[o] = args.decay * out32[o] - args.lr * P.c0 * v[e];
+            }
+          }
+        }
+      } else {
+        // fp16 outputs into padded buffers (zeros outside the logical region)
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = c0 + e;
+          const bool in = (r < M) && (c < N);
+          float y = 0.0f;
+          if (in) {
+            if (epi == EPI_NS_T) {
+              y = (r == c ? args.ka : 0.0f) + args.kb * v[e];
+            } else if (epi == EPI_NS_Y1) {
+              y = args.ka * (aux[static_cast<size_t>(r) * P.ldaux + c] * cval + (r == c ? P.c2 : 0.0f)) +
+                  args.kb * v[e];
+            } else {  // EPI_STORE16, EPI_NS_FINAL
+              y = v[e];
+            }
+          }
+          x[e] = y;
+        }
+        if (epi == EPI_NS_FINAL && out32 != nullptr && r < M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c0 + e < N) out32[static_cast<size_t>(r) * P.ld32 + c0 + e] = x[e] * cval;
+        }
+        if (out16 != nullptr) store16(out16 + static_cast<size_t>(r) * P.ld16 + c0, P.lo16, write_lo, x, s_out);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Deterministic block reductions
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ void block_reduce2(float& amax, float& ss, float* sh) {
+  // wave-level butterfly, then one value per wave through LDS; fixed order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    ss += __shfl_xor(ss, o, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh[2 * w] = amax;
+    sh[2 * w + 1] = ss;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = sh[0], s = sh[1];
+    for (int i = 1; i < NT / 64; ++i) {
+      a = fmaxf(a, sh[2 * i]);
+      s += sh[2 * i + 1];
+    }
+    sh[0] = a;
+    sh[1] = s;
+  }
+  __syncthreads();
+  amax = sh[0];
+  ss = sh[1];
+  __syncthreads();
+}
+
+template <typename Job>
+__device__ __forceinline__ int find_job(const Job* jobs, int n, int gb) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (jobs[mid].blk_begin <= gb) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float nesterov_value(float m, float g, float beta1, float s_t) {
+  const float mn = beta1 * m + (1.0f - beta1) * g;
+  return s_t * (beta1 * mn + (1.0f - beta1) * g);
+}
+
+__global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
+  __shared__ float sh[2 * (kStatThreads / 64)];
+  const int gb = blockIdx.x + a.blk_offset;
+  const StatJob& J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
+  const int lb = gb - J.blk_begin;
+  const int r0 = lb * J.rows_per_blk;
+  const int r1 = min(J.rows, r0 + J.rows_per_blk);
+  const char* src = resolve(J.src, a.ws, a.user);
+  const float* m = J.kind == ST_NESTEROV ? reinterpret_cast<const float*>(resolve(J.src2, a.ws, a.user)) : nullptr;
+  float amax = 0.0f, ss = 0.0f;
+  for (int r = r0; r < r1; ++r) {
+    for (int c = threadIdx.x; c < J.cols; c += kStatThreads) {
+      const size_t o = static_cast<size_t>(r) * J.src_ld + c;
+      float x;
+      if (J.kind == ST_F32) {
+        x = reinterpret_cast<const float*>(src)[o];
+      } else if (J.kind == ST_BF16) {
+        x = bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]);
+      } else {
+        const float g = J.g_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o])
+                                 : reinterpret_cast<const float*>(src)[o];
+        x = nesterov_value(m[o], g, a.beta1, a.s_t);
+      }
+      const float ax = fabsf(x);
+      amax = (ax > amax || ax != ax) ? ax : amax;   // NaN propagates
+      ss += x * x;
+    }
+  }
+  block_reduce2<kStatThreads>(amax, ss, sh);
+  if (threadIdx.x == 0) {
+    a.partials[2 * (J.part_begin + lb)] = amax;
+    a.partials[2 * (J.part_begin + lb) + 1] = ss;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Casts
+// ---------------------------------------------------------------------------
+constexpr int kCastThreads = 256;
+
+__device__ __forceinline__ float pow2_scale(float amax) {
+  if (!(amax > 0.0f) || !(amax < 3.0e38f)) return 1.0f;      // zero, NaN or Inf: leave unscaled
+  int e;
+  const float f = frexpf(amax, &e);                          // amax = f * 2^e, f in [0.5, 1)
+  const int ceil_log2 = (f == 0.5f) ? e - 1 : e;
+  return ldexpf(1.0f, kScaleExp - ceil_log2);
+}
+
+__global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
+  __shared__ float sh[2 * (kCastThreads / 64)];
+  __shared__ float tile[kCastTile][kCastTile + 1];
+  const int gb = blockIdx.x + a.blk_offset;
+  const CastJob& J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
+  const int lb = gb - J.blk_begin;
+
+  // ---- scale from the statistics partials (same fixed order in every block)
+  float amax = 0.0f, ss = 0.0f;
+  for (int i = threadIdx.x; i < J.part_count; i += kCastThreads) {
+    const float pa = a.partials[2 * (J.part_begin + i)];
+    amax = (pa > amax || pa != pa) ? pa : amax;
+    ss += a.partials[2 * (J.part_begin + i) + 1];
+  }
+  block_reduce2<kCastThreads>(amax, ss, sh);
+  float scale;
+  float cinv = 1.0f;
+  if (J.scale_mode == SC_ABSMAX) {
+    scale = pow2_scale(amax);
+    if (lb == 0 && threadIdx.x == 0) a.scal[J.scale_slot] = scale;
+  } else {
+    scale = a.scal[J.scale_slot];
+  }
+  float ddiag = 0.0f;
+  if (J.kind == CA_NS_Y0 || J.kind == CA_NS_Z1) {
+    // damped and normalised: (S + delta c I) / c' with c' = c (1 + delta)
+    const float c = sqrtf(ss) * (1.0f + J.damp);
+    cinv = 1.0f / c;
+    ddiag = J.damp / (1.0f + J.damp);
+    if (lb == 0 && threadIdx.x == 0) {
+      if (J.cinv_slot >= 0) a.scal[J.cinv_slot] = cinv;
+      if (J.rho_slot >= 0) a.scal[J.rho_slot] = 1.0f / sqrtf(c);
+      if (J.sqrtc_slot >= 0) a.scal[J.sqrtc_slot] = sqrtf(c);
+      if (J.p16_slot >= 0) a.scal[J.p16_slot] = J.p16_static * sqrtf(c);
+    }
+  }
+
+  // ---- destination tile
+  const int ty = lb / J.tiles_x, tx = lb - ty * J.tiles_x;
+  const int dr0 = ty * kCastTile, dc0 = tx * kCastTile;
+  const char* src = resolve(J.src, a.ws, a.user);
+  half_t* dst = reinterpret_cast<half_t*>(resolve(J.dst, a.ws, a.user));
+  const bool write_lo = J.write_lo != 0;
+
+  auto load_src = [&](int r, int c) -> float {   // source coordinates, in range
+    const size_t o = static_cast<size_t>(r) * J.src_ld + c;
+    switch (J.kind) {
+      case CA_F32: return reinterpret_cast<const float*>(src)[o];
+      case CA_BF16: return bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]);
+      case CA_NESTEROV: {
+        const char* g = resolve(J.src2, a.ws, a.user);
+        const float gv = J.g_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(g)[o])
+                                  : reinterpret_cast<const float*>(g)[o];
+        float* m = const_cast<float*>(reinterpret_cast<const float*>(src));
+        const float mo = m[o];
+        const float mn = a.beta1 * mo + (1.0f - a.beta1) * gv;
+        if (J.write_m) m[o] = mn;
+        return a.s_t * (a.beta1 * mn + (1.0f - a.beta1) * gv);
+      }
+      case CA_NS_Y0: return reinterpret_cast<const float*>(src)[o] * cinv + (r == c ? ddiag : 0.0f);
+      default:
+        return (r == c ? a.ka : 0.0f) +
+               a.kb * (reinterpret_cast<const float*>(src)[o] * cinv + (r == c ? ddiag : 0.0f));
+    }
+  };
+
+  // thread layout: 16 column quads x 16 rows, 4 row passes
+  const int cq = (threadIdx.x & 15) * 4;
+  const int rr = threadIdx.x >> 4;
+  if (!J.transpose) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = dr0 + rr + 16 * p;
+      if (r >= J.dst_rows_p) continue;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = dc0 + cq + e;
+        x[e] = (r < J.rows && c < J.cols) ? load_src(r, c) : 0.0f;
+      }
+      if (dc0 + cq < J.dst_cols_p)
+        store16(dst + static_cast<size_t>(r) * J.dst_ld + dc0 + cq, J.dst_lo, write_lo, x, scale);
+    }
+  } else {
+    // destination (r, c) = source (c, r); stage the source tile through LDS
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int sr = dc0 + rr + 16 * p;            // source row = destination column
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sc = dr0 + cq + e;               // source column = destination row
+        tile[rr + 16 * p][cq + e] = (sr < J.rows && sc < J.cols) ? load_src(sr, sc) : 0.0f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = dr0 + rr + 16 * p;
+      if (r >= J.dst_rows_p) continue;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = tile[cq + e][rr + 16 * p];
+      if (dc0 + cq < J.dst_cols_p)
+        store16(dst + static_cast<size_t>(r) * J.dst_ld + dc0 + cq, J.dst_lo, write_lo, x, scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State initialisation and finiteness scan
+// ---------------------------------------------------------------------------
+__global__ void init_state_kernel(InitArgs a) {
+  const InitJob& J = a.jobs[blockIdx.y];
+  float* p = static_cast<float*>(a.user.p[J.group][J.kind]);
+  const size_t dd = static_cast<size_t>(J.rows) * J.cols;
+  const size_t total = dd * J.batch;
+  for (size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const size_t w = e % dd;
+    const size_t r = w / J.cols, c = w - r * J.cols;
+    p[e] = (r == c) ? J.diag : 0.0f;
+  }
+}
+
+__global__ void finite_kernel(InitArgs a, int* flag) {
+  const InitJob& J = a.jobs[blockIdx.y];
+  const float* p = static_cast<const float*>(a.user.p[J.group][J.kind]);
+  const size_t total = static_cast<size_t>(J.rows) * J.cols * J.batch;
+  int bad = 0;
+  for (size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const float x = p[e];
+    bad |= !(fabsf(x) <= 3.4028235e38f);
+  }
+  if (bad) atomicOr(flag, 1);
+}
+
+__global__ void zero_int_kernel(int* p) { *p = 0; }
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_gemm(const GemmArgs& a, int n_tiles, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_nt_kernel, dim3(n_tiles), dim3(kGemmThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats(const StatArgs& a, int n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(stats_kernel, dim3(n_blocks), dim3(kStatThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const CastArgs& a, int n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_kernel, dim3(n_blocks), dim3(kCastThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_state(const InitArgs& a, int n_jobs, hipStream_t s) {
+  if (n_jobs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(init_state_kernel, dim3(1024, n_jobs), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_finite(const InitArgs& a, int n_jobs, int* flag_dev, hipStream_t s) {
+  if (n_jobs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, s, flag_dev);
+  hipLaunchKernelGGL(finite_kernel, dim3(1024, n_jobs), dim3(256), 0, s, a, flag_dev);
+  return hipGetLastError();
+}
+
+}  // namespace okls

@@ -1,0 +1,165 @@
+// Internal descriptor types shared by the host scheduler and the gfx950
+// kernels.  Not part of the public ABI.
+#pragma once
+#include <stdint.h>
+
+namespace okls {
+
+constexpr int kMaxGroups = 16;
+constexpr int kTile = 128;           // GEMM output tile (rows and cols) and padding unit
+constexpr int kBK = 64;              // GEMM K step
+constexpr int kCastTile = 64;        // elementwise cast tile
+constexpr int kStatThreads = 256;
+constexpr int kScaleExp = 14;        // dynamic casts put max |x| in (2^13, 2^14]
+
+// Where a buffer lives: the workspace (byte offset from its base) or a
+// caller tensor of one group (byte offset from that tensor's base).
+enum RefKind : int32_t {
+  REF_NONE = -1, REF_WS = 0, REF_W = 1, REF_G = 2, REF_M = 3,
+  REF_SA = 4, REF_SB = 5, REF_PA = 6, REF_PB = 7
+};
+struct Ref {
+  int32_t kind;
+  int32_t group;
+  int64_t off;
+};
+
+// One GEMM workgroup: problem index (relative to the launch's prob_base)
+// and output tile coordinates packed as (ti << 16) | tj.
+struct TileRef {
+  int32_t prob;
+  int32_t ij;
+};
+
+// Caller pointers of one okls_step, passed by value to every launch.
+struct UserPtrs {
+  void* p[kMaxGroups][8];
+};
+
+// ---------------------------------------------------------------------------
+// GEMM: C (M x N) = alpha * A (M x K) * B (N x K)^T, fp16 operands stored
+// row-major with zero padding to multiples of kTile; fp32 accumulation;
+// epilogue selected per problem.
+// ---------------------------------------------------------------------------
+enum Epi : int32_t {
+  EPI_STORE32 = 0,   // out32 = v                                  (logical region)
+  EPI_SYRK = 1,      // S = c0*S + c1*v + c2*I, mirrored, upper tiles only
+  EPI_NS_T = 2,      // T = ka*I + kb*v -> out16 (static scale)
+  EPI_NS_Y1 = 3,     // Y1 = ka*(aux*scal[cslot] + c2*I) + kb*v -> out16
+  EPI_STORE16 = 4,   // out16 = v * scal[s_out]
+  EPI_NS_FINAL = 5,  // out32 = v * scal[cslot] (fp32 root), out16 = v * scal[s_out]
+  EPI_UPDATE = 6     // W = decay*W - lr*c0*v
+};
+
+struct GemmProb {
+  Ref A, B;
+  int32_t lda, ldb;        // row strides in halves
+  int32_t M, N;            // logical output dims
+  int32_t Kp;              // padded K (multiple of kTile): length of the hi part of a row
+  int32_t epi;
+  Ref out32; int32_t ld32;
+  Ref out16; int32_t ld16; int32_t lo16;   // lo part at +lo16 halves within a row
+  Ref aux; int32_t ldaux;
+  int32_t sA, sB;          // scale slots of the operands (alpha = 1/(scal[sA]*scal[sB]))
+  int32_t s_out;           // scale slot for fp16 output
+  int32_t cslot;           // per-problem device scalar used by the epilogue
+  float c0, c1, c2;        // per-problem constants
+  int32_t Mp, Np;          // padded output dims
+};
+
+struct GemmArgs {
+  const GemmProb* probs;   // device
+  const TileRef* tiles;    // device
+  int32_t tile_begin;
+  int32_t prob_base;
+  int32_t split_in;        // 3-segment K loop over [hi | lo] rows
+  int32_t write_lo;        // fp16 outputs also write their lo part
+  float ka, kb;            // Newton-Schulz step coefficients
+  float lr, decay;         // update epilogue
+  char* ws;
+  float* scal;             // device scalar slots
+  UserPtrs user;
+};
+
+// ---------------------------------------------------------------------------
+// Statistics (absmax, sum of squares) per job, as per-block partials.
+// ---------------------------------------------------------------------------
+enum StatKind : int32_t {
+  ST_F32 = 0,        // plain fp32 source
+  ST_BF16 = 1,       // bf16 source
+  ST_NESTEROV = 2    // N = s*(beta1*(beta1*M + (1-beta1)*G) + (1-beta1)*G)
+};
+
+struct StatJob {
+  int32_t kind;
+  Ref src; int32_t src_ld;
+  Ref src2;                // M for ST_NESTEROV
+  int32_t g_bf16;          // ST_NESTEROV: gradient dtype
+  int32_t rows, cols;
+  int32_t rows_per_blk;
+  int32_t part_begin;      // partial index of the job's first block
+  int32_t blk_begin;       // first block of the job in its launch
+};
+
+struct StatArgs {
+  const StatJob* jobs;
+  int32_t n_jobs;
+  int32_t blk_offset;      // block numbering offset (jobs' blk_begin is global)
+  float* partials;         // float2 per block: (absmax, sumsq)
+  float beta1, s_t;
+  char* ws;
+  UserPtrs user;
+};
+
+// ---------------------------------------------------------------------------
+// Casts to padded fp16 (hi, optional lo), optional transpose, with a scale
+// derived from statistics partials.
+// ---------------------------------------------------------------------------
+enum CastKind : int32_t {
+  CA_F32 = 0,        // x from fp32 source
+  CA_BF16 = 1,       // x from bf16 source
+  CA_NESTEROV = 2,   // x = N from (G, M); the non-transposed job also writes M'
+  CA_NS_Y0 = 3,      // x = S / c, c = sqrt(sumsq); static output scale
+  CA_NS_Z1 = 4       // x = ka*I + kb*S/c; static output scale
+};
+enum ScaleMode : int32_t {
+  SC_ABSMAX = 0,     // scale = 2^(kScaleExp - ceil(log2(absmax)))
+  SC_STATIC = 1      // scale = scal[scale_slot] (already set)
+};
+
+struct CastJob {
+  int32_t kind;
+  Ref src; int32_t src_ld;
+  Ref src2;                // G for CA_NESTEROV (src is M)
+  int32_t g_bf16;
+  int32_t write_m;         // CA_NESTEROV: write M' (non-transposed job only)
+  int32_t transpose;
+  int32_t rows, cols;      // logical source dims
+  int32_t dst_rows_p, dst_cols_p;   // padded destination dims (after transpose)
+  Ref dst; int32_t dst_ld; int32_t dst_lo;  // lo at +dst_lo halves within a row
+  int32_t part_begin, part_count;
+  int32_t scale_mode;
+  int32_t scale_slot;      // SC_ABSMAX: written; SC_STATIC: read
+  int32_t cinv_slot;       // CA_NS_*: writes 1/c here (if >= 0)
+  int32_t rho_slot;        // CA_NS_*: writes 1/sqrt(c) here (if >= 0)
+  int32_t sqrtc_slot;      // CA_NS_*: writes sqrt(c) here (if >= 0)
+  int32_t p16_slot;        // CA_NS_*: writes s_Z*sqrt(c) here (if >= 0): scale of the root's fp16 copy
+  float p16_static;        // s_Z
+  float damp;              // CA_NS_*: delta; the chain roots (S + delta c I) / (c (1 + delta))
+  int32_t tiles_x;         // tiles along destination columns
+  int32_t blk_begin;
+  int32_t write_lo;
+};
+
+struct CastArgs {
+  const CastJob* jobs;
+  int32_t n_jobs;
+  int32_t blk_offset;
+  const float* partials;
+  float* scal;
+  float beta1, s_t, ka, kb;
+  char* ws;
+  UserPtrs user;
+};
+
+}  // namespace okls

@@ -1,0 +1,269 @@
+"""Thin Python binding of libokls.so (the C ABI declared in include/okls.h).
+
+Argument marshalling only: every step of the optimizer runs in the HIP
+library.  PyTorch supplies device memory and the current stream.  The
+functions keep the C names; `OKLS` is a convenience wrapper that owns the
+state tensors and the workspace of a list of matrix parameters.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libokls.so")
+
+OKLS_OK = 0
+STATUS = {0: "OKLS_OK", -1: "OKLS_ERR_INVALID_ARG", -2: "OKLS_ERR_SHAPE", -3: "OKLS_ERR_DTYPE",
+          -4: "OKLS_ERR_WORKSPACE", -5: "OKLS_ERR_HIP", -6: "OKLS_ERR_NONFINITE", -7: "OKLS_ERR_UNSUPPORTED"}
+OKLS_F32, OKLS_BF16 = 0, 1
+MODE = {"okls": 0, "shampoo": 1}
+EXPORTED = ("okls_default_config", "okls_workspace_size", "okls_init", "okls_init_state", "okls_step",
+            "okls_check_finite", "okls_ns_coefficients", "okls_destroy", "okls_status_string")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("ns_steps", ctypes.c_int32), ("ns_split_steps", ctypes.c_int32),
+                ("factor_split", ctypes.c_int32), ("nesterov_var_corr", ctypes.c_int32),
+                ("chunk_matrices", ctypes.c_int32), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("lr_peak", ctypes.c_float),
+                ("ns_floor", ctypes.c_float), ("ns_damping", ctypes.c_float)]
+
+
+class GroupDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("m", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("g_dtype", ctypes.c_int32)]
+
+
+class GroupTensors(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("M", ctypes.c_void_p), ("Sa", ctypes.c_void_p),
+                ("Sb", ctypes.c_void_p), ("Pa", ctypes.c_void_p), ("Pb", ctypes.c_void_p)]
+
+
+class OKLSError(RuntimeError):
+    def __init__(self, call, status):
+        self.status = status
+        super().__init__(f"{call} failed: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Loads libokls.so; raises if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.okls_default_config.argtypes = [ctypes.POINTER(Config)]
+    lib.okls_default_config.restype = None
+    lib.okls_workspace_size.argtypes = [ctypes.POINTER(Config), ctypes.c_int, ctypes.POINTER(GroupDesc)]
+    lib.okls_workspace_size.restype = sz
+    lib.okls_init.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(Config), ctypes.c_int,
+                              ctypes.POINTER(GroupDesc), vp, sz, vp]
+    lib.okls_init.restype = ctypes.c_int
+    lib.okls_init_state.argtypes = [vp, ctypes.POINTER(GroupTensors), vp]
+    lib.okls_init_state.restype = ctypes.c_int
+    lib.okls_step.argtypes = [vp, ctypes.POINTER(GroupTensors), i64, f32, vp]
+    lib.okls_step.restype = ctypes.c_int
+    lib.okls_check_finite.argtypes = [vp, ctypes.POINTER(GroupTensors), vp]
+    lib.okls_check_finite.restype = ctypes.c_int
+    lib.okls_ns_coefficients.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    lib.okls_ns_coefficients.restype = ctypes.c_int
+    lib.okls_destroy.argtypes = [vp]
+    lib.okls_destroy.restype = ctypes.c_int
+    lib.okls_status_string.argtypes = [ctypes.c_int]
+    lib.okls_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(call, st):
+    if st != OKLS_OK:
+        raise OKLSError(call, st)
+
+
+# --------------------------------------------------------------------------
+# One-to-one wrappers of the C entry points
+# --------------------------------------------------------------------------
+def default_config(**overrides) -> Config:
+    c = Config()
+    load().okls_default_config(ctypes.byref(c))
+    for k, v in overrides.items():
+        if k == "mode" and isinstance(v, str):
+            v = MODE[v]
+        setattr(c, k, v)
+    return c
+
+
+def precision_config(precision: str = "fp16", **overrides) -> Config:
+    """'fp16': every GEMM with plain fp16 inputs (the pages' path).
+    'fp32': every GEMM split-fp16 (hi*hi + hi*lo + lo*hi), fp32-accurate."""
+    if precision == "fp16":
+        base = dict(ns_split_steps=0, factor_split=0, ns_damping=5e-3)
+    elif precision == "fp32":
+        base = dict(ns_split_steps=-1, factor_split=1, ns_damping=4e-4)
+    else:
+        raise ValueError(precision)
+    base.update(overrides)
+    c = default_config(**{k: v for k, v in base.items() if k != "ns_split_steps"})
+    c.ns_split_steps = c.ns_steps if base["ns_split_steps"] == -1 else base["ns_split_steps"]
+    return c
+
+
+def _groups_array(groups):
+    arr = (GroupDesc * len(groups))()
+    for i, (batch, m, n, gdt) in enumerate(groups):
+        arr[i] = GroupDesc(batch, m, n, gdt)
+    return arr
+
+
+def workspace_size(cfg: Config, groups) -> int:
+    """groups: list of (batch, m, n, g_dtype)."""
+    return int(load().okls_workspace_size(ctypes.byref(cfg), len(groups), _groups_array(groups)))
+
+
+def ns_coefficients(cfg: Config):
+    a = (ctypes.c_double * 32)()
+    b = (ctypes.c_double * 32)()
+    k = load().okls_ns_coefficients(ctypes.byref(cfg), a, b, 32)
+    if k < 0:
+        raise OKLSError("okls_ns_coefficients", -1)
+    return list(a[:k]), list(b[:k])
+
+
+def status_string(st: int) -> str:
+    return load().okls_status_string(st).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def tensors_array(per_group):
+    """per_group: list of dicts with torch tensors W, G, M, Sa, Sb, Pa, Pb."""
+    arr = (GroupTensors * len(per_group))()
+    for i, d in enumerate(per_group):
+        arr[i] = GroupTensors(*[(d[k].data_ptr() if d.get(k) is not None else None)
+                                for k in ("W", "G", "M", "Sa", "Sb", "Pa", "Pb")])
+    return arr
+
+
+def init(cfg: Config, groups, workspace, stream) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    st = load().okls_init(ctypes.byref(h), ctypes.byref(cfg), len(groups), _groups_array(groups),
+                          ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                          ctypes.c_void_p(stream))
+    _check("okls_init", st)
+    return h
+
+
+def init_state(h, tensors, stream):
+    _check("okls_init_state", load().okls_init_state(h, tensors, ctypes.c_void_p(stream)))
+
+
+def step(h, tensors, t: int, lr: float, stream):
+    _check("okls_step", load().okls_step(h, tensors, int(t), float(lr), ctypes.c_void_p(stream)))
+
+
+def check_finite(h, tensors, stream) -> bool:
+    st = load().okls_check_finite(h, tensors, ctypes.c_void_p(stream))
+    if st == -6:
+        return False
+    _check("okls_check_finite", st)
+    return True
+
+
+def destroy(h):
+    _check("okls_destroy", load().okls_destroy(h))
+
+
+# --------------------------------------------------------------------------
+# Convenience optimizer over torch tensors
+# --------------------------------------------------------------------------
+class OKLS:
+    """Online KL Shampoo over a list of matrix parameters (2-D (m, n) or 3-D
+    (N, m, n); each parameter is one group of the C ABI).  Mirrors the README's
+    optimizer interface: OKLS(params, lr, beta1, beta2, eps, weight_decay),
+    .step(), .zero_grad(), .state_dict().  Gradients are read from p.grad
+    (fp32 or bf16) unless `grads` is passed to step()."""
+
+    def __init__(self, params, lr=0.09434, beta1=0.9684, beta2=0.9482, eps=1e-9, weight_decay=0.0303,
+                 mode="okls", precision="fp16", grad_dtype=None, chunk_matrices=0, **cfg_overrides):
+        import torch
+        self.torch = torch
+        self.params = list(params)
+        if not self.params:
+            raise ValueError("no parameters")
+        self.lr = float(lr)
+        self.cfg = precision_config(precision, mode=MODE[mode], beta1=beta1, beta2=beta2, eps=eps,
+                                    weight_decay=weight_decay, lr_peak=float(lr), chunk_matrices=chunk_matrices,
+                                    **cfg_overrides)
+        dev = self.params[0].device
+        self.groups, self.state = [], []
+        for p in self.params:
+            if p.dtype != torch.float32 or not p.is_contiguous():
+                raise ValueError("parameters must be contiguous fp32 tensors")
+            shp = tuple(p.shape) if p.dim() == 3 else (1,) + tuple(p.shape)
+            if len(shp) != 3:
+                raise ValueError("parameters must be 2-D or 3-D")
+            b, m, n = shp
+            gdt = OKLS_BF16 if (grad_dtype or torch.float32) == torch.bfloat16 else OKLS_F32
+            self.groups.append((b, m, n, gdt))
+            self.state.append(dict(M=torch.zeros(b, m, n, device=dev), Sa=torch.empty(b, m, m, device=dev),
+                                   Sb=torch.empty(b, n, n, device=dev), Pa=torch.empty(b, m, m, device=dev),
+                                   Pb=torch.empty(b, n, n, device=dev)))
+        ws_bytes = workspace_size(self.cfg, self.groups)
+        if ws_bytes == 0:
+            raise OKLSError("okls_workspace_size", -1)
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev).cuda_stream
+        self.handle = init(self.cfg, self.groups, self.workspace, self.stream)
+        self.t = 0
+        init_state(self.handle, self._tensors(grads=None), self.stream)
+
+    def _tensors(self, grads):
+        per = []
+        for i, p in enumerate(self.params):
+            g = grads[i] if grads is not None else p.grad
+            d = dict(self.state[i])
+            d["W"] = p
+            d["G"] = g.contiguous() if g is not None else None
+            per.append(d)
+        self._keep = per
+        return tensors_array(per)
+
+    def step(self, grads=None, lr=None):
+        if lr is not None:
+            self.lr = float(lr)
+        self.t += 1
+        self.stream = self.torch.cuda.current_stream(self.params[0].device).cuda_stream
+        step(self.handle, self._tensors(grads), self.t, self.lr, self.stream)
+
+    def zero_grad(self):
+        for p in self.params:
+            p.grad = None
+
+    def check_finite(self) -> bool:
+        return check_finite(self.handle, self._tensors(grads=[p for p in self.params]), self.stream)
+
+    def state_dict(self):
+        return {"t": self.t, "lr": self.lr, "lr_peak": self.cfg.lr_peak,
+                "state": [{k: v.clone() for k, v in s.items()} for s in self.state]}
+
+    def load_state_dict(self, sd):
+        self.t = int(sd["t"])
+        self.lr = float(sd["lr"])
+        for dst, src in zip(self.state, sd["state"]):
+            for k, v in src.items():
+                dst[k].copy_(v)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.okls_destroy(h)
+            self.handle = None

@@ -32,7 +32,9 @@ Parity status of each function (what pins it in the CPU test-suite):
   ns_coefficients .............. classical Newton-Schulz limit (3/2, -1/2),
                                  equioscillation, grid-search optimality
   ns_inv_sqrt / ns_inv_quarter . diagonal S reduces to scalar recurrences,
-                                 eigen closed form, worked example through NS
+                                 eigen closed form, worked example through NS,
+                                 damped isotropic closed form, damped root within
+                                 the coefficient bound of eigh's (S + delta c I)^{-1/2}
   whiten / update_weights ...... G=0 step gives W' = (1 - lr wd) W exactly
   okls_step / shampoo_step ..... orthogonal equivariance, transpose identity,
                                  3-D batch = per-matrix results
@@ -60,6 +62,7 @@ class Hyper:
     nesterov_var_corr: bool = True      # R5
     ns_steps: int = 10                  # [OKLS] intro: 10-step inverse-root method
     ns_floor: float = 1e-3              # R4: lower end of the design interval for sqrt(lambda / ||S||_F)
+    ns_damping: float = 5e-3            # R13: nu; the iteration roots S + (nu/sqrt(d)) ||S||_F I
 
     def peak(self) -> float:
         return self.lr if self.lr_peak is None else self.lr_peak
@@ -195,12 +198,23 @@ def ns_coefficients(floor: float = 1e-3, steps: int = 10):
 # This is the iteration itself (the GPU's algorithm in exact-ish arithmetic);
 # the exact eigh root above is the method's target.
 # ---------------------------------------------------------------------------
-def ns_inv_sqrt(S: np.ndarray, coeffs):
-    """Returns (S^{-1/2} estimate, S^{1/2} estimate) after len(coeffs) steps."""
+#
+# R13 (damping): the pages fix eps = 1e-9 absolutely, far below what fp16
+# inputs resolve; rounding then leaves eigenvalues of the normalised factor
+# slightly negative and the cubic step amplifies them without bound.  The
+# iteration is therefore run on the shifted matrix S + delta c I with
+# delta = nu / sqrt(d) (the size of the rounding perturbation of a
+# Frobenius-normalised d x d matrix scales as 1/sqrt(d)), normalised by
+# c' = c (1 + delta) so its spectrum stays in (0, 1].  nu = 0 is the plain
+# iteration.
+def ns_inv_sqrt(S: np.ndarray, coeffs, nu: float = 0.0):
+    """Returns (P, R): estimates of (S + delta c I)^{-1/2} and (S + delta c I)^{1/2}
+    after len(coeffs) steps, delta = nu / sqrt(d)."""
     d = S.shape[0]
     eye = np.eye(d)
-    c = float(np.linalg.norm(S))
-    Y = S / c
+    delta = nu / math.sqrt(d)
+    c = float(np.linalg.norm(S)) * (1.0 + delta)
+    Y = (S + (delta * c / (1.0 + delta)) * eye) / c
     Z = eye.copy()
     for a, b in coeffs:
         T = a * eye + b * (Z @ Y)
@@ -208,11 +222,11 @@ def ns_inv_sqrt(S: np.ndarray, coeffs):
     return Z / math.sqrt(c), Y * math.sqrt(c)
 
 
-def ns_inv_quarter(S: np.ndarray, coeffs):
+def ns_inv_quarter(S: np.ndarray, coeffs, nu: float = 0.0):
     """S^{-1/4} as two chained inverse-square-root iterations (R8):
     R = S^{1/2} from the first chain's Y output, then P = R^{-1/2}."""
-    _, R = ns_inv_sqrt(S, coeffs)
-    P, _ = ns_inv_sqrt(_sym(R), coeffs)
+    _, R = ns_inv_sqrt(S, coeffs, nu)
+    P, _ = ns_inv_sqrt(_sym(R), coeffs, nu)
     return P
 
 
@@ -290,8 +304,8 @@ def okls_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "exact
     Pa_ex, ka = inv_root_exact(Sa, 2)
     Pb_ex, kb = inv_root_exact(Sb, 2)
     coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
-    Pa_ns, _ = ns_inv_sqrt(Sa, coeffs)
-    Pb_ns, _ = ns_inv_sqrt(Sb, coeffs)
+    Pa_ns, _ = ns_inv_sqrt(Sa, coeffs, hp.ns_damping)
+    Pb_ns, _ = ns_inv_sqrt(Sb, coeffs, hp.ns_damping)
     Pa, Pb = (Pa_ex, Pb_ex) if root == "exact" else (_sym(Pa_ns), _sym(Pb_ns))
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
     U = whiten(Pa, N, Pb)
@@ -308,8 +322,8 @@ def shampoo_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ex
     Pa_ex, ka = inv_root_exact(Sa, 4)
     Pb_ex, kb = inv_root_exact(Sb, 4)
     coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
-    Pa_ns = _sym(ns_inv_quarter(Sa, coeffs))
-    Pb_ns = _sym(ns_inv_quarter(Sb, coeffs))
+    Pa_ns = _sym(ns_inv_quarter(Sa, coeffs, hp.ns_damping))
+    Pb_ns = _sym(ns_inv_quarter(Sb, coeffs, hp.ns_damping))
     Pa, Pb = (Pa_ex, Pb_ex) if root == "exact" else (Pa_ns, Pb_ns)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
     U = whiten(Pa, N, Pb)

@@ -1,0 +1,79 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare each step against the fp64 oracle started from the GPU's own
+previous state (teacher forcing)."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+from oracle import okls_oracle as O
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def make(groups, precision="fp16", mode="okls", grad_dtype="f32", **cfg):
+    """groups: list of (m, n, batch).  Returns (opt, params)."""
+    torch = _torch()
+    from kronecker_factored_second_amd import okls
+    dev = torch.device("cuda:0")
+    params = [torch.zeros(b, m, n, device=dev) for (m, n, b) in groups]
+    gdt = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
+    opt = okls.OKLS(params, mode=mode, precision=precision, grad_dtype=gdt, **cfg)
+    return opt, params
+
+
+def hyper_of(opt, lr=None):
+    c = opt.cfg
+    return O.Hyper(lr=opt.lr if lr is None else lr, beta1=c.beta1, beta2=c.beta2, eps=c.eps,
+                   weight_decay=c.weight_decay, lr_peak=c.lr_peak, nesterov_var_corr=bool(c.nesterov_var_corr),
+                   ns_steps=c.ns_steps, ns_floor=float(np.float32(c.ns_floor)), ns_damping=float(np.float32(c.ns_damping)))
+
+
+def snapshot(opt, gi, idx):
+    """fp64 host copy of matrix idx of group gi."""
+    s = opt.state[gi]
+    f = lambda t: t[idx].detach().double().cpu().numpy()
+    return O.MatState(W=f(opt.params[gi]), M=f(s["M"]), Sa=f(s["Sa"]), Sb=f(s["Sb"]), Pa=f(s["Pa"]), Pb=f(s["Pb"]))
+
+
+def to_device_grad(G: np.ndarray, dtype: str):
+    torch = _torch()
+    g = torch.tensor(G, device="cuda:0")
+    return g.to(torch.bfloat16) if dtype == "bf16" else g
+
+
+class Report:
+    def __init__(self, name):
+        self.name = name
+        self.rows = []
+
+    def add(self, **kw):
+        self.rows.append(kw)
+        msg = " ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}" for k, v in kw.items())
+        print(f"[{self.name}] {msg}", flush=True)
+        sys.stdout.flush()
+
+
+def compare_step(opt, before, after_idx, G, hp, t, mode, gi, idx):
+    """Errors of the GPU result for matrix (gi, idx) against the oracle step
+    from `before` (the GPU's state before this step)."""
+    ref = O.step(before, G.astype(np.float64), hp, t, mode, root="ns")
+    ex = O.step(before, G.astype(np.float64), hp, t, mode, root="exact")
+    after = snapshot(opt, gi, idx)
+    m, n = G.shape
+    decay = 1.0 - hp.lr * hp.weight_decay * (hp.lr / hp.peak())
+    cs = O.c_shape(m, n)
+    U_gpu = (decay * before.W - after.W) / (hp.lr * cs)
+    return dict(
+        S_a=O.rel_frob(after.Sa, ref.state.Sa), S_b=O.rel_frob(after.Sb, ref.state.Sb),
+        P_a=O.rel_frob(after.Pa, ref.Pa_ns), P_b=O.rel_frob(after.Pb, ref.Pb_ns),
+        P_a_exact=O.rel_frob(after.Pa, ex.state.Pa), P_b_exact=O.rel_frob(after.Pb, ex.state.Pb),
+        M=O.rel_frob(after.M, ref.state.M), U=O.rel_frob(U_gpu, ref.U), U_exact=O.rel_frob(U_gpu, ex.U),
+        W=O.rel_frob(after.W, ref.state.W), kappa_a=ex.kappa_a, kappa_b=ex.kappa_b,
+        finite=bool(np.isfinite(after.Pa).all() and np.isfinite(after.Pb).all() and np.isfinite(after.W).all()),
+    )

@@ -243,6 +243,29 @@ def test_ns_matrix_iteration_matches_eigen_closed_form_and_exact_root():
         assert O.rel_frob(P, Pex) < 2 * efin
 
 
+def test_ns_damped_matches_shifted_exact_root():
+    """With damping nu the iteration converges to (S + (nu/sqrt d)||S||_F I)^{-1/2}
+    (eigh of the explicitly shifted matrix), within the coefficient bound."""
+    rng = np.random.default_rng(17)
+    coeffs, efin = O.ns_coefficients(1e-3, 10)
+    for d, nu in [(32, 5e-3), (96, 4e-4)]:
+        S = _spd(rng, d, 1e9) * 3.0           # far beyond the undamped design range
+        shift = nu / math.sqrt(d) * np.linalg.norm(S)
+        Pd, _ = O.inv_root_exact(S + shift * np.eye(d), 2)
+        P, R = O.ns_inv_sqrt(S, coeffs, nu)
+        assert O.rel_frob(P, Pd) < 2 * efin
+        Rd = np.real(scipy.linalg.sqrtm(S + shift * np.eye(d)))
+        assert O.rel_frob(R, Rd) < 2 * efin
+
+
+def test_ns_damped_isotropic():
+    """S = s I: ||S||_F = s sqrt(d), so the shifted matrix is s (1 + nu) I."""
+    coeffs, efin = O.ns_coefficients(1e-3, 10)
+    for s, nu, d in [(1e-6, 5e-3, 16), (7.0, 0.2, 9)]:
+        P, _ = O.ns_inv_sqrt(s * np.eye(d), coeffs, nu)
+        np.testing.assert_allclose(P, np.eye(d) / math.sqrt(s * (1 + nu)), rtol=2 * efin)
+
+
 def test_ns_isotropic():
     coeffs, efin = O.ns_coefficients(1e-3, 10)
     for s in (1e-6, 1.0, 5e3):
