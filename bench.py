@@ -1,0 +1,164 @@
+"""Benchmark of the batched OKLS preconditioner step on one MI355X.
+
+One step = one okls_step over every matrix of the workload (factor updates,
+10-step Newton-Schulz roots, whitening, momentum and the weight update).
+Default workload: one d=1024 transformer block (q, k, v, o 1024x1024;
+gate/up 2816x1024; down 1024x2816) with bf16 gradients 0.02*N(0,1) scaled
+per row by log-uniform[0.1, 10], OKLS defaults, fp16 GEMM inputs with fp32
+accumulation.  Gradients are generated once and kept resident in HBM; the
+timed steps cycle through them.
+
+Prints one JSON line: matrices/s, step latency, the dominant kernel's
+roofline (gemm_nt_kernel, algorithmic FLOPs over its summed launch times,
+measured with HIP events on the launch stream during the timed steps) and
+the CPU oracle's time on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "preconditioned matrices/sec + step latency (ms); % fp16 MFMA peak on NS chain"
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c2")
+    p.add_argument("--precision", default="fp16", choices=["fp16", "fp32"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    return p.parse_args()
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample: one matrix of each
+    distinct shape class of the workload, a full oracle step each (exact eigh
+    roots plus the fp64 Newton-Schulz iteration), scaled to the whole
+    workload's matrix counts."""
+    from oracle import okls_oracle as O
+    from kronecker_factored_second_amd import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    hp = O.Hyper()
+    total_s, sampled, step_s = 0.0, [], 0.0
+    for gi, (m, n, b) in enumerate(w.groups):
+        G = WL.gradient(w, gi, 0, 1).astype(np.float64)
+        st = O.init_state(np.zeros((m, n)), hp.eps)
+        t0 = time.perf_counter()
+        O.okls_step(st, G, hp, 1)
+        dt = time.perf_counter() - t0
+        total_s += dt
+        sampled.append(f"{m}x{n}:{dt:.2f}s")
+        step_s += dt * b
+        if total_s > budget_s:
+            step_s = None
+            break
+    if step_s is None:
+        return None
+    return {"value": w.n_matrices / step_s, "unit": "matrices/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full fp64 oracle step per shape class ({', '.join(sampled)}), "
+                      f"scaled by the class counts to the {w.n_matrices}-matrix workload: {step_s:.1f} s/step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the preconditioner step runs on a single MI355X in this build; "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from kronecker_factored_second_amd import okls, workloads as WL
+
+    w = WL.workload(args.workload)
+    dev = torch.device("cuda:0")
+    bf16 = w.grad_dtype == "bf16"
+    params = [torch.zeros(b, m, n, device=dev) for (m, n, b) in w.groups]
+    for gi, (m, n, b) in enumerate(w.groups):
+        for i in range(b):
+            params[gi][i].copy_(torch.from_numpy(WL.initial_weights(w, gi, i)))
+    n_bufs = 3
+    grads = []
+    for t in range(1, n_bufs + 1):
+        gs = []
+        for gi, (m, n, b) in enumerate(w.groups):
+            g = torch.from_numpy(np.stack([WL.gradient(w, gi, i, t) for i in range(b)])).to(dev)
+            gs.append(g.to(torch.bfloat16) if bf16 else g)
+        grads.append(gs)
+    opt = okls.OKLS(params, mode=w.mode, precision=args.precision,
+                    grad_dtype=torch.bfloat16 if bf16 else torch.float32)
+    for i in range(args.warmup):
+        opt.step(grads=grads[i % n_bufs])
+    torch.cuda.synchronize()
+
+    okls.profile_enable(opt.handle, True)
+    okls.profile_read(opt.handle)       # clear
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        opt.step(grads=grads[i % n_bufs])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = okls.profile_read(opt.handle)
+    okls.profile_enable(opt.handle, False)
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    finite = opt.check_finite()
+
+    g_ms = sum(prof[k]["ms"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
+    g_fl = sum(prof[k]["flops"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
+    g_n = sum(prof[k]["launches"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
+    achieved = g_fl / (g_ms * 1e-3) / 1e12
+    ns = prof["ns_gemm"]
+    ns_tflops = ns["flops"] / (ns["ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": w.n_matrices / (ms_step * 1e-3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16" if args.precision == "fp16" else "fp16x3-split",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: " + ", ".join(f"{b}x {m}x{n}" for m, n, b in w.groups) +
+                   f" ({w.n_matrices} matrices, {w.n_params / 1e6:.1f}M params), {w.mode}, "
+                   f"{w.grad_dtype} gradients, precision {args.precision}",
+                   "matrices": w.n_matrices, "parallelism": "single GPU"},
+        "step_latency_ms": ms_step,
+        "ns_chain": {"tflops": ns_tflops, "frac_fp16_peak": ns_tflops / PEAK_FP16_TFLOPS,
+                     "ms_per_step": ns["ms"] / max(prof["steps"], 1), "launches_per_step": ns["launches"] / max(prof["steps"], 1)},
+        "roofline": {"kernel": "gemm_nt_kernel", "bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None,
+                     "avg_launch_us": g_ms * 1e3 / max(g_n, 1), "launches_per_step": g_n / max(prof["steps"], 1),
+                     "algorithmic_flops_per_step": g_fl / max(prof["steps"], 1)},
+        "profile_ms_per_step": {k: prof[k]["ms"] / max(prof["steps"], 1) for k in okls.PROFILE_CATEGORIES},
+        "state_finite": finite,
+        "host_wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -88,7 +88,7 @@ typedef struct {
                                   optimised on, for sqrt(lambda / ||S||_F); default 1e-3 */
     float ns_damping;          /* nu: the root is taken of S + (nu / sqrt(d)) ||S||_F I, which
                                   keeps the rounded iteration positive definite; default
-                                  5e-3 for the fp16 path, 4e-4 suits the split-fp16 path */
+                                  5e-3 for the fp16 path, 2e-3 suits the split-fp16 path */
 } okls_config;
 
 typedef struct {
@@ -145,6 +145,29 @@ okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* tensors,
  * k < ns_steps (T_k = a_k I + b_k Z_k Y_k), written to caller host arrays of
  * length >= max_steps.  Returns the number of steps, or -1 on bad arguments. */
 int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_steps);
+
+/* Per-launch timing.  While enabled, okls_step records a HIP event before and
+ * after every launch on its stream (events are created on first use and
+ * owned by the handle).  okls_profile_read synchronises the stream of the
+ * last profiled step, sums the elapsed times per category since the last
+ * read and clears them.  Categories (index into the arrays):
+ *   0 Newton-Schulz GEMMs, 1 factor GEMMs (cross-preconditioning and the
+ *   factor update), 2 whitening GEMMs (with the fused weight update),
+ *   3 statistics kernels, 4 cast / momentum kernels.
+ * flops[i] is the algorithmic floating-point work of category i summed over
+ * the profiled steps: 27 GEMMs of 2 d^3 per inverse square root (54 for the
+ * Shampoo fourth root), 3 m n (m + n) for the OKLS factors (m n (m + n) in
+ * Shampoo mode), 2 m n (m + n) for the whitening. */
+#define OKLS_PROFILE_CATEGORIES 5
+typedef struct {
+    double ms[OKLS_PROFILE_CATEGORIES];
+    double flops[OKLS_PROFILE_CATEGORIES];
+    int64_t launches[OKLS_PROFILE_CATEGORIES];
+    int64_t steps;
+} okls_profile_stats;
+
+okls_status okls_profile_enable(okls_handle* h, int enable);
+okls_status okls_profile_read(okls_handle* h, okls_profile_stats* out);
 
 /* Frees the handle's host memory.  Does not touch device memory. */
 okls_status okls_destroy(okls_handle* h);

@@ -82,6 +82,7 @@ float pow2_for_bound(double bound) {   // largest 2^e with bound * 2^e <= 2^kSca
 struct FacBufs {
   int d = 0, dp = 0, ld = 0;
   size_t Y[2] = {0, 0}, Z[2] = {0, 0}, T = 0, R32 = 0;
+  size_t YT[2] = {0, 0}, ZT[2] = {0, 0}, TT = 0;   // transposed copies
   int s_pold = 0, s_cinv = 0, s_rho = 0, s_sqrtc = 0, s_p16 = 0;
   int s_cinv2 = 0, s_rho2 = 0, s_sqrtc2 = 0;
 };
@@ -103,7 +104,10 @@ struct LaunchRec {
   int prob_base = 0;
   int split_in = 0, write_lo = 0;
   float ka = 0.f, kb = 0.f;
+  int cat = 0;                  // profiling category
 };
+
+enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4 };
 
 // Global scale slots
 enum { SL_ONE = 0, SL_Y = 1, SL_Z = 2, SL_T = 3, SL_FIRST_DYN = 4 };
@@ -127,6 +131,16 @@ struct okls_handle {
   size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_scal = 0, off_part = 0, off_flag = 0;
   std::vector<std::vector<LaunchRec>> chunks;
   std::vector<double> na, nb;
+  double step_flops[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+  // profiling
+  bool prof = false;
+  std::vector<hipEvent_t> events;           // pool
+  std::vector<std::pair<int, int>> pending; // (category, event pair index) of unread launches
+  size_t next_event = 0;
+  okls_profile_stats acc{};
+  ~okls_handle() {
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -219,6 +233,7 @@ struct Planner {
       f.d = d; f.dp = pad_tile(d); f.ld = ld_for(f.dp);
       const size_t b16 = static_cast<size_t>(f.dp) * f.ld * 2;
       f.Y[0] = take(b16); f.Y[1] = take(b16); f.Z[0] = take(b16); f.Z[1] = take(b16); f.T = take(b16);
+      f.YT[0] = take(b16); f.YT[1] = take(b16); f.ZT[0] = take(b16); f.ZT[1] = take(b16); f.TT = take(b16);
       if (!okls_mode) f.R32 = take(static_cast<size_t>(d) * d * 4);
       f.s_pold = slot++; f.s_cinv = slot++; f.s_rho = slot++; f.s_sqrtc = slot++; f.s_p16 = slot++;
       f.s_cinv2 = slot++; f.s_rho2 = slot++; f.s_sqrtc2 = slot++;
@@ -263,11 +278,15 @@ struct Planner {
     return r;
   }
 
+  int gemm_cat = CAT_NS;   // category of the GEMM launches being planned
+  double step_flops[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+
   void add_gemm(std::vector<LaunchRec>& L, const std::vector<GemmProb>& ps, bool upper, int split_in,
                 int write_lo, float ka = 0.f, float kb = 0.f) {
     if (ps.empty()) return;
     LaunchRec r;
     r.type = L_GEMM;
+    r.cat = gemm_cat;
     r.prob_base = static_cast<int>(probs.size());
     probs.insert(probs.end(), ps.begin(), ps.end());
     const std::pair<int, int> t = tiles_for(ps, upper);
@@ -286,6 +305,7 @@ struct Planner {
     std::vector<std::pair<int, int>> parts;
     LaunchRec r;
     r.type = L_STAT;
+    r.cat = CAT_STAT;
     r.first = static_cast<int>(stat_jobs.size());
     int blk = 0, part = 0;
     for (const StatSpec& s : specs) {
@@ -325,6 +345,7 @@ struct Planner {
     if (specs.empty()) return;
     LaunchRec r;
     r.type = L_CAST;
+    r.cat = CAT_CAST;
     r.first = static_cast<int>(cast_jobs.size());
     int blk = 0;
     for (const CastSpec& s : specs) {
@@ -350,13 +371,20 @@ struct Planner {
 
   GemmProb prob() {
     GemmProb p{};
-    p.A = p.B = p.out32 = p.out16 = p.aux = no_ref();
+    p.A = p.B = p.out32 = p.out16 = p.out16T = p.aux = no_ref();
     p.s_out = -1;
     p.cslot = -1;
     return p;
   }
 
-  // ---- Newton-Schulz chain for a list of factors.  src(f) is the fp32
+  // Z_k^T: Z_1 = a_0 I + b_0 Y_0 is exactly symmetric (the cast writes one copy);
+  // later Z_k come with a transposed copy from their GEMM.
+  static size_t zt_of(const FacBufs& F, int k) { return k == 1 ? F.Z[1] : F.ZT[k & 1]; }
+
+  // ---- Newton-Schulz chain for a list of factors.  Every product X W runs as
+  // NT(X, W^T) on the transposed copy of W, so it is the plain product of the
+  // iteration (no symmetry of the iterates is assumed: the coupled iteration
+  // is only stable when Y and Z carry consistent rounding).  src(f) is the fp32
   // matrix being rooted (d x d, ld d); returns launches appended to L.
   // final_mode 0: inverse root into the caller P (+ fp16 copy in Z[K%2]);
   // final_mode 1: square root into fac.R32 (the first Shampoo chain).
@@ -401,7 +429,8 @@ struct Planner {
         p.A = p.B = ws_ref(F.Y[0]); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp; p.Mp = p.Np = F.dp;
         p.epi = EPI_NS_Y1; p.aux = src[f]; p.ldaux = F.d; p.cslot = chain == 0 ? F.s_cinv : F.s_cinv2;
         p.c2 = damping(F.d) / (1.0f + damping(F.d));
-        p.out16 = ws_ref(F.Y[1]); p.ld16 = F.ld; p.lo16 = F.dp; p.s_out = SL_Y; p.sA = p.sB = SL_Y;
+        p.out16 = ws_ref(F.Y[1]); p.out16T = ws_ref(F.YT[1]); p.ld16 = F.ld; p.lo16 = F.dp; p.s_out = SL_Y;
+        p.sA = p.sB = SL_Y;
         ps.push_back(p);
       }
       add_gemm(L, ps, false, 0 < ks, 1 < ks, static_cast<float>(na[0]), static_cast<float>(nb[0]));
@@ -414,8 +443,10 @@ struct Planner {
       for (size_t f = 0; f < nf; ++f) {
         FacBufs& F = *facs[f];
         GemmProb p = prob();
-        p.A = ws_ref(F.Z[cb]); p.B = ws_ref(F.Y[cb]); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
-        p.Mp = p.Np = F.dp; p.epi = EPI_NS_T; p.out16 = ws_ref(F.T); p.ld16 = F.ld; p.lo16 = F.dp;
+        // T_k = a_k I + b_k Z_k Y_k as NT(Z_k, Y_k^T); both copies of T are written
+        p.A = ws_ref(F.Z[cb]); p.B = ws_ref(F.YT[cb]); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
+        p.Mp = p.Np = F.dp; p.epi = EPI_NS_T; p.out16 = ws_ref(F.T); p.out16T = ws_ref(F.TT); p.ld16 = F.ld;
+        p.lo16 = F.dp;
         p.s_out = SL_T; p.sA = SL_Z; p.sB = SL_Y;
         pt.push_back(p);
       }
@@ -425,16 +456,18 @@ struct Planner {
         for (size_t f = 0; f < nf; ++f) {   // Y_{k+1} = Y_k T_k
           FacBufs& F = *facs[f];
           GemmProb p = prob();
-          p.A = ws_ref(F.Y[cb]); p.B = ws_ref(F.T); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
-          p.Mp = p.Np = F.dp; p.epi = EPI_STORE16; p.out16 = ws_ref(F.Y[nbuf]); p.ld16 = F.ld; p.lo16 = F.dp;
+          p.A = ws_ref(F.Y[cb]); p.B = ws_ref(F.TT); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
+          p.Mp = p.Np = F.dp; p.epi = EPI_STORE16; p.out16 = ws_ref(F.Y[nbuf]); p.out16T = ws_ref(F.YT[nbuf]);
+          p.ld16 = F.ld; p.lo16 = F.dp;
           p.s_out = SL_Y; p.sA = SL_Y; p.sB = SL_T;
           pu.push_back(p);
         }
         for (size_t f = 0; f < nf; ++f) {   // Z_{k+1} = T_k Z_k
           FacBufs& F = *facs[f];
           GemmProb p = prob();
-          p.A = ws_ref(F.T); p.B = ws_ref(F.Z[cb]); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
-          p.Mp = p.Np = F.dp; p.epi = EPI_STORE16; p.out16 = ws_ref(F.Z[nbuf]); p.ld16 = F.ld; p.lo16 = F.dp;
+          p.A = ws_ref(F.T); p.B = ws_ref(zt_of(F, k)); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp;
+          p.Mp = p.Np = F.dp; p.epi = EPI_STORE16; p.out16 = ws_ref(F.Z[nbuf]); p.out16T = ws_ref(F.ZT[nbuf]);
+          p.ld16 = F.ld; p.lo16 = F.dp;
           p.s_out = SL_Z; p.sA = SL_T; p.sB = SL_Z;
           pu.push_back(p);
         }
@@ -445,11 +478,11 @@ struct Planner {
           GemmProb p = prob();
           p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp; p.Mp = p.Np = F.dp; p.epi = EPI_NS_FINAL;
           if (final_mode == 0) {      // P = Z_K / sqrt(c), fp16 copy Z_K * s_Z
-            p.A = ws_ref(F.T); p.B = ws_ref(F.Z[cb]); p.sA = SL_T; p.sB = SL_Z;
+            p.A = ws_ref(F.T); p.B = ws_ref(zt_of(F, k)); p.sA = SL_T; p.sB = SL_Z;
             p.out32 = pdst[f]; p.ld32 = F.d; p.cslot = chain == 0 ? F.s_rho : F.s_rho2;
             p.out16 = ws_ref(F.Z[nbuf]); p.ld16 = F.ld; p.lo16 = F.dp; p.s_out = SL_Z;
           } else {                    // R = Y_K sqrt(c)
-            p.A = ws_ref(F.Y[cb]); p.B = ws_ref(F.T); p.sA = SL_Y; p.sB = SL_T;
+            p.A = ws_ref(F.Y[cb]); p.B = ws_ref(F.TT); p.sA = SL_Y; p.sB = SL_T;
             p.out32 = ws_ref(F.R32); p.ld32 = F.d; p.cslot = F.s_sqrtc;
           }
           pu.push_back(p);
@@ -469,6 +502,7 @@ struct Planner {
       for (size_t* o : offs) *o += base;
       for (FacBufs* f : {&mb.fa, &mb.fb}) {
         f->Y[0] += base; f->Y[1] += base; f->Z[0] += base; f->Z[1] += base; f->T += base; f->R32 += base;
+        f->YT[0] += base; f->YT[1] += base; f->ZT[0] += base; f->ZT[1] += base; f->TT += base;
       }
     }
     ws_bufs.emplace_back();
@@ -536,6 +570,15 @@ struct Planner {
     }
     add_cast(L, cs);
 
+    // algorithmic work of this chunk (see okls_profile_stats)
+    for (const MatBufs& mb : mats) {
+      const double m = mb.m, n = mb.n;
+      step_flops[CAT_FACTOR] += (okls_mode ? 3.0 : 1.0) * m * n * (m + n);
+      step_flops[CAT_WHITEN] += 2.0 * m * n * (m + n);
+      // 3K - 3 GEMMs per inverse square root (27 at K = 10); two chains for the fourth root
+      step_flops[CAT_NS] += (okls_mode ? 1.0 : 2.0) * (3.0 * cfg.ns_steps - 3.0) * 2.0 * (m * m * m + n * n * n);
+    }
+    gemm_cat = CAT_FACTOR;
     if (okls_mode) {
       // 3. X_a = G P_b (m x n), X_b^T = G^T P_a (n x m)
       std::vector<GemmProb> px;
@@ -602,6 +645,7 @@ struct Planner {
     }
 
     // 5. inverse roots
+    gemm_cat = CAT_NS;
     std::vector<FacBufs*> facs;
     std::vector<Ref> src, pdst;
     for (MatBufs& mb : mats) {
@@ -622,6 +666,7 @@ struct Planner {
     }
 
     // 6. whitening: V^T = P_b N^T (n x m), then U = P_a V fused with the update
+    gemm_cat = CAT_WHITEN;
     {
       std::vector<GemmProb> pv;
       for (const MatBufs& mb : mats) {
@@ -724,6 +769,9 @@ struct Planner {
               const int need_ld = r.write_lo ? p.lo16 + p.Np : p.Np;
               if (p.ld16 < need_ld || (r.write_lo && p.lo16 < p.Np)) return false;
               if (!fits(p.out16, static_cast<size_t>(p.Mp) * p.ld16 * 2)) return false;
+              if (p.out16T.kind != REF_NONE) {
+                if (p.Mp != p.Np || !fits(p.out16T, static_cast<size_t>(p.Np) * p.ld16 * 2)) return false;
+              }
             }
             if (p.epi == EPI_NS_Y1) {
               if (p.aux.kind == REF_NONE || p.ldaux < p.N || !slot_ok(p.cslot)) return false;
@@ -925,6 +973,7 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->chunks = P.chunks;
   h->na = P.na;
   h->nb = P.nb;
+  for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) h->step_flops[i] = P.step_flops[i];
 
   std::vector<float> scal(static_cast<size_t>(P.n_slots), 1.0f);
   scal[SL_ONE] = 1.0f;
@@ -1020,9 +1069,24 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
   float* scal = reinterpret_cast<float*>(ws + h->off_scal);
   float* part = reinterpret_cast<float*>(ws + h->off_part);
 
+  if (h->prof) {
+    h->acc.steps += 1;
+    for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) h->acc.flops[i] += h->step_flops[i];
+  }
   for (const std::vector<LaunchRec>& L : h->chunks) {
     for (const LaunchRec& r : L) {
       hipError_t e = hipSuccess;
+      size_t ev = 0;
+      if (h->prof) {
+        ev = h->next_event;
+        while (h->events.size() < ev + 2) {
+          hipEvent_t x;
+          if (hipEventCreate(&x) != hipSuccess) return OKLS_ERR_HIP;
+          h->events.push_back(x);
+        }
+        h->next_event += 2;
+        if (hipEventRecord(h->events[ev], s) != hipSuccess) return OKLS_ERR_HIP;
+      }
       if (r.type == L_STAT) {
         StatArgs a;
         a.jobs = reinterpret_cast<const StatJob*>(ws + h->off_stat) + r.first;
@@ -1066,6 +1130,10 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         e = launch_gemm(a, r.count, s);
       }
       if (e != hipSuccess) return OKLS_ERR_HIP;
+      if (h->prof) {
+        if (hipEventRecord(h->events[ev + 1], s) != hipSuccess) return OKLS_ERR_HIP;
+        h->pending.push_back({r.cat, static_cast<int>(ev)});
+      }
     }
   }
   return OKLS_OK;
@@ -1105,6 +1173,30 @@ okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* t, void*
   if (hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return OKLS_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return OKLS_ERR_HIP;
   return host_flag ? OKLS_ERR_NONFINITE : OKLS_OK;
+}
+
+okls_status okls_profile_enable(okls_handle* h, int enable) {
+  if (h == nullptr) return OKLS_ERR_INVALID_ARG;
+  h->prof = enable != 0;
+  return OKLS_OK;
+}
+
+okls_status okls_profile_read(okls_handle* h, okls_profile_stats* out) {
+  if (h == nullptr || out == nullptr) return OKLS_ERR_INVALID_ARG;
+  if (!h->pending.empty()) {
+    if (hipEventSynchronize(h->events[h->pending.back().second + 1]) != hipSuccess) return OKLS_ERR_HIP;
+    for (const std::pair<int, int>& p : h->pending) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, h->events[p.second], h->events[p.second + 1]) != hipSuccess) return OKLS_ERR_HIP;
+      h->acc.ms[p.first] += ms;
+      h->acc.launches[p.first] += 1;
+    }
+  }
+  *out = h->acc;
+  h->acc = okls_profile_stats{};
+  h->pending.clear();
+  h->next_event = 0;
+  return OKLS_OK;
 }
 
 okls_status okls_destroy(okls_handle* h) {

@@ -53,6 +53,113 @@ __device__ __forceinline__ void store16(half_t* p, int lo_off, bool write_lo, co
   if (write_lo) *reinterpret_cast<half4_t*>(p + lo_off) = lo;
 }
 
+// Transposed copy: element (r, c0+e) goes to row c0+e, column r.  For a fixed
+// e the 16 lanes of a row group write 16 consecutive halves (32 B).
+__device__ __forceinline__ void store16T(half_t* base, int ld, int lo_off, bool write_lo, int r, int c0,
+                                         const float (&x)[4], float s) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float y = x[e] * s;
+    const half_t h = static_cast<half_t>(y);
+    half_t* p = base + static_cast<size_t>(c0 + e) * ld + r;
+    p[0] = h;
+    if (write_lo) p[lo_off] = static_cast<half_t>(y - static_cast<float>(h));
+  }
+}
+
+struct EpiCtx {
+  float alpha;
+  int M, N, ti, tj, rbase, cbase;
+  bool write_lo;
+  float* out32;
+  half_t* out16;
+  half_t* out16T;
+  const float* aux;
+  float s_out, cval;
+  int ld32, ld16, lo16, ldaux;
+  float c0, c1, c2, ka, kb, lr, decay;
+};
+
+// Epilogue of one output tile, one instantiation per kind so that every
+// accumulator index is a compile-time constant (keeps them in registers).
+// Fragment (i, j) of a wave holds rows rbase + 16 i and the four columns
+// cbase + 16 j + e of each row.
+template <int EPI>
+__device__ __forceinline__ void epilogue(const floatx4 (&acc)[4][4], const EpiCtx& x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = x.rbase + i * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c0 = x.cbase + j * 16;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] * x.alpha;
+      if constexpr (EPI == EPI_STORE32) {
+        if (r < x.M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c0 + e < x.N) x.out32[static_cast<size_t>(r) * x.ld32 + c0 + e] = v[e];
+        }
+      } else if constexpr (EPI == EPI_SYRK) {
+        // S <- c0*S + c1*v + c2*I on the upper triangle, mirrored below.
+        if (r < x.M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = c0 + e;
+            if (c < x.N && (x.ti != x.tj || r <= c)) {
+              const size_t up = static_cast<size_t>(r) * x.ld32 + c;
+              const float s = x.c0 * x.out32[up] + x.c1 * v[e] + (r == c ? x.c2 : 0.0f);
+              x.out32[up] = s;
+              if (r != c) x.out32[static_cast<size_t>(c) * x.ld32 + r] = s;
+            }
+          }
+        }
+      } else if constexpr (EPI == EPI_UPDATE) {
+        if (r < x.M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = c0 + e;
+            if (c < x.N) {
+              const size_t o = static_cast<size_t>(r) * x.ld32 + c;
+              x.out32[o] = x.decay * x.out32[o] - x.lr * x.c0 * v[e];
+            }
+          }
+        }
+      } else {
+        // fp16 outputs into padded buffers (zeros outside the logical region)
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = c0 + e;
+          float t = 0.0f;
+          if (r < x.M && c < x.N) {
+            if constexpr (EPI == EPI_NS_T) {
+              t = (r == c ? x.ka : 0.0f) + x.kb * v[e];
+            } else if constexpr (EPI == EPI_NS_Y1) {
+              const float sym = 0.5f * (x.aux[static_cast<size_t>(r) * x.ldaux + c] +
+                                        x.aux[static_cast<size_t>(c) * x.ldaux + r]);
+              t = x.ka * (sym * x.cval + (r == c ? x.c2 : 0.0f)) + x.kb * v[e];
+            } else {  // EPI_STORE16, EPI_NS_FINAL
+              t = v[e];
+            }
+          }
+          y[e] = t;
+        }
+        if constexpr (EPI == EPI_NS_FINAL) {
+          if (x.out32 != nullptr && r < x.M) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c0 + e < x.N) x.out32[static_cast<size_t>(r) * x.ld32 + c0 + e] = y[e] * x.cval;
+          }
+        }
+        if (x.out16 != nullptr) store16(x.out16 + static_cast<size_t>(r) * x.ld16 + c0, x.lo16, x.write_lo, y, x.s_out);
+        if (x.out16T != nullptr) store16T(x.out16T, x.ld16, x.lo16, x.write_lo, r, c0, y, x.s_out);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args) {
   __shared__ half_t sA[2][kTile * kLdsStride];
   __shared__ half_t sB[2][kTile * kLdsStride];
@@ -135,85 +242,40 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args)
   }
 
   // ---------------- epilogue ----------------
-  const float alpha = 1.0f / (args.scal[P.sA] * args.scal[P.sB]);
-  const int epi = P.epi;
-  const int M = P.M, N = P.N;
-  const bool write_lo = args.write_lo != 0;
-  float* out32 = P.out32.kind != REF_NONE ? reinterpret_cast<float*>(resolve(P.out32, args.ws, args.user)) : nullptr;
-  half_t* out16 = P.out16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16, args.ws, args.user)) : nullptr;
-  const float* aux = P.aux.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(P.aux, args.ws, args.user)) : nullptr;
-  const float s_out = P.s_out >= 0 ? args.scal[P.s_out] : 1.0f;
-  const float cval = P.cslot >= 0 ? args.scal[P.cslot] : 1.0f;
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = ti * kTile + wm * 64 + i * 16 + frow;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c0 = tj * kTile + wn * 64 + j * 16 + (lane >> 4) * 4;
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] * alpha;
-
-      if (epi == EPI_STORE32) {
-        if (r < M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c0 + e < N) out32[static_cast<size_t>(r) * P.ld32 + c0 + e] = v[e];
-        }
-      } else if (epi == EPI_SYRK) {
-        // S <- c0*S + c1*v + c2*I on the upper triangle, mirrored below.
-        if (r < M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = c0 + e;
-            if (c < N && (ti != tj || r <= c)) {
-              const size_t up = static_cast<size_t>(r) * P.ld32 + c;
-              float s = P.c0 * out32[up] + P.c1 * v[e] + (r == c ? P.c2 : 0.0f);
-              out32[up] = s;
-              if (r != c) out32[static_cast<size_t>(c) * P.ld32 + r] = s;
-            }
-          }
-        }
-      } else if (epi == EPI_UPDATE) {
-        if (r < M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = c0 + e;
-            if (c < N) {
-              const size_t o = static_cast<size_t>(r) * P.ld32 + c;
-              out32[o] = args.decay * out32[o] - args.lr * P.c0 * v[e];
-            }
-          }
-        }
-      } else {
-        // fp16 outputs into padded buffers (zeros outside the logical region)
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = c0 + e;
-          const bool in = (r < M) && (c < N);
-          float y = 0.0f;
-          if (in) {
-            if (epi == EPI_NS_T) {
-              y = (r == c ? args.ka : 0.0f) + args.kb * v[e];
-            } else if (epi == EPI_NS_Y1) {
-              y = args.ka * (aux[static_cast<size_t>(r) * P.ldaux + c] * cval + (r == c ? P.c2 : 0.0f)) +
-                  args.kb * v[e];
-            } else {  // EPI_STORE16, EPI_NS_FINAL
-              y = v[e];
-            }
-          }
-          x[e] = y;
-        }
-        if (epi == EPI_NS_FINAL && out32 != nullptr && r < M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c0 + e < N) out32[static_cast<size_t>(r) * P.ld32 + c0 + e] = x[e] * cval;
-        }
-        if (out16 != nullptr) store16(out16 + static_cast<size_t>(r) * P.ld16 + c0, P.lo16, write_lo, x, s_out);
-      }
-    }
+  EpiCtx ctx;
+  ctx.alpha = 1.0f / (args.scal[P.sA] * args.scal[P.sB]);
+  ctx.M = P.M;
+  ctx.N = P.N;
+  ctx.ti = ti;
+  ctx.tj = tj;
+  ctx.rbase = ti * kTile + wm * 64 + frow;
+  ctx.cbase = tj * kTile + wn * 64 + (lane >> 4) * 4;
+  ctx.write_lo = args.write_lo != 0;
+  ctx.out32 = P.out32.kind != REF_NONE ? reinterpret_cast<float*>(resolve(P.out32, args.ws, args.user)) : nullptr;
+  ctx.out16 = P.out16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16, args.ws, args.user)) : nullptr;
+  ctx.out16T = P.out16T.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16T, args.ws, args.user)) : nullptr;
+  ctx.aux = P.aux.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(P.aux, args.ws, args.user)) : nullptr;
+  ctx.s_out = P.s_out >= 0 ? args.scal[P.s_out] : 1.0f;
+  ctx.cval = P.cslot >= 0 ? args.scal[P.cslot] : 1.0f;
+  ctx.ld32 = P.ld32;
+  ctx.ld16 = P.ld16;
+  ctx.lo16 = P.lo16;
+  ctx.ldaux = P.ldaux;
+  ctx.c0 = P.c0;
+  ctx.c1 = P.c1;
+  ctx.c2 = P.c2;
+  ctx.ka = args.ka;
+  ctx.kb = args.kb;
+  ctx.lr = args.lr;
+  ctx.decay = args.decay;
+  switch (P.epi) {
+    case EPI_STORE32: epilogue<EPI_STORE32>(acc, ctx); break;
+    case EPI_SYRK: epilogue<EPI_SYRK>(acc, ctx); break;
+    case EPI_NS_T: epilogue<EPI_NS_T>(acc, ctx); break;
+    case EPI_NS_Y1: epilogue<EPI_NS_Y1>(acc, ctx); break;
+    case EPI_STORE16: epilogue<EPI_STORE16>(acc, ctx); break;
+    case EPI_NS_FINAL: epilogue<EPI_NS_FINAL>(acc, ctx); break;
+    default: epilogue<EPI_UPDATE>(acc, ctx); break;
   }
 }
 
@@ -371,10 +433,15 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
         if (J.write_m) m[o] = mn;
         return a.s_t * (a.beta1 * mn + (1.0f - a.beta1) * gv);
       }
-      case CA_NS_Y0: return reinterpret_cast<const float*>(src)[o] * cinv + (r == c ? ddiag : 0.0f);
-      default:
-        return (r == c ? a.ka : 0.0f) +
-               a.kb * (reinterpret_cast<const float*>(src)[o] * cinv + (r == c ? ddiag : 0.0f));
+      default: {
+        // the rooted matrix is read symmetrised (exact no-op for the factors,
+        // which are stored exactly symmetric; the Shampoo second chain starts
+        // from a computed square root)
+        const float* s = reinterpret_cast<const float*>(src);
+        const float sym = 0.5f * (s[o] + s[static_cast<size_t>(c) * J.src_ld + r]);
+        const float y0 = sym * cinv + (r == c ? ddiag : 0.0f);
+        return J.kind == CA_NS_Y0 ? y0 : (r == c ? a.ka : 0.0f) + a.kb * y0;
+      }
     }
   };
 

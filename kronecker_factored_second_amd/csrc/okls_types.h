@@ -59,6 +59,7 @@ struct GemmProb {
   int32_t epi;
   Ref out32; int32_t ld32;
   Ref out16; int32_t ld16; int32_t lo16;   // lo part at +lo16 halves within a row
+  Ref out16T;              // optional transposed copy (same ld16 / lo16; square problems)
   Ref aux; int32_t ldaux;
   int32_t sA, sB;          // scale slots of the operands (alpha = 1/(scal[sA]*scal[sB]))
   int32_t s_out;           // scale slot for fp16 output

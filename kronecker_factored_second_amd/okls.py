@@ -19,7 +19,9 @@ STATUS = {0: "OKLS_OK", -1: "OKLS_ERR_INVALID_ARG", -2: "OKLS_ERR_SHAPE", -3: "O
 OKLS_F32, OKLS_BF16 = 0, 1
 MODE = {"okls": 0, "shampoo": 1}
 EXPORTED = ("okls_default_config", "okls_workspace_size", "okls_init", "okls_init_state", "okls_step",
-            "okls_check_finite", "okls_ns_coefficients", "okls_destroy", "okls_status_string")
+            "okls_check_finite", "okls_ns_coefficients", "okls_profile_enable", "okls_profile_read",
+            "okls_destroy", "okls_status_string")
+PROFILE_CATEGORIES = ("ns_gemm", "factor_gemm", "whiten_gemm", "stats", "cast")
 
 
 class Config(ctypes.Structure):
@@ -38,6 +40,11 @@ class GroupDesc(ctypes.Structure):
 class GroupTensors(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("M", ctypes.c_void_p), ("Sa", ctypes.c_void_p),
                 ("Sb", ctypes.c_void_p), ("Pa", ctypes.c_void_p), ("Pb", ctypes.c_void_p)]
+
+
+class ProfileStats(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * 5), ("flops", ctypes.c_double * 5), ("launches", ctypes.c_int64 * 5),
+                ("steps", ctypes.c_int64)]
 
 
 class OKLSError(RuntimeError):
@@ -74,6 +81,10 @@ def load(path: str = LIB_PATH):
     lib.okls_ns_coefficients.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(ctypes.c_double), ctypes.c_int]
     lib.okls_ns_coefficients.restype = ctypes.c_int
+    lib.okls_profile_enable.argtypes = [vp, ctypes.c_int]
+    lib.okls_profile_enable.restype = ctypes.c_int
+    lib.okls_profile_read.argtypes = [vp, ctypes.POINTER(ProfileStats)]
+    lib.okls_profile_read.restype = ctypes.c_int
     lib.okls_destroy.argtypes = [vp]
     lib.okls_destroy.restype = ctypes.c_int
     lib.okls_status_string.argtypes = [ctypes.c_int]
@@ -106,7 +117,7 @@ def precision_config(precision: str = "fp16", **overrides) -> Config:
     if precision == "fp16":
         base = dict(ns_split_steps=0, factor_split=0, ns_damping=5e-3)
     elif precision == "fp32":
-        base = dict(ns_split_steps=-1, factor_split=1, ns_damping=4e-4)
+        base = dict(ns_split_steps=-1, factor_split=1, ns_damping=2e-3)
     else:
         raise ValueError(precision)
     base.update(overrides)
@@ -176,6 +187,17 @@ def check_finite(h, tensors, stream) -> bool:
         return False
     _check("okls_check_finite", st)
     return True
+
+
+def profile_enable(h, enable: bool):
+    _check("okls_profile_enable", load().okls_profile_enable(h, 1 if enable else 0))
+
+
+def profile_read(h) -> dict:
+    st = ProfileStats()
+    _check("okls_profile_read", load().okls_profile_read(h, ctypes.byref(st)))
+    return {name: {"ms": st.ms[i], "flops": st.flops[i], "launches": int(st.launches[i])}
+            for i, name in enumerate(PROFILE_CATEGORIES)} | {"steps": int(st.steps)}
 
 
 def destroy(h):

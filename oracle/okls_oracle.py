@@ -140,6 +140,12 @@ def _sym(S):
 # [CLEAN] eq (3) / [SHAMPOO]: L^{-1/4}, R^{-1/4}).  Principal root of an SPD
 # matrix via the symmetric eigendecomposition.
 # ---------------------------------------------------------------------------
+def cond(S: np.ndarray) -> float:
+    """lambda_max / lambda_min of a symmetric matrix (inf if not positive definite)."""
+    lam = np.linalg.eigvalsh(_sym(S))
+    return float(lam[-1] / lam[0]) if lam[0] > 0 else float("inf")
+
+
 def inv_root_exact(S: np.ndarray, p: int):
     """Returns (S^{-1/p}, condition number lambda_max / lambda_min)."""
     lam, V = np.linalg.eigh(_sym(S))
@@ -301,12 +307,13 @@ def okls_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "exact
     coupled Newton-Schulz iteration in fp64.  Both are always reported."""
     G = np.asarray(G, dtype=np.float64)
     Sa, Sb = factor_update_okls(st.Sa, st.Sb, st.Pa, st.Pb, G, hp.beta2, hp.eps)
-    Pa_ex, ka = inv_root_exact(Sa, 2)
-    Pb_ex, kb = inv_root_exact(Sb, 2)
     coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
     Pa_ns, _ = ns_inv_sqrt(Sa, coeffs, hp.ns_damping)
     Pb_ns, _ = ns_inv_sqrt(Sb, coeffs, hp.ns_damping)
-    Pa, Pb = (Pa_ex, Pb_ex) if root == "exact" else (_sym(Pa_ns), _sym(Pb_ns))
+    if root == "exact":
+        (Pa, ka), (Pb, kb) = inv_root_exact(Sa, 2), inv_root_exact(Sb, 2)
+    else:
+        Pa, Pb, ka, kb = Pa_ns, Pb_ns, cond(Sa), cond(Sb)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
     U = whiten(Pa, N, Pb)
     W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
@@ -319,12 +326,13 @@ def shampoo_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ex
     decoupled decay as in OKLS."""
     G = np.asarray(G, dtype=np.float64)
     Sa, Sb = factor_update_shampoo(st.Sa, st.Sb, G, hp.eps)
-    Pa_ex, ka = inv_root_exact(Sa, 4)
-    Pb_ex, kb = inv_root_exact(Sb, 4)
     coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
-    Pa_ns = _sym(ns_inv_quarter(Sa, coeffs, hp.ns_damping))
-    Pb_ns = _sym(ns_inv_quarter(Sb, coeffs, hp.ns_damping))
-    Pa, Pb = (Pa_ex, Pb_ex) if root == "exact" else (Pa_ns, Pb_ns)
+    Pa_ns = ns_inv_quarter(Sa, coeffs, hp.ns_damping)
+    Pb_ns = ns_inv_quarter(Sb, coeffs, hp.ns_damping)
+    if root == "exact":
+        (Pa, ka), (Pb, kb) = inv_root_exact(Sa, 4), inv_root_exact(Sb, 4)
+    else:
+        Pa, Pb, ka, kb = Pa_ns, Pb_ns, cond(Sa), cond(Sb)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
     U = whiten(Pa, N, Pb)
     W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
