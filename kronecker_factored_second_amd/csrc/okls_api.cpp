@@ -36,7 +36,11 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxDim = 32768;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-int pad_tile(int x) { return (x + kTile - 1) / kTile * kTile; }
+// Sides up to 512 pad to 128, larger ones to 256 (so the 256 tile applies).
+int pad_tile(int x) {
+  const int u = x > kBigPadFrom ? kBigTile : kTile;
+  return (x + u - 1) / u * u;
+}
 
 // ---------------------------------------------------------------------------
 // Newton-Schulz coefficients.  The README ("How it works" and the intro
@@ -105,6 +109,7 @@ struct LaunchRec {
   int split_in = 0, write_lo = 0;
   float ka = 0.f, kb = 0.f;
   int cat = 0;                  // profiling category
+  int tile = kTile;             // GEMM block tile
 };
 
 enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4 };
@@ -261,19 +266,37 @@ struct Planner {
   }
 
   // ---- tiles
-  std::pair<int, int> tiles_for(const std::vector<GemmProb>& ps, bool upper) {
-    std::string key = upper ? "U" : "F";
+  // Workgroup w of a launch runs on XCD w % 8.  The tile list (problem-major,
+  // row-major) is cut into 8 contiguous chunks and dealt round-robin, so each
+  // XCD's L2 sees a contiguous band of tiles sharing operand strips.
+  static std::vector<TileRef> xcd_order(const std::vector<TileRef>& t) {
+    const size_t n = t.size(), X = 8;
+    std::vector<size_t> start(X + 1, 0);
+    for (size_t x = 0; x < X; ++x) start[x + 1] = start[x] + n / X + (x < n % X ? 1 : 0);
+    std::vector<TileRef> out;
+    out.reserve(n);
+    for (size_t y = 0; out.size() < n; ++y)
+      for (size_t x = 0; x < X; ++x)
+        if (start[x] + y < start[x + 1]) out.push_back(t[start[x] + y]);
+    return out;
+  }
+
+  std::pair<int, int> tiles_for(const std::vector<GemmProb>& ps, bool upper, int bt) {
+    std::string key = (upper ? "U" : "F") + std::to_string(bt);
     for (const GemmProb& p : ps) key += ":" + std::to_string(p.Mp) + "x" + std::to_string(p.Np);
     auto it = tile_cache.find(key);
     if (it != tile_cache.end()) return it->second;
-    const int first = static_cast<int>(tiles.size());
+    std::vector<TileRef> t;
     for (size_t q = 0; q < ps.size(); ++q) {
-      const int tm = ps[q].Mp / kTile, tn = ps[q].Np / kTile;
+      const int tm = ps[q].Mp / bt, tn = ps[q].Np / bt;
       for (int i = 0; i < tm; ++i)
         for (int j = upper ? i : 0; j < tn; ++j)
-          tiles.push_back(TileRef{static_cast<int32_t>(q), (i << 16) | j});
+          t.push_back(TileRef{static_cast<int32_t>(q), (i << 16) | j});
     }
-    const std::pair<int, int> r{first, static_cast<int>(tiles.size()) - first};
+    t = xcd_order(t);
+    const int first = static_cast<int>(tiles.size());
+    tiles.insert(tiles.end(), t.begin(), t.end());
+    const std::pair<int, int> r{first, static_cast<int>(t.size())};
     tile_cache[key] = r;
     return r;
   }
@@ -289,7 +312,11 @@ struct Planner {
     r.cat = gemm_cat;
     r.prob_base = static_cast<int>(probs.size());
     probs.insert(probs.end(), ps.begin(), ps.end());
-    const std::pair<int, int> t = tiles_for(ps, upper);
+    // the large tile when every problem's padded sides are multiples of it
+    r.tile = kBigTile;
+    for (const GemmProb& p : ps)
+      if (p.Mp % kBigTile || p.Np % kBigTile) r.tile = kTile;
+    const std::pair<int, int> t = tiles_for(ps, upper, r.tile);
     r.first = t.first;
     r.count = t.second;
     r.split_in = split_in;
@@ -739,6 +766,7 @@ struct Planner {
       for (const LaunchRec& r : chunks[ci]) {
         if (r.type == L_GEMM) {
           if (r.first < 0 || r.first + r.count > static_cast<int>(tiles.size())) return false;
+          if (r.tile != kTile && r.tile != kBigTile) return false;
           const int segs = r.split_in ? 2 : 1;
           for (int t = r.first; t < r.first + r.count; ++t) {
             const TileRef tr = tiles[t];
@@ -746,8 +774,8 @@ struct Planner {
             if (tr.prob < 0 || q >= static_cast<int>(probs.size())) return false;
             const GemmProb& p = probs[q];
             const int ti = tr.ij >> 16, tj = tr.ij & 0xffff;
-            if (p.Mp % kTile || p.Np % kTile || p.Kp % kTile || p.Kp <= 0) return false;
-            if (ti < 0 || tj < 0 || ti >= p.Mp / kTile || tj >= p.Np / kTile) return false;
+            if (p.Mp % r.tile || p.Np % r.tile || p.Kp % kTile || p.Kp <= 0) return false;
+            if (ti < 0 || tj < 0 || ti >= p.Mp / r.tile || tj >= p.Np / r.tile) return false;
             if (p.M > p.Mp || p.N > p.Np || p.M < 1 || p.N < 1) return false;
             if (p.lda < segs * p.Kp || p.ldb < segs * p.Kp) return false;
             if (!fits(p.A, static_cast<size_t>(p.Mp) * p.lda * 2) || !fits(p.B, static_cast<size_t>(p.Np) * p.ldb * 2))
@@ -1127,7 +1155,7 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.ws = ws;
         a.scal = scal;
         a.user = user;
-        e = launch_gemm(a, r.count, s);
+        e = launch_gemm(a, r.count, r.tile, s);
       }
       if (e != hipSuccess) return OKLS_ERR_HIP;
       if (h->prof) {

@@ -84,13 +84,13 @@ struct EpiCtx {
 // accumulator index is a compile-time constant (keeps them in registers).
 // Fragment (i, j) of a wave holds rows rbase + 16 i and the four columns
 // cbase + 16 j + e of each row.
-template <int EPI>
-__device__ __forceinline__ void epilogue(const floatx4 (&acc)[4][4], const EpiCtx& x) {
+template <int EPI, int F>
+__device__ __forceinline__ void epilogue(const floatx4 (&acc)[F][F], const EpiCtx& x) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < F; ++i) {
     const int r = x.rbase + i * 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < F; ++j) {
       const int c0 = x.cbase + j * 16;
       float v[4];
 #pragma unroll
@@ -160,9 +160,15 @@ __device__ __forceinline__ void epilogue(const floatx4 (&acc)[4][4], const EpiCt
   }
 }
 
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args) {
-  __shared__ half_t sA[2][kTile * kLdsStride];
-  __shared__ half_t sB[2][kTile * kLdsStride];
+// Block tile BT x BT (BT = 128 or 256), 4 waves in 2 x 2, each wave a
+// (BT/2) x (BT/2) sub-tile of F x F fragments of 16 x 16 (F = BT / 32).
+// BT = 256: 128 KFLOP per KB loaded from L2 per block and 64 FLOP per LDS
+// byte per wave; one block per CU (144 KB of LDS, accumulators in AGPRs).
+template <int BT>
+__global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kernel(GemmArgs args) {
+  constexpr int F = BT / 32;
+  __shared__ half_t sA[2][BT * kLdsStride];
+  __shared__ half_t sB[2][BT * kLdsStride];
 
   const TileRef tr = args.tiles[args.tile_begin + blockIdx.x];
   const GemmProb& P = args.probs[args.prob_base + tr.prob];
@@ -171,9 +177,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args)
   const int lda = P.lda, ldb = P.ldb, Kp = P.Kp;
 
   const half_t* A = reinterpret_cast<const half_t*>(resolve(P.A, args.ws, args.user)) +
-                    static_cast<size_t>(ti) * kTile * lda;
+                    static_cast<size_t>(ti) * BT * lda;
   const half_t* B = reinterpret_cast<const half_t*>(resolve(P.B, args.ws, args.user)) +
-                    static_cast<size_t>(tj) * kTile * ldb;
+                    static_cast<size_t>(tj) * BT * ldb;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,31 +191,31 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args)
   const int kt_per_seg = Kp / kBK;
   const int niter = (args.split_in ? 3 : 1) * kt_per_seg;
 
-  half8_t ra[4], rb[4];
+  half8_t ra[F], rb[F];
   auto gload = [&](int it) {
     const int seg = it / kt_per_seg;
     const int k0 = (it - seg * kt_per_seg) * kBK + lk;
     const int offA = (seg == 2 ? Kp : 0) + k0;
     const int offB = (seg == 1 ? Kp : 0) + k0;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < F; ++p) {
       ra[p] = *reinterpret_cast<const half8_t*>(A + static_cast<size_t>(lrow + 32 * p) * lda + offA);
       rb[p] = *reinterpret_cast<const half8_t*>(B + static_cast<size_t>(lrow + 32 * p) * ldb + offB);
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < F; ++p) {
       *reinterpret_cast<half8_t*>(&sA[buf][(lrow + 32 * p) * kLdsStride + lk]) = ra[p];
       *reinterpret_cast<half8_t*>(&sB[buf][(lrow + 32 * p) * kLdsStride + lk]) = rb[p];
     }
   };
 
-  floatx4 acc[4][4];
+  floatx4 acc[F][F];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < F; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < F; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   gload(0);
   sstore(0);
@@ -217,24 +223,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args)
   int cur = 0;
   const int frow = lane & 15;
   const int fk = (lane >> 4) * 8;
+  const int arow = wm * (BT / 2) + frow;
+  const int brow = wn * (BT / 2) + frow;
   for (int it = 0; it < niter; ++it) {
     if (it + 1 < niter) gload(it + 1);
 #pragma unroll
     for (int kk = 0; kk < kBK; kk += 32) {
-      half8_t fa[4], fb[4];
+      half8_t fb[F];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const half8_t*>(&sA[cur][(wm * 64 + i * 16 + frow) * kLdsStride + kk + fk]);
+      for (int j = 0; j < F; ++j)
+        fb[j] = *reinterpret_cast<const half8_t*>(&sB[cur][(brow + j * 16) * kLdsStride + kk + fk]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const half8_t*>(&sB[cur][(wn * 64 + j * 16 + frow) * kLdsStride + kk + fk]);
-      // Operands swapped (B rows as the MFMA's A) so that each lane ends with
-      // four consecutive output columns of one output row.
+      for (int i = 0; i < F; ++i) {
+        const half8_t fa = *reinterpret_cast<const half8_t*>(&sA[cur][(arow + i * 16) * kLdsStride + kk + fk]);
+        // Operands swapped (B rows as the MFMA's A) so that each lane ends with
+        // four consecutive output columns of one output row.
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < F; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa, acc[i][j], 0, 0, 0);
+      }
     }
     if (it + 1 < niter) sstore(cur ^ 1);
     __syncthreads();
@@ -248,8 +255,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args)
   ctx.N = P.N;
   ctx.ti = ti;
   ctx.tj = tj;
-  ctx.rbase = ti * kTile + wm * 64 + frow;
-  ctx.cbase = tj * kTile + wn * 64 + (lane >> 4) * 4;
+  ctx.rbase = ti * BT + wm * (BT / 2) + frow;
+  ctx.cbase = tj * BT + wn * (BT / 2) + (lane >> 4) * 4;
   ctx.write_lo = args.write_lo != 0;
   ctx.out32 = P.out32.kind != REF_NONE ? reinterpret_cast<float*>(resolve(P.out32, args.ws, args.user)) : nullptr;
   ctx.out16 = P.out16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16, args.ws, args.user)) : nullptr;
@@ -269,13 +276,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs args)
   ctx.lr = args.lr;
   ctx.decay = args.decay;
   switch (P.epi) {
-    case EPI_STORE32: epilogue<EPI_STORE32>(acc, ctx); break;
-    case EPI_SYRK: epilogue<EPI_SYRK>(acc, ctx); break;
-    case EPI_NS_T: epilogue<EPI_NS_T>(acc, ctx); break;
-    case EPI_NS_Y1: epilogue<EPI_NS_Y1>(acc, ctx); break;
-    case EPI_STORE16: epilogue<EPI_STORE16>(acc, ctx); break;
-    case EPI_NS_FINAL: epilogue<EPI_NS_FINAL>(acc, ctx); break;
-    default: epilogue<EPI_UPDATE>(acc, ctx); break;
+    case EPI_STORE32: epilogue<EPI_STORE32, F>(acc, ctx); break;
+    case EPI_SYRK: epilogue<EPI_SYRK, F>(acc, ctx); break;
+    case EPI_NS_T: epilogue<EPI_NS_T, F>(acc, ctx); break;
+    case EPI_NS_Y1: epilogue<EPI_NS_Y1, F>(acc, ctx); break;
+    case EPI_STORE16: epilogue<EPI_STORE16, F>(acc, ctx); break;
+    case EPI_NS_FINAL: epilogue<EPI_NS_FINAL, F>(acc, ctx); break;
+    default: epilogue<EPI_UPDATE, F>(acc, ctx); break;
   }
 }
 
@@ -521,9 +528,15 @@ __global__ void zero_int_kernel(int* p) { *p = 0; }
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_gemm(const GemmArgs& a, int n_tiles, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, int n_tiles, int tile, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_nt_kernel, dim3(n_tiles), dim3(kGemmThreads), 0, s, a);
+  if (tile == 256) {
+    hipLaunchKernelGGL(gemm_nt_kernel<256>, dim3(n_tiles), dim3(kGemmThreads), 0, s, a);
+  } else if (tile == 128) {
+    hipLaunchKernelGGL(gemm_nt_kernel<128>, dim3(n_tiles), dim3(kGemmThreads), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

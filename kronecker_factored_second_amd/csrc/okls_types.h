@@ -6,7 +6,9 @@
 namespace okls {
 
 constexpr int kMaxGroups = 16;
-constexpr int kTile = 128;           // GEMM output tile (rows and cols) and padding unit
+constexpr int kTile = 128;           // smallest GEMM output tile and padding unit
+constexpr int kBigTile = 256;        // large GEMM output tile; sides above kBigPadFrom pad to it
+constexpr int kBigPadFrom = 512;
 constexpr int kBK = 64;              // GEMM K step
 constexpr int kCastTile = 64;        // elementwise cast tile
 constexpr int kStatThreads = 256;
