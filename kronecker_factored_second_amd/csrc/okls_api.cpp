@@ -20,6 +20,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <map>
 #include <new>
 #include <string>
@@ -266,18 +267,31 @@ struct Planner {
   }
 
   // ---- tiles
-  // Workgroup w of a launch runs on XCD w % 8.  The tile list (problem-major,
-  // row-major) is cut into 8 contiguous chunks and dealt round-robin, so each
-  // XCD's L2 sees a contiguous band of tiles sharing operand strips.
-  static std::vector<TileRef> xcd_order(const std::vector<TileRef>& t) {
-    const size_t n = t.size(), X = 8;
-    std::vector<size_t> start(X + 1, 0);
-    for (size_t x = 0; x < X; ++x) start[x + 1] = start[x] + n / X + (x < n % X ? 1 : 0);
+  // Workgroup w of a launch runs on XCD w % 8.  Tiles are grouped into cost
+  // classes (same K); each class's list (in locality order) is cut into 8
+  // contiguous chunks, XCD x gets chunk x of every class (costliest class
+  // first), and the per-XCD lists are dealt round-robin: every XCD gets the
+  // same work and a contiguous band of each class for its L2.
+  static std::vector<TileRef> xcd_order(const std::vector<TileRef>& t, const std::vector<GemmProb>& ps) {
+    const size_t X = 8;
+    std::map<int, std::vector<TileRef>, std::greater<int>> classes;   // by K, descending
+    for (const TileRef& r : t) classes[ps[r.prob].Kp].push_back(r);
+    std::vector<std::vector<TileRef>> per(X);
+    for (auto& kv : classes) {
+      const std::vector<TileRef>& c = kv.second;
+      const size_t n = c.size();
+      size_t s = 0;
+      for (size_t x = 0; x < X; ++x) {
+        const size_t len = n / X + (x < n % X ? 1 : 0);
+        per[x].insert(per[x].end(), c.begin() + s, c.begin() + s + len);
+        s += len;
+      }
+    }
     std::vector<TileRef> out;
-    out.reserve(n);
-    for (size_t y = 0; out.size() < n; ++y)
+    out.reserve(t.size());
+    for (size_t y = 0; out.size() < t.size(); ++y)
       for (size_t x = 0; x < X; ++x)
-        if (start[x] + y < start[x + 1]) out.push_back(t[start[x] + y]);
+        if (y < per[x].size()) out.push_back(per[x][y]);
     return out;
   }
 
@@ -286,14 +300,18 @@ struct Planner {
     for (const GemmProb& p : ps) key += ":" + std::to_string(p.Mp) + "x" + std::to_string(p.Np);
     auto it = tile_cache.find(key);
     if (it != tile_cache.end()) return it->second;
+    // per problem: bands of 8 tile rows, column-major inside a band, so the
+    // 32 blocks an XCD runs at once share few operand row strips
+    constexpr int kBand = 8;
     std::vector<TileRef> t;
     for (size_t q = 0; q < ps.size(); ++q) {
       const int tm = ps[q].Mp / bt, tn = ps[q].Np / bt;
-      for (int i = 0; i < tm; ++i)
-        for (int j = upper ? i : 0; j < tn; ++j)
-          t.push_back(TileRef{static_cast<int32_t>(q), (i << 16) | j});
+      for (int i0 = 0; i0 < tm; i0 += kBand)
+        for (int j = 0; j < tn; ++j)
+          for (int i = i0; i < std::min(tm, i0 + kBand); ++i)
+            if (!upper || j >= i) t.push_back(TileRef{static_cast<int32_t>(q), (i << 16) | j});
     }
-    t = xcd_order(t);
+    t = xcd_order(t, ps);
     const int first = static_cast<int>(tiles.size());
     tiles.insert(tiles.end(), t.begin(), t.end());
     const std::pair<int, int> r{first, static_cast<int>(t.size())};
@@ -312,10 +330,17 @@ struct Planner {
     r.cat = gemm_cat;
     r.prob_base = static_cast<int>(probs.size());
     probs.insert(probs.end(), ps.begin(), ps.end());
-    // the large tile when every problem's padded sides are multiples of it
+    // the large tile when every problem's padded sides are multiples of it and
+    // the launch has at least four blocks of it per CU (1024); otherwise the
+    // 128 tile keeps the CUs busy
     r.tile = kBigTile;
-    for (const GemmProb& p : ps)
+    long big_tiles = 0;
+    for (const GemmProb& p : ps) {
       if (p.Mp % kBigTile || p.Np % kBigTile) r.tile = kTile;
+      const long tm = p.Mp / kBigTile, tn = p.Np / kBigTile;
+      big_tiles += upper ? tm * (tm + 1) / 2 : tm * tn;
+    }
+    if (big_tiles < 1024) r.tile = kTile;
     const std::pair<int, int> t = tiles_for(ps, upper, r.tile);
     r.first = t.first;
     r.count = t.second;

@@ -1,10 +1,12 @@
 // gfx950 kernels of the batched OKLS / Shampoo preconditioner step.
 //
 //  gemm_nt_kernel   grouped fp16 MFMA GEMM, C = alpha A B^T, fp32 accumulation,
-//                   128x128 output tiles, LDS double-buffered K loop, optional
-//                   split-fp16 (hi*hi + hi*lo + lo*hi) as a 3-segment K loop,
-//                   fused epilogues (factor EMA with mirrored store, the
-//                   Newton-Schulz step polynomial, the weight update).
+//                   128x128 or 256x256 output tiles (v_mfma_f32_32x32x16_f16),
+//                   operands streamed global -> LDS by direct loads through a
+//                   4-deep ring, optional split-fp16 (hi*hi + hi*lo + lo*hi) as
+//                   a 3-segment K loop, fused epilogues (factor EMA with
+//                   mirrored store, the Newton-Schulz step polynomial, the
+//                   weight update).
 //  stats_kernel     per-block absmax / sum of squares partials.
 //  cast_kernel      fp32/bf16 -> padded fp16 (hi, lo) with a power-of-two
 //                   scale derived from the partials, optional transpose; also
@@ -16,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "okls_kernels.h"
 
 namespace okls {
@@ -24,6 +28,7 @@ typedef _Float16 half_t;
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ char* resolve(const Ref& r, char* ws, const UserPtrs& u) {
   if (r.kind == REF_WS) return ws + r.off;
@@ -37,7 +42,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // ---------------------------------------------------------------------------
 // GEMM
 // ---------------------------------------------------------------------------
-constexpr int kLdsStride = kBK + 8;   // halves per LDS row: 144 B, breaks the 128 B row aliasing
 constexpr int kGemmThreads = 256;
 
 __device__ __forceinline__ void store16(half_t* p, int lo_off, bool write_lo, const float (&x)[4], float s) {
@@ -82,19 +86,20 @@ struct EpiCtx {
 
 // Epilogue of one output tile, one instantiation per kind so that every
 // accumulator index is a compile-time constant (keeps them in registers).
-// Fragment (i, j) of a wave holds rows rbase + 16 i and the four columns
-// cbase + 16 j + e of each row.
-template <int EPI, int F>
-__device__ __forceinline__ void epilogue(const floatx4 (&acc)[F][F], const EpiCtx& x) {
+// Block (i, j) of a wave holds, in each lane, row rbase + 32 i and the four
+// groups of four consecutive columns cbase + 32 j + 8 g + e.
+template <int EPI, int G>
+__device__ __forceinline__ void epilogue(const floatx16 (&acc)[G][G], const EpiCtx& x) {
 #pragma unroll
-  for (int i = 0; i < F; ++i) {
-    const int r = x.rbase + i * 16;
+  for (int i = 0; i < G; ++i) {
+    const int r = x.rbase + i * 32;
 #pragma unroll
-    for (int j = 0; j < F; ++j) {
-      const int c0 = x.cbase + j * 16;
+    for (int jg = 0; jg < 4 * G; ++jg) {
+      const int j = jg >> 2, g = jg & 3;
+      const int c0 = x.cbase + j * 32 + g * 8;
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] * x.alpha;
+      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * x.alpha;
       if constexpr (EPI == EPI_STORE32) {
         if (r < x.M) {
 #pragma unroll
@@ -160,15 +165,32 @@ __device__ __forceinline__ void epilogue(const floatx4 (&acc)[F][F], const EpiCt
   }
 }
 
-// Block tile BT x BT (BT = 128 or 256), 4 waves in 2 x 2, each wave a
-// (BT/2) x (BT/2) sub-tile of F x F fragments of 16 x 16 (F = BT / 32).
-// BT = 256: 128 KFLOP per KB loaded from L2 per block and 64 FLOP per LDS
-// byte per wave; one block per CU (144 KB of LDS, accumulators in AGPRs).
+// Block tile BT x BT, 4 waves in 2 x 2, each wave (BT/2) x (BT/2) made of
+// G x G blocks of 32 x 32 (G = BT / 64), v_mfma_f32_32x32x16_f16.
+// K advances in stages of 32 through an NS-deep LDS ring filled by
+// global_load_lds_dwordx4 (one wave-instruction = 16 rows of 64 B), issued
+// NS - 1 stages ahead.  Chunk c (0..3) of row r is stored at position
+// c ^ ((r >> 2) & 3) so 16-row fragment reads hit distinct banks.
+constexpr int kSK = 32;                 // K per stage
+__device__ __forceinline__ int swz4(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+// s_waitcnt with vmcnt = v, other counters untouched (gfx9 encoding)
+#define WAIT_VMCNT(v) __builtin_amdgcn_s_waitcnt(((v) & 15) | (7 << 4) | (15 << 8) | (((v) >> 4) << 14))
+
 template <int BT>
 __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kernel(GemmArgs args) {
-  constexpr int F = BT / 32;
-  __shared__ half_t sA[2][BT * kLdsStride];
-  __shared__ half_t sB[2][BT * kLdsStride];
+  constexpr int G = BT / 64;
+  constexpr int NS = 4;                      // LDS ring depth
+  constexpr int LPW = BT / 16 / 4;           // wave-loads per operand per stage
+  __shared__ half_t sA0[BT * kSK], sA1[BT * kSK], sA2[BT * kSK], sA3[BT * kSK];
+  __shared__ half_t sB0[BT * kSK], sB1[BT * kSK], sB2[BT * kSK], sB3[BT * kSK];
+  auto bufA = [&](auto bc) -> half_t* {
+    constexpr int b = decltype(bc)::value;
+    if constexpr (b == 0) return sA0; else if constexpr (b == 1) return sA1; else if constexpr (b == 2) return sA2; else return sA3;
+  };
+  auto bufB = [&](auto bc) -> half_t* {
+    constexpr int b = decltype(bc)::value;
+    if constexpr (b == 0) return sB0; else if constexpr (b == 1) return sB1; else if constexpr (b == 2) return sB2; else return sB3;
+  };
 
   const TileRef tr = args.tiles[args.tile_begin + blockIdx.x];
   const GemmProb& P = args.probs[args.prob_base + tr.prob];
@@ -185,68 +207,112 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid >> 3;          // 0..31
-  const int lk = (tid & 7) * 8;       // 0..56
 
-  const int kt_per_seg = Kp / kBK;
-  const int niter = (args.split_in ? 3 : 1) * kt_per_seg;
+  const int st_per_seg = Kp / kSK;
+  const int nst = (args.split_in ? 3 : 1) * st_per_seg;
 
-  half8_t ra[F], rb[F];
-  auto gload = [&](int it) {
-    const int seg = it / kt_per_seg;
-    const int k0 = (it - seg * kt_per_seg) * kBK + lk;
+  const int lr = lane >> 2, lp = lane & 3;   // lane -> row 16h + lr, position lp
+  auto gload = [&](int st, auto bc) {
+    half_t* dA = bufA(bc);
+    half_t* dB = bufB(bc);
+    const int seg = st / st_per_seg;
+    const int k0 = (st - seg * st_per_seg) * kSK;
     const int offA = (seg == 2 ? Kp : 0) + k0;
     const int offB = (seg == 1 ? Kp : 0) + k0;
 #pragma unroll
-    for (int p = 0; p < F; ++p) {
-      ra[p] = *reinterpret_cast<const half8_t*>(A + static_cast<size_t>(lrow + 32 * p) * lda + offA);
-      rb[p] = *reinterpret_cast<const half8_t*>(B + static_cast<size_t>(lrow + 32 * p) * ldb + offB);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < F; ++p) {
-      *reinterpret_cast<half8_t*>(&sA[buf][(lrow + 32 * p) * kLdsStride + lk]) = ra[p];
-      *reinterpret_cast<half8_t*>(&sB[buf][(lrow + 32 * p) * kLdsStride + lk]) = rb[p];
+    for (int q = 0; q < LPW; ++q) {
+      const int h = wave + 4 * q;
+      const int row = 16 * h + lr;
+      const int c = swz4(row, lp);
+      const half_t* ga = A + static_cast<size_t>(row) * lda + offA + c * 8;
+      const half_t* gb = B + static_cast<size_t>(row) * ldb + offB + c * 8;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ga,
+                                       (__attribute__((address_space(3))) void*)&dA[h * 16 * kSK], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gb,
+                                       (__attribute__((address_space(3))) void*)&dB[h * 16 * kSK], 16, 0, 0);
     }
   };
 
-  floatx4 acc[F][F];
+  floatx16 acc[G][G];
 #pragma unroll
-  for (int i = 0; i < F; ++i)
+  for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int j = 0; j < F; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < G; ++j) acc[i][j] = floatx16{};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  int cur = 0;
-  const int frow = lane & 15;
-  const int fk = (lane >> 4) * 8;
+  const int frow = lane & 31;
+  const int fch = lane >> 5;
   const int arow = wm * (BT / 2) + frow;
   const int brow = wn * (BT / 2) + frow;
-  for (int it = 0; it < niter; ++it) {
-    if (it + 1 < niter) gload(it + 1);
+  auto lfrag = [&](half8_t (&fa)[G], half8_t (&fb)[G], auto bc, int s) {
+    const half_t* lA = bufA(bc);
+    const half_t* lB = bufB(bc);
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      half8_t fb[F];
-#pragma unroll
-      for (int j = 0; j < F; ++j)
-        fb[j] = *reinterpret_cast<const half8_t*>(&sB[cur][(brow + j * 16) * kLdsStride + kk + fk]);
-#pragma unroll
-      for (int i = 0; i < F; ++i) {
-        const half8_t fa = *reinterpret_cast<const half8_t*>(&sA[cur][(arow + i * 16) * kLdsStride + kk + fk]);
-        // Operands swapped (B rows as the MFMA's A) so that each lane ends with
-        // four consecutive output columns of one output row.
-#pragma unroll
-        for (int j = 0; j < F; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa, acc[i][j], 0, 0, 0);
-      }
+    for (int j = 0; j < G; ++j) {
+      const int r = brow + 32 * j;
+      fb[j] = *reinterpret_cast<const half8_t*>(&lB[r * kSK + swz4(r, 2 * s + fch) * 8]);
     }
-    if (it + 1 < niter) sstore(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int r = arow + 32 * i;
+      fa[i] = *reinterpret_cast<const half8_t*>(&lA[r * kSK + swz4(r, 2 * s + fch) * 8]);
+    }
+  };
+  auto mma = [&](const half8_t (&fa)[G], const half8_t (&fb)[G]) {
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // Stage st's fragments are in registers F[st & 1] when body st starts.
+  // Body st: wait for this wave's copies of stage st+1, barrier (all waves'
+  // copies of st+1 visible, all waves done reading slot st % 4), refill slot
+  // st % 4 with stage st+4, then read stage st+1's fragments while the MFMAs
+  // of stage st run.
+  gload(0, I0{});
+  gload(1 < nst ? 1 : nst - 1, I1{});
+  gload(2 < nst ? 2 : nst - 1, I2{});
+  gload(3 < nst ? 3 : nst - 1, I3{});
+  half8_t fa[2][2][G], fb[2][2][G];   // [register set][k16 step][fragment]
+  WAIT_VMCNT(3 * 2 * LPW);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  lfrag(fa[0][0], fb[0][0], I0{}, 0);
+  lfrag(fa[0][1], fb[0][1], I0{}, 1);
+  auto body = [&](int st, auto rc, auto sc, auto nc) {
+    constexpr int R = decltype(rc)::value;      // register set of stage st
+    WAIT_VMCNT(2 * 2 * LPW);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int ld = st + 4;
+    gload(ld < nst ? ld : nst - 1, sc);           // slot st % 4
+    lfrag(fa[R ^ 1][0], fb[R ^ 1][0], nc, 0);     // stage st+1 from slot (st+1) % 4
+    lfrag(fa[R ^ 1][1], fb[R ^ 1][1], nc, 1);
+    mma(fa[R][0], fb[R][0]);
+    mma(fa[R][1], fb[R][1]);
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPW, 0);
+#pragma unroll
+    for (int q = 0; q < 4 * G; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * G * G / (4 * G), 0);
+    }
+    // stage st+1's fragments complete before the next body's MFMAs
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  };
+  for (int st = 0; st < nst; st += 4) {
+    body(st, I0{}, I0{}, I1{});
+    body(st + 1, I1{}, I1{}, I2{});
+    body(st + 2, I0{}, I2{}, I3{});
+    body(st + 3, I1{}, I3{}, I0{});
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---------------- epilogue ----------------
   EpiCtx ctx;
@@ -256,7 +322,7 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   ctx.ti = ti;
   ctx.tj = tj;
   ctx.rbase = ti * BT + wm * (BT / 2) + frow;
-  ctx.cbase = tj * BT + wn * (BT / 2) + (lane >> 4) * 4;
+  ctx.cbase = tj * BT + wn * (BT / 2) + fch * 4;
   ctx.write_lo = args.write_lo != 0;
   ctx.out32 = P.out32.kind != REF_NONE ? reinterpret_cast<float*>(resolve(P.out32, args.ws, args.user)) : nullptr;
   ctx.out16 = P.out16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16, args.ws, args.user)) : nullptr;
@@ -276,13 +342,13 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   ctx.lr = args.lr;
   ctx.decay = args.decay;
   switch (P.epi) {
-    case EPI_STORE32: epilogue<EPI_STORE32, F>(acc, ctx); break;
-    case EPI_SYRK: epilogue<EPI_SYRK, F>(acc, ctx); break;
-    case EPI_NS_T: epilogue<EPI_NS_T, F>(acc, ctx); break;
-    case EPI_NS_Y1: epilogue<EPI_NS_Y1, F>(acc, ctx); break;
-    case EPI_STORE16: epilogue<EPI_STORE16, F>(acc, ctx); break;
-    case EPI_NS_FINAL: epilogue<EPI_NS_FINAL, F>(acc, ctx); break;
-    default: epilogue<EPI_UPDATE, F>(acc, ctx); break;
+    case EPI_STORE32: epilogue<EPI_STORE32, G>(acc, ctx); break;
+    case EPI_SYRK: epilogue<EPI_SYRK, G>(acc, ctx); break;
+    case EPI_NS_T: epilogue<EPI_NS_T, G>(acc, ctx); break;
+    case EPI_NS_Y1: epilogue<EPI_NS_Y1, G>(acc, ctx); break;
+    case EPI_STORE16: epilogue<EPI_STORE16, G>(acc, ctx); break;
+    case EPI_NS_FINAL: epilogue<EPI_NS_FINAL, G>(acc, ctx); break;
+    default: epilogue<EPI_UPDATE, G>(acc, ctx); break;
   }
 }
 
