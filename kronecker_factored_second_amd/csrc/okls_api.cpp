@@ -384,7 +384,7 @@ struct Planner {
     int kind; Ref src; int src_ld; Ref src2; int g_bf16; int write_m; int transpose;
     int rows, cols, dst_rows_p, dst_cols_p; Ref dst; int dst_ld; int dst_lo;
     std::pair<int, int> parts; int scale_mode; int scale_slot;
-    int cinv_slot, rho_slot, sqrtc_slot, p16_slot; int write_lo; float damp;
+    int cinv_slot, rho_slot, sqrtc_slot, p16_slot; int write_lo; float damp; int sym_read;
   };
   CastSpec cast_spec() {
     CastSpec c{};
@@ -408,7 +408,7 @@ struct Planner {
       j.dst_lo = s.dst_lo; j.part_begin = s.parts.first; j.part_count = s.parts.second;
       j.scale_mode = s.scale_mode; j.scale_slot = s.scale_slot; j.cinv_slot = s.cinv_slot;
       j.rho_slot = s.rho_slot; j.sqrtc_slot = s.sqrtc_slot; j.p16_slot = s.p16_slot;
-      j.p16_static = sZ; j.write_lo = s.write_lo; j.damp = s.damp;
+      j.p16_static = sZ; j.write_lo = s.write_lo; j.damp = s.damp; j.sym_read = s.sym_read;
       j.tiles_x = s.dst_cols_p / kCastTile;
       j.blk_begin = blk;
       blk += j.tiles_x * (s.dst_rows_p / kCastTile);
@@ -464,6 +464,7 @@ struct Planner {
       y.p16_slot = (final_mode == 0) ? F.s_p16 : -1;
       y.write_lo = ks > 0;
       y.damp = damping(F.d);
+      y.sym_read = chain == 1;      // the second chain roots a computed square root
       cs.push_back(y);
       CastSpec z = y;
       z.kind = CA_NS_Z1; z.dst = ws_ref(F.Z[1]); z.scale_slot = SL_Z;
@@ -481,6 +482,7 @@ struct Planner {
         p.A = p.B = ws_ref(F.Y[0]); p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp; p.Mp = p.Np = F.dp;
         p.epi = EPI_NS_Y1; p.aux = src[f]; p.ldaux = F.d; p.cslot = chain == 0 ? F.s_cinv : F.s_cinv2;
         p.c2 = damping(F.d) / (1.0f + damping(F.d));
+        p.aux_sym = chain == 1;
         p.out16 = ws_ref(F.Y[1]); p.out16T = ws_ref(F.YT[1]); p.ld16 = F.ld; p.lo16 = F.dp; p.s_out = SL_Y;
         p.sA = p.sB = SL_Y;
         ps.push_back(p);

@@ -80,7 +80,7 @@ struct EpiCtx {
   half_t* out16T;
   const float* aux;
   float s_out, cval;
-  int ld32, ld16, lo16, ldaux;
+  int ld32, ld16, lo16, ldaux, aux_sym;
   float c0, c1, c2, ka, kb, lr, decay;
 };
 
@@ -142,8 +142,8 @@ __device__ __forceinline__ void epilogue(const floatx16 (&acc)[G][G], const EpiC
             if constexpr (EPI == EPI_NS_T) {
               t = (r == c ? x.ka : 0.0f) + x.kb * v[e];
             } else if constexpr (EPI == EPI_NS_Y1) {
-              const float sym = 0.5f * (x.aux[static_cast<size_t>(r) * x.ldaux + c] +
-                                        x.aux[static_cast<size_t>(c) * x.ldaux + r]);
+              const float a0 = x.aux[static_cast<size_t>(r) * x.ldaux + c];
+              const float sym = x.aux_sym ? 0.5f * (a0 + x.aux[static_cast<size_t>(c) * x.ldaux + r]) : a0;
               t = x.ka * (sym * x.cval + (r == c ? x.c2 : 0.0f)) + x.kb * v[e];
             } else {  // EPI_STORE16, EPI_NS_FINAL
               t = v[e];
@@ -334,6 +334,7 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   ctx.ld16 = P.ld16;
   ctx.lo16 = P.lo16;
   ctx.ldaux = P.ldaux;
+  ctx.aux_sym = P.aux_sym;
   ctx.c0 = P.c0;
   ctx.c1 = P.c1;
   ctx.c2 = P.c2;
@@ -408,23 +409,49 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
   const int r1 = min(J.rows, r0 + J.rows_per_blk);
   const char* src = resolve(J.src, a.ws, a.user);
   const float* m = J.kind == ST_NESTEROV ? reinterpret_cast<const float*>(resolve(J.src2, a.ws, a.user)) : nullptr;
+  const bool bf = J.kind == ST_BF16 || (J.kind == ST_NESTEROV && J.g_bf16);
   float amax = 0.0f, ss = 0.0f;
-  for (int r = r0; r < r1; ++r) {
-    for (int c = threadIdx.x; c < J.cols; c += kStatThreads) {
-      const size_t o = static_cast<size_t>(r) * J.src_ld + c;
-      float x;
-      if (J.kind == ST_F32) {
-        x = reinterpret_cast<const float*>(src)[o];
-      } else if (J.kind == ST_BF16) {
-        x = bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]);
+  auto acc1 = [&](float x) {
+    const float ax = fabsf(x);
+    amax = (ax > amax || ax != ax) ? ax : amax;   // NaN propagates
+    ss += x * x;
+  };
+  auto value = [&](size_t o, float raw) {
+    return J.kind == ST_NESTEROV ? nesterov_value(m[o], raw, a.beta1, a.s_t) : raw;
+  };
+  // rows are contiguous when src_ld == cols: one flat range, 4 elements per
+  // thread and iteration (16-byte fp32 / 8-byte bf16 loads when aligned)
+  const size_t e0 = static_cast<size_t>(r0) * J.src_ld, e1 = static_cast<size_t>(r1) * J.src_ld;
+  const bool flat = J.src_ld == J.cols && (e0 & 3) == 0 &&
+                    (reinterpret_cast<uintptr_t>(src) & (bf ? 7 : 15)) == 0 &&
+                    (m == nullptr || (reinterpret_cast<uintptr_t>(m) & 15) == 0);
+  if (flat) {
+    const size_t n4 = (e1 - e0) / 4;
+    for (size_t q = threadIdx.x; q < n4; q += kStatThreads) {
+      const size_t o = e0 + 4 * q;
+      float g[4];
+      if (bf) {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + o);
+        g[0] = __uint_as_float(u.x << 16); g[1] = __uint_as_float(u.x & 0xffff0000u);
+        g[2] = __uint_as_float(u.y << 16); g[3] = __uint_as_float(u.y & 0xffff0000u);
       } else {
-        const float g = J.g_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o])
-                                 : reinterpret_cast<const float*>(src)[o];
-        x = nesterov_value(m[o], g, a.beta1, a.s_t);
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + o);
+        g[0] = f.x; g[1] = f.y; g[2] = f.z; g[3] = f.w;
       }
-      const float ax = fabsf(x);
-      amax = (ax > amax || ax != ax) ? ax : amax;   // NaN propagates
-      ss += x * x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc1(value(o + e, g[e]));
+    }
+    for (size_t o = e0 + 4 * n4 + threadIdx.x; o < e1; o += kStatThreads) {
+      const float raw = bf ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]) : reinterpret_cast<const float*>(src)[o];
+      acc1(value(o, raw));
+    }
+  } else {
+    for (int r = r0; r < r1; ++r) {
+      for (int c = threadIdx.x; c < J.cols; c += kStatThreads) {
+        const size_t o = static_cast<size_t>(r) * J.src_ld + c;
+        const float raw = bf ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]) : reinterpret_cast<const float*>(src)[o];
+        acc1(value(o, raw));
+      }
     }
   }
   block_reduce2<kStatThreads>(amax, ss, sh);
@@ -491,6 +518,61 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
   half_t* dst = reinterpret_cast<half_t*>(resolve(J.dst, a.ws, a.user));
   const bool write_lo = J.write_lo != 0;
 
+  const bool src_bf = J.kind == CA_BF16 || (J.kind == CA_NESTEROV && J.g_bf16);
+  // four consecutive source elements (r, c..c+3), all in range, as one
+  // 16-byte (fp32) or 8-byte (bf16) load when the row segment is aligned
+  auto load4 = [&](int r, int c, float (&x)[4]) {
+    const size_t o = static_cast<size_t>(r) * J.src_ld + c;
+    if (J.kind == CA_F32 && (o & 3) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+      const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + o);
+      x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+      return true;
+    }
+    if (J.kind == CA_BF16 && (o & 3) == 0 && (reinterpret_cast<uintptr_t>(src) & 7) == 0) {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + o);
+      x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+      x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+      return true;
+    }
+    if (J.kind == CA_NESTEROV && (o & 3) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+      const char* g = resolve(J.src2, a.ws, a.user);
+      float gv[4];
+      if (J.g_bf16) {
+        if (reinterpret_cast<uintptr_t>(g) & 7) return false;
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g) + o);
+        gv[0] = __uint_as_float(u.x << 16); gv[1] = __uint_as_float(u.x & 0xffff0000u);
+        gv[2] = __uint_as_float(u.y << 16); gv[3] = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+        if (reinterpret_cast<uintptr_t>(g) & 15) return false;
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g) + o);
+        gv[0] = f.x; gv[1] = f.y; gv[2] = f.z; gv[3] = f.w;
+      }
+      float4* mp = reinterpret_cast<float4*>(const_cast<float*>(reinterpret_cast<const float*>(src)) + o);
+      const float4 mo = *mp;
+      const float mov[4] = {mo.x, mo.y, mo.z, mo.w};
+      float mn[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mn[e] = a.beta1 * mov[e] + (1.0f - a.beta1) * gv[e];
+        x[e] = a.s_t * (a.beta1 * mn[e] + (1.0f - a.beta1) * gv[e]);
+      }
+      if (J.write_m) *mp = float4{mn[0], mn[1], mn[2], mn[3]};
+      return true;
+    }
+    if ((J.kind == CA_NS_Y0 || J.kind == CA_NS_Z1) && !J.sym_read && (o & 3) == 0 &&
+        (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+      const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + o);
+      const float sv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y0 = sv[e] * cinv + (r == c + e ? ddiag : 0.0f);
+        x[e] = J.kind == CA_NS_Y0 ? y0 : (r == c + e ? a.ka : 0.0f) + a.kb * y0;
+      }
+      return true;
+    }
+    return false;
+  };
+  (void)src_bf;
   auto load_src = [&](int r, int c) -> float {   // source coordinates, in range
     const size_t o = static_cast<size_t>(r) * J.src_ld + c;
     switch (J.kind) {
@@ -511,7 +593,7 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
         // which are stored exactly symmetric; the Shampoo second chain starts
         // from a computed square root)
         const float* s = reinterpret_cast<const float*>(src);
-        const float sym = 0.5f * (s[o] + s[static_cast<size_t>(c) * J.src_ld + r]);
+        const float sym = J.sym_read ? 0.5f * (s[o] + s[static_cast<size_t>(c) * J.src_ld + r]) : s[o];
         const float y0 = sym * cinv + (r == c ? ddiag : 0.0f);
         return J.kind == CA_NS_Y0 ? y0 : (r == c ? a.ka : 0.0f) + a.kb * y0;
       }
@@ -527,10 +609,10 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
       const int r = dr0 + rr + 16 * p;
       if (r >= J.dst_rows_p) continue;
       float x[4];
+      const int c = dc0 + cq;
+      if (!(r < J.rows && c + 3 < J.cols && load4(r, c, x))) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = dc0 + cq + e;
-        x[e] = (r < J.rows && c < J.cols) ? load_src(r, c) : 0.0f;
+        for (int e = 0; e < 4; ++e) x[e] = (r < J.rows && c + e < J.cols) ? load_src(r, c + e) : 0.0f;
       }
       if (dc0 + cq < J.dst_cols_p)
         store16(dst + static_cast<size_t>(r) * J.dst_ld + dc0 + cq, J.dst_lo, write_lo, x, scale);
@@ -540,11 +622,14 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int sr = dc0 + rr + 16 * p;            // source row = destination column
+      const int sc = dr0 + cq;                     // source column = destination row
+      float x[4];
+      if (!(sr < J.rows && sc + 3 < J.cols && load4(sr, sc, x))) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int sc = dr0 + cq + e;               // source column = destination row
-        tile[rr + 16 * p][cq + e] = (sr < J.rows && sc < J.cols) ? load_src(sr, sc) : 0.0f;
+        for (int e = 0; e < 4; ++e) x[e] = (sr < J.rows && sc + e < J.cols) ? load_src(sr, sc + e) : 0.0f;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[rr + 16 * p][cq + e] = x[e];
     }
     __syncthreads();
 #pragma unroll

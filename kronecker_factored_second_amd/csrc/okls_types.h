@@ -63,6 +63,7 @@ struct GemmProb {
   Ref out16; int32_t ld16; int32_t lo16;   // lo part at +lo16 halves within a row
   Ref out16T;              // optional transposed copy (same ld16 / lo16; square problems)
   Ref aux; int32_t ldaux;
+  int32_t aux_sym;         // EPI_NS_Y1: 1 = read (aux + aux^T) / 2
   int32_t sA, sB;          // scale slots of the operands (alpha = 1/(scal[sA]*scal[sB]))
   int32_t s_out;           // scale slot for fp16 output
   int32_t cslot;           // per-problem device scalar used by the epilogue
@@ -149,6 +150,7 @@ struct CastJob {
   int32_t p16_slot;        // CA_NS_*: writes s_Z*sqrt(c) here (if >= 0): scale of the root's fp16 copy
   float p16_static;        // s_Z
   float damp;              // CA_NS_*: delta; the chain roots (S + delta c I) / (c (1 + delta))
+  int32_t sym_read;        // CA_NS_*: 1 = read (S + S^T) / 2 (source not exactly symmetric)
   int32_t tiles_x;         // tiles along destination columns
   int32_t blk_begin;
   int32_t write_lo;
