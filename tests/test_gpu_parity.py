@@ -189,3 +189,41 @@ def test_check_finite_flags_nan():
     assert opt.check_finite()
     opt.state[0]["Sa"][0, 3, 3] = float("nan")
     assert not opt.check_finite()
+
+
+@pytest.mark.parametrize("precision,nu,tol", [("fp32", 1e-6, 1e-4), ("fp16", 1e-4, 2e-2)])
+def test_well_conditioned_state_matches_exact_root(precision, nu, tol):
+    """From a factor state with condition number 100 (set through the state
+    tensors) and a small gradient, the new factors stay well conditioned and
+    the GPU's Newton-Schulz root matches the exact eigh root of the oracle's
+    factor (the iteration converges inside its design interval); with a
+    small damping the shift is below the tolerance."""
+    torch = pytest.importorskip("torch")
+    m, n = 192, 320
+    rng = np.random.default_rng(21)
+
+    def spd(d, kappa):
+        Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+        lam = np.logspace(0, -np.log10(kappa), d) * 1e-3
+        return (Q * lam) @ Q.T
+
+    opt, params = H.make([(m, n, 1)], precision=precision, ns_damping=nu)
+    Sa, Sb = spd(m, 100.0), spd(n, 100.0)
+    Pa, _ = O.inv_root_exact(Sa, 2)
+    Pb, _ = O.inv_root_exact(Sb, 2)
+    st = opt.state[0]
+    for k, v in (("Sa", Sa), ("Sb", Sb), ("Pa", Pa), ("Pb", Pb)):
+        st[k][0].copy_(torch.tensor(v, dtype=torch.float32, device="cuda:0"))
+    params[0][0].copy_(torch.tensor(rng.standard_normal((m, n)) * 0.01, dtype=torch.float32, device="cuda:0"))
+    hp = H.hyper_of(opt)
+    rep = H.Report(f"wellcond-{precision}")
+    for t in (1, 2):
+        G = (1e-3 * rng.standard_normal((m, n))).astype(np.float32)
+        before = H.snapshot(opt, 0, 0)
+        opt.step(grads=[torch.tensor(G, device="cuda:0")[None]])
+        torch.cuda.synchronize()
+        e = H.compare_step(opt, before, None, G, hp, t, "okls", 0, 0)
+        rep.add(t=t, **e)
+        assert e["kappa_a"] < 1e3 and e["kappa_b"] < 1e3
+        assert e["P_a_exact"] < tol and e["P_b_exact"] < tol, e
+        assert e["U_exact"] < max(tol, 1e-3), e
