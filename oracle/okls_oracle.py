@@ -31,6 +31,9 @@ Parity status of each function (what pins it in the CPU test-suite):
                                  worked example and problem 14 singular values
   ns_coefficients .............. classical Newton-Schulz limit (3/2, -1/2),
                                  equioscillation, grid-search optimality
+  ns_spectral / closed form .... matrix iterations (damped, p = 2 and 4) on random SPD
+                                 factors; output within the coefficient bound of
+                                 (lambda + delta c)^{-1/2} on the design interval
   ns_inv_sqrt / ns_inv_quarter . diagonal S reduces to scalar recurrences,
                                  eigen closed form, worked example through NS,
                                  damped isotropic closed form, damped root within
@@ -236,19 +239,42 @@ def ns_inv_quarter(S: np.ndarray, coeffs, nu: float = 0.0):
     return P
 
 
-def ns_eigen_closed_form(S: np.ndarray, coeffs, p: int = 2):
-    """Exact-arithmetic output of ns_inv_sqrt through the eigen-decomposition:
-    on each eigen-direction the coupled iteration keeps Z_k Y_k = sigma_k^2 with
-    sigma_0 = sqrt(lambda / c) and sigma_{k+1} = sigma_k (a_k + b_k sigma_k^2),
-    so P = V diag(sigma_K / sqrt(lambda)) V^T.  Used as a diagnostic and a pin."""
-    lam, V = np.linalg.eigh(_sym(S))
-    c = float(np.linalg.norm(S))
-    s = np.sqrt(lam / c)
+def ns_spectral(lam: np.ndarray, coeffs, nu: float = 0.0, p: int = 2):
+    """Exact-arithmetic output of the damped coupled iteration(s) on a
+    symmetric matrix with eigenvalues `lam`, one value per eigen-direction.
+
+    One chain on S (dimension d = len(lam), c = ||S||_F = ||lam||_2,
+    delta = nu / sqrt(d), c' = c (1 + delta)) starts from y = (lam + delta c) / c'.
+    Every matrix of the iteration is a polynomial in Y_0, so in each
+    eigen-direction Z_k Y_k = sigma_k^2 with sigma_0 = sqrt(y) and
+    sigma_{k+1} = sigma_k (a_k + b_k sigma_k^2); Z_K = sigma_K / sqrt(y) and
+    Y_K = sigma_K sqrt(y).  Hence the chain returns
+        P = Z_K / sqrt(c') = sigma_K / sqrt(lam + delta c)
+        R = Y_K sqrt(c')  = sigma_K sqrt(lam + delta c).
+    p = 2 returns P; p = 4 (R8) runs a second chain on R's eigenvalues and
+    returns its P."""
+    lam = np.asarray(lam, dtype=np.float64)
+    d = lam.size
+    delta = nu / math.sqrt(d)
+    c = float(np.linalg.norm(lam))
+    shifted = lam + delta * c
+    s = np.sqrt(shifted / (c * (1.0 + delta)))
     for a, b in coeffs:
         s = s * (a + b * s * s)
     if p == 2:
-        return (V * (s / np.sqrt(lam))) @ V.T
-    raise ValueError("closed form only for p=2")
+        return s / np.sqrt(shifted)
+    if p == 4:
+        return ns_spectral(s * np.sqrt(shifted), coeffs, nu, 2)
+    raise ValueError("p must be 2 or 4")
+
+
+def ns_eigen_closed_form(S: np.ndarray, coeffs, p: int = 2, nu: float = 0.0):
+    """Exact-arithmetic output of ns_inv_sqrt (p = 2) or ns_inv_quarter (p = 4)
+    through the eigendecomposition: P = V diag(ns_spectral(lambda)) V^T.
+    Used as a diagnostic and a pin, and where the matrix iteration in fp64
+    would take too long."""
+    lam, V = np.linalg.eigh(_sym(S))
+    return (V * ns_spectral(lam, coeffs, nu, p)) @ V.T
 
 
 # ---------------------------------------------------------------------------

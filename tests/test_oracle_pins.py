@@ -258,6 +258,39 @@ def test_ns_damped_matches_shifted_exact_root():
         assert O.rel_frob(R, Rd) < 2 * efin
 
 
+@pytest.mark.parametrize("p,nu", [(2, 5e-3), (2, 2e-3), (4, 5e-3), (4, 0.0)])
+def test_ns_spectral_closed_form_matches_matrix_iteration(p, nu):
+    """The per-eigenvalue closed form of the damped iteration equals the fp64
+    matrix iteration (one chain for p = 2, two chained on sym(R) for p = 4)
+    on random SPD factors up to rounding."""
+    rng = np.random.default_rng(31 + p)
+    coeffs, _ = O.ns_coefficients(1e-3, 10)
+    for d, kappa in ((40, 1e2), (72, 1e4)):
+        S = _spd(rng, d, kappa) * 2.3e-5
+        P_iter = O.ns_inv_sqrt(S, coeffs, nu)[0] if p == 2 else O.ns_inv_quarter(S, coeffs, nu)
+        P_cf = O.ns_eigen_closed_form(S, coeffs, p, nu)
+        assert O.rel_frob(P_iter, P_cf) < 1e-10, (d, kappa)
+
+
+def test_ns_spectral_within_coefficient_bound_of_shifted_root():
+    """Inside the design interval (sqrt(y) >= floor) the closed form is within
+    the final minimax error of (lambda + delta c)^{-1/2}, the eigh root of the
+    explicitly shifted factor; p = 4 composes two such maps."""
+    coeffs, efin = O.ns_coefficients(1e-3, 10)
+    rng = np.random.default_rng(5)
+    lam = np.exp(rng.uniform(np.log(1e-4), 0.0, size=500))
+    nu = 5e-3
+    shift = nu / math.sqrt(lam.size) * np.linalg.norm(lam)
+    f = O.ns_spectral(lam, coeffs, nu, 2)
+    np.testing.assert_array_less(np.abs(f * np.sqrt(lam + shift) - 1.0), efin * (1 + 1e-9))
+    # p = 4: the second chain roots R = (S + shift)^{1/2} shifted by its own
+    # nu / sqrt(d) ||R||_F; each chain contributes at most efin
+    r = np.sqrt(lam + shift)
+    shift2 = nu / math.sqrt(lam.size) * np.linalg.norm(r)
+    f4 = O.ns_spectral(lam, coeffs, nu, 4)
+    np.testing.assert_array_less(np.abs(f4 * np.sqrt(r + shift2) - 1.0), 2.5 * efin)
+
+
 def test_ns_damped_isotropic():
     """S = s I: ||S||_F = s sqrt(d), so the shifted matrix is s (1 + nu) I."""
     coeffs, efin = O.ns_coefficients(1e-3, 10)
