@@ -29,6 +29,16 @@ PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
+KERNEL_SRC = os.path.join(ROOT, "kronecker_factored_second_amd", "csrc", "okls_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_kernel_c2_fp16_hbm_traffic.txt")
+COPY_PROBE_BYTES = 1 << 30
+
+
+def kernel_source_hash():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -38,7 +48,84 @@ def parse():
     p.add_argument("--precision", default="fp16", choices=["fp16", "fp32"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 10 times (HBM counter calibration)")
+    p.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV_DIR", "WRITE_CSV_DIR", "COMMANDS"),
+                   help="write the GEMM's HBM traffic summary from two rocprofv3 --pmc runs")
     return p.parse_args()
+
+
+def copy_probe():
+    """A plain copy of COPY_PROBE_BYTES: FETCH_SIZE and WRITE_SIZE of this
+    kernel calibrate the counters (each should read the copy's size)."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 10}), flush=True)
+
+
+def _counter_rows(d, counter):
+    """{kernel name: [values]} of one counter from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir, commands):
+    """HBM bytes per gemm_nt_kernel launch from FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), each scaled by the factor that makes the plain copy's
+    counter equal its known size."""
+    fetch, write = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+
+    def pick(rows, key):
+        vals = [v for k, vs in rows.items() if key(k) for v in vs]
+        return sum(vals) / len(vals), len(vals)
+
+    is_copy = lambda k: "copy" in k.lower() and "okls" not in k
+    is_gemm = lambda k: "gemm_nt_kernel" in k
+    cf, ncf = pick(fetch, is_copy)
+    cw, ncw = pick(write, is_copy)
+    gf, ngf = pick(fetch, is_gemm)
+    gw, ngw = pick(write, is_gemm)
+    kf = COPY_PROBE_BYTES / (cf * 1024.0)
+    kw = COPY_PROBE_BYTES / (cw * 1024.0)
+    traffic = gf * 1024.0 * kf + gw * 1024.0 * kw
+    lines = [
+        "# HBM traffic of gemm_nt_kernel (both block tiles), one d=1024 transformer block, fp16 path",
+        f"# kernel_source_sha256_16 {kernel_source_hash()}",
+        "# commands (repository root as $REPO; cd /tmp first):",
+        *[f"#   {c}" for c in commands.split(";")],
+        f"copy_probe_bytes {COPY_PROBE_BYTES}",
+        f"copy_fetch_kib_avg {cf:.1f} over {ncf} dispatches -> fetch factor {kf:.4f}",
+        f"copy_write_kib_avg {cw:.1f} over {ncw} dispatches -> write factor {kw:.4f}",
+        f"gemm_fetch_kib_avg {gf:.1f} over {ngf} dispatches",
+        f"gemm_write_kib_avg {gw:.1f} over {ngw} dispatches",
+        f"gemm_hbm_bytes_per_launch {traffic:.6e}",
+    ]
+    open(TRAFFIC_FILE, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    when it is missing or was taken on another version of the kernels."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    if f"kernel_source_sha256_16 {kernel_source_hash()}" not in txt:
+        return None
+    for line in txt.splitlines():
+        if line.startswith("gemm_hbm_bytes_per_launch"):
+            return float(line.split()[1])
+    return None
 
 
 def cpu_baseline(w, budget_s):
@@ -76,10 +163,16 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the preconditioner step runs on a single MI355X in this build; "
               "--gpus above 1 is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
     import torch
     from kronecker_factored_second_amd import okls, workloads as WL
 
@@ -148,10 +241,17 @@ def main():
         "ns_chain": {"tflops": ns_tflops, "frac_fp16_peak": ns_tflops / PEAK_FP16_TFLOPS,
                      "ms_per_step": ns["ms"] / max(prof["steps"], 1), "launches_per_step": ns["launches"] / max(prof["steps"], 1)},
         "roofline": {"kernel": "gemm_nt_kernel", "bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS,
+                     "traffic": measured_traffic() if (args.workload == "c2" and args.precision == "fp16") else None,
                      "avg_launch_us": g_ms * 1e3 / max(g_n, 1), "launches_per_step": g_n / max(prof["steps"], 1),
                      "algorithmic_flops_per_step": g_fl / max(prof["steps"], 1)},
         "profile_ms_per_step": {k: prof[k]["ms"] / max(prof["steps"], 1) for k in okls.PROFILE_CATEGORIES},
+        "hbm_kernels": {kern: {"bound": "hbm", "achieved": prof[cat]["bytes"] / (prof[cat]["ms"] * 1e-3) / 1e9,
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": prof[cat]["bytes"] / (prof[cat]["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               "bytes_per_step": prof[cat]["bytes"] / max(prof["steps"], 1),
+                               "launches_per_step": prof[cat]["launches"] / max(prof["steps"], 1)}
+                        for kern, cat in (("stats_kernel", "stats"), ("cast_kernel", "cast")) if prof[cat]["ms"] > 0},
         "state_finite": finite,
         "host_wall_s": wall,
     }

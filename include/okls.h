@@ -157,11 +157,17 @@ int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_s
  * flops[i] is the algorithmic floating-point work of category i summed over
  * the profiled steps: 27 GEMMs of 2 d^3 per inverse square root (54 for the
  * Shampoo fourth root), 3 m n (m + n) for the OKLS factors (m n (m + n) in
- * Shampoo mode), 2 m n (m + n) for the whitening. */
+ * Shampoo mode), 2 m n (m + n) for the whitening.  bytes[i] is the
+ * algorithmic memory traffic of the statistics and cast categories over the
+ * profiled steps: every job reads its source once (4 bytes per fp32 element,
+ * 2 per bf16; the momentum jobs read M and G and write M') and writes its
+ * fp16 output once (2 bytes per element, 4 with the low halves); zero for the
+ * GEMM categories. */
 #define OKLS_PROFILE_CATEGORIES 5
 typedef struct {
     double ms[OKLS_PROFILE_CATEGORIES];
     double flops[OKLS_PROFILE_CATEGORIES];
+    double bytes[OKLS_PROFILE_CATEGORIES];
     int64_t launches[OKLS_PROFILE_CATEGORIES];
     int64_t steps;
 } okls_profile_stats;

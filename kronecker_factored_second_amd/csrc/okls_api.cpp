@@ -138,6 +138,7 @@ struct okls_handle {
   std::vector<std::vector<LaunchRec>> chunks;
   std::vector<double> na, nb;
   double step_flops[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+  double step_bytes[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
   // profiling
   bool prof = false;
   std::vector<hipEvent_t> events;           // pool
@@ -321,6 +322,7 @@ struct Planner {
 
   int gemm_cat = CAT_NS;   // category of the GEMM launches being planned
   double step_flops[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+  double step_bytes[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
 
   void add_gemm(std::vector<LaunchRec>& L, const std::vector<GemmProb>& ps, bool upper, int split_in,
                 int write_lo, float ka = 0.f, float kb = 0.f) {
@@ -365,6 +367,8 @@ struct Planner {
       j.kind = s.kind; j.src = s.src; j.src_ld = s.ld; j.src2 = s.src2; j.g_bf16 = s.g_bf16;
       j.rows = s.rows; j.cols = s.cols;
       j.rows_per_blk = std::max(1, std::min(s.rows, 32768 / std::max(1, s.cols)));
+      const double src_b = s.kind == ST_F32 ? 4.0 : s.kind == ST_BF16 ? 2.0 : 4.0 + (s.g_bf16 ? 2.0 : 4.0);
+      step_bytes[CAT_STAT] += src_b * s.rows * s.cols;
       const int nb = (s.rows + j.rows_per_blk - 1) / j.rows_per_blk;
       j.part_begin = part;
       j.blk_begin = blk;
@@ -410,6 +414,10 @@ struct Planner {
       j.rho_slot = s.rho_slot; j.sqrtc_slot = s.sqrtc_slot; j.p16_slot = s.p16_slot;
       j.p16_static = sZ; j.write_lo = s.write_lo; j.damp = s.damp; j.sym_read = s.sym_read;
       j.tiles_x = s.dst_cols_p / kCastTile;
+      const double src_b = s.kind == CA_BF16 ? 2.0
+                         : s.kind == CA_NESTEROV ? 4.0 + (s.g_bf16 ? 2.0 : 4.0) + (s.write_m ? 4.0 : 0.0)
+                         : 4.0;
+      step_bytes[CAT_CAST] += (src_b + (s.write_lo ? 4.0 : 2.0)) * s.rows * s.cols;
       j.blk_begin = blk;
       blk += j.tiles_x * (s.dst_rows_p / kCastTile);
       cast_jobs.push_back(j);
@@ -1028,7 +1036,10 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->chunks = P.chunks;
   h->na = P.na;
   h->nb = P.nb;
-  for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) h->step_flops[i] = P.step_flops[i];
+  for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
+    h->step_flops[i] = P.step_flops[i];
+    h->step_bytes[i] = P.step_bytes[i];
+  }
 
   std::vector<float> scal(static_cast<size_t>(P.n_slots), 1.0f);
   scal[SL_ONE] = 1.0f;
@@ -1126,7 +1137,10 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
 
   if (h->prof) {
     h->acc.steps += 1;
-    for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) h->acc.flops[i] += h->step_flops[i];
+    for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
+      h->acc.flops[i] += h->step_flops[i];
+      h->acc.bytes[i] += h->step_bytes[i];
+    }
   }
   for (const std::vector<LaunchRec>& L : h->chunks) {
     for (const LaunchRec& r : L) {

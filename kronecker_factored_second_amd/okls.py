@@ -43,8 +43,8 @@ class GroupTensors(ctypes.Structure):
 
 
 class ProfileStats(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 5), ("flops", ctypes.c_double * 5), ("launches", ctypes.c_int64 * 5),
-                ("steps", ctypes.c_int64)]
+    _fields_ = [("ms", ctypes.c_double * 5), ("flops", ctypes.c_double * 5), ("bytes", ctypes.c_double * 5),
+                ("launches", ctypes.c_int64 * 5), ("steps", ctypes.c_int64)]
 
 
 class OKLSError(RuntimeError):
@@ -147,6 +147,28 @@ def ns_coefficients(cfg: Config):
     return list(a[:k]), list(b[:k])
 
 
+def fit_chunk(cfg: Config, groups, limit: int):
+    """Largest chunk_matrices whose workspace is at most `limit` bytes, and
+    that workspace size (bisection; the size grows with the chunk)."""
+    total = sum(g[0] for g in groups)
+    saved = cfg.chunk_matrices
+    try:
+        lo, hi, best = 1, total, None
+        while lo <= hi:
+            mid = (lo + hi) // 2
+            cfg.chunk_matrices = mid
+            ws = workspace_size(cfg, groups)
+            if ws != 0 and ws <= limit:
+                best, lo = (mid, ws), mid + 1
+            else:
+                hi = mid - 1
+    finally:
+        cfg.chunk_matrices = saved
+    if best is None:
+        raise MemoryError(f"one matrix needs more workspace than the limit of {limit} bytes")
+    return best
+
+
 def status_string(st: int) -> str:
     return load().okls_status_string(st).decode()
 
@@ -196,7 +218,7 @@ def profile_enable(h, enable: bool):
 def profile_read(h) -> dict:
     st = ProfileStats()
     _check("okls_profile_read", load().okls_profile_read(h, ctypes.byref(st)))
-    return {name: {"ms": st.ms[i], "flops": st.flops[i], "launches": int(st.launches[i])}
+    return {name: {"ms": st.ms[i], "flops": st.flops[i], "bytes": st.bytes[i], "launches": int(st.launches[i])}
             for i, name in enumerate(PROFILE_CATEGORIES)} | {"steps": int(st.steps)}
 
 
@@ -212,10 +234,15 @@ class OKLS:
     (N, m, n); each parameter is one group of the C ABI).  Mirrors the README's
     optimizer interface: OKLS(params, lr, beta1, beta2, eps, weight_decay),
     .step(), .zero_grad(), .state_dict().  Gradients are read from p.grad
-    (fp32 or bf16) unless `grads` is passed to step()."""
+    (fp32 or bf16) unless `grads` is passed to step().
+
+    chunk_matrices = 0 runs every matrix in one chunk (the largest launches);
+    with workspace_limit (bytes) set and chunk_matrices = 0, the largest
+    chunk whose workspace fits the limit is chosen."""
 
     def __init__(self, params, lr=0.09434, beta1=0.9684, beta2=0.9482, eps=1e-9, weight_decay=0.0303,
-                 mode="okls", precision="fp16", grad_dtype=None, chunk_matrices=0, **cfg_overrides):
+                 mode="okls", precision="fp16", grad_dtype=None, chunk_matrices=0, workspace_limit=None,
+                 **cfg_overrides):
         import torch
         self.torch = torch
         self.params = list(params)
@@ -242,6 +269,8 @@ class OKLS:
         ws_bytes = workspace_size(self.cfg, self.groups)
         if ws_bytes == 0:
             raise OKLSError("okls_workspace_size", -1)
+        if workspace_limit is not None and chunk_matrices == 0 and ws_bytes > workspace_limit:
+            self.cfg.chunk_matrices, ws_bytes = fit_chunk(self.cfg, self.groups, int(workspace_limit))
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream(dev).cuda_stream
         self.handle = init(self.cfg, self.groups, self.workspace, self.stream)

@@ -21,7 +21,8 @@ down projections as the matrices it preconditions) at five sizes:
       fp32 gradients i.i.d. N(0, 1e-3^2); classic Shampoo mode.
   c5  one layer of 5120x5120 (x4), 13824x5120 (x2), 5120x13824 (x1);
       gradients A Z B with Z i.i.d. N(0,1), A = Q_L diag(s_A), B = diag(s_B) Q_R^T,
-      Q Haar orthogonal, s log-uniform on [1e-3, 1] (endpoints included).
+      Q dense random orthogonal (RandomOrthogonal), s log-spaced on [1e-3, 1]
+      (endpoints included) in random order.
 
 Seeds: every draw comes from numpy's default_rng(SeedSequence([cfg, group,
 matrix, t, stream])) except c1, which uses default_rng(0) in step order.
@@ -119,9 +120,91 @@ _C1 = None
 _FIXED = {}
 
 
-def _haar(rng, d):
-    Q, R = np.linalg.qr(rng.standard_normal((d, d)))
-    return Q * np.sign(np.diag(R))
+class RandomOrthogonal:
+    """A dense random orthogonal d x d matrix that is applied in O(d log d)
+    instead of being stored: two rounds of Q_r = P_r D_r C E_r, with C the
+    orthonormal DCT-II, D_r and E_r random sign diagonals and P_r a random
+    row permutation.  Every column has full support (no structure aligned
+    with the coordinate axes), so factors built from it are dense."""
+
+    def __init__(self, rng, d: int, rounds: int = 2):
+        self.d = d
+        self.stages = [(rng.permutation(d), rng.choice([-1.0, 1.0], size=d), rng.choice([-1.0, 1.0], size=d))
+                       for _ in range(rounds)]
+
+    @staticmethod
+    def _bcast(v, Y, axis):
+        return v if Y.ndim == 1 else (v[:, None] if axis == 0 else v[None, :])
+
+    def apply(self, X: np.ndarray, axis: int = 0) -> np.ndarray:
+        """Q @ X (axis 0) or X @ Q^T (axis 1, Q applied to every row) for X of
+        shape (d,), (d, k) or (k, d); works on a copy, in place."""
+        import scipy.fft
+        Y = np.array(X, dtype=np.float64, copy=True)
+        buf = np.empty_like(Y)
+        for perm, dsign, esign in self.stages:
+            Y *= self._bcast(esign, Y, axis)
+            Y = scipy.fft.dct(Y, type=2, norm="ortho", axis=axis, workers=-1, overwrite_x=True)
+            Y *= self._bcast(dsign, Y, axis)
+            np.take(Y, perm, axis=axis, out=buf)
+            Y, buf = buf, Y
+        return Y
+
+    def apply_t(self, X: np.ndarray) -> np.ndarray:
+        """Q^T @ X; works on a copy, in place."""
+        import scipy.fft
+        Y = np.array(X, dtype=np.float64, copy=True)
+        buf = np.empty_like(Y)
+        for perm, dsign, esign in reversed(self.stages):
+            buf[perm] = Y
+            Y, buf = buf, Y
+            Y *= self._bcast(dsign, Y, 0)
+            Y = scipy.fft.idct(Y, type=2, norm="ortho", axis=0, workers=-1, overwrite_x=True)
+            Y *= self._bcast(esign, Y, 0)
+        return Y
+
+    def rows(self, idx) -> np.ndarray:
+        """Rows idx of Q, shape (len(idx), d)."""
+        E = np.zeros((self.d, len(idx)))
+        E[np.asarray(idx), np.arange(len(idx))] = 1.0
+        return self.apply_t(E).T
+
+
+def symmetric_from_spectrum(Q: RandomOrthogonal, v: np.ndarray, rows=None) -> np.ndarray:
+    """Q diag(v) Q^T in fp64 (exactly symmetrised), or only its rows `rows`."""
+    v = np.asarray(v, dtype=np.float64)
+    if rows is not None:
+        R = Q.rows(rows)                      # Q[rows, :]
+        return Q.apply(R * v, axis=1)         # Q[rows] diag(v) Q^T
+    A = Q.apply(np.diag(v))                   # Q diag(v)
+    A = Q.apply(A, axis=1)                    # Q diag(v) Q^T
+    A += A.T.copy()
+    A *= 0.5
+    return A
+
+
+def spectral_factor(cfg: str, group: int, mat: int, side: int, d: int, kappa: float, lam_max: float):
+    """Known-spectrum factor state for the full-size parity checks: the
+    eigenvalues are log-uniform on [lam_max / kappa, lam_max] (both ends
+    included), the eigenvectors the columns of a RandomOrthogonal.  Returns
+    (Q, lam)."""
+    rng = _rng(cfg, group, mat, 0, 10 + side)
+    lam = lam_max * np.exp(rng.uniform(-math.log(kappa), 0.0, size=d))
+    lam[:2] = (lam_max, lam_max / kappa)
+    rng.shuffle(lam)
+    return RandomOrthogonal(rng, d), lam
+
+
+def device_filler(scale: float, shape, seed: int, dtype=None):
+    """Gaussian filler gradients generated on cuda:0 by torch's own seeded
+    generator: scale * N(0, 1).  The full-size checks use them for the
+    matrices they do not sample, so that every launch runs at its real size
+    without generating billions of values on the host."""
+    import torch
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(seed)
+    x = torch.randn(*shape, generator=g, device="cuda:0", dtype=torch.float32) * scale
+    return x if dtype is None else x.to(dtype)
 
 
 def gradient(w: Workload, group: int, mat: int, t: int) -> np.ndarray:
@@ -145,7 +228,6 @@ def gradient(w: Workload, group: int, mat: int, t: int) -> np.ndarray:
         key = (w.name, group, mat)
         if key not in _FIXED:
             fr = _rng(w.name, group, mat, 0, 1)
-            _FIXED.clear()
             _FIXED[key] = (fr.standard_normal((m, 32)), fr.standard_normal((n, 32)))
         A, B = _FIXED[key]
         r = _rng(w.name, group, mat, t)
@@ -164,11 +246,14 @@ def gradient(w: Workload, group: int, mat: int, t: int) -> np.ndarray:
             sB = np.exp(np.linspace(math.log(1e-3), 0.0, n))
             fr.shuffle(sA)
             fr.shuffle(sB)
-            _FIXED.clear()
-            _FIXED[key] = (_haar(fr, m) * sA, sB[:, None] * _haar(fr, n).T)
-        A, B = _FIXED[key]
+            _FIXED[key] = (RandomOrthogonal(fr, m), sA, sB, RandomOrthogonal(fr, n))
+        QL, sA, sB, QR = _FIXED[key]
         Z = _rng(w.name, group, mat, t).standard_normal((m, n))
-        return ((A @ Z) @ B).astype(np.float32)
+        # G = A Z B with A = Q_L diag(sA), B = diag(sB) Q_R^T
+        Z *= sA[:, None]
+        Y = QL.apply(Z)
+        Y *= sB
+        return QR.apply(Y, axis=1).astype(np.float32)
     raise ValueError(w.grad)
 
 

@@ -26,6 +26,7 @@ Parity status of each function (what pins it in the CPU test-suite):
   c_shape ...................... closed forms (square case 1/(2 sqrt n))
   nesterov_scale / momentum .... t=1 gives N=G exactly; Monte-Carlo RMS of N = 1
   factor_update_okls ........... white-Gaussian expectation, equivariance, transpose
+  factor_rows / factor_block ... principal blocks of the full updates (both modes)
   factor_update_shampoo ........ worked example L = G G^T = [[10,3],[3,5]]
   inv_root_exact ............... P S P = I, 2x2 closed form, scipy sqrtm on 3x3,
                                  worked example and problem 14 singular values
@@ -121,6 +122,27 @@ def factor_update_okls(Sa, Sb, Pa, Pb, G, beta2: float, eps: float):
     Sa_new = beta2 * Sa + ((1.0 - beta2) / n) * (Xa @ Xa.T) + eps * np.eye(m)
     Sb_new = beta2 * Sb + ((1.0 - beta2) / m) * (Xb.T @ Xb) + eps * np.eye(n)
     return _sym(Sa_new), _sym(Sb_new)
+
+
+def factor_rows(G, Pa, Pb, K, side: str, mode: str = "okls"):
+    """Rows K of the matrix whose Gram matrix updates one factor: side 'a'
+    gives X_a[K] = G[K] P_b, side 'b' gives (P_a G[:, K])^T, the rows K of
+    X_b^T (Shampoo, R7: X = G).  Sampled form of the products above."""
+    K = np.asarray(K)
+    if side == "a":
+        return G[K] if mode == "shampoo" else G[K] @ Pb
+    return G[:, K].T if mode == "shampoo" else (Pa @ G[:, K]).T
+
+
+def factor_block(S_KK, X_K, beta2: float, eps: float, den: int, mode: str = "okls"):
+    """Principal block S'[K, K] of a factor update from the rows K of its X:
+    (X X^T)[K, K] = X[K] X[K]^T and (eps I)[K, K] = eps I, so the block needs
+    nothing else.  OKLS: beta2 S + (1-beta2)/den X X^T + eps I (den = n for
+    S_a, m for S_b); Shampoo (R7): S + X X^T + eps I."""
+    k = S_KK.shape[0]
+    if mode == "shampoo":
+        return _sym(S_KK + X_K @ X_K.T + eps * np.eye(k))
+    return _sym(beta2 * S_KK + ((1.0 - beta2) / den) * (X_K @ X_K.T) + eps * np.eye(k))
 
 
 # ---------------------------------------------------------------------------
@@ -286,8 +308,9 @@ def whiten(Pa, N, Pb):
     return Pa @ N @ Pb
 
 
-def update_weights(W, U, lr: float, lr_peak: float, wd: float):
-    m, n = W.shape
+def update_weights(W, U, lr: float, lr_peak: float, wd: float, shape=None):
+    """shape: (m, n) of the whole matrix when W and U hold only some of its rows."""
+    m, n = W.shape if shape is None else shape
     decay = 1.0 - lr * wd * (lr / lr_peak)
     return decay * W - lr * c_shape(m, n) * U
 

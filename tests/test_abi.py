@@ -30,6 +30,33 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_binding_struct_layouts_match_header(tmp_path):
+    """sizeof and field offsets of the ABI structs, from the C compiler on
+    include/okls.h, equal the ctypes mirrors of the binding."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"okls_config": okls.Config, "okls_group_desc": okls.GroupDesc,
+               "okls_group_tensors": okls.GroupTensors, "okls_profile_stats": okls.ProfileStats}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "okls.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert int(got[f"{cname}.{fname}"]) == getattr(py, fname).offset, (cname, fname)
+
+
 def test_default_config_matches_pages():
     _lib()
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "okls_defaults.json")))

@@ -1,0 +1,246 @@
+"""Full-size parity: every workload at its real shapes and matrix counts,
+through the C ABI in the same launch configuration as the benchmark (one
+okls_step over all shape groups, fp16-input GEMMs), checked against the fp64
+oracle on sampled outputs.
+
+Two checks per workload:
+
+* gradient steps (t = 1, 2, teacher-forced from the GPU's own state): the
+  momentum of every sampled matrix in full; principal blocks of both factors
+  (rows of X = G P or P G, oracle.factor_block); the preconditioners in full
+  wherever the factor dimension allows an fp64 eigendecomposition (damped
+  Newton-Schulz closed form of the oracle's factor); rows of the whitened
+  update U = P_a N P_b and of the new weights, from the GPU's preconditioners.
+* known spectrum (zero gradient): sampled matrices start from factors
+  S = Q diag(lam) Q^T with Q a dense random orthogonal, so the new factor is
+  beta2 S + eps I (Shampoo: S + eps I) with known eigenvalues and the
+  preconditioner's rows follow from the oracle's per-eigenvalue closed form
+  of the damped iteration -- the whole Newton-Schulz chain checked at every
+  factor size, the largest included.
+
+Matrices that are not sampled get Gaussian filler gradients generated on the
+device, so every launch runs at its real size.
+"""
+import gc
+import math
+import time
+
+import numpy as np
+import pytest
+
+from kronecker_factored_second_amd import workloads as WL
+from oracle import okls_oracle as O
+
+from tests import gpu_harness as H
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+# The new weights' rows are checked at the update's tolerance: where the
+# update dominates the (small, muP-initialised) weights, the weights' relative
+# error is the update's.
+TOL = {"fp16": dict(S=2e-2, P=2e-2, U=3e-2, M=1e-6, W=3e-2), "fp32": dict(S=1e-4, P=1e-4, U=3e-2, M=1e-6, W=3e-2)}
+
+# sampled (group, matrix) pairs, filler gradient scale, largest factor
+# dimension whose preconditioner is checked in full through eigh
+FULL = {
+    "c2": dict(sample=None, filler=0.02, eig_max=2816),
+    "c3": dict(sample=[(0, 0), (0, 95), (1, 0), (1, 47), (2, 0), (2, 23)], filler=0.02, eig_max=2048),
+    "c4": dict(sample=[(0, 0), (1, 0), (2, 0)], filler=1e-3, eig_max=4096),
+    "c5": dict(sample=[(0, 0), (1, 0), (2, 0)], filler=0.07, eig_max=0),
+}
+N_ROWS = 32
+
+
+def _log(msg):
+    print(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def _sampled(w, name):
+    s = FULL[name]["sample"]
+    return [(gi, i) for gi, (_, _, b) in enumerate(w.groups) for i in range(b)] if s is None else s
+
+
+def _free_gpu():
+    torch = pytest.importorskip("torch")
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _build(name, precision):
+    """Full workload: parameters (sampled ones from the spectral-muP init,
+    the rest filler of the same scale) and the optimizer, its workspace
+    limited so that one step's gradients still fit."""
+    torch = pytest.importorskip("torch")
+    w = WL.workload(name)
+    WL.reset_caches()
+    params = []
+    for gi, (m, n, b) in enumerate(w.groups):
+        std = 0.07539 * math.sqrt(m / n) / (math.sqrt(n) + math.sqrt(m))
+        params.append(WL.device_filler(std, (b, m, n), seed=1000 + gi))
+    for gi, i in _sampled(w, name):
+        params[gi][i].copy_(torch.from_numpy(WL.initial_weights(w, gi, i)))
+    bf16 = w.grad_dtype == "bf16"
+    opt_bytes = sum(b * (m * n + 2 * m * m + 2 * n * n) * 4 for m, n, b in w.groups)
+    grad_bytes = sum(b * m * n * (2 if bf16 else 4) for m, n, b in w.groups)
+    free = torch.cuda.mem_get_info(0)[0]
+    limit = free - opt_bytes - 2 * grad_bytes - (8 << 30)
+    from kronecker_factored_second_amd import okls
+    opt = okls.OKLS(params, mode=w.mode, precision=precision, grad_dtype=torch.bfloat16 if bf16 else torch.float32,
+                    workspace_limit=limit)
+    _log(f"{name}-{precision}: {w.n_matrices} matrices, chunk_matrices={opt.cfg.chunk_matrices}, "
+         f"workspace {opt.workspace.numel() / 2**30:.1f} GiB")
+    return w, opt, params
+
+
+def _grads(w, name, t, zero=False):
+    torch = pytest.importorskip("torch")
+    bf16 = w.grad_dtype == "bf16"
+    dt = torch.bfloat16 if bf16 else torch.float32
+    out, host = [], {}
+    for gi, (m, n, b) in enumerate(w.groups):
+        if zero:
+            out.append(torch.zeros(b, m, n, device="cuda:0", dtype=dt))
+            continue
+        out.append(WL.device_filler(FULL[name]["filler"], (b, m, n), seed=(WL.CFG_IDS[name] << 20) + (gi << 8) + t,
+                                    dtype=dt))
+    if not zero:
+        for gi, i in _sampled(w, name):
+            G = WL.gradient(w, gi, i, t)
+            host[(gi, i)] = G.astype(np.float64)
+            out[gi][i].copy_(torch.from_numpy(G).to(dt))
+    return out, host
+
+
+def _f64(x):
+    return x.detach().double().cpu().numpy()
+
+
+def _rows(rng, d, k=N_ROWS):
+    return np.sort(rng.choice(d, size=min(k, d), replace=False))
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_fullsize_gradient_steps(name):
+    torch = pytest.importorskip("torch")
+    _free_gpu()
+    w, opt, params = _build(name, "fp16")
+    hp = H.hyper_of(opt)
+    tol = TOL["fp16"]
+    p_root = 4 if w.mode == "shampoo" else 2
+    coeffs, _ = O.ns_coefficients(hp.ns_floor, hp.ns_steps)
+    rep = H.Report(f"full-{name}")
+    rng = np.random.default_rng(WL.CFG_IDS[name])
+    for t in (1, 2):
+        _log(f"{name} t={t}: gradients")
+        grads, host = _grads(w, name, t)
+        before = {}
+        for gi, i in _sampled(w, name):
+            s = opt.state[gi]
+            before[(gi, i)] = dict(W=_f64(params[gi][i]), M=_f64(s["M"][i]), Sa=_f64(s["Sa"][i]), Sb=_f64(s["Sb"][i]),
+                                   Pa=_f64(s["Pa"][i]), Pb=_f64(s["Pb"][i]))
+        _log(f"{name} t={t}: step")
+        t0 = time.perf_counter()
+        opt.step(grads=grads)
+        torch.cuda.synchronize()
+        _log(f"{name} t={t}: step took {time.perf_counter() - t0:.2f} s; checking")
+        assert opt.check_finite(), f"non-finite state after step {t}"
+        for gi, i in _sampled(w, name):
+            m, n, _ = w.groups[gi]
+            b4, G = before[(gi, i)], host[(gi, i)]
+            s = opt.state[gi]
+            M1, N = O.momentum(b4["M"], G, hp.beta1, t, hp.nesterov_var_corr)
+            e = dict(t=t, g=gi, i=i, M=O.rel_frob(_f64(s["M"][i]), M1))
+            Pa1, Pb1 = _f64(s["Pa"][i]), _f64(s["Pb"][i])
+            for side, d, den, key, Pkey in (("a", m, n, "Sa", "Pa"), ("b", n, m, "Sb", "Pb")):
+                K = _rows(rng, d)
+                X_K = O.factor_rows(G, b4["Pa"], b4["Pb"], K, side, w.mode)
+                blk = O.factor_block(b4[key][np.ix_(K, K)], X_K, hp.beta2, hp.eps, den, w.mode)
+                e["S_" + side] = O.rel_frob(_f64(s[key][i])[np.ix_(K, K)], blk)
+                if d <= FULL[name]["eig_max"]:
+                    # the whole factor: the block over every index
+                    X = O.factor_rows(G, b4["Pa"], b4["Pb"], np.arange(d), side, w.mode)
+                    S2 = O.factor_block(b4[key], X, hp.beta2, hp.eps, den, w.mode)
+                    Pns = O.ns_eigen_closed_form(S2, coeffs, p_root, hp.ns_damping)
+                    e["P_" + side] = O.rel_frob(Pa1 if side == "a" else Pb1, Pns)
+            I = _rows(rng, m)
+            U_orc = O.whiten(Pa1[I], N, Pb1)
+            decay = 1.0 - hp.lr * hp.weight_decay * (hp.lr / hp.peak())
+            W1 = _f64(params[gi][i])[I]
+            U_gpu = (decay * b4["W"][I] - W1) / (hp.lr * O.c_shape(m, n))
+            e["U"] = O.rel_frob(U_gpu, U_orc)
+            e["W"] = O.rel_frob(W1, O.update_weights(b4["W"][I], U_orc, hp.lr, hp.peak(), hp.weight_decay, (m, n)))
+            rep.add(**e)
+            assert e["M"] < tol["M"], e
+            assert e["S_a"] < tol["S"] and e["S_b"] < tol["S"], e
+            for k in ("P_a", "P_b"):
+                if k in e:
+                    assert e[k] < tol["P"], e
+            assert e["U"] < tol["U"] and e["W"] < tol["W"], e
+        del grads, before
+    del opt, params
+    _free_gpu()
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name,precision", [("c2", "fp16"), ("c2", "fp32"), ("c3", "fp16"), ("c3", "fp32"),
+                                            ("c4", "fp16"), ("c5", "fp16"), ("c5", "fp32")])
+def test_fullsize_known_spectrum(name, precision):
+    """Zero gradient from factors with known eigenvalues: rows of the new
+    factors and preconditioners of the sampled matrices against the closed
+    form, the weights purely decayed.  kappa = 1e4 on the fp16-input path and
+    1e2 on the fp32-accurate path (there the fp32 storage of S shifts its
+    eigenvalues by ~1e-8 of the largest, which must stay far below 1e-4 of
+    the smallest)."""
+    torch = pytest.importorskip("torch")
+    _free_gpu()
+    w, opt, params = _build(name, precision)
+    hp = H.hyper_of(opt)
+    tol = TOL[precision]
+    kappa = 1e4 if precision == "fp16" else 1e2
+    p_root = 4 if w.mode == "shampoo" else 2
+    coeffs, _ = O.ns_coefficients(hp.ns_floor, hp.ns_steps)
+    rep = H.Report(f"spectrum-{name}-{precision}")
+    rng = np.random.default_rng(100 + WL.CFG_IDS[name])
+    known = {}
+    for gi, i in _sampled(w, name):
+        m, n, _ = w.groups[gi]
+        for side, d, key in ((0, m, "Sa"), (1, n, "Sb")):
+            Q, lam = WL.spectral_factor(name, gi, i, side, d, kappa, 2e-5)
+            S = WL.symmetric_from_spectrum(Q, lam).astype(np.float32)
+            opt.state[gi][key][i].copy_(torch.from_numpy(S))
+            known[(gi, i, side)] = (Q, lam, S)
+            del S
+    _log(f"{name}-{precision}: known-spectrum factors set")
+    W0 = {k: _f64(params[k[0]][k[1]]) for k in _sampled(w, name)}
+    grads, _ = _grads(w, name, 1, zero=True)
+    t0 = time.perf_counter()
+    opt.step(grads=grads)
+    torch.cuda.synchronize()
+    _log(f"{name}-{precision}: step took {time.perf_counter() - t0:.2f} s; checking")
+    assert opt.check_finite()
+    decay = 1.0 - hp.lr * hp.weight_decay * (hp.lr / hp.peak())
+    for gi, i in _sampled(w, name):
+        m, n, _ = w.groups[gi]
+        e = dict(g=gi, i=i, W=O.rel_frob(_f64(params[gi][i]), decay * W0[(gi, i)]))
+        for side, d, key, pkey in ((0, m, "Sa", "Pa"), (1, n, "Sb", "Pb")):
+            Q, lam, S = known[(gi, i, side)]
+            I = _rows(rng, d)
+            if w.mode == "okls":
+                lam1 = hp.beta2 * lam + hp.eps
+                S1 = hp.beta2 * S[I].astype(np.float64)
+            else:
+                lam1 = lam + hp.eps
+                S1 = S[I].astype(np.float64)
+            S1[np.arange(len(I)), I] += hp.eps
+            P_rows = WL.symmetric_from_spectrum(Q, O.ns_spectral(lam1, coeffs, hp.ns_damping, p_root), rows=I)
+            tag = "ab"[side]
+            e["S_" + tag] = O.rel_frob(_f64(opt.state[gi][key][i][torch.from_numpy(I).cuda()]), S1)
+            e["P_" + tag] = O.rel_frob(_f64(opt.state[gi][pkey][i][torch.from_numpy(I).cuda()]), P_rows)
+        rep.add(**e)
+        assert e["W"] < 1e-6, e
+        assert e["S_a"] < tol["S"] and e["S_b"] < tol["S"], e
+        assert e["P_a"] < tol["P"] and e["P_b"] < tol["P"], e
+    del grads, opt, params, known
+    _free_gpu()

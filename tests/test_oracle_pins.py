@@ -375,6 +375,34 @@ def test_okls_factor_update_brute_force_outer_products():
 
 
 @pytest.mark.parametrize("mode", ["okls", "shampoo"])
+def test_factor_block_is_principal_submatrix_of_full_update(mode):
+    """The sampled factor update (rows of X, principal block) equals the same
+    block of the full update, on both sides."""
+    rng = np.random.default_rng(12)
+    m, n = 23, 31
+    G = rng.standard_normal((m, n))
+    Sa, Sb = _spd(rng, m, 10.0), _spd(rng, n, 10.0)
+    Pa, Pb = _spd(rng, m, 5.0), _spd(rng, n, 5.0)
+    if mode == "okls":
+        Sa2, Sb2 = O.factor_update_okls(Sa, Sb, Pa, Pb, G, 0.9482, 1e-9)
+    else:
+        Sa2, Sb2 = O.factor_update_shampoo(Sa, Sb, G, 1e-9)
+    for side, S, S2, den, d in (("a", Sa, Sa2, n, m), ("b", Sb, Sb2, m, n)):
+        K = np.sort(rng.choice(d, size=7, replace=False))
+        X_K = O.factor_rows(G, Pa, Pb, K, side, mode)
+        blk = O.factor_block(S[np.ix_(K, K)], X_K, 0.9482, 1e-9, den, mode)
+        np.testing.assert_allclose(blk, S2[np.ix_(K, K)], rtol=1e-12, atol=1e-14)
+
+
+def test_update_weights_rows_with_shape():
+    rng = np.random.default_rng(13)
+    W, U = rng.standard_normal((9, 14)), rng.standard_normal((9, 14))
+    full = O.update_weights(W, U, 0.05, 0.09, 0.03)
+    rows = O.update_weights(W[[2, 5]], U[[2, 5]], 0.05, 0.09, 0.03, shape=W.shape)
+    np.testing.assert_array_equal(rows, full[[2, 5]])
+
+
+@pytest.mark.parametrize("mode", ["okls", "shampoo"])
 @pytest.mark.parametrize("root", ["exact", "ns"])
 def test_orthogonal_equivariance(mode, root):
     rng = np.random.default_rng(13)
