@@ -29,14 +29,19 @@ PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
-KERNEL_SRC = os.path.join(ROOT, "kronecker_factored_second_amd", "csrc", "okls_kernels.hip")
+# the GEMM's traffic depends on its kernel and on the planner's launch shapes
+KERNEL_SRCS = [os.path.join(ROOT, "kronecker_factored_second_amd", "csrc", f)
+               for f in ("okls_kernels.hip", "okls_types.h", "okls_api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_kernel_c2_fp16_hbm_traffic.txt")
 COPY_PROBE_BYTES = 1 << 30
 
 
 def kernel_source_hash():
     import hashlib
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -67,12 +72,13 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 10}), flush=True)
 
 
-def _counter_rows(d, counter):
-    """{kernel name: [values]} of one counter from a rocprofv3 --pmc csv directory."""
+def _counter_rows(d, counter, prefix):
+    """{kernel name: [values]} of one counter from the rocprofv3 --pmc csv
+    files <prefix>_counter_collection.csv under directory d."""
     import csv
     import glob
     out = {}
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+    for f in glob.glob(os.path.join(d, "**", f"{prefix}_counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter:
                 out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
@@ -81,34 +87,44 @@ def _counter_rows(d, counter):
 
 def summarize_counters(fetch_dir, write_dir, commands):
     """HBM bytes per gemm_nt_kernel launch from FETCH_SIZE / WRITE_SIZE (KiB
-    per dispatch), each scaled by the factor that makes the plain copy's
-    counter equal its known size."""
-    fetch, write = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    per dispatch) of the benchmark run ('bench' files), each scaled by the
+    factor that makes the counter of the plain 1 GiB copy ('copy' files, the
+    runtime's copy kernel) read the copy's size."""
 
-    def pick(rows, key):
-        vals = [v for k, vs in rows.items() if key(k) for v in vs]
+    def avg(d, counter, prefix, key):
+        vals = [v for k, vs in _counter_rows(d, counter, prefix).items() if key(k) for v in vs]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {prefix} in {d}")
         return sum(vals) / len(vals), len(vals)
 
-    is_copy = lambda k: "copy" in k.lower() and "okls" not in k
+    is_copy = lambda k: k.startswith("__amd_rocclr_copyBuffer")
     is_gemm = lambda k: "gemm_nt_kernel" in k
-    cf, ncf = pick(fetch, is_copy)
-    cw, ncw = pick(write, is_copy)
-    gf, ngf = pick(fetch, is_gemm)
-    gw, ngw = pick(write, is_gemm)
+    cf, ncf = avg(fetch_dir, "FETCH_SIZE", "copy", is_copy)
+    cw, ncw = avg(write_dir, "WRITE_SIZE", "copy", is_copy)
+    gf, ngf = avg(fetch_dir, "FETCH_SIZE", "bench", is_gemm)
+    gw, ngw = avg(write_dir, "WRITE_SIZE", "bench", is_gemm)
     kf = COPY_PROBE_BYTES / (cf * 1024.0)
     kw = COPY_PROBE_BYTES / (cw * 1024.0)
     traffic = gf * 1024.0 * kf + gw * 1024.0 * kw
+    others = []
+    for kern in ("stats_kernel", "cast_kernel"):
+        of, nof = avg(fetch_dir, "FETCH_SIZE", "bench", lambda k: kern in k)
+        ow, _ = avg(write_dir, "WRITE_SIZE", "bench", lambda k: kern in k)
+        others.append(f"{kern}_hbm_bytes_per_launch {of * 1024.0 * kf + ow * 1024.0 * kw:.6e} "
+                      f"(fetch {of * 1024.0 * kf:.4e}, write {ow * 1024.0 * kw:.4e}, {nof} dispatches)")
     lines = [
-        "# HBM traffic of gemm_nt_kernel (both block tiles), one d=1024 transformer block, fp16 path",
-        f"# kernel_source_sha256_16 {kernel_source_hash()}",
-        "# commands (repository root as $REPO; cd /tmp first):",
-        *[f"#   {c}" for c in commands.split(";")],
+        "# HBM traffic of gemm_nt_kernel (both block tiles, every launch of a step),",
+        "# one d=1024 transformer block (4x 1024x1024, 2x 2816x1024, 1x 1024x2816), fp16 path",
+        f"# kernel_source_sha256_16 {kernel_source_hash()} (okls_kernels.hip, okls_types.h, okls_api.cpp)",
+        "# commands (repository root as $REPO, output directory OUT; cd /tmp first):",
+        *[f"#   {c.strip()}" for c in commands.split(";")],
         f"copy_probe_bytes {COPY_PROBE_BYTES}",
         f"copy_fetch_kib_avg {cf:.1f} over {ncf} dispatches -> fetch factor {kf:.4f}",
         f"copy_write_kib_avg {cw:.1f} over {ncw} dispatches -> write factor {kw:.4f}",
         f"gemm_fetch_kib_avg {gf:.1f} over {ngf} dispatches",
         f"gemm_write_kib_avg {gw:.1f} over {ngw} dispatches",
         f"gemm_hbm_bytes_per_launch {traffic:.6e}",
+        *others,
     ]
     open(TRAFFIC_FILE, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -120,7 +136,7 @@ def measured_traffic():
     if not os.path.exists(TRAFFIC_FILE):
         return None
     txt = open(TRAFFIC_FILE).read()
-    if f"kernel_source_sha256_16 {kernel_source_hash()}" not in txt:
+    if f"kernel_source_sha256_16 {kernel_source_hash()} " not in txt:
         return None
     for line in txt.splitlines():
         if line.startswith("gemm_hbm_bytes_per_launch"):
@@ -217,6 +233,7 @@ def main():
     g_ms = sum(prof[k]["ms"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     g_fl = sum(prof[k]["flops"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     g_n = sum(prof[k]["launches"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
+    g_b = sum(prof[k]["bytes"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     achieved = g_fl / (g_ms * 1e-3) / 1e12
     ns = prof["ns_gemm"]
     ns_tflops = ns["flops"] / (ns["ms"] * 1e-3) / 1e12
@@ -244,7 +261,8 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS,
                      "traffic": measured_traffic() if (args.workload == "c2" and args.precision == "fp16") else None,
                      "avg_launch_us": g_ms * 1e3 / max(g_n, 1), "launches_per_step": g_n / max(prof["steps"], 1),
-                     "algorithmic_flops_per_step": g_fl / max(prof["steps"], 1)},
+                     "algorithmic_flops_per_step": g_fl / max(prof["steps"], 1),
+                     "algorithmic_bytes_per_launch": g_b / max(g_n, 1)},
         "profile_ms_per_step": {k: prof[k]["ms"] / max(prof["steps"], 1) for k in okls.PROFILE_CATEGORIES},
         "hbm_kernels": {kern: {"bound": "hbm", "achieved": prof[cat]["bytes"] / (prof[cat]["ms"] * 1e-3) / 1e9,
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",

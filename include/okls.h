@@ -158,11 +158,12 @@ int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_s
  * the profiled steps: 27 GEMMs of 2 d^3 per inverse square root (54 for the
  * Shampoo fourth root), 3 m n (m + n) for the OKLS factors (m n (m + n) in
  * Shampoo mode), 2 m n (m + n) for the whitening.  bytes[i] is the
- * algorithmic memory traffic of the statistics and cast categories over the
- * profiled steps: every job reads its source once (4 bytes per fp32 element,
- * 2 per bf16; the momentum jobs read M and G and write M') and writes its
- * fp16 output once (2 bytes per element, 4 with the low halves); zero for the
- * GEMM categories. */
+ * algorithmic memory traffic of category i over the profiled steps: every
+ * job reads its source once (4 bytes per fp32 element, 2 per bf16 or fp16,
+ * twice that for split hi/lo operands; the momentum jobs read M and G and
+ * write M'), reads the fp32 matrix its epilogue combines with once, and
+ * writes each output once (fp16 outputs 2 bytes per element, 4 with the low
+ * halves; fp32 outputs 4). */
 #define OKLS_PROFILE_CATEGORIES 5
 typedef struct {
     double ms[OKLS_PROFILE_CATEGORIES];

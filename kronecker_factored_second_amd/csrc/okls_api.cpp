@@ -332,6 +332,17 @@ struct Planner {
     r.cat = gemm_cat;
     r.prob_base = static_cast<int>(probs.size());
     probs.insert(probs.end(), ps.begin(), ps.end());
+    // algorithmic bytes: both fp16 operands once (hi and lo halves when split),
+    // every output and the fp32 matrix the epilogue reads, once
+    for (const GemmProb& p : ps) {
+      const double mn = static_cast<double>(p.M) * p.N;
+      double b = 2.0 * (split_in ? 2.0 : 1.0) * (static_cast<double>(p.M) + p.N) * p.Kp;
+      if (p.out32.kind != REF_NONE) b += 4.0 * mn;
+      if (p.out16.kind != REF_NONE) b += (write_lo ? 4.0 : 2.0) * mn;
+      if (p.out16T.kind != REF_NONE) b += (write_lo ? 4.0 : 2.0) * mn;
+      if (p.aux.kind != REF_NONE) b += 4.0 * mn;
+      step_bytes[gemm_cat] += b;
+    }
     // the large tile when every problem's padded sides are multiples of it and
     // the launch has at least four blocks of it per CU (1024); otherwise the
     // 128 tile keeps the CUs busy
