@@ -111,6 +111,7 @@ struct LaunchRec {
   float ka = 0.f, kb = 0.f;
   int cat = 0;                  // profiling category
   int tile = kTile;             // GEMM block tile
+  int epi = EPI_STORE32;        // GEMM epilogue kind (one per launch)
 };
 
 enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4 };
@@ -343,8 +344,10 @@ struct Planner {
       if (p.aux.kind != REF_NONE) b += 4.0 * mn;
       step_bytes[gemm_cat] += b;
     }
+    // one epilogue kind per launch (the kernel is specialised on it)
+    r.epi = ps.front().epi;
     // the large tile when every problem's padded sides are multiples of it and
-    // the launch has at least four blocks of it per CU (1024); otherwise the
+    // the launch has at least two blocks of it per CU (512); otherwise the
     // 128 tile keeps the CUs busy
     r.tile = kBigTile;
     long big_tiles = 0;
@@ -353,7 +356,7 @@ struct Planner {
       const long tm = p.Mp / kBigTile, tn = p.Np / kBigTile;
       big_tiles += upper ? tm * (tm + 1) / 2 : tm * tn;
     }
-    if (big_tiles < 1024) r.tile = kTile;
+    if (big_tiles < 512) r.tile = kTile;
     const std::pair<int, int> t = tiles_for(ps, upper, r.tile);
     r.first = t.first;
     r.count = t.second;
@@ -813,12 +816,14 @@ struct Planner {
         if (r.type == L_GEMM) {
           if (r.first < 0 || r.first + r.count > static_cast<int>(tiles.size())) return false;
           if (r.tile != kTile && r.tile != kBigTile) return false;
+          if (r.epi < EPI_STORE32 || r.epi > EPI_UPDATE) return false;
           const int segs = r.split_in ? 2 : 1;
           for (int t = r.first; t < r.first + r.count; ++t) {
             const TileRef tr = tiles[t];
             const int q = r.prob_base + tr.prob;
             if (tr.prob < 0 || q >= static_cast<int>(probs.size())) return false;
             const GemmProb& p = probs[q];
+            if (p.epi != r.epi) return false;
             const int ti = tr.ij >> 16, tj = tr.ij & 0xffff;
             if (p.Mp % r.tile || p.Np % r.tile || p.Kp % kTile || p.Kp <= 0) return false;
             if (ti < 0 || tj < 0 || ti >= p.Mp / r.tile || tj >= p.Np / r.tile) return false;
@@ -1207,7 +1212,7 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.ws = ws;
         a.scal = scal;
         a.user = user;
-        e = launch_gemm(a, r.count, r.tile, s);
+        e = launch_gemm(a, r.count, r.tile, r.epi, s);
       }
       if (e != hipSuccess) return OKLS_ERR_HIP;
       if (h->prof) {

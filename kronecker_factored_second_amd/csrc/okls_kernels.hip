@@ -6,12 +6,16 @@
 //                   4-deep ring, optional split-fp16 (hi*hi + hi*lo + lo*hi) as
 //                   a 3-segment K loop, fused epilogues (factor EMA with
 //                   mirrored store, the Newton-Schulz step polynomial, the
-//                   weight update).
+//                   weight update); one instantiation per tile size, epilogue
+//                   kind and fp16 output form keeps each epilogue in registers.
 //  stats_kernel     per-block absmax / sum of squares partials.
 //  cast_kernel      fp32/bf16 -> padded fp16 (hi, lo) with a power-of-two
 //                   scale derived from the partials, optional transpose; also
 //                   the Nesterov momentum update and the Newton-Schulz start.
 //  init_state_kernel, finite_kernel.
+//
+// fp16 outputs are staged through LDS and leave as whole cache lines (both
+// the row-major and the transposed copy).
 //
 // The operation each epilogue performs is documented on okls::Epi; the
 // mathematics follows the "Online KL Shampoo" README, section "How it works".
@@ -57,24 +61,12 @@ __device__ __forceinline__ void store16(half_t* p, int lo_off, bool write_lo, co
   if (write_lo) *reinterpret_cast<half4_t*>(p + lo_off) = lo;
 }
 
-// Transposed copy: element (r, c0+e) goes to row c0+e, column r.  For a fixed
-// e the 16 lanes of a row group write 16 consecutive halves (32 B).
-__device__ __forceinline__ void store16T(half_t* base, int ld, int lo_off, bool write_lo, int r, int c0,
-                                         const float (&x)[4], float s) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float y = x[e] * s;
-    const half_t h = static_cast<half_t>(y);
-    half_t* p = base + static_cast<size_t>(c0 + e) * ld + r;
-    p[0] = h;
-    if (write_lo) p[lo_off] = static_cast<half_t>(y - static_cast<float>(h));
-  }
-}
-
 struct EpiCtx {
   float alpha;
   int M, N, ti, tj, rbase, cbase;
-  bool write_lo;
+  int tr0, tc0;             // origin of this wave's (BT/2) x (BT/2) region in the output
+  half_t* lds0;             // this wave's staging region: rows [0, 64) and [64, BT/2)
+  half_t* lds1;
   float* out32;
   half_t* out16;
   half_t* out16T;
@@ -84,12 +76,70 @@ struct EpiCtx {
   float c0, c1, c2, ka, kb, lr, decay;
 };
 
+// fp16 outputs go through LDS: each wave stages its (BT/2) x (BT/2) region
+// (rows of BT/2 halves, 16-byte chunks XOR-swizzled by the row so that the
+// accumulator writes, the row reads and the column reads below are free of
+// bank conflicts), then writes the row-major copy as 16-byte row segments and
+// the transposed copy as 16-byte segments of eight rows of one column, so
+// both copies leave as whole cache lines.
+template <int G>
+__device__ __forceinline__ int stage_off(int r, int c) {
+  constexpr int HB = 32 * G, CH = HB / 8;
+  const int sw = ((r & 7) ^ (r >> 3)) & (CH - 1);
+  return (r & 63) * HB + (((c >> 3) ^ sw) << 3) + (c & 7);
+}
+
+template <int G>
+__device__ __forceinline__ void stage_put(const EpiCtx& x, int r, int c, half4_t h) {
+  half_t* base = (G == 4 && r >= 64) ? x.lds1 : x.lds0;
+  *reinterpret_cast<half4_t*>(base + stage_off<G>(r, c)) = h;
+}
+
+template <int G>
+__device__ __forceinline__ void stage_flush(const EpiCtx& x, int col_off) {
+  constexpr int HB = 32 * G, CH = HB / 8;
+  const int lane = threadIdx.x & 63;
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // this wave's LDS writes done
+  asm volatile("" ::: "memory");
+  if (x.out16 != nullptr) {
+    constexpr int RPI = 64 / CH;                 // rows per instruction
+#pragma unroll
+    for (int it = 0; it < HB / RPI; ++it) {
+      const int r = it * RPI + lane / CH, k = lane % CH;
+      const half_t* base = (G == 4 && r >= 64) ? x.lds1 : x.lds0;
+      const half8_t v = *reinterpret_cast<const half8_t*>(base + stage_off<G>(r, k * 8));
+      *reinterpret_cast<half8_t*>(x.out16 + static_cast<size_t>(x.tr0 + r) * x.ld16 + col_off + x.tc0 + k * 8) = v;
+    }
+  }
+  if (x.out16T != nullptr) {
+    constexpr int LPC = HB / 8;                  // lanes per column (8 rows each)
+    constexpr int CPI = 64 / LPC;                // columns per instruction
+    const int r0 = 8 * (lane % LPC);
+    const half_t* base = (G == 4 && r0 >= 64) ? x.lds1 : x.lds0;
+#pragma unroll
+    for (int it = 0; it < HB / CPI; ++it) {
+      const int c = it * CPI + lane / LPC;
+      half8_t v;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = base[stage_off<G>(r0 + q, c)];
+      *reinterpret_cast<half8_t*>(x.out16T + static_cast<size_t>(x.tc0 + c) * x.ld16 + col_off + x.tr0 + r0) = v;
+    }
+  }
+  // the next staging pass overwrites this wave's region
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("" ::: "memory");
+}
+
 // Epilogue of one output tile, one instantiation per kind so that every
 // accumulator index is a compile-time constant (keeps them in registers).
 // Block (i, j) of a wave holds, in each lane, row rbase + 32 i and the four
 // groups of four consecutive columns cbase + 32 j + 8 g + e.
-template <int EPI, int G>
-__device__ __forceinline__ void epilogue(const floatx16 (&acc)[G][G], const EpiCtx& x) {
+// One pass over the accumulators.  fp32 kinds store directly; fp16 kinds
+// stage PART 0 (the fp16 values, or the hi halves of the split layout) or
+// PART 1 (the lo halves, y s - fp16(y s)) through LDS.
+template <int EPI, int G, int PART>
+__device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[G][G], const EpiCtx& x) {
+  constexpr bool kF16 = EPI == EPI_NS_T || EPI == EPI_NS_Y1 || EPI == EPI_STORE16 || EPI == EPI_NS_FINAL;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const int r = x.rbase + i * 32;
@@ -151,18 +201,31 @@ __device__ __forceinline__ void epilogue(const floatx16 (&acc)[G][G], const EpiC
           }
           y[e] = t;
         }
-        if constexpr (EPI == EPI_NS_FINAL) {
+        if constexpr (EPI == EPI_NS_FINAL && PART == 0) {
           if (x.out32 != nullptr && r < x.M) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               if (c0 + e < x.N) x.out32[static_cast<size_t>(r) * x.ld32 + c0 + e] = y[e] * x.cval;
           }
         }
-        if (x.out16 != nullptr) store16(x.out16 + static_cast<size_t>(r) * x.ld16 + c0, x.lo16, x.write_lo, y, x.s_out);
-        if (x.out16T != nullptr) store16T(x.out16T, x.ld16, x.lo16, x.write_lo, r, c0, y, x.s_out);
+        half4_t h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ys = y[e] * x.s_out;
+          const half_t hi = static_cast<half_t>(ys);
+          h[e] = PART == 0 ? hi : static_cast<half_t>(ys - static_cast<float>(hi));
+        }
+        stage_put<G>(x, r - x.tr0, c0 - x.tc0, h);
       }
     }
   }
+  if constexpr (kF16) stage_flush<G>(x, PART == 0 ? 0 : x.lo16);
+}
+
+template <int EPI, int G, bool WL>
+__device__ __forceinline__ void epilogue(const floatx16 (&acc)[G][G], const EpiCtx& x) {
+  epilogue_pass<EPI, G, 0>(acc, x);
+  if constexpr (WL) epilogue_pass<EPI, G, 1>(acc, x);
 }
 
 // Block tile BT x BT, 4 waves in 2 x 2, each wave (BT/2) x (BT/2) made of
@@ -176,7 +239,7 @@ __device__ __forceinline__ int swz4(int row, int chunk) { return chunk ^ ((row >
 // s_waitcnt with vmcnt = v, other counters untouched (gfx9 encoding)
 #define WAIT_VMCNT(v) __builtin_amdgcn_s_waitcnt(((v) & 15) | (7 << 4) | (15 << 8) | (((v) >> 4) << 14))
 
-template <int BT>
+template <int BT, int EPI, bool WL>
 __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kernel(GemmArgs args) {
   constexpr int G = BT / 64;
   constexpr int NS = 4;                      // LDS ring depth
@@ -313,9 +376,19 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
     body(st + 3, I1{}, I3{}, I0{});
   }
   __builtin_amdgcn_s_waitcnt(0);
+  // every wave is done reading the ring: its slots become the staging area
+  __syncthreads();
 
   // ---------------- epilogue ----------------
   EpiCtx ctx;
+  ctx.tr0 = ti * BT + wm * (BT / 2);
+  ctx.tc0 = tj * BT + wn * (BT / 2);
+  if constexpr (BT == 256) {
+    ctx.lds0 = wave == 0 ? sA0 : wave == 1 ? sA2 : wave == 2 ? sB0 : sB2;
+    ctx.lds1 = wave == 0 ? sA1 : wave == 1 ? sA3 : wave == 2 ? sB1 : sB3;
+  } else {
+    ctx.lds0 = ctx.lds1 = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3;
+  }
   ctx.alpha = 1.0f / (args.scal[P.sA] * args.scal[P.sB]);
   ctx.M = P.M;
   ctx.N = P.N;
@@ -323,7 +396,6 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   ctx.tj = tj;
   ctx.rbase = ti * BT + wm * (BT / 2) + frow;
   ctx.cbase = tj * BT + wn * (BT / 2) + fch * 4;
-  ctx.write_lo = args.write_lo != 0;
   ctx.out32 = P.out32.kind != REF_NONE ? reinterpret_cast<float*>(resolve(P.out32, args.ws, args.user)) : nullptr;
   ctx.out16 = P.out16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16, args.ws, args.user)) : nullptr;
   ctx.out16T = P.out16T.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16T, args.ws, args.user)) : nullptr;
@@ -342,15 +414,7 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   ctx.kb = args.kb;
   ctx.lr = args.lr;
   ctx.decay = args.decay;
-  switch (P.epi) {
-    case EPI_STORE32: epilogue<EPI_STORE32, G>(acc, ctx); break;
-    case EPI_SYRK: epilogue<EPI_SYRK, G>(acc, ctx); break;
-    case EPI_NS_T: epilogue<EPI_NS_T, G>(acc, ctx); break;
-    case EPI_NS_Y1: epilogue<EPI_NS_Y1, G>(acc, ctx); break;
-    case EPI_STORE16: epilogue<EPI_STORE16, G>(acc, ctx); break;
-    case EPI_NS_FINAL: epilogue<EPI_NS_FINAL, G>(acc, ctx); break;
-    default: epilogue<EPI_UPDATE, G>(acc, ctx); break;
-  }
+  epilogue<EPI, G, WL>(acc, ctx);
 }
 
 // ---------------------------------------------------------------------------
@@ -679,16 +743,32 @@ __global__ void zero_int_kernel(int* p) { *p = 0; }
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_gemm(const GemmArgs& a, int n_tiles, int tile, hipStream_t s) {
-  if (n_tiles <= 0) return hipSuccess;
-  if (tile == 256) {
-    hipLaunchKernelGGL(gemm_nt_kernel<256>, dim3(n_tiles), dim3(kGemmThreads), 0, s, a);
-  } else if (tile == 128) {
-    hipLaunchKernelGGL(gemm_nt_kernel<128>, dim3(n_tiles), dim3(kGemmThreads), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
+template <int BT>
+hipError_t launch_gemm_bt(const GemmArgs& a, int n_tiles, int epi, hipStream_t s) {
+  const dim3 grid(n_tiles), block(kGemmThreads);
+  // fp16-output kinds come in two forms: fp16 values only, or the split
+  // layout's hi and lo halves (write_lo); the fp32 kinds ignore write_lo
+  const bool wl = a.write_lo != 0;
+#define OKLS_GEMM(E, W) hipLaunchKernelGGL((gemm_nt_kernel<BT, E, W>), grid, block, 0, s, a)
+  switch (epi) {
+    case EPI_STORE32: OKLS_GEMM(EPI_STORE32, false); break;
+    case EPI_SYRK: OKLS_GEMM(EPI_SYRK, false); break;
+    case EPI_UPDATE: OKLS_GEMM(EPI_UPDATE, false); break;
+    case EPI_NS_T: if (wl) OKLS_GEMM(EPI_NS_T, true); else OKLS_GEMM(EPI_NS_T, false); break;
+    case EPI_NS_Y1: if (wl) OKLS_GEMM(EPI_NS_Y1, true); else OKLS_GEMM(EPI_NS_Y1, false); break;
+    case EPI_STORE16: if (wl) OKLS_GEMM(EPI_STORE16, true); else OKLS_GEMM(EPI_STORE16, false); break;
+    case EPI_NS_FINAL: if (wl) OKLS_GEMM(EPI_NS_FINAL, true); else OKLS_GEMM(EPI_NS_FINAL, false); break;
+    default: return hipErrorInvalidValue;
   }
+#undef OKLS_GEMM
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int n_tiles, int tile, int epi, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  if (tile == 256) return launch_gemm_bt<256>(a, n_tiles, epi, s);
+  if (tile == 128) return launch_gemm_bt<128>(a, n_tiles, epi, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_stats(const StatArgs& a, int n_blocks, hipStream_t s) {
