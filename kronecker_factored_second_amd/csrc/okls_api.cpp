@@ -347,8 +347,11 @@ struct Planner {
     // one epilogue kind per launch (the kernel is specialised on it)
     r.epi = ps.front().epi;
     // the large tile when every problem's padded sides are multiples of it and
-    // the launch has at least two blocks of it per CU (512); otherwise the
-    // 128 tile keeps the CUs busy
+    // the launch has enough blocks of it: 64 for the fp16-output kinds (their
+    // outputs are staged through LDS; measured faster than the 128 tile from a
+    // quarter of a block per CU on up), 512 for the fp32-output kinds (stored
+    // from registers, where the 128 tile's second block per CU wins below two
+    // blocks per CU); otherwise the 128 tile
     r.tile = kBigTile;
     long big_tiles = 0;
     for (const GemmProb& p : ps) {
@@ -356,7 +359,8 @@ struct Planner {
       const long tm = p.Mp / kBigTile, tn = p.Np / kBigTile;
       big_tiles += upper ? tm * (tm + 1) / 2 : tm * tn;
     }
-    if (big_tiles < 512) r.tile = kTile;
+    const bool f16_out = r.epi == EPI_NS_T || r.epi == EPI_NS_Y1 || r.epi == EPI_STORE16 || r.epi == EPI_NS_FINAL;
+    if (big_tiles < (f16_out ? 64 : 512)) r.tile = kTile;
     const std::pair<int, int> t = tiles_for(ps, upper, r.tile);
     r.first = t.first;
     r.count = t.second;

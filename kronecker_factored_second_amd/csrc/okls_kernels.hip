@@ -1,21 +1,19 @@
 // gfx950 kernels of the batched OKLS / Shampoo preconditioner step.
 //
 //  gemm_nt_kernel   grouped fp16 MFMA GEMM, C = alpha A B^T, fp32 accumulation,
-//                   128x128 or 256x256 output tiles (v_mfma_f32_32x32x16_f16),
+//                   256x256 output tiles on 8 waves (two per SIMD, each a
+//                   128x64 region) or 128x128 tiles on 4 waves (two blocks per
+//                   CU, fragments double-buffered), v_mfma_f32_32x32x16_f16,
 //                   operands streamed global -> LDS by direct loads through a
 //                   4-deep ring, optional split-fp16 (hi*hi + hi*lo + lo*hi) as
 //                   a 3-segment K loop, fused epilogues (factor EMA with
 //                   mirrored store, the Newton-Schulz step polynomial, the
-//                   weight update); one instantiation per tile size, epilogue
-//                   kind and fp16 output form keeps each epilogue in registers.
+//                   weight update).
 //  stats_kernel     per-block absmax / sum of squares partials.
 //  cast_kernel      fp32/bf16 -> padded fp16 (hi, lo) with a power-of-two
 //                   scale derived from the partials, optional transpose; also
 //                   the Nesterov momentum update and the Newton-Schulz start.
 //  init_state_kernel, finite_kernel.
-//
-// fp16 outputs are staged through LDS and leave as whole cache lines (both
-// the row-major and the transposed copy).
 //
 // The operation each epilogue performs is documented on okls::Epi; the
 // mathematics follows the "Online KL Shampoo" README, section "How it works".
@@ -46,7 +44,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // ---------------------------------------------------------------------------
 // GEMM
 // ---------------------------------------------------------------------------
-constexpr int kGemmThreads = 256;
 
 __device__ __forceinline__ void store16(half_t* p, int lo_off, bool write_lo, const float (&x)[4], float s) {
   half4_t hi, lo;
@@ -61,11 +58,29 @@ __device__ __forceinline__ void store16(half_t* p, int lo_off, bool write_lo, co
   if (write_lo) *reinterpret_cast<half4_t*>(p + lo_off) = lo;
 }
 
+// Tile shape of one GEMM instantiation: BT x BT output tile, WM x WN waves,
+// each wave a (BT/WM) x (BT/WN) region of GI x GJ blocks of 32 x 32.  DB
+// double-buffers the fragments across stages (one wave per SIMD); without it
+// the second wave on each SIMD hides the fragment reads.
+template <int BT_, int WM_, int WN_, bool DB_>
+struct TileCfg {
+  static constexpr int BT = BT_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, THREADS = 64 * NW;
+  static constexpr int RM = BT / WM, RN = BT / WN;
+  static constexpr int GI = RM / 32, GJ = RN / 32;
+  static constexpr int LPW = (BT / 16) / NW;        // wave-loads per operand per stage
+  static constexpr bool DB = DB_;
+  static constexpr int BLOCKS_PER_CU = BT == 128 ? 2 : 1;
+  static_assert(LPW * NW * 16 == BT, "loads must cover the tile");
+};
+using TileSmall = TileCfg<128, 2, 2, true>;
+using TileBig8 = TileCfg<256, 2, 4, false>;
+
 struct EpiCtx {
   float alpha;
   int M, N, ti, tj, rbase, cbase;
-  int tr0, tc0;             // origin of this wave's (BT/2) x (BT/2) region in the output
-  half_t* lds0;             // this wave's staging region: rows [0, 64) and [64, BT/2)
+  int tr0, tc0;             // origin of this wave's region in the output
+  half_t* lds0;             // this wave's staging region (rows [0, RPA) and [RPA, RM))
   half_t* lds1;
   float* out32;
   half_t* out16;
@@ -76,75 +91,85 @@ struct EpiCtx {
   float c0, c1, c2, ka, kb, lr, decay;
 };
 
-// fp16 outputs go through LDS: each wave stages its (BT/2) x (BT/2) region
-// (rows of BT/2 halves, 16-byte chunks XOR-swizzled by the row so that the
-// accumulator writes, the row reads and the column reads below are free of
-// bank conflicts), then writes the row-major copy as 16-byte row segments and
-// the transposed copy as 16-byte segments of eight rows of one column, so
-// both copies leave as whole cache lines.
-template <int G>
-__device__ __forceinline__ int stage_off(int r, int c) {
-  constexpr int HB = 32 * G, CH = HB / 8;
-  const int sw = ((r & 7) ^ (r >> 3)) & (CH - 1);
-  return (r & 63) * HB + (((c >> 3) ^ sw) << 3) + (c & 7);
-}
+// K advances in stages of 32 through a 4-deep LDS ring filled by
+// global_load_lds_dwordx4 (one wave-instruction = 16 rows of 64 B).  Chunk c
+// (0..3) of row r is stored at position c ^ ((r >> 2) & 3) so 16-row fragment
+// reads hit distinct banks.
+constexpr int kSK = 32;                 // K per stage
+__device__ __forceinline__ int swz4(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+// s_waitcnt with vmcnt = v, other counters untouched (gfx9 encoding)
+#define WAIT_VMCNT(v) __builtin_amdgcn_s_waitcnt(((v) & 15) | (7 << 4) | (15 << 8) | (((v) >> 4) << 14))
+#define WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
 
-template <int G>
-__device__ __forceinline__ void stage_put(const EpiCtx& x, int r, int c, half4_t h) {
-  half_t* base = (G == 4 && r >= 64) ? x.lds1 : x.lds0;
-  *reinterpret_cast<half4_t*>(base + stage_off<G>(r, c)) = h;
-}
-
-template <int G>
-__device__ __forceinline__ void stage_flush(const EpiCtx& x, int col_off) {
-  constexpr int HB = 32 * G, CH = HB / 8;
-  const int lane = threadIdx.x & 63;
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // this wave's LDS writes done
-  asm volatile("" ::: "memory");
-  if (x.out16 != nullptr) {
-    constexpr int RPI = 64 / CH;                 // rows per instruction
-#pragma unroll
-    for (int it = 0; it < HB / RPI; ++it) {
-      const int r = it * RPI + lane / CH, k = lane % CH;
-      const half_t* base = (G == 4 && r >= 64) ? x.lds1 : x.lds0;
-      const half8_t v = *reinterpret_cast<const half8_t*>(base + stage_off<G>(r, k * 8));
-      *reinterpret_cast<half8_t*>(x.out16 + static_cast<size_t>(x.tr0 + r) * x.ld16 + col_off + x.tc0 + k * 8) = v;
-    }
+// fp16 outputs go through LDS: each wave stages its RM x RN region (rows of
+// RN halves, 16-byte chunks XOR-swizzled by the row so that the accumulator
+// writes, the row reads and the column reads below avoid bank conflicts),
+// then writes the row-major copy as 16-byte row segments and the transposed
+// copy as 16-byte segments of eight rows of one column, so both copies leave
+// as whole cache lines.  The stores are non-temporal: every block of a launch
+// finishes its tile at about the same time and the burst of outputs (larger
+// than L2) is the next launch's input, not this one's.  The region spans one or two ring slots of
+// BT * kSK halves; RPA rows fit in one.
+template <class C>
+struct Stage {
+  static constexpr int CH = C::RN / 8;
+  static constexpr int RPA = C::BT * kSK / C::RN;
+  __device__ static __forceinline__ int off(int r, int c) {
+    const int sw = ((r & 7) ^ (r >> 3)) & (CH - 1);
+    return (r % RPA) * C::RN + (((c >> 3) ^ sw) << 3) + (c & 7);
   }
-  if (x.out16T != nullptr) {
-    constexpr int LPC = HB / 8;                  // lanes per column (8 rows each)
-    constexpr int CPI = 64 / LPC;                // columns per instruction
-    const int r0 = 8 * (lane % LPC);
-    const half_t* base = (G == 4 && r0 >= 64) ? x.lds1 : x.lds0;
-#pragma unroll
-    for (int it = 0; it < HB / CPI; ++it) {
-      const int c = it * CPI + lane / LPC;
-      half8_t v;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = base[stage_off<G>(r0 + q, c)];
-      *reinterpret_cast<half8_t*>(x.out16T + static_cast<size_t>(x.tc0 + c) * x.ld16 + col_off + x.tr0 + r0) = v;
-    }
+  __device__ static __forceinline__ half_t* base(const EpiCtx& x, int r) {
+    return (C::RM > RPA && r >= RPA) ? x.lds1 : x.lds0;
   }
-  // the next staging pass overwrites this wave's region
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-  asm volatile("" ::: "memory");
-}
+  __device__ static __forceinline__ void put(const EpiCtx& x, int r, int c, half4_t h) {
+    *reinterpret_cast<half4_t*>(base(x, r) + off(r, c)) = h;
+  }
+  __device__ static __forceinline__ void flush(const EpiCtx& x, int col_off) {
+    const int lane = threadIdx.x & 63;
+    WAIT_LGKM0();                                  // this wave's LDS writes done
+    asm volatile("" ::: "memory");
+    if (x.out16 != nullptr) {
+      constexpr int RPI = 64 / CH;                 // rows per instruction
+#pragma unroll
+      for (int it = 0; it < C::RM / RPI; ++it) {
+        const int r = it * RPI + lane / CH, k = lane % CH;
+        const half8_t v = *reinterpret_cast<const half8_t*>(base(x, r) + off(r, k * 8));
+        __builtin_nontemporal_store(v, reinterpret_cast<half8_t*>(x.out16 + static_cast<size_t>(x.tr0 + r) * x.ld16 + col_off + x.tc0 + k * 8));
+      }
+    }
+    if (x.out16T != nullptr) {
+      constexpr int LPC = C::RM / 8;               // lanes per column (8 rows each)
+      constexpr int CPI = 64 / LPC;                // columns per instruction
+      const int r0 = 8 * (lane % LPC);
+      const half_t* b = base(x, r0);
+#pragma unroll
+      for (int it = 0; it < C::RN / CPI; ++it) {
+        const int c = it * CPI + lane / LPC;
+        half8_t v;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = b[off(r0 + q, c)];
+        __builtin_nontemporal_store(v, reinterpret_cast<half8_t*>(x.out16T + static_cast<size_t>(x.tc0 + c) * x.ld16 + col_off + x.tr0 + r0));
+      }
+    }
+    // the next staging pass overwrites this wave's region
+    WAIT_LGKM0();
+    asm volatile("" ::: "memory");
+  }
+};
 
-// Epilogue of one output tile, one instantiation per kind so that every
-// accumulator index is a compile-time constant (keeps them in registers).
-// Block (i, j) of a wave holds, in each lane, row rbase + 32 i and the four
-// groups of four consecutive columns cbase + 32 j + 8 g + e.
 // One pass over the accumulators.  fp32 kinds store directly; fp16 kinds
 // stage PART 0 (the fp16 values, or the hi halves of the split layout) or
-// PART 1 (the lo halves, y s - fp16(y s)) through LDS.
-template <int EPI, int G, int PART>
-__device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[G][G], const EpiCtx& x) {
+// PART 1 (the lo halves, y s - fp16(y s)) through LDS.  Block (i, j) of a
+// wave holds, in each lane, row rbase + 32 i and the four groups of four
+// consecutive columns cbase + 32 j + 8 g + e.
+template <class C, int EPI, int PART>
+__device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ], const EpiCtx& x) {
   constexpr bool kF16 = EPI == EPI_NS_T || EPI == EPI_NS_Y1 || EPI == EPI_STORE16 || EPI == EPI_NS_FINAL;
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
+  for (int i = 0; i < C::GI; ++i) {
     const int r = x.rbase + i * 32;
 #pragma unroll
-    for (int jg = 0; jg < 4 * G; ++jg) {
+    for (int jg = 0; jg < 4 * C::GJ; ++jg) {
       const int j = jg >> 2, g = jg & 3;
       const int c0 = x.cbase + j * 32 + g * 8;
       float v[4];
@@ -215,35 +240,16 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[G][G], const
           const half_t hi = static_cast<half_t>(ys);
           h[e] = PART == 0 ? hi : static_cast<half_t>(ys - static_cast<float>(hi));
         }
-        stage_put<G>(x, r - x.tr0, c0 - x.tc0, h);
+        Stage<C>::put(x, r - x.tr0, c0 - x.tc0, h);
       }
     }
   }
-  if constexpr (kF16) stage_flush<G>(x, PART == 0 ? 0 : x.lo16);
+  if constexpr (kF16) Stage<C>::flush(x, PART == 0 ? 0 : x.lo16);
 }
 
-template <int EPI, int G, bool WL>
-__device__ __forceinline__ void epilogue(const floatx16 (&acc)[G][G], const EpiCtx& x) {
-  epilogue_pass<EPI, G, 0>(acc, x);
-  if constexpr (WL) epilogue_pass<EPI, G, 1>(acc, x);
-}
-
-// Block tile BT x BT, 4 waves in 2 x 2, each wave (BT/2) x (BT/2) made of
-// G x G blocks of 32 x 32 (G = BT / 64), v_mfma_f32_32x32x16_f16.
-// K advances in stages of 32 through an NS-deep LDS ring filled by
-// global_load_lds_dwordx4 (one wave-instruction = 16 rows of 64 B), issued
-// NS - 1 stages ahead.  Chunk c (0..3) of row r is stored at position
-// c ^ ((r >> 2) & 3) so 16-row fragment reads hit distinct banks.
-constexpr int kSK = 32;                 // K per stage
-__device__ __forceinline__ int swz4(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
-// s_waitcnt with vmcnt = v, other counters untouched (gfx9 encoding)
-#define WAIT_VMCNT(v) __builtin_amdgcn_s_waitcnt(((v) & 15) | (7 << 4) | (15 << 8) | (((v) >> 4) << 14))
-
-template <int BT, int EPI, bool WL>
-__global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kernel(GemmArgs args) {
-  constexpr int G = BT / 64;
-  constexpr int NS = 4;                      // LDS ring depth
-  constexpr int LPW = BT / 16 / 4;           // wave-loads per operand per stage
+template <class C, int EPI, bool WL>
+__global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_nt_kernel(GemmArgs args) {
+  constexpr int BT = C::BT, GI = C::GI, GJ = C::GJ, LPW = C::LPW, NW = C::NW;
   __shared__ half_t sA0[BT * kSK], sA1[BT * kSK], sA2[BT * kSK], sA3[BT * kSK];
   __shared__ half_t sB0[BT * kSK], sB1[BT * kSK], sB2[BT * kSK], sB3[BT * kSK];
   auto bufA = [&](auto bc) -> half_t* {
@@ -253,6 +259,10 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   auto bufB = [&](auto bc) -> half_t* {
     constexpr int b = decltype(bc)::value;
     if constexpr (b == 0) return sB0; else if constexpr (b == 1) return sB1; else if constexpr (b == 2) return sB2; else return sB3;
+  };
+  // slot k of the eight ring arrays in order sA0..sA3, sB0..sB3
+  auto slot = [&](int k) -> half_t* {
+    return k == 0 ? sA0 : k == 1 ? sA1 : k == 2 ? sA2 : k == 3 ? sA3 : k == 4 ? sB0 : k == 5 ? sB1 : k == 6 ? sB2 : sB3;
   };
 
   const TileRef tr = args.tiles[args.tile_begin + blockIdx.x];
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WN, wn = wave % C::WN;
 
   const int st_per_seg = Kp / kSK;
   const int nst = (args.split_in ? 3 : 1) * st_per_seg;
@@ -284,7 +294,7 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
     const int offB = (seg == 1 ? Kp : 0) + k0;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-      const int h = wave + 4 * q;
+      const int h = wave + NW * q;
       const int row = 16 * h + lr;
       const int c = swz4(row, lp);
       const half_t* ga = A + static_cast<size_t>(row) * lda + offA + c * 8;
@@ -296,84 +306,110 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
     }
   };
 
-  floatx16 acc[G][G];
+  floatx16 acc[GI][GJ];
 #pragma unroll
-  for (int i = 0; i < G; ++i)
+  for (int i = 0; i < GI; ++i)
 #pragma unroll
-    for (int j = 0; j < G; ++j) acc[i][j] = floatx16{};
+    for (int j = 0; j < GJ; ++j) acc[i][j] = floatx16{};
 
   const int frow = lane & 31;
   const int fch = lane >> 5;
-  const int arow = wm * (BT / 2) + frow;
-  const int brow = wn * (BT / 2) + frow;
-  auto lfrag = [&](half8_t (&fa)[G], half8_t (&fb)[G], auto bc, int s) {
+  const int arow = wm * C::RM + frow;
+  const int brow = wn * C::RN + frow;
+  auto lfrag = [&](half8_t (&fa)[GI], half8_t (&fb)[GJ], auto bc, int s) {
     const half_t* lA = bufA(bc);
     const half_t* lB = bufB(bc);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
+    for (int j = 0; j < GJ; ++j) {
       const int r = brow + 32 * j;
       fb[j] = *reinterpret_cast<const half8_t*>(&lB[r * kSK + swz4(r, 2 * s + fch) * 8]);
     }
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
+    for (int i = 0; i < GI; ++i) {
       const int r = arow + 32 * i;
       fa[i] = *reinterpret_cast<const half8_t*>(&lA[r * kSK + swz4(r, 2 * s + fch) * 8]);
     }
   };
-  auto mma = [&](const half8_t (&fa)[G], const half8_t (&fb)[G]) {
+  auto mma = [&](const half8_t (&fa)[GI], const half8_t (&fb)[GJ]) {
 #pragma unroll
-    for (int i = 0; i < G; ++i)
+    for (int i = 0; i < GI; ++i)
 #pragma unroll
-      for (int j = 0; j < G; ++j)
+      for (int j = 0; j < GJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // Stage st's fragments are in registers F[st & 1] when body st starts.
-  // Body st: wait for this wave's copies of stage st+1, barrier (all waves'
-  // copies of st+1 visible, all waves done reading slot st % 4), refill slot
-  // st % 4 with stage st+4, then read stage st+1's fragments while the MFMAs
-  // of stage st run.
   gload(0, I0{});
   gload(1 < nst ? 1 : nst - 1, I1{});
   gload(2 < nst ? 2 : nst - 1, I2{});
   gload(3 < nst ? 3 : nst - 1, I3{});
-  half8_t fa[2][2][G], fb[2][2][G];   // [register set][k16 step][fragment]
-  WAIT_VMCNT(3 * 2 * LPW);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  lfrag(fa[0][0], fb[0][0], I0{}, 0);
-  lfrag(fa[0][1], fb[0][1], I0{}, 1);
-  auto body = [&](int st, auto rc, auto sc, auto nc) {
-    constexpr int R = decltype(rc)::value;      // register set of stage st
-    WAIT_VMCNT(2 * 2 * LPW);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const int ld = st + 4;
-    gload(ld < nst ? ld : nst - 1, sc);           // slot st % 4
-    lfrag(fa[R ^ 1][0], fb[R ^ 1][0], nc, 0);     // stage st+1 from slot (st+1) % 4
-    lfrag(fa[R ^ 1][1], fb[R ^ 1][1], nc, 1);
-    mma(fa[R][0], fb[R][0]);
-    mma(fa[R][1], fb[R][1]);
-    __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPW, 0);
+  if constexpr (C::DB) {
+    // Stage st's fragments are in registers F[st & 1] when body st starts.
+    // Body st: wait for this wave's copies of stage st+1, barrier (all waves'
+    // copies of st+1 visible, all waves done reading slot st % 4), refill
+    // slot st % 4 with stage st+4, then read stage st+1's fragments while the
+    // MFMAs of stage st run.
+    half8_t fa[2][2][GI], fb[2][2][GJ];   // [register set][k16 step][fragment]
+    WAIT_VMCNT(3 * 2 * LPW);
+    barrier();
+    lfrag(fa[0][0], fb[0][0], I0{}, 0);
+    lfrag(fa[0][1], fb[0][1], I0{}, 1);
+    auto body = [&](int st, auto rc, auto sc, auto nc) {
+      constexpr int R = decltype(rc)::value;      // register set of stage st
+      WAIT_VMCNT(2 * 2 * LPW);
+      barrier();
+      const int ld = st + 4;
+      gload(ld < nst ? ld : nst - 1, sc);           // slot st % 4
+      lfrag(fa[R ^ 1][0], fb[R ^ 1][0], nc, 0);     // stage st+1 from slot (st+1) % 4
+      lfrag(fa[R ^ 1][1], fb[R ^ 1][1], nc, 1);
+      mma(fa[R][0], fb[R][0]);
+      mma(fa[R][1], fb[R][1]);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPW, 0);
 #pragma unroll
-    for (int q = 0; q < 4 * G; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * G * G / (4 * G), 0);
+      for (int q = 0; q < 2 * (GI + GJ); ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * GI * GJ / (2 * (GI + GJ)), 0);
+      }
+      // stage st+1's fragments complete before the next body's MFMAs
+      WAIT_LGKM0();
+    };
+    for (int st = 0; st < nst; st += 4) {
+      body(st, I0{}, I0{}, I1{});
+      body(st + 1, I1{}, I1{}, I2{});
+      body(st + 2, I0{}, I2{}, I3{});
+      body(st + 3, I1{}, I3{}, I0{});
     }
-    // stage st+1's fragments complete before the next body's MFMAs
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-  };
-  for (int st = 0; st < nst; st += 4) {
-    body(st, I0{}, I0{}, I1{});
-    body(st + 1, I1{}, I1{}, I2{});
-    body(st + 2, I0{}, I2{}, I3{});
-    body(st + 3, I1{}, I3{}, I0{});
+  } else {
+    // Body st: wait for this wave's copies of stage st, barrier (all waves'
+    // copies of st visible, all waves done reading slot (st-1) % 4), refill
+    // that slot with stage st+3, read stage st's fragments and run its MFMAs;
+    // the other wave on the SIMD covers the fragment latency.
+    half8_t fa[2][GI], fb[2][GJ];         // [k16 step][fragment]
+    auto body = [&](int st, auto sc, auto pc) {
+      // issued so far: stages up to st + 2 (st + 3 before the first body)
+      if (st == 0) WAIT_VMCNT(3 * 2 * LPW); else WAIT_VMCNT(2 * 2 * LPW);
+      barrier();
+      const int ld = st + 3;
+      if (st > 0) gload(ld < nst ? ld : nst - 1, pc);  // slot (st - 1) % 4
+      lfrag(fa[0], fb[0], sc, 0);
+      lfrag(fa[1], fb[1], sc, 1);
+      mma(fa[0], fb[0]);
+      mma(fa[1], fb[1]);
+    };
+    for (int st = 0; st < nst; st += 4) {
+      body(st, I0{}, I3{});
+      body(st + 1, I1{}, I0{});
+      body(st + 2, I2{}, I1{});
+      body(st + 3, I3{}, I2{});
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   // every wave is done reading the ring: its slots become the staging area
@@ -381,21 +417,18 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
 
   // ---------------- epilogue ----------------
   EpiCtx ctx;
-  ctx.tr0 = ti * BT + wm * (BT / 2);
-  ctx.tc0 = tj * BT + wn * (BT / 2);
-  if constexpr (BT == 256) {
-    ctx.lds0 = wave == 0 ? sA0 : wave == 1 ? sA2 : wave == 2 ? sB0 : sB2;
-    ctx.lds1 = wave == 0 ? sA1 : wave == 1 ? sA3 : wave == 2 ? sB1 : sB3;
-  } else {
-    ctx.lds0 = ctx.lds1 = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sA3;
-  }
+  ctx.tr0 = ti * BT + wm * C::RM;
+  ctx.tc0 = tj * BT + wn * C::RN;
+  constexpr int kSlots = (C::RM + Stage<C>::RPA - 1) / Stage<C>::RPA;   // ring slots per wave region
+  ctx.lds0 = slot(kSlots * wave);
+  ctx.lds1 = slot(kSlots * wave + kSlots - 1);
   ctx.alpha = 1.0f / (args.scal[P.sA] * args.scal[P.sB]);
   ctx.M = P.M;
   ctx.N = P.N;
   ctx.ti = ti;
   ctx.tj = tj;
-  ctx.rbase = ti * BT + wm * (BT / 2) + frow;
-  ctx.cbase = tj * BT + wn * (BT / 2) + fch * 4;
+  ctx.rbase = ctx.tr0 + frow;
+  ctx.cbase = ctx.tc0 + fch * 4;
   ctx.out32 = P.out32.kind != REF_NONE ? reinterpret_cast<float*>(resolve(P.out32, args.ws, args.user)) : nullptr;
   ctx.out16 = P.out16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16, args.ws, args.user)) : nullptr;
   ctx.out16T = P.out16T.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16T, args.ws, args.user)) : nullptr;
@@ -414,7 +447,8 @@ __global__ __launch_bounds__(kGemmThreads, BT == 128 ? 2 : 1) void gemm_nt_kerne
   ctx.kb = args.kb;
   ctx.lr = args.lr;
   ctx.decay = args.decay;
-  epilogue<EPI, G, WL>(acc, ctx);
+  epilogue_pass<C, EPI, 0>(acc, ctx);
+  if constexpr (WL) epilogue_pass<C, EPI, 1>(acc, ctx);
 }
 
 // ---------------------------------------------------------------------------
@@ -743,13 +777,13 @@ __global__ void zero_int_kernel(int* p) { *p = 0; }
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <int BT>
-hipError_t launch_gemm_bt(const GemmArgs& a, int n_tiles, int epi, hipStream_t s) {
-  const dim3 grid(n_tiles), block(kGemmThreads);
+template <class C>
+hipError_t launch_gemm_cfg(const GemmArgs& a, int n_tiles, int epi, hipStream_t s) {
+  const dim3 grid(n_tiles), block(C::THREADS);
   // fp16-output kinds come in two forms: fp16 values only, or the split
   // layout's hi and lo halves (write_lo); the fp32 kinds ignore write_lo
   const bool wl = a.write_lo != 0;
-#define OKLS_GEMM(E, W) hipLaunchKernelGGL((gemm_nt_kernel<BT, E, W>), grid, block, 0, s, a)
+#define OKLS_GEMM(E, W) hipLaunchKernelGGL((gemm_nt_kernel<C, E, W>), grid, block, 0, s, a)
   switch (epi) {
     case EPI_STORE32: OKLS_GEMM(EPI_STORE32, false); break;
     case EPI_SYRK: OKLS_GEMM(EPI_SYRK, false); break;
@@ -766,8 +800,8 @@ hipError_t launch_gemm_bt(const GemmArgs& a, int n_tiles, int epi, hipStream_t s
 
 hipError_t launch_gemm(const GemmArgs& a, int n_tiles, int tile, int epi, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  if (tile == 256) return launch_gemm_bt<256>(a, n_tiles, epi, s);
-  if (tile == 128) return launch_gemm_bt<128>(a, n_tiles, epi, s);
+  if (tile == 256) return launch_gemm_cfg<TileBig8>(a, n_tiles, epi, s);
+  if (tile == 128) return launch_gemm_cfg<TileSmall>(a, n_tiles, epi, s);
   return hipErrorInvalidValue;
 }
 
