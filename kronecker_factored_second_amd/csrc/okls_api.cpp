@@ -347,11 +347,11 @@ struct Planner {
     // one epilogue kind per launch (the kernel is specialised on it)
     r.epi = ps.front().epi;
     // the large tile when every problem's padded sides are multiples of it and
-    // the launch has enough blocks of it: 64 for the fp16-output kinds (their
-    // outputs are staged through LDS; measured faster than the 128 tile from a
-    // quarter of a block per CU on up), 512 for the fp32-output kinds (stored
-    // from registers, where the 128 tile's second block per CU wins below two
-    // blocks per CU); otherwise the 128 tile
+    // the launch has enough blocks of it: 64 for the fp16-output kinds
+    // (measured faster than the 128 tile from a quarter of a block per CU on
+    // up), 512 for the fp32-output kinds (factor and whitening products,
+    // whose read-modify-write epilogues favour the 128 tile's second block
+    // per CU below two blocks per CU); otherwise the 128 tile
     r.tile = kBigTile;
     long big_tiles = 0;
     for (const GemmProb& p : ps) {

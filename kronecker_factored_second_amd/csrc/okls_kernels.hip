@@ -157,6 +157,129 @@ struct Stage {
   }
 };
 
+// fp32 outputs (plain store, the weight update, the factor update with its
+// mirrored lower triangle) also go through LDS, half of the wave's region at
+// a time (RM/2 rows of RN floats fill one ring slot): 16-byte chunks of four
+// floats, XOR-swizzled by (r ^ (r >> 2)) so that the accumulator writes, the
+// row reads and the 4-row column reads of the mirror avoid bank conflicts.
+// Rows leave as 16-byte segments (read-modify-write for the update and the
+// factor); the factor's mirrored copy leaves as 16-byte segments of four
+// rows of one column.
+template <class C>
+struct Stage32 {
+  static constexpr int HR = C::RM / 2;          // rows per half
+  static constexpr int CH = C::RN / 4;          // chunks per row
+  static_assert(HR * C::RN * 4 <= C::BT * kSK * 2, "half region fits one ring slot");
+  __device__ static __forceinline__ int off(int r, int c) {
+    const int sw = (r ^ (r >> 2)) & (CH - 1);
+    return r * C::RN + (((c >> 2) ^ sw) << 2) + (c & 3);
+  }
+};
+
+template <class C, int EPI>
+__device__ __forceinline__ void epilogue_f32(const floatx16 (&acc)[C::GI][C::GJ], const EpiCtx& x) {
+  using S32 = Stage32<C>;
+  float* lds = reinterpret_cast<float*>(x.lds0);
+  const int lane = threadIdx.x & 63;
+  const bool vec_ok = (x.ld32 & 3) == 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // stage rows [h HR, (h + 1) HR) of the wave's region
+#pragma unroll
+    for (int i = h * C::GI / 2; i < (h + 1) * C::GI / 2; ++i) {
+      const int rl = x.rbase - x.tr0 + i * 32 - h * S32::HR;
+#pragma unroll
+      for (int jg = 0; jg < 4 * C::GJ; ++jg) {
+        const int j = jg >> 2, g = jg & 3;
+        const int cl = x.cbase - x.tc0 + j * 32 + g * 8;
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * x.alpha;
+        *reinterpret_cast<floatx4*>(lds + S32::off(rl, cl)) = v;
+      }
+    }
+    WAIT_LGKM0();
+    asm volatile("" ::: "memory");
+    const int rb = x.tr0 + h * S32::HR;           // global row of local row 0
+    constexpr int RPI = 64 / S32::CH;             // rows per instruction
+#pragma unroll
+    for (int it = 0; it < S32::HR / RPI; ++it) {
+      const int rl = it * RPI + lane / S32::CH, k = lane % S32::CH;
+      const int r = rb + rl, c = x.tc0 + 4 * k;
+      floatx4 v = *reinterpret_cast<const floatx4*>(lds + S32::off(rl, 4 * k));
+      if (r < x.M) {
+        float* row = x.out32 + static_cast<size_t>(r) * x.ld32;
+        const bool full = vec_ok && c + 3 < x.N;
+        if constexpr (EPI == EPI_STORE32) {
+          if (full) {
+            *reinterpret_cast<floatx4*>(row + c) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c + e < x.N) row[c + e] = v[e];
+          }
+        } else if constexpr (EPI == EPI_UPDATE) {
+          if (full) {
+            const floatx4 w = *reinterpret_cast<const floatx4*>(row + c);
+            *reinterpret_cast<floatx4*>(row + c) = x.decay * w - (x.lr * x.c0) * v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c + e < x.N) row[c + e] = x.decay * row[c + e] - x.lr * x.c0 * v[e];
+          }
+        } else {  // EPI_SYRK: S <- c0*S + c1*v + c2*I on the upper triangle
+          const bool diag_tile = x.ti == x.tj;
+          if (full && (!diag_tile || r <= c)) {
+            const floatx4 o = *reinterpret_cast<const floatx4*>(row + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = x.c0 * o[e] + x.c1 * v[e] + (r == c + e ? x.c2 : 0.0f);
+            *reinterpret_cast<floatx4*>(row + c) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (c + e < x.N && (!diag_tile || r <= c + e)) {
+                v[e] = x.c0 * row[c + e] + x.c1 * v[e] + (r == c + e ? x.c2 : 0.0f);
+                row[c + e] = v[e];
+              }
+            }
+          }
+          *reinterpret_cast<floatx4*>(lds + S32::off(rl, 4 * k)) = v;   // the value the mirror copies
+        }
+      }
+    }
+    if constexpr (EPI == EPI_SYRK) {
+      // mirrored copy: S[c][r] = S[r][c] for the upper elements, r < c
+      WAIT_LGKM0();
+      asm volatile("" ::: "memory");
+      constexpr int LPC = S32::HR / 4;            // lanes per column (4 rows each)
+      constexpr int CPI = 64 / LPC;               // columns per instruction
+      const int r0 = 4 * (lane % LPC);
+      const bool diag_tile = x.ti == x.tj;
+#pragma unroll
+      for (int it = 0; it < C::RN / CPI; ++it) {
+        const int cl = it * CPI + lane / LPC;
+        const int c = x.tc0 + cl, r = rb + r0;
+        if (c < x.N) {
+          floatx4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = lds[S32::off(r0 + q, cl)];
+          float* row = x.out32 + static_cast<size_t>(c) * x.ld32;
+          if (vec_ok && r + 3 < x.M && (!diag_tile || r + 3 < c)) {
+            *reinterpret_cast<floatx4*>(row + r) = v;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (r + q < x.M && (!diag_tile || r + q < c)) row[r + q] = v[q];
+          }
+        }
+      }
+    }
+    // the next half overwrites this wave's staging slot
+    WAIT_LGKM0();
+    asm volatile("" ::: "memory");
+  }
+}
+
 // One pass over the accumulators.  fp32 kinds store directly; fp16 kinds
 // stage PART 0 (the fp16 values, or the hi halves of the split layout) or
 // PART 1 (the lo halves, y s - fp16(y s)) through LDS.  Block (i, j) of a
@@ -447,8 +570,12 @@ __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_nt_kernel(G
   ctx.kb = args.kb;
   ctx.lr = args.lr;
   ctx.decay = args.decay;
-  epilogue_pass<C, EPI, 0>(acc, ctx);
-  if constexpr (WL) epilogue_pass<C, EPI, 1>(acc, ctx);
+  if constexpr (EPI == EPI_STORE32 || EPI == EPI_UPDATE || EPI == EPI_SYRK) {
+    epilogue_f32<C, EPI>(acc, ctx);
+  } else {
+    epilogue_pass<C, EPI, 0>(acc, ctx);
+    if constexpr (WL) epilogue_pass<C, EPI, 1>(acc, ctx);
+  }
 }
 
 // ---------------------------------------------------------------------------
