@@ -9,9 +9,11 @@ accumulation.  Gradients are generated once and kept resident in HBM; the
 timed steps cycle through them.
 
 Prints one JSON line: matrices/s, step latency, the dominant kernel's
-roofline (gemm_nt_kernel, algorithmic FLOPs over its summed launch times,
-measured with HIP events on the launch stream during the timed steps) and
-the CPU oracle's time on a bounded sample of the same workload.
+roofline (gemm_nt_kernel: algorithmic FLOPs over the union of its launches'
+intervals, measured with HIP events on the launch streams during the timed
+steps; the average launch duration is reported beside it for comparison
+with rocprofv3) and the CPU oracle's time on a bounded sample of the same
+workload.
 """
 import argparse
 import json
@@ -231,12 +233,16 @@ def main():
     finite = opt.check_finite()
 
     g_ms = sum(prof[k]["ms"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
+    # the three GEMM categories run in different phases of the step, so their
+    # busy times add; within the Newton-Schulz phase two chains overlap
+    g_busy = sum(prof[k]["busy_ms"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     g_fl = sum(prof[k]["flops"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     g_n = sum(prof[k]["launches"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     g_b = sum(prof[k]["bytes"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
-    achieved = g_fl / (g_ms * 1e-3) / 1e12
+    achieved = g_fl / (g_busy * 1e-3) / 1e12
+    per_launch = g_fl / (g_ms * 1e-3) / 1e12
     ns = prof["ns_gemm"]
-    ns_tflops = ns["flops"] / (ns["ms"] * 1e-3) / 1e12
+    ns_tflops = ns["flops"] / (ns["busy_ms"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": w.n_matrices / (ms_step * 1e-3),
@@ -256,17 +262,20 @@ def main():
                    "matrices": w.n_matrices, "parallelism": "single GPU"},
         "step_latency_ms": ms_step,
         "ns_chain": {"tflops": ns_tflops, "frac_fp16_peak": ns_tflops / PEAK_FP16_TFLOPS,
-                     "ms_per_step": ns["ms"] / max(prof["steps"], 1), "launches_per_step": ns["launches"] / max(prof["steps"], 1)},
+                     "ms_per_step": ns["busy_ms"] / max(prof["steps"], 1), "launches_per_step": ns["launches"] / max(prof["steps"], 1)},
         "roofline": {"kernel": "gemm_nt_kernel", "bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS,
                      "traffic": measured_traffic() if (args.workload == "c2" and args.precision == "fp16") else None,
-                     "avg_launch_us": g_ms * 1e3 / max(g_n, 1), "launches_per_step": g_n / max(prof["steps"], 1),
+                     "method": "algorithmic FLOPs of every gemm_nt_kernel launch over the union of their intervals "
+                               "(HIP events on the launch streams); the two Newton-Schulz chains' launches overlap",
+                     "avg_launch_us": g_ms * 1e3 / max(g_n, 1), "achieved_per_launch_duration": per_launch,
+                     "launches_per_step": g_n / max(prof["steps"], 1),
                      "algorithmic_flops_per_step": g_fl / max(prof["steps"], 1),
                      "algorithmic_bytes_per_launch": g_b / max(g_n, 1)},
-        "profile_ms_per_step": {k: prof[k]["ms"] / max(prof["steps"], 1) for k in okls.PROFILE_CATEGORIES},
-        "hbm_kernels": {kern: {"bound": "hbm", "achieved": prof[cat]["bytes"] / (prof[cat]["ms"] * 1e-3) / 1e9,
+        "profile_ms_per_step": {k: prof[k]["busy_ms"] / max(prof["steps"], 1) for k in okls.PROFILE_CATEGORIES},
+        "hbm_kernels": {kern: {"bound": "hbm", "achieved": prof[cat]["bytes"] / (prof[cat]["busy_ms"] * 1e-3) / 1e9,
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": prof[cat]["bytes"] / (prof[cat]["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               "frac": prof[cat]["bytes"] / (prof[cat]["busy_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                "bytes_per_step": prof[cat]["bytes"] / max(prof["steps"], 1),
                                "launches_per_step": prof[cat]["launches"] / max(prof["steps"], 1)}
                         for kern, cat in (("stats_kernel", "stats"), ("cast_kernel", "cast")) if prof[cat]["ms"] > 0},

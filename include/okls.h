@@ -147,10 +147,13 @@ okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* tensors,
 int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_steps);
 
 /* Per-launch timing.  While enabled, okls_step records a HIP event before and
- * after every launch on its stream (events are created on first use and
- * owned by the handle).  okls_profile_read synchronises the stream of the
- * last profiled step, sums the elapsed times per category since the last
- * read and clears them.  Categories (index into the arrays):
+ * after every launch on the stream it runs on (events are created on first
+ * use and owned by the handle).  okls_profile_read synchronises the last
+ * profiled step, sums the elapsed times per category since the last read
+ * (ms) and the length of the union of each category's launch intervals
+ * (busy_ms: launches of the two concurrent Newton-Schulz chains overlap, so
+ * their durations add up to more than the time the category keeps the GPU
+ * busy), then clears them.  Categories (index into the arrays):
  *   0 Newton-Schulz GEMMs, 1 factor GEMMs (cross-preconditioning and the
  *   factor update), 2 whitening GEMMs (with the fused weight update),
  *   3 statistics kernels, 4 cast / momentum kernels.
@@ -166,7 +169,8 @@ int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_s
  * halves; fp32 outputs 4). */
 #define OKLS_PROFILE_CATEGORIES 5
 typedef struct {
-    double ms[OKLS_PROFILE_CATEGORIES];
+    double ms[OKLS_PROFILE_CATEGORIES];       /* sum of the launches' durations */
+    double busy_ms[OKLS_PROFILE_CATEGORIES];  /* length of the union of the launches' intervals */
     double flops[OKLS_PROFILE_CATEGORIES];
     double bytes[OKLS_PROFILE_CATEGORIES];
     int64_t launches[OKLS_PROFILE_CATEGORIES];

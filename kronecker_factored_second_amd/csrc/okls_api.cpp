@@ -99,7 +99,7 @@ struct MatBufs {
   FacBufs fa, fb;
 };
 
-enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2 };
+enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4 };
 
 struct LaunchRec {
   int type = L_STAT;
@@ -112,9 +112,18 @@ struct LaunchRec {
   int cat = 0;                  // profiling category
   int tile = kTile;             // GEMM block tile
   int epi = EPI_STORE32;        // GEMM epilogue kind (one per launch)
+  int stream = 0;               // 0: the caller's stream; 1: the library's side stream (between a fork and a join)
 };
 
 enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4 };
+
+// The factors' Newton-Schulz chains are independent: they run as two chains
+// of launches, one on the caller's stream and one on a side stream, so one
+// chain's launches fill the CUs the other's leave idle in their last round.
+#ifndef OKLS_NS_STREAMS
+#define OKLS_NS_STREAMS 2
+#endif
+constexpr int kNsStreams = OKLS_NS_STREAMS;
 
 // Global scale slots
 enum { SL_ONE = 0, SL_Y = 1, SL_Z = 2, SL_T = 3, SL_FIRST_DYN = 4 };
@@ -146,8 +155,16 @@ struct okls_handle {
   std::vector<std::pair<int, int>> pending; // (category, event pair index) of unread launches
   size_t next_event = 0;
   okls_profile_stats acc{};
+  // side stream of the second Newton-Schulz chain and its fork / join events
+  // (created by okls_init when the plan forks; default priority)
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  size_t part_stride = 0;                   // floats between the streams' partial regions
   ~okls_handle() {
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    if (ev_fork != nullptr) (void)hipEventDestroy(ev_fork);
+    if (ev_join != nullptr) (void)hipEventDestroy(ev_join);
+    if (side != nullptr) (void)hipStreamDestroy(side);
   }
 };
 
@@ -736,13 +753,50 @@ struct Planner {
       src.push_back(user_ref(REF_SB, mb.group, boff(mb)));
       pdst.push_back(user_ref(REF_PB, mb.group, boff(mb)));
     }
-    if (okls_mode) {
-      ns_chain(L, facs, src, pdst, 0, 0);
-    } else {
-      ns_chain(L, facs, src, pdst, 1, 0);
-      std::vector<Ref> rsrc;
-      for (FacBufs* f : facs) rsrc.push_back(ws_ref(f->R32));
-      ns_chain(L, facs, rsrc, pdst, 0, 1);
+    // split the factors into kNsStreams sets of near-equal cost (d^3, largest first)
+    std::vector<size_t> order(facs.size());
+    for (size_t f = 0; f < order.size(); ++f) order[f] = f;
+    std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return facs[x]->d > facs[y]->d; });
+    const int nset = std::min<int>(kNsStreams, static_cast<int>(facs.size()));
+    std::vector<double> load(nset, 0.0);
+    std::vector<std::vector<size_t>> sets(nset);
+    for (size_t f : order) {
+      const int b = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+      sets[b].push_back(f);
+      load[b] += std::pow(static_cast<double>(facs[f]->d), 3.0);
+    }
+    std::vector<std::vector<LaunchRec>> chains(nset);
+    for (int c = 0; c < nset; ++c) {
+      std::sort(sets[c].begin(), sets[c].end());
+      std::vector<FacBufs*> cf;
+      std::vector<Ref> cs, cp;
+      for (size_t f : sets[c]) { cf.push_back(facs[f]); cs.push_back(src[f]); cp.push_back(pdst[f]); }
+      if (okls_mode) {
+        ns_chain(chains[c], cf, cs, cp, 0, 0);
+      } else {
+        ns_chain(chains[c], cf, cs, cp, 1, 0);
+        std::vector<Ref> rsrc;
+        for (FacBufs* f : cf) rsrc.push_back(ws_ref(f->R32));
+        ns_chain(chains[c], cf, rsrc, cp, 0, 1);
+      }
+      for (LaunchRec& r : chains[c]) r.stream = c;
+    }
+    if (nset > 1) {
+      LaunchRec fork;
+      fork.type = L_FORK;
+      L.push_back(fork);
+    }
+    // issue the chains' launches interleaved so both streams have work queued
+    for (size_t i = 0;; ++i) {
+      bool any = false;
+      for (int c = 0; c < nset; ++c)
+        if (i < chains[c].size()) { L.push_back(chains[c][i]); any = true; }
+      if (!any) break;
+    }
+    if (nset > 1) {
+      LaunchRec join;
+      join.type = L_JOIN;
+      L.push_back(join);
     }
 
     // 6. whitening: V^T = P_b N^T (n x m), then U = P_a V fused with the update
@@ -816,7 +870,14 @@ struct Planner {
     if (ws_bufs.size() != chunks.size()) return false;
     for (size_t ci = 0; ci < chunks.size(); ++ci) {
       cur_bufs = &ws_bufs[ci];
+      bool forked = false;
       for (const LaunchRec& r : chunks[ci]) {
+        if (r.type == L_FORK || r.type == L_JOIN) {
+          if (forked == (r.type == L_FORK)) return false;
+          forked = r.type == L_FORK;
+          continue;
+        }
+        if (r.stream < 0 || r.stream >= kNsStreams || (r.stream != 0 && !forked)) return false;
         if (r.type == L_GEMM) {
           if (r.first < 0 || r.first + r.count > static_cast<int>(tiles.size())) return false;
           if (r.tile != kTile && r.tile != kBigTile) return false;
@@ -902,6 +963,7 @@ struct Planner {
           if (blk != r.nblocks) return false;
         }
       }
+      if (forked) return false;
     }
     return true;
   }
@@ -945,7 +1007,7 @@ WsLayout ws_layout(Planner& P) {
   w.stat = take(P.stat_jobs.size() * sizeof(StatJob));
   w.cast = take(P.cast_jobs.size() * sizeof(CastJob));
   w.scal = take(static_cast<size_t>(P.n_slots) * sizeof(float));
-  w.part = take(static_cast<size_t>(P.max_partials) * 2 * sizeof(float));
+  w.part = take(static_cast<size_t>(P.max_partials) * 2 * sizeof(float) * kNsStreams);   // one region per stream
   w.flag = take(sizeof(int));
   w.chunk = off;
   w.total = off + P.chunk_bytes;
@@ -1054,6 +1116,18 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_part = w.part;
   h->off_flag = w.flag;
   h->chunks = P.chunks;
+  h->part_stride = static_cast<size_t>(P.max_partials) * 2;
+  bool forks = false;
+  for (const std::vector<LaunchRec>& L : P.chunks)
+    for (const LaunchRec& r : L) forks = forks || r.type == L_FORK;
+  if (forks) {
+    if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
+      delete h;
+      return OKLS_ERR_HIP;
+    }
+  }
   h->na = P.na;
   h->nb = P.nb;
   for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
@@ -1165,6 +1239,18 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
   for (const std::vector<LaunchRec>& L : h->chunks) {
     for (const LaunchRec& r : L) {
       hipError_t e = hipSuccess;
+      if (r.type == L_FORK) {          // the side stream starts after everything queued so far
+        if (hipEventRecord(h->ev_fork, s) != hipSuccess || hipStreamWaitEvent(h->side, h->ev_fork, 0) != hipSuccess)
+          return OKLS_ERR_HIP;
+        continue;
+      }
+      if (r.type == L_JOIN) {          // the caller's stream continues after the side stream's work
+        if (hipEventRecord(h->ev_join, h->side) != hipSuccess || hipStreamWaitEvent(s, h->ev_join, 0) != hipSuccess)
+          return OKLS_ERR_HIP;
+        continue;
+      }
+      const hipStream_t rs = r.stream == 0 ? s : h->side;
+      float* rpart = part + static_cast<size_t>(r.stream) * h->part_stride;
       size_t ev = 0;
       if (h->prof) {
         ev = h->next_event;
@@ -1174,25 +1260,25 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
           h->events.push_back(x);
         }
         h->next_event += 2;
-        if (hipEventRecord(h->events[ev], s) != hipSuccess) return OKLS_ERR_HIP;
+        if (hipEventRecord(h->events[ev], rs) != hipSuccess) return OKLS_ERR_HIP;
       }
       if (r.type == L_STAT) {
         StatArgs a;
         a.jobs = reinterpret_cast<const StatJob*>(ws + h->off_stat) + r.first;
         a.n_jobs = r.count;
         a.blk_offset = 0;
-        a.partials = part;
+        a.partials = rpart;
         a.beta1 = static_cast<float>(b1);
         a.s_t = static_cast<float>(s_t);
         a.ws = ws;
         a.user = user;
-        e = launch_stats(a, r.nblocks, s);
+        e = launch_stats(a, r.nblocks, rs);
       } else if (r.type == L_CAST) {
         CastArgs a;
         a.jobs = reinterpret_cast<const CastJob*>(ws + h->off_cast) + r.first;
         a.n_jobs = r.count;
         a.blk_offset = 0;
-        a.partials = part;
+        a.partials = rpart;
         a.scal = scal;
         a.beta1 = static_cast<float>(b1);
         a.s_t = static_cast<float>(s_t);
@@ -1200,7 +1286,7 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.kb = r.kb;
         a.ws = ws;
         a.user = user;
-        e = launch_cast(a, r.nblocks, s);
+        e = launch_cast(a, r.nblocks, rs);
       } else {
         GemmArgs a;
         a.probs = reinterpret_cast<const GemmProb*>(ws + h->off_probs);
@@ -1216,11 +1302,11 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.ws = ws;
         a.scal = scal;
         a.user = user;
-        e = launch_gemm(a, r.count, r.tile, r.epi, s);
+        e = launch_gemm(a, r.count, r.tile, r.epi, rs);
       }
       if (e != hipSuccess) return OKLS_ERR_HIP;
       if (h->prof) {
-        if (hipEventRecord(h->events[ev + 1], s) != hipSuccess) return OKLS_ERR_HIP;
+        if (hipEventRecord(h->events[ev + 1], rs) != hipSuccess) return OKLS_ERR_HIP;
         h->pending.push_back({r.cat, static_cast<int>(ev)});
       }
     }
@@ -1274,11 +1360,32 @@ okls_status okls_profile_read(okls_handle* h, okls_profile_stats* out) {
   if (h == nullptr || out == nullptr) return OKLS_ERR_INVALID_ARG;
   if (!h->pending.empty()) {
     if (hipEventSynchronize(h->events[h->pending.back().second + 1]) != hipSuccess) return OKLS_ERR_HIP;
+    // intervals relative to the first event; union per category
+    const hipEvent_t ref = h->events[h->pending.front().second];
+    std::vector<std::vector<std::pair<float, float>>> iv(OKLS_PROFILE_CATEGORIES);
     for (const std::pair<int, int>& p : h->pending) {
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, h->events[p.second], h->events[p.second + 1]) != hipSuccess) return OKLS_ERR_HIP;
-      h->acc.ms[p.first] += ms;
+      float t0 = 0.f, t1 = 0.f;
+      if (hipEventElapsedTime(&t0, ref, h->events[p.second]) != hipSuccess ||
+          hipEventElapsedTime(&t1, ref, h->events[p.second + 1]) != hipSuccess)
+        return OKLS_ERR_HIP;
+      h->acc.ms[p.first] += t1 - t0;
       h->acc.launches[p.first] += 1;
+      iv[p.first].push_back({t0, t1});
+    }
+    for (int c = 0; c < OKLS_PROFILE_CATEGORIES; ++c) {
+      std::sort(iv[c].begin(), iv[c].end());
+      double busy = 0.0, lo = 0.0, hi = -1.0;
+      for (const std::pair<float, float>& x : iv[c]) {
+        if (x.first > hi) {
+          if (hi > lo) busy += hi - lo;
+          lo = x.first;
+          hi = x.second;
+        } else if (x.second > hi) {
+          hi = x.second;
+        }
+      }
+      if (hi > lo) busy += hi - lo;
+      h->acc.busy_ms[c] += busy;
     }
   }
   *out = h->acc;

@@ -43,7 +43,8 @@ class GroupTensors(ctypes.Structure):
 
 
 class ProfileStats(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 5), ("flops", ctypes.c_double * 5), ("bytes", ctypes.c_double * 5),
+    _fields_ = [("ms", ctypes.c_double * 5), ("busy_ms", ctypes.c_double * 5), ("flops", ctypes.c_double * 5),
+                ("bytes", ctypes.c_double * 5),
                 ("launches", ctypes.c_int64 * 5), ("steps", ctypes.c_int64)]
 
 
@@ -218,7 +219,8 @@ def profile_enable(h, enable: bool):
 def profile_read(h) -> dict:
     st = ProfileStats()
     _check("okls_profile_read", load().okls_profile_read(h, ctypes.byref(st)))
-    return {name: {"ms": st.ms[i], "flops": st.flops[i], "bytes": st.bytes[i], "launches": int(st.launches[i])}
+    return {name: {"ms": st.ms[i], "busy_ms": st.busy_ms[i], "flops": st.flops[i], "bytes": st.bytes[i],
+                   "launches": int(st.launches[i])}
             for i, name in enumerate(PROFILE_CATEGORIES)} | {"steps": int(st.steps)}
 
 
