@@ -28,12 +28,18 @@
  *     section: a 3-D parameter is N independent matrices that share the
  *     hyperparameters).
  *   - The caller owns every tensor and the workspace.  The library never
- *     allocates device memory; the handle owns host memory only.
- *   - All device work is enqueued on the given stream (a hipStream_t passed
- *     as void*; NULL is the default stream).  okls_init and okls_init_state
- *     synchronise that stream once (init uploads descriptor tables);
- *     okls_step never synchronises.  Device faults surface at the caller's
- *     next synchronisation.
+ *     allocates device memory; the handle owns host memory plus, when the
+ *     plan has more than one factor, one HIP stream and two events (created
+ *     by okls_init, destroyed by okls_destroy).
+ *   - All device work is ordered on the given stream (a hipStream_t passed
+ *     as void*; NULL is the default stream).  okls_step runs the second of
+ *     its two concurrent Newton-Schulz chains on the handle's stream, which
+ *     waits for everything queued on the given stream before it and which
+ *     the given stream waits for before the step's remaining work, so the
+ *     step is ordered on the given stream as a whole.  okls_init and
+ *     okls_init_state synchronise that stream once (init uploads descriptor
+ *     tables); okls_step never synchronises.  Device faults surface at the
+ *     caller's next synchronisation.
  *   - Errors are returned as okls_status; no exception crosses the ABI.
  *     Argument errors are detected on the host before any launch.
  *   - A handle may be used by one host thread at a time.  Two steps that
