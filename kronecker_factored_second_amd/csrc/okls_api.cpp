@@ -155,16 +155,18 @@ struct okls_handle {
   std::vector<std::pair<int, int>> pending; // (category, event pair index) of unread launches
   size_t next_event = 0;
   okls_profile_stats acc{};
-  // side stream of the second Newton-Schulz chain and its fork / join events
-  // (created by okls_init when the plan forks; default priority)
-  hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // side streams of the Newton-Schulz chains after the first, the fork event
+  // and one join event per side stream (created by okls_init when the plan
+  // forks; default priority)
+  std::vector<hipStream_t> side;
+  hipEvent_t ev_fork = nullptr;
+  std::vector<hipEvent_t> ev_join;
   size_t part_stride = 0;                   // floats between the streams' partial regions
   ~okls_handle() {
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
     if (ev_fork != nullptr) (void)hipEventDestroy(ev_fork);
-    if (ev_join != nullptr) (void)hipEventDestroy(ev_join);
-    if (side != nullptr) (void)hipStreamDestroy(side);
+    for (hipEvent_t e : ev_join) (void)hipEventDestroy(e);
+    for (hipStream_t x : side) (void)hipStreamDestroy(x);
   }
 };
 
@@ -1117,13 +1119,20 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_flag = w.flag;
   h->chunks = P.chunks;
   h->part_stride = static_cast<size_t>(P.max_partials) * 2;
-  bool forks = false;
+  int nstreams = 1;
   for (const std::vector<LaunchRec>& L : P.chunks)
-    for (const LaunchRec& r : L) forks = forks || r.type == L_FORK;
-  if (forks) {
-    if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
+    for (const LaunchRec& r : L) nstreams = std::max(nstreams, r.stream + 1);
+  if (nstreams > 1) {
+    bool ok = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) == hipSuccess;
+    for (int i = 1; i < nstreams && ok; ++i) {
+      hipStream_t x = nullptr;
+      hipEvent_t j = nullptr;
+      ok = hipStreamCreateWithFlags(&x, hipStreamNonBlocking) == hipSuccess;
+      if (ok) h->side.push_back(x);
+      ok = ok && hipEventCreateWithFlags(&j, hipEventDisableTiming) == hipSuccess;
+      if (ok) h->ev_join.push_back(j);
+    }
+    if (!ok) {
       delete h;
       return OKLS_ERR_HIP;
     }
@@ -1239,17 +1248,19 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
   for (const std::vector<LaunchRec>& L : h->chunks) {
     for (const LaunchRec& r : L) {
       hipError_t e = hipSuccess;
-      if (r.type == L_FORK) {          // the side stream starts after everything queued so far
-        if (hipEventRecord(h->ev_fork, s) != hipSuccess || hipStreamWaitEvent(h->side, h->ev_fork, 0) != hipSuccess)
-          return OKLS_ERR_HIP;
+      if (r.type == L_FORK) {          // the side streams start after everything queued so far
+        if (hipEventRecord(h->ev_fork, s) != hipSuccess) return OKLS_ERR_HIP;
+        for (hipStream_t x : h->side)
+          if (hipStreamWaitEvent(x, h->ev_fork, 0) != hipSuccess) return OKLS_ERR_HIP;
         continue;
       }
-      if (r.type == L_JOIN) {          // the caller's stream continues after the side stream's work
-        if (hipEventRecord(h->ev_join, h->side) != hipSuccess || hipStreamWaitEvent(s, h->ev_join, 0) != hipSuccess)
-          return OKLS_ERR_HIP;
+      if (r.type == L_JOIN) {          // the caller's stream continues after the side streams' work
+        for (size_t i = 0; i < h->side.size(); ++i)
+          if (hipEventRecord(h->ev_join[i], h->side[i]) != hipSuccess || hipStreamWaitEvent(s, h->ev_join[i], 0) != hipSuccess)
+            return OKLS_ERR_HIP;
         continue;
       }
-      const hipStream_t rs = r.stream == 0 ? s : h->side;
+      const hipStream_t rs = r.stream == 0 ? s : h->side[r.stream - 1];
       float* rpart = part + static_cast<size_t>(r.stream) * h->part_stride;
       size_t ev = 0;
       if (h->prof) {
