@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
                     (m == nullptr || (reinterpret_cast<uintptr_t>(m) & 15) == 0);
   if (flat) {
     const size_t n4 = (e1 - e0) / 4;
-    for (size_t q = threadIdx.x; q < n4; q += kStatThreads) {
+    auto quad = [&](size_t q) {
       const size_t o = e0 + 4 * q;
       float g[4];
       if (bf) {
@@ -665,7 +665,14 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc1(value(o + e, g[e]));
+    };
+    // four quads per thread and iteration: their loads are issued together
+    size_t q = threadIdx.x;
+    for (; q + 3 * kStatThreads < n4; q += 4 * kStatThreads) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) quad(q + u * kStatThreads);
     }
+    for (; q < n4; q += kStatThreads) quad(q);
     for (size_t o = e0 + 4 * n4 + threadIdx.x; o < e1; o += kStatThreads) {
       const float raw = bf ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]) : reinterpret_cast<const float*>(src)[o];
       acc1(value(o, raw));
@@ -706,14 +713,33 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
   const CastJob& J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
   const int lb = gb - J.blk_begin;
 
-  // ---- scale from the statistics partials (same fixed order in every block)
+  // ---- scale from the statistics partials (same fixed order in every block):
+  // per-thread strided sums, wave butterflies, then every thread combines the
+  // waves' results in wave order (one barrier)
   float amax = 0.0f, ss = 0.0f;
   for (int i = threadIdx.x; i < J.part_count; i += kCastThreads) {
     const float pa = a.partials[2 * (J.part_begin + i)];
     amax = (pa > amax || pa != pa) ? pa : amax;
     ss += a.partials[2 * (J.part_begin + i) + 1];
   }
-  block_reduce2<kCastThreads>(amax, ss, sh);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(amax, o, 64);
+    amax = (om > amax || om != om) ? om : amax;
+    ss += __shfl_xor(ss, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sh[2 * (threadIdx.x >> 6)] = amax;
+    sh[2 * (threadIdx.x >> 6) + 1] = ss;
+  }
+  __syncthreads();
+  amax = sh[0];
+  ss = sh[1];
+#pragma unroll
+  for (int w = 1; w < kCastThreads / 64; ++w) {
+    amax = (sh[2 * w] > amax || sh[2 * w] != sh[2 * w]) ? sh[2 * w] : amax;
+    ss += sh[2 * w + 1];
+  }
   float scale;
   float cinv = 1.0f;
   if (J.scale_mode == SC_ABSMAX) {
