@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--precision", default="fp16", choices=["fp16", "fp32"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    p.add_argument("--device-grads", action="store_true",
+                   help="Gaussian gradients of the workload's scale generated on the GPU (the default for "
+                        "workloads above 1e9 parameters, whose host recipes would take minutes per step)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 10 times (HBM counter calibration)")
     p.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV_DIR", "WRITE_CSV_DIR", "COMMANDS"),
@@ -197,20 +200,34 @@ def main():
     w = WL.workload(args.workload)
     dev = torch.device("cuda:0")
     bf16 = w.grad_dtype == "bf16"
+    big = w.n_params > 1e9
+    device_grads = args.device_grads or big
     params = [torch.zeros(b, m, n, device=dev) for (m, n, b) in w.groups]
     for gi, (m, n, b) in enumerate(w.groups):
-        for i in range(b):
-            params[gi][i].copy_(torch.from_numpy(WL.initial_weights(w, gi, i)))
-    n_bufs = 3
+        std = 0.07539 * (m / n) ** 0.5 / (n ** 0.5 + m ** 0.5)
+        if big:
+            params[gi].copy_(WL.device_filler(std, (b, m, n), seed=1000 + gi))
+        else:
+            for i in range(b):
+                params[gi][i].copy_(torch.from_numpy(WL.initial_weights(w, gi, i)))
+    n_bufs = 1 if big else 3
+    scale = {"gauss1": 1.0, "rowscaled": 0.02, "lowrank": 0.02, "gauss1e-3": 1e-3, "illcond": 0.07}[w.grad]
     grads = []
     for t in range(1, n_bufs + 1):
         gs = []
         for gi, (m, n, b) in enumerate(w.groups):
-            g = torch.from_numpy(np.stack([WL.gradient(w, gi, i, t) for i in range(b)])).to(dev)
+            if device_grads:
+                g = WL.device_filler(scale, (b, m, n), seed=(t << 8) + gi)
+            else:
+                g = torch.from_numpy(np.stack([WL.gradient(w, gi, i, t) for i in range(b)])).to(dev)
             gs.append(g.to(torch.bfloat16) if bf16 else g)
         grads.append(gs)
+    limit = None
+    if big:   # leave room for the caller's tensors: the workspace takes what the card has left
+        limit = torch.cuda.mem_get_info(0)[0] - sum(b * (m * n + 2 * m * m + 2 * n * n) * 4 for m, n, b in w.groups) \
+            - (8 << 30)
     opt = okls.OKLS(params, mode=w.mode, precision=args.precision,
-                    grad_dtype=torch.bfloat16 if bf16 else torch.float32)
+                    grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit)
     for i in range(args.warmup):
         opt.step(grads=grads[i % n_bufs])
     torch.cuda.synchronize()
@@ -258,7 +275,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: " + ", ".join(f"{b}x {m}x{n}" for m, n, b in w.groups) +
                    f" ({w.n_matrices} matrices, {w.n_params / 1e6:.1f}M params), {w.mode}, "
-                   f"{w.grad_dtype} gradients, precision {args.precision}",
+                   f"{w.grad_dtype} gradients" + (" (device Gaussian)" if device_grads else "") +
+                   f", precision {args.precision}" +
+                   (f", chunks of {opt.cfg.chunk_matrices} matrices" if opt.cfg.chunk_matrices else ""),
                    "matrices": w.n_matrices, "parallelism": "single GPU"},
         "step_latency_ms": ms_step,
         "ns_chain": {"tflops": ns_tflops, "frac_fp16_peak": ns_tflops / PEAK_FP16_TFLOPS,

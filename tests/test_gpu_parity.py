@@ -183,6 +183,34 @@ def test_step_is_deterministic():
         assert torch.equal(a, b)
 
 
+def test_step_is_ordered_on_the_callers_stream():
+    """okls_step on a non-default stream: the second Newton-Schulz chain runs on
+    the library's side stream, forked from and joined back into the caller's
+    stream.  Work the caller queues on its stream right after the step (here
+    copies of every state tensor) must see the finished step, and the result
+    must equal the default-stream run bit for bit."""
+    torch = pytest.importorskip("torch")
+    groups = [(256, 384, 2), (512, 128, 1)]
+
+    def run(stream):
+        opt, params = H.make(groups, precision="fp16")
+        copies = []
+        with torch.cuda.stream(stream):
+            for t in (1, 2):
+                gs = [torch.tensor(np.random.default_rng([t, gi]).standard_normal((b, m, n)).astype(np.float32),
+                                   device="cuda:0") for gi, (m, n, b) in enumerate(groups)]
+                opt.step(grads=gs)
+            for gi in range(len(groups)):
+                copies += [params[gi].clone()] + [opt.state[gi][k].clone() for k in ("M", "Sa", "Sb", "Pa", "Pb")]
+        torch.cuda.synchronize()
+        return [c.cpu() for c in copies]
+
+    ref = run(torch.cuda.default_stream())
+    got = run(torch.cuda.Stream())
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
 def test_check_finite_flags_nan():
     torch = pytest.importorskip("torch")
     opt, params = H.make([(64, 64, 1)], precision="fp16")
