@@ -17,7 +17,7 @@ title and section.  Short names used in the citations:
              Nyström Sketching", section 2, equations (2)-(3).
 
 Where the pages leave a step open, the reading taken is named in the
-docstring as R1..R12; the list of readings lives with the project's design
+docstring as R1..R15; the list of readings lives with the project's design
 notes.  All arithmetic is numpy float64; eigendecompositions use LAPACK
 (numpy.linalg.eigh).  Nothing here is blocked, fused or reordered beyond the
 definitions.
@@ -42,6 +42,8 @@ Parity status of each function (what pins it in the CPU test-suite):
   whiten / update_weights ...... G=0 step gives W' = (1 - lr wd) W exactly
   okls_step / shampoo_step ..... orthogonal equivariance, transpose identity,
                                  3-D batch = per-matrix results
+  Hyper.refresh (R15) .......... worked example with a refresh period: the singular
+                                 values follow the last refresh's accumulation count
 """
 from __future__ import annotations
 
@@ -67,9 +69,17 @@ class Hyper:
     ns_steps: int = 10                  # [OKLS] intro: 10-step inverse-root method
     ns_floor: float = 1e-3              # R4: lower end of the design interval for sqrt(lambda / ||S||_F)
     ns_damping: float = 5e-3            # R13: nu; the iteration roots S + (nu/sqrt(d)) ||S||_F I
+    root_period: int = 1                # roots refreshed on steps 1, 1 + p, 1 + 2p, ... (R15)
 
     def peak(self) -> float:
         return self.lr if self.lr_peak is None else self.lr_peak
+
+    def refresh(self, t: int) -> bool:
+        """R15: whether step t (1-based) recomputes the roots.  [OKLS] intro
+        refreshes every step (p = 1, no staleness); [SHAMPOO] "Shampoo" and
+        [CLEAN] section 2 describe recomputing the roots only every few steps
+        and keeping them in between."""
+        return self.root_period <= 1 or (t - 1) % self.root_period == 0
 
 
 # ---------------------------------------------------------------------------
@@ -356,13 +366,17 @@ def okls_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "exact
     coupled Newton-Schulz iteration in fp64.  Both are always reported."""
     G = np.asarray(G, dtype=np.float64)
     Sa, Sb = factor_update_okls(st.Sa, st.Sb, st.Pa, st.Pb, G, hp.beta2, hp.eps)
-    coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
-    Pa_ns, _ = ns_inv_sqrt(Sa, coeffs, hp.ns_damping)
-    Pb_ns, _ = ns_inv_sqrt(Sb, coeffs, hp.ns_damping)
-    if root == "exact":
-        (Pa, ka), (Pb, kb) = inv_root_exact(Sa, 2), inv_root_exact(Sb, 2)
+    if not hp.refresh(t):          # R15: the previous roots are kept
+        Pa, Pb = st.Pa, st.Pb
+        Pa_ns, Pb_ns, ka, kb = Pa, Pb, float("nan"), float("nan")
     else:
-        Pa, Pb, ka, kb = Pa_ns, Pb_ns, cond(Sa), cond(Sb)
+        coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+        Pa_ns, _ = ns_inv_sqrt(Sa, coeffs, hp.ns_damping)
+        Pb_ns, _ = ns_inv_sqrt(Sb, coeffs, hp.ns_damping)
+        if root == "exact":
+            (Pa, ka), (Pb, kb) = inv_root_exact(Sa, 2), inv_root_exact(Sb, 2)
+        else:
+            Pa, Pb, ka, kb = Pa_ns, Pb_ns, cond(Sa), cond(Sb)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
     U = whiten(Pa, N, Pb)
     W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
@@ -375,13 +389,17 @@ def shampoo_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ex
     decoupled decay as in OKLS."""
     G = np.asarray(G, dtype=np.float64)
     Sa, Sb = factor_update_shampoo(st.Sa, st.Sb, G, hp.eps)
-    coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
-    Pa_ns = ns_inv_quarter(Sa, coeffs, hp.ns_damping)
-    Pb_ns = ns_inv_quarter(Sb, coeffs, hp.ns_damping)
-    if root == "exact":
-        (Pa, ka), (Pb, kb) = inv_root_exact(Sa, 4), inv_root_exact(Sb, 4)
+    if not hp.refresh(t):          # R15: the previous roots are kept
+        Pa, Pb = st.Pa, st.Pb
+        Pa_ns, Pb_ns, ka, kb = Pa, Pb, float("nan"), float("nan")
     else:
-        Pa, Pb, ka, kb = Pa_ns, Pb_ns, cond(Sa), cond(Sb)
+        coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+        Pa_ns = ns_inv_quarter(Sa, coeffs, hp.ns_damping)
+        Pb_ns = ns_inv_quarter(Sb, coeffs, hp.ns_damping)
+        if root == "exact":
+            (Pa, ka), (Pb, kb) = inv_root_exact(Sa, 4), inv_root_exact(Sb, 4)
+        else:
+            Pa, Pb, ka, kb = Pa_ns, Pb_ns, cond(Sa), cond(Sb)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
     U = whiten(Pa, N, Pb)
     W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)

@@ -92,6 +92,50 @@ def test_worked_example_full_shampoo_step_first_update():
     np.testing.assert_allclose(np.linalg.svd(r.U, compute_uv=False), [1.0, 1.0], atol=1e-6)
 
 
+def test_refresh_period_worked_example():
+    """Roots refreshed every 3 steps on the worked example's fixed G (Shampoo
+    sums): the factor accumulates every step, but P_a G P_b keeps the
+    singular values of the last refresh, r^{-1/2} after r accumulations --
+    1 at t = 1..3 and 0.5 at t = 4..6 (the page's value for four
+    accumulations), then 1/sqrt(7)."""
+    g = _gold("shampoo_worked_example.json")
+    G = np.array(g["G"], dtype=np.float64)
+    hp = O.Hyper(eps=1e-12, root_period=3)
+    st = O.init_state(np.zeros_like(G), hp.eps)
+    for t in range(1, 8):
+        r = O.shampoo_step(st, G, hp, t)
+        st = r.state
+        last = 1 + 3 * ((t - 1) // 3)
+        sv = np.linalg.svd(st.Pa @ G @ st.Pb, compute_uv=False)
+        np.testing.assert_allclose(sv, [last ** -0.5] * 2, atol=1e-6)
+        np.testing.assert_allclose(st.Sa, t * (G @ G.T) + (t + 1) * hp.eps * np.eye(2), rtol=1e-12)
+    assert abs(0.5 - 4 ** -0.5) < 1e-15 and abs(g["singular_values_after_4_identical_accumulations"][0] - 0.5) < 1e-3
+
+
+@pytest.mark.parametrize("mode", ["okls", "shampoo"])
+def test_refresh_period_keeps_roots_and_updates_factors(mode):
+    """A non-refresh step is a full step with the previous roots: the factors,
+    momentum, whitening and update are unchanged in form; period 1 is the
+    default every-step refresh."""
+    rng = np.random.default_rng(41)
+    m, n = 7, 5
+    st = O.init_state(rng.standard_normal((m, n)), 1e-9)
+    hp1, hp2 = O.Hyper(), O.Hyper(root_period=2)
+    for t in (1, 2, 3):
+        G = rng.standard_normal((m, n))
+        r1 = O.step(st, G, hp1, t, mode, "exact")
+        r2 = O.step(st, G, hp2, t, mode, "exact")
+        np.testing.assert_array_equal(r1.state.Sa, r2.state.Sa)
+        np.testing.assert_array_equal(r1.state.M, r2.state.M)
+        if t == 2:
+            np.testing.assert_array_equal(r2.state.Pa, st.Pa)
+            np.testing.assert_array_equal(r2.state.Pb, st.Pb)
+            np.testing.assert_allclose(r2.U, st.Pa @ r2.N @ st.Pb, rtol=1e-12)
+        else:
+            np.testing.assert_array_equal(r1.state.Pa, r2.state.Pa)
+        st = r2.state
+
+
 def test_problem14_exponent_and_scale():
     g = _gold("shampoo_problem14_scale.json")
     G = np.array(g["G"], dtype=np.float64)
