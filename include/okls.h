@@ -95,6 +95,11 @@ typedef struct {
     float ns_damping;          /* nu: the root is taken of S + (nu / sqrt(d)) ||S||_F I, which
                                   keeps the rounded iteration positive definite; default
                                   5e-3 for the fp16 path, 2e-3 suits the split-fp16 path */
+    int32_t root_period;       /* p >= 1: the roots are recomputed on steps t = 1, 1 + p,
+                                  1 + 2p, ... and kept in between (the factors, momentum,
+                                  whitening and update run every step).  1 (default) is the
+                                  README's every-step refresh; the Shampoo chapter and the
+                                  Clean paper describe refreshing only every few steps. */
 } okls_config;
 
 typedef struct {

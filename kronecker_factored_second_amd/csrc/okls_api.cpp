@@ -145,10 +145,13 @@ struct okls_handle {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_scal = 0, off_part = 0, off_flag = 0;
-  std::vector<std::vector<LaunchRec>> chunks;
+  std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
+  std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them
   std::vector<double> na, nb;
   double step_flops[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
   double step_bytes[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+  double step_flops_stale[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+  double step_bytes_stale[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
   // profiling
   bool prof = false;
   std::vector<hipEvent_t> events;           // pool
@@ -190,6 +193,7 @@ okls_status check_config(const okls_config* c) {
   if (!(c->lr_peak > 0.f && std::isfinite(c->lr_peak))) return OKLS_ERR_INVALID_ARG;
   if (!(c->ns_floor > 0.f && c->ns_floor < 1.f)) return OKLS_ERR_INVALID_ARG;
   if (!(c->ns_damping >= 0.f && c->ns_damping < 1.f)) return OKLS_ERR_INVALID_ARG;
+  if (c->root_period < 1) return OKLS_ERR_INVALID_ARG;
   return OKLS_OK;
 }
 
@@ -219,7 +223,8 @@ struct Planner {
   std::vector<TileRef> tiles;
   std::vector<StatJob> stat_jobs;
   std::vector<CastJob> cast_jobs;
-  std::vector<std::vector<LaunchRec>> chunks;
+  std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
+  std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them (root_period > 1)
   std::map<std::string, std::pair<int, int>> tile_cache;
 
   std::vector<std::map<size_t, size_t>> ws_bufs;   // per chunk: workspace buffer offset -> bytes
@@ -343,6 +348,8 @@ struct Planner {
   int gemm_cat = CAT_NS;   // category of the GEMM launches being planned
   double step_flops[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
   double step_bytes[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+  double step_flops_stale[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+  double step_bytes_stale[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
 
   void add_gemm(std::vector<LaunchRec>& L, const std::vector<GemmProb>& ps, bool upper, int split_in,
                 int write_lo, float ka = 0.f, float kb = 0.f) {
@@ -594,19 +601,26 @@ struct Planner {
   // P16 produced by the chain of this factor, in Z[K % 2]
   size_t p16_of(const FacBufs& F) const { return F.Z[cfg.ns_steps & 1]; }
 
-  void plan_chunk(std::vector<MatBufs>& mats, size_t base) {
-    // rebase offsets
-    for (MatBufs& mb : mats) {
-      size_t* offs[] = {&mb.G16, &mb.G16T, &mb.N16, &mb.Xa32, &mb.XbT32, &mb.Xa16, &mb.XbT16, &mb.VT32, &mb.VT16};
-      for (size_t* o : offs) *o += base;
-      for (FacBufs* f : {&mb.fa, &mb.fb}) {
-        f->Y[0] += base; f->Y[1] += base; f->Z[0] += base; f->Z[1] += base; f->T += base; f->R32 += base;
-        f->YT[0] += base; f->YT[1] += base; f->ZT[0] += base; f->ZT[1] += base; f->TT += base;
+  // refresh: the launches of a step that recomputes the roots; otherwise the
+  // roots are kept and the whitening uses the fp16 copies of the previous P.
+  // The first call for a chunk rebases its buffers and registers them.
+  void plan_chunk(std::vector<MatBufs>& mats, size_t base, bool refresh, bool rebase) {
+    if (rebase) {
+      for (MatBufs& mb : mats) {
+        size_t* offs[] = {&mb.G16, &mb.G16T, &mb.N16, &mb.Xa32, &mb.XbT32, &mb.Xa16, &mb.XbT16, &mb.VT32, &mb.VT16};
+        for (size_t* o : offs) *o += base;
+        for (FacBufs* f : {&mb.fa, &mb.fb}) {
+          f->Y[0] += base; f->Y[1] += base; f->Z[0] += base; f->Z[1] += base; f->T += base; f->R32 += base;
+          f->YT[0] += base; f->YT[1] += base; f->ZT[0] += base; f->ZT[1] += base; f->TT += base;
+        }
       }
+      ws_bufs.emplace_back();
+      for (const std::pair<size_t, size_t>& b : pending) ws_bufs.back()[b.first + base] = b.second;
     }
-    ws_bufs.emplace_back();
-    for (const std::pair<size_t, size_t>& b : pending) ws_bufs.back()[b.first + base] = b.second;
     std::vector<LaunchRec> L;
+    // fp16 copies of the previous preconditioners: the OKLS factor products
+    // read them, and a step that keeps the roots whitens with them
+    const bool p_old = okls_mode || !refresh;
     const int fs = cfg.factor_split;
     auto gdt = [&](const MatBufs& mb) { return groups[mb.group].g_dtype; };
     auto goff = [&](const MatBufs& mb) {
@@ -623,7 +637,7 @@ struct Planner {
       st.push_back(StatSpec{gk, user_ref(REF_G, mb.group, goff(mb)), mb.n, no_ref(), 0, mb.m, mb.n});
       st.push_back(StatSpec{ST_NESTEROV, user_ref(REF_G, mb.group, goff(mb)), mb.n,
                             user_ref(REF_M, mb.group, moff(mb)), gdt(mb) == OKLS_BF16, mb.m, mb.n});
-      if (okls_mode) {
+      if (p_old) {
         st.push_back(StatSpec{ST_F32, user_ref(REF_PA, mb.group, aoff(mb)), mb.m, no_ref(), 0, mb.m, mb.m});
         st.push_back(StatSpec{ST_F32, user_ref(REF_PB, mb.group, boff(mb)), mb.n, no_ref(), 0, mb.n, mb.n});
       }
@@ -631,7 +645,7 @@ struct Planner {
     std::vector<std::pair<int, int>> parts = add_stats(L, st);
     // 2. casts
     std::vector<CastSpec> cs;
-    const int per = okls_mode ? 4 : 2;
+    const int per = p_old ? 4 : 2;
     for (size_t q = 0; q < mats.size(); ++q) {
       const MatBufs& mb = mats[q];
       const bool bf = gdt(mb) == OKLS_BF16;
@@ -652,7 +666,7 @@ struct Planner {
       nn.dst_ld = mb.ldn; nn.dst_lo = mb.np; nn.parts = parts[per * q + 1]; nn.scale_mode = SC_ABSMAX;
       nn.scale_slot = mb.s_n; nn.write_lo = fs;
       cs.push_back(nn);
-      if (okls_mode) {
+      if (p_old) {
         const FacBufs* fl[2] = {&mb.fa, &mb.fb};
         const int kinds[2] = {REF_PA, REF_PB};
         const size_t offs[2] = {aoff(mb), boff(mb)};
@@ -675,7 +689,8 @@ struct Planner {
       step_flops[CAT_FACTOR] += (okls_mode ? 3.0 : 1.0) * m * n * (m + n);
       step_flops[CAT_WHITEN] += 2.0 * m * n * (m + n);
       // 3K - 3 GEMMs per inverse square root (27 at K = 10); two chains for the fourth root
-      step_flops[CAT_NS] += (okls_mode ? 1.0 : 2.0) * (3.0 * cfg.ns_steps - 3.0) * 2.0 * (m * m * m + n * n * n);
+      if (refresh)
+        step_flops[CAT_NS] += (okls_mode ? 1.0 : 2.0) * (3.0 * cfg.ns_steps - 3.0) * 2.0 * (m * m * m + n * n * n);
     }
     gemm_cat = CAT_FACTOR;
     if (okls_mode) {
@@ -745,61 +760,67 @@ struct Planner {
 
     // 5. inverse roots
     gemm_cat = CAT_NS;
-    std::vector<FacBufs*> facs;
-    std::vector<Ref> src, pdst;
-    for (MatBufs& mb : mats) {
-      facs.push_back(&mb.fa);
-      src.push_back(user_ref(REF_SA, mb.group, aoff(mb)));
-      pdst.push_back(user_ref(REF_PA, mb.group, aoff(mb)));
-      facs.push_back(&mb.fb);
-      src.push_back(user_ref(REF_SB, mb.group, boff(mb)));
-      pdst.push_back(user_ref(REF_PB, mb.group, boff(mb)));
-    }
-    // split the factors into kNsStreams sets of near-equal cost (d^3, largest first)
-    std::vector<size_t> order(facs.size());
-    for (size_t f = 0; f < order.size(); ++f) order[f] = f;
-    std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return facs[x]->d > facs[y]->d; });
-    const int nset = std::min<int>(kNsStreams, static_cast<int>(facs.size()));
-    std::vector<double> load(nset, 0.0);
-    std::vector<std::vector<size_t>> sets(nset);
-    for (size_t f : order) {
-      const int b = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
-      sets[b].push_back(f);
-      load[b] += std::pow(static_cast<double>(facs[f]->d), 3.0);
-    }
-    std::vector<std::vector<LaunchRec>> chains(nset);
-    for (int c = 0; c < nset; ++c) {
-      std::sort(sets[c].begin(), sets[c].end());
-      std::vector<FacBufs*> cf;
-      std::vector<Ref> cs, cp;
-      for (size_t f : sets[c]) { cf.push_back(facs[f]); cs.push_back(src[f]); cp.push_back(pdst[f]); }
-      if (okls_mode) {
-        ns_chain(chains[c], cf, cs, cp, 0, 0);
-      } else {
-        ns_chain(chains[c], cf, cs, cp, 1, 0);
-        std::vector<Ref> rsrc;
-        for (FacBufs* f : cf) rsrc.push_back(ws_ref(f->R32));
-        ns_chain(chains[c], cf, rsrc, cp, 0, 1);
+    if (refresh) {
+      std::vector<FacBufs*> facs;
+      std::vector<Ref> src, pdst;
+      for (MatBufs& mb : mats) {
+        facs.push_back(&mb.fa);
+        src.push_back(user_ref(REF_SA, mb.group, aoff(mb)));
+        pdst.push_back(user_ref(REF_PA, mb.group, aoff(mb)));
+        facs.push_back(&mb.fb);
+        src.push_back(user_ref(REF_SB, mb.group, boff(mb)));
+        pdst.push_back(user_ref(REF_PB, mb.group, boff(mb)));
       }
-      for (LaunchRec& r : chains[c]) r.stream = c;
+      // split the factors into kNsStreams sets of near-equal cost (d^3, largest first)
+      std::vector<size_t> order(facs.size());
+      for (size_t f = 0; f < order.size(); ++f) order[f] = f;
+      std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return facs[x]->d > facs[y]->d; });
+      const int nset = std::min<int>(kNsStreams, static_cast<int>(facs.size()));
+      std::vector<double> load(nset, 0.0);
+      std::vector<std::vector<size_t>> sets(nset);
+      for (size_t f : order) {
+        const int b = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+        sets[b].push_back(f);
+        load[b] += std::pow(static_cast<double>(facs[f]->d), 3.0);
+      }
+      std::vector<std::vector<LaunchRec>> chains(nset);
+      for (int c = 0; c < nset; ++c) {
+        std::sort(sets[c].begin(), sets[c].end());
+        std::vector<FacBufs*> cf;
+        std::vector<Ref> cs, cp;
+        for (size_t f : sets[c]) { cf.push_back(facs[f]); cs.push_back(src[f]); cp.push_back(pdst[f]); }
+        if (okls_mode) {
+          ns_chain(chains[c], cf, cs, cp, 0, 0);
+        } else {
+          ns_chain(chains[c], cf, cs, cp, 1, 0);
+          std::vector<Ref> rsrc;
+          for (FacBufs* f : cf) rsrc.push_back(ws_ref(f->R32));
+          ns_chain(chains[c], cf, rsrc, cp, 0, 1);
+        }
+        for (LaunchRec& r : chains[c]) r.stream = c;
+      }
+      if (nset > 1) {
+        LaunchRec fork;
+        fork.type = L_FORK;
+        L.push_back(fork);
+      }
+      // issue the chains' launches interleaved so both streams have work queued
+      for (size_t i = 0;; ++i) {
+        bool any = false;
+        for (int c = 0; c < nset; ++c)
+          if (i < chains[c].size()) { L.push_back(chains[c][i]); any = true; }
+        if (!any) break;
+      }
+      if (nset > 1) {
+        LaunchRec join;
+        join.type = L_JOIN;
+        L.push_back(join);
+      }
     }
-    if (nset > 1) {
-      LaunchRec fork;
-      fork.type = L_FORK;
-      L.push_back(fork);
-    }
-    // issue the chains' launches interleaved so both streams have work queued
-    for (size_t i = 0;; ++i) {
-      bool any = false;
-      for (int c = 0; c < nset; ++c)
-        if (i < chains[c].size()) { L.push_back(chains[c][i]); any = true; }
-      if (!any) break;
-    }
-    if (nset > 1) {
-      LaunchRec join;
-      join.type = L_JOIN;
-      L.push_back(join);
-    }
+    // the fp16 preconditioner each whitening product reads: the chain's own
+    // output when the roots were just recomputed, else the copy cast above
+    auto pw = [&](const FacBufs& F) { return ws_ref(refresh ? p16_of(F) : F.T); };
+    auto pw_scale = [&](const FacBufs& F) { return refresh ? F.s_p16 : F.s_pold; };
 
     // 6. whitening: V^T = P_b N^T (n x m), then U = P_a V fused with the update
     gemm_cat = CAT_WHITEN;
@@ -807,9 +828,9 @@ struct Planner {
       std::vector<GemmProb> pv;
       for (const MatBufs& mb : mats) {
         GemmProb p = prob();
-        p.A = ws_ref(p16_of(mb.fb)); p.lda = mb.fb.ld; p.B = ws_ref(mb.N16); p.ldb = mb.ldn;
+        p.A = pw(mb.fb); p.lda = mb.fb.ld; p.B = ws_ref(mb.N16); p.ldb = mb.ldn;
         p.M = mb.n; p.N = mb.m; p.Kp = mb.np; p.Mp = mb.np; p.Np = mb.mp; p.epi = EPI_STORE32;
-        p.out32 = ws_ref(mb.VT32); p.ld32 = mb.m; p.sA = mb.fb.s_p16; p.sB = mb.s_n;
+        p.out32 = ws_ref(mb.VT32); p.ld32 = mb.m; p.sA = pw_scale(mb.fb); p.sB = mb.s_n;
         pv.push_back(p);
       }
       add_gemm(L, pv, false, fs, 0);
@@ -829,16 +850,16 @@ struct Planner {
       std::vector<GemmProb> pu;
       for (const MatBufs& mb : mats) {
         GemmProb p = prob();
-        p.A = ws_ref(p16_of(mb.fa)); p.lda = mb.fa.ld; p.B = ws_ref(mb.VT16); p.ldb = mb.ldm;
+        p.A = pw(mb.fa); p.lda = mb.fa.ld; p.B = ws_ref(mb.VT16); p.ldb = mb.ldm;
         p.M = mb.m; p.N = mb.n; p.Kp = mb.mp; p.Mp = mb.mp; p.Np = mb.np; p.epi = EPI_UPDATE;
-        p.out32 = user_ref(REF_W, mb.group, moff(mb)); p.ld32 = mb.n; p.sA = mb.fa.s_p16; p.sB = mb.s_vt;
+        p.out32 = user_ref(REF_W, mb.group, moff(mb)); p.ld32 = mb.n; p.sA = pw_scale(mb.fa); p.sB = mb.s_vt;
         p.c0 = static_cast<float>(std::sqrt(static_cast<double>(mb.m) / mb.n) /
                                   (std::sqrt(static_cast<double>(mb.m)) + std::sqrt(static_cast<double>(mb.n))));
         pu.push_back(p);
       }
       add_gemm(L, pu, false, fs, 0);
     }
-    chunks.push_back(std::move(L));
+    (refresh ? chunks : chunks_stale).push_back(std::move(L));
   }
 
   // ---- host-side extent checks of every descriptor against the buffer it
@@ -869,11 +890,15 @@ struct Planner {
   bool slot_ok(int s) const { return s >= 0 && s < n_slots; }
 
   bool validate() {
-    if (ws_bufs.size() != chunks.size()) return false;
-    for (size_t ci = 0; ci < chunks.size(); ++ci) {
+    if (!validate_plan(chunks)) return false;
+    return cfg.root_period <= 1 ? chunks_stale.empty() : validate_plan(chunks_stale);
+  }
+  bool validate_plan(const std::vector<std::vector<LaunchRec>>& plan_chunks) {
+    if (ws_bufs.size() != plan_chunks.size()) return false;
+    for (size_t ci = 0; ci < plan_chunks.size(); ++ci) {
       cur_bufs = &ws_bufs[ci];
       bool forked = false;
-      for (const LaunchRec& r : chunks[ci]) {
+      for (const LaunchRec& r : plan_chunks[ci]) {
         if (r.type == L_FORK || r.type == L_JOIN) {
           if (forked == (r.type == L_FORK)) return false;
           forked = r.type == L_FORK;
@@ -989,7 +1014,21 @@ struct Planner {
       int slot = SL_FIRST_DYN;
       chunk_bytes = std::max(chunk_bytes, layout_chunk(c, slot));
       n_slots = std::max(n_slots, slot);
-      plan_chunk(c, base);
+      plan_chunk(c, base, true, true);
+    }
+    if (cfg.root_period > 1) {
+      // the plan of the steps that keep the roots, over the same buffers,
+      // with its own algorithmic work
+      double f[OKLS_PROFILE_CATEGORIES], b[OKLS_PROFILE_CATEGORIES];
+      for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
+        f[i] = step_flops[i]; b[i] = step_bytes[i];
+        step_flops[i] = step_bytes[i] = 0.0;
+      }
+      for (std::vector<MatBufs>& c : all) plan_chunk(c, base, false, false);
+      for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
+        step_flops_stale[i] = step_flops[i]; step_bytes_stale[i] = step_bytes[i];
+        step_flops[i] = f[i]; step_bytes[i] = b[i];
+      }
     }
   }
 };
@@ -1058,6 +1097,7 @@ void okls_default_config(okls_config* c) {
   c->lr_peak = 0.09434f;
   c->ns_floor = 1e-3f;
   c->ns_damping = 5e-3f;
+  c->root_period = 1;
 }
 
 size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups) {
@@ -1118,6 +1158,7 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_part = w.part;
   h->off_flag = w.flag;
   h->chunks = P.chunks;
+  h->chunks_stale = P.chunks_stale;
   h->part_stride = static_cast<size_t>(P.max_partials) * 2;
   int nstreams = 1;
   for (const std::vector<LaunchRec>& L : P.chunks)
@@ -1142,6 +1183,8 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
     h->step_flops[i] = P.step_flops[i];
     h->step_bytes[i] = P.step_bytes[i];
+    h->step_flops_stale[i] = P.step_flops_stale[i];
+    h->step_bytes_stale[i] = P.step_bytes_stale[i];
   }
 
   std::vector<float> scal(static_cast<size_t>(P.n_slots), 1.0f);
@@ -1238,14 +1281,16 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
   float* scal = reinterpret_cast<float*>(ws + h->off_scal);
   float* part = reinterpret_cast<float*>(ws + h->off_part);
 
+  // the roots are recomputed on steps 1, 1 + p, 1 + 2p, ... (p = root_period)
+  const bool refresh = h->cfg.root_period <= 1 || (step - 1) % h->cfg.root_period == 0;
   if (h->prof) {
     h->acc.steps += 1;
     for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
-      h->acc.flops[i] += h->step_flops[i];
-      h->acc.bytes[i] += h->step_bytes[i];
+      h->acc.flops[i] += refresh ? h->step_flops[i] : h->step_flops_stale[i];
+      h->acc.bytes[i] += refresh ? h->step_bytes[i] : h->step_bytes_stale[i];
     }
   }
-  for (const std::vector<LaunchRec>& L : h->chunks) {
+  for (const std::vector<LaunchRec>& L : refresh ? h->chunks : h->chunks_stale) {
     for (const LaunchRec& r : L) {
       hipError_t e = hipSuccess;
       if (r.type == L_FORK) {          // the side streams start after everything queued so far

@@ -33,7 +33,8 @@ def hyper_of(opt, lr=None):
     c = opt.cfg
     return O.Hyper(lr=opt.lr if lr is None else lr, beta1=c.beta1, beta2=c.beta2, eps=c.eps,
                    weight_decay=c.weight_decay, lr_peak=c.lr_peak, nesterov_var_corr=bool(c.nesterov_var_corr),
-                   ns_steps=c.ns_steps, ns_floor=float(np.float32(c.ns_floor)), ns_damping=float(np.float32(c.ns_damping)))
+                   ns_steps=c.ns_steps, ns_floor=float(np.float32(c.ns_floor)), ns_damping=float(np.float32(c.ns_damping)),
+                   root_period=int(c.root_period))
 
 
 def snapshot(opt, gi, idx):

@@ -118,6 +118,49 @@ def test_shampoo_mode_small(precision):
     _run_teacher_forced(f"shampoo-{precision}", groups, grad, 3, precision, mode="shampoo")
 
 
+@pytest.mark.parametrize("mode", ["okls", "shampoo"])
+@pytest.mark.parametrize("precision", ["fp16", "fp32"])
+def test_root_refresh_period(mode, precision):
+    """Roots recomputed on steps 1, 4, 7 only (period 3) over ragged shapes:
+    on the other steps P stays bitwise what it was, while the factors,
+    momentum and the update (whitened with the kept roots) follow the
+    oracle's step with the same period.  W is zeroed before every step:
+    the first roots of these rank-deficient factors are large, and the
+    updates of the steps that keep them grow W far beyond a later step's
+    update, which could then not be read back from W's fp32 difference."""
+    torch = pytest.importorskip("torch")
+    groups = [(96, 160, 2), (130, 72, 1)]
+    scale = 0.02 if mode == "okls" else 1e-3
+
+    def grad(gi, i, t):
+        m, n, _ = groups[gi]
+        return (scale * np.random.default_rng([gi, i, t, 31]).standard_normal((m, n))).astype(np.float32)
+
+    opt, params = H.make(groups, precision=precision, mode=mode, root_period=3)
+    hp = H.hyper_of(opt)
+    assert hp.root_period == 3
+    tol = TOL[precision]
+    for t in range(1, 8):
+        host = {gi: [grad(gi, i, t) for i in range(b)] for gi, (m, n, b) in enumerate(groups)}
+        for p in params:
+            p.zero_()
+        before = {(gi, i): H.snapshot(opt, gi, i) for gi, (m, n, b) in enumerate(groups) for i in range(b)}
+        opt.step(grads=[H.to_device_grad(np.stack(host[gi]), "f32") for gi in range(len(groups))])
+        torch.cuda.synchronize()
+        for (gi, i), bf in before.items():
+            e = H.compare_step(opt, bf, None, host[gi][i], hp, t, mode, gi, i)
+            assert e["finite"]
+            assert e["M"] < tol["M"]
+            assert e["S_a"] < tol["S"] and e["S_b"] < tol["S"], (t, gi, i, e)
+            assert e["P_a"] < tol["P"] and e["P_b"] < tol["P"], (t, gi, i, e)
+            assert e["U"] < tol["U"], (t, gi, i, e)
+            after = H.snapshot(opt, gi, i)
+            if hp.refresh(t):
+                assert not np.array_equal(after.Pa, bf.Pa), (t, gi, i)
+            else:
+                assert np.array_equal(after.Pa, bf.Pa) and np.array_equal(after.Pb, bf.Pb), (t, gi, i)
+
+
 def test_bf16_gradients_rowscaled():
     """bf16 gradients with per-row log-uniform scales (the transformer-block
     workload's distribution) at a reduced shape spanning several tiles."""
