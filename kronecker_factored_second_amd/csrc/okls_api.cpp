@@ -411,6 +411,8 @@ struct Planner {
       j.kind = s.kind; j.src = s.src; j.src_ld = s.ld; j.src2 = s.src2; j.g_bf16 = s.g_bf16;
       j.rows = s.rows; j.cols = s.cols;
       j.rows_per_blk = std::max(1, std::min(s.rows, 32768 / std::max(1, s.cols)));
+      // at most kMaxJobParts partials per job: every cast block of the job combines them all
+      j.rows_per_blk = std::max(j.rows_per_blk, (s.rows + kMaxJobParts - 1) / kMaxJobParts);
       const double src_b = s.kind == ST_F32 ? 4.0 : s.kind == ST_BF16 ? 2.0 : 4.0 + (s.g_bf16 ? 2.0 : 4.0);
       step_bytes[CAT_STAT] += src_b * s.rows * s.cols;
       const int nb = (s.rows + j.rows_per_blk - 1) / j.rows_per_blk;
@@ -433,12 +435,14 @@ struct Planner {
     int rows, cols, dst_rows_p, dst_cols_p; Ref dst; int dst_ld; int dst_lo;
     std::pair<int, int> parts; int scale_mode; int scale_slot;
     int cinv_slot, rho_slot, sqrtc_slot, p16_slot; int write_lo; float damp; int sym_read;
+    Ref dst2; int scale_slot2; int write_lo2;
   };
   CastSpec cast_spec() {
     CastSpec c{};
     c.src2 = no_ref();
     c.dst = no_ref();
-    c.cinv_slot = c.rho_slot = c.sqrtc_slot = c.p16_slot = -1;
+    c.dst2 = no_ref();
+    c.cinv_slot = c.rho_slot = c.sqrtc_slot = c.p16_slot = c.scale_slot2 = -1;
     return c;
   }
   void add_cast(std::vector<LaunchRec>& L, const std::vector<CastSpec>& specs, float ka = 0.f, float kb = 0.f) {
@@ -457,13 +461,15 @@ struct Planner {
       j.scale_mode = s.scale_mode; j.scale_slot = s.scale_slot; j.cinv_slot = s.cinv_slot;
       j.rho_slot = s.rho_slot; j.sqrtc_slot = s.sqrtc_slot; j.p16_slot = s.p16_slot;
       j.p16_static = sZ; j.write_lo = s.write_lo; j.damp = s.damp; j.sym_read = s.sym_read;
-      j.tiles_x = s.dst_cols_p / kCastTile;
+      j.dst2 = s.dst2; j.scale_slot2 = s.scale_slot2; j.write_lo2 = s.write_lo2;
+      j.tiles_x = (s.dst_cols_p + kCastCols - 1) / kCastCols;
       const double src_b = s.kind == CA_BF16 ? 2.0
                          : s.kind == CA_NESTEROV ? 4.0 + (s.g_bf16 ? 2.0 : 4.0) + (s.write_m ? 4.0 : 0.0)
                          : 4.0;
-      step_bytes[CAT_CAST] += (src_b + (s.write_lo ? 4.0 : 2.0)) * s.rows * s.cols;
+      const double dst2_b = s.dst2.kind == REF_NONE ? 0.0 : s.write_lo2 ? 4.0 : 2.0;
+      step_bytes[CAT_CAST] += (src_b + (s.write_lo ? 4.0 : 2.0) + dst2_b) * s.rows * s.cols;
       j.blk_begin = blk;
-      blk += j.tiles_x * (s.dst_rows_p / kCastTile);
+      blk += j.tiles_x * (s.dst_rows_p / kCastRows);
       cast_jobs.push_back(j);
     }
     r.count = static_cast<int>(specs.size());
@@ -517,12 +523,8 @@ struct Planner {
       y.write_lo = ks > 0;
       y.damp = damping(F.d);
       y.sym_read = chain == 1;      // the second chain roots a computed square root
+      y.dst2 = ws_ref(F.Z[1]); y.scale_slot2 = SL_Z; y.write_lo2 = ks > 1;   // Z_1 in the same pass
       cs.push_back(y);
-      CastSpec z = y;
-      z.kind = CA_NS_Z1; z.dst = ws_ref(F.Z[1]); z.scale_slot = SL_Z;
-      z.cinv_slot = z.rho_slot = z.sqrtc_slot = z.p16_slot = -1;
-      z.write_lo = ks > 1;
-      cs.push_back(z);
     }
     add_cast(L, cs, static_cast<float>(na[0]), static_cast<float>(nb[0]));
     // step 0: Y_1 = a_0 Y_0 + b_0 Y_0 Y_0
@@ -968,8 +970,9 @@ struct Planner {
           for (int j = r.first; j < r.first + r.count; ++j) {
             const CastJob& c = cast_jobs[j];
             if (c.blk_begin != blk) return false;
-            if (c.dst_rows_p % kCastTile || c.dst_cols_p % kCastTile || c.tiles_x != c.dst_cols_p / kCastTile) return false;
-            blk += c.tiles_x * (c.dst_rows_p / kCastTile);
+            if (c.dst_rows_p % kCastRows || c.dst_cols_p % 4 ||
+                c.tiles_x != (c.dst_cols_p + kCastCols - 1) / kCastCols) return false;
+            blk += c.tiles_x * (c.dst_rows_p / kCastRows);
             const int drows = c.transpose ? c.cols : c.rows, dcols = c.transpose ? c.rows : c.cols;
             if (drows > c.dst_rows_p || dcols > c.dst_cols_p || c.src_ld < c.cols || c.rows < 1 || c.cols < 1) return false;
             const int need_ld = c.write_lo ? c.dst_lo + c.dst_cols_p : c.dst_cols_p;
@@ -981,8 +984,14 @@ struct Planner {
               if (c.transpose) return false;
               if (!fits(c.src2, (static_cast<size_t>(c.rows - 1) * c.src_ld + c.cols) * (c.g_bf16 ? 2 : 4))) return false;
             }
-            if ((c.kind == CA_NS_Y0 || c.kind == CA_NS_Z1) && c.rows != c.cols) return false;
-            if (c.part_begin < 0 || c.part_count < 1 || c.part_begin + c.part_count > max_partials) return false;
+            if (c.kind == CA_NS_Y0 && (c.rows != c.cols || c.transpose)) return false;
+            if (c.dst2.kind != REF_NONE) {
+              if (c.kind != CA_NS_Y0 || !slot_ok(c.scale_slot2)) return false;
+              if (c.write_lo2 && !c.write_lo) return false;     // the lo offset is checked through dst's
+              if (!fits(c.dst2, static_cast<size_t>(c.dst_rows_p) * c.dst_ld * 2)) return false;
+            }
+            if (c.part_begin < 0 || c.part_count < 1 || c.part_count > kMaxJobParts ||
+                c.part_begin + c.part_count > max_partials) return false;
             if (!slot_ok(c.scale_slot)) return false;
             for (int s : {c.cinv_slot, c.rho_slot, c.sqrtc_slot, c.p16_slot})
               if (s >= 0 && !slot_ok(s)) return false;

@@ -10,7 +10,9 @@ constexpr int kTile = 128;           // smallest GEMM output tile and padding un
 constexpr int kBigTile = 256;        // large GEMM output tile; sides above kBigPadFrom pad to it
 constexpr int kBigPadFrom = 512;
 constexpr int kBK = 64;              // GEMM K step
-constexpr int kCastTile = 64;        // elementwise cast tile
+constexpr int kCastRows = 64;        // destination rows of one cast block
+constexpr int kCastCols = 256;       // destination columns of one cast block
+constexpr int kMaxJobParts = 256;    // statistics partials per job, at most
 constexpr int kStatThreads = 256;
 constexpr int kScaleExp = 14;        // dynamic casts put max |x| in (2^13, 2^14]
 
@@ -123,8 +125,8 @@ enum CastKind : int32_t {
   CA_F32 = 0,        // x from fp32 source
   CA_BF16 = 1,       // x from bf16 source
   CA_NESTEROV = 2,   // x = N from (G, M); the non-transposed job also writes M'
-  CA_NS_Y0 = 3,      // x = S / c, c = sqrt(sumsq); static output scale
-  CA_NS_Z1 = 4       // x = ka*I + kb*S/c; static output scale
+  CA_NS_Y0 = 3       // x = (S + delta c I) / c', c = sqrt(sumsq); static output scale; the
+                     // second destination, if any, gets ka*I + kb*x (Z_1) in the same pass
 };
 enum ScaleMode : int32_t {
   SC_ABSMAX = 0,     // scale = 2^(kScaleExp - ceil(log2(absmax)))
@@ -151,9 +153,12 @@ struct CastJob {
   float p16_static;        // s_Z
   float damp;              // CA_NS_*: delta; the chain roots (S + delta c I) / (c (1 + delta))
   int32_t sym_read;        // CA_NS_*: 1 = read (S + S^T) / 2 (source not exactly symmetric)
-  int32_t tiles_x;         // tiles along destination columns
+  int32_t tiles_x;         // blocks along destination columns (kCastCols each)
   int32_t blk_begin;
   int32_t write_lo;
+  Ref dst2;                // CA_NS_Y0: second destination (same ld and lo offset), or REF_NONE
+  int32_t scale_slot2;     // its static scale
+  int32_t write_lo2;
 };
 
 struct CastArgs {
