@@ -625,10 +625,60 @@ __device__ __forceinline__ float nesterov_value(float m, float g, float beta1, f
   return s_t * (beta1 * mn + (1.0f - beta1) * g);
 }
 
+// Flat statistics loop over n4 quads from element e0: four quads per thread
+// and iteration, all their loads issued before any is used (one loop per
+// source form, so no branch sits between the loads).
+template <bool BF, bool NEST>
+__device__ __forceinline__ void stats_flat(const char* src, const float* m, size_t e0, size_t n4, float beta1,
+                                           float s_t, float& amax, float& ss) {
+  auto acc1 = [&](float x) {
+    const float ax = fabsf(x);
+    amax = (ax > amax || ax != ax) ? ax : amax;   // NaN propagates
+    ss += x * x;
+  };
+  auto ld = [&](size_t o) -> float4 {
+    if constexpr (BF) {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + o);
+      return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                    __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+    } else {
+      return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + o);
+    }
+  };
+  auto use = [&](const float4& g, const float4& mm) {
+    if constexpr (NEST) {
+      acc1(nesterov_value(mm.x, g.x, beta1, s_t));
+      acc1(nesterov_value(mm.y, g.y, beta1, s_t));
+      acc1(nesterov_value(mm.z, g.z, beta1, s_t));
+      acc1(nesterov_value(mm.w, g.w, beta1, s_t));
+    } else {
+      acc1(g.x); acc1(g.y); acc1(g.z); acc1(g.w);
+    }
+  };
+  size_t q = threadIdx.x;
+  for (; q + 3 * kStatThreads < n4; q += 4 * kStatThreads) {
+    float4 g[4], mm[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t o = e0 + 4 * (q + u * kStatThreads);
+      g[u] = ld(o);
+      if constexpr (NEST) mm[u] = *reinterpret_cast<const float4*>(m + o);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) use(g[u], mm[u]);
+  }
+  for (; q < n4; q += kStatThreads) {
+    const size_t o = e0 + 4 * q;
+    float4 mm{};
+    if constexpr (NEST) mm = *reinterpret_cast<const float4*>(m + o);
+    use(ld(o), mm);
+  }
+}
+
 __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
   __shared__ float sh[2 * (kStatThreads / 64)];
   const int gb = blockIdx.x + a.blk_offset;
-  const StatJob& J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
+  const StatJob J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
   const int lb = gb - J.blk_begin;
   const int r0 = lb * J.rows_per_blk;
   const int r1 = min(J.rows, r0 + J.rows_per_blk);
@@ -644,35 +694,21 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
   auto value = [&](size_t o, float raw) {
     return J.kind == ST_NESTEROV ? nesterov_value(m[o], raw, a.beta1, a.s_t) : raw;
   };
-  // rows are contiguous when src_ld == cols: one flat range, 4 elements per
-  // thread and iteration (16-byte fp32 / 8-byte bf16 loads when aligned)
+  // rows are contiguous when src_ld == cols: one flat range, 16-byte fp32 /
+  // 8-byte bf16 loads when aligned
   const size_t e0 = static_cast<size_t>(r0) * J.src_ld, e1 = static_cast<size_t>(r1) * J.src_ld;
   const bool flat = J.src_ld == J.cols && (e0 & 3) == 0 &&
                     (reinterpret_cast<uintptr_t>(src) & (bf ? 7 : 15)) == 0 &&
                     (m == nullptr || (reinterpret_cast<uintptr_t>(m) & 15) == 0);
   if (flat) {
     const size_t n4 = (e1 - e0) / 4;
-    auto quad = [&](size_t q) {
-      const size_t o = e0 + 4 * q;
-      float g[4];
-      if (bf) {
-        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + o);
-        g[0] = __uint_as_float(u.x << 16); g[1] = __uint_as_float(u.x & 0xffff0000u);
-        g[2] = __uint_as_float(u.y << 16); g[3] = __uint_as_float(u.y & 0xffff0000u);
-      } else {
-        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + o);
-        g[0] = f.x; g[1] = f.y; g[2] = f.z; g[3] = f.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc1(value(o + e, g[e]));
-    };
-    // four quads per thread and iteration: their loads are issued together
-    size_t q = threadIdx.x;
-    for (; q + 3 * kStatThreads < n4; q += 4 * kStatThreads) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) quad(q + u * kStatThreads);
+    if (m != nullptr) {
+      if (bf) stats_flat<true, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      else stats_flat<false, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+    } else {
+      if (bf) stats_flat<true, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      else stats_flat<false, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
     }
-    for (; q < n4; q += kStatThreads) quad(q);
     for (size_t o = e0 + 4 * n4 + threadIdx.x; o < e1; o += kStatThreads) {
       const float raw = bf ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]) : reinterpret_cast<const float*>(src)[o];
       acc1(value(o, raw));
@@ -737,7 +773,7 @@ __device__ __noinline__ float cast_element(int kind, int ld, bool g_bf16, bool w
 __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
   constexpr int kPass = kCastRows * kCastCols / (4 * kCastThreads);   // quads per thread
   static_assert(kPass == 16 && kCastCols == 4 * 64 && kCastThreads == 256, "cast block layout");
-  static_assert(kMaxJobParts <= kCastThreads, "one partial per thread");
+  static_assert(kMaxJobParts % kCastThreads == 0, "partials per thread");
   __shared__ float sh[2 * (kCastThreads / 64)];
   __shared__ float tile[kCastCols * kCastRows];     // transposed jobs: [source row][source column]
   const int gb = blockIdx.x + a.blk_offset;
@@ -768,10 +804,17 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
     return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
   };
-  // the job's statistics partials (at most one per thread), loaded ahead of the data
-  const bool has_part = static_cast<int>(threadIdx.x) < J.part_count;
-  const float part_a = has_part ? a.partials[2 * (J.part_begin + threadIdx.x)] : 0.0f;
-  const float part_s = has_part ? a.partials[2 * (J.part_begin + threadIdx.x) + 1] : 0.0f;
+  // the job's statistics partials (at most kMaxJobParts / kCastThreads per
+  // thread, strided), loaded ahead of the data
+  constexpr int kPartsPerThread = kMaxJobParts / kCastThreads;
+  float part_a[kPartsPerThread], part_s[kPartsPerThread];
+#pragma unroll
+  for (int k = 0; k < kPartsPerThread; ++k) {
+    const int i = static_cast<int>(threadIdx.x) + k * kCastThreads;
+    const bool has = i < J.part_count;
+    part_a[k] = has ? a.partials[2 * (J.part_begin + i)] : 0.0f;
+    part_s[k] = has ? a.partials[2 * (J.part_begin + i) + 1] : 0.0f;
+  }
 
   float x[kPass][4];
   // a block whose source region lies wholly inside the matrix loads without
@@ -836,7 +879,12 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
   // ---- 2. the scale from the statistics partials (same fixed order in every
   // block): wave butterflies, then every thread combines the waves' results
   // in wave order
-  float amax = part_a, ss = part_s;
+  float amax = part_a[0], ss = part_s[0];
+#pragma unroll
+  for (int k = 1; k < kPartsPerThread; ++k) {
+    amax = (part_a[k] > amax || part_a[k] != part_a[k]) ? part_a[k] : amax;
+    ss += part_s[k];
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float om = __shfl_xor(amax, o, 64);

@@ -12,7 +12,7 @@ constexpr int kBigPadFrom = 512;
 constexpr int kBK = 64;              // GEMM K step
 constexpr int kCastRows = 64;        // destination rows of one cast block
 constexpr int kCastCols = 256;       // destination columns of one cast block
-constexpr int kMaxJobParts = 256;    // statistics partials per job, at most
+constexpr int kMaxJobParts = 1024;   // statistics partials per job, at most
 constexpr int kStatThreads = 256;
 constexpr int kScaleExp = 14;        // dynamic casts put max |x| in (2^13, 2^14]
 
