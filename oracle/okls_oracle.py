@@ -14,10 +14,14 @@ title and section.  Short names used in the citations:
              sections "2 × 3 그래디언트 하나로 손계산" (worked example) and
              "문제 14" (problem 14, exponent and scale).
   [CLEAN]    "Clean: Second-order LLM Training at Linear Memory Cost via
-             Nyström Sketching", section 2, equations (2)-(3).
+             Nyström Sketching", section 2, equations (2)-(3); Table 6
+             (optimizer-specific hyperparameters).
+  [MUON]     [SHAMPOO] section "ML에서: 대회 우승과 그다음" (with accumulation
+             off, the Shampoo step is the gradient with every singular value
+             set to 1; Muon reaches it with matrix products only).
 
 Where the pages leave a step open, the reading taken is named in the
-docstring as R1..R15; the list of readings lives with the project's design
+docstring as R1..R16; the list of readings lives with the project's design
 notes.  All arithmetic is numpy float64; eigendecompositions use LAPACK
 (numpy.linalg.eigh).  Nothing here is blocked, fused or reordered beyond the
 definitions.
@@ -44,6 +48,11 @@ Parity status of each function (what pins it in the CPU test-suite):
                                  3-D batch = per-matrix results
   Hyper.refresh (R15) .......... worked example with a refresh period: the singular
                                  values follow the last refresh's accumulation count
+  ns_polar / muon_step (R16) ... converges to the SVD polar factor; equals the exact
+                                 un-accumulated Shampoo step on the worked example
+                                 (singular values 1, 1); 5-step output = the scalar map
+                                 on SVD singular values; scale invariance (problem 14),
+                                 transpose identity, t = 1 update
 """
 from __future__ import annotations
 
@@ -406,11 +415,60 @@ def shampoo_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ex
     return StepResult(MatState(W, M, Sa, Sb, Pa, Pb), N, U, Pa_ns, Pb_ns, ka, kb)
 
 
+# ---------------------------------------------------------------------------
+# Muon ([MUON]; [CLEAN] Table 6: Nesterov momentum, 5 Newton-Schulz iterations).
+# R16: the iteration X <- a_k X + b_k (X X^T) X maps every singular value by
+# sigma (a_k + b_k sigma^2), the scalar map of the coupled inverse-root
+# iteration, so it takes the same minimax table (R4) on [l_0, 1]; the Muon
+# configuration is 5 steps with l_0 = 1e-2 (final half-width 0.156).  The
+# start X_0 = N / ||N N^T||_F^{1/2} puts every singular value in (0, 1]
+# (||N N^T||_F = (sum sigma^4)^{1/2} >= sigma_max^2); it is the scaling the
+# OKLS chain applies to S = G G^T-like factors.  Momentum, c_shape and the
+# decoupled decay are those of the OKLS step.
+# ---------------------------------------------------------------------------
+def muon_hyper(**kw) -> Hyper:
+    """The Muon configuration of R16 (5 steps, l_0 = 1e-2) on top of Hyper's defaults."""
+    kw.setdefault("ns_steps", 5)
+    kw.setdefault("ns_floor", 1e-2)
+    return Hyper(**kw)
+
+
+def ns_polar(N: np.ndarray, coeffs) -> np.ndarray:
+    """The R16 iteration on N; the Gram of the smaller side is formed
+    ((X X^T) X and X (X^T X) are the same matrix)."""
+    N = np.asarray(N, dtype=np.float64)
+    wide = N.shape[0] <= N.shape[1]
+    gram = N @ N.T if wide else N.T @ N
+    X = N / math.sqrt(float(np.linalg.norm(gram)))
+    for a, b in coeffs:
+        X = a * X + b * ((X @ X.T) @ X if wide else X @ (X.T @ X))
+    return X
+
+
+def muon_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ns") -> StepResult:
+    """One Muon step (R16): Nesterov momentum (R5), N orthogonalised by the
+    polar iteration, c_shape-scaled update with the decoupled decay (R6).
+    The factors and roots of the state are neither used nor changed.
+    root='exact' replaces the iteration by the SVD polar factor U V^T."""
+    G = np.asarray(G, dtype=np.float64)
+    M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
+    if root == "exact":
+        u, _, vt = np.linalg.svd(N, full_matrices=False)
+        U = u @ vt
+    else:
+        coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+        U = ns_polar(N, coeffs)
+    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
+    return StepResult(MatState(W, M, st.Sa, st.Sb, st.Pa, st.Pb), N, U, st.Pa, st.Pb, float("nan"), float("nan"))
+
+
 def step(st: MatState, G, hp: Hyper, t: int, mode: str = "okls", root: str = "exact") -> StepResult:
     if mode == "okls":
         return okls_step(st, G, hp, t, root)
     if mode == "shampoo":
         return shampoo_step(st, G, hp, t, root)
+    if mode == "muon":
+        return muon_step(st, G, hp, t, root)
     raise ValueError(mode)
 
 

@@ -513,3 +513,95 @@ def test_batched_equals_per_matrix():
     for i in range(3):
         ri = O.okls_step(O.init_state(Ws[i], hp.eps), Gs[i], hp, 1)
         np.testing.assert_array_equal(rb[i].state.W, ri.state.W)
+
+
+# --------------------------------------------------------------------------
+# Muon (R16): the un-accumulated Shampoo step through matrix products only.
+# --------------------------------------------------------------------------
+def test_muon_is_the_unaccumulated_shampoo_step_on_the_worked_example():
+    """The Shampoo chapter: with one gradient and no accumulation the step
+    L^{-1/4} G R^{-1/4} has singular values 1, 1, and Muon reaches that matrix
+    with products alone.  A converged iteration (12 steps) equals the exact
+    -1/4 step built from eigh roots; the Muon configuration (5 steps) keeps
+    both singular values within its final half-width of 1."""
+    g = _gold("shampoo_worked_example.json")
+    G = np.array(g["G"], dtype=np.float64)
+    L, R = G @ G.T, G.T @ G
+    Lq = O.inv_root_exact(L, 4)[0]
+    # R is rank 2 (3 x 3): the -1/4 step acts on its range only
+    lam, V = np.linalg.eigh(R)
+    keep = lam > 1e-9 * lam.max()
+    Rq = (V[:, keep] * lam[keep] ** -0.25) @ V[:, keep].T
+    step_exact = Lq @ G @ Rq
+    np.testing.assert_allclose(np.linalg.svd(step_exact, compute_uv=False), g["singular_values_preconditioned_one_accumulation"],
+                               atol=g["printed_precision"])
+    coeffs12, err12 = O.ns_coefficients(1e-2, 12)
+    assert err12 < 1e-12
+    np.testing.assert_allclose(O.ns_polar(G, coeffs12), step_exact, atol=1e-12)
+    coeffs5, err5 = O.ns_coefficients(1e-2, 5)
+    sv = np.linalg.svd(O.ns_polar(G, coeffs5), compute_uv=False)
+    assert np.all(np.abs(sv - 1.0) <= err5 + 1e-12) and np.all(np.abs(sv - 1.0) < 0.05), sv
+
+
+@pytest.mark.parametrize("shape", [(7, 5), (5, 7), (6, 6)])
+def test_polar_iteration_converges_to_svd_polar_factor(shape):
+    """Many steps reach U V^T from LAPACK's SVD (a different routine from the
+    products the iteration uses), for both Gram orientations."""
+    rng = np.random.default_rng(61)
+    m, n = shape
+    k = min(m, n)
+    u, _ = np.linalg.qr(rng.standard_normal((m, k)))
+    v, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    N = (u * np.logspace(0, -1.5, k)) @ v.T
+    coeffs, err = O.ns_coefficients(1e-3, 14)
+    assert err < 1e-10
+    np.testing.assert_allclose(O.ns_polar(N, coeffs), u @ v.T, atol=1e-9)
+
+
+def test_polar_five_steps_is_the_scalar_map_on_singular_values():
+    """After 5 steps every singular value sigma has become p(sigma / c) with
+    c = (sum sigma^4)^{1/4} and p the composed cubic steps; singular vectors
+    are untouched (SVD route, not the products)."""
+    rng = np.random.default_rng(62)
+    m, n = 9, 13
+    u, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    v, _ = np.linalg.qr(rng.standard_normal((n, m)))
+    sig = np.exp(rng.uniform(-3, 0, m))
+    N = (u * sig) @ v.T
+    coeffs, _ = O.ns_coefficients(1e-2, 5)
+    s = sig / np.sum(sig ** 4) ** 0.25
+    for a, b in coeffs:
+        s = s * (a + b * s * s)
+    np.testing.assert_allclose(O.ns_polar(N, coeffs), (u * s) @ v.T, atol=1e-13)
+
+
+def test_muon_step_is_scale_free_and_transposes():
+    """Problem 14's point for the -1/4 step holds for Muon: G and 10 G give the
+    same update; the transposed gradient gives the transposed update."""
+    rng = np.random.default_rng(63)
+    G = rng.standard_normal((6, 10))
+    hp = O.muon_hyper()
+    st = O.init_state(np.zeros((6, 10)), hp.eps)
+    stT = O.init_state(np.zeros((10, 6)), hp.eps)
+    r1 = O.muon_step(st, G, hp, 1)
+    r10 = O.muon_step(st, 10.0 * G, hp, 1)
+    rT = O.muon_step(stT, G.T, hp, 1)
+    np.testing.assert_allclose(r10.U, r1.U, atol=1e-13)
+    np.testing.assert_allclose(rT.U, r1.U.T, atol=1e-13)
+    # t = 1: N = G (R5), W' = decay W - lr c_shape U from W = 0
+    np.testing.assert_allclose(r1.N, G, atol=1e-15)
+    np.testing.assert_allclose(r1.state.W, -hp.lr * O.c_shape(6, 10) * r1.U, atol=1e-15)
+    # the factors and roots of the state are left as they were
+    assert r1.state.Sa is st.Sa and r1.state.Pb is st.Pb
+
+
+def test_muon_step_orthogonal_equivariance():
+    rng = np.random.default_rng(64)
+    G = rng.standard_normal((5, 8))
+    Qa, Qb = _orth(rng, 5), _orth(rng, 8)
+    hp = O.muon_hyper()
+    st = O.init_state(rng.standard_normal((5, 8)), hp.eps)
+    stQ = O.init_state(Qa @ st.W @ Qb.T, hp.eps)
+    r = O.muon_step(st, G, hp, 1)
+    rQ = O.muon_step(stQ, Qa @ G @ Qb.T, hp, 1)
+    np.testing.assert_allclose(rQ.U, Qa @ r.U @ Qb.T, atol=1e-12)
