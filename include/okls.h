@@ -70,7 +70,15 @@ typedef enum { OKLS_F32 = 0, OKLS_BF16 = 1 } okls_dtype;
 
 typedef enum {
     OKLS_MODE_OKLS = 0,      /* KL factor EMAs, P = S^{-1/2} */
-    OKLS_MODE_SHAMPOO = 1    /* plain sums, P = S^{-1/4} via two chained roots */
+    OKLS_MODE_SHAMPOO = 1,   /* plain sums, P = S^{-1/4} via two chained roots */
+    OKLS_MODE_MUON = 2       /* no factors: the momentum N is orthogonalised by the polar
+                                Newton-Schulz iteration X <- a_k X + b_k (X X^T) X from
+                                X_0 = N / ||N N^T||_F^{1/2} (the Shampoo chapter's
+                                "ML에서: 대회 우승과 그다음": the un-accumulated Shampoo
+                                step, every singular value set to 1, by products alone;
+                                the Clean paper's Table 6: 5 iterations).  ns_steps and
+                                ns_floor are the iteration's (Muon setting: 5 and 1e-2);
+                                beta2, eps, ns_damping and root_period are not used */
 } okls_mode;
 
 typedef struct {
@@ -116,6 +124,7 @@ typedef struct {
     float* Sb;         /* (N, n, n) right factor */
     float* Pa;         /* (N, m, m) left preconditioner S_a^{-1/2} (Shampoo S_a^{-1/4}) */
     float* Pb;         /* (N, n, n) right preconditioner */
+                       /* OKLS_MODE_MUON reads none of Sa, Sb, Pa, Pb: they may be NULL */
 } okls_group_tensors;
 
 typedef struct okls_handle okls_handle;
@@ -137,8 +146,9 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups,
                       void* stream);
 
 /* Fills the state for a fresh start (README "Hyperparameters": eps at factor
- * initialisation): S = eps I, P = I, M = 0.  W and G are not touched (may be
- * NULL).  `tensors` points to n_groups entries.  Asynchronous on `stream`. */
+ * initialisation): S = eps I, P = I, M = 0 (Muon mode: M = 0 only).  W and G
+ * are not touched (may be NULL).  `tensors` points to n_groups entries.
+ * Synchronises `stream` once. */
 okls_status okls_init_state(okls_handle* h, const okls_group_tensors* tensors, void* stream);
 
 /* One optimizer step (1-based step counter t, current learning rate lr) for

@@ -97,6 +97,10 @@ struct MatBufs {
   size_t G16 = 0, G16T = 0, N16 = 0, Xa32 = 0, XbT32 = 0, Xa16 = 0, XbT16 = 0, VT32 = 0, VT16 = 0;
   int s_g = 0, s_n = 0, s_xa = 0, s_xb = 0, s_vt = 0;
   FacBufs fa, fb;
+  // Muon: N^T, the iterates X_k and X_k^T, the Gram of the smaller side (p x p)
+  int pd = 0, pdp = 0, ldp = 0;
+  size_t NT16 = 0, X[2] = {0, 0}, XT[2] = {0, 0}, A32 = 0, A16 = 0;
+  int s_gcinv = 0, s_grho = 0;
 };
 
 enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4 };
@@ -180,7 +184,7 @@ namespace {
 // ---------------------------------------------------------------------------
 okls_status check_config(const okls_config* c) {
   if (c == nullptr) return OKLS_ERR_INVALID_ARG;
-  if (c->mode != OKLS_MODE_OKLS && c->mode != OKLS_MODE_SHAMPOO) return OKLS_ERR_INVALID_ARG;
+  if (c->mode != OKLS_MODE_OKLS && c->mode != OKLS_MODE_SHAMPOO && c->mode != OKLS_MODE_MUON) return OKLS_ERR_INVALID_ARG;
   if (c->ns_steps < 2 || c->ns_steps > 16) return OKLS_ERR_INVALID_ARG;
   if (c->ns_split_steps < 0 || c->ns_split_steps > c->ns_steps) return OKLS_ERR_INVALID_ARG;
   if (c->factor_split != 0 && c->factor_split != 1) return OKLS_ERR_INVALID_ARG;
@@ -214,6 +218,7 @@ struct Planner {
   const okls_config& cfg;
   const std::vector<okls_group_desc>& groups;
   bool okls_mode;
+  bool muon_mode;
   bool lo_layout;
   std::vector<double> na, nb;
   float sY = 0, sZ = 0, sT = 0;
@@ -233,7 +238,7 @@ struct Planner {
   int max_partials = 1;
 
   Planner(const okls_config& c, const std::vector<okls_group_desc>& g)
-      : cfg(c), groups(g), okls_mode(c.mode == OKLS_MODE_OKLS),
+      : cfg(c), groups(g), okls_mode(c.mode == OKLS_MODE_OKLS), muon_mode(c.mode == OKLS_MODE_MUON),
         lo_layout(c.factor_split != 0 || c.ns_split_steps > 0) {
     ns_table(cfg.ns_floor, cfg.ns_steps, na, nb, nullptr);
     double prod = 1.0, amax = 0.0;
@@ -274,6 +279,16 @@ struct Planner {
       const okls_group_desc& g = groups[mb.group];
       mb.m = g.m; mb.n = g.n; mb.mp = pad_tile(g.m); mb.np = pad_tile(g.n);
       mb.ldm = ld_for(mb.mp); mb.ldn = ld_for(mb.np);
+      if (muon_mode) {
+        const size_t bx = static_cast<size_t>(mb.mp) * mb.ldn * 2, bxt = static_cast<size_t>(mb.np) * mb.ldm * 2;
+        mb.pd = std::min(g.m, g.n); mb.pdp = pad_tile(mb.pd); mb.ldp = ld_for(mb.pdp);
+        mb.N16 = take(bx); mb.NT16 = take(bxt);
+        mb.X[0] = take(bx); mb.X[1] = take(bx); mb.XT[0] = take(bxt); mb.XT[1] = take(bxt);
+        mb.A32 = take(static_cast<size_t>(mb.pd) * mb.pd * 4);
+        mb.A16 = take(static_cast<size_t>(mb.pdp) * mb.ldp * 2);
+        mb.s_n = slot++; mb.s_gcinv = slot++; mb.s_grho = slot++;
+        continue;
+      }
       mb.G16 = take(static_cast<size_t>(mb.mp) * mb.ldn * 2);
       mb.G16T = take(static_cast<size_t>(mb.np) * mb.ldm * 2);
       mb.N16 = take(static_cast<size_t>(mb.mp) * mb.ldn * 2);
@@ -358,7 +373,10 @@ struct Planner {
     r.type = L_GEMM;
     r.cat = gemm_cat;
     r.prob_base = static_cast<int>(probs.size());
-    probs.insert(probs.end(), ps.begin(), ps.end());
+    for (GemmProb p : ps) {
+      if (p.ld16T < 0) { p.ld16T = p.ld16; p.lo16T = p.lo16; }   // square problems: same layout
+      probs.push_back(p);
+    }
     // algorithmic bytes: both fp16 operands once (hi and lo halves when split),
     // every output and the fp32 matrix the epilogue reads, once
     for (const GemmProb& p : ps) {
@@ -367,7 +385,8 @@ struct Planner {
       if (p.out32.kind != REF_NONE) b += 4.0 * mn;
       if (p.out16.kind != REF_NONE) b += (write_lo ? 4.0 : 2.0) * mn;
       if (p.out16T.kind != REF_NONE) b += (write_lo ? 4.0 : 2.0) * mn;
-      if (p.aux.kind != REF_NONE) b += 4.0 * mn;
+      const bool aux16 = p.epi == EPI_POLAR || p.epi == EPI_POLAR_UPDATE;
+      if (p.aux.kind != REF_NONE) b += (aux16 ? (p.aux_lo >= 0 ? 4.0 : 2.0) : 4.0) * mn;
       step_bytes[gemm_cat] += b;
     }
     // one epilogue kind per launch (the kernel is specialised on it)
@@ -385,7 +404,8 @@ struct Planner {
       const long tm = p.Mp / kBigTile, tn = p.Np / kBigTile;
       big_tiles += upper ? tm * (tm + 1) / 2 : tm * tn;
     }
-    const bool f16_out = r.epi == EPI_NS_T || r.epi == EPI_NS_Y1 || r.epi == EPI_STORE16 || r.epi == EPI_NS_FINAL;
+    const bool f16_out = r.epi == EPI_NS_T || r.epi == EPI_NS_Y1 || r.epi == EPI_STORE16 || r.epi == EPI_NS_FINAL ||
+                         r.epi == EPI_POLAR;
     if (big_tiles < (f16_out ? 64 : 512)) r.tile = kTile;
     const std::pair<int, int> t = tiles_for(ps, upper, r.tile);
     r.first = t.first;
@@ -436,12 +456,14 @@ struct Planner {
     std::pair<int, int> parts; int scale_mode; int scale_slot;
     int cinv_slot, rho_slot, sqrtc_slot, p16_slot; int write_lo; float damp; int sym_read;
     Ref dst2; int scale_slot2; int write_lo2;
+    Ref dstT; int dstT_ld; int dstT_lo;
   };
   CastSpec cast_spec() {
     CastSpec c{};
     c.src2 = no_ref();
     c.dst = no_ref();
     c.dst2 = no_ref();
+    c.dstT = no_ref();
     c.cinv_slot = c.rho_slot = c.sqrtc_slot = c.p16_slot = c.scale_slot2 = -1;
     return c;
   }
@@ -462,12 +484,14 @@ struct Planner {
       j.rho_slot = s.rho_slot; j.sqrtc_slot = s.sqrtc_slot; j.p16_slot = s.p16_slot;
       j.p16_static = sZ; j.write_lo = s.write_lo; j.damp = s.damp; j.sym_read = s.sym_read;
       j.dst2 = s.dst2; j.scale_slot2 = s.scale_slot2; j.write_lo2 = s.write_lo2;
+      j.dstT = s.dstT; j.dstT_ld = s.dstT_ld; j.dstT_lo = s.dstT_lo;
       j.tiles_x = (s.dst_cols_p + kCastCols - 1) / kCastCols;
       const double src_b = s.kind == CA_BF16 ? 2.0
                          : s.kind == CA_NESTEROV ? 4.0 + (s.g_bf16 ? 2.0 : 4.0) + (s.write_m ? 4.0 : 0.0)
                          : 4.0;
       const double dst2_b = s.dst2.kind == REF_NONE ? 0.0 : s.write_lo2 ? 4.0 : 2.0;
-      step_bytes[CAT_CAST] += (src_b + (s.write_lo ? 4.0 : 2.0) + dst2_b) * s.rows * s.cols;
+      const double dstT_b = s.dstT.kind == REF_NONE ? 0.0 : s.write_lo ? 4.0 : 2.0;
+      step_bytes[CAT_CAST] += (src_b + (s.write_lo ? 4.0 : 2.0) + dst2_b + dstT_b) * s.rows * s.cols;
       j.blk_begin = blk;
       blk += j.tiles_x * (s.dst_rows_p / kCastRows);
       cast_jobs.push_back(j);
@@ -484,6 +508,9 @@ struct Planner {
     p.A = p.B = p.out32 = p.out16 = p.out16T = p.aux = no_ref();
     p.s_out = -1;
     p.cslot = -1;
+    p.ld16T = -1;
+    p.aux_lo = -1;
+    p.s_aux = -1;
     return p;
   }
 
@@ -600,6 +627,125 @@ struct Planner {
     }
   }
 
+  // Muon: N's fp16 copies (both orientations, M' written), then the polar
+  // iteration X <- a_k X + b_k (X X^T) X from X_0 = N / ||N N^T||_F^{1/2},
+  // with the Gram of the smaller side; the last step's product goes straight
+  // into the weight update.  Step k's GEMMs are split-fp16 when k <
+  // ns_split_steps.
+  void plan_muon(std::vector<LaunchRec>& L, std::vector<MatBufs>& mats) {
+    const int K = cfg.ns_steps, ks = cfg.ns_split_steps;
+    auto sp = [&](int k) { return k < ks ? 1 : 0; };
+    auto gdt = [&](const MatBufs& mb) { return groups[mb.group].g_dtype; };
+    auto goff = [&](const MatBufs& mb) {
+      return static_cast<size_t>(mb.index) * mb.m * mb.n * (gdt(mb) == OKLS_BF16 ? 2 : 4);
+    };
+    auto moff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.n * 4; };
+    auto wide = [](const MatBufs& mb) { return mb.m <= mb.n; };
+    // 1. statistics of N
+    std::vector<StatSpec> st;
+    for (const MatBufs& mb : mats)
+      st.push_back(StatSpec{ST_NESTEROV, user_ref(REF_G, mb.group, goff(mb)), mb.n,
+                            user_ref(REF_M, mb.group, moff(mb)), gdt(mb) == OKLS_BF16, mb.m, mb.n});
+    std::vector<std::pair<int, int>> parts = add_stats(L, st);
+    // 2. N and N^T in fp16 (absmax scale), M' written
+    std::vector<CastSpec> cs;
+    for (size_t q = 0; q < mats.size(); ++q) {
+      const MatBufs& mb = mats[q];
+      CastSpec nn = cast_spec();
+      nn.kind = CA_NESTEROV; nn.src = user_ref(REF_M, mb.group, moff(mb)); nn.src_ld = mb.n;
+      nn.src2 = user_ref(REF_G, mb.group, goff(mb)); nn.g_bf16 = gdt(mb) == OKLS_BF16; nn.write_m = 1;
+      nn.rows = mb.m; nn.cols = mb.n; nn.dst_rows_p = mb.mp; nn.dst_cols_p = mb.np; nn.dst = ws_ref(mb.N16);
+      nn.dst_ld = mb.ldn; nn.dst_lo = mb.np; nn.parts = parts[q]; nn.scale_mode = SC_ABSMAX;
+      nn.scale_slot = mb.s_n; nn.write_lo = sp(0);
+      nn.dstT = ws_ref(mb.NT16); nn.dstT_ld = mb.ldm; nn.dstT_lo = mb.mp;
+      cs.push_back(nn);
+    }
+    add_cast(L, cs);
+    gemm_cat = CAT_NS;
+    for (const MatBufs& mb : mats) {
+      const double p = mb.pd, q = std::max(mb.m, mb.n);
+      step_flops[CAT_NS] += 4.0 * K * p * p * q;     // a Gram and an update product per step
+    }
+    // 3. Gram of the smaller side in fp32: A_0 = N N^T (wide) or N^T N (tall)
+    {
+      std::vector<GemmProb> pg;
+      for (const MatBufs& mb : mats) {
+        GemmProb g = prob();
+        const bool w = wide(mb);
+        g.A = g.B = ws_ref(w ? mb.N16 : mb.NT16); g.lda = g.ldb = w ? mb.ldn : mb.ldm;
+        g.M = g.N = mb.pd; g.Kp = w ? mb.np : mb.mp; g.Mp = g.Np = mb.pdp; g.epi = EPI_STORE32;
+        g.out32 = ws_ref(mb.A32); g.ld32 = mb.pd; g.sA = g.sB = mb.s_n;
+        pg.push_back(g);
+      }
+      add_gemm(L, pg, false, sp(0), 0);
+    }
+    // 4-5. ||A_0||_F, then A_0 / ||A_0||_F in fp16; the cast records
+    // 1 / ||A_0||_F^{1/2}, the scaling of X_0 = N / ||A_0||_F^{1/2}
+    {
+      std::vector<StatSpec> sa;
+      for (const MatBufs& mb : mats) sa.push_back(StatSpec{ST_F32, ws_ref(mb.A32), mb.pd, no_ref(), 0, mb.pd, mb.pd});
+      std::vector<std::pair<int, int>> pa = add_stats(L, sa);
+      std::vector<CastSpec> ca;
+      for (size_t q = 0; q < mats.size(); ++q) {
+        const MatBufs& mb = mats[q];
+        CastSpec y = cast_spec();
+        y.kind = CA_NS_Y0; y.src = ws_ref(mb.A32); y.src_ld = mb.pd; y.rows = y.cols = mb.pd;
+        y.dst_rows_p = y.dst_cols_p = mb.pdp; y.dst = ws_ref(mb.A16); y.dst_ld = mb.ldp; y.dst_lo = mb.pdp;
+        y.parts = pa[q]; y.scale_mode = SC_STATIC; y.scale_slot = SL_Y;
+        y.cinv_slot = mb.s_gcinv; y.rho_slot = mb.s_grho; y.write_lo = sp(0); y.damp = 0.0f;
+        ca.push_back(y);
+      }
+      add_cast(L, ca);
+    }
+    // 6. the steps
+    for (int k = 0; k < K; ++k) {
+      const int cur = k & 1, nxt = (k + 1) & 1;
+      if (k > 0) {   // Gram A_k of the current iterate (fp16, |A_k| <= 1)
+        std::vector<GemmProb> pg;
+        for (const MatBufs& mb : mats) {
+          GemmProb g = prob();
+          const bool w = wide(mb);
+          g.A = g.B = ws_ref(w ? mb.X[cur] : mb.XT[cur]); g.lda = g.ldb = w ? mb.ldn : mb.ldm;
+          g.M = g.N = mb.pd; g.Kp = w ? mb.np : mb.mp; g.Mp = g.Np = mb.pdp; g.epi = EPI_STORE16;
+          g.out16 = ws_ref(mb.A16); g.ld16 = mb.ldp; g.lo16 = mb.pdp; g.s_out = SL_Y; g.sA = g.sB = SL_Y;
+          pg.push_back(g);
+        }
+        add_gemm(L, pg, false, sp(k), sp(k));
+      }
+      // update: X_{k+1} = c (a_k X_k + b_k A_k X_k), c = ||A_0||_F^{-1/2} at k = 0 (X_0 = N c), else 1
+      std::vector<GemmProb> pu;
+      const bool last = k == K - 1;
+      for (const MatBufs& mb : mats) {
+        GemmProb u = prob();
+        const bool w = wide(mb);
+        const size_t xk = k == 0 ? mb.N16 : mb.X[cur], xtk = k == 0 ? mb.NT16 : mb.XT[cur];
+        const int sx = k == 0 ? mb.s_n : SL_Y;
+        if (w) {   // A_k X_k = NT(A_k, X_k^T), K = m
+          u.A = ws_ref(mb.A16); u.lda = mb.ldp; u.B = ws_ref(xtk); u.ldb = mb.ldm; u.Kp = mb.mp;
+          u.sA = SL_Y; u.sB = sx;
+        } else {   // X_k A_k = NT(X_k, A_k), K = n
+          u.A = ws_ref(xk); u.lda = mb.ldn; u.B = ws_ref(mb.A16); u.ldb = mb.ldp; u.Kp = mb.np;
+          u.sA = sx; u.sB = SL_Y;
+        }
+        u.M = mb.m; u.N = mb.n; u.Mp = mb.mp; u.Np = mb.np;
+        u.aux = ws_ref(xk); u.ldaux = mb.ldn; u.aux_lo = sp(k) ? mb.np : -1; u.s_aux = sx;
+        u.cslot = k == 0 ? mb.s_grho : SL_ONE;
+        if (!last) {
+          u.epi = EPI_POLAR;
+          u.out16 = ws_ref(mb.X[nxt]); u.ld16 = mb.ldn; u.lo16 = mb.np; u.s_out = SL_Y;
+          u.out16T = ws_ref(mb.XT[nxt]); u.ld16T = mb.ldm; u.lo16T = mb.mp;
+        } else {
+          u.epi = EPI_POLAR_UPDATE;
+          u.out32 = user_ref(REF_W, mb.group, moff(mb)); u.ld32 = mb.n;
+          u.c0 = static_cast<float>(std::sqrt(static_cast<double>(mb.m) / mb.n) /
+                                    (std::sqrt(static_cast<double>(mb.m)) + std::sqrt(static_cast<double>(mb.n))));
+        }
+        pu.push_back(u);
+      }
+      add_gemm(L, pu, false, sp(k), last ? 0 : sp(k + 1), static_cast<float>(na[k]), static_cast<float>(nb[k]));
+    }
+  }
+
   // P16 produced by the chain of this factor, in Z[K % 2]
   size_t p16_of(const FacBufs& F) const { return F.Z[cfg.ns_steps & 1]; }
 
@@ -609,7 +755,8 @@ struct Planner {
   void plan_chunk(std::vector<MatBufs>& mats, size_t base, bool refresh, bool rebase) {
     if (rebase) {
       for (MatBufs& mb : mats) {
-        size_t* offs[] = {&mb.G16, &mb.G16T, &mb.N16, &mb.Xa32, &mb.XbT32, &mb.Xa16, &mb.XbT16, &mb.VT32, &mb.VT16};
+        size_t* offs[] = {&mb.G16, &mb.G16T, &mb.N16, &mb.Xa32, &mb.XbT32, &mb.Xa16, &mb.XbT16, &mb.VT32, &mb.VT16,
+                          &mb.NT16, &mb.X[0], &mb.X[1], &mb.XT[0], &mb.XT[1], &mb.A32, &mb.A16};
         for (size_t* o : offs) *o += base;
         for (FacBufs* f : {&mb.fa, &mb.fb}) {
           f->Y[0] += base; f->Y[1] += base; f->Z[0] += base; f->Z[1] += base; f->T += base; f->R32 += base;
@@ -620,6 +767,11 @@ struct Planner {
       for (const std::pair<size_t, size_t>& b : pending) ws_bufs.back()[b.first + base] = b.second;
     }
     std::vector<LaunchRec> L;
+    if (muon_mode) {
+      plan_muon(L, mats);
+      chunks.push_back(std::move(L));
+      return;
+    }
     // fp16 copies of the previous preconditioners: the OKLS factor products
     // read them, and a step that keeps the roots whitens with them
     const bool p_old = okls_mode || !refresh;
@@ -893,7 +1045,7 @@ struct Planner {
 
   bool validate() {
     if (!validate_plan(chunks)) return false;
-    return cfg.root_period <= 1 ? chunks_stale.empty() : validate_plan(chunks_stale);
+    return (cfg.root_period <= 1 || muon_mode) ? chunks_stale.empty() : validate_plan(chunks_stale);
   }
   bool validate_plan(const std::vector<std::vector<LaunchRec>>& plan_chunks) {
     if (ws_bufs.size() != plan_chunks.size()) return false;
@@ -910,7 +1062,7 @@ struct Planner {
         if (r.type == L_GEMM) {
           if (r.first < 0 || r.first + r.count > static_cast<int>(tiles.size())) return false;
           if (r.tile != kTile && r.tile != kBigTile) return false;
-          if (r.epi < EPI_STORE32 || r.epi > EPI_UPDATE) return false;
+          if (r.epi < EPI_STORE32 || r.epi > EPI_POLAR_UPDATE) return false;
           const int segs = r.split_in ? 2 : 1;
           for (int t = r.first; t < r.first + r.count; ++t) {
             const TileRef tr = tiles[t];
@@ -929,22 +1081,31 @@ struct Planner {
             if (p.s_out >= 0 && !slot_ok(p.s_out)) return false;
             if (p.cslot >= 0 && !slot_ok(p.cslot)) return false;
             const bool need32 = p.epi == EPI_STORE32 || p.epi == EPI_SYRK || p.epi == EPI_UPDATE ||
-                                (p.epi == EPI_NS_FINAL && p.out32.kind != REF_NONE);
+                                p.epi == EPI_POLAR_UPDATE || (p.epi == EPI_NS_FINAL && p.out32.kind != REF_NONE);
             if (need32) {
               if (p.out32.kind == REF_NONE || p.ld32 < p.N) return false;
               if (!fits(p.out32, (static_cast<size_t>(p.M - 1) * p.ld32 + p.N) * 4)) return false;
               if (p.epi == EPI_SYRK && p.M != p.N) return false;
             }
             const bool need16 = p.epi == EPI_NS_T || p.epi == EPI_NS_Y1 || p.epi == EPI_STORE16 ||
-                                (p.epi == EPI_NS_FINAL && p.out16.kind != REF_NONE);
+                                p.epi == EPI_POLAR || (p.epi == EPI_NS_FINAL && p.out16.kind != REF_NONE);
             if (need16) {
               if (p.out16.kind == REF_NONE || !slot_ok(p.s_out)) return false;
               const int need_ld = r.write_lo ? p.lo16 + p.Np : p.Np;
               if (p.ld16 < need_ld || (r.write_lo && p.lo16 < p.Np)) return false;
               if (!fits(p.out16, static_cast<size_t>(p.Mp) * p.ld16 * 2)) return false;
-              if (p.out16T.kind != REF_NONE) {
-                if (p.Mp != p.Np || !fits(p.out16T, static_cast<size_t>(p.Np) * p.ld16 * 2)) return false;
+              if (p.out16T.kind != REF_NONE) {   // Np x Mp with its own stride and lo offset
+                const int need_ldT = r.write_lo ? p.lo16T + p.Mp : p.Mp;
+                if (p.ld16T < need_ldT || (r.write_lo && p.lo16T < p.Mp)) return false;
+                if (!fits(p.out16T, static_cast<size_t>(p.Np) * p.ld16T * 2)) return false;
               }
+            }
+            if (p.epi == EPI_POLAR || p.epi == EPI_POLAR_UPDATE) {   // fp16 aux over the padded output
+              if (p.aux.kind == REF_NONE || !slot_ok(p.s_aux) || !slot_ok(p.cslot)) return false;
+              const int need_lda = p.aux_lo >= 0 ? p.aux_lo + p.Np : p.Np;
+              if (p.ldaux < need_lda || (p.aux_lo >= 0 && p.aux_lo < p.Np) || (p.ldaux & 3) || (p.aux_lo > 0 && (p.aux_lo & 3)))
+                return false;
+              if (!fits(p.aux, static_cast<size_t>(p.Mp) * p.ldaux * 2)) return false;
             }
             if (p.epi == EPI_NS_Y1) {
               if (p.aux.kind == REF_NONE || p.ldaux < p.N || !slot_ok(p.cslot)) return false;
@@ -985,6 +1146,12 @@ struct Planner {
               if (!fits(c.src2, (static_cast<size_t>(c.rows - 1) * c.src_ld + c.cols) * (c.g_bf16 ? 2 : 4))) return false;
             }
             if (c.kind == CA_NS_Y0 && (c.rows != c.cols || c.transpose)) return false;
+            if (c.dstT.kind != REF_NONE) {   // dst_cols_p x dst_rows_p, same lo flag
+              if (c.transpose) return false;
+              const int need_ldT = c.write_lo ? c.dstT_lo + c.dst_rows_p : c.dst_rows_p;
+              if (c.dstT_ld < need_ldT || (c.write_lo && c.dstT_lo < c.dst_rows_p)) return false;
+              if (!fits(c.dstT, static_cast<size_t>(c.dst_cols_p) * c.dstT_ld * 2)) return false;
+            }
             if (c.dst2.kind != REF_NONE) {
               if (c.kind != CA_NS_Y0 || !slot_ok(c.scale_slot2)) return false;
               if (c.write_lo2 && !c.write_lo) return false;     // the lo offset is checked through dst's
@@ -1025,7 +1192,7 @@ struct Planner {
       n_slots = std::max(n_slots, slot);
       plan_chunk(c, base, true, true);
     }
-    if (cfg.root_period > 1) {
+    if (cfg.root_period > 1 && !muon_mode) {
       // the plan of the steps that keep the roots, over the same buffers,
       // with its own algorithmic work
       double f[OKLS_PROFILE_CATEGORIES], b[OKLS_PROFILE_CATEGORIES];
@@ -1225,10 +1392,12 @@ static okls_status check_tensors(const okls_handle* h, const okls_group_tensors*
   if (t == nullptr) return OKLS_ERR_INVALID_ARG;
   for (size_t g = 0; g < h->groups.size(); ++g) {
     const okls_group_tensors& x = t[g];
-    if (x.M == nullptr || x.Sa == nullptr || x.Sb == nullptr || x.Pa == nullptr || x.Pb == nullptr)
-      return OKLS_ERR_INVALID_ARG;
-    if (!aligned(x.M, 4) || !aligned(x.Sa, 4) || !aligned(x.Sb, 4) || !aligned(x.Pa, 4) || !aligned(x.Pb, 4))
-      return OKLS_ERR_INVALID_ARG;
+    if (x.M == nullptr || !aligned(x.M, 4)) return OKLS_ERR_INVALID_ARG;
+    // the Muon mode has no factors or roots: Sa, Sb, Pa and Pb are not read and may be null
+    if (h->cfg.mode != OKLS_MODE_MUON) {
+      if (x.Sa == nullptr || x.Sb == nullptr || x.Pa == nullptr || x.Pb == nullptr) return OKLS_ERR_INVALID_ARG;
+      if (!aligned(x.Sa, 4) || !aligned(x.Sb, 4) || !aligned(x.Pa, 4) || !aligned(x.Pb, 4)) return OKLS_ERR_INVALID_ARG;
+    }
     if (need_wg) {
       if (x.W == nullptr || x.G == nullptr) return OKLS_ERR_INVALID_ARG;
       if (!aligned(x.W, 4) || !aligned(x.G, h->groups[g].g_dtype == OKLS_BF16 ? 2 : 4)) return OKLS_ERR_INVALID_ARG;
@@ -1248,10 +1417,12 @@ okls_status okls_init_state(okls_handle* h, const okls_group_tensors* t, void* s
   int n = 0;
   for (size_t g = 0; g < h->groups.size(); ++g) {
     const okls_group_desc& d = h->groups[g];
-    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, h->cfg.eps};
-    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, h->cfg.eps};
-    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, d.m, 1.0f};
-    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, d.n, 1.0f};
+    if (h->cfg.mode != OKLS_MODE_MUON) {
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, h->cfg.eps};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, h->cfg.eps};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, d.m, 1.0f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, d.n, 1.0f};
+    }
     a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_M, d.batch, d.m, d.n, 0.0f};
   }
   hipStream_t s = as_stream(stream);
@@ -1291,7 +1462,7 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
   float* part = reinterpret_cast<float*>(ws + h->off_part);
 
   // the roots are recomputed on steps 1, 1 + p, 1 + 2p, ... (p = root_period)
-  const bool refresh = h->cfg.root_period <= 1 || (step - 1) % h->cfg.root_period == 0;
+  const bool refresh = h->cfg.mode == OKLS_MODE_MUON || h->cfg.root_period <= 1 || (step - 1) % h->cfg.root_period == 0;
   if (h->prof) {
     h->acc.steps += 1;
     for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
@@ -1389,10 +1560,12 @@ okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* t, void*
   int n = 0;
   for (size_t g = 0; g < h->groups.size(); ++g) {
     const okls_group_desc& d = h->groups[g];
-    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, 0.f};
-    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, 0.f};
-    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, d.m, 0.f};
-    a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, d.n, 0.f};
+    if (h->cfg.mode != OKLS_MODE_MUON) {
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, 0.f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, 0.f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, d.m, 0.f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, d.n, 0.f};
+    }
     a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_M, d.batch, d.m, d.n, 0.f};
   }
   hipStream_t s = as_stream(stream);

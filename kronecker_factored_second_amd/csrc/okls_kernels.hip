@@ -86,8 +86,9 @@ struct EpiCtx {
   half_t* out16;
   half_t* out16T;
   const float* aux;
-  float s_out, cval;
-  int ld32, ld16, lo16, ldaux, aux_sym;
+  const half_t* aux16;      // EPI_POLAR*: previous iterate (fp16, scale 1 / aux_inv)
+  float s_out, cval, aux_inv;
+  int ld32, ld16, lo16, ld16T, lo16T, ldaux, aux_sym, aux_lo;
   float c0, c1, c2, ka, kb, lr, decay;
 };
 
@@ -124,7 +125,7 @@ struct Stage {
   __device__ static __forceinline__ void put(const EpiCtx& x, int r, int c, half4_t h) {
     *reinterpret_cast<half4_t*>(base(x, r) + off(r, c)) = h;
   }
-  __device__ static __forceinline__ void flush(const EpiCtx& x, int col_off) {
+  __device__ static __forceinline__ void flush(const EpiCtx& x, int col_off, int col_off_t) {
     const int lane = threadIdx.x & 63;
     WAIT_LGKM0();                                  // this wave's LDS writes done
     asm volatile("" ::: "memory");
@@ -148,7 +149,7 @@ struct Stage {
         half8_t v;
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] = b[off(r0 + q, c)];
-        __builtin_nontemporal_store(v, reinterpret_cast<half8_t*>(x.out16T + static_cast<size_t>(x.tc0 + c) * x.ld16 + col_off + x.tr0 + r0));
+        __builtin_nontemporal_store(v, reinterpret_cast<half8_t*>(x.out16T + static_cast<size_t>(x.tc0 + c) * x.ld16T + col_off_t + x.tr0 + r0));
       }
     }
     // the next staging pass overwrites this wave's region
@@ -175,6 +176,23 @@ struct Stage32 {
     return r * C::RN + (((c >> 2) ^ sw) << 2) + (c & 3);
   }
 };
+
+// Four consecutive elements (r, c..c+3) of the fp16 aux (the polar
+// iteration's previous iterate), hi + lo when it has lo halves, unscaled.
+// The aux is padded to the tile grid, so the quad is always inside it.
+__device__ __forceinline__ void aux16_quad(const EpiCtx& x, int r, int c, float (&v)[4]) {
+  const half_t* p = x.aux16 + static_cast<size_t>(r) * x.ldaux + c;
+  const half4_t h = *reinterpret_cast<const half4_t*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(h[e]);
+  if (x.aux_lo >= 0) {
+    const half4_t l = *reinterpret_cast<const half4_t*>(p + x.aux_lo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += static_cast<float>(l[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] *= x.aux_inv;
+}
 
 template <class C, int EPI>
 __device__ __forceinline__ void epilogue_f32(const floatx16 (&acc)[C::GI][C::GJ], const EpiCtx& x) {
@@ -218,7 +236,13 @@ __device__ __forceinline__ void epilogue_f32(const floatx16 (&acc)[C::GI][C::GJ]
             for (int e = 0; e < 4; ++e)
               if (c + e < x.N) row[c + e] = v[e];
           }
-        } else if constexpr (EPI == EPI_UPDATE) {
+        } else if constexpr (EPI == EPI_UPDATE || EPI == EPI_POLAR_UPDATE) {
+          if constexpr (EPI == EPI_POLAR_UPDATE) {
+            float xa[4];
+            aux16_quad(x, r, c, xa);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = x.cval * (x.ka * xa[e] + x.kb * v[e]);
+          }
           if (full) {
             const floatx4 w = *reinterpret_cast<const floatx4*>(row + c);
             *reinterpret_cast<floatx4*>(row + c) = x.decay * w - (x.lr * x.c0) * v;
@@ -287,7 +311,8 @@ __device__ __forceinline__ void epilogue_f32(const floatx16 (&acc)[C::GI][C::GJ]
 // consecutive columns cbase + 32 j + 8 g + e.
 template <class C, int EPI, int PART>
 __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ], const EpiCtx& x) {
-  constexpr bool kF16 = EPI == EPI_NS_T || EPI == EPI_NS_Y1 || EPI == EPI_STORE16 || EPI == EPI_NS_FINAL;
+  constexpr bool kF16 = EPI == EPI_NS_T || EPI == EPI_NS_Y1 || EPI == EPI_STORE16 || EPI == EPI_NS_FINAL ||
+                        EPI == EPI_POLAR;
 #pragma unroll
   for (int i = 0; i < C::GI; ++i) {
     const int r = x.rbase + i * 32;
@@ -331,6 +356,8 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
         }
       } else {
         // fp16 outputs into padded buffers (zeros outside the logical region)
+        float xa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (EPI == EPI_POLAR) aux16_quad(x, r, c0, xa);
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -339,6 +366,8 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
           if (r < x.M && c < x.N) {
             if constexpr (EPI == EPI_NS_T) {
               t = (r == c ? x.ka : 0.0f) + x.kb * v[e];
+            } else if constexpr (EPI == EPI_POLAR) {
+              t = x.cval * (x.ka * xa[e] + x.kb * v[e]);
             } else if constexpr (EPI == EPI_NS_Y1) {
               const float a0 = x.aux[static_cast<size_t>(r) * x.ldaux + c];
               const float sym = x.aux_sym ? 0.5f * (a0 + x.aux[static_cast<size_t>(c) * x.ldaux + r]) : a0;
@@ -367,7 +396,7 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
       }
     }
   }
-  if constexpr (kF16) Stage<C>::flush(x, PART == 0 ? 0 : x.lo16);
+  if constexpr (kF16) Stage<C>::flush(x, PART == 0 ? 0 : x.lo16, PART == 0 ? 0 : x.lo16T);
 }
 
 template <class C, int EPI, bool WL>
@@ -556,6 +585,11 @@ __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_nt_kernel(G
   ctx.out16 = P.out16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16, args.ws, args.user)) : nullptr;
   ctx.out16T = P.out16T.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16T, args.ws, args.user)) : nullptr;
   ctx.aux = P.aux.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(P.aux, args.ws, args.user)) : nullptr;
+  ctx.aux16 = reinterpret_cast<const half_t*>(ctx.aux);
+  ctx.aux_inv = P.s_aux >= 0 ? 1.0f / args.scal[P.s_aux] : 1.0f;
+  ctx.aux_lo = P.aux_lo;
+  ctx.ld16T = P.ld16T;
+  ctx.lo16T = P.lo16T;
   ctx.s_out = P.s_out >= 0 ? args.scal[P.s_out] : 1.0f;
   ctx.cval = P.cslot >= 0 ? args.scal[P.cslot] : 1.0f;
   ctx.ld32 = P.ld32;
@@ -570,7 +604,7 @@ __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_nt_kernel(G
   ctx.kb = args.kb;
   ctx.lr = args.lr;
   ctx.decay = args.decay;
-  if constexpr (EPI == EPI_STORE32 || EPI == EPI_UPDATE || EPI == EPI_SYRK) {
+  if constexpr (EPI == EPI_STORE32 || EPI == EPI_UPDATE || EPI == EPI_SYRK || EPI == EPI_POLAR_UPDATE) {
     epilogue_f32<C, EPI>(acc, ctx);
   } else {
     epilogue_pass<C, EPI, 0>(acc, ctx);
@@ -949,6 +983,35 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
       const int r = dr0 + wave + 4 * p, c0 = dc0 + 4 * lane;
       if (c0 < J.dst_cols_p) store16(dst + static_cast<size_t>(r) * J.dst_ld + c0, J.dst_lo, write_lo, x[p], scale);
     }
+    if (J.dstT.kind == REF_NONE) return;
+    // transposed copy (dst_cols_p x dst_rows_p): column j (0..255) of the
+    // block's region and row i (0..63) live at j * 64 + (i ^ ((j >> 2) & 31)),
+    // so both the writes below (one row, columns 4 lane + e) and the reads
+    // (one column, rows 4 q + e) spread over the banks
+    half_t* dstT = reinterpret_cast<half_t*>(resolve(J.dstT, a.ws, a.user));
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int i = wave + 4 * p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * lane + e;
+        tile[j * kCastRows + (i ^ ((j >> 2) & 31))] = x[p][e];
+      }
+    }
+    WAIT_LGKM0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int q = threadIdx.x & 15;
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int j = (threadIdx.x >> 4) + 16 * p;     // row dc0 + j of the transposed copy
+      if (dc0 + j >= J.dst_cols_p) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = tile[j * kCastRows + ((4 * q + e) ^ ((j >> 2) & 31))];
+      store16(dstT + static_cast<size_t>(dc0 + j) * J.dstT_ld + dr0 + 4 * q, J.dstT_lo, write_lo, v, scale);
+    }
     return;
   }
   // ---- transposed: destination (r, c) = source (c, r).  Source row i of the
@@ -1028,6 +1091,8 @@ hipError_t launch_gemm_cfg(const GemmArgs& a, int n_tiles, int epi, hipStream_t 
     case EPI_NS_Y1: if (wl) OKLS_GEMM(EPI_NS_Y1, true); else OKLS_GEMM(EPI_NS_Y1, false); break;
     case EPI_STORE16: if (wl) OKLS_GEMM(EPI_STORE16, true); else OKLS_GEMM(EPI_STORE16, false); break;
     case EPI_NS_FINAL: if (wl) OKLS_GEMM(EPI_NS_FINAL, true); else OKLS_GEMM(EPI_NS_FINAL, false); break;
+    case EPI_POLAR: if (wl) OKLS_GEMM(EPI_POLAR, true); else OKLS_GEMM(EPI_POLAR, false); break;
+    case EPI_POLAR_UPDATE: OKLS_GEMM(EPI_POLAR_UPDATE, false); break;
     default: return hipErrorInvalidValue;
   }
 #undef OKLS_GEMM

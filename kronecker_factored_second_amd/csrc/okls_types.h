@@ -52,7 +52,9 @@ enum Epi : int32_t {
   EPI_NS_Y1 = 3,     // Y1 = ka*(aux*scal[cslot] + c2*I) + kb*v -> out16
   EPI_STORE16 = 4,   // out16 = v * scal[s_out]
   EPI_NS_FINAL = 5,  // out32 = v * scal[cslot] (fp32 root), out16 = v * scal[s_out]
-  EPI_UPDATE = 6     // W = decay*W - lr*c0*v
+  EPI_UPDATE = 6,    // W = decay*W - lr*c0*v
+  EPI_POLAR = 7,     // X' = scal[cslot] * (ka*X + kb*v) -> out16 (+ out16T), X = fp16 aux
+  EPI_POLAR_UPDATE = 8   // W = decay*W - lr*c0*scal[cslot]*(ka*X + kb*v), X = fp16 aux
 };
 
 struct GemmProb {
@@ -63,9 +65,12 @@ struct GemmProb {
   int32_t epi;
   Ref out32; int32_t ld32;
   Ref out16; int32_t ld16; int32_t lo16;   // lo part at +lo16 halves within a row
-  Ref out16T;              // optional transposed copy (same ld16 / lo16; square problems)
-  Ref aux; int32_t ldaux;
+  Ref out16T;              // optional transposed copy (Np x Mp)
+  int32_t ld16T, lo16T;    // its row stride and lo offset, in halves
+  Ref aux; int32_t ldaux;  // EPI_NS_Y1: fp32; EPI_POLAR*: fp16 (padded, Mp x Np)
   int32_t aux_sym;         // EPI_NS_Y1: 1 = read (aux + aux^T) / 2
+  int32_t aux_lo;          // EPI_POLAR*: lo part at +aux_lo halves within a row, or -1
+  int32_t s_aux;           // EPI_POLAR*: scale slot of the fp16 aux
   int32_t sA, sB;          // scale slots of the operands (alpha = 1/(scal[sA]*scal[sB]))
   int32_t s_out;           // scale slot for fp16 output
   int32_t cslot;           // per-problem device scalar used by the epilogue
@@ -159,6 +164,8 @@ struct CastJob {
   Ref dst2;                // CA_NS_Y0: second destination (same ld and lo offset), or REF_NONE
   int32_t scale_slot2;     // its static scale
   int32_t write_lo2;
+  Ref dstT;                // non-transposed jobs: transposed copy of the destination, or REF_NONE
+  int32_t dstT_ld, dstT_lo;   // (dst_cols_p x dst_rows_p; same scale and lo flag as dst)
 };
 
 struct CastArgs {

@@ -17,7 +17,9 @@ OKLS_OK = 0
 STATUS = {0: "OKLS_OK", -1: "OKLS_ERR_INVALID_ARG", -2: "OKLS_ERR_SHAPE", -3: "OKLS_ERR_DTYPE",
           -4: "OKLS_ERR_WORKSPACE", -5: "OKLS_ERR_HIP", -6: "OKLS_ERR_NONFINITE", -7: "OKLS_ERR_UNSUPPORTED"}
 OKLS_F32, OKLS_BF16 = 0, 1
-MODE = {"okls": 0, "shampoo": 1}
+MODE = {"okls": 0, "shampoo": 1, "muon": 2}
+# the Muon setting of the polar iteration: 5 steps (Clean, Table 6) on [1e-2, 1]
+MUON_DEFAULTS = dict(ns_steps=5, ns_floor=1e-2)
 EXPORTED = ("okls_default_config", "okls_workspace_size", "okls_init", "okls_init_state", "okls_step",
             "okls_check_finite", "okls_ns_coefficients", "okls_profile_enable", "okls_profile_read",
             "okls_destroy", "okls_status_string")
@@ -251,6 +253,9 @@ class OKLS:
         if not self.params:
             raise ValueError("no parameters")
         self.lr = float(lr)
+        self.mode = mode
+        if mode == "muon":
+            cfg_overrides = {**MUON_DEFAULTS, **cfg_overrides}
         self.cfg = precision_config(precision, mode=MODE[mode], beta1=beta1, beta2=beta2, eps=eps,
                                     weight_decay=weight_decay, lr_peak=float(lr), chunk_matrices=chunk_matrices,
                                     **cfg_overrides)
@@ -265,9 +270,12 @@ class OKLS:
             b, m, n = shp
             gdt = OKLS_BF16 if (grad_dtype or torch.float32) == torch.bfloat16 else OKLS_F32
             self.groups.append((b, m, n, gdt))
-            self.state.append(dict(M=torch.zeros(b, m, n, device=dev), Sa=torch.empty(b, m, m, device=dev),
-                                   Sb=torch.empty(b, n, n, device=dev), Pa=torch.empty(b, m, m, device=dev),
-                                   Pb=torch.empty(b, n, n, device=dev)))
+            if mode == "muon":     # no factors or roots
+                self.state.append(dict(M=torch.zeros(b, m, n, device=dev)))
+            else:
+                self.state.append(dict(M=torch.zeros(b, m, n, device=dev), Sa=torch.empty(b, m, m, device=dev),
+                                       Sb=torch.empty(b, n, n, device=dev), Pa=torch.empty(b, m, m, device=dev),
+                                       Pb=torch.empty(b, n, n, device=dev)))
         ws_bytes = workspace_size(self.cfg, self.groups)
         if ws_bytes == 0:
             raise OKLSError("okls_workspace_size", -1)

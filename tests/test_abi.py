@@ -133,3 +133,16 @@ def test_binding_raises_without_library(tmp_path):
             okls.load(str(tmp_path / "nope.so"))
     finally:
         okls._lib = saved
+
+
+def test_muon_plans_validate_on_the_host():
+    """Muon mode (polar iteration of the momentum) plans and validates its
+    descriptors for wide, tall, ragged and tiny shapes on both paths; the
+    iteration needs at least two steps."""
+    for prec in ("fp16", "fp32"):
+        cfg = okls.precision_config(prec, mode=okls.MODE["muon"], **okls.MUON_DEFAULTS)
+        for groups in ([(2, 96, 160, 0)], [(1, 200, 72, 0), (3, 33, 40, 1)], [(1, 1, 7, 0)],
+                       [(4, 1024, 1024, 1), (2, 2816, 1024, 1), (1, 1024, 2816, 1)]):
+            assert okls.workspace_size(cfg, groups) > 0, (prec, groups)
+        cfg.ns_steps = 1
+        assert okls.workspace_size(cfg, [(1, 64, 80, 0)]) == 0

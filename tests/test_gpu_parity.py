@@ -161,6 +161,70 @@ def test_root_refresh_period(mode, precision):
                 assert np.array_equal(after.Pa, bf.Pa) and np.array_equal(after.Pb, bf.Pb), (t, gi, i)
 
 
+def _muon_snapshot(opt, gi, i):
+    f = lambda t: t[i].detach().double().cpu().numpy()
+    return O.MatState(W=f(opt.params[gi]), M=f(opt.state[gi]["M"]), Sa=None, Sb=None, Pa=None, Pb=None)
+
+
+@pytest.mark.parametrize("precision,u_tol", [("fp16", 2e-2), ("fp32", 1e-4)])
+def test_muon_mode(precision, u_tol):
+    """Muon (polar Newton-Schulz of the momentum, 5 steps) over wide, tall,
+    square-ish and tiny shapes (ragged against the tiles), 4 teacher-forced
+    steps: M, and the orthogonalised update read back from W (zeroed before
+    each step), against the oracle's fp64 iteration."""
+    torch = pytest.importorskip("torch")
+    groups = [(96, 160, 2), (200, 72, 1), (33, 40, 2), (1, 7, 1)]
+    opt, params = H.make(groups, precision=precision, mode="muon")
+    hp = H.hyper_of(opt)
+    assert hp.ns_steps == 5 and abs(hp.ns_floor - 1e-2) < 1e-9
+    assert all(set(st) == {"M"} for st in opt.state)          # no factors or roots are allocated
+    worst = 0.0
+    for t in range(1, 5):
+        host = {gi: [(0.02 * np.random.default_rng([gi, i, t, 91]).standard_normal((m, n))).astype(np.float32)
+                     for i in range(b)] for gi, (m, n, b) in enumerate(groups)}
+        for p in params:
+            p.zero_()
+        before = {(gi, i): _muon_snapshot(opt, gi, i) for gi, (m, n, b) in enumerate(groups) for i in range(b)}
+        opt.step(grads=[H.to_device_grad(np.stack(host[gi]), "f32") for gi in range(len(groups))])
+        torch.cuda.synchronize()
+        for (gi, i), bf in before.items():
+            ref = O.muon_step(bf, host[gi][i].astype(np.float64), hp, t)
+            af = _muon_snapshot(opt, gi, i)
+            m, n = af.W.shape
+            U = -af.W / (hp.lr * O.c_shape(m, n))
+            assert np.isfinite(af.W).all()
+            e_m, e_u = O.rel_frob(af.M, ref.state.M), O.rel_frob(U, ref.U)
+            assert e_m < 1e-6, (t, gi, i, e_m)
+            assert e_u < u_tol, (t, gi, i, e_u)
+            worst = max(worst, e_u)
+    print(f"[muon-{precision}] worst U {worst:.2e}", flush=True)
+
+
+def test_muon_worked_example_on_gpu():
+    """The Shampoo chapter's 2 x 3 gradient through the HIP path in Muon mode
+    (split path): the update's singular values are those of the 5-step
+    scalar map at sigma / (sum sigma^4)^{1/4}, both within 0.03 of 1 (the
+    un-accumulated Shampoo step's 1, 1)."""
+    torch = pytest.importorskip("torch")
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "shampoo_worked_example.json")))
+    G = np.array(g["G"], dtype=np.float32)
+    opt, params = H.make([(2, 3, 1)], precision="fp32", mode="muon")
+    opt.step(grads=[torch.tensor(G, device="cuda:0")[None]])
+    torch.cuda.synchronize()
+    hp = H.hyper_of(opt)
+    U = -params[0][0].double().cpu().numpy() / (hp.lr * O.c_shape(2, 3))
+    sv = np.linalg.svd(U, compute_uv=False)
+    coeffs, _ = O.ns_coefficients(hp.ns_floor, hp.ns_steps)
+    s = np.array(g["singular_values_G"]) / np.sum(np.array(g["singular_values_G"]) ** 4) ** 0.25
+    for a, b in coeffs:
+        s = s * (a + b * s * s)
+    print(f"[muon-worked-example] sv={sv} expected={s}", flush=True)
+    np.testing.assert_allclose(sv, s, atol=2e-3)    # the page prints G's singular values to 3 decimals
+    assert np.all(np.abs(sv - 1.0) < 0.03)
+
+
 def test_bf16_gradients_rowscaled():
     """bf16 gradients with per-row log-uniform scales (the transformer-block
     workload's distribution) at a reduced shape spanning several tiles."""
