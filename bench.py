@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--device-grads", action="store_true",
                    help="Gaussian gradients of the workload's scale generated on the GPU (the default for "
                         "workloads above 1e9 parameters, whose host recipes would take minutes per step)")
+    p.add_argument("--mode", choices=["okls", "shampoo", "muon"], default=None,
+                   help="optimizer mode (default: the workload's); muon runs the polar iteration of the momentum "
+                        "on the same matrices, the pages' throughput comparison")
     p.add_argument("--root-period", type=int, default=1,
                    help="recompute the roots every this many steps (1: every step)")
     p.add_argument("--copy-probe", action="store_true",
@@ -151,7 +154,7 @@ def measured_traffic():
     return None
 
 
-def cpu_baseline(w, budget_s, root_period=1):
+def cpu_baseline(w, budget_s, root_period=1, mode=None):
     """The fp64 oracle, as it stands, on a bounded sample: one matrix of each
     distinct shape class of the workload, a full oracle step each (exact eigh
     roots plus the fp64 Newton-Schulz iteration), scaled to the whole
@@ -164,18 +167,19 @@ def cpu_baseline(w, budget_s, root_period=1):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
-    hp = O.Hyper(root_period=root_period)
+    mode = mode or w.mode
+    hp = O.muon_hyper() if mode == "muon" else O.Hyper(root_period=root_period)
     total_s, sampled, step_s = 0.0, [], 0.0
     for gi, (m, n, b) in enumerate(w.groups):
         G = WL.gradient(w, gi, 0, 1).astype(np.float64)
         st = O.init_state(np.zeros((m, n)), hp.eps)
         t0 = time.perf_counter()
-        r = O.step(st, G, hp, 1, w.mode)
+        r = O.step(st, G, hp, 1, mode)
         dt = time.perf_counter() - t0
         total_s += dt
         if root_period > 1:
             t0 = time.perf_counter()
-            O.step(r.state, G, hp, 2, w.mode)
+            O.step(r.state, G, hp, 2, mode)
             dt2 = time.perf_counter() - t0
             total_s += dt2
             dt = (dt + (root_period - 1) * dt2) / root_period
@@ -207,6 +211,7 @@ def main():
     from kronecker_factored_second_amd import okls, workloads as WL
 
     w = WL.workload(args.workload)
+    mode = args.mode or w.mode
     dev = torch.device("cuda:0")
     bf16 = w.grad_dtype == "bf16"
     big = w.n_params > 1e9
@@ -235,7 +240,7 @@ def main():
     if big:   # leave room for the caller's tensors: the workspace takes what the card has left
         limit = torch.cuda.mem_get_info(0)[0] - sum(b * (m * n + 2 * m * m + 2 * n * n) * 4 for m, n, b in w.groups) \
             - (8 << 30)
-    opt = okls.OKLS(params, mode=w.mode, precision=args.precision,
+    opt = okls.OKLS(params, mode=mode, precision=args.precision,
                     grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit,
                     root_period=args.root_period)
     for i in range(args.warmup):
@@ -284,7 +289,7 @@ def main():
         "dtype": "fp16" if args.precision == "fp16" else "fp16x3-split",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: " + ", ".join(f"{b}x {m}x{n}" for m, n, b in w.groups) +
-                   f" ({w.n_matrices} matrices, {w.n_params / 1e6:.1f}M params), {w.mode}, "
+                   f" ({w.n_matrices} matrices, {w.n_params / 1e6:.1f}M params), {mode}, "
                    f"{w.grad_dtype} gradients" + (" (device Gaussian)" if device_grads else "") +
                    f", precision {args.precision}" +
                    (f", chunks of {opt.cfg.chunk_matrices} matrices" if opt.cfg.chunk_matrices else "") +
@@ -313,7 +318,7 @@ def main():
         "host_wall_s": wall,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds, args.root_period)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds, args.root_period, mode)
     print(json.dumps(line), flush=True)
 
 

@@ -449,17 +449,20 @@ def muon_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ns") 
     """One Muon step (R16): Nesterov momentum (R5), N orthogonalised by the
     polar iteration, c_shape-scaled update with the decoupled decay (R6).
     The factors and roots of the state are neither used nor changed.
-    root='exact' replaces the iteration by the SVD polar factor U V^T."""
+    root='exact' updates with the SVD polar factor U V^T (the method's
+    target) instead of the iteration's result; both are always computed and
+    the iteration's is in extra["U_ns"]."""
     G = np.asarray(G, dtype=np.float64)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
+    coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+    U_ns = ns_polar(N, coeffs)
+    U = U_ns
     if root == "exact":
         u, _, vt = np.linalg.svd(N, full_matrices=False)
         U = u @ vt
-    else:
-        coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
-        U = ns_polar(N, coeffs)
     W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
-    return StepResult(MatState(W, M, st.Sa, st.Sb, st.Pa, st.Pb), N, U, st.Pa, st.Pb, float("nan"), float("nan"))
+    return StepResult(MatState(W, M, st.Sa, st.Sb, st.Pa, st.Pb), N, U, st.Pa, st.Pb, float("nan"), float("nan"),
+                      extra={"U_ns": U_ns})
 
 
 def step(st: MatState, G, hp: Hyper, t: int, mode: str = "okls", root: str = "exact") -> StepResult:

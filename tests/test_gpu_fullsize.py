@@ -67,10 +67,11 @@ def _free_gpu():
     torch.cuda.empty_cache()
 
 
-def _build(name, precision):
+def _build(name, precision, mode=None):
     """Full workload: parameters (sampled ones from the spectral-muP init,
     the rest filler of the same scale) and the optimizer, its workspace
-    limited so that one step's gradients still fit."""
+    limited so that one step's gradients still fit.  mode overrides the
+    workload's optimizer mode."""
     torch = pytest.importorskip("torch")
     w = WL.workload(name)
     WL.reset_caches()
@@ -86,8 +87,8 @@ def _build(name, precision):
     free = torch.cuda.mem_get_info(0)[0]
     limit = free - opt_bytes - 2 * grad_bytes - (8 << 30)
     from kronecker_factored_second_amd import okls
-    opt = okls.OKLS(params, mode=w.mode, precision=precision, grad_dtype=torch.bfloat16 if bf16 else torch.float32,
-                    workspace_limit=limit)
+    opt = okls.OKLS(params, mode=mode or w.mode, precision=precision,
+                    grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit)
     _log(f"{name}-{precision}: {w.n_matrices} matrices, chunk_matrices={opt.cfg.chunk_matrices}, "
          f"workspace {opt.workspace.numel() / 2**30:.1f} GiB")
     return w, opt, params
@@ -244,3 +245,44 @@ def test_fullsize_known_spectrum(name, precision):
         assert e["P_a"] < tol["P"] and e["P_b"] < tol["P"], e
     del grads, opt, params, known
     _free_gpu()
+
+
+# Muon mode at full size: the whole orthogonalised update of every checked
+# matrix against the oracle's fp64 polar iteration of the same momentum
+# (13B-class: the 5120 x 5120 matrix only, the fp64 iteration of the
+# 13824-wide ones taking minutes).
+MUON_CHECK = {"c2": None, "c3": [(0, 0), (1, 0), (2, 0)], "c5": [(0, 0)]}
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+def test_fullsize_muon(name):
+    torch = pytest.importorskip("torch")
+    _free_gpu()
+    w, opt, params = _build(name, "fp16", mode="muon")
+    hp = H.hyper_of(opt)
+    checked = MUON_CHECK[name] or _sampled(w, name)
+    rep = H.Report(f"full-muon-{name}")
+    for t in (1, 2):
+        grads, host = _grads(w, name, t)
+        before = {k: (_f64(params[k[0]][k[1]]), _f64(opt.state[k[0]]["M"][k[1]])) for k in checked}
+        opt.step(grads=grads)
+        torch.cuda.synchronize()
+        assert opt.check_finite(), f"non-finite state after step {t}"
+        for gi, i in checked:
+            m, n, _ = w.groups[gi]
+            W0, M0 = before[(gi, i)]
+            st = O.MatState(W=W0, M=M0, Sa=None, Sb=None, Pa=None, Pb=None)
+            _log(f"muon {name} t={t} ({gi},{i}): fp64 polar iteration of {m} x {n}")
+            ref = O.muon_step(st, host[(gi, i)], hp, t)
+            W1 = _f64(params[gi][i])
+            decay = 1.0 - hp.lr * hp.weight_decay * (hp.lr / hp.peak())
+            U_gpu = (decay * W0 - W1) / (hp.lr * O.c_shape(m, n))
+            e = dict(t=t, g=gi, i=i, M=O.rel_frob(_f64(opt.state[gi]["M"][i]), ref.state.M),
+                     U=O.rel_frob(U_gpu, ref.U), W=O.rel_frob(W1, ref.state.W))
+            rep.add(**e)
+            assert e["M"] < TOL["fp16"]["M"] and e["U"] < TOL["fp16"]["U"] and e["W"] < TOL["fp16"]["W"], e
+        del grads
+    del opt, params
+    _free_gpu()
+
