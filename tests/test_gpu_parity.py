@@ -225,6 +225,30 @@ def test_muon_worked_example_on_gpu():
     assert np.all(np.abs(sv - 1.0) < 0.03)
 
 
+@pytest.mark.parametrize("mode", ["okls", "shampoo", "muon"])
+def test_chunked_steps_are_bitwise_unchunked(mode):
+    """chunk_matrices = 1 and 2 (one launch list per chunk, workspace reused)
+    give bit-identical states to one chunk: every output element is computed
+    by the same kernels in the same order whichever problems share a launch."""
+    torch = pytest.importorskip("torch")
+    groups = [(96, 160, 2), (130, 72, 1), (33, 40, 2)]
+    runs = []
+    for chunk in (0, 1, 2):
+        opt, params = H.make(groups, precision="fp16", mode=mode, chunk_matrices=chunk)
+        for t in (1, 2):
+            grads = [H.to_device_grad((0.02 * np.random.default_rng([gi, t, 17]).standard_normal((b, m, n)))
+                                      .astype(np.float32), "f32") for gi, (m, n, b) in enumerate(groups)]
+            opt.step(grads=grads)
+        torch.cuda.synchronize()
+        runs.append([{k: v.cpu().numpy().copy() for k, v in st.items()} | {"W": params[gi].cpu().numpy().copy()}
+                     for gi, st in enumerate(opt.state)])
+        del opt, params
+    for other in runs[1:]:
+        for a, b in zip(runs[0], other):
+            for k in a:
+                assert np.array_equal(a[k], b[k]), (mode, k)
+
+
 def test_bf16_gradients_rowscaled():
     """bf16 gradients with per-row log-uniform scales (the transformer-block
     workload's distribution) at a reduced shape spanning several tiles."""
