@@ -406,7 +406,9 @@ struct Planner {
     }
     const bool f16_out = r.epi == EPI_NS_T || r.epi == EPI_NS_Y1 || r.epi == EPI_STORE16 || r.epi == EPI_NS_FINAL ||
                          r.epi == EPI_POLAR;
-    if (big_tiles < (f16_out ? 64 : 512)) r.tile = kTile;
+    // a Muon launch has no concurrent chain to fill a partly idle round: the
+    // 256 tile only from one full round of it
+    if (big_tiles < (f16_out ? (muon_mode ? 256 : 64) : 512)) r.tile = kTile;
     const std::pair<int, int> t = tiles_for(ps, upper, r.tile);
     r.first = t.first;
     r.count = t.second;
