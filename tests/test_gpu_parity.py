@@ -249,6 +249,43 @@ def test_chunked_steps_are_bitwise_unchunked(mode):
                 assert np.array_equal(a[k], b[k]), (mode, k)
 
 
+@pytest.mark.parametrize("mode", ["okls", "muon"])
+def test_step_replays_bitwise_from_a_hip_graph(mode):
+    """okls_step captured into a HIP graph (its side-stream fork and join
+    included) replays bit-identically to the eager step: three replays, each
+    from the same restored state with eager copies in between."""
+    torch = pytest.importorskip("torch")
+    from kronecker_factored_second_amd import okls
+    groups = [(96, 160, 2), (130, 72, 1)]
+    grads = [H.to_device_grad((0.02 * np.random.default_rng([gi, 23]).standard_normal((b, m, n))).astype(np.float32), "f32")
+             for gi, (m, n, b) in enumerate(groups)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        opt, params = H.make(groups, precision="fp16", mode=mode)
+        for _ in range(2):
+            opt.step(grads=grads)
+        def state():
+            return [t for st, p in zip(opt.state, params) for t in (*st.values(), p)]
+        saved = [t.clone() for t in state()]
+        opt.step(grads=grads)          # eager step t = 3
+        torch.cuda.synchronize()
+        eager = [t.clone() for t in state()]
+        for t, v in zip(state(), saved):
+            t.copy_(v)
+        tensors = opt._tensors(grads)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            okls.step(opt.handle, tensors, 3, opt.lr, torch.cuda.current_stream().cuda_stream)
+        for rep in range(3):
+            for t, v in zip(state(), saved):
+                t.copy_(v)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(state(), eager):
+                assert torch.equal(a, b), (mode, rep)
+
+
 def test_bf16_gradients_rowscaled():
     """bf16 gradients with per-row log-uniform scales (the transformer-block
     workload's distribution) at a reduced shape spanning several tiles."""
