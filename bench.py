@@ -201,7 +201,7 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the preconditioner step runs on a single MI355X in this build; "
+        print("bench.py measures one GPU: the preconditioner step runs on a single MI355X; "
               "--gpus above 1 is not supported", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:

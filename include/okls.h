@@ -63,7 +63,7 @@ typedef enum {
     OKLS_ERR_WORKSPACE = -4,     /* workspace null, misaligned or smaller than okls_workspace_size */
     OKLS_ERR_HIP = -5,           /* a HIP runtime call or launch failed */
     OKLS_ERR_NONFINITE = -6,     /* okls_check_finite found Inf/NaN in the state */
-    OKLS_ERR_UNSUPPORTED = -7    /* a combination this build does not implement */
+    OKLS_ERR_UNSUPPORTED = -7    /* a combination the library does not implement */
 } okls_status;
 
 typedef enum { OKLS_F32 = 0, OKLS_BF16 = 1 } okls_dtype;
