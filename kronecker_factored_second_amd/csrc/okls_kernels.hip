@@ -89,6 +89,7 @@ struct EpiCtx {
   const half_t* aux16;      // EPI_POLAR*: previous iterate (fp16, scale 1 / aux_inv)
   float s_out, cval, aux_inv;
   int ld32, ld16, lo16, ld16T, lo16T, ldaux, aux_sym, aux_lo;
+  bool aux_vec, out32_vec;  // fp32 aux rows / fp32 output rows are 16-byte aligned
   float c0, c1, c2, ka, kb, lr, decay;
 };
 
@@ -358,6 +359,24 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
         // fp16 outputs into padded buffers (zeros outside the logical region)
         float xa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (EPI == EPI_POLAR) aux16_quad(x, r, c0, xa);
+        if constexpr (EPI == EPI_NS_Y1) {
+          // the rooted matrix at (r, c0..c0+3): one 16-byte load when the quad
+          // is inside and its rows are 16-byte aligned (not for the
+          // symmetrised read, whose second term is a column)
+          if (x.aux_vec && r < x.M && c0 + 3 < x.N) {
+            const float4 a4 = *reinterpret_cast<const float4*>(x.aux + static_cast<size_t>(r) * x.ldaux + c0);
+            xa[0] = a4.x; xa[1] = a4.y; xa[2] = a4.z; xa[3] = a4.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int c = c0 + e;
+              if (r < x.M && c < x.N) {
+                const float a0 = x.aux[static_cast<size_t>(r) * x.ldaux + c];
+                xa[e] = x.aux_sym ? 0.5f * (a0 + x.aux[static_cast<size_t>(c) * x.ldaux + r]) : a0;
+              }
+            }
+          }
+        }
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -369,9 +388,7 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
             } else if constexpr (EPI == EPI_POLAR) {
               t = x.cval * (x.ka * xa[e] + x.kb * v[e]);
             } else if constexpr (EPI == EPI_NS_Y1) {
-              const float a0 = x.aux[static_cast<size_t>(r) * x.ldaux + c];
-              const float sym = x.aux_sym ? 0.5f * (a0 + x.aux[static_cast<size_t>(c) * x.ldaux + r]) : a0;
-              t = x.ka * (sym * x.cval + (r == c ? x.c2 : 0.0f)) + x.kb * v[e];
+              t = x.ka * (xa[e] * x.cval + (r == c ? x.c2 : 0.0f)) + x.kb * v[e];
             } else {  // EPI_STORE16, EPI_NS_FINAL
               t = v[e];
             }
@@ -380,9 +397,14 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
         }
         if constexpr (EPI == EPI_NS_FINAL && PART == 0) {
           if (x.out32 != nullptr && r < x.M) {
+            float* o = x.out32 + static_cast<size_t>(r) * x.ld32 + c0;
+            if (x.out32_vec && c0 + 3 < x.N) {
+              *reinterpret_cast<float4*>(o) = float4{y[0] * x.cval, y[1] * x.cval, y[2] * x.cval, y[3] * x.cval};
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (c0 + e < x.N) x.out32[static_cast<size_t>(r) * x.ld32 + c0 + e] = y[e] * x.cval;
+              for (int e = 0; e < 4; ++e)
+                if (c0 + e < x.N) o[e] = y[e] * x.cval;
+            }
           }
         }
         half4_t h;
@@ -586,6 +608,8 @@ __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_nt_kernel(G
   ctx.out16T = P.out16T.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(P.out16T, args.ws, args.user)) : nullptr;
   ctx.aux = P.aux.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(P.aux, args.ws, args.user)) : nullptr;
   ctx.aux16 = reinterpret_cast<const half_t*>(ctx.aux);
+  ctx.aux_vec = ctx.aux != nullptr && !P.aux_sym && (P.ldaux & 3) == 0 && (reinterpret_cast<uintptr_t>(ctx.aux) & 15) == 0;
+  ctx.out32_vec = ctx.out32 != nullptr && (P.ld32 & 3) == 0 && (reinterpret_cast<uintptr_t>(ctx.out32) & 15) == 0;
   ctx.aux_inv = P.s_aux >= 0 ? 1.0f / args.scal[P.s_aux] : 1.0f;
   ctx.aux_lo = P.aux_lo;
   ctx.ld16T = P.ld16T;
