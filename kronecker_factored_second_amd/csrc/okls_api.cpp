@@ -810,11 +810,8 @@ struct Planner {
       g.rows = mb.m; g.cols = mb.n; g.dst_rows_p = mb.mp; g.dst_cols_p = mb.np; g.dst = ws_ref(mb.G16);
       g.dst_ld = mb.ldn; g.dst_lo = mb.np; g.parts = parts[per * q]; g.scale_mode = SC_ABSMAX;
       g.scale_slot = mb.s_g; g.write_lo = fs;
+      g.dstT = ws_ref(mb.G16T); g.dstT_ld = mb.ldm; g.dstT_lo = mb.mp;   // G^T from the same pass over G
       cs.push_back(g);
-      CastSpec gt = g;
-      gt.transpose = 1; gt.dst_rows_p = mb.np; gt.dst_cols_p = mb.mp; gt.dst = ws_ref(mb.G16T);
-      gt.dst_ld = mb.ldm; gt.dst_lo = mb.mp;
-      cs.push_back(gt);
       CastSpec nn = cast_spec();
       nn.kind = CA_NESTEROV; nn.src = user_ref(REF_M, mb.group, moff(mb)); nn.src_ld = mb.n;
       nn.src2 = user_ref(REF_G, mb.group, goff(mb)); nn.g_bf16 = bf; nn.write_m = 1;
