@@ -305,15 +305,15 @@ __device__ __forceinline__ void epilogue_f32(const floatx16 (&acc)[C::GI][C::GJ]
   }
 }
 
-// One pass over the accumulators.  fp32 kinds store directly; fp16 kinds
-// stage PART 0 (the fp16 values, or the hi halves of the split layout) or
-// PART 1 (the lo halves, y s - fp16(y s)) through LDS.  Block (i, j) of a
+// One pass over the accumulators of an fp16-output kind: stages PART 0 (the
+// fp16 values, or the hi halves of the split layout) or PART 1 (the lo
+// halves, y s - fp16(y s)) through LDS.  Block (i, j) of a
 // wave holds, in each lane, row rbase + 32 i and the four groups of four
 // consecutive columns cbase + 32 j + 8 g + e.
 template <class C, int EPI, int PART>
 __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ], const EpiCtx& x) {
-  constexpr bool kF16 = EPI == EPI_NS_T || EPI == EPI_NS_Y1 || EPI == EPI_STORE16 || EPI == EPI_NS_FINAL ||
-                        EPI == EPI_POLAR;
+  static_assert(EPI == EPI_NS_T || EPI == EPI_NS_Y1 || EPI == EPI_STORE16 || EPI == EPI_NS_FINAL || EPI == EPI_POLAR,
+                "fp32-output kinds go through epilogue_f32");
 #pragma unroll
   for (int i = 0; i < C::GI; ++i) {
     const int r = x.rbase + i * 32;
@@ -324,38 +324,7 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * x.alpha;
-      if constexpr (EPI == EPI_STORE32) {
-        if (r < x.M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c0 + e < x.N) x.out32[static_cast<size_t>(r) * x.ld32 + c0 + e] = v[e];
-        }
-      } else if constexpr (EPI == EPI_SYRK) {
-        // S <- c0*S + c1*v + c2*I on the upper triangle, mirrored below.
-        if (r < x.M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = c0 + e;
-            if (c < x.N && (x.ti != x.tj || r <= c)) {
-              const size_t up = static_cast<size_t>(r) * x.ld32 + c;
-              const float s = x.c0 * x.out32[up] + x.c1 * v[e] + (r == c ? x.c2 : 0.0f);
-              x.out32[up] = s;
-              if (r != c) x.out32[static_cast<size_t>(c) * x.ld32 + r] = s;
-            }
-          }
-        }
-      } else if constexpr (EPI == EPI_UPDATE) {
-        if (r < x.M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = c0 + e;
-            if (c < x.N) {
-              const size_t o = static_cast<size_t>(r) * x.ld32 + c;
-              x.out32[o] = x.decay * x.out32[o] - x.lr * x.c0 * v[e];
-            }
-          }
-        }
-      } else {
+      {
         // fp16 outputs into padded buffers (zeros outside the logical region)
         float xa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (EPI == EPI_POLAR) aux16_quad(x, r, c0, xa);
@@ -418,7 +387,7 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
       }
     }
   }
-  if constexpr (kF16) Stage<C>::flush(x, PART == 0 ? 0 : x.lo16, PART == 0 ? 0 : x.lo16T);
+  Stage<C>::flush(x, PART == 0 ? 0 : x.lo16, PART == 0 ? 0 : x.lo16T);
 }
 
 template <class C, int EPI, bool WL>
