@@ -20,10 +20,14 @@
  *   4. W <- (1 - lr wd lr/lr_peak) W - lr c_shape U,
  *      c_shape = sqrt(m/n) / (sqrt(m) + sqrt(n))  (README "How it works";
  *      AdamC decay per "Learning-rate schedule" and "Hyperparameters").
+ * With okls_config.root_period = p > 1 the roots of step 2 are recomputed
+ * only on steps 1, 1 + p, ... and kept in between.  OKLS_MODE_MUON replaces
+ * steps 1-3's whitening by the polar iteration of N (see okls_mode).
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers on the current HIP device,
- *     row-major and contiguous, at least 16-byte aligned.  A group of N
+ *     row-major and contiguous, aligned to their element size (16-byte
+ *     alignment lets the kernels use their 16-byte access paths).  A group of N
  *     same-shaped matrices is one (N, rows, cols) tensor ("Batched matrices"
  *     section: a 3-D parameter is N independent matrices that share the
  *     hyperparameters).
@@ -153,18 +157,20 @@ okls_status okls_init_state(okls_handle* h, const okls_group_tensors* tensors, v
 
 /* One optimizer step (1-based step counter t, current learning rate lr) for
  * every matrix of every group: steps 1-4 in the header comment.  G is read
- * only; W, M, S_a, S_b, P_a, P_b are updated in place.  S must be symmetric
- * on entry (only its upper triangle is read).  Asynchronous on `stream`. */
+ * only; W, M, S_a, S_b, P_a, P_b are updated in place (P only on steps that
+ * recompute the roots; Muon mode: W and M only).  S must be symmetric on
+ * entry (only its upper triangle is read).  Asynchronous on `stream`. */
 okls_status okls_step(okls_handle* h, const okls_group_tensors* tensors, int64_t t, float lr,
                       void* stream);
 
-/* Scans W, M, S and P of every group for Inf/NaN; synchronises `stream`.
- * Returns OKLS_OK or OKLS_ERR_NONFINITE. */
+/* Scans W, M, S and P of every group (Muon mode: W and M) for Inf/NaN;
+ * synchronises `stream`.  Returns OKLS_OK or OKLS_ERR_NONFINITE. */
 okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* tensors, void* stream);
 
 /* The Newton-Schulz coefficient table the handle uses: a[k], b[k] for
- * k < ns_steps (T_k = a_k I + b_k Z_k Y_k), written to caller host arrays of
- * length >= max_steps.  Returns the number of steps, or -1 on bad arguments. */
+ * k < ns_steps (T_k = a_k I + b_k Z_k Y_k; in Muon mode X <- a_k X +
+ * b_k (X X^T) X), written to caller host arrays of length >= max_steps.
+ * Returns the number of steps, or -1 on bad arguments. */
 int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_steps);
 
 /* Per-launch timing.  While enabled, okls_step records a HIP event before and
@@ -181,11 +187,14 @@ int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_s
  * flops[i] is the algorithmic floating-point work of category i summed over
  * the profiled steps: 27 GEMMs of 2 d^3 per inverse square root (54 for the
  * Shampoo fourth root), 3 m n (m + n) for the OKLS factors (m n (m + n) in
- * Shampoo mode), 2 m n (m + n) for the whitening.  bytes[i] is the
+ * Shampoo mode), 2 m n (m + n) for the whitening; in Muon mode every GEMM
+ * is in category 0, 4 K p^2 q per matrix (p, q = its smaller and larger
+ * side, K = ns_steps: a Gram and an update product per step).  bytes[i] is the
  * algorithmic memory traffic of category i over the profiled steps: every
  * job reads its source once (4 bytes per fp32 element, 2 per bf16 or fp16,
  * twice that for split hi/lo operands; the momentum jobs read M and G and
- * write M'), reads the fp32 matrix its epilogue combines with once, and
+ * write M'), reads the matrix its epilogue combines with once (4 bytes per
+ * fp32 element, 2 per fp16, 4 with low halves), and
  * writes each output once (fp16 outputs 2 bytes per element, 4 with the low
  * halves; fp32 outputs 4). */
 #define OKLS_PROFILE_CATEGORIES 5
