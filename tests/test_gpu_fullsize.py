@@ -186,7 +186,7 @@ def test_fullsize_gradient_steps(name):
 
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("name,precision", [("c2", "fp16"), ("c2", "fp32"), ("c3", "fp16"), ("c3", "fp32"),
-                                            ("c4", "fp16"), ("c5", "fp16"), ("c5", "fp32")])
+                                            ("c4", "fp16"), ("c4", "fp32"), ("c5", "fp16"), ("c5", "fp32")])
 def test_fullsize_known_spectrum(name, precision):
     """Zero gradient from factors with known eigenvalues: rows of the new
     factors and preconditioners of the sampled matrices against the closed
