@@ -825,7 +825,7 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
   const char* g = J.kind == CA_NESTEROV ? resolve(J.src2, a.ws, a.user) : nullptr;
   const bool g_bf = J.g_bf16 != 0;
   const bool vec = ((reinterpret_cast<uintptr_t>(src) & (src_bf ? 7 : 15)) == 0) && (J.src_ld & 3) == 0 &&
-                   (g == nullptr || (reinterpret_cast<uintptr_t>(g) & (g_bf ? 7 : 15)) == 0) && !J.sym_read;
+                   (g == nullptr || (reinterpret_cast<uintptr_t>(g) & (g_bf ? 7 : 15)) == 0);
   auto bf4 = [](const uint16_t* p) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
     return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
@@ -848,6 +848,21 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
   // per-element checks, every load of the thread issued before any is used
   const bool fast = vec && (tr ? (sr0 + kCastCols <= J.rows && sc0 + kCastRows <= J.cols)
                                : (dr0 + kCastRows <= J.rows && dc0 + kCastCols <= J.cols));
+  // a symmetrised read (square source, non-transposed job) also needs the
+  // mirrored region, source rows dc0.. dc0 + 255 and columns dr0 .. dr0 + 63,
+  // loaded as 16-byte quads (row dc0 + (tid >> 4) + 16 p, columns dr0 + 4 (tid & 15))
+  // and transposed through LDS once the scale is known
+  const bool sym_fast = fast && J.sym_read && !tr;
+  float xm[kPass][4];
+  if (sym_fast) {
+    const float* f32 = reinterpret_cast<const float*>(src);
+    const size_t om = static_cast<size_t>(dc0 + (threadIdx.x >> 4)) * J.src_ld + dr0 + 4 * (threadIdx.x & 15);
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(f32 + om + static_cast<size_t>(16 * p) * J.src_ld);
+      xm[p][0] = v.x; xm[p][1] = v.y; xm[p][2] = v.z; xm[p][3] = v.w;
+    }
+  }
   if (fast) {
     const size_t o0 = static_cast<size_t>(sr0 + q_row) * J.src_ld + sc0 + q_col;
     const size_t op = static_cast<size_t>(q_step) * J.src_ld;
@@ -950,6 +965,32 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
       if (J.rho_slot >= 0) a.scal[J.rho_slot] = 1.0f / sqrtf(c);
       if (J.sqrtc_slot >= 0) a.scal[J.sqrtc_slot] = sqrtf(c);
       if (J.p16_slot >= 0) a.scal[J.p16_slot] = J.p16_static * sqrtf(c);
+    }
+    if (sym_fast) {
+      // x <- (x + mirrored^T) / 2: mirrored row i (0..255), column j (0..63)
+      // at i * 64 + (j ^ ((i >> 2) & 31)), the transposed path's layout
+#pragma unroll
+      for (int p = 0; p < kPass; ++p) {
+        const int i = (threadIdx.x >> 4) + 16 * p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * (threadIdx.x & 15) + e;
+          tile[i * kCastRows + (j ^ ((i >> 2) & 31))] = xm[p][e];
+        }
+      }
+      WAIT_LGKM0();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int p = 0; p < kPass; ++p) {
+        const int j = wave + 4 * p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * lane + e;
+          x[p][e] = 0.5f * (x[p][e] + tile[i * kCastRows + (j ^ ((i >> 2) & 31))]);
+        }
+      }
     }
     half_t* dst2 = J.dst2.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(J.dst2, a.ws, a.user)) : nullptr;
     const float scale2 = dst2 != nullptr ? a.scal[J.scale_slot2] : 1.0f;

@@ -286,6 +286,19 @@ def test_step_replays_bitwise_from_a_hip_graph(mode):
                 assert torch.equal(a, b), (mode, rep)
 
 
+@pytest.mark.parametrize("precision", ["fp16", "fp32"])
+def test_shampoo_mode_midsize(precision):
+    """Factors of 300 and 520 (padded 384 and 768): the second chain's start
+    reads the computed square root symmetrised, through its coalesced path in
+    whole 64 x 256 blocks and element by element in the edge blocks."""
+    groups = [(300, 520, 1)]
+
+    def grad(gi, i, t):
+        return (1e-3 * np.random.default_rng([gi, i, t, 6]).standard_normal((300, 520))).astype(np.float32)
+
+    _run_teacher_forced(f"shampoo-mid-{precision}", groups, grad, 2, precision, mode="shampoo")
+
+
 def test_bf16_gradients_rowscaled():
     """bf16 gradients with per-row log-uniform scales (the transformer-block
     workload's distribution) at a reduced shape spanning several tiles."""
