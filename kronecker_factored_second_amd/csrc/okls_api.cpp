@@ -432,7 +432,9 @@ struct Planner {
       StatJob j{};
       j.kind = s.kind; j.src = s.src; j.src_ld = s.ld; j.src2 = s.src2; j.g_bf16 = s.g_bf16;
       j.rows = s.rows; j.cols = s.cols;
-      j.rows_per_blk = std::max(1, std::min(s.rows, 32768 / std::max(1, s.cols)));
+      // about 16K elements per block: twice the blocks the chip holds at once
+      // on the larger launches, so the scheduler balances their tails
+      j.rows_per_blk = std::max(1, std::min(s.rows, 16384 / std::max(1, s.cols)));
       // at most kMaxJobParts partials per job: every cast block of the job combines them all
       j.rows_per_blk = std::max(j.rows_per_blk, (s.rows + kMaxJobParts - 1) / kMaxJobParts);
       const double src_b = s.kind == ST_F32 ? 4.0 : s.kind == ST_BF16 ? 2.0 : 4.0 + (s.g_bf16 ? 2.0 : 4.0);
