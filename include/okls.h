@@ -70,7 +70,7 @@ typedef enum {
     OKLS_ERR_UNSUPPORTED = -7    /* a combination the library does not implement */
 } okls_status;
 
-typedef enum { OKLS_F32 = 0, OKLS_BF16 = 1 } okls_dtype;
+typedef enum { OKLS_F32 = 0, OKLS_BF16 = 1, OKLS_F16 = 2 } okls_dtype;
 
 typedef enum {
     OKLS_MODE_OKLS = 0,      /* KL factor EMAs, P = S^{-1/2} */
@@ -117,12 +117,12 @@ typedef struct {
 typedef struct {
     int32_t batch;     /* N >= 1 matrices of this shape */
     int32_t m, n;      /* rows (fan-out) and columns of each matrix, 1..32768 */
-    int32_t g_dtype;   /* okls_dtype of the gradient; W, M, S, P are fp32 */
+    int32_t g_dtype;   /* okls_dtype of the gradient (fp32, bf16 or fp16); W, M, S, P are fp32 */
 } okls_group_desc;
 
 typedef struct {
     float* W;          /* (N, m, n) weights, updated in place */
-    const void* G;     /* (N, m, n) gradient, read only, fp32 or bf16 */
+    const void* G;     /* (N, m, n) gradient, read only, fp32, bf16 or fp16 */
     float* M;          /* (N, m, n) momentum, updated in place */
     float* Sa;         /* (N, m, m) left factor, symmetric, updated in place */
     float* Sb;         /* (N, n, n) right factor */

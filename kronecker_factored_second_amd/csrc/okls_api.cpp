@@ -206,7 +206,7 @@ okls_status check_groups(int n_groups, const okls_group_desc* g) {
   if (n_groups < 1 || n_groups > kMaxGroups) return OKLS_ERR_SHAPE;
   for (int i = 0; i < n_groups; ++i) {
     if (g[i].batch < 1 || g[i].m < 1 || g[i].n < 1 || g[i].m > kMaxDim || g[i].n > kMaxDim) return OKLS_ERR_SHAPE;
-    if (g[i].g_dtype != OKLS_F32 && g[i].g_dtype != OKLS_BF16) return OKLS_ERR_DTYPE;
+    if (g[i].g_dtype != OKLS_F32 && g[i].g_dtype != OKLS_BF16 && g[i].g_dtype != OKLS_F16) return OKLS_ERR_DTYPE;
   }
   return OKLS_OK;
 }
@@ -420,7 +420,7 @@ struct Planner {
   }
 
   // ---- statistics: returns (part_begin, part_count) per job appended
-  struct StatSpec { int kind; Ref src; int ld; Ref src2; int g_bf16; int rows, cols; };
+  struct StatSpec { int kind; Ref src; int ld; Ref src2; int g_fmt; int rows, cols; };
   std::vector<std::pair<int, int>> add_stats(std::vector<LaunchRec>& L, const std::vector<StatSpec>& specs) {
     std::vector<std::pair<int, int>> parts;
     LaunchRec r;
@@ -430,14 +430,14 @@ struct Planner {
     int blk = 0, part = 0;
     for (const StatSpec& s : specs) {
       StatJob j{};
-      j.kind = s.kind; j.src = s.src; j.src_ld = s.ld; j.src2 = s.src2; j.g_bf16 = s.g_bf16;
+      j.kind = s.kind; j.src = s.src; j.src_ld = s.ld; j.src2 = s.src2; j.g_fmt = s.g_fmt;
       j.rows = s.rows; j.cols = s.cols;
       // about 16K elements per block: twice the blocks the chip holds at once
       // on the larger launches, so the scheduler balances their tails
       j.rows_per_blk = std::max(1, std::min(s.rows, 16384 / std::max(1, s.cols)));
       // at most kMaxJobParts partials per job: every cast block of the job combines them all
       j.rows_per_blk = std::max(j.rows_per_blk, (s.rows + kMaxJobParts - 1) / kMaxJobParts);
-      const double src_b = s.kind == ST_F32 ? 4.0 : s.kind == ST_BF16 ? 2.0 : 4.0 + (s.g_bf16 ? 2.0 : 4.0);
+      const double src_b = s.kind == ST_F32 ? 4.0 : s.kind == ST_H16 ? 2.0 : 4.0 + (s.g_fmt == GF_F32 ? 4.0 : 2.0);
       step_bytes[CAT_STAT] += src_b * s.rows * s.cols;
       const int nb = (s.rows + j.rows_per_blk - 1) / j.rows_per_blk;
       j.part_begin = part;
@@ -455,7 +455,7 @@ struct Planner {
   }
 
   struct CastSpec {
-    int kind; Ref src; int src_ld; Ref src2; int g_bf16; int write_m; int transpose;
+    int kind; Ref src; int src_ld; Ref src2; int g_fmt; int write_m; int transpose;
     int rows, cols, dst_rows_p, dst_cols_p; Ref dst; int dst_ld; int dst_lo;
     std::pair<int, int> parts; int scale_mode; int scale_slot;
     int cinv_slot, rho_slot, sqrtc_slot, p16_slot; int write_lo; float damp; int sym_read;
@@ -480,7 +480,7 @@ struct Planner {
     int blk = 0;
     for (const CastSpec& s : specs) {
       CastJob j{};
-      j.kind = s.kind; j.src = s.src; j.src_ld = s.src_ld; j.src2 = s.src2; j.g_bf16 = s.g_bf16;
+      j.kind = s.kind; j.src = s.src; j.src_ld = s.src_ld; j.src2 = s.src2; j.g_fmt = s.g_fmt;
       j.write_m = s.write_m; j.transpose = s.transpose; j.rows = s.rows; j.cols = s.cols;
       j.dst_rows_p = s.dst_rows_p; j.dst_cols_p = s.dst_cols_p; j.dst = s.dst; j.dst_ld = s.dst_ld;
       j.dst_lo = s.dst_lo; j.part_begin = s.parts.first; j.part_count = s.parts.second;
@@ -490,8 +490,8 @@ struct Planner {
       j.dst2 = s.dst2; j.scale_slot2 = s.scale_slot2; j.write_lo2 = s.write_lo2;
       j.dstT = s.dstT; j.dstT_ld = s.dstT_ld; j.dstT_lo = s.dstT_lo;
       j.tiles_x = (s.dst_cols_p + kCastCols - 1) / kCastCols;
-      const double src_b = s.kind == CA_BF16 ? 2.0
-                         : s.kind == CA_NESTEROV ? 4.0 + (s.g_bf16 ? 2.0 : 4.0) + (s.write_m ? 4.0 : 0.0)
+      const double src_b = s.kind == CA_H16 ? 2.0
+                         : s.kind == CA_NESTEROV ? 4.0 + (s.g_fmt == GF_F32 ? 4.0 : 2.0) + (s.write_m ? 4.0 : 0.0)
                          : 4.0;
       const double dst2_b = s.dst2.kind == REF_NONE ? 0.0 : s.write_lo2 ? 4.0 : 2.0;
       const double dstT_b = s.dstT.kind == REF_NONE ? 0.0 : s.write_lo ? 4.0 : 2.0;
@@ -640,8 +640,11 @@ struct Planner {
     const int K = cfg.ns_steps, ks = cfg.ns_split_steps;
     auto sp = [&](int k) { return k < ks ? 1 : 0; };
     auto gdt = [&](const MatBufs& mb) { return groups[mb.group].g_dtype; };
+    auto gfmt = [&](const MatBufs& mb) {
+      return gdt(mb) == OKLS_F32 ? GF_F32 : gdt(mb) == OKLS_BF16 ? GF_BF16 : GF_F16;
+    };
     auto goff = [&](const MatBufs& mb) {
-      return static_cast<size_t>(mb.index) * mb.m * mb.n * (gdt(mb) == OKLS_BF16 ? 2 : 4);
+      return static_cast<size_t>(mb.index) * mb.m * mb.n * (gdt(mb) == OKLS_F32 ? 4 : 2);
     };
     auto moff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.n * 4; };
     auto wide = [](const MatBufs& mb) { return mb.m <= mb.n; };
@@ -649,7 +652,7 @@ struct Planner {
     std::vector<StatSpec> st;
     for (const MatBufs& mb : mats)
       st.push_back(StatSpec{ST_NESTEROV, user_ref(REF_G, mb.group, goff(mb)), mb.n,
-                            user_ref(REF_M, mb.group, moff(mb)), gdt(mb) == OKLS_BF16, mb.m, mb.n});
+                            user_ref(REF_M, mb.group, moff(mb)), gfmt(mb), mb.m, mb.n});
     std::vector<std::pair<int, int>> parts = add_stats(L, st);
     // 2. N and N^T in fp16 (absmax scale), M' written
     std::vector<CastSpec> cs;
@@ -657,7 +660,7 @@ struct Planner {
       const MatBufs& mb = mats[q];
       CastSpec nn = cast_spec();
       nn.kind = CA_NESTEROV; nn.src = user_ref(REF_M, mb.group, moff(mb)); nn.src_ld = mb.n;
-      nn.src2 = user_ref(REF_G, mb.group, goff(mb)); nn.g_bf16 = gdt(mb) == OKLS_BF16; nn.write_m = 1;
+      nn.src2 = user_ref(REF_G, mb.group, goff(mb)); nn.g_fmt = gfmt(mb); nn.write_m = 1;
       nn.rows = mb.m; nn.cols = mb.n; nn.dst_rows_p = mb.mp; nn.dst_cols_p = mb.np; nn.dst = ws_ref(mb.N16);
       nn.dst_ld = mb.ldn; nn.dst_lo = mb.np; nn.parts = parts[q]; nn.scale_mode = SC_ABSMAX;
       nn.scale_slot = mb.s_n; nn.write_lo = sp(0);
@@ -781,8 +784,11 @@ struct Planner {
     const bool p_old = okls_mode || !refresh;
     const int fs = cfg.factor_split;
     auto gdt = [&](const MatBufs& mb) { return groups[mb.group].g_dtype; };
+    auto gfmt = [&](const MatBufs& mb) {
+      return gdt(mb) == OKLS_F32 ? GF_F32 : gdt(mb) == OKLS_BF16 ? GF_BF16 : GF_F16;
+    };
     auto goff = [&](const MatBufs& mb) {
-      return static_cast<size_t>(mb.index) * mb.m * mb.n * (gdt(mb) == OKLS_BF16 ? 2 : 4);
+      return static_cast<size_t>(mb.index) * mb.m * mb.n * (gdt(mb) == OKLS_F32 ? 4 : 2);
     };
     auto moff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.n * 4; };
     auto aoff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.m * 4; };
@@ -791,10 +797,10 @@ struct Planner {
     // 1. statistics of G, N and the previous preconditioners
     std::vector<StatSpec> st;
     for (const MatBufs& mb : mats) {
-      const int gk = gdt(mb) == OKLS_BF16 ? ST_BF16 : ST_F32;
-      st.push_back(StatSpec{gk, user_ref(REF_G, mb.group, goff(mb)), mb.n, no_ref(), 0, mb.m, mb.n});
+      const int gk = gdt(mb) == OKLS_F32 ? ST_F32 : ST_H16;
+      st.push_back(StatSpec{gk, user_ref(REF_G, mb.group, goff(mb)), mb.n, no_ref(), gfmt(mb), mb.m, mb.n});
       st.push_back(StatSpec{ST_NESTEROV, user_ref(REF_G, mb.group, goff(mb)), mb.n,
-                            user_ref(REF_M, mb.group, moff(mb)), gdt(mb) == OKLS_BF16, mb.m, mb.n});
+                            user_ref(REF_M, mb.group, moff(mb)), gfmt(mb), mb.m, mb.n});
       if (p_old) {
         st.push_back(StatSpec{ST_F32, user_ref(REF_PA, mb.group, aoff(mb)), mb.m, no_ref(), 0, mb.m, mb.m});
         st.push_back(StatSpec{ST_F32, user_ref(REF_PB, mb.group, boff(mb)), mb.n, no_ref(), 0, mb.n, mb.n});
@@ -806,9 +812,8 @@ struct Planner {
     const int per = p_old ? 4 : 2;
     for (size_t q = 0; q < mats.size(); ++q) {
       const MatBufs& mb = mats[q];
-      const bool bf = gdt(mb) == OKLS_BF16;
       CastSpec g = cast_spec();
-      g.kind = bf ? CA_BF16 : CA_F32; g.src = user_ref(REF_G, mb.group, goff(mb)); g.src_ld = mb.n;
+      g.kind = gdt(mb) == OKLS_F32 ? CA_F32 : CA_H16; g.g_fmt = gfmt(mb); g.src = user_ref(REF_G, mb.group, goff(mb)); g.src_ld = mb.n;
       g.rows = mb.m; g.cols = mb.n; g.dst_rows_p = mb.mp; g.dst_cols_p = mb.np; g.dst = ws_ref(mb.G16);
       g.dst_ld = mb.ldn; g.dst_lo = mb.np; g.parts = parts[per * q]; g.scale_mode = SC_ABSMAX;
       g.scale_slot = mb.s_g; g.write_lo = fs;
@@ -816,7 +821,7 @@ struct Planner {
       cs.push_back(g);
       CastSpec nn = cast_spec();
       nn.kind = CA_NESTEROV; nn.src = user_ref(REF_M, mb.group, moff(mb)); nn.src_ld = mb.n;
-      nn.src2 = user_ref(REF_G, mb.group, goff(mb)); nn.g_bf16 = bf; nn.write_m = 1;
+      nn.src2 = user_ref(REF_G, mb.group, goff(mb)); nn.g_fmt = gfmt(mb); nn.write_m = 1;
       nn.rows = mb.m; nn.cols = mb.n; nn.dst_rows_p = mb.mp; nn.dst_cols_p = mb.np; nn.dst = ws_ref(mb.N16);
       nn.dst_ld = mb.ldn; nn.dst_lo = mb.np; nn.parts = parts[per * q + 1]; nn.scale_mode = SC_ABSMAX;
       nn.scale_slot = mb.s_n; nn.write_lo = fs;
@@ -1031,7 +1036,7 @@ struct Planner {
     const size_t b = static_cast<size_t>(g.batch);
     switch (kind) {
       case REF_W: case REF_M: return b * g.m * g.n * 4;
-      case REF_G: return b * g.m * g.n * (g.g_dtype == OKLS_BF16 ? 2 : 4);
+      case REF_G: return b * g.m * g.n * (g.g_dtype == OKLS_F32 ? 4 : 2);
       case REF_SA: case REF_PA: return b * g.m * g.m * 4;
       case REF_SB: case REF_PB: return b * g.n * g.n * 4;
     }
@@ -1121,7 +1126,7 @@ struct Planner {
             const int nb = (s.rows + s.rows_per_blk - 1) / s.rows_per_blk;
             blk += nb;
             if (s.part_begin < 0 || s.part_begin + nb > max_partials) return false;
-            const size_t esz = (s.kind == ST_BF16 || (s.kind == ST_NESTEROV && s.g_bf16)) ? 2 : 4;
+            const size_t esz = (s.kind == ST_H16 || (s.kind == ST_NESTEROV && s.g_fmt != GF_F32)) ? 2 : 4;
             if (!fits(s.src, (static_cast<size_t>(s.rows - 1) * s.src_ld + s.cols) * esz)) return false;
             if (s.kind == ST_NESTEROV && !fits(s.src2, (static_cast<size_t>(s.rows - 1) * s.src_ld + s.cols) * 4))
               return false;
@@ -1140,11 +1145,11 @@ struct Planner {
             const int need_ld = c.write_lo ? c.dst_lo + c.dst_cols_p : c.dst_cols_p;
             if (c.dst_ld < need_ld || (c.write_lo && c.dst_lo < c.dst_cols_p)) return false;
             if (!fits(c.dst, static_cast<size_t>(c.dst_rows_p) * c.dst_ld * 2)) return false;
-            const size_t esz = (c.kind == CA_BF16) ? 2 : 4;
+            const size_t esz = (c.kind == CA_H16) ? 2 : 4;
             if (!fits(c.src, (static_cast<size_t>(c.rows - 1) * c.src_ld + c.cols) * esz)) return false;
             if (c.kind == CA_NESTEROV) {
               if (c.transpose) return false;
-              if (!fits(c.src2, (static_cast<size_t>(c.rows - 1) * c.src_ld + c.cols) * (c.g_bf16 ? 2 : 4))) return false;
+              if (!fits(c.src2, (static_cast<size_t>(c.rows - 1) * c.src_ld + c.cols) * (c.g_fmt == GF_F32 ? 4 : 2))) return false;
             }
             if (c.kind == CA_NS_Y0 && (c.rows != c.cols || c.transpose)) return false;
             if (c.dstT.kind != REF_NONE) {   // dst_cols_p x dst_rows_p, same lo flag
@@ -1401,7 +1406,7 @@ static okls_status check_tensors(const okls_handle* h, const okls_group_tensors*
     }
     if (need_wg) {
       if (x.W == nullptr || x.G == nullptr) return OKLS_ERR_INVALID_ARG;
-      if (!aligned(x.W, 4) || !aligned(x.G, h->groups[g].g_dtype == OKLS_BF16 ? 2 : 4)) return OKLS_ERR_INVALID_ARG;
+      if (!aligned(x.W, 4) || !aligned(x.G, h->groups[g].g_dtype == OKLS_F32 ? 4 : 2)) return OKLS_ERR_INVALID_ARG;
     }
   }
   return OKLS_OK;

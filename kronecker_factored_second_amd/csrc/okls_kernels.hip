@@ -10,7 +10,7 @@
 //                   mirrored store, the Newton-Schulz step polynomial, the
 //                   weight update).
 //  stats_kernel     per-block absmax / sum of squares partials.
-//  cast_kernel      fp32/bf16 -> padded fp16 (hi, lo) with a power-of-two
+//  cast_kernel      fp32/bf16/fp16 -> padded fp16 (hi, lo) with a power-of-two
 //                   scale derived from the partials, optional transpose; also
 //                   the Nesterov momentum update and the Newton-Schulz start.
 //  init_state_kernel, finite_kernel.
@@ -39,6 +39,33 @@ __device__ __forceinline__ char* resolve(const Ref& r, char* ws, const UserPtrs&
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// one gradient element of format fmt (GradFmt) at element offset o
+__device__ __forceinline__ float grad_elem(const void* p, size_t o, int fmt) {
+  if (fmt == GF_F32) return reinterpret_cast<const float*>(p)[o];
+  if (fmt == GF_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[o]);
+  return static_cast<float>(reinterpret_cast<const half_t*>(p)[o]);
+}
+// four consecutive gradient elements from one aligned 16-byte (fp32) or
+// 8-byte (bf16, fp16) load
+template <int FMT>
+__device__ __forceinline__ float4 grad_quad(const void* p, size_t o) {
+  if constexpr (FMT == GF_F32) {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + o);
+  } else if constexpr (FMT == GF_BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + o);
+    return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+  } else {
+    const half4_t h = *reinterpret_cast<const half4_t*>(reinterpret_cast<const half_t*>(p) + o);
+    return float4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]), static_cast<float>(h[3])};
+  }
+}
+// kPass quads at element offsets o0 + p * op, all issued before any is used
+template <int FMT, int N>
+__device__ __forceinline__ void load_quads(float4 (&v)[N], const void* p, size_t o0, size_t op) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = grad_quad<FMT>(p, o0 + k * op);
 }
 
 // ---------------------------------------------------------------------------
@@ -655,7 +682,7 @@ __device__ __forceinline__ float nesterov_value(float m, float g, float beta1, f
 // Flat statistics loop over n4 quads from element e0: four quads per thread
 // and iteration, all their loads issued before any is used (one loop per
 // source form, so no branch sits between the loads).
-template <bool BF, bool NEST>
+template <int FMT, bool NEST>
 __device__ __forceinline__ void stats_flat(const char* src, const float* m, size_t e0, size_t n4, float beta1,
                                            float s_t, float& amax, float& ss) {
   auto acc1 = [&](float x) {
@@ -663,15 +690,7 @@ __device__ __forceinline__ void stats_flat(const char* src, const float* m, size
     amax = (ax > amax || ax != ax) ? ax : amax;   // NaN propagates
     ss += x * x;
   };
-  auto ld = [&](size_t o) -> float4 {
-    if constexpr (BF) {
-      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + o);
-      return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                    __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
-    } else {
-      return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + o);
-    }
-  };
+  auto ld = [&](size_t o) -> float4 { return grad_quad<FMT>(src, o); };
   auto use = [&](const float4& g, const float4& mm) {
     if constexpr (NEST) {
       acc1(nesterov_value(mm.x, g.x, beta1, s_t));
@@ -711,7 +730,7 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
   const int r1 = min(J.rows, r0 + J.rows_per_blk);
   const char* src = resolve(J.src, a.ws, a.user);
   const float* m = J.kind == ST_NESTEROV ? reinterpret_cast<const float*>(resolve(J.src2, a.ws, a.user)) : nullptr;
-  const bool bf = J.kind == ST_BF16 || (J.kind == ST_NESTEROV && J.g_bf16);
+  const int fmt = (J.kind == ST_H16 || J.kind == ST_NESTEROV) ? J.g_fmt : static_cast<int>(GF_F32);
   float amax = 0.0f, ss = 0.0f;
   auto acc1 = [&](float x) {
     const float ax = fabsf(x);
@@ -722,30 +741,30 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
     return J.kind == ST_NESTEROV ? nesterov_value(m[o], raw, a.beta1, a.s_t) : raw;
   };
   // rows are contiguous when src_ld == cols: one flat range, 16-byte fp32 /
-  // 8-byte bf16 loads when aligned
+  // 8-byte bf16 and fp16 loads when aligned
   const size_t e0 = static_cast<size_t>(r0) * J.src_ld, e1 = static_cast<size_t>(r1) * J.src_ld;
   const bool flat = J.src_ld == J.cols && (e0 & 3) == 0 &&
-                    (reinterpret_cast<uintptr_t>(src) & (bf ? 7 : 15)) == 0 &&
+                    (reinterpret_cast<uintptr_t>(src) & (fmt == GF_F32 ? 15 : 7)) == 0 &&
                     (m == nullptr || (reinterpret_cast<uintptr_t>(m) & 15) == 0);
   if (flat) {
     const size_t n4 = (e1 - e0) / 4;
     if (m != nullptr) {
-      if (bf) stats_flat<true, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
-      else stats_flat<false, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      if (fmt == GF_BF16) stats_flat<GF_BF16, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      else if (fmt == GF_F16) stats_flat<GF_F16, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      else stats_flat<GF_F32, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
     } else {
-      if (bf) stats_flat<true, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
-      else stats_flat<false, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      if (fmt == GF_BF16) stats_flat<GF_BF16, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      else if (fmt == GF_F16) stats_flat<GF_F16, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      else stats_flat<GF_F32, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
     }
     for (size_t o = e0 + 4 * n4 + threadIdx.x; o < e1; o += kStatThreads) {
-      const float raw = bf ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]) : reinterpret_cast<const float*>(src)[o];
-      acc1(value(o, raw));
+      acc1(value(o, grad_elem(src, o, fmt)));
     }
   } else {
     for (int r = r0; r < r1; ++r) {
       for (int c = threadIdx.x; c < J.cols; c += kStatThreads) {
         const size_t o = static_cast<size_t>(r) * J.src_ld + c;
-        const float raw = bf ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]) : reinterpret_cast<const float*>(src)[o];
-        acc1(value(o, raw));
+        acc1(value(o, grad_elem(src, o, fmt)));
       }
     }
   }
@@ -770,14 +789,14 @@ __device__ __forceinline__ float pow2_scale(float amax) {
 }
 
 // One in-range source element of a cast job (the edge blocks' path).
-__device__ __noinline__ float cast_element(int kind, int ld, bool g_bf16, bool write_m, bool sym_read, const char* src,
+__device__ __noinline__ float cast_element(int kind, int ld, int g_fmt, bool write_m, bool sym_read, const char* src,
                                            const char* g, float beta1, float s_t, int r, int c) {
   const size_t o = static_cast<size_t>(r) * ld + c;
   switch (kind) {
     case CA_F32: return reinterpret_cast<const float*>(src)[o];
-    case CA_BF16: return bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[o]);
+    case CA_H16: return grad_elem(src, o, g_fmt);
     case CA_NESTEROV: {
-      const float gv = g_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(g)[o]) : reinterpret_cast<const float*>(g)[o];
+      const float gv = grad_elem(g, o, g_fmt);
       float* m = const_cast<float*>(reinterpret_cast<const float*>(src));
       const float mn = beta1 * m[o] + (1.0f - beta1) * gv;
       if (write_m) m[o] = mn;
@@ -821,16 +840,12 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
   const int q_row = tr ? (threadIdx.x >> 4) : wave;
   const int q_step = tr ? 16 : 4;
   const int sr0 = tr ? dc0 : dr0, sc0 = tr ? dr0 : dc0;
-  const bool src_bf = J.kind == CA_BF16;
+  // gradient format of the source (CA_H16) or of the second source (CA_NESTEROV)
+  const int gfmt = J.g_fmt;
+  const bool src_h = J.kind == CA_H16;
   const char* g = J.kind == CA_NESTEROV ? resolve(J.src2, a.ws, a.user) : nullptr;
-  const bool g_bf = J.g_bf16 != 0;
-  const bool vec = ((reinterpret_cast<uintptr_t>(src) & (src_bf ? 7 : 15)) == 0) && (J.src_ld & 3) == 0 &&
-                   (g == nullptr || (reinterpret_cast<uintptr_t>(g) & (g_bf ? 7 : 15)) == 0);
-  auto bf4 = [](const uint16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
-  };
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & (src_h ? 7 : 15)) == 0) && (J.src_ld & 3) == 0 &&
+                   (g == nullptr || (reinterpret_cast<uintptr_t>(g) & (gfmt == GF_F32 ? 15 : 7)) == 0);
   // the job's statistics partials (at most kMaxJobParts / kCastThreads per
   // thread, strided), loaded ahead of the data
   constexpr int kPartsPerThread = kMaxJobParts / kCastThreads;
@@ -867,27 +882,20 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
     const size_t o0 = static_cast<size_t>(sr0 + q_row) * J.src_ld + sc0 + q_col;
     const size_t op = static_cast<size_t>(q_step) * J.src_ld;
     const float* f32 = reinterpret_cast<const float*>(src);
-    if (J.kind == CA_BF16) {
+    if (src_h) {
+      float4 v[kPass];
+      if (gfmt == GF_BF16) load_quads<GF_BF16>(v, src, o0, op);
+      else load_quads<GF_F16>(v, src, o0, op);
 #pragma unroll
       for (int p = 0; p < kPass; ++p) {
-        const float4 v = bf4(reinterpret_cast<const uint16_t*>(src) + o0 + p * op);
-        x[p][0] = v.x; x[p][1] = v.y; x[p][2] = v.z; x[p][3] = v.w;
+        x[p][0] = v[p].x; x[p][1] = v[p].y; x[p][2] = v[p].z; x[p][3] = v[p].w;
       }
     } else if (J.kind == CA_NESTEROV) {
       float4 mo[kPass], gv[kPass];
-      if (g_bf) {
-#pragma unroll
-        for (int p = 0; p < kPass; ++p) {
-          mo[p] = *reinterpret_cast<const float4*>(f32 + o0 + p * op);
-          gv[p] = bf4(reinterpret_cast<const uint16_t*>(g) + o0 + p * op);
-        }
-      } else {
-#pragma unroll
-        for (int p = 0; p < kPass; ++p) {
-          mo[p] = *reinterpret_cast<const float4*>(f32 + o0 + p * op);
-          gv[p] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g) + o0 + p * op);
-        }
-      }
+      load_quads<GF_F32>(mo, src, o0, op);
+      if (gfmt == GF_BF16) load_quads<GF_BF16>(gv, g, o0, op);
+      else if (gfmt == GF_F16) load_quads<GF_F16>(gv, g, o0, op);
+      else load_quads<GF_F32>(gv, g, o0, op);
       const float b1 = a.beta1, b0 = 1.0f - a.beta1;
 #pragma unroll
       for (int p = 0; p < kPass; ++p) {
@@ -913,7 +921,7 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         x[p][e] = (r < J.rows && c + e < J.cols)
-                      ? cast_element(J.kind, J.src_ld, g_bf, J.write_m != 0, J.sym_read != 0, src, g, a.beta1, a.s_t, r, c + e)
+                      ? cast_element(J.kind, J.src_ld, gfmt, J.write_m != 0, J.sym_read != 0, src, g, a.beta1, a.s_t, r, c + e)
                       : 0.0f;
     }
   }

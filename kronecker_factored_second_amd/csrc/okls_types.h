@@ -95,9 +95,12 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // Statistics (absmax, sum of squares) per job, as per-block partials.
 // ---------------------------------------------------------------------------
+// Element format of a gradient source (g_fmt below).
+enum GradFmt : int32_t { GF_F32 = 0, GF_BF16 = 1, GF_F16 = 2 };
+
 enum StatKind : int32_t {
   ST_F32 = 0,        // plain fp32 source
-  ST_BF16 = 1,       // bf16 source
+  ST_H16 = 1,        // 16-bit gradient source, bf16 or fp16 (g_fmt)
   ST_NESTEROV = 2    // N = s*(beta1*(beta1*M + (1-beta1)*G) + (1-beta1)*G)
 };
 
@@ -105,7 +108,7 @@ struct StatJob {
   int32_t kind;
   Ref src; int32_t src_ld;
   Ref src2;                // M for ST_NESTEROV
-  int32_t g_bf16;          // ST_NESTEROV: gradient dtype
+  int32_t g_fmt;           // ST_H16 / ST_NESTEROV: the gradient's GradFmt
   int32_t rows, cols;
   int32_t rows_per_blk;
   int32_t part_begin;      // partial index of the job's first block
@@ -128,7 +131,7 @@ struct StatArgs {
 // ---------------------------------------------------------------------------
 enum CastKind : int32_t {
   CA_F32 = 0,        // x from fp32 source
-  CA_BF16 = 1,       // x from bf16 source
+  CA_H16 = 1,        // x from a 16-bit gradient source, bf16 or fp16 (g_fmt)
   CA_NESTEROV = 2,   // x = N from (G, M); the non-transposed job also writes M'
   CA_NS_Y0 = 3       // x = (S + delta c I) / c', c = sqrt(sumsq); static output scale; the
                      // second destination, if any, gets ka*I + kb*x (Z_1) in the same pass
@@ -142,7 +145,7 @@ struct CastJob {
   int32_t kind;
   Ref src; int32_t src_ld;
   Ref src2;                // G for CA_NESTEROV (src is M)
-  int32_t g_bf16;
+  int32_t g_fmt;           // CA_H16 / CA_NESTEROV: the gradient's GradFmt
   int32_t write_m;         // CA_NESTEROV: write M' (non-transposed job only)
   int32_t transpose;
   int32_t rows, cols;      // logical source dims

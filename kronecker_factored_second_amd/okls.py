@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libokls.so")
 OKLS_OK = 0
 STATUS = {0: "OKLS_OK", -1: "OKLS_ERR_INVALID_ARG", -2: "OKLS_ERR_SHAPE", -3: "OKLS_ERR_DTYPE",
           -4: "OKLS_ERR_WORKSPACE", -5: "OKLS_ERR_HIP", -6: "OKLS_ERR_NONFINITE", -7: "OKLS_ERR_UNSUPPORTED"}
-OKLS_F32, OKLS_BF16 = 0, 1
+OKLS_F32, OKLS_BF16, OKLS_F16 = 0, 1, 2
 MODE = {"okls": 0, "shampoo": 1, "muon": 2}
 # the Muon setting of the polar iteration: 5 steps (Clean, Table 6) on [1e-2, 1]
 MUON_DEFAULTS = dict(ns_steps=5, ns_floor=1e-2)
@@ -268,7 +268,10 @@ class OKLS:
             if len(shp) != 3:
                 raise ValueError("parameters must be 2-D or 3-D")
             b, m, n = shp
-            gdt = OKLS_BF16 if (grad_dtype or torch.float32) == torch.bfloat16 else OKLS_F32
+            gdt = {torch.float32: OKLS_F32, torch.bfloat16: OKLS_BF16,
+                   torch.float16: OKLS_F16}.get(grad_dtype or torch.float32)
+            if gdt is None:
+                raise ValueError("grad_dtype must be float32, bfloat16 or float16")
             self.groups.append((b, m, n, gdt))
             if mode == "muon":     # no factors or roots
                 self.state.append(dict(M=torch.zeros(b, m, n, device=dev)))

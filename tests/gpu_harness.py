@@ -24,7 +24,7 @@ def make(groups, precision="fp16", mode="okls", grad_dtype="f32", **cfg):
     from kronecker_factored_second_amd import okls
     dev = torch.device("cuda:0")
     params = [torch.zeros(b, m, n, device=dev) for (m, n, b) in groups]
-    gdt = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
+    gdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[grad_dtype]
     opt = okls.OKLS(params, mode=mode, precision=precision, grad_dtype=gdt, **cfg)
     return opt, params
 
@@ -47,7 +47,7 @@ def snapshot(opt, gi, idx):
 def to_device_grad(G: np.ndarray, dtype: str):
     torch = _torch()
     g = torch.tensor(G, device="cuda:0")
-    return g.to(torch.bfloat16) if dtype == "bf16" else g
+    return g.to({"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype])
 
 
 class Report:

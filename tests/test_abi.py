@@ -85,6 +85,8 @@ def test_workspace_size_validation():
     assert okls.workspace_size(c, [(1, 0, 256, 0)]) == 0
     assert okls.workspace_size(c, [(1, 40000, 8, 0)]) == 0        # beyond the maximum side
     assert okls.workspace_size(c, [(1, 8, 8, 7)]) == 0            # bad dtype
+    for gdt in (okls.OKLS_F32, okls.OKLS_BF16, okls.OKLS_F16):    # fp32, bf16, fp16 gradients
+        assert okls.workspace_size(c, [(1, 128, 256, gdt)]) > 0
     assert okls.workspace_size(c, [(1, 8, 8, 0)] * 17) == 0       # too many groups
     bad = okls.default_config(ns_steps=1)
     assert okls.workspace_size(bad, [(1, 8, 8, 0)]) == 0

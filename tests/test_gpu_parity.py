@@ -166,15 +166,15 @@ def _muon_snapshot(opt, gi, i):
     return O.MatState(W=f(opt.params[gi]), M=f(opt.state[gi]["M"]), Sa=None, Sb=None, Pa=None, Pb=None)
 
 
-@pytest.mark.parametrize("precision,u_tol", [("fp16", 2e-2), ("fp32", 1e-4)])
-def test_muon_mode(precision, u_tol):
+@pytest.mark.parametrize("precision,u_tol,gdt", [("fp16", 2e-2, "f32"), ("fp32", 1e-4, "f32"), ("fp16", 2e-2, "f16")])
+def test_muon_mode(precision, u_tol, gdt):
     """Muon (polar Newton-Schulz of the momentum, 5 steps) over wide, tall,
     square-ish and tiny shapes (ragged against the tiles), 4 teacher-forced
     steps: M, and the orthogonalised update read back from W (zeroed before
     each step), against the oracle's fp64 iteration."""
     torch = pytest.importorskip("torch")
     groups = [(96, 160, 2), (200, 72, 1), (33, 40, 2), (1, 7, 1)]
-    opt, params = H.make(groups, precision=precision, mode="muon")
+    opt, params = H.make(groups, precision=precision, mode="muon", grad_dtype=gdt)
     hp = H.hyper_of(opt)
     assert hp.ns_steps == 5 and abs(hp.ns_floor - 1e-2) < 1e-9
     assert all(set(st) == {"M"} for st in opt.state)          # no factors or roots are allocated
@@ -182,10 +182,12 @@ def test_muon_mode(precision, u_tol):
     for t in range(1, 5):
         host = {gi: [(0.02 * np.random.default_rng([gi, i, t, 91]).standard_normal((m, n))).astype(np.float32)
                      for i in range(b)] for gi, (m, n, b) in enumerate(groups)}
+        if gdt == "f16":         # values the fp16 gradient holds exactly
+            host = {gi: [g.astype(np.float16).astype(np.float32) for g in gs] for gi, gs in host.items()}
         for p in params:
             p.zero_()
         before = {(gi, i): _muon_snapshot(opt, gi, i) for gi, (m, n, b) in enumerate(groups) for i in range(b)}
-        opt.step(grads=[H.to_device_grad(np.stack(host[gi]), "f32") for gi in range(len(groups))])
+        opt.step(grads=[H.to_device_grad(np.stack(host[gi]), gdt) for gi in range(len(groups))])
         torch.cuda.synchronize()
         for (gi, i), bf in before.items():
             ref = O.muon_step(bf, host[gi][i].astype(np.float64), hp, t)
@@ -197,7 +199,7 @@ def test_muon_mode(precision, u_tol):
             assert e_m < 1e-6, (t, gi, i, e_m)
             assert e_u < u_tol, (t, gi, i, e_u)
             worst = max(worst, e_u)
-    print(f"[muon-{precision}] worst U {worst:.2e}", flush=True)
+    print(f"[muon-{precision}-{gdt}] worst U {worst:.2e}", flush=True)
 
 
 def test_muon_worked_example_on_gpu():
@@ -310,6 +312,21 @@ def test_bf16_gradients_rowscaled():
         return WL.round_to_bf16((0.02 * z * r0).astype(np.float32))
 
     _run_teacher_forced("bf16-rowscaled", [(m, n, 2)], grad, 3, "fp16", grad_dtype="bf16")
+
+
+@pytest.mark.parametrize("mode", ["okls", "shampoo"])
+def test_f16_gradients_rowscaled(mode):
+    """fp16 gradients (the same row-scaled distribution, rounded to fp16 on
+    the host so that both sides see identical values, fp16 subnormals
+    included) at a ragged shape spanning several tiles."""
+    m, n = 330, 270
+    r0 = np.exp(np.random.default_rng(10).uniform(math.log(0.1), math.log(10.0), size=(m, 1)))
+
+    def grad(gi, i, t):
+        z = np.random.default_rng([i, t, 16]).standard_normal((m, n))
+        return (0.02 * z * r0).astype(np.float16).astype(np.float32)
+
+    _run_teacher_forced(f"f16-rowscaled-{mode}", [(m, n, 2)], grad, 3, "fp16", mode=mode, grad_dtype="f16")
 
 
 def test_shampoo_worked_example_on_gpu():
