@@ -162,11 +162,21 @@ def cpu_baseline(w, budget_s, root_period=1, mode=None):
     the roots is timed too and the two are averaged over one period."""
     from oracle import okls_oracle as O
     from kronecker_factored_second_amd import workloads as WL
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                         for i in info if i.get("user_api") == "blas") or blas
     except Exception:
         threads = os.cpu_count()
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     mode = mode or w.mode
     hp = O.muon_hyper() if mode == "muon" else O.Hyper(root_period=root_period)
     total_s, sampled, step_s = 0.0, [], 0.0
@@ -191,6 +201,7 @@ def cpu_baseline(w, budget_s, root_period=1, mode=None):
     if step_s is None:
         return None
     return {"value": w.n_matrices / step_s, "unit": "matrices/s", "cores": threads, "kind": "oracle",
+            "host_cpu": cpu, "host_cpus_visible": os.cpu_count(), "blas": blas,
             "sample": f"one full fp64 oracle step per shape class ({', '.join(sampled)}), "
                       f"scaled by the class counts to the {w.n_matrices}-matrix workload: {step_s:.1f} s/step"}
 
@@ -260,6 +271,17 @@ def main():
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
+    # per-step latencies (an event on the caller's stream after every step):
+    # their median and maximum, beside the mean of the timed block above
+    lat_steps = min(args.steps, 3) if big else args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(lat_steps + 1)]
+    evs[0].record()
+    for i in range(lat_steps):
+        opt.step(grads=grads[(args.steps + i) % n_bufs])
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    lat = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(lat_steps))
+    lat_median = float(np.median(lat))
     # then the same steps again with a HIP event pair around every launch:
     # per-category busy times, the GEMM roofline and the HBM kernels' rates
     prof_steps = min(args.steps, 3) if big else args.steps
@@ -268,7 +290,7 @@ def main():
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record()
     for i in range(prof_steps):
-        opt.step(grads=grads[(args.steps + i) % n_bufs])
+        opt.step(grads=grads[(args.steps + lat_steps + i) % n_bufs])
     p1.record()
     torch.cuda.synchronize()
     prof = okls.profile_read(opt.handle)
@@ -308,6 +330,8 @@ def main():
                    (f", roots every {args.root_period} steps" if args.root_period > 1 else ""),
                    "matrices": w.n_matrices, "parallelism": "single GPU"},
         "step_latency_ms": ms_step,
+        "step_latency_ms_median": lat_median,
+        "step_latency_ms_max": lat[-1],
         "ms_per_step_with_launch_events": ms_step_profiled,
         "ns_chain": {"tflops": ns_tflops, "frac_fp16_peak": ns_tflops / PEAK_FP16_TFLOPS,
                      "ms_per_step": ns["busy_ms"] / max(prof["steps"], 1), "launches_per_step": ns["launches"] / max(prof["steps"], 1)},
