@@ -207,13 +207,20 @@ typedef struct {
     int64_t steps;
 } okls_profile_stats;
 
+/* okls_profile_enable returns OKLS_ERR_INVALID_ARG for a NULL handle;
+ * okls_profile_read returns OKLS_ERR_INVALID_ARG for NULL arguments and
+ * OKLS_ERR_HIP if an event query fails (the accumulated sums are then kept). */
 okls_status okls_profile_enable(okls_handle* h, int enable);
 okls_status okls_profile_read(okls_handle* h, okls_profile_stats* out);
 
-/* Frees the handle's host memory.  Does not touch device memory. */
+/* Destroys the handle's stream and events and frees its host memory; the
+ * caller's tensors and workspace are not touched.  Work already queued by
+ * okls_step still completes: each step joins the handle's stream back into
+ * the caller's stream, so once the caller's stream has passed the last step
+ * the workspace may be freed.  OKLS_ERR_INVALID_ARG for a NULL handle. */
 okls_status okls_destroy(okls_handle* h);
 
-/* Static string describing a status code. */
+/* Static string describing a status code ("unknown status" for any other value). */
 const char* okls_status_string(okls_status s);
 
 #ifdef __cplusplus

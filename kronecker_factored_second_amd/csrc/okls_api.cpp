@@ -1602,6 +1602,9 @@ okls_status okls_profile_enable(okls_handle* h, int enable) {
 
 okls_status okls_profile_read(okls_handle* h, okls_profile_stats* out) {
   if (h == nullptr || out == nullptr) return OKLS_ERR_INVALID_ARG;
+  // summed into a copy: on an event error the handle's sums and pending
+  // launches stay as they were
+  okls_profile_stats acc = h->acc;
   if (!h->pending.empty()) {
     if (hipEventSynchronize(h->events[h->pending.back().second + 1]) != hipSuccess) return OKLS_ERR_HIP;
     // intervals relative to the first event; union per category
@@ -1612,8 +1615,8 @@ okls_status okls_profile_read(okls_handle* h, okls_profile_stats* out) {
       if (hipEventElapsedTime(&t0, ref, h->events[p.second]) != hipSuccess ||
           hipEventElapsedTime(&t1, ref, h->events[p.second + 1]) != hipSuccess)
         return OKLS_ERR_HIP;
-      h->acc.ms[p.first] += t1 - t0;
-      h->acc.launches[p.first] += 1;
+      acc.ms[p.first] += t1 - t0;
+      acc.launches[p.first] += 1;
       iv[p.first].push_back({t0, t1});
     }
     for (int c = 0; c < OKLS_PROFILE_CATEGORIES; ++c) {
@@ -1629,10 +1632,10 @@ okls_status okls_profile_read(okls_handle* h, okls_profile_stats* out) {
         }
       }
       if (hi > lo) busy += hi - lo;
-      h->acc.busy_ms[c] += busy;
+      acc.busy_ms[c] += busy;
     }
   }
-  *out = h->acc;
+  *out = acc;
   h->acc = okls_profile_stats{};
   h->pending.clear();
   h->next_event = 0;
