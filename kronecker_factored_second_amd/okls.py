@@ -238,7 +238,8 @@ class OKLS:
     (N, m, n); each parameter is one group of the C ABI).  Mirrors the README's
     optimizer interface: OKLS(params, lr, beta1, beta2, eps, weight_decay),
     .step(), .zero_grad(), .state_dict().  Gradients are read from p.grad
-    (fp32 or bf16) unless `grads` is passed to step().
+    (fp32, bf16 or fp16, as grad_dtype declares; checked against the
+    parameter's shape and device) unless `grads` is passed to step().
 
     chunk_matrices = 0 runs every matrix in one chunk (the largest launches);
     with workspace_limit (bytes) set and chunk_matrices = 0, the largest
@@ -290,10 +291,30 @@ class OKLS:
         self.t = 0
         init_state(self.handle, self._tensors(grads=None), self.stream)
 
-    def _tensors(self, grads):
+    _GRAD_DTYPES = {OKLS_F32: "float32", OKLS_BF16: "bfloat16", OKLS_F16: "float16"}
+
+    def _check_grad(self, i, g):
+        """The library reads G as the dtype and shape declared at init: a
+        mismatch would misread it or read past its end, so it is refused here."""
+        b, m, n, gdt = self.groups[i]
+        p = self.params[i]
+        if g is None:
+            raise ValueError(f"parameter {i} has no gradient")
+        if g.dtype != getattr(self.torch, self._GRAD_DTYPES[gdt]):
+            raise ValueError(f"gradient {i} is {g.dtype}, the optimizer was built for {self._GRAD_DTYPES[gdt]}")
+        if tuple(g.shape) != tuple(p.shape):
+            raise ValueError(f"gradient {i} has shape {tuple(g.shape)}, parameter {tuple(p.shape)}")
+        if g.device != p.device:
+            raise ValueError(f"gradient {i} is on {g.device}, parameter on {p.device}")
+
+    def _tensors(self, grads, check=False):
+        if grads is not None and len(grads) != len(self.params):
+            raise ValueError(f"{len(grads)} gradients for {len(self.params)} parameters")
         per = []
         for i, p in enumerate(self.params):
             g = grads[i] if grads is not None else p.grad
+            if check:
+                self._check_grad(i, g)
             d = dict(self.state[i])
             d["W"] = p
             d["G"] = g.contiguous() if g is not None else None
@@ -304,22 +325,27 @@ class OKLS:
     def step(self, grads=None, lr=None):
         if lr is not None:
             self.lr = float(lr)
-        self.t += 1
         self.stream = self.torch.cuda.current_stream(self.params[0].device).cuda_stream
-        step(self.handle, self._tensors(grads), self.t, self.lr, self.stream)
+        tensors = self._tensors(grads, check=True)
+        self.t += 1
+        step(self.handle, tensors, self.t, self.lr, self.stream)
 
     def zero_grad(self):
         for p in self.params:
             p.grad = None
 
     def check_finite(self) -> bool:
-        return check_finite(self.handle, self._tensors(grads=[p for p in self.params]), self.stream)
+        # G is not read by the scan; W stands in for its pointer
+        return check_finite(self.handle, self._tensors(grads=list(self.params)), self.stream)
 
     def state_dict(self):
         return {"t": self.t, "lr": self.lr, "lr_peak": self.cfg.lr_peak,
                 "state": [{k: v.clone() for k, v in s.items()} for s in self.state]}
 
     def load_state_dict(self, sd):
+        # lr_peak is part of the handle's configuration (the AdamC correction)
+        if abs(float(sd["lr_peak"]) - float(self.cfg.lr_peak)) > 1e-6 * abs(float(self.cfg.lr_peak)):
+            raise ValueError(f"state was saved with lr_peak {sd['lr_peak']}, this optimizer has {self.cfg.lr_peak}")
         self.t = int(sd["t"])
         self.lr = float(sd["lr"])
         for dst, src in zip(self.state, sd["state"]):

@@ -409,6 +409,27 @@ def test_step_is_ordered_on_the_callers_stream():
         assert torch.equal(a, b)
 
 
+def test_step_refuses_mismatched_gradients():
+    """The wrapper refuses a gradient whose dtype, shape or presence differs
+    from what the handle was built for (the library would misread it, or read
+    past its end), before anything is launched: the step counter and the
+    state are untouched."""
+    torch = pytest.importorskip("torch")
+    opt, params = H.make([(64, 48, 2)], precision="fp16", grad_dtype="bf16")
+    good = torch.zeros(2, 64, 48, device="cuda:0", dtype=torch.bfloat16)
+    M0 = opt.state[0]["M"].clone()
+    for bad in (good.float(), good.half(), good[:1], torch.zeros(2, 48, 64, device="cuda:0", dtype=torch.bfloat16),
+                good.cpu(), None):
+        with pytest.raises(ValueError):
+            opt.step(grads=[bad])
+    with pytest.raises(ValueError):
+        opt.step(grads=[good, good])
+    assert opt.t == 0 and torch.equal(opt.state[0]["M"], M0)
+    opt.step(grads=[good])
+    torch.cuda.synchronize()
+    assert opt.t == 1
+
+
 def test_check_finite_flags_nan():
     torch = pytest.importorskip("torch")
     opt, params = H.make([(64, 64, 1)], precision="fp16")
