@@ -286,3 +286,90 @@ def test_fullsize_muon(name):
     del opt, params
     _free_gpu()
 
+
+
+# The largest side the library accepts.  One fp32 factor of this side is
+# 4 GiB, so byte offsets inside a single matrix pass 2^32 (and element offsets
+# of the split path's hi/lo rows reach 2^31 - 1).
+MAX_SIDE = 32768
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("precision,kappa", [("fp16", 1e4), ("fp32", 1e2)])
+def test_max_side_rotated_diagonal(precision, kappa):
+    """A (1, 32768, 8) matrix, zero gradient, left factor S = R diag(lam) R^T
+    where R rotates disjoint index pairs (a random perfect matching, so most
+    pairs lie thousands of rows apart) by random angles and lam is
+    log-uniform over kappa.  Every matrix of the iteration is a polynomial in
+    S and keeps its sparsity exactly (a product entry can be non-zero only
+    where the pair index sets meet), so the new factor beta2 S + eps I and the
+    preconditioner have exactly 2 d non-zeros, each pair's 2 x 2 block has the
+    closed form of the oracle's per-eigenvalue iteration over the whole
+    spectrum, and the right factor (8 x 8, eps I) its isotropic closed form."""
+    torch = pytest.importorskip("torch")
+    from kronecker_factored_second_amd import okls
+    _free_gpu()
+    d, n = MAX_SIDE, 8
+    W = torch.zeros(1, d, n, device="cuda:0")
+    opt = okls.OKLS([W], precision=precision)
+    hp = H.hyper_of(opt)
+    tol = TOL[precision]
+    coeffs, _ = O.ns_coefficients(hp.ns_floor, hp.ns_steps)
+    rng = np.random.default_rng(32768)
+    perm = rng.permutation(d)
+    partner = np.empty(d, dtype=np.int64)
+    partner[perm[0::2]] = perm[1::2]
+    partner[perm[1::2]] = perm[0::2]
+    I = np.sort(perm[0::2])
+    J = partner[I]
+    theta = rng.uniform(0.0, math.pi, size=I.size)
+    lam = np.exp(rng.uniform(-math.log(kappa), 0.0, size=(2, I.size))) * 2e-5
+
+    def blocks(f1, f2, c, s):
+        # f(S) on the pair (i, j) with eigenvectors (c, s) -> f1 and (-s, c) -> f2
+        return f1 * c * c + f2 * s * s, f1 * s * s + f2 * c * c, (f1 - f2) * c * s
+
+    # the factor's entries are stored in fp32: the reference is the exact
+    # eigendecomposition of each stored 2 x 2 block
+    a, b, o = (x.astype(np.float32) for x in blocks(lam[0], lam[1], np.cos(theta), np.sin(theta)))
+    a64, b64, o64 = (x.astype(np.float64) for x in (a, b, o))
+    phi = 0.5 * np.arctan2(2.0 * o64, a64 - b64)
+    c, s = np.cos(phi), np.sin(phi)
+    l1 = a64 * c * c + 2.0 * o64 * c * s + b64 * s * s
+    l2 = a64 * s * s - 2.0 * o64 * c * s + b64 * c * c
+    assert np.allclose(blocks(l1, l2, c, s), (a64, b64, o64), rtol=1e-12, atol=1e-22)
+    assert (np.minimum(l1, l2) > 0).all()
+    Sa = opt.state[0]["Sa"][0]
+    Sa.zero_()
+    ti, tj = torch.from_numpy(I).cuda(), torch.from_numpy(J).cuda()
+    Sa[ti, ti] = torch.from_numpy(a).cuda()
+    Sa[tj, tj] = torch.from_numpy(b).cuda()
+    Sa[ti, tj] = torch.from_numpy(o).cuda()
+    Sa[tj, ti] = torch.from_numpy(o).cuda()
+    _log(f"max-side-{precision}: factor set ({d} x {d}, {I.size} rotated pairs)")
+    t0 = time.perf_counter()
+    opt.step(grads=[torch.zeros(1, d, n, device="cuda:0")])
+    torch.cuda.synchronize()
+    _log(f"max-side-{precision}: step took {time.perf_counter() - t0:.2f} s; checking")
+    assert opt.check_finite()
+    lam1 = hp.beta2 * np.concatenate([l1, l2]) + hp.eps
+    p = O.ns_spectral(lam1, coeffs, hp.ns_damping, 2)
+    S1 = opt.state[0]["Sa"][0]
+    P1 = opt.state[0]["Pa"][0]
+    for name, M, ref in (("S_a", S1, blocks(lam1[:I.size], lam1[I.size:], c, s)),
+                         ("P_a", P1, blocks(p[:I.size], p[I.size:], c, s))):
+        # exactly the pair structure: nothing written outside it
+        assert int(torch.count_nonzero(M)) == 2 * d, name
+        got = np.concatenate([_f64(M[ti, ti]), _f64(M[tj, tj]), _f64(M[ti, tj]), _f64(M[tj, ti])])
+        want = np.concatenate([ref[0], ref[1], ref[2], ref[2]])
+        err = O.rel_frob(got, want)
+        _log(f"max-side-{precision}: {name} pair blocks rel err {err:.2e}")
+        assert err < (tol["S"] if name == "S_a" else tol["P"]), (name, err)
+    # the 8 x 8 right factor: eps I -> beta2 eps + eps, isotropic root
+    lb1 = np.full(n, hp.beta2 * hp.eps + hp.eps)
+    Pb = _f64(opt.state[0]["Pb"][0])
+    assert O.rel_frob(Pb, np.diag(O.ns_spectral(lb1, coeffs, hp.ns_damping, 2))) < tol["P"]
+    decay = 1.0 - hp.lr * hp.weight_decay * (hp.lr / hp.peak())
+    assert float(W.abs().max()) == 0.0 and decay < 1.0     # zero weights stay zero: U = 0
+    del opt, W, S1, P1, Sa
+    _free_gpu()
