@@ -43,7 +43,13 @@ Parity status of each function (what pins it in the CPU test-suite):
                                  eigen closed form, worked example through NS,
                                  damped isotropic closed form, damped root within
                                  the coefficient bound of eigh's (S + delta c I)^{-1/2}
-  whiten / update_weights ...... G=0 step gives W' = (1 - lr wd) W exactly
+  whiten / update_weights ...... G=0 step gives W' = (1 - lr wd) W exactly; R6 decay
+                                 order: both give decay W for a zero update, decay-after
+                                 from W = 0 is decay x the decay-free step; R7 plain
+                                 update: the worked example's singular values 1, 1 / 0.5
+                                 / 0.1 appear in the weight steps themselves
+  eps placement (R1) ........... zero-gradient geometric series (literal) and the
+                                 exact fixed point eps I (convex)
   okls_step / shampoo_step ..... orthogonal equivariance, transpose identity,
                                  3-D batch = per-matrix results
   Hyper.refresh (R15) .......... worked example with a refresh period: the singular
@@ -79,6 +85,9 @@ class Hyper:
     ns_floor: float = 1e-3              # R4: lower end of the design interval for sqrt(lambda / ||S||_F)
     ns_damping: float = 5e-3            # R13: nu; the iteration roots S + (nu/sqrt(d)) ||S||_F I
     root_period: int = 1                # roots refreshed on steps 1, 1 + p, 1 + 2p, ... (R15)
+    eps_convex: bool = False            # R1 alternative: OKLS factors get (1-beta2) eps I per update
+    decay_after: bool = False           # R6 alternative: decay applied after the update
+    shape_scale: bool = True            # R7 alternative (False): the plain update W - lr U, no c_shape
 
     def peak(self) -> float:
         return self.lr if self.lr_peak is None else self.lr_peak
@@ -132,14 +141,21 @@ def momentum(M: np.ndarray, G: np.ndarray, beta1: float, t: int, var_corr: bool 
 #   S_a <- beta2 S_a + (1-beta2)/n (G P_b)(G P_b)^T
 #   S_b <- beta2 S_b + (1-beta2)/m (P_a G)^T (P_a G)
 # [OKLS] "Hyperparameters": eps is added during factor initialisation and
-# updates (R1: + eps I after every update).
+# updates (R1: + eps I after every update).  R1's convex alternative keeps
+# the update a convex combination, beta2 S + (1-beta2)(X X^T / n + eps I):
+# the eps term is weighted by (1-beta2), and eps I is then its fixed point.
 # ---------------------------------------------------------------------------
-def factor_update_okls(Sa, Sb, Pa, Pb, G, beta2: float, eps: float):
+def _eps_term(eps: float, beta2: float, convex: bool) -> float:
+    return (1.0 - beta2) * eps if convex else eps
+
+
+def factor_update_okls(Sa, Sb, Pa, Pb, G, beta2: float, eps: float, eps_convex: bool = False):
     m, n = G.shape
     Xa = G @ Pb
     Xb = Pa @ G
-    Sa_new = beta2 * Sa + ((1.0 - beta2) / n) * (Xa @ Xa.T) + eps * np.eye(m)
-    Sb_new = beta2 * Sb + ((1.0 - beta2) / m) * (Xb.T @ Xb) + eps * np.eye(n)
+    e = _eps_term(eps, beta2, eps_convex)
+    Sa_new = beta2 * Sa + ((1.0 - beta2) / n) * (Xa @ Xa.T) + e * np.eye(m)
+    Sb_new = beta2 * Sb + ((1.0 - beta2) / m) * (Xb.T @ Xb) + e * np.eye(n)
     return _sym(Sa_new), _sym(Sb_new)
 
 
@@ -153,7 +169,7 @@ def factor_rows(G, Pa, Pb, K, side: str, mode: str = "okls"):
     return G[:, K].T if mode == "shampoo" else (Pa @ G[:, K]).T
 
 
-def factor_block(S_KK, X_K, beta2: float, eps: float, den: int, mode: str = "okls"):
+def factor_block(S_KK, X_K, beta2: float, eps: float, den: int, mode: str = "okls", eps_convex: bool = False):
     """Principal block S'[K, K] of a factor update from the rows K of its X:
     (X X^T)[K, K] = X[K] X[K]^T and (eps I)[K, K] = eps I, so the block needs
     nothing else.  OKLS: beta2 S + (1-beta2)/den X X^T + eps I (den = n for
@@ -161,7 +177,7 @@ def factor_block(S_KK, X_K, beta2: float, eps: float, den: int, mode: str = "okl
     k = S_KK.shape[0]
     if mode == "shampoo":
         return _sym(S_KK + X_K @ X_K.T + eps * np.eye(k))
-    return _sym(beta2 * S_KK + ((1.0 - beta2) / den) * (X_K @ X_K.T) + eps * np.eye(k))
+    return _sym(beta2 * S_KK + ((1.0 - beta2) / den) * (X_K @ X_K.T) + _eps_term(eps, beta2, eps_convex) * np.eye(k))
 
 
 # ---------------------------------------------------------------------------
@@ -327,11 +343,18 @@ def whiten(Pa, N, Pb):
     return Pa @ N @ Pb
 
 
-def update_weights(W, U, lr: float, lr_peak: float, wd: float, shape=None):
-    """shape: (m, n) of the whole matrix when W and U hold only some of its rows."""
+def update_weights(W, U, lr: float, lr_peak: float, wd: float, shape=None, decay_after: bool = False,
+                   shape_scale: bool = True):
+    """shape: (m, n) of the whole matrix when W and U hold only some of its rows.
+    R6: the decay multiplies the previous weights (decay_after: the updated
+    ones, decay (W - lr c U)).  R7's alternative (shape_scale False) is the
+    original Shampoo update, the step without the muP multiplier."""
     m, n = W.shape if shape is None else shape
     decay = 1.0 - lr * wd * (lr / lr_peak)
-    return decay * W - lr * c_shape(m, n) * U
+    c = c_shape(m, n) if shape_scale else 1.0
+    if decay_after:
+        return decay * (W - lr * c * U)
+    return decay * W - lr * c * U
 
 
 # ---------------------------------------------------------------------------
@@ -374,7 +397,7 @@ def okls_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "exact
     root='exact' uses eigh roots (the method's target); root='ns' uses the
     coupled Newton-Schulz iteration in fp64.  Both are always reported."""
     G = np.asarray(G, dtype=np.float64)
-    Sa, Sb = factor_update_okls(st.Sa, st.Sb, st.Pa, st.Pb, G, hp.beta2, hp.eps)
+    Sa, Sb = factor_update_okls(st.Sa, st.Sb, st.Pa, st.Pb, G, hp.beta2, hp.eps, hp.eps_convex)
     if not hp.refresh(t):          # R15: the previous roots are kept
         Pa, Pb = st.Pa, st.Pb
         Pa_ns, Pb_ns, ka, kb = Pa, Pb, float("nan"), float("nan")
@@ -388,7 +411,8 @@ def okls_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "exact
             Pa, Pb, ka, kb = Pa_ns, Pb_ns, cond(Sa), cond(Sb)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
     U = whiten(Pa, N, Pb)
-    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
+    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay, decay_after=hp.decay_after,
+                       shape_scale=hp.shape_scale)
     return StepResult(MatState(W, M, Sa, Sb, Pa, Pb), N, U, Pa_ns, Pb_ns, ka, kb)
 
 
@@ -411,7 +435,8 @@ def shampoo_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ex
             Pa, Pb, ka, kb = Pa_ns, Pb_ns, cond(Sa), cond(Sb)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
     U = whiten(Pa, N, Pb)
-    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
+    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay, decay_after=hp.decay_after,
+                       shape_scale=hp.shape_scale)
     return StepResult(MatState(W, M, Sa, Sb, Pa, Pb), N, U, Pa_ns, Pb_ns, ka, kb)
 
 
@@ -460,7 +485,8 @@ def muon_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ns") 
     if root == "exact":
         u, _, vt = np.linalg.svd(N, full_matrices=False)
         U = u @ vt
-    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay)
+    W = update_weights(st.W, U, hp.lr, hp.peak(), hp.weight_decay, decay_after=hp.decay_after,
+                       shape_scale=hp.shape_scale)
     return StepResult(MatState(W, M, st.Sa, st.Sb, st.Pa, st.Pb), N, U, st.Pa, st.Pb, float("nan"), float("nan"),
                       extra={"U_ns": U_ns})
 

@@ -605,3 +605,69 @@ def test_muon_step_orthogonal_equivariance():
     r = O.muon_step(st, G, hp, 1)
     rQ = O.muon_step(stQ, Qa @ G @ Qb.T, hp, 1)
     np.testing.assert_allclose(rQ.U, Qa @ r.U @ Qb.T, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Readings kept as configuration switches (R1 convex eps, R6 decay order,
+# R7 plain update).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("convex", [False, True])
+def test_eps_placement_zero_gradient_closed_form(convex):
+    """Zero gradients from S_0 = eps I: X = 0, so each update only rescales S
+    and adds the eps term.  Literal R1 (+ eps I): S_t = (beta2^t + (1 - beta2^t)
+    / (1 - beta2)) eps I, a geometric series tending to eps / (1 - beta2).
+    Convex (+ (1 - beta2) eps I): eps I is a fixed point, S_t = eps I."""
+    m, n, eps, beta2 = 5, 3, 1e-9, 0.9482
+    hp = O.Hyper(eps=eps, beta2=beta2, eps_convex=convex)
+    st = O.init_state(np.zeros((m, n)), eps)
+    for t in range(1, 41):
+        st = O.okls_step(st, np.zeros((m, n)), hp, t).state
+        want = eps if convex else eps * (beta2 ** t + (1.0 - beta2 ** t) / (1.0 - beta2))
+        np.testing.assert_allclose(st.Sa, want * np.eye(m), rtol=1e-12, atol=0)
+        np.testing.assert_allclose(st.Sb, want * np.eye(n), rtol=1e-12, atol=0)
+    blk = O.factor_block(eps * np.eye(2), np.zeros((2, 4)), beta2, eps, 4, "okls", eps_convex=convex)
+    np.testing.assert_allclose(blk, (eps if convex else (beta2 + 1.0) * eps) * np.eye(2), rtol=1e-12)
+
+
+def test_decay_after_scales_the_whole_step():
+    """R6's two orders differ only in what the decay multiplies.  With a zero
+    update both give decay * W; from W = 0 the decay-after step is exactly
+    decay times the decay-free step (the update term is decayed too), while
+    the decay-before step equals the decay-free one."""
+    rng = np.random.default_rng(61)
+    W, U = rng.standard_normal((6, 4)), rng.standard_normal((6, 4))
+    lr, peak, wd = 0.05, 0.1, 0.2
+    decay = 1.0 - lr * wd * lr / peak
+    for after in (False, True):
+        np.testing.assert_allclose(O.update_weights(W, 0 * U, lr, peak, wd, decay_after=after), decay * W, rtol=1e-15)
+    free = O.update_weights(0 * W, U, lr, peak, 0.0)
+    np.testing.assert_allclose(O.update_weights(0 * W, U, lr, peak, wd, decay_after=True), decay * free, rtol=1e-14)
+    np.testing.assert_allclose(O.update_weights(0 * W, U, lr, peak, wd, decay_after=False), free, rtol=1e-15)
+
+
+def test_plain_shampoo_update_reproduces_the_worked_example_in_the_weights():
+    """R7's alternative, the original Shampoo step: no momentum (beta1 = 0,
+    no variance correction), no decay, no c_shape.  With lr = 1, W_0 = 0 and
+    the worked example's G repeated, the step W_{t-1} - W_t is
+    L^{-1/4} G R^{-1/4} itself, so its singular values are the page's: 1, 1
+    after one accumulation, 0.5 after four and 0.1 after a hundred."""
+    g = _gold("shampoo_worked_example.json")
+    G = np.array(g["G"], dtype=np.float64)
+    hp = O.Hyper(lr=1.0, beta1=0.0, nesterov_var_corr=False, weight_decay=0.0, shape_scale=False, eps=1e-12)
+    st = O.init_state(np.zeros_like(G), hp.eps)
+    want = {1: g["singular_values_preconditioned_one_accumulation"],
+            4: g["singular_values_after_4_identical_accumulations"],
+            100: g["singular_values_after_100_identical_accumulations"]}
+    for t in range(1, 101):
+        W_prev = st.W
+        st = O.shampoo_step(st, G, hp, t).state
+        if t in want:
+            sv = np.linalg.svd(W_prev - st.W, compute_uv=False)
+            np.testing.assert_allclose(sv, want[t], atol=g["printed_precision"])
+            np.testing.assert_allclose(sv, [t ** -0.5] * 2, atol=1e-6)
+    # the default (muP) step is the same update scaled by c_shape(2, 3)
+    st0 = O.init_state(np.zeros_like(G), hp.eps)
+    plain = O.shampoo_step(st0, G, hp, 1).state.W
+    scaled = O.shampoo_step(st0, G, O.Hyper(lr=1.0, beta1=0.0, nesterov_var_corr=False, weight_decay=0.0,
+                                           eps=1e-12), 1).state.W
+    np.testing.assert_allclose(scaled, O.c_shape(2, 3) * plain, rtol=1e-12)
