@@ -112,6 +112,19 @@ typedef struct {
                                   whitening and update run every step).  1 (default) is the
                                   README's every-step refresh; the Shampoo chapter and the
                                   Clean paper describe refreshing only every few steps. */
+    /* Readings of the pages kept as switches (the defaults are the readings the
+       library takes; see the README's "Hyperparameters" and "How it works"): */
+    int32_t eps_convex;        /* 0 (default): + eps I after every factor update;
+                                  1: the OKLS update stays a convex combination,
+                                  beta2 S + (1 - beta2)(X X^T / n + eps I), so eps I is its
+                                  fixed point.  Shampoo mode: no effect (+ eps I either way) */
+    int32_t decay_after;       /* 0 (default): W <- decay W - lr c U (the decay multiplies the
+                                  previous weights); 1: W <- decay (W - lr c U) */
+    int32_t shape_scale;       /* 1 (default): c = c_shape(m, n), the README's muP multiplier;
+                                  0: c = 1, the original Shampoo update W - lr P_a N P_b
+                                  (with beta1 = 0, nesterov_var_corr = 0 and weight_decay = 0
+                                  it is W - lr S_a^{-1/4} G S_b^{-1/4}, the Shampoo chapter's
+                                  step) */
 } okls_config;
 
 typedef struct {

@@ -198,6 +198,7 @@ okls_status check_config(const okls_config* c) {
   if (!(c->ns_floor > 0.f && c->ns_floor < 1.f)) return OKLS_ERR_INVALID_ARG;
   if (!(c->ns_damping >= 0.f && c->ns_damping < 1.f)) return OKLS_ERR_INVALID_ARG;
   if (c->root_period < 1) return OKLS_ERR_INVALID_ARG;
+  if ((c->eps_convex | c->decay_after | c->shape_scale) & ~1) return OKLS_ERR_INVALID_ARG;
   return OKLS_OK;
 }
 
@@ -507,6 +508,19 @@ struct Planner {
     L.push_back(r);
   }
 
+  // eps term of every factor update: + eps I (R1), or (1 - beta2) eps I in
+  // the convex form of the OKLS update
+  float factor_eps() const {
+    return (okls_mode && cfg.eps_convex) ? static_cast<float>((1.0 - cfg.beta2) * cfg.eps) : cfg.eps;
+  }
+  // multiplier of lr U in the weight update: the muP c_shape = sqrt(m/n) /
+  // (sqrt(m) + sqrt(n)), or 1 for the plain update (shape_scale = 0)
+  float update_scale(const MatBufs& mb) const {
+    if (!cfg.shape_scale) return 1.0f;
+    const double m = mb.m, n = mb.n;
+    return static_cast<float>(std::sqrt(m / n) / (std::sqrt(m) + std::sqrt(n)));
+  }
+
   GemmProb prob() {
     GemmProb p{};
     p.A = p.B = p.out32 = p.out16 = p.out16T = p.aux = no_ref();
@@ -744,8 +758,7 @@ struct Planner {
         } else {
           u.epi = EPI_POLAR_UPDATE;
           u.out32 = user_ref(REF_W, mb.group, moff(mb)); u.ld32 = mb.n;
-          u.c0 = static_cast<float>(std::sqrt(static_cast<double>(mb.m) / mb.n) /
-                                    (std::sqrt(static_cast<double>(mb.m)) + std::sqrt(static_cast<double>(mb.n))));
+          u.c0 = update_scale(mb);
         }
         pu.push_back(u);
       }
@@ -903,7 +916,7 @@ struct Planner {
         a.sA = a.sB = okls_mode ? mb.s_xa : mb.s_g;
         a.c0 = okls_mode ? cfg.beta2 : 1.0f;
         a.c1 = okls_mode ? static_cast<float>((1.0 - cfg.beta2) / mb.n) : 1.0f;
-        a.c2 = cfg.eps;
+        a.c2 = factor_eps();
         ps.push_back(a);
         GemmProb b = prob();
         b.A = b.B = ws_ref(okls_mode ? mb.XbT16 : mb.G16T); b.lda = b.ldb = mb.ldm;
@@ -912,7 +925,7 @@ struct Planner {
         b.sA = b.sB = okls_mode ? mb.s_xb : mb.s_g;
         b.c0 = okls_mode ? cfg.beta2 : 1.0f;
         b.c1 = okls_mode ? static_cast<float>((1.0 - cfg.beta2) / mb.m) : 1.0f;
-        b.c2 = cfg.eps;
+        b.c2 = factor_eps();
         ps.push_back(b);
       }
       add_gemm(L, ps, true, fs, 0);
@@ -1013,8 +1026,7 @@ struct Planner {
         p.A = pw(mb.fa); p.lda = mb.fa.ld; p.B = ws_ref(mb.VT16); p.ldb = mb.ldm;
         p.M = mb.m; p.N = mb.n; p.Kp = mb.mp; p.Mp = mb.mp; p.Np = mb.np; p.epi = EPI_UPDATE;
         p.out32 = user_ref(REF_W, mb.group, moff(mb)); p.ld32 = mb.n; p.sA = pw_scale(mb.fa); p.sB = mb.s_vt;
-        p.c0 = static_cast<float>(std::sqrt(static_cast<double>(mb.m) / mb.n) /
-                                  (std::sqrt(static_cast<double>(mb.m)) + std::sqrt(static_cast<double>(mb.n))));
+        p.c0 = update_scale(mb);
         pu.push_back(p);
       }
       add_gemm(L, pu, false, fs, 0);
@@ -1280,6 +1292,9 @@ void okls_default_config(okls_config* c) {
   c->ns_floor = 1e-3f;
   c->ns_damping = 5e-3f;
   c->root_period = 1;
+  c->eps_convex = 0;
+  c->decay_after = 0;
+  c->shape_scale = 1;
 }
 
 size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups) {
@@ -1460,6 +1475,9 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
     s_t = 1.0 / std::sqrt(v);
   }
   const double decay = 1.0 - static_cast<double>(lr) * h->cfg.weight_decay * (static_cast<double>(lr) / h->cfg.lr_peak);
+  // the update epilogue computes decay W - lr_update c U: decay after the
+  // update, decay (W - lr c U), is the same form with lr_update = decay lr
+  const float lr_update = h->cfg.decay_after ? static_cast<float>(decay * lr) : lr;
 
   const UserPtrs user = user_ptrs(h, t);
   hipStream_t s = as_stream(stream);
@@ -1539,7 +1557,7 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.write_lo = r.write_lo;
         a.ka = r.ka;
         a.kb = r.kb;
-        a.lr = lr;
+        a.lr = lr_update;
         a.decay = static_cast<float>(decay);
         a.ws = ws;
         a.scal = scal;

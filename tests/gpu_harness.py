@@ -34,7 +34,8 @@ def hyper_of(opt, lr=None):
     return O.Hyper(lr=opt.lr if lr is None else lr, beta1=c.beta1, beta2=c.beta2, eps=c.eps,
                    weight_decay=c.weight_decay, lr_peak=c.lr_peak, nesterov_var_corr=bool(c.nesterov_var_corr),
                    ns_steps=c.ns_steps, ns_floor=float(np.float32(c.ns_floor)), ns_damping=float(np.float32(c.ns_damping)),
-                   root_period=int(c.root_period))
+                   root_period=int(c.root_period), eps_convex=bool(c.eps_convex), decay_after=bool(c.decay_after),
+                   shape_scale=bool(c.shape_scale))
 
 
 def snapshot(opt, gi, idx):
@@ -79,8 +80,12 @@ def compare_step(opt, before, after_idx, G, hp, t, mode, gi, idx):
     after = snapshot(opt, gi, idx)
     m, n = G.shape
     decay = 1.0 - hp.lr * hp.weight_decay * (hp.lr / hp.peak())
-    cs = O.c_shape(m, n)
-    U_gpu = (decay * before.W - after.W) / (hp.lr * cs)
+    cs = O.c_shape(m, n) if hp.shape_scale else 1.0
+    # U read back from the weights, inverting the update form the switches select
+    if hp.decay_after:
+        U_gpu = (before.W - after.W / decay) / (hp.lr * cs)
+    else:
+        U_gpu = (decay * before.W - after.W) / (hp.lr * cs)
     return dict(
         S_a=O.rel_frob(after.Sa, ref.state.Sa), S_b=O.rel_frob(after.Sb, ref.state.Sb),
         P_a=O.rel_frob(after.Pa, ref.Pa_ns), P_b=O.rel_frob(after.Pb, ref.Pb_ns),

@@ -88,6 +88,11 @@ def test_workspace_size_validation():
     for gdt in (okls.OKLS_F32, okls.OKLS_BF16, okls.OKLS_F16):    # fp32, bf16, fp16 gradients
         assert okls.workspace_size(c, [(1, 128, 256, gdt)]) > 0
     assert okls.workspace_size(c, [(1, 8, 8, 0)] * 17) == 0       # too many groups
+    for k in ("eps_convex", "decay_after", "shape_scale"):      # the reading switches are 0 or 1
+        assert okls.workspace_size(okls.default_config(**{k: 2}), [(1, 8, 8, 0)]) == 0
+        assert okls.workspace_size(okls.default_config(**{k: 1}), [(1, 8, 8, 0)]) > 0
+    d = okls.default_config()
+    assert (d.eps_convex, d.decay_after, d.shape_scale) == (0, 0, 1)
     bad = okls.default_config(ns_steps=1)
     assert okls.workspace_size(bad, [(1, 8, 8, 0)]) == 0
     one = okls.workspace_size(c, [(1, 1024, 1024, 1)])

@@ -409,6 +409,51 @@ def test_step_is_ordered_on_the_callers_stream():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("mode,switches", [("okls", dict(eps_convex=1, decay_after=1)), ("okls", dict(shape_scale=0)),
+                                           ("shampoo", dict(decay_after=1, shape_scale=0))])
+@pytest.mark.parametrize("precision", ["fp16", "fp32"])
+def test_reading_switches(mode, switches, precision):
+    """The readings kept as switches (R1 convex eps, R6 decay after the
+    update, R7 plain update without c_shape), teacher-forced against the
+    oracle's step with the same switches over ragged shapes."""
+    groups = [(96, 160, 2), (130, 72, 1)]
+    scale = 0.02 if mode == "okls" else 1e-3
+
+    def grad(gi, i, t):
+        m, n, _ = groups[gi]
+        return (scale * np.random.default_rng([gi, i, t, 77]).standard_normal((m, n))).astype(np.float32)
+
+    tag = "-".join(f"{k}{v}" for k, v in switches.items())
+    _run_teacher_forced(f"switches-{mode}-{tag}-{precision}", groups, grad, 3, precision, mode=mode, **switches)
+
+
+def test_plain_shampoo_worked_example_in_the_weights():
+    """The original Shampoo step through the HIP path (no momentum, decay or
+    c_shape; lr 1; split path with nu = 1e-6): the weight steps W_{t-1} - W_t
+    on the worked example's repeated G have the page's singular values 1, 1
+    after one accumulation, 0.5 after four and 0.1 after a hundred."""
+    torch = pytest.importorskip("torch")
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "shampoo_worked_example.json")))
+    G = np.array(g["G"], dtype=np.float32)
+    opt, params = H.make([(2, 3, 1)], precision="fp32", mode="shampoo", ns_damping=1e-6, beta1=0.0,
+                         nesterov_var_corr=0, weight_decay=0.0, shape_scale=0)
+    opt.lr = 1.0
+    gd = torch.tensor(G, device="cuda:0")[None]
+    want = {1: g["singular_values_preconditioned_one_accumulation"],
+            4: g["singular_values_after_4_identical_accumulations"],
+            100: g["singular_values_after_100_identical_accumulations"]}
+    for t in range(1, 101):
+        W_prev = params[0][0].double().cpu().numpy()
+        opt.step(grads=[gd])
+        if t in want:
+            torch.cuda.synchronize()
+            sv = np.linalg.svd(W_prev - params[0][0].double().cpu().numpy(), compute_uv=False)
+            print(f"[plain-shampoo] t={t} singular values {sv}", flush=True)
+            np.testing.assert_allclose(sv, want[t], atol=g["printed_precision"])
+
+
 def test_step_refuses_mismatched_gradients():
     """The wrapper refuses a gradient whose dtype, shape or presence differs
     from what the handle was built for (the library would misread it, or read
