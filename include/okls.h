@@ -125,6 +125,10 @@ typedef struct {
                                   (with beta1 = 0, nesterov_var_corr = 0 and weight_decay = 0
                                   it is W - lr S_a^{-1/4} G S_b^{-1/4}, the Shampoo chapter's
                                   step) */
+    int32_t ns_classical;      /* 0 (default): the per-step minimax table on [ns_floor, 1];
+                                  1: the classical Newton-Schulz step a = 3/2, b = -1/2 at every
+                                  step (ns_floor unused); 10 such steps converge only for
+                                  condition numbers up to about 1e2 */
 } okls_config;
 
 typedef struct {

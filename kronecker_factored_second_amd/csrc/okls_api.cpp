@@ -79,6 +79,17 @@ void ns_table(double floor, int steps, std::vector<double>& a, std::vector<doubl
   if (final_err) *final_err = err;
 }
 
+// The table a handle uses: the minimax table above, or (ns_classical) the
+// classical Newton-Schulz step T = (3 I - Z Y) / 2 at every step.
+void coeff_table(const okls_config& c, std::vector<double>& a, std::vector<double>& b) {
+  if (c.ns_classical) {
+    a.assign(c.ns_steps, 1.5);
+    b.assign(c.ns_steps, -0.5);
+    return;
+  }
+  ns_table(c.ns_floor, c.ns_steps, a, b, nullptr);
+}
+
 float pow2_for_bound(double bound) {   // largest 2^e with bound * 2^e <= 2^kScaleExp
   const int e = kScaleExp - static_cast<int>(std::ceil(std::log2(std::max(bound, 1e-30))));
   return std::ldexp(1.0f, e);
@@ -198,7 +209,7 @@ okls_status check_config(const okls_config* c) {
   if (!(c->ns_floor > 0.f && c->ns_floor < 1.f)) return OKLS_ERR_INVALID_ARG;
   if (!(c->ns_damping >= 0.f && c->ns_damping < 1.f)) return OKLS_ERR_INVALID_ARG;
   if (c->root_period < 1) return OKLS_ERR_INVALID_ARG;
-  if ((c->eps_convex | c->decay_after | c->shape_scale) & ~1) return OKLS_ERR_INVALID_ARG;
+  if ((c->eps_convex | c->decay_after | c->shape_scale | c->ns_classical) & ~1) return OKLS_ERR_INVALID_ARG;
   return OKLS_OK;
 }
 
@@ -241,7 +252,7 @@ struct Planner {
   Planner(const okls_config& c, const std::vector<okls_group_desc>& g)
       : cfg(c), groups(g), okls_mode(c.mode == OKLS_MODE_OKLS), muon_mode(c.mode == OKLS_MODE_MUON),
         lo_layout(c.factor_split != 0 || c.ns_split_steps > 0) {
-    ns_table(cfg.ns_floor, cfg.ns_steps, na, nb, nullptr);
+    coeff_table(cfg, na, nb);
     double prod = 1.0, amax = 0.0;
     for (int k = 0; k < cfg.ns_steps; ++k) {
       prod *= std::max(std::fabs(na[k]), std::fabs(na[k] + nb[k]));
@@ -1295,6 +1306,7 @@ void okls_default_config(okls_config* c) {
   c->eps_convex = 0;
   c->decay_after = 0;
   c->shape_scale = 1;
+  c->ns_classical = 0;
 }
 
 size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups) {
@@ -1309,7 +1321,7 @@ size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_grou
 int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_steps) {
   if (check_config(cfg) != OKLS_OK || a == nullptr || b == nullptr || max_steps < cfg->ns_steps) return -1;
   std::vector<double> na, nb;
-  ns_table(cfg->ns_floor, cfg->ns_steps, na, nb, nullptr);
+  coeff_table(*cfg, na, nb);
   for (int k = 0; k < cfg->ns_steps; ++k) {
     a[k] = na[k];
     b[k] = nb[k];

@@ -32,7 +32,8 @@ class Config(ctypes.Structure):
                 ("chunk_matrices", ctypes.c_int32), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("lr_peak", ctypes.c_float),
                 ("ns_floor", ctypes.c_float), ("ns_damping", ctypes.c_float), ("root_period", ctypes.c_int32),
-                ("eps_convex", ctypes.c_int32), ("decay_after", ctypes.c_int32), ("shape_scale", ctypes.c_int32)]
+                ("eps_convex", ctypes.c_int32), ("decay_after", ctypes.c_int32), ("shape_scale", ctypes.c_int32),
+                ("ns_classical", ctypes.c_int32)]
 
 
 class GroupDesc(ctypes.Structure):

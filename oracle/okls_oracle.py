@@ -88,9 +88,14 @@ class Hyper:
     eps_convex: bool = False            # R1 alternative: OKLS factors get (1-beta2) eps I per update
     decay_after: bool = False           # R6 alternative: decay applied after the update
     shape_scale: bool = True            # R7 alternative (False): the plain update W - lr U, no c_shape
+    ns_classical: bool = False          # R4 alternative: the classical step (3/2, -1/2) at every step
 
     def peak(self) -> float:
         return self.lr if self.lr_peak is None else self.lr_peak
+
+    def coeffs(self):
+        """The Newton-Schulz table of this configuration (R4 or its classical alternative)."""
+        return ns_coefficients(self.ns_floor, self.ns_steps, self.ns_classical)[0]
 
     def refresh(self, t: int) -> bool:
         """R15: whether step t (1-based) recomputes the roots.  [OKLS] intro
@@ -241,8 +246,13 @@ def _minimax_cubic(lo: float, hi: float):
     return a, b, err
 
 
-def ns_coefficients(floor: float = 1e-3, steps: int = 10):
-    """List of (a_k, b_k) for k = 0..steps-1 and the final interval half-width."""
+def ns_coefficients(floor: float = 1e-3, steps: int = 10, classical: bool = False):
+    """List of (a_k, b_k) for k = 0..steps-1 and the final interval half-width.
+    classical: the textbook Newton-Schulz step T = (3 I - Z Y) / 2, i.e.
+    sigma -> sigma (3 - sigma^2) / 2, at every step (R4's plainest
+    alternative); no interval is designed, so the half-width is None."""
+    if classical:
+        return [(1.5, -0.5)] * steps, None
     lo, hi = floor, 1.0
     coeffs = []
     err = 0.0
@@ -402,7 +412,7 @@ def okls_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "exact
         Pa, Pb = st.Pa, st.Pb
         Pa_ns, Pb_ns, ka, kb = Pa, Pb, float("nan"), float("nan")
     else:
-        coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+        coeffs = hp.coeffs()
         Pa_ns, _ = ns_inv_sqrt(Sa, coeffs, hp.ns_damping)
         Pb_ns, _ = ns_inv_sqrt(Sb, coeffs, hp.ns_damping)
         if root == "exact":
@@ -426,7 +436,7 @@ def shampoo_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ex
         Pa, Pb = st.Pa, st.Pb
         Pa_ns, Pb_ns, ka, kb = Pa, Pb, float("nan"), float("nan")
     else:
-        coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+        coeffs = hp.coeffs()
         Pa_ns = ns_inv_quarter(Sa, coeffs, hp.ns_damping)
         Pb_ns = ns_inv_quarter(Sb, coeffs, hp.ns_damping)
         if root == "exact":
@@ -479,7 +489,7 @@ def muon_step(st: MatState, G: np.ndarray, hp: Hyper, t: int, root: str = "ns") 
     the iteration's is in extra["U_ns"]."""
     G = np.asarray(G, dtype=np.float64)
     M, N = momentum(st.M, G, hp.beta1, t, hp.nesterov_var_corr)
-    coeffs, _ = ns_coefficients(hp.ns_floor, hp.ns_steps)
+    coeffs = hp.coeffs()
     U_ns = ns_polar(N, coeffs)
     U = U_ns
     if root == "exact":

@@ -35,7 +35,7 @@ def hyper_of(opt, lr=None):
                    weight_decay=c.weight_decay, lr_peak=c.lr_peak, nesterov_var_corr=bool(c.nesterov_var_corr),
                    ns_steps=c.ns_steps, ns_floor=float(np.float32(c.ns_floor)), ns_damping=float(np.float32(c.ns_damping)),
                    root_period=int(c.root_period), eps_convex=bool(c.eps_convex), decay_after=bool(c.decay_after),
-                   shape_scale=bool(c.shape_scale))
+                   shape_scale=bool(c.shape_scale), ns_classical=bool(c.ns_classical))
 
 
 def snapshot(opt, gi, idx):

@@ -671,3 +671,23 @@ def test_plain_shampoo_update_reproduces_the_worked_example_in_the_weights():
     scaled = O.shampoo_step(st0, G, O.Hyper(lr=1.0, beta1=0.0, nesterov_var_corr=False, weight_decay=0.0,
                                            eps=1e-12), 1).state.W
     np.testing.assert_allclose(scaled, O.c_shape(2, 3) * plain, rtol=1e-12)
+
+
+def test_classical_coefficients_converge_to_the_exact_root():
+    """R4's classical alternative, T = (3 I - Z Y) / 2 at every step: sigma = 1
+    is its fixed point, and on a well-conditioned factor (kappa 10, spectrum
+    in (0, 1] after the Frobenius scaling) the coupled iteration converges
+    quadratically to the exact eigh inverse square root."""
+    coeffs, err = O.ns_coefficients(1e-3, 25, classical=True)
+    assert err is None and coeffs == [(1.5, -0.5)] * 25
+    assert 1.0 * (1.5 - 0.5 * 1.0) == 1.0
+    rng = np.random.default_rng(71)
+    Q, _ = np.linalg.qr(rng.standard_normal((12, 12)))
+    S = (Q * np.linspace(0.1, 1.0, 12)) @ Q.T
+    P, _ = O.ns_inv_sqrt(S, coeffs, 0.0)
+    exact, _ = O.inv_root_exact(S, 2)
+    assert O.rel_frob(P, exact) < 1e-12
+    # and the per-eigenvalue closed form follows the same table
+    np.testing.assert_allclose(O.ns_eigen_closed_form(S, coeffs, 2, 0.0), P, rtol=1e-10, atol=1e-12)
+    hp = O.Hyper(ns_classical=True, ns_steps=7)
+    assert hp.coeffs() == [(1.5, -0.5)] * 7
