@@ -411,7 +411,7 @@ def test_step_is_ordered_on_the_callers_stream():
 
 @pytest.mark.parametrize("mode,switches", [("okls", dict(eps_convex=1, decay_after=1)), ("okls", dict(shape_scale=0)),
                                            ("shampoo", dict(decay_after=1, shape_scale=0)),
-                                           ("okls", dict(ns_classical=1, ns_steps=16)), ("shampoo", dict(ns_classical=1))])
+                                           ("okls", dict(ns_classical=1)), ("shampoo", dict(ns_classical=1))])
 @pytest.mark.parametrize("precision", ["fp16", "fp32"])
 def test_reading_switches(mode, switches, precision):
     """The readings kept as switches (R1 convex eps, R6 decay after the
