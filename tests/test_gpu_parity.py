@@ -227,19 +227,24 @@ def test_muon_worked_example_on_gpu():
     assert np.all(np.abs(sv - 1.0) < 0.03)
 
 
-@pytest.mark.parametrize("mode", ["okls", "shampoo", "muon"])
-def test_chunked_steps_are_bitwise_unchunked(mode):
+@pytest.mark.parametrize("mode,gdt,period,precision", [("okls", "f32", 1, "fp16"), ("shampoo", "f32", 1, "fp16"),
+                                                       ("muon", "f32", 1, "fp16"), ("okls", "bf16", 2, "fp16"),
+                                                       ("shampoo", "f16", 2, "fp32"), ("muon", "f16", 1, "fp32")])
+def test_chunked_steps_are_bitwise_unchunked(mode, gdt, period, precision):
     """chunk_matrices = 1 and 2 (one launch list per chunk, workspace reused)
     give bit-identical states to one chunk: every output element is computed
-    by the same kernels in the same order whichever problems share a launch."""
+    by the same kernels in the same order whichever problems share a launch.
+    Also with a root period (three steps: refresh, keep, refresh), 16-bit
+    gradients and the split path."""
     torch = pytest.importorskip("torch")
     groups = [(96, 160, 2), (130, 72, 1), (33, 40, 2)]
     runs = []
     for chunk in (0, 1, 2):
-        opt, params = H.make(groups, precision="fp16", mode=mode, chunk_matrices=chunk)
-        for t in (1, 2):
+        opt, params = H.make(groups, precision=precision, mode=mode, grad_dtype=gdt, chunk_matrices=chunk,
+                             root_period=period)
+        for t in (1, 2, 3):
             grads = [H.to_device_grad((0.02 * np.random.default_rng([gi, t, 17]).standard_normal((b, m, n)))
-                                      .astype(np.float32), "f32") for gi, (m, n, b) in enumerate(groups)]
+                                      .astype(np.float32), gdt) for gi, (m, n, b) in enumerate(groups)]
             opt.step(grads=grads)
         torch.cuda.synchronize()
         runs.append([{k: v.cpu().numpy().copy() for k, v in st.items()} | {"W": params[gi].cpu().numpy().copy()}
@@ -248,7 +253,7 @@ def test_chunked_steps_are_bitwise_unchunked(mode):
     for other in runs[1:]:
         for a, b in zip(runs[0], other):
             for k in a:
-                assert np.array_equal(a[k], b[k]), (mode, k)
+                assert np.array_equal(a[k], b[k]), (mode, gdt, period, precision, k)
 
 
 @pytest.mark.parametrize("mode", ["okls", "muon"])
