@@ -406,8 +406,8 @@ struct Planner {
     // the large tile when every problem's padded sides are multiples of it and
     // the launch has enough blocks of it: 64 for the fp16-output kinds
     // (measured faster than the 128 tile from a quarter of a block per CU on
-    // up), 512 for the fp32-output kinds (factor and whitening products,
-    // whose read-modify-write epilogues favour the 128 tile's second block
+    // up), 512 for the other fp32-output kinds (the factor update and the
+    // whitening products, whose epilogues favour the 128 tile's second block
     // per CU below two blocks per CU); otherwise the 128 tile
     r.tile = kBigTile;
     long big_tiles = 0;
@@ -420,7 +420,10 @@ struct Planner {
                          r.epi == EPI_POLAR;
     // a Muon launch has no concurrent chain to fill a partly idle round: the
     // 256 tile only from one full round of it
-    if (big_tiles < (f16_out ? (muon_mode ? 256 : 64) : 512)) r.tile = kTile;
+    // the cross-preconditioning products X = G P (fp32 stores, no
+    // read-modify-write) take it from 64 like the fp16 kinds
+    const bool x_product = r.epi == EPI_STORE32 && gemm_cat == CAT_FACTOR;
+    if (big_tiles < ((f16_out || x_product) ? (muon_mode ? 256 : 64) : 512)) r.tile = kTile;
     const std::pair<int, int> t = tiles_for(ps, upper, r.tile);
     r.first = t.first;
     r.count = t.second;
