@@ -461,6 +461,44 @@ def test_plain_shampoo_worked_example_in_the_weights():
             np.testing.assert_allclose(sv, want[t], atol=g["printed_precision"])
 
 
+def test_step_argument_errors_launch_nothing():
+    """okls_step's host checks through the C ABI on a live handle: t < 1, a
+    non-finite or negative lr, missing tensors, a null or misaligned G each
+    return OKLS_ERR_INVALID_ARG before any launch (the state stays
+    bit-identical), and a valid step still runs afterwards."""
+    import ctypes
+    torch = pytest.importorskip("torch")
+    from kronecker_factored_second_amd import okls
+    opt, params = H.make([(64, 48, 1)], precision="fp16")
+    lib = okls.load()
+    g = torch.zeros(1, 64, 48, device="cuda:0")
+    before = {k: v.clone() for k, v in opt.state[0].items()} | {"W": params[0].clone()}
+    good = opt._tensors([g])
+    s = ctypes.c_void_p(opt.stream)
+    assert lib.okls_step(opt.handle, good, 0, ctypes.c_float(0.1), s) == -1
+    assert lib.okls_step(opt.handle, good, 1, ctypes.c_float(float("nan")), s) == -1
+    assert lib.okls_step(opt.handle, good, 1, ctypes.c_float(-0.1), s) == -1
+    assert lib.okls_step(opt.handle, None, 1, ctypes.c_float(0.1), s) == -1
+    no_g = opt._tensors([g])
+    no_g[0].G = None
+    assert lib.okls_step(opt.handle, no_g, 1, ctypes.c_float(0.1), s) == -1
+    odd = opt._tensors([g])
+    odd[0].G = g.data_ptr() + 2                   # fp32 G must be 4-byte aligned
+    assert lib.okls_step(opt.handle, odd, 1, ctypes.c_float(0.1), s) == -1
+    no_s = opt._tensors([g])
+    no_s[0].Sa = None
+    assert lib.okls_step(opt.handle, no_s, 1, ctypes.c_float(0.1), s) == -1
+    assert lib.okls_check_finite(opt.handle, None, s) == -1
+    assert lib.okls_profile_read(opt.handle, None) == -1
+    torch.cuda.synchronize()
+    after = {k: v for k, v in opt.state[0].items()} | {"W": params[0]}
+    for k in before:
+        assert torch.equal(before[k], after[k]), k
+    assert lib.okls_step(opt.handle, good, 1, ctypes.c_float(0.1), s) == 0
+    torch.cuda.synchronize()
+    assert not torch.equal(before["Pa"], opt.state[0]["Pa"])
+
+
 def test_step_refuses_mismatched_gradients():
     """The wrapper refuses a gradient whose dtype, shape or presence differs
     from what the handle was built for (the library would misread it, or read
