@@ -154,6 +154,11 @@ def measured_traffic():
     return None
 
 
+def progress(msg):
+    """One line per finished phase on stderr (stdout carries only the JSON line)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(w, budget_s, root_period=1, mode=None):
     """The fp64 oracle, as it stands, on a bounded sample: one matrix of each
     distinct shape class of the workload, a full oracle step each (exact eigh
@@ -247,6 +252,7 @@ def main():
                 g = torch.from_numpy(np.stack([WL.gradient(w, gi, i, t) for i in range(b)])).to(dev)
             gs.append(g.to(torch.bfloat16) if bf16 else g)
         grads.append(gs)
+    progress(f"{w.name}: inputs ready ({len(grads)} gradient set(s))")
     limit = None
     if big:   # leave room for the caller's tensors: the workspace takes what the card has left
         limit = torch.cuda.mem_get_info(0)[0] - sum(b * (m * n + 2 * m * m + 2 * n * n) * 4 for m, n, b in w.groups) \
@@ -254,9 +260,11 @@ def main():
     opt = okls.OKLS(params, mode=mode, precision=args.precision,
                     grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit,
                     root_period=args.root_period)
+    progress(f"{w.name}: optimizer ready (workspace {opt.workspace.numel() / 2**30:.1f} GiB)")
     for i in range(args.warmup):
         opt.step(grads=grads[i % n_bufs])
     torch.cuda.synchronize()
+    progress(f"{w.name}: {args.warmup} warm-up step(s) done")
 
     # the timed steps run as a user runs them: the library's per-launch
     # profiling events are off
@@ -271,6 +279,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
+    progress(f"{w.name}: {args.steps} timed step(s), {ms_step:.2f} ms/step")
     # per-step latencies (an event on the caller's stream after every step):
     # their median and maximum, beside the mean of the timed block above
     lat_steps = min(args.steps, 3) if big else args.steps
@@ -282,6 +291,7 @@ def main():
     torch.cuda.synchronize()
     lat = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(lat_steps))
     lat_median = float(np.median(lat))
+    progress(f"{w.name}: per-step latency pass done")
     # then the same steps again with a HIP event pair around every launch:
     # per-category busy times, the GEMM roofline and the HBM kernels' rates
     prof_steps = min(args.steps, 3) if big else args.steps
@@ -294,6 +304,7 @@ def main():
     p1.record()
     torch.cuda.synchronize()
     prof = okls.profile_read(opt.handle)
+    progress(f"{w.name}: instrumented pass done")
     okls.profile_enable(opt.handle, False)
     ms_step_profiled = p0.elapsed_time(p1) / prof_steps
     finite = opt.check_finite()
