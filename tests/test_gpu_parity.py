@@ -461,6 +461,24 @@ def test_plain_shampoo_worked_example_in_the_weights():
             np.testing.assert_allclose(sv, want[t], atol=g["printed_precision"])
 
 
+def test_maximum_group_count():
+    """Sixteen groups, the most one handle takes, of distinct ragged shapes
+    (tall, wide, square, vectors; batches 1 and 2) in one step: the
+    per-group pointer table at capacity, teacher-forced for two steps."""
+    rng = np.random.default_rng(1616)
+    groups = []
+    while len(groups) < 16:
+        m, n = (int(x) for x in rng.integers(1, 200, size=2))
+        if all((m, n) != (a, b) for a, b, _ in groups):
+            groups.append((m, n, int(rng.integers(1, 3))))
+
+    def grad(gi, i, t):
+        m, n, _ = groups[gi]
+        return (0.02 * np.random.default_rng([gi, i, t, 161]).standard_normal((m, n))).astype(np.float32)
+
+    _run_teacher_forced("sixteen-groups", groups, grad, 2, "fp16")
+
+
 def test_step_argument_errors_launch_nothing():
     """okls_step's host checks through the C ABI on a live handle: t < 1, a
     non-finite or negative lr, missing tensors, a null or misaligned G each
