@@ -479,6 +479,19 @@ def test_maximum_group_count():
     _run_teacher_forced("sixteen-groups", groups, grad, 2, "fp16")
 
 
+def test_many_small_matrices():
+    """Thousands of small matrices in one step (2048 of 8 x 8 and 1024 of
+    12 x 20): thousands of statistics, cast and GEMM problems per launch,
+    each padded to one 128 tile; every matrix teacher-forced for two steps."""
+    groups = [(8, 8, 2048), (12, 20, 1024)]
+
+    def grad(gi, i, t):
+        m, n, _ = groups[gi]
+        return (0.02 * np.random.default_rng([gi, i, t, 2048]).standard_normal((m, n))).astype(np.float32)
+
+    _run_teacher_forced("many-small", groups, grad, 2, "fp16")
+
+
 def test_step_argument_errors_launch_nothing():
     """okls_step's host checks through the C ABI on a live handle: t < 1, a
     non-finite or negative lr, missing tensors, a null or misaligned G each
