@@ -492,6 +492,49 @@ def test_many_small_matrices():
     _run_teacher_forced("many-small", groups, grad, 2, "fp16")
 
 
+@pytest.mark.parametrize("mode,period", [("okls", 2), ("shampoo", 1), ("muon", 1)])
+def test_checkpoint_resume_is_bitwise(tmp_path, mode, period):
+    """state_dict() after two steps, saved with torch.save and read back with
+    weights_only=True into a fresh optimizer (new handle and workspace), then
+    two more steps: bit-identical to four uninterrupted steps.  With a root
+    period of 2 the first step after the resume keeps the roots, so the
+    library carries nothing between steps beyond the caller's state and t."""
+    torch = pytest.importorskip("torch")
+    groups = [(96, 160, 2), (33, 40, 1)]
+
+    def grads(t):
+        return [H.to_device_grad((0.02 * np.random.default_rng([gi, t, 29]).standard_normal((b, m, n)))
+                                 .astype(np.float32), "f32") for gi, (m, n, b) in enumerate(groups)]
+
+    def fresh():
+        opt, params = H.make(groups, precision="fp16", mode=mode, root_period=period)
+        for gi, p in enumerate(params):
+            p.copy_(0.01 * torch.ones_like(p) * (gi + 1))
+        return opt, params
+
+    ref, ref_p = fresh()
+    for t in range(1, 5):
+        ref.step(grads=grads(t))
+    a, a_p = fresh()
+    for t in (1, 2):
+        a.step(grads=grads(t))
+    torch.save({"opt": a.state_dict(), "params": [p.detach().clone() for p in a_p]}, tmp_path / "ckpt.pt")
+    del a, a_p
+    ck = torch.load(tmp_path / "ckpt.pt", weights_only=True)
+    b, b_p = fresh()
+    b.load_state_dict(ck["opt"])
+    for p, q in zip(b_p, ck["params"]):
+        p.copy_(q)
+    assert b.t == 2
+    for t in (3, 4):
+        b.step(grads=grads(t))
+    torch.cuda.synchronize()
+    for gi in range(len(groups)):
+        assert torch.equal(ref_p[gi], b_p[gi]), (mode, gi, "W")
+        for k in ref.state[gi]:
+            assert torch.equal(ref.state[gi][k], b.state[gi][k]), (mode, gi, k)
+
+
 def test_step_argument_errors_launch_nothing():
     """okls_step's host checks through the C ABI on a live handle: t < 1, a
     non-finite or negative lr, missing tensors, a null or misaligned G each
