@@ -594,6 +594,42 @@ def test_step_refuses_mismatched_gradients():
     assert opt.t == 1
 
 
+def test_only_the_upper_triangle_of_s_is_read():
+    """S must be symmetric on entry and only its upper triangle is read: a
+    factor whose lower triangle holds junk gives bit-identically the step of
+    the factor with the upper triangle mirrored (both modes)."""
+    torch = pytest.importorskip("torch")
+    for mode in ("okls", "shampoo"):
+        outs = []
+        for junk in (False, True):
+            opt, params = H.make([(96, 160, 1)], precision="fp16", mode=mode)
+            rng = np.random.default_rng(5)
+            A = rng.standard_normal((96, 96))
+            S = 1e-4 * (A @ A.T / 96 + np.eye(96))
+            if junk:
+                S = np.triu(S) + np.tril(np.random.default_rng(6).standard_normal((96, 96)), -1)
+            opt.state[0]["Sa"][0].copy_(torch.tensor(S, dtype=torch.float32))
+            G = 0.02 * np.random.default_rng(7).standard_normal((1, 96, 160))
+            g = torch.tensor(G.astype(np.float32), device="cuda:0")
+            opt.step(grads=[g])
+            torch.cuda.synchronize()
+            outs.append({k: v.clone() for k, v in opt.state[0].items()} | {"W": params[0].clone()})
+        for k in outs[0]:
+            assert torch.equal(outs[0][k], outs[1][k]), (mode, k)
+
+
+def test_nan_gradient_is_detected():
+    """A NaN in the gradient reaches the momentum and the update, and
+    okls_check_finite reports it (OKLS_ERR_NONFINITE through the binding)."""
+    torch = pytest.importorskip("torch")
+    opt, params = H.make([(64, 48, 1)], precision="fp16")
+    g = torch.zeros(1, 64, 48, device="cuda:0")
+    g[0, 5, 7] = float("nan")
+    opt.step(grads=[g])
+    assert not opt.check_finite()
+    assert torch.isnan(opt.state[0]["M"][0, 5, 7])
+
+
 def test_check_finite_flags_nan():
     torch = pytest.importorskip("torch")
     opt, params = H.make([(64, 64, 1)], precision="fp16")
