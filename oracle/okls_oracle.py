@@ -35,7 +35,9 @@ Parity status of each function (what pins it in the CPU test-suite):
   inv_root_exact ............... P S P = I, 2x2 closed form, scipy sqrtm on 3x3,
                                  worked example and problem 14 singular values
   ns_coefficients .............. classical Newton-Schulz limit (3/2, -1/2),
-                                 equioscillation, grid-search optimality
+                                 equioscillation, grid-search optimality; the
+                                 classical table (R4 alternative) converges
+                                 quadratically to the eigh root
   ns_spectral / closed form .... matrix iterations (damped, p = 2 and 4) on random SPD
                                  factors; output within the coefficient bound of
                                  (lambda + delta c)^{-1/2} on the design interval
