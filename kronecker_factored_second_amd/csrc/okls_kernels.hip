@@ -248,8 +248,26 @@ __device__ __forceinline__ void epilogue_f32(const floatx16 (&acc)[C::GI][C::GJ]
     asm volatile("" ::: "memory");
     const int rb = x.tr0 + h * S32::HR;           // global row of local row 0
     constexpr int RPI = 64 / S32::CH;             // rows per instruction
+    constexpr int NIT = S32::HR / RPI;
+    // read-modify-write kinds: the half's old values (S or W) are all
+    // loaded before its first store.  Every quad is read and written by one
+    // lane only, and the mirror writes land below the diagonal, which the row
+    // pass never reads, so this is the same data; the loads no longer wait
+    // one by one behind stores the compiler cannot tell apart from them.
+    // (Loading the polar aux ahead too measured slower: its registers spill.)
+    constexpr bool kRmw = EPI == EPI_SYRK || EPI == EPI_UPDATE || EPI == EPI_POLAR_UPDATE;
+    floatx4 old[kRmw ? NIT : 1];
+    if constexpr (kRmw) {
 #pragma unroll
-    for (int it = 0; it < S32::HR / RPI; ++it) {
+      for (int it = 0; it < NIT; ++it) {
+        const int r = rb + it * RPI + lane / S32::CH, c = x.tc0 + 4 * (lane % S32::CH);
+        old[it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (r < x.M && vec_ok && c + 3 < x.N)
+          old[it] = *reinterpret_cast<const floatx4*>(x.out32 + static_cast<size_t>(r) * x.ld32 + c);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
       const int rl = it * RPI + lane / S32::CH, k = lane % S32::CH;
       const int r = rb + rl, c = x.tc0 + 4 * k;
       floatx4 v = *reinterpret_cast<const floatx4*>(lds + S32::off(rl, 4 * k));
@@ -271,26 +289,32 @@ __device__ __forceinline__ void epilogue_f32(const floatx16 (&acc)[C::GI][C::GJ]
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = x.cval * (x.ka * xa[e] + x.kb * v[e]);
           }
+          // one fixed rounding, W' = fma(decay, W, -(lr c) v), in both branches
+          const float step = x.lr * x.c0;
           if (full) {
-            const floatx4 w = *reinterpret_cast<const floatx4*>(row + c);
-            *reinterpret_cast<floatx4*>(row + c) = x.decay * w - (x.lr * x.c0) * v;
+            const floatx4 w = old[it];
+            floatx4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(x.decay, w[e], -step * v[e]);
+            *reinterpret_cast<floatx4*>(row + c) = o;
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (c + e < x.N) row[c + e] = x.decay * row[c + e] - x.lr * x.c0 * v[e];
+              if (c + e < x.N) row[c + e] = __builtin_fmaf(x.decay, row[c + e], -step * v[e]);
           }
         } else {  // EPI_SYRK: S <- c0*S + c1*v + c2*I on the upper triangle
           const bool diag_tile = x.ti == x.tj;
+          // one fixed rounding, S' = fma(c0, S, c1 v) (+ eps on the diagonal), in both branches
           if (full && (!diag_tile || r <= c)) {
-            const floatx4 o = *reinterpret_cast<const floatx4*>(row + c);
+            const floatx4 o = old[it];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = x.c0 * o[e] + x.c1 * v[e] + (r == c + e ? x.c2 : 0.0f);
+            for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(x.c0, o[e], x.c1 * v[e]) + (r == c + e ? x.c2 : 0.0f);
             *reinterpret_cast<floatx4*>(row + c) = v;
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if (c + e < x.N && (!diag_tile || r <= c + e)) {
-                v[e] = x.c0 * row[c + e] + x.c1 * v[e] + (r == c + e ? x.c2 : 0.0f);
+                v[e] = __builtin_fmaf(x.c0, row[c + e], x.c1 * v[e]) + (r == c + e ? x.c2 : 0.0f);
                 row[c + e] = v[e];
               }
             }
