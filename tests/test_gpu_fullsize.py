@@ -5,7 +5,8 @@ oracle on sampled outputs.
 
 Two checks per workload:
 
-* gradient steps (t = 1, 2, teacher-forced from the GPU's own state): the
+* gradient steps (the workload's schedule, every checked step teacher-forced
+  from the GPU's own state; c2 runs 100 steps): the
   momentum of every sampled matrix in full; principal blocks of both factors
   (rows of X = G P or P G, oracle.factor_block); the preconditioners in full
   wherever the factor dimension allows an fp64 eigendecomposition (damped
@@ -124,6 +125,10 @@ def _rows(rng, d, k=N_ROWS):
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
 def test_fullsize_gradient_steps(name):
+    """The workload's own schedule: max(parity_steps) steps of its gradient
+    recipe (c2: 100 steps, checked at t = 1, 2, 5, 10, 25, 50, 100; c3: 10,
+    at 1, 2, 10; c4 and c5: 5, at 1, 2, 5), each checked step teacher-forced
+    from the GPU's own state."""
     torch = pytest.importorskip("torch")
     _free_gpu()
     w, opt, params = _build(name, "fp16")
@@ -133,9 +138,14 @@ def test_fullsize_gradient_steps(name):
     coeffs, _ = O.ns_coefficients(hp.ns_floor, hp.ns_steps)
     rep = H.Report(f"full-{name}")
     rng = np.random.default_rng(WL.CFG_IDS[name])
-    for t in (1, 2):
-        _log(f"{name} t={t}: gradients")
+    checks = set(w.parity_steps)
+    for t in range(1, max(checks) + 1):
         grads, host = _grads(w, name, t)
+        if t not in checks:
+            opt.step(grads=grads)
+            del grads
+            continue
+        _log(f"{name} t={t}: checked step")
         before = {}
         for gi, i in _sampled(w, name):
             s = opt.state[gi]
