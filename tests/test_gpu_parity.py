@@ -594,6 +594,49 @@ def test_step_refuses_mismatched_gradients():
     assert opt.t == 1
 
 
+def test_factors_are_exactly_symmetric():
+    """The factor update computes the upper triangle and mirrors it, so S_a
+    and S_b are bitwise symmetric after every step (both modes, ragged
+    shapes, three steps)."""
+    torch = pytest.importorskip("torch")
+    groups = [(200, 72, 1), (130, 300, 1), (33, 40, 2)]
+    for mode in ("okls", "shampoo"):
+        opt, params = H.make(groups, precision="fp16", mode=mode)
+        for t in (1, 2, 3):
+            opt.step(grads=[H.to_device_grad((0.02 * np.random.default_rng([gi, t, 53]).standard_normal((b, m, n)))
+                                             .astype(np.float32), "f32") for gi, (m, n, b) in enumerate(groups)])
+            torch.cuda.synchronize()
+            for st in opt.state:
+                for k in ("Sa", "Sb"):
+                    assert torch.equal(st[k], st[k].transpose(1, 2)), (mode, t, k)
+
+
+@pytest.mark.parametrize("precision,tol", [("fp16", 2e-2), ("fp32", 1e-4)])
+def test_diagonal_factor_follows_the_scalar_recurrence(precision, tol):
+    """A diagonal factor with distinct eigenvalues (log-uniform over kappa 1e3)
+    and a zero gradient: every Newton-Schulz iterate stays diagonal, so P is
+    exactly diagonal and each entry is the oracle's scalar recurrence
+    (ns_spectral) at beta2 lambda + eps, over d = 300 (ragged against the
+    tiles)."""
+    torch = pytest.importorskip("torch")
+    d, n = 300, 40
+    opt, params = H.make([(d, n, 1)], precision=precision)
+    hp = H.hyper_of(opt)
+    lam = np.exp(np.random.default_rng(19).uniform(np.log(1e-3), 0.0, d)) * 1e-4
+    lam32 = lam.astype(np.float32)
+    opt.state[0]["Sa"][0].copy_(torch.diag(torch.tensor(lam32)))
+    opt.step(grads=[torch.zeros(1, d, n, device="cuda:0")])
+    torch.cuda.synchronize()
+    P = opt.state[0]["Pa"][0].double().cpu().numpy()
+    off = P - np.diag(np.diag(P))
+    assert np.count_nonzero(off) == 0
+    lam1 = hp.beta2 * lam32.astype(np.float64) + hp.eps
+    want = O.ns_spectral(lam1, O.ns_coefficients(hp.ns_floor, hp.ns_steps)[0], hp.ns_damping, 2)
+    err = O.rel_frob(np.diag(P), want)
+    print(f"[diagonal-{precision}] P vs scalar recurrence {err:.2e}", flush=True)
+    assert err < tol
+
+
 def test_only_the_upper_triangle_of_s_is_read():
     """S must be symmetric on entry and only its upper triangle is read: a
     factor whose lower triangle holds junk gives bit-identically the step of
