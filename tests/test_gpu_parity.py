@@ -594,6 +594,32 @@ def test_step_refuses_mismatched_gradients():
     assert opt.t == 1
 
 
+@pytest.mark.parametrize("mode", ["okls", "shampoo"])
+def test_factor_gemm_matches_fp64_on_exact_fp16_inputs(mode):
+    """The GEMM on inputs the fp16 cast represents exactly: G holds
+    fp16-representable values and the cast's scale is a power of two, so at
+    t = 1 (P = I) the factor update multiplies exactly G.  S_1 minus its eps
+    terms then equals c1 G G^T (c1 = (1 - beta2)/n or 1) to fp32 accumulation
+    accuracy, over a ragged 300 x 520 matrix (K = 520 and 300)."""
+    torch = pytest.importorskip("torch")
+    m, n = 300, 520
+    G = (np.random.default_rng(37).standard_normal((m, n)).astype(np.float16).astype(np.float64)) * 0.125
+    opt, params = H.make([(m, n, 1)], precision="fp16", mode=mode)
+    hp = H.hyper_of(opt)
+    opt.step(grads=[torch.tensor(G.astype(np.float32), device="cuda:0")[None]])
+    torch.cuda.synchronize()
+    okls_mode = mode == "okls"
+    c0 = hp.beta2 if okls_mode else 1.0
+    for key, gram, den in (("Sa", G @ G.T, n), ("Sb", G.T @ G, m)):
+        c1 = (1.0 - hp.beta2) / den if okls_mode else 1.0
+        d = gram.shape[0]
+        want = c1 * gram + (c0 * hp.eps + hp.eps) * np.eye(d)
+        got = opt.state[0][key][0].double().cpu().numpy()
+        err = O.rel_frob(got, want)
+        print(f"[exact-gemm-{mode}] {key} rel err {err:.2e}", flush=True)
+        assert err < 1e-5, (key, err)
+
+
 def test_factors_are_exactly_symmetric():
     """The factor update computes the upper triangle and mirrors it, so S_a
     and S_b are bitwise symmetric after every step (both modes, ragged
