@@ -24,6 +24,7 @@ device, so every launch runs at its real size.
 """
 import gc
 import math
+import sys
 import time
 
 import numpy as np
@@ -53,7 +54,9 @@ N_ROWS = 32
 
 
 def _log(msg):
-    print(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    # to the process's own stderr, past pytest's capture: these tests run for
+    # minutes, and their progress should show however pytest is invoked
+    print(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}", file=sys.__stderr__, flush=True)
 
 
 def _sampled(w, name):
