@@ -176,7 +176,13 @@ okls_status okls_init_state(okls_handle* h, const okls_group_tensors* tensors, v
  * every matrix of every group: steps 1-4 in the header comment.  G is read
  * only; W, M, S_a, S_b, P_a, P_b are updated in place (P only on steps that
  * recompute the roots; Muon mode: W and M only).  S must be symmetric on
- * entry (only its upper triangle is read).  Asynchronous on `stream`. */
+ * entry (only its upper triangle is read).  Asynchronous on `stream`; it
+ * issues no allocation, memset or synchronisation, so it can be captured
+ * into a HIP graph.  t and lr, and what follows from them (the Nesterov
+ * scale, the decay, whether the roots are recomputed), are launch arguments:
+ * a captured step replays with the values it was captured with, so capture
+ * one graph per distinct (t-dependent, lr) step rather than replaying one
+ * graph across steps. */
 okls_status okls_step(okls_handle* h, const okls_group_tensors* tensors, int64_t t, float lr,
                       void* stream);
 
