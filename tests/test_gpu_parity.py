@@ -573,6 +573,35 @@ def test_step_argument_errors_launch_nothing():
     assert not torch.equal(before["Pa"], opt.state[0]["Pa"])
 
 
+def test_step_reads_p_grad():
+    """step() without grads reads each parameter's .grad (2-D parameters, as a
+    model holds them): bit-identical to passing the same tensors explicitly;
+    a parameter without a gradient is refused."""
+    torch = pytest.importorskip("torch")
+    from kronecker_factored_second_amd import okls
+    shapes = [(96, 160), (40, 33)]
+    runs = []
+    for explicit in (False, True):
+        params = [torch.zeros(m, n, device="cuda:0") for m, n in shapes]
+        opt = okls.OKLS(params, precision="fp16")
+        for t in (1, 2):
+            gs = [torch.tensor((0.02 * np.random.default_rng([i, t]).standard_normal(s_)).astype(np.float32),
+                               device="cuda:0") for i, s_ in enumerate(shapes)]
+            if explicit:
+                opt.step(grads=gs)
+            else:
+                for p_, g in zip(params, gs):
+                    p_.grad = g
+                opt.step()
+                opt.zero_grad()
+        torch.cuda.synchronize()
+        runs.append([p_.clone() for p_ in params] + [v.clone() for st in opt.state for v in st.values()])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+    with pytest.raises(ValueError):
+        opt.step()                      # zero_grad() left no gradients
+
+
 def test_step_refuses_mismatched_gradients():
     """The wrapper refuses a gradient whose dtype, shape or presence differs
     from what the handle was built for (the library would misread it, or read
