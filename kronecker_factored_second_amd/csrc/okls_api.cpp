@@ -780,6 +780,36 @@ struct Planner {
     }
   }
 
+  // Whether a second concurrent Newton-Schulz chain pays for this chunk.
+  // It fills the CUs that the last, partly filled round of a launch leaves
+  // idle; with a full last round, or many rounds, it only adds launches and
+  // contention.  The measure is the single-chain T_k launch in rounds of
+  // kCUs blocks, each tile weighted by its K against the largest K.  Measured
+  // (A/B per workload): two chains +5.5 % on the d=1024 block (1.7 rounds);
+  // one chain +6 % on the 1.2B-class workload and +11 % on the 13B-class
+  // layer, and +1.6 to +5.7 % on batches of equal square factors whose
+  // launches are whole rounds.
+  static constexpr int kCUs = 256;
+  bool two_chains_pay(const std::vector<FacBufs*>& facs) const {
+    if (facs.size() < 2) return false;
+    int kmax = 0;
+    long big = 0;
+    bool big_ok = true;
+    for (const FacBufs* f : facs) {
+      kmax = std::max(kmax, f->dp);
+      if (f->dp % kBigTile) big_ok = false;
+      big += static_cast<long>(f->dp / kBigTile) * (f->dp / kBigTile);
+    }
+    // the tile the launch takes (add_gemm's rule for the fp16-output kinds)
+    const int bt = (big_ok && big >= 64) ? kBigTile : kTile;
+    const double slots = bt == kBigTile ? kCUs : 2.0 * kCUs;   // the 128 tile runs two blocks per CU
+    double w = 0.0;
+    for (const FacBufs* f : facs) w += std::pow(static_cast<double>(f->dp / bt), 2.0) * f->dp / kmax;
+    const double rounds = w / slots;
+    const double last = rounds - std::floor(rounds);
+    return rounds < 4.0 && last > 0.0 && last <= 0.75;
+  }
+
   // P16 produced by the chain of this factor, in Z[K % 2]
   size_t p16_of(const FacBufs& F) const { return F.Z[cfg.ns_steps & 1]; }
 
@@ -962,7 +992,7 @@ struct Planner {
       std::vector<size_t> order(facs.size());
       for (size_t f = 0; f < order.size(); ++f) order[f] = f;
       std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return facs[x]->d > facs[y]->d; });
-      const int nset = std::min<int>(kNsStreams, static_cast<int>(facs.size()));
+      const int nset = two_chains_pay(facs) ? std::min<int>(kNsStreams, static_cast<int>(facs.size())) : 1;
       std::vector<double> load(nset, 0.0);
       std::vector<std::vector<size_t>> sets(nset);
       for (size_t f : order) {
