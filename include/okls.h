@@ -33,14 +33,16 @@
  *     hyperparameters).
  *   - The caller owns every tensor and the workspace.  The library never
  *     allocates device memory; the handle owns host memory plus, when the
- *     plan has more than one factor, one HIP stream and two events (created
- *     by okls_init, destroyed by okls_destroy).
+ *     plan runs two concurrent Newton-Schulz chains, one HIP stream and two
+ *     events (created by okls_init, destroyed by okls_destroy).
  *   - All device work is ordered on the given stream (a hipStream_t passed
- *     as void*; NULL is the default stream).  okls_step runs the second of
- *     its two concurrent Newton-Schulz chains on the handle's stream, which
- *     waits for everything queued on the given stream before it and which
- *     the given stream waits for before the step's remaining work, so the
- *     step is ordered on the given stream as a whole.  okls_init and
+ *     as void*; NULL is the default stream).  The plan runs a second,
+ *     concurrent Newton-Schulz chain where it fills otherwise idle compute
+ *     units (launches of few, partly filled rounds of tiles).  That chain
+ *     runs on the handle's stream, which waits for everything queued on the
+ *     given stream before it and which the given stream waits for before the
+ *     step's remaining work, so the step is ordered on the given stream as a
+ *     whole.  okls_init and
  *     okls_init_state synchronise that stream once (init uploads descriptor
  *     tables); okls_step never synchronises.  Device faults surface at the
  *     caller's next synchronisation.
@@ -201,7 +203,7 @@ int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_s
  * use and owned by the handle).  okls_profile_read synchronises the last
  * profiled step, sums the elapsed times per category since the last read
  * (ms) and the length of the union of each category's launch intervals
- * (busy_ms: launches of the two concurrent Newton-Schulz chains overlap, so
+ * (busy_ms: launches of two concurrent Newton-Schulz chains overlap, so
  * their durations add up to more than the time the category keeps the GPU
  * busy), then clears them.  Categories (index into the arrays):
  *   0 Newton-Schulz GEMMs, 1 factor GEMMs (cross-preconditioning and the
