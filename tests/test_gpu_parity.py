@@ -461,6 +461,20 @@ def test_plain_shampoo_worked_example_in_the_weights():
             np.testing.assert_allclose(sv, want[t], atol=g["printed_precision"])
 
 
+def test_single_chain_plan():
+    """A chunk whose single-chain Newton-Schulz launch is exactly one full
+    round of 256 tiles (128 matrices of 256 x 256) runs one chain, with no
+    side stream: every 16th matrix teacher-forced for two steps."""
+    groups = [(256, 256, 128)]
+
+    def grad(gi, i, t):
+        return (0.02 * np.random.default_rng([i, t, 256]).standard_normal((256, 256))).astype(np.float32)
+
+    opt = _run_teacher_forced("single-chain", groups, grad, 2, "fp16", check=lambda gi, i, t: i % 16 == 0)
+    from kronecker_factored_second_amd import okls
+    assert okls.workspace_size(opt.cfg, opt.groups) > 0
+
+
 def test_maximum_group_count():
     """Sixteen groups, the most one handle takes, of distinct ragged shapes
     (tall, wide, square, vectors; batches 1 and 2) in one step: the
