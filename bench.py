@@ -352,7 +352,7 @@ def main():
                                                        mode == "okls" and args.root_period == 1) else None,
                      "method": "algorithmic FLOPs of every gemm_nt_kernel launch over the union of their intervals, "
                                "from HIP events on the launch streams in a second pass of the same steps (the timed "
-                               "pass runs without them); the two Newton-Schulz chains' launches overlap",
+                               "pass runs without them); where the plan runs two Newton-Schulz chains their launches overlap",
                      "avg_launch_us": g_ms * 1e3 / max(g_n, 1), "achieved_per_launch_duration": per_launch,
                      "launches_per_step": g_n / max(prof["steps"], 1),
                      "algorithmic_flops_per_step": g_fl / max(prof["steps"], 1),
