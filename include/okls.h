@@ -160,6 +160,27 @@ void okls_default_config(okls_config* cfg);
  * host function.  Returns 0 if the arguments are invalid. */
 size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups);
 
+/* What a step of these groups runs, from the same plan okls_init builds.
+ * Pure host function (no device, no workspace).  chunks: matrix chunks per
+ * step; launches / launches_stale: kernel launches of a step that recomputes
+ * the roots / keeps them (equal when root_period is 1 and in Muon mode);
+ * ns_chains: the most Newton-Schulz chains any chunk runs at once (2 when a
+ * second chain on the library's side stream fills a partly idle last round
+ * of tiles, else 1; 0 in Muon mode); flops / bytes: the algorithmic work of
+ * a step that recomputes the roots, per profile category, as
+ * okls_profile_read counts it (categories and units below).
+ * OKLS_ERR_INVALID_ARG for a NULL out or invalid config or groups. */
+typedef struct {
+    int chunks;
+    int launches;
+    int launches_stale;
+    int ns_chains;
+    double flops[5];
+    double bytes[5];
+} okls_plan_info;
+okls_status okls_plan_query(const okls_config* cfg, int n_groups, const okls_group_desc* groups,
+                            okls_plan_info* out);
+
 /* Validates the groups, plans the launches and uploads descriptor tables into
  * the caller's workspace (ws_bytes >= okls_workspace_size, 256-byte aligned).
  * The workspace must stay valid and unused by others until okls_destroy.

@@ -1351,6 +1351,44 @@ size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_grou
   return w.total;
 }
 
+okls_status okls_plan_query(const okls_config* cfg, int n_groups, const okls_group_desc* groups,
+                            okls_plan_info* out) {
+  if (out == nullptr) return OKLS_ERR_INVALID_ARG;
+  okls_status st = check_config(cfg);
+  if (st != OKLS_OK) return st;
+  st = check_groups(n_groups, groups);
+  if (st != OKLS_OK) return st;
+  std::vector<okls_group_desc> g(groups, groups + n_groups);
+  Planner P(*cfg, g);
+  (void)ws_layout(P);
+  if (!P.validate()) return OKLS_ERR_INVALID_ARG;
+  static_assert(OKLS_PROFILE_CATEGORIES == 5, "okls_plan_info holds five categories");
+  okls_plan_info info{};
+  auto kernels = [](const std::vector<std::vector<LaunchRec>>& cs) {
+    int n = 0;
+    for (const std::vector<LaunchRec>& L : cs)
+      for (const LaunchRec& r : L) n += (r.type == L_STAT || r.type == L_CAST || r.type == L_GEMM);
+    return n;
+  };
+  info.chunks = static_cast<int>(P.chunks.size());
+  info.launches = kernels(P.chunks);
+  info.launches_stale = P.chunks_stale.empty() ? info.launches : kernels(P.chunks_stale);
+  info.ns_chains = 0;
+  if (!P.muon_mode) {
+    for (const std::vector<LaunchRec>& L : P.chunks) {
+      int streams = 1;
+      for (const LaunchRec& r : L) streams = std::max(streams, r.stream + 1);
+      info.ns_chains = std::max(info.ns_chains, streams);
+    }
+  }
+  for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
+    info.flops[i] = P.step_flops[i];
+    info.bytes[i] = P.step_bytes[i];
+  }
+  *out = info;
+  return OKLS_OK;
+}
+
 int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_steps) {
   if (check_config(cfg) != OKLS_OK || a == nullptr || b == nullptr || max_steps < cfg->ns_steps) return -1;
   std::vector<double> na, nb;

@@ -22,7 +22,7 @@ MODE = {"okls": 0, "shampoo": 1, "muon": 2}
 MUON_DEFAULTS = dict(ns_steps=5, ns_floor=1e-2)
 EXPORTED = ("okls_default_config", "okls_workspace_size", "okls_init", "okls_init_state", "okls_step",
             "okls_check_finite", "okls_ns_coefficients", "okls_profile_enable", "okls_profile_read",
-            "okls_destroy", "okls_status_string")
+            "okls_destroy", "okls_status_string", "okls_plan_query")
 PROFILE_CATEGORIES = ("ns_gemm", "factor_gemm", "whiten_gemm", "stats", "cast")
 
 
@@ -50,6 +50,11 @@ class ProfileStats(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double * 5), ("busy_ms", ctypes.c_double * 5), ("flops", ctypes.c_double * 5),
                 ("bytes", ctypes.c_double * 5),
                 ("launches", ctypes.c_int64 * 5), ("steps", ctypes.c_int64)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("chunks", ctypes.c_int32), ("launches", ctypes.c_int32), ("launches_stale", ctypes.c_int32),
+                ("ns_chains", ctypes.c_int32), ("flops", ctypes.c_double * 5), ("bytes", ctypes.c_double * 5)]
 
 
 class OKLSError(RuntimeError):
@@ -92,6 +97,9 @@ def load(path: str = LIB_PATH):
     lib.okls_profile_read.restype = ctypes.c_int
     lib.okls_destroy.argtypes = [vp]
     lib.okls_destroy.restype = ctypes.c_int
+    lib.okls_plan_query.argtypes = [ctypes.POINTER(Config), ctypes.c_int, ctypes.POINTER(GroupDesc),
+                                    ctypes.POINTER(PlanInfo)]
+    lib.okls_plan_query.restype = ctypes.c_int
     lib.okls_status_string.argtypes = [ctypes.c_int]
     lib.okls_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -141,6 +149,19 @@ def _groups_array(groups):
 def workspace_size(cfg: Config, groups) -> int:
     """groups: list of (batch, m, n, g_dtype)."""
     return int(load().okls_workspace_size(ctypes.byref(cfg), len(groups), _groups_array(groups)))
+
+
+def plan_query(cfg: Config, groups) -> dict:
+    """What a step of these groups runs (host only): chunks, kernel launches of
+    a refresh / stale step, concurrent Newton-Schulz chains, and the refresh
+    step's algorithmic FLOPs and bytes per profile category."""
+    info = PlanInfo()
+    st = load().okls_plan_query(ctypes.byref(cfg), len(groups), _groups_array(groups), ctypes.byref(info))
+    if st != 0:
+        raise OKLSError("okls_plan_query", st)
+    return {"chunks": info.chunks, "launches": info.launches, "launches_stale": info.launches_stale,
+            "ns_chains": info.ns_chains,
+            "flops": dict(zip(PROFILE_CATEGORIES, info.flops)), "bytes": dict(zip(PROFILE_CATEGORIES, info.bytes))}
 
 
 def ns_coefficients(cfg: Config):

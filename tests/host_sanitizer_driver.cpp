@@ -1,6 +1,6 @@
 // Host-side sweep of the library's planner for a sanitizer build: every call
 // here is a host function (okls_default_config, okls_workspace_size,
-// okls_ns_coefficients, okls_status_string), so no device is touched.  The
+// okls_plan_query, okls_ns_coefficients, okls_status_string), so no device is touched.  The
 // planner lays out the workspace, builds the launch lists and checks every
 // descriptor against its buffer; built with address and undefined-behaviour
 // sanitizers on the host pass, this sweep makes any out-of-bounds access or
@@ -47,6 +47,13 @@ int main(int argc, char** argv) {
     }
     const size_t ws = okls_workspace_size(&c, ng, g.data());
     if (ws == 0) ++refused; else ++planned;
+    okls_plan_info info;
+    const okls_status qs = okls_plan_query(&c, ng, g.data(), &info);
+    if ((qs == OKLS_OK) != (ws != 0) ||
+        (qs == OKLS_OK && (info.chunks < 1 || info.launches < 1 || info.ns_chains < 0 || info.ns_chains > 2))) {
+      std::fprintf(stderr, "plan query disagrees with the workspace query\n");
+      return 1;
+    }
     double a[16], b[16];
     if (okls_ns_coefficients(&c, a, b, 16) != c.ns_steps) {
       std::fprintf(stderr, "coefficient table length mismatch\n");

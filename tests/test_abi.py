@@ -39,7 +39,8 @@ def test_binding_struct_layouts_match_header(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     structs = {"okls_config": okls.Config, "okls_group_desc": okls.GroupDesc,
-               "okls_group_tensors": okls.GroupTensors, "okls_profile_stats": okls.ProfileStats}
+               "okls_group_tensors": okls.GroupTensors, "okls_profile_stats": okls.ProfileStats,
+               "okls_plan_info": okls.PlanInfo}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "okls.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
@@ -155,3 +156,89 @@ def test_muon_plans_validate_on_the_host():
             assert okls.workspace_size(cfg, groups) > 0, (prec, groups)
         cfg.ns_steps = 1
         assert okls.workspace_size(cfg, [(1, 64, 80, 0)]) == 0
+
+
+def _plan(groups, precision="fp16", **kw):
+    _lib()
+    return okls.plan_query(okls.precision_config(precision, **kw), groups)
+
+
+def test_plan_query_chain_rule():
+    """A second Newton-Schulz chain runs only when the single chain's T launch
+    has fewer than 4 rounds of tiles on the 256 CUs and its last round is at
+    most three quarters full.  256 x 256 matrices give one 256 tile per factor,
+    two factors per matrix; 1024 x 1024 ones sixteen per factor."""
+    cases = [  # (matrices, side, tiles of the launch) -> chains
+        (64, 256, 128, 2),      # one round, half full
+        (96, 256, 192, 2),      # one round, exactly 3/4 full
+        (97, 256, 194, 1),      # one round, just over 3/4
+        (128, 256, 256, 1),     # one full round
+        (192, 256, 384, 2),     # two rounds, the last half full
+        (384, 256, 768, 1),     # three full rounds
+        (512, 256, 1024, 1),    # four rounds
+        (8, 1024, 256, 1),
+        (12, 1024, 384, 2),
+        (13, 1024, 416, 2),     # last round 160/256
+        (16, 1024, 512, 1),
+    ]
+    for nmat, d, tiles, chains in cases:
+        assert 2 * nmat * (d // 256) ** 2 == tiles
+        got = _plan([(nmat, d, d, 0)], mode=okls.MODE["okls"])["ns_chains"]
+        assert got == chains, (nmat, d, got)
+
+
+def test_plan_query_workloads_and_modes():
+    """The d=1024 block runs two chains, the 1.2B-, 6.5B- and 13B-class
+    workloads one; Muon mode has no Newton-Schulz root chain; a step that
+    keeps the roots launches no Newton-Schulz GEMM."""
+    from kronecker_factored_second_amd import workloads as W
+    expect = {"c2": 2, "c3": 1, "c4": 1, "c5": 1}
+    for name, chains in expect.items():
+        w = W.workload(name)
+        groups = [(b, m, n, okls.OKLS_BF16) for m, n, b in w.groups]
+        info = _plan(groups, mode=okls.MODE[w.mode])
+        assert info["chunks"] == 1 and info["ns_chains"] == chains, (name, info["ns_chains"])
+    groups = [(4, 1024, 1024, 0), (2, 2816, 1024, 0), (1, 1024, 2816, 0)]
+    assert _plan(groups, mode=okls.MODE["muon"], **okls.MUON_DEFAULTS)["ns_chains"] == 0
+    fresh = _plan(groups, mode=okls.MODE["okls"])
+    kept = _plan(groups, mode=okls.MODE["okls"], root_period=3)
+    assert fresh["launches_stale"] == fresh["launches"]
+    assert kept["launches"] == fresh["launches"] and kept["launches_stale"] < kept["launches"]
+
+
+def test_plan_query_flops_are_the_closed_forms():
+    """The algorithmic FLOPs that the profile and the roofline divide by:
+    per matrix (m, n), 27 products of 2 d^3 per inverse square root (54 for
+    the Shampoo fourth root) over d = m and d = n, 3 m n (m + n) for the OKLS
+    factor products (m n (m + n) for the Shampoo sums), 2 m n (m + n) for the
+    whitening; Muon: 4 K p^2 q with p, q the smaller and larger side."""
+    groups = [(4, 1024, 1024, 0), (2, 2816, 1024, 0), (1, 1024, 2816, 0), (3, 200, 72, 0)]
+    mats = [(m, n) for b, m, n, _ in groups for _ in range(b)]
+    cube = sum(float(m) ** 3 + float(n) ** 3 for m, n in mats)
+    mn = sum(float(m) * n * (m + n) for m, n in mats)
+    for prec in ("fp16", "fp32"):
+        f = _plan(groups, prec, mode=okls.MODE["okls"])["flops"]
+        assert f["ns_gemm"] == pytest.approx(27 * 2 * cube, rel=1e-12)
+        assert f["factor_gemm"] == pytest.approx(3 * mn, rel=1e-12)
+        assert f["whiten_gemm"] == pytest.approx(2 * mn, rel=1e-12)
+        f = _plan(groups, prec, mode=okls.MODE["shampoo"])["flops"]
+        assert f["ns_gemm"] == pytest.approx(54 * 2 * cube, rel=1e-12)
+        assert f["factor_gemm"] == pytest.approx(mn, rel=1e-12)
+        f = _plan(groups, prec, mode=okls.MODE["muon"], **okls.MUON_DEFAULTS)["flops"]
+        k = okls.MUON_DEFAULTS["ns_steps"]
+        assert f["ns_gemm"] == pytest.approx(sum(4 * k * float(min(m, n)) ** 2 * max(m, n) for m, n in mats), rel=1e-12)
+
+
+def test_plan_query_rejects_invalid_arguments():
+    _lib()
+    cfg = okls.precision_config("fp16")
+    with pytest.raises(okls.OKLSError):
+        okls.plan_query(cfg, [])
+    with pytest.raises(okls.OKLSError):
+        okls.plan_query(cfg, [(1, 0, 8, 0)])
+    cfg.ns_steps = 0
+    with pytest.raises(okls.OKLSError):
+        okls.plan_query(cfg, [(1, 8, 8, 0)])
+    lib = okls.load()
+    assert lib.okls_plan_query(ctypes.byref(okls.precision_config("fp16")), 1,
+                               okls._groups_array([(1, 8, 8, 0)]), None) != 0
