@@ -105,10 +105,13 @@ typedef struct {
     float weight_decay;        /* AdamC decoupled decay coefficient (default 0.0303) */
     float lr_peak;             /* initial learning rate kept for the AdamC correction */
     float ns_floor;            /* lower end l_0 of the interval the NS coefficients are
-                                  optimised on, for sqrt(lambda / ||S||_F); default 1e-3 */
-    float ns_damping;          /* nu: the root is taken of S + (nu / sqrt(d)) ||S||_F I, which
-                                  keeps the rounded iteration positive definite; default
-                                  5e-3 for the fp16 path, 2e-3 suits the split-fp16 path */
+                                  optimised on, for sqrt(lambda / ||S||_F); default 3e-2, matched
+                                  to fp16 GEMM inputs: the table's gain on directions below
+                                  the interval is about 1/l_0-fold larger than 1, and fp16
+                                  rounding noise in them must stay bounded (1e-3 suits the
+                                  fp32-accurate split path) */
+    float ns_damping;          /* nu: the root is taken of S + (nu / sqrt(d)) ||S||_F I; default
+                                  0 (the root of S itself, P = S^{-1/2}) */
     int32_t root_period;       /* p >= 1: the roots are recomputed on steps t = 1, 1 + p,
                                   1 + 2p, ... and kept in between (the factors, momentum,
                                   whitening and update run every step).  1 (default) is the
@@ -131,6 +134,11 @@ typedef struct {
                                   1: the classical Newton-Schulz step a = 3/2, b = -1/2 at every
                                   step (ns_floor unused); 10 such steps converge only for
                                   condition numbers up to about 1e2 */
+    int32_t whiten_split;      /* 1 (default): the whitening products P_b N^T and P_a V run
+                                  split-fp16 (fp32-accurate) also when factor_split is 0:
+                                  their fp16 rounding error grows with the preconditioners'
+                                  eigenvalue spread, which rank-deficient factors make large;
+                                  0: plain fp16 inputs (the fp16 path's other products) */
 } okls_config;
 
 typedef struct {

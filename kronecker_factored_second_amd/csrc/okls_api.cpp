@@ -96,8 +96,9 @@ float pow2_for_bound(double bound) {   // largest 2^e with bound * 2^e <= 2^kSca
 }
 
 struct FacBufs {
-  int d = 0, dp = 0, ld = 0;
+  int d = 0, dp = 0, ld = 0, ldw = 0;
   size_t Y[2] = {0, 0}, Z[2] = {0, 0}, T = 0, R32 = 0;
+  size_t P16w = 0;   // the root's fp16 copy (ld ldw) the cross-preconditioning and whitening read
   size_t YT[2] = {0, 0}, ZT[2] = {0, 0}, TT = 0;   // transposed copies
   int s_pold = 0, s_cinv = 0, s_rho = 0, s_sqrtc = 0, s_p16 = 0;
   int s_cinv2 = 0, s_rho2 = 0, s_sqrtc2 = 0;
@@ -105,6 +106,7 @@ struct FacBufs {
 
 struct MatBufs {
   int group = 0, index = 0, m = 0, n = 0, mp = 0, np = 0, ldm = 0, ldn = 0;
+  int ldmw = 0, ldnw = 0;   // strides of the whitening operands N16 (ldnw) and VT16 (ldmw)
   size_t G16 = 0, G16T = 0, N16 = 0, Xa32 = 0, XbT32 = 0, Xa16 = 0, XbT16 = 0, VT32 = 0, VT16 = 0;
   int s_g = 0, s_n = 0, s_xa = 0, s_xb = 0, s_vt = 0;
   FacBufs fa, fb;
@@ -114,7 +116,7 @@ struct MatBufs {
   int s_gcinv = 0, s_grho = 0;
 };
 
-enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4 };
+enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4, L_SYM = 5 };
 
 struct LaunchRec {
   int type = L_STAT;
@@ -159,7 +161,7 @@ struct okls_handle {
   std::vector<okls_group_desc> groups;
   char* ws = nullptr;
   size_t ws_bytes = 0;
-  size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_scal = 0, off_part = 0, off_flag = 0;
+  size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_sym = 0, off_scal = 0, off_part = 0, off_flag = 0;
   std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
   std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them
   std::vector<double> na, nb;
@@ -199,6 +201,7 @@ okls_status check_config(const okls_config* c) {
   if (c->ns_steps < 2 || c->ns_steps > 16) return OKLS_ERR_INVALID_ARG;
   if (c->ns_split_steps < 0 || c->ns_split_steps > c->ns_steps) return OKLS_ERR_INVALID_ARG;
   if (c->factor_split != 0 && c->factor_split != 1) return OKLS_ERR_INVALID_ARG;
+  if (c->whiten_split != 0 && c->whiten_split != 1) return OKLS_ERR_INVALID_ARG;
   if (c->nesterov_var_corr != 0 && c->nesterov_var_corr != 1) return OKLS_ERR_INVALID_ARG;
   if (c->chunk_matrices < 0) return OKLS_ERR_INVALID_ARG;
   if (!(c->beta1 >= 0.f && c->beta1 < 1.f)) return OKLS_ERR_INVALID_ARG;
@@ -240,6 +243,7 @@ struct Planner {
   std::vector<TileRef> tiles;
   std::vector<StatJob> stat_jobs;
   std::vector<CastJob> cast_jobs;
+  std::vector<SymJob> sym_jobs;
   std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
   std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them (root_period > 1)
   std::map<std::string, std::pair<int, int>> tile_cache;
@@ -264,6 +268,11 @@ struct Planner {
   }
 
   int ld_for(int dp) const { return lo_layout ? 2 * dp : dp; }
+  // rows of a buffer hold [hi | lo] only where a split product reads it: the
+  // factor operands, the Newton-Schulz iterates and the whitening operands
+  int ld_fac(int dp) const { return cfg.factor_split ? 2 * dp : dp; }
+  int ld_ns(int dp) const { return cfg.ns_split_steps > 0 ? 2 * dp : dp; }
+  int ld_wh(int dp) const { return wsplit() ? 2 * dp : dp; }
   // relative shift of the rooted matrix: delta = nu / sqrt(d)
   float damping(int d) const { return static_cast<float>(cfg.ns_damping / std::sqrt(static_cast<double>(d))); }
 
@@ -279,10 +288,11 @@ struct Planner {
       return o;
     };
     auto fac = [&](FacBufs& f, int d) {
-      f.d = d; f.dp = pad_tile(d); f.ld = ld_for(f.dp);
+      f.d = d; f.dp = pad_tile(d); f.ld = ld_ns(f.dp); f.ldw = ld_wh(f.dp);
       const size_t b16 = static_cast<size_t>(f.dp) * f.ld * 2;
       f.Y[0] = take(b16); f.Y[1] = take(b16); f.Z[0] = take(b16); f.Z[1] = take(b16); f.T = take(b16);
       f.YT[0] = take(b16); f.YT[1] = take(b16); f.ZT[0] = take(b16); f.ZT[1] = take(b16); f.TT = take(b16);
+      f.P16w = take(static_cast<size_t>(f.dp) * f.ldw * 2);
       if (!okls_mode) f.R32 = take(static_cast<size_t>(d) * d * 4);
       f.s_pold = slot++; f.s_cinv = slot++; f.s_rho = slot++; f.s_sqrtc = slot++; f.s_p16 = slot++;
       f.s_cinv2 = slot++; f.s_rho2 = slot++; f.s_sqrtc2 = slot++;
@@ -301,9 +311,11 @@ struct Planner {
         mb.s_n = slot++; mb.s_gcinv = slot++; mb.s_grho = slot++;
         continue;
       }
+      mb.ldm = ld_fac(mb.mp); mb.ldn = ld_fac(mb.np);
+      mb.ldmw = ld_wh(mb.mp); mb.ldnw = ld_wh(mb.np);
       mb.G16 = take(static_cast<size_t>(mb.mp) * mb.ldn * 2);
       mb.G16T = take(static_cast<size_t>(mb.np) * mb.ldm * 2);
-      mb.N16 = take(static_cast<size_t>(mb.mp) * mb.ldn * 2);
+      mb.N16 = take(static_cast<size_t>(mb.mp) * mb.ldnw * 2);
       if (okls_mode) {
         mb.Xa32 = take(static_cast<size_t>(mb.m) * mb.n * 4);
         mb.XbT32 = take(static_cast<size_t>(mb.n) * mb.m * 4);
@@ -311,7 +323,7 @@ struct Planner {
         mb.XbT16 = take(static_cast<size_t>(mb.np) * mb.ldm * 2);
       }
       mb.VT32 = take(static_cast<size_t>(mb.n) * mb.m * 4);
-      mb.VT16 = take(static_cast<size_t>(mb.np) * mb.ldm * 2);
+      mb.VT16 = take(static_cast<size_t>(mb.np) * mb.ldmw * 2);
       mb.s_g = slot++; mb.s_n = slot++; mb.s_xa = slot++; mb.s_xb = slot++; mb.s_vt = slot++;
       fac(mb.fa, g.m);
       fac(mb.fb, g.n);
@@ -473,7 +485,7 @@ struct Planner {
     int kind; Ref src; int src_ld; Ref src2; int g_fmt; int write_m; int transpose;
     int rows, cols, dst_rows_p, dst_cols_p; Ref dst; int dst_ld; int dst_lo;
     std::pair<int, int> parts; int scale_mode; int scale_slot;
-    int cinv_slot, rho_slot, sqrtc_slot, p16_slot; int write_lo; float damp; int sym_read;
+    int cinv_slot, rho_slot, sqrtc_slot, p16_slot, p16_inv_sqrt; int write_lo; float damp; int sym_read;
     Ref dst2; int scale_slot2; int write_lo2;
     Ref dstT; int dstT_ld; int dstT_lo;
   };
@@ -501,7 +513,7 @@ struct Planner {
       j.dst_lo = s.dst_lo; j.part_begin = s.parts.first; j.part_count = s.parts.second;
       j.scale_mode = s.scale_mode; j.scale_slot = s.scale_slot; j.cinv_slot = s.cinv_slot;
       j.rho_slot = s.rho_slot; j.sqrtc_slot = s.sqrtc_slot; j.p16_slot = s.p16_slot;
-      j.p16_static = sZ; j.write_lo = s.write_lo; j.damp = s.damp; j.sym_read = s.sym_read;
+      j.p16_static = s.p16_inv_sqrt ? sY : sZ / 16.0f; j.p16_inv_sqrt = s.p16_inv_sqrt; j.write_lo = s.write_lo; j.damp = s.damp; j.sym_read = s.sym_read;
       j.dst2 = s.dst2; j.scale_slot2 = s.scale_slot2; j.write_lo2 = s.write_lo2;
       j.dstT = s.dstT; j.dstT_ld = s.dstT_ld; j.dstT_lo = s.dstT_lo;
       j.tiles_x = (s.dst_cols_p + kCastCols - 1) / kCastCols;
@@ -521,6 +533,32 @@ struct Planner {
     r.kb = kb;
     L.push_back(r);
   }
+
+  // ---- root symmetrisation: P <- (P + P^T) / 2 in place for each factor of
+  // a chain, with the fp16 copy the whitening reads (scale slot s_p16)
+  void add_sym(std::vector<LaunchRec>& L, const std::vector<FacBufs*>& facs, const std::vector<Ref>& pdst) {
+    LaunchRec r;
+    r.type = L_SYM;
+    r.cat = CAT_CAST;
+    r.first = static_cast<int>(sym_jobs.size());
+    int blk = 0;
+    for (size_t f = 0; f < facs.size(); ++f) {
+      const FacBufs& F = *facs[f];
+      SymJob j{};
+      j.p = pdst[f]; j.d = F.d; j.dp = F.dp; j.nt = F.dp / kSymTile;   // the padded side: zeros beyond d
+      j.dst16 = ws_ref(F.P16w); j.ld16 = F.ldw; j.lo16 = F.dp; j.write_lo = wsplit();
+      j.scale_slot = F.s_p16; j.blk_begin = blk;
+      blk += j.nt * (j.nt + 1) / 2;
+      step_bytes[CAT_CAST] += (8.0 + (j.write_lo ? 4.0 : 2.0)) * static_cast<double>(F.d) * F.d;
+      sym_jobs.push_back(j);
+    }
+    r.count = static_cast<int>(facs.size());
+    r.nblocks = blk;
+    if (!facs.empty()) L.push_back(r);
+  }
+
+  // split-fp16 whitening products (and the lo halves of the operands they read)
+  int wsplit() const { return (cfg.factor_split || cfg.whiten_split) ? 1 : 0; }
 
   // eps term of every factor update: + eps I (R1), or (1 - beta2) eps I in
   // the convex form of the OKLS update
@@ -555,10 +593,15 @@ struct Planner {
   // iteration (no symmetry of the iterates is assumed: the coupled iteration
   // is only stable when Y and Z carry consistent rounding).  src(f) is the fp32
   // matrix being rooted (d x d, ld d); returns launches appended to L.
-  // final_mode 0: inverse root into the caller P (+ fp16 copy in Z[K%2]);
-  // final_mode 1: square root into fac.R32 (the first Shampoo chain).
+  // out OUT_INV: the inverse root Z_K / sqrt(c) into pdst (fp32);
+  // out OUT_SQRT: the square root Y_K sqrt(c) into pdst.  With p16 the last
+  // product also writes the output's fp16 copy into Z[K % 2] (Z_K s_Z or
+  // Y_K s_Y), the operand the whitening reads, and the start cast records its
+  // scale.  The Shampoo fourth root chains OUT_INV (into fac.R32, no copy)
+  // and OUT_SQRT of that result.
+  enum { OUT_INV = 0, OUT_SQRT = 1 };
   void ns_chain(std::vector<LaunchRec>& L, std::vector<FacBufs*>& facs, std::vector<Ref>& src,
-                std::vector<Ref>& pdst, int final_mode, int chain) {
+                std::vector<Ref>& pdst, int out, bool p16, int chain) {
     const int K = cfg.ns_steps;
     const int ks = cfg.ns_split_steps;
     const size_t nf = facs.size();
@@ -578,7 +621,8 @@ struct Planner {
       y.cinv_slot = chain == 0 ? F.s_cinv : F.s_cinv2;
       y.rho_slot = chain == 0 ? F.s_rho : F.s_rho2;
       y.sqrtc_slot = chain == 0 ? F.s_sqrtc : F.s_sqrtc2;
-      y.p16_slot = (final_mode == 0) ? F.s_p16 : -1;
+      y.p16_slot = p16 ? F.s_p16 : -1;
+      y.p16_inv_sqrt = out == OUT_SQRT;
       y.write_lo = ks > 0;
       y.damp = damping(F.d);
       y.sym_read = chain == 1;      // the second chain roots a computed square root
@@ -644,17 +688,20 @@ struct Planner {
           FacBufs& F = *facs[f];
           GemmProb p = prob();
           p.lda = p.ldb = F.ld; p.M = p.N = F.d; p.Kp = F.dp; p.Mp = p.Np = F.dp; p.epi = EPI_NS_FINAL;
-          if (final_mode == 0) {      // P = Z_K / sqrt(c), fp16 copy Z_K * s_Z
+          p.out32 = pdst[f]; p.ld32 = F.d;
+          if (out == OUT_INV) {       // P = Z_K / sqrt(c), fp16 copy Z_K * s_Z
             p.A = ws_ref(F.T); p.B = ws_ref(zt_of(F, k)); p.sA = SL_T; p.sB = SL_Z;
-            p.out32 = pdst[f]; p.ld32 = F.d; p.cslot = chain == 0 ? F.s_rho : F.s_rho2;
-            p.out16 = ws_ref(F.Z[nbuf]); p.ld16 = F.ld; p.lo16 = F.dp; p.s_out = SL_Z;
-          } else {                    // R = Y_K sqrt(c)
+            p.cslot = chain == 0 ? F.s_rho : F.s_rho2; p.s_out = SL_Z;
+          } else {                    // P = Y_K sqrt(c), fp16 copy Y_K * s_Y
             p.A = ws_ref(F.Y[cb]); p.B = ws_ref(F.TT); p.sA = SL_Y; p.sB = SL_T;
-            p.out32 = ws_ref(F.R32); p.ld32 = F.d; p.cslot = F.s_sqrtc;
+            p.cslot = chain == 0 ? F.s_sqrtc : F.s_sqrtc2; p.s_out = SL_Y;
           }
           pu.push_back(p);
         }
-        add_gemm(L, pu, false, k < ks, cfg.factor_split);
+        add_gemm(L, pu, false, k < ks, 0);    // fp32 output only
+        // the stored root is symmetrised (the iteration's output is symmetric
+        // only up to rounding), and its fp16 copy written from the symmetric values
+        if (p16) add_sym(L, facs, pdst);
       }
     }
   }
@@ -810,8 +857,6 @@ struct Planner {
     return rounds < 4.0 && last > 0.0 && last <= 0.75;
   }
 
-  // P16 produced by the chain of this factor, in Z[K % 2]
-  size_t p16_of(const FacBufs& F) const { return F.Z[cfg.ns_steps & 1]; }
 
   // refresh: the launches of a step that recomputes the roots; otherwise the
   // roots are kept and the whitening uses the fp16 copies of the previous P.
@@ -825,6 +870,7 @@ struct Planner {
         for (FacBufs* f : {&mb.fa, &mb.fb}) {
           f->Y[0] += base; f->Y[1] += base; f->Z[0] += base; f->Z[1] += base; f->T += base; f->R32 += base;
           f->YT[0] += base; f->YT[1] += base; f->ZT[0] += base; f->ZT[1] += base; f->TT += base;
+          f->P16w += base;
         }
       }
       ws_bufs.emplace_back();
@@ -880,8 +926,8 @@ struct Planner {
       nn.kind = CA_NESTEROV; nn.src = user_ref(REF_M, mb.group, moff(mb)); nn.src_ld = mb.n;
       nn.src2 = user_ref(REF_G, mb.group, goff(mb)); nn.g_fmt = gfmt(mb); nn.write_m = 1;
       nn.rows = mb.m; nn.cols = mb.n; nn.dst_rows_p = mb.mp; nn.dst_cols_p = mb.np; nn.dst = ws_ref(mb.N16);
-      nn.dst_ld = mb.ldn; nn.dst_lo = mb.np; nn.parts = parts[per * q + 1]; nn.scale_mode = SC_ABSMAX;
-      nn.scale_slot = mb.s_n; nn.write_lo = fs;
+      nn.dst_ld = mb.ldnw; nn.dst_lo = mb.np; nn.parts = parts[per * q + 1]; nn.scale_mode = SC_ABSMAX;
+      nn.scale_slot = mb.s_n; nn.write_lo = wsplit();
       cs.push_back(nn);
       if (p_old) {
         const FacBufs* fl[2] = {&mb.fa, &mb.fb};
@@ -891,9 +937,9 @@ struct Planner {
           const FacBufs& F = *fl[s];
           CastSpec p = cast_spec();
           p.kind = CA_F32; p.src = user_ref(kinds[s], mb.group, offs[s]); p.src_ld = F.d;
-          p.rows = p.cols = F.d; p.dst_rows_p = p.dst_cols_p = F.dp; p.dst = ws_ref(F.T);
-          p.dst_ld = F.ld; p.dst_lo = F.dp; p.parts = parts[per * q + 2 + s]; p.scale_mode = SC_ABSMAX;
-          p.scale_slot = F.s_pold; p.write_lo = fs;
+          p.rows = p.cols = F.d; p.dst_rows_p = p.dst_cols_p = F.dp; p.dst = ws_ref(F.P16w);
+          p.dst_ld = F.ldw; p.dst_lo = F.dp; p.parts = parts[per * q + 2 + s]; p.scale_mode = SC_ABSMAX;
+          p.scale_slot = F.s_pold; p.write_lo = wsplit();
           cs.push_back(p);
         }
       }
@@ -915,12 +961,12 @@ struct Planner {
       std::vector<GemmProb> px;
       for (const MatBufs& mb : mats) {
         GemmProb p = prob();
-        p.A = ws_ref(mb.G16); p.lda = mb.ldn; p.B = ws_ref(mb.fb.T); p.ldb = mb.fb.ld;
+        p.A = ws_ref(mb.G16); p.lda = mb.ldn; p.B = ws_ref(mb.fb.P16w); p.ldb = mb.fb.ldw;
         p.M = mb.m; p.N = mb.n; p.Kp = mb.np; p.Mp = mb.mp; p.Np = mb.np; p.epi = EPI_STORE32;
         p.out32 = ws_ref(mb.Xa32); p.ld32 = mb.n; p.sA = mb.s_g; p.sB = mb.fb.s_pold;
         px.push_back(p);
         GemmProb r = prob();
-        r.A = ws_ref(mb.G16T); r.lda = mb.ldm; r.B = ws_ref(mb.fa.T); r.ldb = mb.fa.ld;
+        r.A = ws_ref(mb.G16T); r.lda = mb.ldm; r.B = ws_ref(mb.fa.P16w); r.ldb = mb.fa.ldw;
         r.M = mb.n; r.N = mb.m; r.Kp = mb.mp; r.Mp = mb.np; r.Np = mb.mp; r.epi = EPI_STORE32;
         r.out32 = ws_ref(mb.XbT32); r.ld32 = mb.m; r.sA = mb.s_g; r.sB = mb.fa.s_pold;
         px.push_back(r);
@@ -1007,12 +1053,14 @@ struct Planner {
         std::vector<Ref> cs, cp;
         for (size_t f : sets[c]) { cf.push_back(facs[f]); cs.push_back(src[f]); cp.push_back(pdst[f]); }
         if (okls_mode) {
-          ns_chain(chains[c], cf, cs, cp, 0, 0);
+          ns_chain(chains[c], cf, cs, cp, OUT_INV, true, 0);
         } else {
-          ns_chain(chains[c], cf, cs, cp, 1, 0);
+          // S^{-1/4} = (S^{-1/2})^{1/2}: the first chain's inverse root into
+          // R32, then the square root of sym(R32) into the caller's P
           std::vector<Ref> rsrc;
           for (FacBufs* f : cf) rsrc.push_back(ws_ref(f->R32));
-          ns_chain(chains[c], cf, rsrc, cp, 0, 1);
+          ns_chain(chains[c], cf, cs, rsrc, OUT_INV, false, 0);
+          ns_chain(chains[c], cf, rsrc, cp, OUT_SQRT, true, 1);
         }
         for (LaunchRec& r : chains[c]) r.stream = c;
       }
@@ -1034,9 +1082,10 @@ struct Planner {
         L.push_back(join);
       }
     }
-    // the fp16 preconditioner each whitening product reads: the chain's own
-    // output when the roots were just recomputed, else the copy cast above
-    auto pw = [&](const FacBufs& F) { return ws_ref(refresh ? p16_of(F) : F.T); };
+    // the fp16 preconditioner each whitening product reads: the symmetrised
+    // chain output's copy when the roots were just recomputed, else the copy
+    // cast above (both in P16w)
+    auto pw = [&](const FacBufs& F) { return ws_ref(F.P16w); };
     auto pw_scale = [&](const FacBufs& F) { return refresh ? F.s_p16 : F.s_pold; };
 
     // 6. whitening: V^T = P_b N^T (n x m), then U = P_a V fused with the update
@@ -1045,12 +1094,12 @@ struct Planner {
       std::vector<GemmProb> pv;
       for (const MatBufs& mb : mats) {
         GemmProb p = prob();
-        p.A = pw(mb.fb); p.lda = mb.fb.ld; p.B = ws_ref(mb.N16); p.ldb = mb.ldn;
+        p.A = pw(mb.fb); p.lda = mb.fb.ldw; p.B = ws_ref(mb.N16); p.ldb = mb.ldnw;
         p.M = mb.n; p.N = mb.m; p.Kp = mb.np; p.Mp = mb.np; p.Np = mb.mp; p.epi = EPI_STORE32;
         p.out32 = ws_ref(mb.VT32); p.ld32 = mb.m; p.sA = pw_scale(mb.fb); p.sB = mb.s_n;
         pv.push_back(p);
       }
-      add_gemm(L, pv, false, fs, 0);
+      add_gemm(L, pv, false, wsplit(), 0);
       std::vector<StatSpec> sv;
       for (const MatBufs& mb : mats) sv.push_back(StatSpec{ST_F32, ws_ref(mb.VT32), mb.m, no_ref(), 0, mb.n, mb.m});
       std::vector<std::pair<int, int>> pvp = add_stats(L, sv);
@@ -1059,21 +1108,21 @@ struct Planner {
         const MatBufs& mb = mats[q];
         CastSpec c = cast_spec();
         c.kind = CA_F32; c.src = ws_ref(mb.VT32); c.src_ld = mb.m; c.rows = mb.n; c.cols = mb.m;
-        c.dst_rows_p = mb.np; c.dst_cols_p = mb.mp; c.dst = ws_ref(mb.VT16); c.dst_ld = mb.ldm; c.dst_lo = mb.mp;
-        c.parts = pvp[q]; c.scale_mode = SC_ABSMAX; c.scale_slot = mb.s_vt; c.write_lo = fs;
+        c.dst_rows_p = mb.np; c.dst_cols_p = mb.mp; c.dst = ws_ref(mb.VT16); c.dst_ld = mb.ldmw; c.dst_lo = mb.mp;
+        c.parts = pvp[q]; c.scale_mode = SC_ABSMAX; c.scale_slot = mb.s_vt; c.write_lo = wsplit();
         cv.push_back(c);
       }
       add_cast(L, cv);
       std::vector<GemmProb> pu;
       for (const MatBufs& mb : mats) {
         GemmProb p = prob();
-        p.A = pw(mb.fa); p.lda = mb.fa.ld; p.B = ws_ref(mb.VT16); p.ldb = mb.ldm;
+        p.A = pw(mb.fa); p.lda = mb.fa.ldw; p.B = ws_ref(mb.VT16); p.ldb = mb.ldmw;
         p.M = mb.m; p.N = mb.n; p.Kp = mb.mp; p.Mp = mb.mp; p.Np = mb.np; p.epi = EPI_UPDATE;
         p.out32 = user_ref(REF_W, mb.group, moff(mb)); p.ld32 = mb.n; p.sA = pw_scale(mb.fa); p.sB = mb.s_vt;
         p.c0 = update_scale(mb);
         pu.push_back(p);
       }
-      add_gemm(L, pu, false, fs, 0);
+      add_gemm(L, pu, false, wsplit(), 0);
     }
     (refresh ? chunks : chunks_stale).push_back(std::move(L));
   }
@@ -1174,6 +1223,21 @@ struct Planner {
               if (!fits(p.aux, (static_cast<size_t>(p.M - 1) * p.ldaux + p.N) * 4)) return false;
             }
           }
+        } else if (r.type == L_SYM) {
+          int blk = 0;
+          if (r.first < 0 || r.first + r.count > static_cast<int>(sym_jobs.size())) return false;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const SymJob& y = sym_jobs[j];
+            if (y.blk_begin != blk || y.d < 1 || y.dp < y.d || y.dp % kSymTile || y.nt != y.dp / kSymTile) return false;
+            blk += y.nt * (y.nt + 1) / 2;
+            if (!fits(y.p, static_cast<size_t>(y.d) * y.d * 4)) return false;
+            if (y.dst16.kind != REF_NONE) {
+              const int need_ld = y.write_lo ? y.lo16 + y.dp : y.dp;
+              if (y.ld16 < need_ld || (y.write_lo && y.lo16 < y.dp) || !slot_ok(y.scale_slot)) return false;
+              if (!fits(y.dst16, static_cast<size_t>(y.dp) * y.ld16 * 2)) return false;
+            }
+          }
+          if (blk != r.nblocks) return false;
         } else if (r.type == L_STAT) {
           int blk = 0;
           for (int j = r.first; j < r.first + r.count; ++j) {
@@ -1272,7 +1336,7 @@ struct Planner {
 };
 
 struct WsLayout {
-  size_t probs = 0, tiles = 0, stat = 0, cast = 0, scal = 0, part = 0, flag = 0, chunk = 0, total = 0;
+  size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, scal = 0, part = 0, flag = 0, chunk = 0, total = 0;
 };
 
 WsLayout ws_layout(Planner& P) {
@@ -1285,6 +1349,7 @@ WsLayout ws_layout(Planner& P) {
   w.tiles = take(P.tiles.size() * sizeof(TileRef));
   w.stat = take(P.stat_jobs.size() * sizeof(StatJob));
   w.cast = take(P.cast_jobs.size() * sizeof(CastJob));
+  w.sym = take(P.sym_jobs.size() * sizeof(SymJob));
   w.scal = take(static_cast<size_t>(P.n_slots) * sizeof(float));
   w.part = take(static_cast<size_t>(P.max_partials) * 2 * sizeof(float) * kNsStreams);   // one region per stream
   w.flag = take(sizeof(int));
@@ -1333,13 +1398,14 @@ void okls_default_config(okls_config* c) {
   c->eps = 1e-9f;
   c->weight_decay = 0.0303f;
   c->lr_peak = 0.09434f;
-  c->ns_floor = 1e-3f;
-  c->ns_damping = 5e-3f;
+  c->ns_floor = 3e-2f;
+  c->ns_damping = 0.0f;
   c->root_period = 1;
   c->eps_convex = 0;
   c->decay_after = 0;
   c->shape_scale = 1;
   c->ns_classical = 0;
+  c->whiten_split = 1;
 }
 
 size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups) {
@@ -1367,7 +1433,7 @@ okls_status okls_plan_query(const okls_config* cfg, int n_groups, const okls_gro
   auto kernels = [](const std::vector<std::vector<LaunchRec>>& cs) {
     int n = 0;
     for (const std::vector<LaunchRec>& L : cs)
-      for (const LaunchRec& r : L) n += (r.type == L_STAT || r.type == L_CAST || r.type == L_GEMM);
+      for (const LaunchRec& r : L) n += (r.type == L_STAT || r.type == L_CAST || r.type == L_GEMM || r.type == L_SYM);
     return n;
   };
   info.chunks = static_cast<int>(P.chunks.size());
@@ -1434,6 +1500,7 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_tiles = w.tiles;
   h->off_stat = w.stat;
   h->off_cast = w.cast;
+  h->off_sym = w.sym;
   h->off_scal = w.scal;
   h->off_part = w.part;
   h->off_flag = w.flag;
@@ -1482,6 +1549,7 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   up(w.tiles, P.tiles.data(), P.tiles.size() * sizeof(TileRef));
   up(w.stat, P.stat_jobs.data(), P.stat_jobs.size() * sizeof(StatJob));
   up(w.cast, P.cast_jobs.data(), P.cast_jobs.size() * sizeof(CastJob));
+  up(w.sym, P.sym_jobs.data(), P.sym_jobs.size() * sizeof(SymJob));
   up(w.scal, scal.data(), scal.size() * sizeof(float));
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
@@ -1630,6 +1698,14 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.ws = ws;
         a.user = user;
         e = launch_cast(a, r.nblocks, rs);
+      } else if (r.type == L_SYM) {
+        SymArgs a;
+        a.jobs = reinterpret_cast<const SymJob*>(ws + h->off_sym) + r.first;
+        a.n_jobs = r.count;
+        a.scal = scal;
+        a.ws = ws;
+        a.user = user;
+        e = launch_sym(a, r.nblocks, rs);
       } else {
         GemmArgs a;
         a.probs = reinterpret_cast<const GemmProb*>(ws + h->off_probs);

@@ -26,6 +26,7 @@ struct InitArgs {
 hipError_t launch_gemm(const GemmArgs& a, int n_tiles, int tile, int epi, hipStream_t s);  // tile 128 or 256; epi: the launch's (single) Epi kind
 hipError_t launch_stats(const StatArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_cast(const CastArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_sym(const SymArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_init_state(const InitArgs& a, int n_jobs, hipStream_t s);
 hipError_t launch_check_finite(const InitArgs& a, int n_jobs, int* flag_dev, hipStream_t s);
 

@@ -227,7 +227,7 @@ __device__ __forceinline__ void epilogue_f32(const floatx16 (&acc)[C::GI][C::GJ]
   using S32 = Stage32<C>;
   float* lds = reinterpret_cast<float*>(x.lds0);
   const int lane = threadIdx.x & 63;
-  const bool vec_ok = (x.ld32 & 3) == 0;
+  const bool vec_ok = x.out32_vec;    // 16-byte rows: stride and base pointer both aligned
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     // stage rows [h HR, (h + 1) HR) of the wave's region
@@ -996,7 +996,7 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
       if (J.cinv_slot >= 0) a.scal[J.cinv_slot] = cinv;
       if (J.rho_slot >= 0) a.scal[J.rho_slot] = 1.0f / sqrtf(c);
       if (J.sqrtc_slot >= 0) a.scal[J.sqrtc_slot] = sqrtf(c);
-      if (J.p16_slot >= 0) a.scal[J.p16_slot] = J.p16_static * sqrtf(c);
+      if (J.p16_slot >= 0) a.scal[J.p16_slot] = J.p16_inv_sqrt ? J.p16_static / sqrtf(c) : J.p16_static * sqrtf(c);
     }
     if (sym_fast) {
       // x <- (x + mirrored^T) / 2: mirrored row i (0..255), column j (0..63)
@@ -1109,6 +1109,56 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Root symmetrisation (SymJob): the block of pair (I, J) loads tiles (I, J)
+// and (J, I), then writes (A + B^T) / 2 to the first and its transpose to the
+// second, row by row, with the fp16 copy at the same positions.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSymThreads) void sym_kernel(SymArgs a) {
+  __shared__ float tA[kSymTile][kSymTile + 1], tB[kSymTile][kSymTile + 1];
+  const int gb = blockIdx.x;
+  const SymJob J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
+  int lb = gb - J.blk_begin;
+  int ti = 0;                                  // pairs (ti, tj), tj >= ti, row by row
+  while (lb >= J.nt - ti) {
+    lb -= J.nt - ti;
+    ++ti;
+  }
+  const int tj = ti + lb;
+  float* P = reinterpret_cast<float*>(resolve(J.p, a.ws, a.user));
+  const size_t d = static_cast<size_t>(J.d);
+  const int r0 = ti * kSymTile, c0 = tj * kSymTile;
+  for (int k = threadIdx.x; k < kSymTile * kSymTile; k += kSymThreads) {
+    const int r = k / kSymTile, c = k % kSymTile;
+    const bool in_a = r0 + r < J.d && c0 + c < J.d, in_b = c0 + r < J.d && r0 + c < J.d;
+    tA[r][c] = in_a ? P[(r0 + r) * d + c0 + c] : 0.0f;
+    tB[r][c] = in_b ? P[(c0 + r) * d + r0 + c] : 0.0f;
+  }
+  __syncthreads();
+  half_t* dst = J.dst16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(J.dst16, a.ws, a.user)) : nullptr;
+  const float sc = dst != nullptr ? a.scal[J.scale_slot] : 1.0f;
+  auto put = [&](size_t gr, size_t gc, float v) {
+    if (gr < d && gc < d) P[gr * d + gc] = v;
+    if (dst != nullptr) {
+      const float y = v * sc;
+      const half_t h = static_cast<half_t>(y);
+      half_t* q = dst + gr * J.ld16 + gc;
+      q[0] = h;
+      if (J.write_lo) q[J.lo16] = static_cast<half_t>(y - static_cast<float>(h));
+    }
+  };
+  // positions beyond d (the copy's padding) get zeros: the tiles hold zeros there
+  for (int k = threadIdx.x; k < kSymTile * kSymTile; k += kSymThreads) {
+    const int r = k / kSymTile, c = k % kSymTile;
+    put(r0 + r, c0 + c, 0.5f * (tA[r][c] + tB[c][r]));
+  }
+  if (ti == tj) return;
+  for (int k = threadIdx.x; k < kSymTile * kSymTile; k += kSymThreads) {
+    const int r = k / kSymTile, c = k % kSymTile;
+    put(c0 + r, r0 + c, 0.5f * (tB[r][c] + tA[c][r]));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // State initialisation and finiteness scan
 // ---------------------------------------------------------------------------
 __global__ void init_state_kernel(InitArgs a) {
@@ -1181,6 +1231,12 @@ hipError_t launch_stats(const StatArgs& a, int n_blocks, hipStream_t s) {
 hipError_t launch_cast(const CastArgs& a, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(cast_kernel, dim3(n_blocks), dim3(kCastThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sym(const SymArgs& a, int n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sym_kernel, dim3(n_blocks), dim3(kSymThreads), 0, s, a);
   return hipGetLastError();
 }
 

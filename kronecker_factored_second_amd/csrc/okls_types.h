@@ -157,8 +157,13 @@ struct CastJob {
   int32_t cinv_slot;       // CA_NS_*: writes 1/c here (if >= 0)
   int32_t rho_slot;        // CA_NS_*: writes 1/sqrt(c) here (if >= 0)
   int32_t sqrtc_slot;      // CA_NS_*: writes sqrt(c) here (if >= 0)
-  int32_t p16_slot;        // CA_NS_*: writes s_Z*sqrt(c) here (if >= 0): scale of the root's fp16 copy
-  float p16_static;        // s_Z
+  int32_t p16_slot;        // CA_NS_*: writes the scale of the root's fp16 copy here (if >= 0):
+                           // p16_static * sqrt(c) (inverse root, copy Z_K s_Z / 16), or
+                           // p16_static / sqrt(c) with p16_inv_sqrt (square root, copy Y_K s_Y)
+  float p16_static;        // s_Z / 16 (headroom for directions the iteration does not
+                           // resolve, which can leave the last step above the iterates'
+                           // bound), or s_Y with p16_inv_sqrt
+  int32_t p16_inv_sqrt;
   float damp;              // CA_NS_*: delta; the chain roots (S + delta c I) / (c (1 + delta))
   int32_t sym_read;        // CA_NS_*: 1 = read (S + S^T) / 2 (source not exactly symmetric)
   int32_t tiles_x;         // blocks along destination columns (kCastCols each)
@@ -178,6 +183,32 @@ struct CastArgs {
   const float* partials;
   float* scal;
   float beta1, s_t, ka, kb;
+  char* ws;
+  UserPtrs user;
+};
+
+// ---------------------------------------------------------------------------
+// Symmetrisation of a computed root in place, P <- (P + P^T) / 2, with its
+// fp16 copy (static scale): one block per pair of kSymTile x kSymTile tiles
+// (I, J), I <= J, so every element pair is read and written by one block.
+// ---------------------------------------------------------------------------
+constexpr int kSymTile = 64;
+constexpr int kSymThreads = 256;
+
+struct SymJob {
+  Ref p;                   // fp32 d x d, row stride d
+  int32_t d, dp;           // side and padded side of the fp16 copy (a multiple of kSymTile)
+  int32_t nt;              // tiles per padded side, dp / kSymTile; the copy gets zeros beyond d
+  Ref dst16;               // the fp16 copy (dp rows of ld16 halves, lo at +lo16), or REF_NONE
+  int32_t ld16, lo16, write_lo;
+  int32_t scale_slot;      // the copy's scale
+  int32_t blk_begin;
+};
+
+struct SymArgs {
+  const SymJob* jobs;
+  int32_t n_jobs;
+  const float* scal;
   char* ws;
   UserPtrs user;
 };

@@ -33,7 +33,7 @@ class Config(ctypes.Structure):
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("lr_peak", ctypes.c_float),
                 ("ns_floor", ctypes.c_float), ("ns_damping", ctypes.c_float), ("root_period", ctypes.c_int32),
                 ("eps_convex", ctypes.c_int32), ("decay_after", ctypes.c_int32), ("shape_scale", ctypes.c_int32),
-                ("ns_classical", ctypes.c_int32)]
+                ("ns_classical", ctypes.c_int32), ("whiten_split", ctypes.c_int32)]
 
 
 class GroupDesc(ctypes.Structure):
@@ -125,12 +125,14 @@ def default_config(**overrides) -> Config:
 
 
 def precision_config(precision: str = "fp16", **overrides) -> Config:
-    """'fp16': every GEMM with plain fp16 inputs (the pages' path).
-    'fp32': every GEMM split-fp16 (hi*hi + hi*lo + lo*hi), fp32-accurate."""
+    """'fp16': the Newton-Schulz and factor GEMMs with plain fp16 inputs (the
+    pages' path), the whitening products split-fp16 (whiten_split).
+    'fp32': every GEMM split-fp16 (hi*hi + hi*lo + lo*hi), fp32-accurate.
+    Each takes the coefficient table's floor matched to its arithmetic."""
     if precision == "fp16":
-        base = dict(ns_split_steps=0, factor_split=0, ns_damping=5e-3)
+        base = dict(ns_split_steps=0, factor_split=0, whiten_split=1, ns_floor=3e-2, ns_damping=0.0)
     elif precision == "fp32":
-        base = dict(ns_split_steps=-1, factor_split=1, ns_damping=2e-3)
+        base = dict(ns_split_steps=-1, factor_split=1, whiten_split=1, ns_floor=1e-3, ns_damping=0.0)
     else:
         raise ValueError(precision)
     base.update(overrides)
@@ -346,12 +348,14 @@ class OKLS:
         return tensors_array(per)
 
     def step(self, grads=None, lr=None):
-        if lr is not None:
-            self.lr = float(lr)
+        lr = self.lr if lr is None else float(lr)
         self.stream = self.torch.cuda.current_stream(self.params[0].device).cuda_stream
         tensors = self._tensors(grads, check=True)
+        # the counter and the learning rate change only once the library has
+        # accepted the step
+        step(self.handle, tensors, self.t + 1, lr, self.stream)
         self.t += 1
-        step(self.handle, tensors, self.t, self.lr, self.stream)
+        self.lr = lr
 
     def zero_grad(self):
         for p in self.params:
@@ -369,6 +373,17 @@ class OKLS:
         # lr_peak is part of the handle's configuration (the AdamC correction)
         if abs(float(sd["lr_peak"]) - float(self.cfg.lr_peak)) > 1e-6 * abs(float(self.cfg.lr_peak)):
             raise ValueError(f"state was saved with lr_peak {sd['lr_peak']}, this optimizer has {self.cfg.lr_peak}")
+        # every tensor is checked before anything is copied, so a mismatched
+        # checkpoint leaves this optimizer untouched
+        if len(sd["state"]) != len(self.state):
+            raise ValueError(f"state holds {len(sd['state'])} parameters, this optimizer has {len(self.state)}")
+        for i, (dst, src) in enumerate(zip(self.state, sd["state"])):
+            if set(src) != set(dst):
+                raise ValueError(f"parameter {i}: state keys {sorted(src)}, expected {sorted(dst)}")
+            for k, v in src.items():
+                if tuple(v.shape) != tuple(dst[k].shape) or v.dtype != dst[k].dtype:
+                    raise ValueError(f"parameter {i} {k}: {tuple(v.shape)} {v.dtype}, "
+                                     f"expected {tuple(dst[k].shape)} {dst[k].dtype}")
         self.t = int(sd["t"])
         self.lr = float(sd["lr"])
         for dst, src in zip(self.state, sd["state"]):

@@ -84,8 +84,9 @@ class Hyper:
     lr_peak: float | None = None        # [OKLS] "Learning-rate schedule": the initial lr is kept as lr_peak
     nesterov_var_corr: bool = True      # R5
     ns_steps: int = 10                  # [OKLS] intro: 10-step inverse-root method
-    ns_floor: float = 1e-3              # R4: lower end of the design interval for sqrt(lambda / ||S||_F)
-    ns_damping: float = 5e-3            # R13: nu; the iteration roots S + (nu/sqrt(d)) ||S||_F I
+    ns_floor: float = 3e-2              # R4: lower end of the design interval for sqrt(lambda / ||S||_F)
+                                        # (the fp16 path's; 1e-3 for the fp32-accurate path)
+    ns_damping: float = 0.0             # R13: nu; the iteration roots S + (nu/sqrt(d)) ||S||_F I
     root_period: int = 1                # roots refreshed on steps 1, 1 + p, 1 + 2p, ... (R15)
     eps_convex: bool = False            # R1 alternative: OKLS factors get (1-beta2) eps I per update
     decay_after: bool = False           # R6 alternative: decay applied after the update
@@ -301,14 +302,15 @@ def ns_inv_sqrt(S: np.ndarray, coeffs, nu: float = 0.0):
 
 
 def ns_inv_quarter(S: np.ndarray, coeffs, nu: float = 0.0):
-    """S^{-1/4} as two chained inverse-square-root iterations (R8):
-    R = S^{1/2} from the first chain's Y output, then P = R^{-1/2}."""
-    _, R = ns_inv_sqrt(S, coeffs, nu)
-    P, _ = ns_inv_sqrt(_sym(R), coeffs, nu)
+    """S^{-1/4} = (S^{-1/2})^{1/2} as two chained iterations (R8): the first
+    chain's Z output P1 = S^{-1/2}, then the square root of sym(P1) from the
+    second chain's Y output."""
+    P1, _ = ns_inv_sqrt(S, coeffs, nu)
+    _, P = ns_inv_sqrt(_sym(P1), coeffs, nu)
     return P
 
 
-def ns_spectral(lam: np.ndarray, coeffs, nu: float = 0.0, p: int = 2):
+def ns_spectral(lam: np.ndarray, coeffs, nu: float = 0.0, p: int = 2, out: str = "inv"):
     """Exact-arithmetic output of the damped coupled iteration(s) on a
     symmetric matrix with eigenvalues `lam`, one value per eigen-direction.
 
@@ -318,10 +320,10 @@ def ns_spectral(lam: np.ndarray, coeffs, nu: float = 0.0, p: int = 2):
     eigen-direction Z_k Y_k = sigma_k^2 with sigma_0 = sqrt(y) and
     sigma_{k+1} = sigma_k (a_k + b_k sigma_k^2); Z_K = sigma_K / sqrt(y) and
     Y_K = sigma_K sqrt(y).  Hence the chain returns
-        P = Z_K / sqrt(c') = sigma_K / sqrt(lam + delta c)
-        R = Y_K sqrt(c')  = sigma_K sqrt(lam + delta c).
-    p = 2 returns P; p = 4 (R8) runs a second chain on R's eigenvalues and
-    returns its P."""
+        P = Z_K / sqrt(c') = sigma_K / sqrt(lam + delta c)    (out='inv')
+        R = Y_K sqrt(c')  = sigma_K sqrt(lam + delta c)      (out='sqrt').
+    p = 2 returns that chain's output; p = 4 (R8) runs a second chain on
+    the first chain's P eigenvalues and returns its R."""
     lam = np.asarray(lam, dtype=np.float64)
     d = lam.size
     delta = nu / math.sqrt(d)
@@ -331,9 +333,9 @@ def ns_spectral(lam: np.ndarray, coeffs, nu: float = 0.0, p: int = 2):
     for a, b in coeffs:
         s = s * (a + b * s * s)
     if p == 2:
-        return s / np.sqrt(shifted)
+        return s / np.sqrt(shifted) if out == "inv" else s * np.sqrt(shifted)
     if p == 4:
-        return ns_spectral(s * np.sqrt(shifted), coeffs, nu, 2)
+        return ns_spectral(s / np.sqrt(shifted), coeffs, nu, 2, "sqrt")
     raise ValueError("p must be 2 or 4")
 
 

@@ -30,6 +30,7 @@ int main(int argc, char** argv) {
     c.decay_after = uni(0, 1);
     c.shape_scale = uni(0, 1);
     c.ns_classical = uni(0, 1);
+    c.whiten_split = uni(0, 1);
     const int ng = uni(1, 16);
     std::vector<okls_group_desc> g(ng);
     for (okls_group_desc& d : g) {

@@ -89,11 +89,13 @@ def test_workspace_size_validation():
     for gdt in (okls.OKLS_F32, okls.OKLS_BF16, okls.OKLS_F16):    # fp32, bf16, fp16 gradients
         assert okls.workspace_size(c, [(1, 128, 256, gdt)]) > 0
     assert okls.workspace_size(c, [(1, 8, 8, 0)] * 17) == 0       # too many groups
-    for k in ("eps_convex", "decay_after", "shape_scale", "ns_classical"):   # the reading switches are 0 or 1
+    for k in ("eps_convex", "decay_after", "shape_scale", "ns_classical", "whiten_split"):   # switches are 0 or 1
         assert okls.workspace_size(okls.default_config(**{k: 2}), [(1, 8, 8, 0)]) == 0
         assert okls.workspace_size(okls.default_config(**{k: 1}), [(1, 8, 8, 0)]) > 0
     d = okls.default_config()
-    assert (d.eps_convex, d.decay_after, d.shape_scale, d.ns_classical) == (0, 0, 1, 0)
+    assert (d.eps_convex, d.decay_after, d.shape_scale, d.ns_classical, d.whiten_split) == (0, 0, 1, 0, 1)
+    # the fp16 path's defaults: the table's floor matched to fp16, no damping
+    assert abs(d.ns_floor - 3e-2) < 1e-9 and d.ns_damping == 0.0
     a, b = okls.ns_coefficients(okls.default_config(ns_classical=1, ns_steps=12))
     assert a == [1.5] * 12 and b == [-0.5] * 12
     bad = okls.default_config(ns_steps=1)

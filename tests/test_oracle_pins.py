@@ -327,12 +327,13 @@ def test_ns_spectral_within_coefficient_bound_of_shifted_root():
     shift = nu / math.sqrt(lam.size) * np.linalg.norm(lam)
     f = O.ns_spectral(lam, coeffs, nu, 2)
     np.testing.assert_array_less(np.abs(f * np.sqrt(lam + shift) - 1.0), efin * (1 + 1e-9))
-    # p = 4: the second chain roots R = (S + shift)^{1/2} shifted by its own
-    # nu / sqrt(d) ||R||_F; each chain contributes at most efin
-    r = np.sqrt(lam + shift)
+    # p = 4: the second chain takes the square root of R = (S + shift)^{-1/2}
+    # shifted by its own nu / sqrt(d) ||R||_F; each chain contributes at most
+    # efin (the first one's relative error halves under the square root)
+    r = 1.0 / np.sqrt(lam + shift)
     shift2 = nu / math.sqrt(lam.size) * np.linalg.norm(r)
     f4 = O.ns_spectral(lam, coeffs, nu, 4)
-    np.testing.assert_array_less(np.abs(f4 * np.sqrt(r + shift2) - 1.0), 2.5 * efin)
+    np.testing.assert_array_less(np.abs(f4 / np.sqrt(r + shift2) - 1.0), 2.5 * efin)
 
 
 def test_ns_damped_isotropic():
