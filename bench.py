@@ -2,11 +2,12 @@
 
 One step = one okls_step over every matrix of the workload (factor updates,
 10-step Newton-Schulz roots, whitening, momentum and the weight update).
-Default workload: one d=1024 transformer block (q, k, v, o 1024x1024;
-gate/up 2816x1024; down 1024x2816) with bf16 gradients 0.02*N(0,1) scaled
-per row by log-uniform[0.1, 10], OKLS defaults, fp16 GEMM inputs with fp32
-accumulation.  Gradients are generated once and kept resident in HBM; the
-timed steps cycle through them.
+Default workload: the 1.2B-class model's optimizer step, 24 layers of
+{4x 2048x2048, 2x 5632x2048, 1x 2048x5632} (168 matrices, 1.23e9
+parameters), fp32 gradients 0.02*(sqrt(0.9) rank-32 + sqrt(0.1) noise)
+generated on the device, OKLS defaults, fp16 Newton-Schulz and factor GEMM
+inputs with fp32 accumulation.  Gradients are generated once and kept
+resident in HBM; the timed steps cycle through them.
 
 Prints one JSON line: matrices/s, step latency, the dominant kernel's
 roofline (gemm_nt_kernel: algorithmic FLOPs over the union of its launches'
@@ -34,7 +35,8 @@ PEAK_HBM_GBS = 8000.0
 # the GEMM's traffic depends on its kernel and on the planner's launch shapes
 KERNEL_SRCS = [os.path.join(ROOT, "kronecker_factored_second_amd", "csrc", f)
                for f in ("okls_kernels.hip", "okls_types.h", "okls_api.cpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_kernel_c2_fp16_hbm_traffic.txt")
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"gemm_nt_kernel_{workload}_fp16_hbm_traffic.txt")
 COPY_PROBE_BYTES = 1 << 30
 
 
@@ -51,10 +53,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c2")
+    p.add_argument("--workload", default="c3")
     p.add_argument("--precision", default="fp16", choices=["fp16", "fp32"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    p.add_argument("--cpu-sample-seconds", type=float, default=90.0)
     p.add_argument("--device-grads", action="store_true",
                    help="Gaussian gradients of the workload's scale generated on the GPU (the default for "
                         "workloads above 1e9 parameters, whose host recipes would take minutes per step)")
@@ -66,7 +68,7 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 10 times (HBM counter calibration)")
     p.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV_DIR", "WRITE_CSV_DIR", "COMMANDS"),
-                   help="write the GEMM's HBM traffic summary from two rocprofv3 --pmc runs")
+                   help="write the GEMM's HBM traffic summary of --workload from two rocprofv3 --pmc runs")
     return p.parse_args()
 
 
@@ -95,7 +97,7 @@ def _counter_rows(d, counter, prefix):
     return out
 
 
-def summarize_counters(fetch_dir, write_dir, commands):
+def summarize_counters(fetch_dir, write_dir, commands, workload):
     """HBM bytes per gemm_nt_kernel launch from FETCH_SIZE / WRITE_SIZE (KiB
     per dispatch) of the benchmark run ('bench' files), each scaled by the
     factor that makes the counter of the plain 1 GiB copy ('copy' files, the
@@ -122,9 +124,11 @@ def summarize_counters(fetch_dir, write_dir, commands):
         ow, _ = avg(write_dir, "WRITE_SIZE", "bench", lambda k: kern in k)
         others.append(f"{kern}_hbm_bytes_per_launch {of * 1024.0 * kf + ow * 1024.0 * kw:.6e} "
                       f"(fetch {of * 1024.0 * kf:.4e}, write {ow * 1024.0 * kw:.4e}, {nof} dispatches)")
+    from kronecker_factored_second_amd import workloads as WL
+    w = WL.workload(workload)
     lines = [
         "# HBM traffic of gemm_nt_kernel (both block tiles, every launch of a step),",
-        "# one d=1024 transformer block (4x 1024x1024, 2x 2816x1024, 1x 1024x2816), fp16 path",
+        f"# workload {w.name}: " + ", ".join(f"{b}x {m}x{n}" for m, n, b in w.groups) + ", fp16 path",
         f"# kernel_source_sha256_16 {kernel_source_hash()} (okls_kernels.hip, okls_types.h, okls_api.cpp)",
         "# commands (repository root as $REPO, output directory OUT; cd /tmp first):",
         *[f"#   {c.strip()}" for c in commands.split(";")],
@@ -136,16 +140,18 @@ def summarize_counters(fetch_dir, write_dir, commands):
         f"gemm_hbm_bytes_per_launch {traffic:.6e}",
         *others,
     ]
-    open(TRAFFIC_FILE, "w").write("\n".join(lines) + "\n")
+    open(traffic_file(workload), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def measured_traffic():
-    """HBM bytes per GEMM launch from the committed counter summary, or None
-    when it is missing or was taken on another version of the kernels."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed counter summary of this
+    workload, or None when it is missing or was taken on another version of
+    the kernels."""
+    f = traffic_file(workload)
+    if not os.path.exists(f):
         return None
-    txt = open(TRAFFIC_FILE).read()
+    txt = open(f).read()
     if f"kernel_source_sha256_16 {kernel_source_hash()} " not in txt:
         return None
     for line in txt.splitlines():
@@ -163,8 +169,11 @@ def cpu_baseline(w, budget_s, root_period=1, mode=None):
     """The fp64 oracle, as it stands, on a bounded sample: one matrix of each
     distinct shape class of the workload, a full oracle step each (exact eigh
     roots plus the fp64 Newton-Schulz iteration), scaled to the whole
-    workload's matrix counts.  With a root period p > 1 the step that keeps
-    the roots is timed too and the two are averaged over one period."""
+    workload's matrix counts.  An m x n class and its n x m transpose run the
+    same products and eigendecompositions (the same two factor sides), so the
+    second takes the first one's time.  With a root period p > 1 the step
+    that keeps the roots is timed too and the two are averaged over one
+    period."""
     from oracle import okls_oracle as O
     from kronecker_factored_second_amd import workloads as WL
     blas = "unknown"
@@ -185,7 +194,13 @@ def cpu_baseline(w, budget_s, root_period=1, mode=None):
     mode = mode or w.mode
     hp = O.muon_hyper() if mode == "muon" else O.Hyper(root_period=root_period)
     total_s, sampled, step_s = 0.0, [], 0.0
+    timed = {}
     for gi, (m, n, b) in enumerate(w.groups):
+        key = (min(m, n), max(m, n))
+        if key in timed:
+            sampled.append(f"{m}x{n}: as {timed[key][0]}")
+            step_s += timed[key][1] * b
+            continue
         G = WL.gradient(w, gi, 0, 1).astype(np.float64)
         st = O.init_state(np.zeros((m, n)), hp.eps)
         t0 = time.perf_counter()
@@ -199,6 +214,7 @@ def cpu_baseline(w, budget_s, root_period=1, mode=None):
             total_s += dt2
             dt = (dt + (root_period - 1) * dt2) / root_period
         sampled.append(f"{m}x{n}:{dt:.2f}s")
+        timed[key] = (f"{m}x{n}", dt)
         step_s += dt * b
         if total_s > budget_s:
             step_s = None
@@ -214,7 +230,7 @@ def cpu_baseline(w, budget_s, root_period=1, mode=None):
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the preconditioner step runs on a single MI355X; "
@@ -246,7 +262,9 @@ def main():
     for t in range(1, n_bufs + 1):
         gs = []
         for gi, (m, n, b) in enumerate(w.groups):
-            if device_grads:
+            if device_grads and w.grad == "lowrank":      # the recipe itself, on the device
+                g = WL.device_lowrank((b, m, n), seed_fixed=(1 << 16) + gi, seed_t=(t << 8) + gi, scale=scale)
+            elif device_grads:
                 g = WL.device_filler(scale, (b, m, n), seed=(t << 8) + gi)
             else:
                 g = torch.from_numpy(np.stack([WL.gradient(w, gi, i, t) for i in range(b)])).to(dev)
@@ -348,8 +366,8 @@ def main():
                      "ms_per_step": ns["busy_ms"] / max(prof["steps"], 1), "launches_per_step": ns["launches"] / max(prof["steps"], 1)},
         "roofline": {"kernel": "gemm_nt_kernel", "bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS,
-                     "traffic": measured_traffic() if (args.workload == "c2" and args.precision == "fp16" and
-                                                       mode == "okls" and args.root_period == 1) else None,
+                     "traffic": measured_traffic(args.workload) if (args.precision == "fp16" and mode == w.mode and
+                                                                    args.root_period == 1) else None,
                      "method": "algorithmic FLOPs of every gemm_nt_kernel launch over the union of their intervals, "
                                "from HIP events on the launch streams in a second pass of the same steps (the timed "
                                "pass runs without them); where the plan runs two Newton-Schulz chains their launches overlap",

@@ -207,6 +207,28 @@ def device_filler(scale: float, shape, seed: int, dtype=None):
     return x if dtype is None else x.to(dtype)
 
 
+def device_lowrank(shape, seed_fixed: int, seed_t: int, scale: float = 0.02, rank: int = 32):
+    """The low-rank workload's recipe generated on cuda:0 (torch's seeded
+    generator) for a whole (b, m, n) group: per matrix
+    scale * (sqrt(0.9) L + sqrt(0.1) Z), L = A C B^T normalised to unit RMS,
+    with A (m x rank) and B (n x rank) Gaussian fixed by seed_fixed and C
+    (rank x rank) and Z fresh from seed_t.  The benchmark uses it for the
+    1.2B-class workload, whose host recipe takes minutes per step."""
+    import torch
+    b, m, n = shape
+    gf = torch.Generator(device="cuda:0")
+    gf.manual_seed(seed_fixed)
+    A = torch.randn(b, m, rank, generator=gf, device="cuda:0")
+    B = torch.randn(b, n, rank, generator=gf, device="cuda:0")
+    gt = torch.Generator(device="cuda:0")
+    gt.manual_seed(seed_t)
+    C = torch.randn(b, rank, rank, generator=gt, device="cuda:0")
+    L = torch.bmm(torch.bmm(A, C), B.transpose(1, 2).contiguous())
+    L = L / torch.sqrt(torch.mean(L * L, dim=(1, 2), keepdim=True))
+    Z = torch.randn(b, m, n, generator=gt, device="cuda:0")
+    return scale * (math.sqrt(0.9) * L + math.sqrt(0.1) * Z)
+
+
 def gradient(w: Workload, group: int, mat: int, t: int) -> np.ndarray:
     """fp32 array (m, n) holding the gradient of matrix `mat` of shape group
     `group` at step t (1-based).  bf16 workloads return bf16-representable
