@@ -197,6 +197,25 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups,
                       const okls_group_desc* groups, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): okls_init
+ * with the library's own static device scratch as the workspace, so the
+ * caller passes only its tensors.  The scratch is OKLS_STATIC_SCRATCH_BYTES
+ * per device, held by the library until the process ends; groups whose
+ * okls_workspace_size exceeds it return OKLS_ERR_WORKSPACE (set
+ * chunk_matrices to fit).  Nothing is allocated on the device: the plan runs
+ * one Newton-Schulz chain (no side stream or event), and the handle holds
+ * host memory only.  Every static handle on a device shares that device's
+ * scratch, which keeps the last init's tables: a static handle is valid
+ * until the next okls_init_static on the same device, and steps of static
+ * handles that overlap on one device race.  Nothing in the scratch is
+ * assumed zero: every step writes each buffer before reading it.  Results
+ * are bit-identical to okls_init with a workspace.  Synchronises `stream`
+ * once (table upload). */
+#define OKLS_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+okls_status okls_init_static(okls_handle** out, const okls_config* cfg, int n_groups,
+                             const okls_group_desc* groups, void* stream);
+
 /* Fills the state for a fresh start (README "Hyperparameters": eps at factor
  * initialisation): S = eps I, P = I, M = 0 (Muon mode: M = 0 only).  W and G
  * are not touched (may be NULL).  `tensors` points to n_groups entries.

@@ -235,6 +235,7 @@ struct Planner {
   bool okls_mode;
   bool muon_mode;
   bool lo_layout;
+  bool single_chain = false;   // never plan a second Newton-Schulz chain (no side stream)
   std::vector<double> na, nb;
   float sY = 0, sZ = 0, sT = 0;
 
@@ -1038,7 +1039,7 @@ struct Planner {
       std::vector<size_t> order(facs.size());
       for (size_t f = 0; f < order.size(); ++f) order[f] = f;
       std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return facs[x]->d > facs[y]->d; });
-      const int nset = two_chains_pay(facs) ? std::min<int>(kNsStreams, static_cast<int>(facs.size())) : 1;
+      const int nset = (!single_chain && two_chains_pay(facs)) ? std::min<int>(kNsStreams, static_cast<int>(facs.size())) : 1;
       std::vector<double> load(nset, 0.0);
       std::vector<std::vector<size_t>> sets(nset);
       for (size_t f : order) {
@@ -1466,8 +1467,9 @@ int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_s
   return cfg->ns_steps;
 }
 
-okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, const okls_group_desc* groups,
-                      void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, const okls_group_desc* groups,
+                      void* workspace, size_t ws_bytes, void* stream, bool single_chain) {
   if (out == nullptr) return OKLS_ERR_INVALID_ARG;
   *out = nullptr;
   okls_status st = check_config(cfg);
@@ -1479,11 +1481,13 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
 
   std::vector<okls_group_desc> g(groups, groups + n_groups);
   Planner sizing(*cfg, g);
+  sizing.single_chain = single_chain;
   const WsLayout w = ws_layout(sizing);
   if (ws_bytes < w.total) return OKLS_ERR_WORKSPACE;
 
   // plan again with the real chunk base
   Planner P(*cfg, g);
+  P.single_chain = single_chain;
   P.plan(w.chunk);
   if (!P.validate() || P.probs.size() != sizing.probs.size() || P.chunk_bytes != sizing.chunk_bytes)
     return OKLS_ERR_UNSUPPORTED;
@@ -1558,6 +1562,29 @@ okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, c
   }
   *out = h;
   return OKLS_OK;
+}
+}  // namespace
+
+okls_status okls_init(okls_handle** out, const okls_config* cfg, int n_groups, const okls_group_desc* groups,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  return init_impl(out, cfg, n_groups, groups, workspace, ws_bytes, stream, false);
+}
+
+// The workspace is the library's static device scratch; the plan runs one
+// Newton-Schulz chain, so no side stream or event is created, and nothing
+// is allocated on the device.
+okls_status okls_init_static(okls_handle** out, const okls_config* cfg, int n_groups,
+                             const okls_group_desc* groups, void* stream) {
+  if (out == nullptr) return OKLS_ERR_INVALID_ARG;
+  *out = nullptr;
+  okls_status st = check_config(cfg);
+  if (st != OKLS_OK) return st;
+  st = check_groups(n_groups, groups);
+  if (st != OKLS_OK) return st;
+  if (okls_workspace_size(cfg, n_groups, groups) > kStaticScratchBytes) return OKLS_ERR_WORKSPACE;
+  void* ptr = nullptr;
+  if (static_scratch(&ptr) != hipSuccess) return OKLS_ERR_HIP;
+  return init_impl(out, cfg, n_groups, groups, ptr, kStaticScratchBytes, stream, true);
 }
 
 static okls_status check_tensors(const okls_handle* h, const okls_group_tensors* t, bool need_wg) {

@@ -29,5 +29,8 @@ hipError_t launch_cast(const CastArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_sym(const SymArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_init_state(const InitArgs& a, int n_jobs, hipStream_t s);
 hipError_t launch_check_finite(const InitArgs& a, int n_jobs, int* flag_dev, hipStream_t s);
+// device address of the static scratch (kStaticScratchBytes) on the current
+// device; looked up once per device and kept
+hipError_t static_scratch(void** ptr);
 
 }  // namespace okls

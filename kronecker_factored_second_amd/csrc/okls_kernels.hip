@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "okls_kernels.h"
@@ -1232,6 +1233,34 @@ hipError_t launch_cast(const CastArgs& a, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(cast_kernel, dim3(n_blocks), dim3(kCastThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch: the workspace of handles made by okls_init_static.  Each
+// device holds its own copy for the life of the process; the host code uses
+// only the address hipGetSymbolAddress returns for the current device (the
+// array's name on the host is a stand-in, not a device address).
+// ---------------------------------------------------------------------------
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_sym(const SymArgs& a, int n_blocks, hipStream_t s) {

@@ -12,6 +12,9 @@ constexpr int kBigPadFrom = 512;
 constexpr int kBK = 64;              // GEMM K step
 constexpr int kCastRows = 64;        // destination rows of one cast block
 constexpr int kCastCols = 256;       // destination columns of one cast block
+// bytes of the library's static device scratch (the workspace of handles
+// made by okls_init_static, for callers that cannot allocate device memory)
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
 constexpr int kMaxJobParts = 1024;   // statistics partials per job, at most
 constexpr int kStatThreads = 256;
 constexpr int kScaleExp = 14;        // dynamic casts put max |x| in (2^13, 2^14]

@@ -22,7 +22,8 @@ MODE = {"okls": 0, "shampoo": 1, "muon": 2}
 MUON_DEFAULTS = dict(ns_steps=5, ns_floor=1e-2)
 EXPORTED = ("okls_default_config", "okls_workspace_size", "okls_init", "okls_init_state", "okls_step",
             "okls_check_finite", "okls_ns_coefficients", "okls_profile_enable", "okls_profile_read",
-            "okls_destroy", "okls_status_string", "okls_plan_query")
+            "okls_destroy", "okls_status_string", "okls_plan_query", "okls_init_static")
+STATIC_SCRATCH_BYTES = 128 << 20
 PROFILE_CATEGORIES = ("ns_gemm", "factor_gemm", "whiten_gemm", "stats", "cast")
 
 
@@ -82,6 +83,9 @@ def load(path: str = LIB_PATH):
     lib.okls_init.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(Config), ctypes.c_int,
                               ctypes.POINTER(GroupDesc), vp, sz, vp]
     lib.okls_init.restype = ctypes.c_int
+    lib.okls_init_static.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(Config), ctypes.c_int,
+                                     ctypes.POINTER(GroupDesc), vp]
+    lib.okls_init_static.restype = ctypes.c_int
     lib.okls_init_state.argtypes = [vp, ctypes.POINTER(GroupTensors), vp]
     lib.okls_init_state.restype = ctypes.c_int
     lib.okls_step.argtypes = [vp, ctypes.POINTER(GroupTensors), i64, f32, vp]
@@ -220,6 +224,16 @@ def init(cfg: Config, groups, workspace, stream) -> ctypes.c_void_p:
                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
                           ctypes.c_void_p(stream))
     _check("okls_init", st)
+    return h
+
+
+def init_static(cfg: Config, groups, stream) -> ctypes.c_void_p:
+    """okls_init_static: a handle whose workspace is the library's static
+    device scratch (nothing is allocated on the device)."""
+    h = ctypes.c_void_p()
+    st = load().okls_init_static(ctypes.byref(h), ctypes.byref(cfg), len(groups), _groups_array(groups),
+                                 ctypes.c_void_p(stream))
+    _check("okls_init_static", st)
     return h
 
 
