@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-seconds", type=float, default=90.0)
     p.add_argument("--device-grads", action="store_true",
-                   help="Gaussian gradients of the workload's scale generated on the GPU (the default for "
+                   help="gradients of the workload's recipe drawn on the GPU (the default for "
                         "workloads above 1e9 parameters, whose host recipes would take minutes per step)")
     p.add_argument("--mode", choices=["okls", "shampoo", "muon"], default=None,
                    help="optimizer mode (default: the workload's); muon runs the polar iteration of the momentum "
@@ -69,6 +69,8 @@ def parse():
                    help="only run a plain 1 GiB device-to-device copy 10 times (HBM counter calibration)")
     p.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV_DIR", "WRITE_CSV_DIR", "COMMANDS"),
                    help="write the GEMM's HBM traffic summary of --workload from two rocprofv3 --pmc runs")
+    p.add_argument("--summarize-sq", nargs=2, metavar=("SQ_CSV_DIR", "COMMANDS"),
+                   help="write the GEMM's SQ counter table of --workload from a rocprofv3 --pmc run of SQ_COUNTERS")
     return p.parse_args()
 
 
@@ -141,6 +143,74 @@ def summarize_counters(fetch_dir, write_dir, commands, workload):
         *others,
     ]
     open(traffic_file(workload), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+EPI_NAMES = ["STORE32", "SYRK", "NS_T", "NS_Y1", "STORE16", "NS_FINAL", "UPDATE", "POLAR", "POLAR_UPDATE"]
+SQ_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+               "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES"]
+
+
+def sq_file(workload):
+    return os.path.join(ROOT, "profiles", f"gemm_nt_kernel_{workload}_fp16_sq_counters.txt")
+
+
+def summarize_sq(sq_dir, commands, workload):
+    """Per-instantiation table of gemm_nt_kernel from one rocprofv3 --pmc pass
+    of SQ_COUNTERS (with --kernel-trace, so every counter row carries its
+    dispatch's start and end): duration, MFMA rate, the shader clock the
+    launch ran at (GRBM_GUI_ACTIVE cycles over 8 XCDs per microsecond) and
+    the matrix cores' busy share at that clock."""
+    import csv
+    import glob
+    import re
+    disp = {}
+    for f in glob.glob(os.path.join(sq_dir, "**", "bench_counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "gemm_nt_kernel" not in r["Kernel_Name"]:
+                continue
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                         "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    if not disp:
+        raise SystemExit(f"no gemm_nt_kernel counter rows in {sq_dir}")
+    groups = {}
+    for d in disp.values():
+        m = re.search(r"TileCfg<(\d+), \d+, \d+, \w+>, (\d+), (\w+)>", d["name"])
+        groups.setdefault((int(m.group(1)), EPI_NAMES[int(m.group(2))], m.group(3) == "true"), []).append(d)
+    lines = [
+        f"# gemm_nt_kernel SQ counters per launch, workload {workload}, fp16 path",
+        f"# kernel_source_sha256_16 {kernel_source_hash()} (okls_kernels.hip, okls_types.h, okls_api.cpp)",
+        "# commands (repository root as $REPO, output directory OUT; cd /tmp first):",
+        *[f"#   {c.strip()}" for c in commands.split(";")],
+        "# Under counters the launches run one at a time (no overlap of two chains).",
+        "# Columns (averages over the launches of one instantiation):",
+        "#   gflop     = SQ_INSTS_VALU_MFMA_MOPS_F16 * 512 (the planner's algorithmic FLOPs of these launches)",
+        "#   frac      = TFLOP/s / 2500 (dense fp16 peak at 2.4 GHz)",
+        "#   clk_mhz   = GRBM_GUI_ACTIVE / 8 XCDs / us: the shader clock the launch ran at",
+        "#   mfma@2.4  = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (us * 2400): matrix-core busy share at the peak clock",
+        "#   mfma@clk  = the same share at clk_mhz",
+        "#   wait_any  = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: share of wave time stalled in s_waitcnt",
+        "#   lds_confl = SQ_LDS_BANK_CONFLICT / 256 CUs / (us * clk_mhz): bank-conflict cycles per CU cycle",
+        "tile epilogue      lo launches        us    gflop  TFLOP/s  frac clk_mhz mfma@2.4 mfma@clk wait_any lds_confl",
+    ]
+    tot_fl = tot_us = 0.0
+    for (tile, epi, wl), ds in sorted(groups.items()):
+        n = len(ds)
+        us = sum(d["us"] for d in ds) / n
+        fl = sum(d["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 for d in ds) / n
+        clk = sum(d["GRBM_GUI_ACTIVE"] / 8 / d["us"] for d in ds) / n
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / n / 1024
+        wait = sum(d["SQ_WAIT_INST_ANY"] for d in ds) / max(sum(d["SQ_WAVE_CYCLES"] for d in ds), 1)
+        confl = sum(d["SQ_LDS_BANK_CONFLICT"] for d in ds) / n / 256 / (us * clk)
+        tf = fl / us / 1e6
+        tot_fl += fl * n
+        tot_us += us * n
+        lines.append(f"{tile:4d} {epi:>12s} {int(wl):3d} {n:8d} {us:9.1f} {fl / 1e9:8.1f} {tf:8.1f} {tf / PEAK_FP16_TFLOPS:5.3f} "
+                     f"{clk:7.0f} {busy / (us * 2400):8.3f} {busy / (us * clk):8.3f} {wait:8.3f} {confl:9.4f}")
+    lines.append(f"# all gemm_nt_kernel launches: {len(disp)}, {tot_fl / tot_us / 1e6:.1f} TFLOP/s "
+                 f"({tot_fl / tot_us / 1e6 / PEAK_FP16_TFLOPS:.3f} of peak) over their summed durations")
+    open(sq_file(workload), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -231,6 +301,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.workload)
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq, args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the preconditioner step runs on a single MI355X; "
@@ -353,7 +426,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: " + ", ".join(f"{b}x {m}x{n}" for m, n, b in w.groups) +
                    f" ({w.n_matrices} matrices, {w.n_params / 1e6:.1f}M params), {mode}, "
-                   f"{w.grad_dtype} gradients" + (" (device Gaussian)" if device_grads else "") +
+                   f"{w.grad_dtype} gradients" + ((" (low-rank recipe drawn on the device)" if w.grad == "lowrank" else
+                                                   " (device Gaussian)") if device_grads else "") +
                    f", precision {args.precision}" +
                    (f", chunks of {opt.cfg.chunk_matrices} matrices" if opt.cfg.chunk_matrices else "") +
                    (f", roots every {args.root_period} steps" if args.root_period > 1 else ""),
