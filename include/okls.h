@@ -77,7 +77,7 @@ typedef enum { OKLS_F32 = 0, OKLS_BF16 = 1, OKLS_F16 = 2 } okls_dtype;
 typedef enum {
     OKLS_MODE_OKLS = 0,      /* KL factor EMAs, P = S^{-1/2} */
     OKLS_MODE_SHAMPOO = 1,   /* plain sums, P = S^{-1/4} via two chained roots */
-    OKLS_MODE_MUON = 2       /* no factors: the momentum N is orthogonalised by the polar
+    OKLS_MODE_MUON = 2,      /* no factors: the momentum N is orthogonalised by the polar
                                 Newton-Schulz iteration X <- a_k X + b_k (X X^T) X from
                                 X_0 = N / ||N N^T||_F^{1/2} (the Shampoo chapter's
                                 "ML에서: 대회 우승과 그다음": the un-accumulated Shampoo
@@ -85,6 +85,23 @@ typedef enum {
                                 the Clean paper's Table 6: 5 iterations).  ns_steps and
                                 ns_floor are the iteration's (Muon setting: 5 and 1e-2);
                                 beta2, eps, ns_damping and root_period are not used */
+    OKLS_MODE_SOAP = 3       /* Adam in the factors' eigenbasis ("Clean: Second-order LLM
+                                Training at Linear Memory Cost via Nystrom Sketching",
+                                Appendix C, Algorithm 4 (SOAP); "KPOP Optimiser Explained",
+                                "Transforming the Gradient"): per matrix
+                                  G' = Q_a^T G Q_b, M <- beta1 M + (1-beta1) G, M' = Q_a^T M Q_b,
+                                  V <- beta2 V + (1-beta2) G'^2,
+                                  N' = (M'/(1-beta1^t)) / (sqrt(V/(1-beta2^t)) + eps),
+                                  W <- (1 - lr wd) W - lr Q_a N' Q_b^T,
+                                  S_a <- sb S_a + (1-sb) G G^T, S_b <- sb S_b + (1-sb) G^T G
+                                  (sb = soap_beta), and after steps t with t % precond_freq
+                                  == 0 the bases Q_a, Q_b become eigenbases of S_a, S_b,
+                                  computed by block Jacobi sweeps warm-started from the
+                                  current bases.  The tensors' Sa, Sb hold the factors, Pa,
+                                  Pb the bases (columns = eigenvectors), V the second moment;
+                                  ns_*, nesterov_var_corr, root_period, eps_convex,
+                                  decay_after and shape_scale are not used; the GEMMs are
+                                  split-fp16 (fp32-accurate) when factor_split is 1 */
 } okls_mode;
 
 typedef struct {
@@ -139,6 +156,19 @@ typedef struct {
                                   their fp16 rounding error grows with the preconditioners'
                                   eigenvalue spread, which rank-deficient factors make large;
                                   0: plain fp16 inputs (the fp16 path's other products) */
+    /* OKLS_MODE_SOAP only (the Clean paper's Tables 4 and 6 give the values in
+       brackets; beta1, beta2, eps and weight_decay are Adam's there): */
+    float soap_beta;           /* EMA coefficient of the factors [0.95] */
+    int32_t precond_freq;      /* f >= 1: bases recomputed after steps t with t % f == 0 [10] */
+    int32_t soap_moments;      /* 0 (default): M in the parameter space, rotated every step
+                                  (Algorithm 4); 1: M kept in the eigenbasis, M <- beta1 M +
+                                  (1-beta1) G' (KPOP's Adam) */
+    int32_t bias_correction;   /* 1 (default): Adam's 1/(1-beta^t) corrections; 0: none */
+    int32_t jacobi_sweeps;     /* most sweeps of a basis refresh, 1..64 (default 20; a refresh
+                                  stops once converged: measured cold starts from the identity
+                                  need 12 sweeps at d = 1024 and 13 at d = 2816) */
+    float jacobi_tol;          /* a refresh stops once ||off(Q^T S Q)||_F <= tol ||diag||_F
+                                  (default 2e-6) */
 } okls_config;
 
 typedef struct {
@@ -156,6 +186,7 @@ typedef struct {
     float* Pa;         /* (N, m, m) left preconditioner S_a^{-1/2} (Shampoo S_a^{-1/4}) */
     float* Pb;         /* (N, n, n) right preconditioner */
                        /* OKLS_MODE_MUON reads none of Sa, Sb, Pa, Pb: they may be NULL */
+    float* V;          /* (N, m, n) second moment, OKLS_MODE_SOAP only (else NULL) */
 } okls_group_tensors;
 
 typedef struct okls_handle okls_handle;
@@ -183,8 +214,8 @@ typedef struct {
     int launches;
     int launches_stale;
     int ns_chains;
-    double flops[5];
-    double bytes[5];
+    double flops[6];
+    double bytes[6];
 } okls_plan_info;
 okls_status okls_plan_query(const okls_config* cfg, int n_groups, const okls_group_desc* groups,
                             okls_plan_info* out);
@@ -217,7 +248,8 @@ okls_status okls_init_static(okls_handle** out, const okls_config* cfg, int n_gr
                              const okls_group_desc* groups, void* stream);
 
 /* Fills the state for a fresh start (README "Hyperparameters": eps at factor
- * initialisation): S = eps I, P = I, M = 0 (Muon mode: M = 0 only).  W and G
+ * initialisation): S = eps I, P = I, M = 0 (Muon mode: M = 0 only; SOAP
+ * mode: S = 0, bases P = I, M = V = 0).  W and G
  * are not touched (may be NULL).  `tensors` points to n_groups entries.
  * Synchronises `stream` once. */
 okls_status okls_init_state(okls_handle* h, const okls_group_tensors* tensors, void* stream);
@@ -256,7 +288,10 @@ int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_s
  * busy), then clears them.  Categories (index into the arrays):
  *   0 Newton-Schulz GEMMs, 1 factor GEMMs (cross-preconditioning and the
  *   factor update), 2 whitening GEMMs (with the fused weight update),
- *   3 statistics kernels, 4 cast / momentum kernels.
+ *   3 statistics kernels, 4 cast / momentum kernels, 5 eigensolver (SOAP
+ *   mode: the Jacobi kernels of a basis refresh; the refresh's products
+ *   Q^T S Q count in category 0, the rotations into and out of the basis
+ *   in category 2 and the Adam kernel in category 4).
  * flops[i] is the algorithmic floating-point work of category i summed over
  * the profiled steps: 27 GEMMs of 2 d^3 per inverse square root (54 for the
  * Shampoo fourth root), 3 m n (m + n) for the OKLS factors (m n (m + n) in
@@ -270,7 +305,7 @@ int okls_ns_coefficients(const okls_config* cfg, double* a, double* b, int max_s
  * fp32 element, 2 per fp16, 4 with low halves), and
  * writes each output once (fp16 outputs 2 bytes per element, 4 with the low
  * halves; fp32 outputs 4). */
-#define OKLS_PROFILE_CATEGORIES 5
+#define OKLS_PROFILE_CATEGORIES 6
 typedef struct {
     double ms[OKLS_PROFILE_CATEGORIES];       /* sum of the launches' durations */
     double busy_ms[OKLS_PROFILE_CATEGORIES];  /* length of the union of the launches' intervals */

@@ -14,6 +14,10 @@
 //   GEMM  U = P_a V with the fused update W <- decay W - lr c_shape U
 // The order is the "Online KL Shampoo" README's "How it works": factors
 // with the previous preconditioners, fresh roots, whitening, update.
+// The SOAP mode (plan_soap) runs the Clean paper's Algorithm 4 instead:
+// rotations into the eigenbasis, the Adam kernel, the rotation back with the
+// fused update, the factor EMAs, and on refresh steps Q^T S Q followed by
+// block Jacobi sweeps on it that rotate the bases in place.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -102,6 +106,11 @@ struct FacBufs {
   size_t YT[2] = {0, 0}, ZT[2] = {0, 0}, TT = 0;   // transposed copies
   int s_pold = 0, s_cinv = 0, s_rho = 0, s_sqrtc = 0, s_p16 = 0;
   int s_cinv2 = 0, s_rho2 = 0, s_sqrtc2 = 0;
+  // SOAP: the basis' fp16 copies (ld), the factor's copy, (Q^T S)^T = Q^T S
+  // as fp16, Q^T S Q in fp32 (d x d) and the Jacobi rotations of a round
+  size_t Q16 = 0, Q16T = 0, L16 = 0, HT16 = 0, B32 = 0, jbuf = 0;
+  int ldq = 0;   // row stride of those four: [hi | lo] always (the refresh's last products are split)
+  int s_l = 0, s_lx = 0;
 };
 
 struct MatBufs {
@@ -114,9 +123,12 @@ struct MatBufs {
   int pd = 0, pdp = 0, ldp = 0;
   size_t NT16 = 0, X[2] = {0, 0}, XT[2] = {0, 0}, A32 = 0, A16 = 0;
   int s_gcinv = 0, s_grho = 0;
+  // SOAP: M' fp16, (G Q_b)^T and (M Q_b)^T fp16, G' and M' fp32, N' fp16, (N' Q_b^T)^T fp16
+  size_t M16 = 0, XGT16 = 0, XMT16 = 0, Gr32 = 0, Mr32 = 0, NP16 = 0, ZT16 = 0;
+  int s_m = 0, s_gx = 0, s_mx = 0;
 };
 
-enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4, L_SYM = 5 };
+enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4, L_SYM = 5, L_ADAM = 6, L_JAC = 7 };
 
 struct LaunchRec {
   int type = L_STAT;
@@ -130,9 +142,11 @@ struct LaunchRec {
   int tile = kTile;             // GEMM block tile
   int epi = EPI_STORE32;        // GEMM epilogue kind (one per launch)
   int stream = 0;               // 0: the caller's stream; 1: the library's side stream (between a fork and a join)
+  int jac_kind = 0, round = 0;  // L_JAC: JacKind and tournament round
+  size_t jac_part = 0, jac_flag = 0;   // L_JAC: workspace offsets of the chunk's partials and flags
 };
 
-enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4 };
+enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4, CAT_EIG = 5 };
 
 // The factors' Newton-Schulz chains are independent: they run as two chains
 // of launches, one on the caller's stream and one on a side stream, so one
@@ -142,8 +156,12 @@ enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4 };
 #endif
 constexpr int kNsStreams = OKLS_NS_STREAMS;
 
-// Global scale slots
+// Global scale slots.  SOAP adds SL_Q (the bases' static fp16 scale), SL_NP
+// (the Adam direction's) and SL_ZT + e (the direction's scale / 2^e, e =
+// ceil(log2 sqrt(n)): the rotated direction (N' Q_b^T)^T, whose rows have
+// Euclidean norm at most sqrt(n) max|N'|); its chunk slots start after them.
 enum { SL_ONE = 0, SL_Y = 1, SL_Z = 2, SL_T = 3, SL_FIRST_DYN = 4 };
+enum { SL_Q = 4, SL_NP = 5, SL_ZT = 6, kZtSlots = 16, SL_FIRST_DYN_SOAP = SL_ZT + kZtSlots };
 
 Ref ws_ref(size_t off) { return Ref{REF_WS, 0, static_cast<int64_t>(off)}; }
 Ref user_ref(int kind, int group, size_t byte_off) { return Ref{kind, group, static_cast<int64_t>(byte_off)}; }
@@ -162,13 +180,15 @@ struct okls_handle {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_sym = 0, off_scal = 0, off_part = 0, off_flag = 0;
+  size_t off_adam = 0, off_jac = 0;
+  float s_np = 1.0f;                        // SOAP: static scale of the Adam direction
   std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
   std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them
   std::vector<double> na, nb;
-  double step_flops[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
-  double step_bytes[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
-  double step_flops_stale[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
-  double step_bytes_stale[OKLS_PROFILE_CATEGORIES] = {0, 0, 0, 0, 0};
+  double step_flops[OKLS_PROFILE_CATEGORIES] = {};
+  double step_bytes[OKLS_PROFILE_CATEGORIES] = {};
+  double step_flops_stale[OKLS_PROFILE_CATEGORIES] = {};
+  double step_bytes_stale[OKLS_PROFILE_CATEGORIES] = {};
   // profiling
   bool prof = false;
   std::vector<hipEvent_t> events;           // pool
@@ -197,7 +217,8 @@ namespace {
 // ---------------------------------------------------------------------------
 okls_status check_config(const okls_config* c) {
   if (c == nullptr) return OKLS_ERR_INVALID_ARG;
-  if (c->mode != OKLS_MODE_OKLS && c->mode != OKLS_MODE_SHAMPOO && c->mode != OKLS_MODE_MUON) return OKLS_ERR_INVALID_ARG;
+  if (c->mode != OKLS_MODE_OKLS && c->mode != OKLS_MODE_SHAMPOO && c->mode != OKLS_MODE_MUON && c->mode != OKLS_MODE_SOAP)
+    return OKLS_ERR_INVALID_ARG;
   if (c->ns_steps < 2 || c->ns_steps > 16) return OKLS_ERR_INVALID_ARG;
   if (c->ns_split_steps < 0 || c->ns_split_steps > c->ns_steps) return OKLS_ERR_INVALID_ARG;
   if (c->factor_split != 0 && c->factor_split != 1) return OKLS_ERR_INVALID_ARG;
@@ -213,7 +234,39 @@ okls_status check_config(const okls_config* c) {
   if (!(c->ns_damping >= 0.f && c->ns_damping < 1.f)) return OKLS_ERR_INVALID_ARG;
   if (c->root_period < 1) return OKLS_ERR_INVALID_ARG;
   if ((c->eps_convex | c->decay_after | c->shape_scale | c->ns_classical) & ~1) return OKLS_ERR_INVALID_ARG;
+  if (c->mode == OKLS_MODE_SOAP) {
+    if (!(c->beta2 >= 0.f && c->beta2 < 1.f) || !(c->soap_beta >= 0.f && c->soap_beta < 1.f)) return OKLS_ERR_INVALID_ARG;
+    if (!(c->eps > 0.f)) return OKLS_ERR_INVALID_ARG;      // the direction divides by sqrt(V) + eps
+    if (c->precond_freq < 1 || ((c->soap_moments | c->bias_correction) & ~1)) return OKLS_ERR_INVALID_ARG;
+    if (c->jacobi_sweeps < 1 || c->jacobi_sweeps > 64 || !(c->jacobi_tol > 0.f && c->jacobi_tol < 1.f))
+      return OKLS_ERR_INVALID_ARG;
+    // the direction is bounded (and its fp16 operand can take a static scale)
+    // only when beta1^2 < beta2, or beta1 = 0
+    if (!(c->beta1 == 0.f || static_cast<double>(c->beta1) * c->beta1 < c->beta2)) return OKLS_ERR_UNSUPPORTED;
+  }
   return OKLS_OK;
+}
+
+// Largest |N'| the Adam direction can take.  By Cauchy-Schwarz on the two
+// EMAs of step t, |sum_k a_k g_k| <= sqrt(sum_k a_k^2 / b_k) sqrt(sum_k b_k g_k^2)
+// with a_k = (1-beta1) beta1^k and b_k = (1-beta2) beta2^k (k < t), so
+// |M'| / sqrt(V) <= (1-beta1) / sqrt(1-beta2) sqrt(sum_{k<t} (beta1^2/beta2)^k),
+// times sqrt(1-beta2^t) / (1-beta1^t) with bias correction; eps only lowers
+// it.  The supremum over t (dense to 2000, then geometric, then the limit).
+double adam_ratio_bound(const okls_config& c) {
+  const double b1 = c.beta1, b2 = c.beta2;
+  if (b2 == 0.0) return 1.0;                  // then beta1 = 0: |G'| / (|G'| + eps)
+  const double r = b1 * b1 / b2;
+  auto at = [&](double t) {
+    const double sum = r == 0.0 ? 1.0 : (1.0 - std::pow(r, t)) / (1.0 - r);
+    double v = (1.0 - b1) / std::sqrt(1.0 - b2) * std::sqrt(sum);
+    if (c.bias_correction) v *= std::sqrt(1.0 - std::pow(b2, t)) / (1.0 - std::pow(b1, t));
+    return v;
+  };
+  double best = at(1.0);
+  for (double t = 2.0; t < 1e9; t = t < 2000.0 ? t + 1.0 : std::floor(t * 1.01)) best = std::max(best, at(t));
+  best = std::max(best, (1.0 - b1) / std::sqrt((1.0 - b2) * (1.0 - r)));
+  return best;
 }
 
 okls_status check_groups(int n_groups, const okls_group_desc* g) {
@@ -234,6 +287,7 @@ struct Planner {
   const std::vector<okls_group_desc>& groups;
   bool okls_mode;
   bool muon_mode;
+  bool soap_mode;
   bool lo_layout;
   bool single_chain = false;   // never plan a second Newton-Schulz chain (no side stream)
   std::vector<double> na, nb;
@@ -245,6 +299,9 @@ struct Planner {
   std::vector<StatJob> stat_jobs;
   std::vector<CastJob> cast_jobs;
   std::vector<SymJob> sym_jobs;
+  std::vector<AdamJob> adam_jobs;
+  std::vector<JacJob> jac_jobs;
+  float s_np = 1.0f;          // SOAP: static scale of the Adam direction's fp16 operand
   std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
   std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them (root_period > 1)
   std::map<std::string, std::pair<int, int>> tile_cache;
@@ -252,11 +309,16 @@ struct Planner {
   std::vector<std::map<size_t, size_t>> ws_bufs;   // per chunk: workspace buffer offset -> bytes
   size_t chunk_bytes = 0;     // per-chunk buffer region size (max over chunks)
   int n_slots = SL_FIRST_DYN; // max over chunks
+  int first_dyn = SL_FIRST_DYN;
   int max_partials = 1;
 
   Planner(const okls_config& c, const std::vector<okls_group_desc>& g)
       : cfg(c), groups(g), okls_mode(c.mode == OKLS_MODE_OKLS), muon_mode(c.mode == OKLS_MODE_MUON),
-        lo_layout(c.factor_split != 0 || c.ns_split_steps > 0) {
+        soap_mode(c.mode == OKLS_MODE_SOAP), lo_layout(c.factor_split != 0 || c.ns_split_steps > 0) {
+    if (soap_mode) {
+      first_dyn = n_slots = SL_FIRST_DYN_SOAP;
+      s_np = pow2_for_bound(adam_ratio_bound(cfg));
+    }
     coeff_table(cfg, na, nb);
     double prod = 1.0, amax = 0.0;
     for (int k = 0; k < cfg.ns_steps; ++k) {
@@ -279,6 +341,7 @@ struct Planner {
 
   // lays out one chunk's buffers from offset 0 (relative); returns size
   std::vector<std::pair<size_t, size_t>> pending;   // chunk-relative buffers of the chunk being laid out
+  size_t jac_part_rel = 0, jac_flag_rel = 0;   // SOAP: chunk-relative Jacobi partials and flags
   size_t layout_chunk(std::vector<MatBufs>& mats, int& slot) {
     size_t off = 0;
     pending.clear();
@@ -288,6 +351,37 @@ struct Planner {
       pending.push_back({o, bytes});
       return o;
     };
+    if (soap_mode) {
+      int parts = 0, flags = 0;
+      auto sfac = [&](FacBufs& f, int d) {
+        f.d = d; f.dp = pad_tile(d); f.ld = ld_fac(f.dp); f.ldq = 2 * f.dp;
+        const size_t b16 = static_cast<size_t>(f.dp) * f.ldq * 2;
+        f.Q16 = take(b16); f.Q16T = take(b16);
+        f.L16 = take(b16); f.HT16 = take(b16);
+        f.B32 = take(static_cast<size_t>(d) * d * 4);
+        const int nb = jac_blocks(d), np = nb / 2;
+        f.jbuf = take(static_cast<size_t>(np) * kJp * kJp * 4);
+        parts += np * (np + 1) / 2;
+        flags += 1;
+        f.s_l = slot++; f.s_lx = slot++;
+      };
+      for (MatBufs& mb : mats) {
+        const okls_group_desc& g = groups[mb.group];
+        mb.m = g.m; mb.n = g.n; mb.mp = pad_tile(g.m); mb.np = pad_tile(g.n);
+        mb.ldm = ld_fac(mb.mp); mb.ldn = ld_fac(mb.np);
+        const size_t bmn = static_cast<size_t>(mb.mp) * mb.ldn * 2, bnm = static_cast<size_t>(mb.np) * mb.ldm * 2;
+        const size_t f32 = static_cast<size_t>(mb.m) * mb.n * 4;
+        mb.G16 = take(bmn); mb.G16T = take(bnm); mb.XGT16 = take(bnm); mb.Gr32 = take(f32);
+        if (!cfg.soap_moments) { mb.M16 = take(bmn); mb.XMT16 = take(bnm); mb.Mr32 = take(f32); }
+        mb.NP16 = take(bmn); mb.ZT16 = take(bnm);
+        mb.s_g = slot++; mb.s_gx = slot++; mb.s_m = slot++; mb.s_mx = slot++; mb.s_n = slot++; mb.s_vt = slot++;
+        sfac(mb.fa, g.m);
+        sfac(mb.fb, g.n);
+      }
+      jac_part_rel = take(static_cast<size_t>(parts) * 2 * sizeof(float));
+      jac_flag_rel = take(static_cast<size_t>(flags) * sizeof(int32_t));
+      return off;
+    }
     auto fac = [&](FacBufs& f, int d) {
       f.d = d; f.dp = pad_tile(d); f.ld = ld_ns(f.dp); f.ldw = ld_wh(f.dp);
       const size_t b16 = static_cast<size_t>(f.dp) * f.ld * 2;
@@ -331,6 +425,15 @@ struct Planner {
     }
     return off;
   }
+
+  // Jacobi blocks of a side d: ceil(d / kJb), even (the round-robin pairs them all)
+  static int jac_blocks(int d) {
+    const int nb = (d + kJb - 1) / kJb;
+    return nb + (nb & 1);
+  }
+  // e = ceil(log2 sqrt(k)): 2^-e bounds sqrt(k) from below by its reciprocal,
+  // the scale factor of a product of an operand with k columns and an orthogonal matrix
+  static int sqrt_exp(int k) { return static_cast<int>(std::ceil(0.5 * std::log2(static_cast<double>(k)) - 1e-12)); }
 
   // ---- tiles
   // Workgroup w of a launch runs on XCD w % 8.  Tiles are grouped into cost
@@ -489,6 +592,7 @@ struct Planner {
     int cinv_slot, rho_slot, sqrtc_slot, p16_slot, p16_inv_sqrt; int write_lo; float damp; int sym_read;
     Ref dst2; int scale_slot2; int write_lo2;
     Ref dstT; int dstT_ld; int dstT_lo;
+    int aux_slot; float aux_mul;
   };
   CastSpec cast_spec() {
     CastSpec c{};
@@ -496,7 +600,8 @@ struct Planner {
     c.dst = no_ref();
     c.dst2 = no_ref();
     c.dstT = no_ref();
-    c.cinv_slot = c.rho_slot = c.sqrtc_slot = c.p16_slot = c.scale_slot2 = -1;
+    c.cinv_slot = c.rho_slot = c.sqrtc_slot = c.p16_slot = c.scale_slot2 = c.aux_slot = -1;
+    c.aux_mul = 1.0f;
     return c;
   }
   void add_cast(std::vector<LaunchRec>& L, const std::vector<CastSpec>& specs, float ka = 0.f, float kb = 0.f) {
@@ -517,6 +622,7 @@ struct Planner {
       j.p16_static = s.p16_inv_sqrt ? sY : sZ / 16.0f; j.p16_inv_sqrt = s.p16_inv_sqrt; j.write_lo = s.write_lo; j.damp = s.damp; j.sym_read = s.sym_read;
       j.dst2 = s.dst2; j.scale_slot2 = s.scale_slot2; j.write_lo2 = s.write_lo2;
       j.dstT = s.dstT; j.dstT_ld = s.dstT_ld; j.dstT_lo = s.dstT_lo;
+      j.aux_slot = s.aux_slot; j.aux_mul = s.aux_mul;
       j.tiles_x = (s.dst_cols_p + kCastCols - 1) / kCastCols;
       const double src_b = s.kind == CA_H16 ? 2.0
                          : s.kind == CA_NESTEROV ? 4.0 + (s.g_fmt == GF_F32 ? 4.0 : 2.0) + (s.write_m ? 4.0 : 0.0)
@@ -560,6 +666,8 @@ struct Planner {
 
   // split-fp16 whitening products (and the lo halves of the operands they read)
   int wsplit() const { return (cfg.factor_split || cfg.whiten_split) ? 1 : 0; }
+  // SOAP: every product split-fp16 with factor_split
+  bool wsplit_soap() const { return cfg.factor_split != 0; }
 
   // eps term of every factor update: + eps I (R1), or (1 - beta2) eps I in
   // the convex form of the OKLS update
@@ -828,6 +936,337 @@ struct Planner {
     }
   }
 
+  // ---- SOAP (the Clean paper's Algorithm 4).  Every product with a basis
+  // runs on the basis' fp16 copies (scale 2^kScaleExp: |q| <= 1); an operand
+  // X with k columns multiplied by an orthogonal matrix has rows of norm at
+  // most sqrt(k) max|X|, so its product gets X's scale over 2^sqrt_exp(k).
+  //   casts: G, G^T; M' = beta1 M + (1-beta1) G (written back); Q_a, Q_a^T, Q_b, Q_b^T
+  //   GEMM   (G Q_b)^T = Q_b^T G^T, (M' Q_b)^T                 -> fp16
+  //   GEMM   G' = Q_a^T (G Q_b), M' rotated                     -> fp32
+  //   Adam   V <- beta2 V + (1-beta2) G'^2, N'                  -> fp16 (static scale)
+  //   GEMM   (N' Q_b^T)^T = Q_b N'^T                             -> fp16
+  //   GEMM   W <- decay W - lr Q_a (N' Q_b^T)
+  //   GEMM   S_a <- sb S_a + (1-sb) G G^T, S_b likewise (upper tiles, mirrored)
+  //   refresh: stats + cast of S, (Q^T S) as fp16, B = Q^T S Q in fp32, then
+  //   block Jacobi sweeps on B that rotate the caller's Q in place.
+  void plan_soap(std::vector<LaunchRec>& L, std::vector<MatBufs>& mats, bool refresh) {
+    const int fs = cfg.factor_split;
+    const bool param_m = cfg.soap_moments == 0;
+    auto gdt = [&](const MatBufs& mb) { return groups[mb.group].g_dtype; };
+    auto gfmt = [&](const MatBufs& mb) {
+      return gdt(mb) == OKLS_F32 ? GF_F32 : gdt(mb) == OKLS_BF16 ? GF_BF16 : GF_F16;
+    };
+    auto goff = [&](const MatBufs& mb) {
+      return static_cast<size_t>(mb.index) * mb.m * mb.n * (gdt(mb) == OKLS_F32 ? 4 : 2);
+    };
+    auto moff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.n * 4; };
+    auto aoff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.m * 4; };
+    auto boff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.n * mb.n * 4; };
+    auto xmul = [](int k) { return std::ldexp(1.0f, -sqrt_exp(k)); };
+
+    // 1. statistics of G and of M' (the plain EMA: the step's momentum read with (1, 0))
+    std::vector<StatSpec> st;
+    for (const MatBufs& mb : mats) {
+      const int gk = gdt(mb) == OKLS_F32 ? ST_F32 : ST_H16;
+      st.push_back(StatSpec{gk, user_ref(REF_G, mb.group, goff(mb)), mb.n, no_ref(), gfmt(mb), mb.m, mb.n});
+      if (param_m)
+        st.push_back(StatSpec{ST_NESTEROV, user_ref(REF_G, mb.group, goff(mb)), mb.n,
+                              user_ref(REF_M, mb.group, moff(mb)), gfmt(mb), mb.m, mb.n});
+    }
+    std::vector<std::pair<int, int>> parts = add_stats(L, st);
+    const int per = param_m ? 2 : 1;
+    // 2. casts
+    std::vector<CastSpec> cs;
+    for (size_t q = 0; q < mats.size(); ++q) {
+      const MatBufs& mb = mats[q];
+      CastSpec g = cast_spec();
+      g.kind = gdt(mb) == OKLS_F32 ? CA_F32 : CA_H16; g.g_fmt = gfmt(mb);
+      g.src = user_ref(REF_G, mb.group, goff(mb)); g.src_ld = mb.n;
+      g.rows = mb.m; g.cols = mb.n; g.dst_rows_p = mb.mp; g.dst_cols_p = mb.np; g.dst = ws_ref(mb.G16);
+      g.dst_ld = mb.ldn; g.dst_lo = mb.np; g.parts = parts[per * q]; g.scale_mode = SC_ABSMAX;
+      g.scale_slot = mb.s_g; g.write_lo = fs;
+      g.dstT = ws_ref(mb.G16T); g.dstT_ld = mb.ldm; g.dstT_lo = mb.mp;
+      g.aux_slot = mb.s_gx; g.aux_mul = xmul(mb.n);
+      cs.push_back(g);
+      if (param_m) {
+        CastSpec mm = cast_spec();
+        mm.kind = CA_NESTEROV; mm.src = user_ref(REF_M, mb.group, moff(mb)); mm.src_ld = mb.n;
+        mm.src2 = user_ref(REF_G, mb.group, goff(mb)); mm.g_fmt = gfmt(mb); mm.write_m = 1;
+        mm.rows = mb.m; mm.cols = mb.n; mm.dst_rows_p = mb.mp; mm.dst_cols_p = mb.np; mm.dst = ws_ref(mb.M16);
+        mm.dst_ld = mb.ldn; mm.dst_lo = mb.np; mm.parts = parts[per * q + 1]; mm.scale_mode = SC_ABSMAX;
+        mm.scale_slot = mb.s_m; mm.write_lo = fs;
+        mm.aux_slot = mb.s_mx; mm.aux_mul = xmul(mb.n);
+        cs.push_back(mm);
+      }
+      const FacBufs* fl[2] = {&mb.fa, &mb.fb};
+      const int kinds[2] = {REF_PA, REF_PB};
+      const size_t offs[2] = {aoff(mb), boff(mb)};
+      for (int sd = 0; sd < 2; ++sd) {   // the bases and their transposes, static scale
+        const FacBufs& F = *fl[sd];
+        CastSpec c = cast_spec();
+        c.kind = CA_F32; c.src = user_ref(kinds[sd], mb.group, offs[sd]); c.src_ld = F.d;
+        c.rows = c.cols = F.d; c.dst_rows_p = c.dst_cols_p = F.dp; c.dst = ws_ref(F.Q16);
+        c.dst_ld = F.ldq; c.dst_lo = F.dp; c.parts = parts[per * q]; c.scale_mode = SC_STATIC;
+        c.scale_slot = SL_Q; c.write_lo = fs;
+        c.dstT = ws_ref(F.Q16T); c.dstT_ld = F.ldq; c.dstT_lo = F.dp;
+        cs.push_back(c);
+      }
+    }
+    add_cast(L, cs);
+
+    for (const MatBufs& mb : mats) {
+      const double m = mb.m, n = mb.n;
+      step_flops[CAT_WHITEN] += (param_m ? 6.0 : 4.0) * m * n * (m + n);
+      step_flops[CAT_FACTOR] += m * n * (m + n);
+      if (refresh) step_flops[CAT_NS] += 4.0 * (m * m * m + n * n * n);
+    }
+    // 3. rotations into the basis: (X Q_b)^T = Q_b^T X^T (n x m), X = G, M'
+    gemm_cat = CAT_WHITEN;
+    {
+      std::vector<GemmProb> px;
+      for (const MatBufs& mb : mats) {
+        for (int w = 0; w < (param_m ? 2 : 1); ++w) {
+          GemmProb p = prob();
+          p.A = ws_ref(mb.fb.Q16T); p.lda = mb.fb.ldq; p.B = ws_ref(w == 0 ? mb.G16 : mb.M16); p.ldb = mb.ldn;
+          p.M = mb.n; p.N = mb.m; p.Kp = mb.np; p.Mp = mb.np; p.Np = mb.mp; p.epi = EPI_STORE16;
+          p.out16 = ws_ref(w == 0 ? mb.XGT16 : mb.XMT16); p.ld16 = mb.ldm; p.lo16 = mb.mp;
+          p.sA = SL_Q; p.sB = w == 0 ? mb.s_g : mb.s_m; p.s_out = w == 0 ? mb.s_gx : mb.s_mx;
+          px.push_back(p);
+        }
+      }
+      add_gemm(L, px, false, fs, fs);
+      std::vector<GemmProb> pr;
+      for (const MatBufs& mb : mats) {
+        for (int w = 0; w < (param_m ? 2 : 1); ++w) {   // X' = Q_a^T (X Q_b), fp32
+          GemmProb p = prob();
+          p.A = ws_ref(mb.fa.Q16T); p.lda = mb.fa.ldq; p.B = ws_ref(w == 0 ? mb.XGT16 : mb.XMT16); p.ldb = mb.ldm;
+          p.M = mb.m; p.N = mb.n; p.Kp = mb.mp; p.Mp = mb.mp; p.Np = mb.np; p.epi = EPI_STORE32;
+          p.out32 = ws_ref(w == 0 ? mb.Gr32 : mb.Mr32); p.ld32 = mb.n;
+          p.sA = SL_Q; p.sB = w == 0 ? mb.s_gx : mb.s_mx;
+          pr.push_back(p);
+        }
+      }
+      add_gemm(L, pr, false, fs, 0);
+    }
+    // 4. Adam in the basis.  With the moments kept in the basis, M' and V
+    // are EMAs of the same sequence of rotated entries, so |N'| has the
+    // static bound of adam_ratio_bound and N' goes straight to fp16.  With M
+    // in the parameter space (Algorithm 4) M' is rotated by the current
+    // bases while V accumulated the coordinates of earlier ones: after a
+    // refresh |N'| can reach |M'| / eps, so N' is written in fp32 (over G',
+    // which it no longer needs) and cast with its own absmax scale.
+    {
+      LaunchRec r;
+      r.type = L_ADAM;
+      r.cat = CAT_CAST;
+      r.first = static_cast<int>(adam_jobs.size());
+      int blk = 0;
+      for (const MatBufs& mb : mats) {
+        AdamJob j{};
+        j.g = ws_ref(mb.Gr32);
+        j.m = param_m ? ws_ref(mb.Mr32) : user_ref(REF_M, mb.group, moff(mb));
+        j.v = user_ref(REF_V, mb.group, moff(mb));
+        j.dst = param_m ? no_ref() : ws_ref(mb.NP16);
+        j.dst32 = param_m ? ws_ref(mb.Gr32) : no_ref();
+        j.rows = mb.m; j.cols = mb.n; j.rows_p = mb.mp; j.cols_p = mb.np; j.ld16 = mb.ldn; j.lo16 = mb.np;
+        j.eigen_m = param_m ? 0 : 1;
+        j.tiles_x = (mb.np + 255) / 256;
+        j.blk_begin = blk;
+        blk += j.tiles_x * (mb.mp / kAdamRows);
+        // G', M' (or M, read and written), V read and written, N' written
+        step_bytes[CAT_CAST] += (4.0 + 4.0 * (param_m ? 1 : 2) + 8.0 + (param_m ? 4.0 : fs ? 4.0 : 2.0)) * mb.m * mb.n;
+        adam_jobs.push_back(j);
+      }
+      r.count = static_cast<int>(mats.size());
+      r.nblocks = blk;
+      L.push_back(r);
+      if (param_m) {
+        std::vector<StatSpec> sn;
+        for (const MatBufs& mb : mats) sn.push_back(StatSpec{ST_F32, ws_ref(mb.Gr32), mb.n, no_ref(), 0, mb.m, mb.n});
+        std::vector<std::pair<int, int>> pn = add_stats(L, sn);
+        std::vector<CastSpec> cn;
+        for (size_t q = 0; q < mats.size(); ++q) {
+          const MatBufs& mb = mats[q];
+          CastSpec c = cast_spec();
+          c.kind = CA_F32; c.src = ws_ref(mb.Gr32); c.src_ld = mb.n; c.rows = mb.m; c.cols = mb.n;
+          c.dst_rows_p = mb.mp; c.dst_cols_p = mb.np; c.dst = ws_ref(mb.NP16); c.dst_ld = mb.ldn; c.dst_lo = mb.np;
+          c.parts = pn[q]; c.scale_mode = SC_ABSMAX; c.scale_slot = mb.s_n; c.write_lo = fs;
+          c.aux_slot = mb.s_vt; c.aux_mul = xmul(mb.n);
+          cn.push_back(c);
+        }
+        add_cast(L, cn);
+      }
+    }
+    // 5. the rotation back with the update: (N' Q_b^T)^T = Q_b N'^T, then W
+    {
+      std::vector<GemmProb> pz;
+      for (const MatBufs& mb : mats) {
+        GemmProb p = prob();
+        p.A = ws_ref(mb.fb.Q16); p.lda = mb.fb.ldq; p.B = ws_ref(mb.NP16); p.ldb = mb.ldn;
+        p.M = mb.n; p.N = mb.m; p.Kp = mb.np; p.Mp = mb.np; p.Np = mb.mp; p.epi = EPI_STORE16;
+        p.out16 = ws_ref(mb.ZT16); p.ld16 = mb.ldm; p.lo16 = mb.mp;
+        p.sA = SL_Q; p.sB = param_m ? mb.s_n : SL_NP; p.s_out = param_m ? mb.s_vt : SL_ZT + sqrt_exp(mb.n);
+        pz.push_back(p);
+      }
+      add_gemm(L, pz, false, fs, fs);
+      std::vector<GemmProb> pu;
+      for (const MatBufs& mb : mats) {
+        GemmProb p = prob();
+        p.A = ws_ref(mb.fa.Q16); p.lda = mb.fa.ldq; p.B = ws_ref(mb.ZT16); p.ldb = mb.ldm;
+        p.M = mb.m; p.N = mb.n; p.Kp = mb.mp; p.Mp = mb.mp; p.Np = mb.np; p.epi = EPI_UPDATE;
+        p.out32 = user_ref(REF_W, mb.group, moff(mb)); p.ld32 = mb.n;
+        p.sA = SL_Q; p.sB = param_m ? mb.s_vt : SL_ZT + sqrt_exp(mb.n); p.c0 = 1.0f;
+        pu.push_back(p);
+      }
+      add_gemm(L, pu, false, fs, 0);
+    }
+    // 6. factor EMAs (upper tiles, mirrored)
+    gemm_cat = CAT_FACTOR;
+    {
+      std::vector<GemmProb> ps;
+      for (const MatBufs& mb : mats) {
+        GemmProb a = prob();
+        a.A = a.B = ws_ref(mb.G16); a.lda = a.ldb = mb.ldn;
+        a.M = a.N = mb.m; a.Kp = mb.np; a.Mp = a.Np = mb.mp; a.epi = EPI_SYRK;
+        a.out32 = user_ref(REF_SA, mb.group, aoff(mb)); a.ld32 = mb.m;
+        a.sA = a.sB = mb.s_g; a.c0 = cfg.soap_beta; a.c1 = 1.0f - cfg.soap_beta; a.c2 = 0.0f;
+        ps.push_back(a);
+        GemmProb b = prob();
+        b.A = b.B = ws_ref(mb.G16T); b.lda = b.ldb = mb.ldm;
+        b.M = b.N = mb.n; b.Kp = mb.mp; b.Mp = b.Np = mb.np; b.epi = EPI_SYRK;
+        b.out32 = user_ref(REF_SB, mb.group, boff(mb)); b.ld32 = mb.n;
+        b.sA = b.sB = mb.s_g; b.c0 = cfg.soap_beta; b.c1 = 1.0f - cfg.soap_beta; b.c2 = 0.0f;
+        ps.push_back(b);
+      }
+      add_gemm(L, ps, true, fs, 0);
+    }
+    if (!refresh) return;
+    // 7. basis refresh: B = Q^T S Q for every factor
+    gemm_cat = CAT_NS;
+    std::vector<FacBufs*> facs;
+    std::vector<Ref> fsrc, fbasis;
+    for (MatBufs& mb : mats) {
+      facs.push_back(&mb.fa);
+      fsrc.push_back(user_ref(REF_SA, mb.group, aoff(mb)));
+      fbasis.push_back(user_ref(REF_PA, mb.group, aoff(mb)));
+      facs.push_back(&mb.fb);
+      fsrc.push_back(user_ref(REF_SB, mb.group, boff(mb)));
+      fbasis.push_back(user_ref(REF_PB, mb.group, boff(mb)));
+    }
+    std::vector<StatSpec> sf;
+    for (size_t f = 0; f < facs.size(); ++f)
+      sf.push_back(StatSpec{ST_F32, fsrc[f], facs[f]->d, no_ref(), 0, facs[f]->d, facs[f]->d});
+    std::vector<std::pair<int, int>> fparts = add_stats(L, sf);
+    std::vector<CastSpec> cf;
+    for (size_t f = 0; f < facs.size(); ++f) {
+      const FacBufs& F = *facs[f];
+      CastSpec c = cast_spec();
+      c.kind = CA_F32; c.src = fsrc[f]; c.src_ld = F.d; c.rows = c.cols = F.d;
+      c.dst_rows_p = c.dst_cols_p = F.dp; c.dst = ws_ref(F.L16); c.dst_ld = F.ldq; c.dst_lo = F.dp;
+      c.parts = fparts[f]; c.scale_mode = SC_ABSMAX; c.scale_slot = F.s_l; c.write_lo = fs;
+      c.aux_slot = F.s_lx; c.aux_mul = xmul(F.d);
+      cf.push_back(c);
+    }
+    add_cast(L, cf);
+    {
+      std::vector<GemmProb> ph, pb;
+      for (size_t f = 0; f < facs.size(); ++f) {
+        const FacBufs& F = *facs[f];
+        GemmProb h = prob();   // (S Q)^T = Q^T S (S symmetric: its rows are its columns)
+        h.A = ws_ref(F.Q16T); h.lda = F.ldq; h.B = ws_ref(F.L16); h.ldb = F.ldq;
+        h.M = h.N = F.d; h.Kp = F.dp; h.Mp = h.Np = F.dp; h.epi = EPI_STORE16;
+        h.out16 = ws_ref(F.HT16); h.ld16 = F.ldq; h.lo16 = F.dp; h.sA = SL_Q; h.sB = F.s_l; h.s_out = F.s_lx;
+        ph.push_back(h);
+        GemmProb b = prob();   // B = Q^T (S Q)
+        b.A = ws_ref(F.Q16T); b.lda = F.ldq; b.B = ws_ref(F.HT16); b.ldb = F.ldq;
+        b.M = b.N = F.d; b.Kp = F.dp; b.Mp = b.Np = F.dp; b.epi = EPI_STORE32;
+        b.out32 = ws_ref(F.B32); b.ld32 = F.d; b.sA = SL_Q; b.sB = F.s_lx;
+        pb.push_back(b);
+      }
+      add_gemm(L, ph, false, fs, fs);
+      add_gemm(L, pb, false, fs, 0);
+    }
+    // 8. Jacobi sweeps: reset, then per sweep every round's solve and apply, and a check
+    const int first = static_cast<int>(jac_jobs.size());
+    int solve_blk = 0, apply_blk = 0, part = 0, max_rounds = 0;
+    double sweep_flops = 0.0, sweep_bytes = 0.0;
+    for (size_t f = 0; f < facs.size(); ++f) {
+      const FacBufs& F = *facs[f];
+      JacJob j{};
+      j.B = ws_ref(F.B32); j.V = fbasis[f]; j.d = F.d; j.nb = jac_blocks(F.d); j.npairs = j.nb / 2;
+      j.btiles = j.npairs * (j.npairs + 1) / 2; j.vrows = (F.d + kJp - 1) / kJp;
+      j.jbuf = static_cast<int64_t>(F.jbuf); j.part = part; j.flag = static_cast<int32_t>(f);
+      j.solve_begin = solve_blk; j.apply_begin = apply_blk;
+      solve_blk += j.npairs;
+      apply_blk += j.btiles + j.vrows * j.npairs;
+      part += j.btiles;
+      max_rounds = std::max(max_rounds, j.nb - 1);
+      const double tile = static_cast<double>(kJp) * kJp * kJp;   // one 64^3 product
+      sweep_flops += (j.nb - 1) * (2.0 * tile * 2.0 * j.btiles + 2.0 * tile * j.vrows * j.npairs);
+      // per round: B and V read and written once, the rotations written and read
+      sweep_bytes += (j.nb - 1) * (16.0 * F.d * F.d + 8.0 * j.npairs * kJp * kJp);
+      jac_jobs.push_back(j);
+    }
+    step_flops[CAT_EIG] += cfg.jacobi_sweeps * sweep_flops;
+    step_bytes[CAT_EIG] += cfg.jacobi_sweeps * sweep_bytes;
+    auto jac = [&](int kind, int round, int nblocks) {
+      LaunchRec r;
+      r.type = L_JAC;
+      r.cat = CAT_EIG;
+      r.first = first;
+      r.count = static_cast<int>(facs.size());
+      r.jac_kind = kind;
+      r.round = round;
+      r.nblocks = nblocks;
+      r.jac_part = jac_part_rel;
+      r.jac_flag = jac_flag_rel;
+      L.push_back(r);
+    };
+    jac(JAC_RESET, 0, 1);
+    for (int sw = 0; sw < cfg.jacobi_sweeps; ++sw) {
+      for (int rd = 0; rd < max_rounds; ++rd) {
+        jac(JAC_SOLVE, rd, solve_blk);
+        jac(JAC_APPLY, rd, apply_blk);
+      }
+      jac(JAC_CHECK, 0, static_cast<int>(facs.size()));
+    }
+    // 9. one Newton-Schulz step towards the nearest orthogonal matrix,
+    // Q <- Q (3 I - Q^T Q) / 2, split-fp16 (fp32-accurate) whatever the
+    // precision: each sweep's rotations leave Q orthogonal only to ~1e-6, and
+    // a basis that is refreshed from itself would otherwise drift a little
+    // further from orthogonal at every refresh; the step squares that error.
+    // T and T^T go through the buffers of S's copy and of (Q^T S).
+    std::vector<CastSpec> cq;
+    for (size_t f = 0; f < facs.size(); ++f) {
+      const FacBufs& F = *facs[f];
+      CastSpec c = cast_spec();
+      c.kind = CA_F32; c.src = fbasis[f]; c.src_ld = F.d; c.rows = c.cols = F.d;
+      c.dst_rows_p = c.dst_cols_p = F.dp; c.dst = ws_ref(F.Q16); c.dst_ld = F.ldq; c.dst_lo = F.dp;
+      c.parts = fparts[f]; c.scale_mode = SC_STATIC; c.scale_slot = SL_Q; c.write_lo = 1;
+      c.dstT = ws_ref(F.Q16T); c.dstT_ld = F.ldq; c.dstT_lo = F.dp;
+      cq.push_back(c);
+    }
+    add_cast(L, cq);
+    std::vector<GemmProb> pt, pq;
+    for (size_t f = 0; f < facs.size(); ++f) {
+      const FacBufs& F = *facs[f];
+      GemmProb t = prob();   // T = 3/2 I - 1/2 Q^T Q (and T^T)
+      t.A = t.B = ws_ref(F.Q16T); t.lda = t.ldb = F.ldq;
+      t.M = t.N = F.d; t.Kp = F.dp; t.Mp = t.Np = F.dp; t.epi = EPI_NS_T;
+      t.out16 = ws_ref(F.L16); t.out16T = ws_ref(F.HT16); t.ld16 = F.ldq; t.lo16 = F.dp;
+      t.sA = t.sB = SL_Q; t.s_out = SL_Q;
+      pt.push_back(t);
+      GemmProb q = prob();   // Q <- Q T
+      q.A = ws_ref(F.Q16); q.lda = F.ldq; q.B = ws_ref(F.HT16); q.ldb = F.ldq;
+      q.M = q.N = F.d; q.Kp = F.dp; q.Mp = q.Np = F.dp; q.epi = EPI_STORE32;
+      q.out32 = fbasis[f]; q.ld32 = F.d; q.sA = q.sB = SL_Q;
+      pq.push_back(q);
+      step_flops[CAT_NS] += 4.0 * std::pow(static_cast<double>(F.d), 3.0);
+    }
+    add_gemm(L, pt, false, 1, 1, 1.5f, -0.5f);
+    add_gemm(L, pq, false, 1, 0);
+  }
+
   // Whether a second concurrent Newton-Schulz chain pays for this chunk.
   // It fills the CUs that the last, partly filled round of a launch leaves
   // idle; with a full last round, or many rounds, it only adds launches and
@@ -866,13 +1305,19 @@ struct Planner {
     if (rebase) {
       for (MatBufs& mb : mats) {
         size_t* offs[] = {&mb.G16, &mb.G16T, &mb.N16, &mb.Xa32, &mb.XbT32, &mb.Xa16, &mb.XbT16, &mb.VT32, &mb.VT16,
-                          &mb.NT16, &mb.X[0], &mb.X[1], &mb.XT[0], &mb.XT[1], &mb.A32, &mb.A16};
+                          &mb.NT16, &mb.X[0], &mb.X[1], &mb.XT[0], &mb.XT[1], &mb.A32, &mb.A16,
+                          &mb.M16, &mb.XGT16, &mb.XMT16, &mb.Gr32, &mb.Mr32, &mb.NP16, &mb.ZT16};
         for (size_t* o : offs) *o += base;
         for (FacBufs* f : {&mb.fa, &mb.fb}) {
           f->Y[0] += base; f->Y[1] += base; f->Z[0] += base; f->Z[1] += base; f->T += base; f->R32 += base;
           f->YT[0] += base; f->YT[1] += base; f->ZT[0] += base; f->ZT[1] += base; f->TT += base;
           f->P16w += base;
+          f->Q16 += base; f->Q16T += base; f->L16 += base; f->HT16 += base; f->B32 += base; f->jbuf += base;
         }
+      }
+      if (soap_mode) {
+        jac_part_rel += base;
+        jac_flag_rel += base;
       }
       ws_bufs.emplace_back();
       for (const std::pair<size_t, size_t>& b : pending) ws_bufs.back()[b.first + base] = b.second;
@@ -881,6 +1326,11 @@ struct Planner {
     if (muon_mode) {
       plan_muon(L, mats);
       chunks.push_back(std::move(L));
+      return;
+    }
+    if (soap_mode) {
+      plan_soap(L, mats, refresh);
+      (refresh ? chunks : chunks_stale).push_back(std::move(L));
       return;
     }
     // fp16 copies of the previous preconditioners: the OKLS factor products
@@ -1141,7 +1591,7 @@ struct Planner {
     const okls_group_desc& g = groups[group];
     const size_t b = static_cast<size_t>(g.batch);
     switch (kind) {
-      case REF_W: case REF_M: return b * g.m * g.n * 4;
+      case REF_W: case REF_M: case REF_V: return b * g.m * g.n * 4;
       case REF_G: return b * g.m * g.n * (g.g_dtype == OKLS_F32 ? 4 : 2);
       case REF_SA: case REF_PA: return b * g.m * g.m * 4;
       case REF_SB: case REF_PB: return b * g.n * g.n * 4;
@@ -1150,14 +1600,17 @@ struct Planner {
   }
   bool fits(const Ref& r, size_t bytes) const {
     if (r.kind == REF_WS) return fits_ws(r, bytes);
-    if (r.kind < REF_W || r.kind > REF_PB || r.group < 0 || r.group >= static_cast<int>(groups.size())) return false;
+    if (r.kind < REF_W || r.kind > REF_V || r.group < 0 || r.group >= static_cast<int>(groups.size())) return false;
+    if (r.kind == REF_V && !soap_mode) return false;
     return r.off >= 0 && static_cast<size_t>(r.off) + bytes <= user_bytes(r.kind, r.group);
   }
   bool slot_ok(int s) const { return s >= 0 && s < n_slots; }
 
+  // whether some steps keep the roots (SOAP: the bases) and run their own plan
+  bool has_stale() const { return soap_mode ? cfg.precond_freq > 1 : (cfg.root_period > 1 && !muon_mode); }
   bool validate() {
     if (!validate_plan(chunks)) return false;
-    return (cfg.root_period <= 1 || muon_mode) ? chunks_stale.empty() : validate_plan(chunks_stale);
+    return has_stale() ? validate_plan(chunks_stale) : chunks_stale.empty();
   }
   bool validate_plan(const std::vector<std::vector<LaunchRec>>& plan_chunks) {
     if (ws_bufs.size() != plan_chunks.size()) return false;
@@ -1224,6 +1677,47 @@ struct Planner {
               if (!fits(p.aux, (static_cast<size_t>(p.M - 1) * p.ldaux + p.N) * 4)) return false;
             }
           }
+        } else if (r.type == L_ADAM) {
+          int blk = 0;
+          if (r.first < 0 || r.first + r.count > static_cast<int>(adam_jobs.size())) return false;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const AdamJob& a = adam_jobs[j];
+            if (a.blk_begin != blk || a.rows < 1 || a.cols < 1 || a.rows_p < a.rows || a.cols_p < a.cols) return false;
+            if (a.rows_p % kAdamRows || a.cols_p % 4 || a.tiles_x != (a.cols_p + 255) / 256) return false;
+            blk += a.tiles_x * (a.rows_p / kAdamRows);
+            const size_t f32 = static_cast<size_t>(a.rows) * a.cols * 4;
+            if (!fits(a.g, f32) || !fits(a.m, f32) || !fits(a.v, f32)) return false;
+            if (a.dst.kind == REF_NONE) {
+              if (!fits(a.dst32, f32)) return false;
+            } else {
+              const int need_ld = wsplit_soap() ? a.lo16 + a.cols_p : a.cols_p;
+              if (a.ld16 < need_ld || (wsplit_soap() && a.lo16 < a.cols_p)) return false;
+              if (!fits(a.dst, static_cast<size_t>(a.rows_p) * a.ld16 * 2)) return false;
+            }
+          }
+          if (blk != r.nblocks) return false;
+        } else if (r.type == L_JAC) {
+          if (r.jac_kind < JAC_RESET || r.jac_kind > JAC_CHECK) return false;
+          if (r.first < 0 || r.first + r.count > static_cast<int>(jac_jobs.size())) return false;
+          int solve = 0, apply = 0, part = 0;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const JacJob& q = jac_jobs[j];
+            if (q.d < 1 || q.nb < 2 || (q.nb & 1) || q.nb * kJb < q.d || q.npairs * 2 != q.nb) return false;
+            if (q.btiles != q.npairs * (q.npairs + 1) / 2 || q.vrows != (q.d + kJp - 1) / kJp) return false;
+            if (q.solve_begin != solve || q.apply_begin != apply || q.part != part || q.flag != j - r.first) return false;
+            solve += q.npairs;
+            apply += q.btiles + q.vrows * q.npairs;
+            part += q.btiles;
+            const size_t dd = static_cast<size_t>(q.d) * q.d * 4;
+            if (!fits(q.B, dd) || !fits(q.V, dd)) return false;
+            if (q.V.kind != REF_PA && q.V.kind != REF_PB) return false;
+            if (!fits(ws_ref(static_cast<size_t>(q.jbuf)), static_cast<size_t>(q.npairs) * kJp * kJp * 4)) return false;
+          }
+          if (!fits(ws_ref(r.jac_part), static_cast<size_t>(part) * 2 * sizeof(float))) return false;
+          if (!fits(ws_ref(r.jac_flag), static_cast<size_t>(r.count) * sizeof(int32_t))) return false;
+          const int want = r.jac_kind == JAC_SOLVE ? solve : r.jac_kind == JAC_APPLY ? apply
+                         : r.jac_kind == JAC_CHECK ? r.count : 1;
+          if (r.nblocks != want || r.round < 0) return false;
         } else if (r.type == L_SYM) {
           int blk = 0;
           if (r.first < 0 || r.first + r.count > static_cast<int>(sym_jobs.size())) return false;
@@ -1287,6 +1781,7 @@ struct Planner {
             if (c.part_begin < 0 || c.part_count < 1 || c.part_count > kMaxJobParts ||
                 c.part_begin + c.part_count > max_partials) return false;
             if (!slot_ok(c.scale_slot)) return false;
+            if (c.aux_slot >= 0 && !slot_ok(c.aux_slot)) return false;
             for (int s : {c.cinv_slot, c.rho_slot, c.sqrtc_slot, c.p16_slot})
               if (s >= 0 && !slot_ok(s)) return false;
           }
@@ -1314,14 +1809,14 @@ struct Planner {
     if (!cur.empty()) all.push_back(cur);
     chunk_bytes = 0;
     for (std::vector<MatBufs>& c : all) {
-      int slot = SL_FIRST_DYN;
+      int slot = first_dyn;
       chunk_bytes = std::max(chunk_bytes, layout_chunk(c, slot));
       n_slots = std::max(n_slots, slot);
       plan_chunk(c, base, true, true);
     }
-    if (cfg.root_period > 1 && !muon_mode) {
-      // the plan of the steps that keep the roots, over the same buffers,
-      // with its own algorithmic work
+    if (has_stale()) {
+      // the plan of the steps that keep the roots (SOAP: the bases), over
+      // the same buffers, with its own algorithmic work
       double f[OKLS_PROFILE_CATEGORIES], b[OKLS_PROFILE_CATEGORIES];
       for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
         f[i] = step_flops[i]; b[i] = step_bytes[i];
@@ -1337,7 +1832,8 @@ struct Planner {
 };
 
 struct WsLayout {
-  size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, scal = 0, part = 0, flag = 0, chunk = 0, total = 0;
+  size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, adam = 0, jac = 0, scal = 0, part = 0, flag = 0, chunk = 0,
+         total = 0;
 };
 
 WsLayout ws_layout(Planner& P) {
@@ -1351,6 +1847,8 @@ WsLayout ws_layout(Planner& P) {
   w.stat = take(P.stat_jobs.size() * sizeof(StatJob));
   w.cast = take(P.cast_jobs.size() * sizeof(CastJob));
   w.sym = take(P.sym_jobs.size() * sizeof(SymJob));
+  w.adam = take(P.adam_jobs.size() * sizeof(AdamJob));
+  w.jac = take(P.jac_jobs.size() * sizeof(JacJob));
   w.scal = take(static_cast<size_t>(P.n_slots) * sizeof(float));
   w.part = take(static_cast<size_t>(P.max_partials) * 2 * sizeof(float) * kNsStreams);   // one region per stream
   w.flag = take(sizeof(int));
@@ -1372,6 +1870,7 @@ UserPtrs user_ptrs(const okls_handle* h, const okls_group_tensors* t) {
     u.p[g][REF_SB] = t[g].Sb;
     u.p[g][REF_PA] = t[g].Pa;
     u.p[g][REF_PB] = t[g].Pb;
+    u.p[g][REF_V] = t[g].V;
   }
   return u;
 }
@@ -1407,6 +1906,12 @@ void okls_default_config(okls_config* c) {
   c->shape_scale = 1;
   c->ns_classical = 0;
   c->whiten_split = 1;
+  c->soap_beta = 0.95f;
+  c->precond_freq = 10;
+  c->soap_moments = 0;
+  c->bias_correction = 1;
+  c->jacobi_sweeps = 20;
+  c->jacobi_tol = 2e-6f;
 }
 
 size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups) {
@@ -1429,19 +1934,21 @@ okls_status okls_plan_query(const okls_config* cfg, int n_groups, const okls_gro
   Planner P(*cfg, g);
   (void)ws_layout(P);
   if (!P.validate()) return OKLS_ERR_INVALID_ARG;
-  static_assert(OKLS_PROFILE_CATEGORIES == 5, "okls_plan_info holds five categories");
+  static_assert(OKLS_PROFILE_CATEGORIES == 6, "okls_plan_info holds six categories");
   okls_plan_info info{};
   auto kernels = [](const std::vector<std::vector<LaunchRec>>& cs) {
     int n = 0;
     for (const std::vector<LaunchRec>& L : cs)
-      for (const LaunchRec& r : L) n += (r.type == L_STAT || r.type == L_CAST || r.type == L_GEMM || r.type == L_SYM);
+      for (const LaunchRec& r : L)
+        n += (r.type == L_STAT || r.type == L_CAST || r.type == L_GEMM || r.type == L_SYM || r.type == L_ADAM ||
+              r.type == L_JAC);
     return n;
   };
   info.chunks = static_cast<int>(P.chunks.size());
   info.launches = kernels(P.chunks);
   info.launches_stale = P.chunks_stale.empty() ? info.launches : kernels(P.chunks_stale);
   info.ns_chains = 0;
-  if (!P.muon_mode) {
+  if (!P.muon_mode && !P.soap_mode) {
     for (const std::vector<LaunchRec>& L : P.chunks) {
       int streams = 1;
       for (const LaunchRec& r : L) streams = std::max(streams, r.stream + 1);
@@ -1489,7 +1996,8 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   Planner P(*cfg, g);
   P.single_chain = single_chain;
   P.plan(w.chunk);
-  if (!P.validate() || P.probs.size() != sizing.probs.size() || P.chunk_bytes != sizing.chunk_bytes)
+  if (!P.validate() || P.probs.size() != sizing.probs.size() || P.chunk_bytes != sizing.chunk_bytes ||
+      P.adam_jobs.size() != sizing.adam_jobs.size() || P.jac_jobs.size() != sizing.jac_jobs.size())
     return OKLS_ERR_UNSUPPORTED;
   // the regions the tables and slots occupy must end before the chunk buffers
   if (w.flag + sizeof(int) > w.chunk) return OKLS_ERR_UNSUPPORTED;
@@ -1505,6 +2013,9 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_stat = w.stat;
   h->off_cast = w.cast;
   h->off_sym = w.sym;
+  h->off_adam = w.adam;
+  h->off_jac = w.jac;
+  h->s_np = P.s_np;
   h->off_scal = w.scal;
   h->off_part = w.part;
   h->off_flag = w.flag;
@@ -1543,6 +2054,11 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   scal[SL_Y] = P.sY;
   scal[SL_Z] = P.sZ;
   scal[SL_T] = P.sT;
+  if (P.soap_mode) {
+    scal[SL_Q] = std::ldexp(1.0f, kScaleExp);
+    scal[SL_NP] = P.s_np;
+    for (int e = 0; e < kZtSlots; ++e) scal[SL_ZT + e] = std::ldexp(P.s_np, -e);
+  }
 
   hipStream_t s = as_stream(stream);
   hipError_t e = hipSuccess;
@@ -1554,6 +2070,8 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   up(w.stat, P.stat_jobs.data(), P.stat_jobs.size() * sizeof(StatJob));
   up(w.cast, P.cast_jobs.data(), P.cast_jobs.size() * sizeof(CastJob));
   up(w.sym, P.sym_jobs.data(), P.sym_jobs.size() * sizeof(SymJob));
+  up(w.adam, P.adam_jobs.data(), P.adam_jobs.size() * sizeof(AdamJob));
+  up(w.jac, P.jac_jobs.data(), P.jac_jobs.size() * sizeof(JacJob));
   up(w.scal, scal.data(), scal.size() * sizeof(float));
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
@@ -1597,6 +2115,7 @@ static okls_status check_tensors(const okls_handle* h, const okls_group_tensors*
       if (x.Sa == nullptr || x.Sb == nullptr || x.Pa == nullptr || x.Pb == nullptr) return OKLS_ERR_INVALID_ARG;
       if (!aligned(x.Sa, 4) || !aligned(x.Sb, 4) || !aligned(x.Pa, 4) || !aligned(x.Pb, 4)) return OKLS_ERR_INVALID_ARG;
     }
+    if (h->cfg.mode == OKLS_MODE_SOAP && (x.V == nullptr || !aligned(x.V, 4))) return OKLS_ERR_INVALID_ARG;
     if (need_wg) {
       if (x.W == nullptr || x.G == nullptr) return OKLS_ERR_INVALID_ARG;
       if (!aligned(x.W, 4) || !aligned(x.G, h->groups[g].g_dtype == OKLS_F32 ? 4 : 2)) return OKLS_ERR_INVALID_ARG;
@@ -1617,12 +2136,15 @@ okls_status okls_init_state(okls_handle* h, const okls_group_tensors* t, void* s
   for (size_t g = 0; g < h->groups.size(); ++g) {
     const okls_group_desc& d = h->groups[g];
     if (h->cfg.mode != OKLS_MODE_MUON) {
-      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, h->cfg.eps};
-      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, h->cfg.eps};
+      // SOAP: zero factors (the Clean paper's Algorithm 4 starts from none), identity bases
+      const float s0 = h->cfg.mode == OKLS_MODE_SOAP ? 0.0f : h->cfg.eps;
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, s0};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, s0};
       a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, d.m, 1.0f};
       a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, d.n, 1.0f};
     }
     a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_M, d.batch, d.m, d.n, 0.0f};
+    if (h->cfg.mode == OKLS_MODE_SOAP) a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_V, d.batch, d.m, d.n, 0.0f};
   }
   hipStream_t s = as_stream(stream);
   if (launch_init_state(a, n, s) != hipSuccess) return OKLS_ERR_HIP;
@@ -1652,10 +2174,20 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
     }
     s_t = 1.0 / std::sqrt(v);
   }
-  const double decay = 1.0 - static_cast<double>(lr) * h->cfg.weight_decay * (static_cast<double>(lr) / h->cfg.lr_peak);
+  const bool soap = h->cfg.mode == OKLS_MODE_SOAP;
+  // SOAP: AdamW's decoupled decay 1 - lr wd (the Clean paper's Table 4); the
+  // other modes: AdamC's 1 - lr wd lr / lr_peak
+  const double decay = soap ? 1.0 - static_cast<double>(lr) * h->cfg.weight_decay
+                            : 1.0 - static_cast<double>(lr) * h->cfg.weight_decay * (static_cast<double>(lr) / h->cfg.lr_peak);
+  if (soap) s_t = 1.0;
+  // the momentum read: the Nesterov look-ahead, or (SOAP) the first moment itself
+  const float nest_a = soap ? 1.0f : static_cast<float>(b1), nest_b = soap ? 0.0f : 1.0f - static_cast<float>(b1);
+  const double bc1 = (soap && h->cfg.bias_correction) ? 1.0 / (1.0 - std::pow(b1, static_cast<double>(step))) : 1.0;
+  const double bc2 = (soap && h->cfg.bias_correction)
+                         ? 1.0 / (1.0 - std::pow(static_cast<double>(h->cfg.beta2), static_cast<double>(step))) : 1.0;
   // the update epilogue computes decay W - lr_update c U: decay after the
   // update, decay (W - lr c U), is the same form with lr_update = decay lr
-  const float lr_update = h->cfg.decay_after ? static_cast<float>(decay * lr) : lr;
+  const float lr_update = (h->cfg.decay_after && !soap) ? static_cast<float>(decay * lr) : lr;
 
   const UserPtrs user = user_ptrs(h, t);
   hipStream_t s = as_stream(stream);
@@ -1664,7 +2196,9 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
   float* part = reinterpret_cast<float*>(ws + h->off_part);
 
   // the roots are recomputed on steps 1, 1 + p, 1 + 2p, ... (p = root_period)
-  const bool refresh = h->cfg.mode == OKLS_MODE_MUON || h->cfg.root_period <= 1 || (step - 1) % h->cfg.root_period == 0;
+  // SOAP: the bases are recomputed after steps t with t % precond_freq == 0
+  const bool refresh = soap ? (h->cfg.precond_freq <= 1 || step % h->cfg.precond_freq == 0)
+                            : (h->cfg.mode == OKLS_MODE_MUON || h->cfg.root_period <= 1 || (step - 1) % h->cfg.root_period == 0);
   if (h->prof) {
     h->acc.steps += 1;
     for (int i = 0; i < OKLS_PROFILE_CATEGORIES; ++i) {
@@ -1708,6 +2242,8 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.partials = rpart;
         a.beta1 = static_cast<float>(b1);
         a.s_t = static_cast<float>(s_t);
+        a.nest_a = nest_a;
+        a.nest_b = nest_b;
         a.ws = ws;
         a.user = user;
         e = launch_stats(a, r.nblocks, rs);
@@ -1722,6 +2258,8 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.s_t = static_cast<float>(s_t);
         a.ka = r.ka;
         a.kb = r.kb;
+        a.nest_a = nest_a;
+        a.nest_b = nest_b;
         a.ws = ws;
         a.user = user;
         e = launch_cast(a, r.nblocks, rs);
@@ -1733,6 +2271,31 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.ws = ws;
         a.user = user;
         e = launch_sym(a, r.nblocks, rs);
+      } else if (r.type == L_ADAM) {
+        AdamArgs a;
+        a.jobs = reinterpret_cast<const AdamJob*>(ws + h->off_adam) + r.first;
+        a.n_jobs = r.count;
+        a.beta1 = static_cast<float>(b1);
+        a.beta2 = h->cfg.beta2;
+        a.eps = h->cfg.eps;
+        a.bc1 = static_cast<float>(bc1);
+        a.bc2 = static_cast<float>(bc2);
+        a.s_out = h->s_np;
+        a.write_lo = h->cfg.factor_split;
+        a.ws = ws;
+        a.user = user;
+        e = launch_adam(a, r.nblocks, rs);
+      } else if (r.type == L_JAC) {
+        JacArgs a;
+        a.jobs = reinterpret_cast<const JacJob*>(ws + h->off_jac) + r.first;
+        a.n_jobs = r.count;
+        a.round = r.round;
+        a.tol = h->cfg.jacobi_tol;
+        a.partials = reinterpret_cast<float*>(ws + r.jac_part);
+        a.flags = reinterpret_cast<int32_t*>(ws + r.jac_flag);
+        a.ws = ws;
+        a.user = user;
+        e = launch_jacobi(a, r.jac_kind, r.nblocks, rs);
       } else {
         GemmArgs a;
         a.probs = reinterpret_cast<const GemmProb*>(ws + h->off_probs);
@@ -1777,6 +2340,7 @@ okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* t, void*
       a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, d.n, 0.f};
     }
     a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_M, d.batch, d.m, d.n, 0.f};
+    if (h->cfg.mode == OKLS_MODE_SOAP) a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_V, d.batch, d.m, d.n, 0.f};
   }
   hipStream_t s = as_stream(stream);
   int* flag = reinterpret_cast<int*>(h->ws + h->off_flag);

@@ -27,6 +27,11 @@ hipError_t launch_gemm(const GemmArgs& a, int n_tiles, int tile, int epi, hipStr
 hipError_t launch_stats(const StatArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_cast(const CastArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_sym(const SymArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_adam(const AdamArgs& a, int n_blocks, hipStream_t s);
+enum JacKind { JAC_RESET = 0, JAC_SOLVE = 1, JAC_APPLY = 2, JAC_CHECK = 3 };
+// JAC_RESET ignores n_blocks (one block clears every job's flag); JAC_CHECK
+// takes one block per job
+hipError_t launch_jacobi(const JacArgs& a, int kind, int n_blocks, hipStream_t s);
 hipError_t launch_init_state(const InitArgs& a, int n_jobs, hipStream_t s);
 hipError_t launch_check_finite(const InitArgs& a, int n_jobs, int* flag_dev, hipStream_t s);
 // device address of the static scratch (kStaticScratchBytes) on the current

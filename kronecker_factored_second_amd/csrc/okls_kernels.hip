@@ -699,9 +699,12 @@ __device__ __forceinline__ int find_job(const Job* jobs, int n, int gb) {
   return lo;
 }
 
-__device__ __forceinline__ float nesterov_value(float m, float g, float beta1, float s_t) {
+// The momentum read of a step: s_t (na M' + nb G) with M' = beta1 M + (1 - beta1) G;
+// (na, nb) = (beta1, 1 - beta1) is the Nesterov look-ahead, (1, 0) with s_t = 1
+// the first moment M' itself.
+__device__ __forceinline__ float nesterov_value(float m, float g, float beta1, float s_t, float na, float nb) {
   const float mn = beta1 * m + (1.0f - beta1) * g;
-  return s_t * (beta1 * mn + (1.0f - beta1) * g);
+  return s_t * (na * mn + nb * g);
 }
 
 // Flat statistics loop over n4 quads from element e0: four quads per thread
@@ -709,7 +712,7 @@ __device__ __forceinline__ float nesterov_value(float m, float g, float beta1, f
 // source form, so no branch sits between the loads).
 template <int FMT, bool NEST>
 __device__ __forceinline__ void stats_flat(const char* src, const float* m, size_t e0, size_t n4, float beta1,
-                                           float s_t, float& amax, float& ss) {
+                                           float s_t, float na, float nb, float& amax, float& ss) {
   auto acc1 = [&](float x) {
     const float ax = fabsf(x);
     amax = (ax > amax || ax != ax) ? ax : amax;   // NaN propagates
@@ -718,10 +721,10 @@ __device__ __forceinline__ void stats_flat(const char* src, const float* m, size
   auto ld = [&](size_t o) -> float4 { return grad_quad<FMT>(src, o); };
   auto use = [&](const float4& g, const float4& mm) {
     if constexpr (NEST) {
-      acc1(nesterov_value(mm.x, g.x, beta1, s_t));
-      acc1(nesterov_value(mm.y, g.y, beta1, s_t));
-      acc1(nesterov_value(mm.z, g.z, beta1, s_t));
-      acc1(nesterov_value(mm.w, g.w, beta1, s_t));
+      acc1(nesterov_value(mm.x, g.x, beta1, s_t, na, nb));
+      acc1(nesterov_value(mm.y, g.y, beta1, s_t, na, nb));
+      acc1(nesterov_value(mm.z, g.z, beta1, s_t, na, nb));
+      acc1(nesterov_value(mm.w, g.w, beta1, s_t, na, nb));
     } else {
       acc1(g.x); acc1(g.y); acc1(g.z); acc1(g.w);
     }
@@ -763,7 +766,7 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
     ss += x * x;
   };
   auto value = [&](size_t o, float raw) {
-    return J.kind == ST_NESTEROV ? nesterov_value(m[o], raw, a.beta1, a.s_t) : raw;
+    return J.kind == ST_NESTEROV ? nesterov_value(m[o], raw, a.beta1, a.s_t, a.nest_a, a.nest_b) : raw;
   };
   // rows are contiguous when src_ld == cols: one flat range, 16-byte fp32 /
   // 8-byte bf16 and fp16 loads when aligned
@@ -774,13 +777,13 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(StatArgs a) {
   if (flat) {
     const size_t n4 = (e1 - e0) / 4;
     if (m != nullptr) {
-      if (fmt == GF_BF16) stats_flat<GF_BF16, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
-      else if (fmt == GF_F16) stats_flat<GF_F16, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
-      else stats_flat<GF_F32, true>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      if (fmt == GF_BF16) stats_flat<GF_BF16, true>(src, m, e0, n4, a.beta1, a.s_t, a.nest_a, a.nest_b, amax, ss);
+      else if (fmt == GF_F16) stats_flat<GF_F16, true>(src, m, e0, n4, a.beta1, a.s_t, a.nest_a, a.nest_b, amax, ss);
+      else stats_flat<GF_F32, true>(src, m, e0, n4, a.beta1, a.s_t, a.nest_a, a.nest_b, amax, ss);
     } else {
-      if (fmt == GF_BF16) stats_flat<GF_BF16, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
-      else if (fmt == GF_F16) stats_flat<GF_F16, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
-      else stats_flat<GF_F32, false>(src, m, e0, n4, a.beta1, a.s_t, amax, ss);
+      if (fmt == GF_BF16) stats_flat<GF_BF16, false>(src, m, e0, n4, a.beta1, a.s_t, a.nest_a, a.nest_b, amax, ss);
+      else if (fmt == GF_F16) stats_flat<GF_F16, false>(src, m, e0, n4, a.beta1, a.s_t, a.nest_a, a.nest_b, amax, ss);
+      else stats_flat<GF_F32, false>(src, m, e0, n4, a.beta1, a.s_t, a.nest_a, a.nest_b, amax, ss);
     }
     for (size_t o = e0 + 4 * n4 + threadIdx.x; o < e1; o += kStatThreads) {
       acc1(value(o, grad_elem(src, o, fmt)));
@@ -815,7 +818,7 @@ __device__ __forceinline__ float pow2_scale(float amax) {
 
 // One in-range source element of a cast job (the edge blocks' path).
 __device__ __noinline__ float cast_element(int kind, int ld, int g_fmt, bool write_m, bool sym_read, const char* src,
-                                           const char* g, float beta1, float s_t, int r, int c) {
+                                           const char* g, float beta1, float s_t, float na, float nb, int r, int c) {
   const size_t o = static_cast<size_t>(r) * ld + c;
   switch (kind) {
     case CA_F32: return reinterpret_cast<const float*>(src)[o];
@@ -825,7 +828,7 @@ __device__ __noinline__ float cast_element(int kind, int ld, int g_fmt, bool wri
       float* m = const_cast<float*>(reinterpret_cast<const float*>(src));
       const float mn = beta1 * m[o] + (1.0f - beta1) * gv;
       if (write_m) m[o] = mn;
-      return s_t * (beta1 * mn + (1.0f - beta1) * gv);
+      return s_t * (na * mn + nb * gv);
     }
     default: {
       // the rooted matrix is read symmetrised when it is not exactly
@@ -921,16 +924,16 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
       if (gfmt == GF_BF16) load_quads<GF_BF16>(gv, g, o0, op);
       else if (gfmt == GF_F16) load_quads<GF_F16>(gv, g, o0, op);
       else load_quads<GF_F32>(gv, g, o0, op);
-      const float b1 = a.beta1, b0 = 1.0f - a.beta1;
+      const float b1 = a.beta1, b0 = 1.0f - a.beta1, na = a.nest_a, nb = a.nest_b;
 #pragma unroll
       for (int p = 0; p < kPass; ++p) {
         const float4 mn{b1 * mo[p].x + b0 * gv[p].x, b1 * mo[p].y + b0 * gv[p].y,
                         b1 * mo[p].z + b0 * gv[p].z, b1 * mo[p].w + b0 * gv[p].w};
         if (J.write_m) *reinterpret_cast<float4*>(const_cast<float*>(f32) + o0 + p * op) = mn;
-        x[p][0] = a.s_t * (b1 * mn.x + b0 * gv[p].x);
-        x[p][1] = a.s_t * (b1 * mn.y + b0 * gv[p].y);
-        x[p][2] = a.s_t * (b1 * mn.z + b0 * gv[p].z);
-        x[p][3] = a.s_t * (b1 * mn.w + b0 * gv[p].w);
+        x[p][0] = a.s_t * (na * mn.x + nb * gv[p].x);
+        x[p][1] = a.s_t * (na * mn.y + nb * gv[p].y);
+        x[p][2] = a.s_t * (na * mn.z + nb * gv[p].z);
+        x[p][3] = a.s_t * (na * mn.w + nb * gv[p].w);
       }
     } else {
 #pragma unroll
@@ -946,7 +949,8 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         x[p][e] = (r < J.rows && c + e < J.cols)
-                      ? cast_element(J.kind, J.src_ld, gfmt, J.write_m != 0, J.sym_read != 0, src, g, a.beta1, a.s_t, r, c + e)
+                      ? cast_element(J.kind, J.src_ld, gfmt, J.write_m != 0, J.sym_read != 0, src, g, a.beta1, a.s_t,
+                                     a.nest_a, a.nest_b, r, c + e)
                       : 0.0f;
     }
   }
@@ -984,6 +988,7 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(CastArgs a) {
   }
   const float scale = J.scale_mode == SC_ABSMAX ? pow2_scale(amax) : a.scal[J.scale_slot];
   if (J.scale_mode == SC_ABSMAX && lb == 0 && threadIdx.x == 0) a.scal[J.scale_slot] = scale;
+  if (J.aux_slot >= 0 && lb == 0 && threadIdx.x == 0) a.scal[J.aux_slot] = scale * J.aux_mul;
 
   half_t* dst = reinterpret_cast<half_t*>(resolve(J.dst, a.ws, a.user));
   const bool write_lo = J.write_lo != 0;
@@ -1191,6 +1196,378 @@ __global__ void finite_kernel(InitArgs a, int* flag) {
 __global__ void zero_int_kernel(int* p) { *p = 0; }
 
 // ---------------------------------------------------------------------------
+// Eigenbasis Adam (AdamJob): V <- beta2 V + (1 - beta2) G'^2 and the direction
+// N' = (M' bc1) / (sqrt(V bc2) + eps) element by element (with eigen_m the
+// first moment M <- beta1 M + (1 - beta1) G' is updated first and is M'),
+// written into the zero-padded fp16 operand of the rotation back, or as fp32
+// (where no static bound on |N'| holds, for a cast with its own scale).  One block
+// covers kAdamRows x 256 of the padded destination; thread (wave, lane) holds
+// columns 4 lane .. 4 lane + 3 of rows wave + 4 p.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kAdamThreads) void adam_kernel(AdamArgs a) {
+  const int gb = blockIdx.x;
+  const AdamJob J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
+  const int lb = gb - J.blk_begin;
+  const int ty = lb / J.tiles_x, tx = lb - ty * J.tiles_x;
+  const int c0 = tx * 256 + 4 * (threadIdx.x & 63);
+  const float* g = reinterpret_cast<const float*>(resolve(J.g, a.ws, a.user));
+  float* m = reinterpret_cast<float*>(resolve(J.m, a.ws, a.user));
+  float* v = reinterpret_cast<float*>(resolve(J.v, a.ws, a.user));
+  const bool to16 = J.dst.kind != REF_NONE;
+  half_t* dst = to16 ? reinterpret_cast<half_t*>(resolve(J.dst, a.ws, a.user)) : nullptr;
+  float* d32 = to16 ? nullptr : reinterpret_cast<float*>(resolve(J.dst32, a.ws, a.user));
+  const float b1 = a.beta1, b1c = 1.0f - a.beta1, b2 = a.beta2, b2c = 1.0f - a.beta2;
+  const bool vec = (J.cols & 3) == 0 && (reinterpret_cast<uintptr_t>(g) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(m) & 15) == 0 && (reinterpret_cast<uintptr_t>(v) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(d32) & 15) == 0;
+  if (c0 >= J.cols_p) return;
+#pragma unroll
+  for (int p = 0; p < kAdamRows / 4; ++p) {
+    const int r = ty * kAdamRows + (threadIdx.x >> 6) + 4 * p;
+    if (r >= J.rows_p) continue;
+    float gq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, mq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const size_t o = static_cast<size_t>(r) * J.cols + c0;
+    const bool row_in = r < J.rows;
+    const bool full = row_in && vec && c0 + 3 < J.cols;
+    if (full) {
+      const float4 g4 = *reinterpret_cast<const float4*>(g + o);
+      const float4 m4 = *reinterpret_cast<const float4*>(m + o);
+      const float4 v4 = *reinterpret_cast<const float4*>(v + o);
+      gq[0] = g4.x; gq[1] = g4.y; gq[2] = g4.z; gq[3] = g4.w;
+      mq[0] = m4.x; mq[1] = m4.y; mq[2] = m4.z; mq[3] = m4.w;
+      vq[0] = v4.x; vq[1] = v4.y; vq[2] = v4.z; vq[3] = v4.w;
+    } else if (row_in) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c0 + e < J.cols) { gq[e] = g[o + e]; mq[e] = m[o + e]; vq[e] = v[o + e]; }
+    }
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (J.eigen_m) mq[e] = b1 * mq[e] + b1c * gq[e];
+      vq[e] = b2 * vq[e] + b2c * gq[e] * gq[e];
+      y[e] = (mq[e] * a.bc1) / (sqrtf(vq[e] * a.bc2) + a.eps);
+      if (!(row_in && c0 + e < J.cols)) y[e] = 0.0f;
+    }
+    if (full) {
+      *reinterpret_cast<float4*>(v + o) = float4{vq[0], vq[1], vq[2], vq[3]};
+      if (J.eigen_m) *reinterpret_cast<float4*>(m + o) = float4{mq[0], mq[1], mq[2], mq[3]};
+      if (!to16) *reinterpret_cast<float4*>(d32 + o) = float4{y[0], y[1], y[2], y[3]};
+    } else if (row_in) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c0 + e < J.cols) {
+          v[o + e] = vq[e];
+          if (J.eigen_m) m[o + e] = mq[e];
+          if (!to16) d32[o + e] = y[e];
+        }
+    }
+    if (to16) store16(dst + static_cast<size_t>(r) * J.ld16 + c0, J.lo16, a.write_lo != 0, y, a.s_out);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block Jacobi (JacJob).  Pairing: the round-robin ("circle") schedule of n
+// players, player 0 fixed and the others rotated by one each round, pairs
+// position k with position n - 1 - k; over n - 1 rounds every pair meets once.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void circle_pair(int round, int k, int n, int& p, int& q) {
+  const int a = k == 0 ? 0 : ((k - 1 + round) % (n - 1)) + 1;
+  const int kb = n - 1 - k;
+  const int b = kb == 0 ? 0 : ((kb - 1 + round) % (n - 1)) + 1;
+  p = min(a, b);
+  q = max(a, b);
+}
+// global row of local index i (0 .. kJp - 1) of the pair block (p, q)
+__device__ __forceinline__ int pair_index(int p, int q, int i) { return i < kJb ? p * kJb + i : q * kJb + i - kJb; }
+
+template <bool APPLY>
+__device__ __forceinline__ int find_jac_job(const JacJob* jobs, int n, int gb) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((APPLY ? jobs[mid].apply_begin : jobs[mid].solve_begin) <= gb) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr int kJacInnerSweeps = 12;
+
+// Diagonalises the pair block A = sym(B[I, I]), I the rows of blocks p and q,
+// by cyclic Jacobi rotations in round-robin order (kJb disjoint rotations per
+// round, applied to rows, then columns and the accumulated J), and stores J.
+// Rotation of (u, w): with tau = (a_ww - a_uu) / (2 a_uw), t = sign(tau) /
+// (|tau| + sqrt(1 + tau^2)), c = 1 / sqrt(1 + t^2), s = t c, the plane rotation
+// [[c, s], [-s, c]] zeroes a_uw (the symmetric Schur decomposition of a 2 x 2
+// block, Golub and Van Loan, "Matrix Computations", the classical Jacobi method).
+__global__ __launch_bounds__(kJacThreads) void jacobi_solve_kernel(JacArgs a) {
+  __shared__ float A[kJp][kJp + 1];
+  __shared__ float Jm[kJp][kJp + 1];
+  __shared__ float rc[kJb], rs[kJb], rdu[kJb], rdw[kJb];
+  __shared__ int ru[kJb], rw[kJb], rrot[kJb];
+  __shared__ int any_rot;
+  __shared__ float red[kJacThreads / 64];
+  const int gb = blockIdx.x;
+  const JacJob J = a.jobs[find_jac_job<false>(a.jobs, a.n_jobs, gb)];
+  const int k = gb - J.solve_begin;
+  if (a.round >= J.nb - 1 || a.flags[J.flag] != 0) return;
+  int p, q;
+  circle_pair(a.round, k, J.nb, p, q);
+  const float* B = reinterpret_cast<const float*>(resolve(J.B, a.ws, a.user));
+  const size_t d = static_cast<size_t>(J.d);
+  float ss = 0.0f;
+  for (int e = threadIdx.x; e < kJp * kJp; e += kJacThreads) {
+    const int i = e / kJp, j = e % kJp;
+    const size_t gi = pair_index(p, q, i), gj = pair_index(p, q, j);
+    float x = 0.0f;
+    if (gi < d && gj < d) x = 0.5f * (B[gi * d + gj] + B[gj * d + gi]);
+    A[i][j] = x;
+    Jm[i][j] = i == j ? 1.0f : 0.0f;
+    ss += x * x;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float fro2 = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kJacThreads / 64; ++w) fro2 += red[w];
+  // rotations below this size are rounding noise of the block (or exact zeros)
+  const float floor_abs = 1e-10f * sqrtf(fro2);
+  for (int sweep = 0; sweep < kJacInnerSweeps; ++sweep) {
+    if (threadIdx.x == 0) any_rot = 0;
+    __syncthreads();
+    for (int r = 0; r < kJp - 1; ++r) {
+      if (threadIdx.x < kJb) {
+        int u, w;
+        circle_pair(r, threadIdx.x, kJp, u, w);
+        const float auu = A[u][u], aww = A[w][w], auw = A[u][w];
+        float c = 1.0f, sn = 0.0f, du = auu, dw = aww;
+        int rot = 0;
+        if (fabsf(auw) > floor_abs && fabsf(auw) > 1e-7f * sqrtf(fabsf(auu * aww))) {
+          // in fp64, so that c and s are the fp32 roundings of one exact
+          // rotation: fp32 arithmetic here leaves c^2 + s^2 - 1 biased, and the
+          // bias compounds over the thousands of rotations a basis goes through
+          // (measured: orthogonality 1e-4 against 4e-6)
+          const double tau = (static_cast<double>(aww) - auu) / (2.0 * auw);
+          const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+          const double cd = 1.0 / sqrt(1.0 + t * t);
+          c = static_cast<float>(cd);
+          sn = static_cast<float>(t * cd);
+          du = static_cast<float>(auu - t * auw);
+          dw = static_cast<float>(aww + t * auw);
+          rot = 1;
+          any_rot = 1;
+        }
+        ru[threadIdx.x] = u; rw[threadIdx.x] = w; rc[threadIdx.x] = c; rs[threadIdx.x] = sn;
+        rdu[threadIdx.x] = du; rdw[threadIdx.x] = dw; rrot[threadIdx.x] = rot;
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < kJb * kJp; e += kJacThreads) {   // rows u, w of A
+        const int kk = e / kJp, col = e % kJp;
+        if (rrot[kk]) {
+          const int u = ru[kk], w = rw[kk];
+          const float c = rc[kk], sn = rs[kk];
+          const float xu = A[u][col], xw = A[w][col];
+          A[u][col] = c * xu - sn * xw;
+          A[w][col] = sn * xu + c * xw;
+        }
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < kJb * kJp; e += kJacThreads) {   // columns u, w of A and of J
+        const int kk = e / kJp, row = e % kJp;
+        if (rrot[kk]) {
+          const int u = ru[kk], w = rw[kk];
+          const float c = rc[kk], sn = rs[kk];
+          const float xu = A[row][u], xw = A[row][w];
+          A[row][u] = c * xu - sn * xw;
+          A[row][w] = sn * xu + c * xw;
+          const float ju = Jm[row][u], jw = Jm[row][w];
+          Jm[row][u] = c * ju - sn * jw;
+          Jm[row][w] = sn * ju + c * jw;
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x < kJb && rrot[threadIdx.x]) {   // the rotated 2 x 2 block exactly diagonal
+        const int u = ru[threadIdx.x], w = rw[threadIdx.x];
+        A[u][w] = 0.0f;
+        A[w][u] = 0.0f;
+        A[u][u] = rdu[threadIdx.x];
+        A[w][w] = rdw[threadIdx.x];
+      }
+      __syncthreads();
+    }
+    const bool more = any_rot != 0;
+    __syncthreads();
+    if (!more) break;
+  }
+  float* jb = reinterpret_cast<float*>(a.ws + J.jbuf) + static_cast<size_t>(k) * kJp * kJp;
+  for (int e = threadIdx.x; e < kJp * kJp; e += kJacThreads) jb[e] = Jm[e / kJp][e % kJp];
+}
+
+// B <- R^T B R on the pair-block tiles (P, Q), P <= Q (the lower tile gets the
+// transpose), and V <- V R on kJp-row chunks of V; every B tile records the
+// squared Frobenius norms of its off-diagonal and diagonal entries (the
+// mirrored tile counted twice).  Each thread computes a 4 x 4 block of the
+// 64 x 64 products from LDS.
+__global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
+  constexpr int LD = kJp + 4;                      // 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) float X[kJp][LD];
+  __shared__ __attribute__((aligned(16))) float JP[kJp][LD];
+  __shared__ __attribute__((aligned(16))) float JQ[kJp][LD];
+  __shared__ float red[2 * (kJacThreads / 64)];
+  const int gb = blockIdx.x;
+  const JacJob J = a.jobs[find_jac_job<true>(a.jobs, a.n_jobs, gb)];
+  if (a.round >= J.nb - 1 || a.flags[J.flag] != 0) return;
+  int t = gb - J.apply_begin;
+  const float* jb = reinterpret_cast<const float*>(a.ws + J.jbuf);
+  const size_t d = static_cast<size_t>(J.d);
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+  float acc[4][4];
+  auto product = [&](float (*L)[LD], float (*R)[LD]) {   // acc = sum_k L[k][4 tr + i] R[k][4 tc + j]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int kk = 0; kk < kJp; ++kk) {
+      const float4 l = *reinterpret_cast<const float4*>(&L[kk][4 * tr]);
+      const float4 r = *reinterpret_cast<const float4*>(&R[kk][4 * tc]);
+      const float lv[4] = {l.x, l.y, l.z, l.w}, rv[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += lv[i] * rv[j];
+    }
+  };
+  if (t < J.btiles) {
+    int P = 0, rem = t;
+    while (rem >= J.npairs - P) {
+      rem -= J.npairs - P;
+      ++P;
+    }
+    const int Q = P + rem;
+    int p1, p2, q1, q2;
+    circle_pair(a.round, P, J.nb, p1, p2);
+    circle_pair(a.round, Q, J.nb, q1, q2);
+    float* B = reinterpret_cast<float*>(resolve(J.B, a.ws, a.user));
+    const float* jp = jb + static_cast<size_t>(P) * kJp * kJp;
+    const float* jq = jb + static_cast<size_t>(Q) * kJp * kJp;
+    for (int e = threadIdx.x; e < kJp * kJp; e += kJacThreads) {
+      const int i = e / kJp, j = e % kJp;
+      const size_t gi = pair_index(p1, p2, i), gj = pair_index(q1, q2, j);
+      X[i][j] = (gi < d && gj < d) ? B[gi * d + gj] : 0.0f;
+      JP[i][j] = jp[e];
+      JQ[i][j] = jq[e];
+    }
+    __syncthreads();
+    product(JP, X);                                // T = J_P^T X
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)                    // X <- T^T (row c holds column c of T)
+      *reinterpret_cast<float4*>(&X[4 * tc + j][4 * tr]) = float4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
+    __syncthreads();
+    product(X, JQ);                                // Y = T J_Q
+    float off = 0.0f, dg = 0.0f;
+    const float wgt = P == Q ? 1.0f : 2.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t gi = pair_index(p1, p2, 4 * tr + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t gj = pair_index(q1, q2, 4 * tc + j);
+        if (gi < d && gj < d) {
+          const float y = acc[i][j];
+          B[gi * d + gj] = y;
+          if (P != Q) B[gj * d + gi] = y;
+          if (gi == gj) dg += y * y; else off += wgt * y * y;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o, 64);
+      dg += __shfl_xor(dg, o, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      red[2 * (threadIdx.x >> 6)] = off;
+      red[2 * (threadIdx.x >> 6) + 1] = dg;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float so = 0.0f, sd = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kJacThreads / 64; ++w) {
+        so += red[2 * w];
+        sd += red[2 * w + 1];
+      }
+      a.partials[2 * (J.part + t)] = so;
+      a.partials[2 * (J.part + t) + 1] = sd;
+    }
+    return;
+  }
+  t -= J.btiles;
+  const int chunk = t / J.npairs, Q = t - chunk * J.npairs;
+  int q1, q2;
+  circle_pair(a.round, Q, J.nb, q1, q2);
+  float* V = reinterpret_cast<float*>(resolve(J.V, a.ws, a.user));
+  const float* jq = jb + static_cast<size_t>(Q) * kJp * kJp;
+  const size_t r0 = static_cast<size_t>(chunk) * kJp;
+  for (int e = threadIdx.x; e < kJp * kJp; e += kJacThreads) {
+    const int i = e / kJp, j = e % kJp;            // X holds V's chunk transposed: X[j][i] = V[r0 + i][col j]
+    const size_t gj = pair_index(q1, q2, j);
+    X[j][i] = (r0 + i < d && gj < d) ? V[(r0 + i) * d + gj] : 0.0f;
+    JQ[i][j] = jq[e];
+  }
+  __syncthreads();
+  product(X, JQ);                                  // Y = V_chunk J_Q
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const size_t r = r0 + 4 * tr + i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t gj = pair_index(q1, q2, 4 * tc + j);
+      if (r < d && gj < d) V[r * d + gj] = acc[i][j];
+    }
+  }
+}
+
+// After a sweep: converged when ||off(B)||_F <= tol ||diag(B)||_F (or B = 0).
+__global__ __launch_bounds__(kJacThreads) void jacobi_check_kernel(JacArgs a) {
+  __shared__ float red[2 * (kJacThreads / 64)];
+  const JacJob J = a.jobs[blockIdx.x];
+  if (a.flags[J.flag] != 0) return;
+  float off = 0.0f, dg = 0.0f;
+  for (int t = threadIdx.x; t < J.btiles; t += kJacThreads) {
+    off += a.partials[2 * (J.part + t)];
+    dg += a.partials[2 * (J.part + t) + 1];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    off += __shfl_xor(off, o, 64);
+    dg += __shfl_xor(dg, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[2 * (threadIdx.x >> 6)] = off;
+    red[2 * (threadIdx.x >> 6) + 1] = dg;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float so = 0.0f, sd = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kJacThreads / 64; ++w) {
+      so += red[2 * w];
+      sd += red[2 * w + 1];
+    }
+    a.flags[J.flag] = (so <= a.tol * a.tol * sd) ? 1 : 0;
+  }
+}
+
+// Clears the converged flags of every job (start of a refresh).
+__global__ void jacobi_reset_kernel(JacArgs a) {
+  for (int j = threadIdx.x; j < a.n_jobs; j += blockDim.x) a.flags[a.jobs[j].flag] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
 template <class C>
@@ -1266,6 +1643,24 @@ hipError_t static_scratch(void** ptr) {
 hipError_t launch_sym(const SymArgs& a, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(sym_kernel, dim3(n_blocks), dim3(kSymThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_adam(const AdamArgs& a, int n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  adam_kernel<<<dim3(n_blocks), dim3(kAdamThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_jacobi(const JacArgs& a, int kind, int n_blocks, hipStream_t s) {
+  if (kind == JAC_RESET) {
+    jacobi_reset_kernel<<<dim3(1), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+  }
+  if (n_blocks <= 0) return hipSuccess;
+  if (kind == JAC_SOLVE) jacobi_solve_kernel<<<dim3(n_blocks), dim3(kJacThreads), 0, s>>>(a);
+  else if (kind == JAC_APPLY) jacobi_apply_kernel<<<dim3(n_blocks), dim3(kJacThreads), 0, s>>>(a);
+  else jacobi_check_kernel<<<dim3(n_blocks), dim3(kJacThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 

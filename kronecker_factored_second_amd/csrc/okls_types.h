@@ -23,7 +23,7 @@ constexpr int kScaleExp = 14;        // dynamic casts put max |x| in (2^13, 2^14
 // caller tensor of one group (byte offset from that tensor's base).
 enum RefKind : int32_t {
   REF_NONE = -1, REF_WS = 0, REF_W = 1, REF_G = 2, REF_M = 3,
-  REF_SA = 4, REF_SB = 5, REF_PA = 6, REF_PB = 7
+  REF_SA = 4, REF_SB = 5, REF_PA = 6, REF_PB = 7, REF_V = 8
 };
 struct Ref {
   int32_t kind;
@@ -40,7 +40,7 @@ struct TileRef {
 
 // Caller pointers of one okls_step, passed by value to every launch.
 struct UserPtrs {
-  void* p[kMaxGroups][8];
+  void* p[kMaxGroups][9];
 };
 
 // ---------------------------------------------------------------------------
@@ -124,6 +124,7 @@ struct StatArgs {
   int32_t blk_offset;      // block numbering offset (jobs' blk_begin is global)
   float* partials;         // float2 per block: (absmax, sumsq)
   float beta1, s_t;
+  float nest_a, nest_b;    // ST_NESTEROV value s_t (nest_a M' + nest_b G)
   char* ws;
   UserPtrs user;
 };
@@ -177,6 +178,8 @@ struct CastJob {
   int32_t write_lo2;
   Ref dstT;                // non-transposed jobs: transposed copy of the destination, or REF_NONE
   int32_t dstT_ld, dstT_lo;   // (dst_cols_p x dst_rows_p; same scale and lo flag as dst)
+  int32_t aux_slot;        // if >= 0: receives the job's scale times aux_mul (a derived static
+  float aux_mul;           // scale for a product of this operand with an orthogonal matrix)
 };
 
 struct CastArgs {
@@ -186,6 +189,7 @@ struct CastArgs {
   const float* partials;
   float* scal;
   float beta1, s_t, ka, kb;
+  float nest_a, nest_b;    // CA_NESTEROV value s_t (nest_a M' + nest_b G)
   char* ws;
   UserPtrs user;
 };
@@ -212,6 +216,76 @@ struct SymArgs {
   const SymJob* jobs;
   int32_t n_jobs;
   const float* scal;
+  char* ws;
+  UserPtrs user;
+};
+
+// ---------------------------------------------------------------------------
+// Eigenbasis Adam (SOAP): element-wise second moment and direction from the
+// rotated gradient G' and first moment M' (fp32), written as the padded fp16
+// operand of the rotation back (static scale).
+// ---------------------------------------------------------------------------
+constexpr int kAdamRows = 16;        // destination rows of one block (256 columns)
+constexpr int kAdamThreads = 256;
+
+struct AdamJob {
+  Ref g;                   // G' (rows x cols fp32, row stride cols)
+  Ref m;                   // M' (same layout); with eigen_m the caller's M, updated in place
+  Ref v;                   // the caller's V (same layout), updated in place
+  Ref dst;                 // N' fp16, rows_p rows of ld16 halves, lo at +lo16 (static scale s_out);
+                           // REF_NONE: N' goes to dst32 instead
+  Ref dst32;               // N' fp32 (rows x cols, row stride cols); may be g itself (read first)
+  int32_t rows, cols, rows_p, cols_p, ld16, lo16;
+  int32_t eigen_m;         // 1: M <- beta1 M + (1 - beta1) G' first (moments kept in the eigenbasis)
+  int32_t tiles_x;         // blocks along the columns (256 each)
+  int32_t blk_begin;
+};
+
+struct AdamArgs {
+  const AdamJob* jobs;
+  int32_t n_jobs;
+  float beta1, beta2, eps;
+  float bc1, bc2;          // 1 / (1 - beta^t), or 1 without bias correction
+  float s_out;             // static scale of the fp16 direction
+  int32_t write_lo;
+  char* ws;
+  UserPtrs user;
+};
+
+// ---------------------------------------------------------------------------
+// Block Jacobi eigensolver (two-sided, cyclic over pairs of kJb-row blocks in
+// round-robin order).  A round pairs every block with one other; the solve
+// kernel diagonalises each pair's 2 kJb x 2 kJb principal submatrix with
+// scalar Jacobi rotations and stores the accumulated rotation J; the apply
+// kernel then updates B <- R^T B R (R the block-diagonal product of the
+// round's J, in the pair ordering) and V <- V R.  A sweep is nb - 1 rounds;
+// after each sweep the check kernel compares the off-diagonal Frobenius norm
+// with the diagonal's and marks the matrix converged.
+// ---------------------------------------------------------------------------
+constexpr int kJb = 32;
+constexpr int kJp = 2 * kJb;         // side of a pair block
+constexpr int kJacThreads = 256;
+
+struct JacJob {
+  Ref B;                   // d x d fp32 (row stride d): Q^T A Q on entry, rotated in place
+  Ref V;                   // d x d fp32 (row stride d): the basis Q on entry, rotated in place
+  int32_t d, nb, npairs;   // nb: blocks (even, nb * kJb >= d), npairs = nb / 2
+  int32_t btiles;          // pair-block tiles of B on and above the diagonal, npairs (npairs + 1) / 2
+  int32_t vrows;           // kJp-row chunks of V, ceil(d / kJp)
+  int64_t jbuf;            // workspace byte offset of npairs kJp x kJp rotations (fp32)
+  int32_t part;            // first partial (float2 per B tile)
+  int32_t flag;            // index of the converged flag
+  int32_t solve_begin;     // first block of the job in a solve launch
+  int32_t apply_begin;     // first block of the job in an apply launch
+};
+
+struct JacArgs {
+  const JacJob* jobs;
+  int32_t n_jobs;
+  int32_t round;           // 0 .. nb - 2 (jobs with fewer rounds skip the rest)
+  float tol;               // converged when ||off(B)||_F <= tol ||diag(B)||_F
+  float* partials;         // float2 (off^2, diag^2) per B tile
+  int32_t* flags;
   char* ws;
   UserPtrs user;
 };

@@ -17,14 +17,18 @@ OKLS_OK = 0
 STATUS = {0: "OKLS_OK", -1: "OKLS_ERR_INVALID_ARG", -2: "OKLS_ERR_SHAPE", -3: "OKLS_ERR_DTYPE",
           -4: "OKLS_ERR_WORKSPACE", -5: "OKLS_ERR_HIP", -6: "OKLS_ERR_NONFINITE", -7: "OKLS_ERR_UNSUPPORTED"}
 OKLS_F32, OKLS_BF16, OKLS_F16 = 0, 1, 2
-MODE = {"okls": 0, "shampoo": 1, "muon": 2}
+MODE = {"okls": 0, "shampoo": 1, "muon": 2, "soap": 3}
 # the Muon setting of the polar iteration: 5 steps (Clean, Table 6) on [1e-2, 1]
 MUON_DEFAULTS = dict(ns_steps=5, ns_floor=1e-2)
+# optimizer hyperparameters per mode: the README's "Hyperparameters" table, and
+# SOAP's from the Clean paper's Tables 4 and 6
+HYPER_DEFAULTS = {"okls": dict(lr=0.09434, beta1=0.9684, beta2=0.9482, eps=1e-9, weight_decay=0.0303),
+                  "soap": dict(lr=2.8e-3, beta1=0.95, beta2=0.95, eps=1e-8, weight_decay=0.1)}
 EXPORTED = ("okls_default_config", "okls_workspace_size", "okls_init", "okls_init_state", "okls_step",
             "okls_check_finite", "okls_ns_coefficients", "okls_profile_enable", "okls_profile_read",
             "okls_destroy", "okls_status_string", "okls_plan_query", "okls_init_static")
 STATIC_SCRATCH_BYTES = 128 << 20
-PROFILE_CATEGORIES = ("ns_gemm", "factor_gemm", "whiten_gemm", "stats", "cast")
+PROFILE_CATEGORIES = ("ns_gemm", "factor_gemm", "whiten_gemm", "stats", "cast", "eigensolver")
 
 
 class Config(ctypes.Structure):
@@ -34,7 +38,9 @@ class Config(ctypes.Structure):
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("lr_peak", ctypes.c_float),
                 ("ns_floor", ctypes.c_float), ("ns_damping", ctypes.c_float), ("root_period", ctypes.c_int32),
                 ("eps_convex", ctypes.c_int32), ("decay_after", ctypes.c_int32), ("shape_scale", ctypes.c_int32),
-                ("ns_classical", ctypes.c_int32), ("whiten_split", ctypes.c_int32)]
+                ("ns_classical", ctypes.c_int32), ("whiten_split", ctypes.c_int32),
+                ("soap_beta", ctypes.c_float), ("precond_freq", ctypes.c_int32), ("soap_moments", ctypes.c_int32),
+                ("bias_correction", ctypes.c_int32), ("jacobi_sweeps", ctypes.c_int32), ("jacobi_tol", ctypes.c_float)]
 
 
 class GroupDesc(ctypes.Structure):
@@ -44,18 +50,18 @@ class GroupDesc(ctypes.Structure):
 
 class GroupTensors(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("M", ctypes.c_void_p), ("Sa", ctypes.c_void_p),
-                ("Sb", ctypes.c_void_p), ("Pa", ctypes.c_void_p), ("Pb", ctypes.c_void_p)]
+                ("Sb", ctypes.c_void_p), ("Pa", ctypes.c_void_p), ("Pb", ctypes.c_void_p), ("V", ctypes.c_void_p)]
 
 
 class ProfileStats(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 5), ("busy_ms", ctypes.c_double * 5), ("flops", ctypes.c_double * 5),
-                ("bytes", ctypes.c_double * 5),
-                ("launches", ctypes.c_int64 * 5), ("steps", ctypes.c_int64)]
+    _fields_ = [("ms", ctypes.c_double * 6), ("busy_ms", ctypes.c_double * 6), ("flops", ctypes.c_double * 6),
+                ("bytes", ctypes.c_double * 6),
+                ("launches", ctypes.c_int64 * 6), ("steps", ctypes.c_int64)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("chunks", ctypes.c_int32), ("launches", ctypes.c_int32), ("launches_stale", ctypes.c_int32),
-                ("ns_chains", ctypes.c_int32), ("flops", ctypes.c_double * 5), ("bytes", ctypes.c_double * 5)]
+                ("ns_chains", ctypes.c_int32), ("flops", ctypes.c_double * 6), ("bytes", ctypes.c_double * 6)]
 
 
 class OKLSError(RuntimeError):
@@ -132,7 +138,8 @@ def precision_config(precision: str = "fp16", **overrides) -> Config:
     """'fp16': the Newton-Schulz and factor GEMMs with plain fp16 inputs (the
     pages' path), the whitening products split-fp16 (whiten_split).
     'fp32': every GEMM split-fp16 (hi*hi + hi*lo + lo*hi), fp32-accurate.
-    Each takes the coefficient table's floor matched to its arithmetic."""
+    Each takes the coefficient table's floor matched to its arithmetic.
+    (SOAP mode follows factor_split alone: every product split with 'fp32'.)"""
     if precision == "fp16":
         base = dict(ns_split_steps=0, factor_split=0, whiten_split=1, ns_floor=3e-2, ns_damping=0.0)
     elif precision == "fp32":
@@ -210,11 +217,11 @@ def _ptr(t):
 
 
 def tensors_array(per_group):
-    """per_group: list of dicts with torch tensors W, G, M, Sa, Sb, Pa, Pb."""
+    """per_group: list of dicts with torch tensors W, G, M, Sa, Sb, Pa, Pb (and V in SOAP mode)."""
     arr = (GroupTensors * len(per_group))()
     for i, d in enumerate(per_group):
         arr[i] = GroupTensors(*[(d[k].data_ptr() if d.get(k) is not None else None)
-                                for k in ("W", "G", "M", "Sa", "Sb", "Pa", "Pb")])
+                                for k in ("W", "G", "M", "Sa", "Sb", "Pa", "Pb", "V")])
     return arr
 
 
@@ -284,7 +291,7 @@ class OKLS:
     with workspace_limit (bytes) set and chunk_matrices = 0, the largest
     chunk whose workspace fits the limit is chosen."""
 
-    def __init__(self, params, lr=0.09434, beta1=0.9684, beta2=0.9482, eps=1e-9, weight_decay=0.0303,
+    def __init__(self, params, lr=None, beta1=None, beta2=None, eps=None, weight_decay=None,
                  mode="okls", precision="fp16", grad_dtype=None, chunk_matrices=0, workspace_limit=None,
                  **cfg_overrides):
         import torch
@@ -292,6 +299,12 @@ class OKLS:
         self.params = list(params)
         if not self.params:
             raise ValueError("no parameters")
+        hyper = HYPER_DEFAULTS["soap" if mode == "soap" else "okls"]
+        lr = hyper["lr"] if lr is None else lr
+        beta1 = hyper["beta1"] if beta1 is None else beta1
+        beta2 = hyper["beta2"] if beta2 is None else beta2
+        eps = hyper["eps"] if eps is None else eps
+        weight_decay = hyper["weight_decay"] if weight_decay is None else weight_decay
         self.lr = float(lr)
         self.mode = mode
         if mode == "muon":
@@ -315,6 +328,10 @@ class OKLS:
             self.groups.append((b, m, n, gdt))
             if mode == "muon":     # no factors or roots
                 self.state.append(dict(M=torch.zeros(b, m, n, device=dev)))
+            elif mode == "soap":   # factors, bases and both moments
+                self.state.append(dict(M=torch.zeros(b, m, n, device=dev), V=torch.zeros(b, m, n, device=dev),
+                                       Sa=torch.empty(b, m, m, device=dev), Sb=torch.empty(b, n, n, device=dev),
+                                       Pa=torch.empty(b, m, m, device=dev), Pb=torch.empty(b, n, n, device=dev)))
             else:
                 self.state.append(dict(M=torch.zeros(b, m, n, device=dev), Sa=torch.empty(b, m, m, device=dev),
                                        Sb=torch.empty(b, n, n, device=dev), Pa=torch.empty(b, m, m, device=dev),
