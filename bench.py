@@ -60,9 +60,12 @@ def parse():
     p.add_argument("--device-grads", action="store_true",
                    help="gradients of the workload's recipe drawn on the GPU (the default for "
                         "workloads above 1e9 parameters, whose host recipes would take minutes per step)")
-    p.add_argument("--mode", choices=["okls", "shampoo", "muon"], default=None,
+    p.add_argument("--mode", choices=["okls", "shampoo", "muon", "soap"], default=None,
                    help="optimizer mode (default: the workload's); muon runs the polar iteration of the momentum "
-                        "on the same matrices, the pages' throughput comparison")
+                        "on the same matrices, the pages' throughput comparison; soap runs Adam in the factors' "
+                        "eigenbasis (bases refreshed every --precond-freq steps)")
+    p.add_argument("--precond-freq", type=int, default=10,
+                   help="soap mode: refresh the eigenbases after every this many steps (the Clean paper's Table 6: 10)")
     p.add_argument("--root-period", type=int, default=1,
                    help="recompute the roots every this many steps (1: every step)")
     p.add_argument("--copy-probe", action="store_true",
@@ -235,6 +238,42 @@ def progress(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_baseline_soap(w, budget_s, freq):
+    """The fp64 eigenbasis-Adam oracle on the same bounded sample as
+    cpu_baseline: per shape class one step that keeps the bases and one that
+    refreshes them (eigh of both factors), averaged over one period of freq
+    steps and scaled to the workload's matrix counts."""
+    from oracle import soap_oracle as S
+    from kronecker_factored_second_amd import workloads as WL
+    hp = S.SoapHyper(freq=freq)
+    total_s, step_s, sampled, timed = 0.0, 0.0, [], {}
+    for gi, (m, n, b) in enumerate(w.groups):
+        key = (min(m, n), max(m, n))
+        if key in timed:
+            sampled.append(f"{m}x{n}: as {timed[key][0]}")
+            step_s += timed[key][1] * b
+            continue
+        G = WL.gradient(w, gi, 0, 1).astype(np.float64)
+        st = S.init_state(np.zeros((m, n)))
+        t0 = time.perf_counter()
+        S.soap_step(st, G, hp, 1)
+        dt_keep = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        S.soap_step(st, G, hp, freq)
+        dt_ref = time.perf_counter() - t0
+        total_s += dt_keep + dt_ref
+        dt = (dt_ref + (freq - 1) * dt_keep) / freq
+        sampled.append(f"{m}x{n}:{dt:.2f}s")
+        timed[key] = (f"{m}x{n}", dt)
+        step_s += dt * b
+        if total_s > budget_s:
+            return None
+    return {"value": w.n_matrices / step_s, "unit": "matrices/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"per shape class one fp64 oracle step keeping the bases and one refreshing them, averaged "
+                      f"over {freq} steps ({', '.join(sampled)}), scaled to the {w.n_matrices}-matrix workload: "
+                      f"{step_s:.2f} s/step"}
+
+
 def cpu_baseline(w, budget_s, root_period=1, mode=None):
     """The fp64 oracle, as it stands, on a bounded sample: one matrix of each
     distinct shape class of the workload, a full oracle step each (exact eigh
@@ -348,9 +387,9 @@ def main():
     if big:   # leave room for the caller's tensors: the workspace takes what the card has left
         limit = torch.cuda.mem_get_info(0)[0] - sum(b * (m * n + 2 * m * m + 2 * n * n) * 4 for m, n, b in w.groups) \
             - (8 << 30)
+    extra = dict(precond_freq=args.precond_freq) if mode == "soap" else dict(root_period=args.root_period)
     opt = okls.OKLS(params, mode=mode, precision=args.precision,
-                    grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit,
-                    root_period=args.root_period)
+                    grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit, **extra)
     progress(f"{w.name}: optimizer ready (workspace {opt.workspace.numel() / 2**30:.1f} GiB)")
     for i in range(args.warmup):
         opt.step(grads=grads[i % n_bufs])
@@ -430,7 +469,8 @@ def main():
                                                    " (device Gaussian)") if device_grads else "") +
                    f", precision {args.precision}" +
                    (f", chunks of {opt.cfg.chunk_matrices} matrices" if opt.cfg.chunk_matrices else "") +
-                   (f", roots every {args.root_period} steps" if args.root_period > 1 else ""),
+                   (f", roots every {args.root_period} steps" if args.root_period > 1 and mode != "soap" else "") +
+                   (f", eigenbases refreshed every {args.precond_freq} steps" if mode == "soap" else ""),
                    "matrices": w.n_matrices, "parallelism": "single GPU"},
         "step_latency_ms": ms_step,
         "step_latency_ms_median": lat_median,
@@ -460,7 +500,8 @@ def main():
         "host_wall_s": wall,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds, args.root_period, mode)
+        line["cpu_baseline"] = (cpu_baseline_soap(w, args.cpu_sample_seconds, args.precond_freq) if mode == "soap"
+                                else cpu_baseline(w, args.cpu_sample_seconds, args.root_period, mode))
     print(json.dumps(line), flush=True)
 
 

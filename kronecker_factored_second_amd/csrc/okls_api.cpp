@@ -947,8 +947,9 @@ struct Planner {
   //   GEMM   (N' Q_b^T)^T = Q_b N'^T                             -> fp16
   //   GEMM   W <- decay W - lr Q_a (N' Q_b^T)
   //   GEMM   S_a <- sb S_a + (1-sb) G G^T, S_b likewise (upper tiles, mirrored)
-  //   refresh: stats + cast of S, (Q^T S) as fp16, B = Q^T S Q in fp32, then
-  //   block Jacobi sweeps on B that rotate the caller's Q in place.
+  //   refresh: stats + cast of S, (Q^T S) as fp16, B = Q^T S Q in fp32 (these
+  //   products split-fp16 in either precision), then block Jacobi sweeps on B
+  //   that rotate the caller's Q in place, then one orthogonalisation step.
   void plan_soap(std::vector<LaunchRec>& L, std::vector<MatBufs>& mats, bool refresh) {
     const int fs = cfg.factor_split;
     const bool param_m = cfg.soap_moments == 0;
@@ -1007,7 +1008,7 @@ struct Planner {
         c.kind = CA_F32; c.src = user_ref(kinds[sd], mb.group, offs[sd]); c.src_ld = F.d;
         c.rows = c.cols = F.d; c.dst_rows_p = c.dst_cols_p = F.dp; c.dst = ws_ref(F.Q16);
         c.dst_ld = F.ldq; c.dst_lo = F.dp; c.parts = parts[per * q]; c.scale_mode = SC_STATIC;
-        c.scale_slot = SL_Q; c.write_lo = fs;
+        c.scale_slot = SL_Q; c.write_lo = refresh ? 1 : fs;   // a refresh reads Q^T split
         c.dstT = ws_ref(F.Q16T); c.dstT_ld = F.ldq; c.dstT_lo = F.dp;
         cs.push_back(c);
       }
@@ -1163,7 +1164,7 @@ struct Planner {
       CastSpec c = cast_spec();
       c.kind = CA_F32; c.src = fsrc[f]; c.src_ld = F.d; c.rows = c.cols = F.d;
       c.dst_rows_p = c.dst_cols_p = F.dp; c.dst = ws_ref(F.L16); c.dst_ld = F.ldq; c.dst_lo = F.dp;
-      c.parts = fparts[f]; c.scale_mode = SC_ABSMAX; c.scale_slot = F.s_l; c.write_lo = fs;
+      c.parts = fparts[f]; c.scale_mode = SC_ABSMAX; c.scale_slot = F.s_l; c.write_lo = 1;
       c.aux_slot = F.s_lx; c.aux_mul = xmul(F.d);
       cf.push_back(c);
     }
@@ -1183,8 +1184,11 @@ struct Planner {
         b.out32 = ws_ref(F.B32); b.ld32 = F.d; b.sA = SL_Q; b.sB = F.s_lx;
         pb.push_back(b);
       }
-      add_gemm(L, ph, false, fs, fs);
-      add_gemm(L, pb, false, fs, 0);
+      // split-fp16 whatever the precision: the sweeps converge on B as it is
+      // computed, and fp16 operands would leave ~1e-3 of it off the diagonal
+      // for them to chase
+      add_gemm(L, ph, false, 1, 1);
+      add_gemm(L, pb, false, 1, 0);
     }
     // 8. Jacobi sweeps: reset, then per sweep every round's solve and apply, and a check
     const int first = static_cast<int>(jac_jobs.size());
