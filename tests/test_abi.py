@@ -231,6 +231,61 @@ def test_plan_query_flops_are_the_closed_forms():
         assert f["ns_gemm"] == pytest.approx(sum(4 * k * float(min(m, n)) ** 2 * max(m, n) for m, n in mats), rel=1e-12)
 
 
+def _soap_cfg(precision="fp32", **kw):
+    base = dict(mode=okls.MODE["soap"], beta1=0.95, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    base.update(kw)
+    return okls.precision_config(precision, **base)
+
+
+def test_soap_plans_validate_and_flops_are_the_closed_forms():
+    """SOAP mode plans and validates for ragged, tiny, wide, tall and
+    transformer-block shapes on both paths and both moment placements; a
+    step that keeps the bases launches fewer kernels; the FLOPs per category
+    are the closed forms: the rotations 6 m n (m + n) (G and M in, N' out;
+    4 with the moments in the eigenbasis), the factor EMAs m n (m + n) (upper
+    triangles), and on a refresh 4 d^3 for Q^T S Q plus 4 d^3 for the
+    orthogonalisation step per factor side d."""
+    _lib()
+    shapes = ([(2, 96, 160, 0), (1, 200, 72, 0)], [(1, 1, 7, 0), (3, 33, 40, 1)],
+              [(4, 1024, 1024, 1), (2, 2816, 1024, 1), (1, 1024, 2816, 1)])
+    for prec in ("fp16", "fp32"):
+        for moments in (0, 1):
+            for groups in shapes:
+                cfg = _soap_cfg(prec, soap_moments=moments, precond_freq=3)
+                assert okls.workspace_size(cfg, groups) > 0, (prec, moments, groups)
+                info = okls.plan_query(cfg, groups)
+                assert info["launches_stale"] < info["launches"] and info["ns_chains"] == 0
+                mats = [(m, n) for b, m, n, _ in groups for _ in range(b)]
+                cube = sum(float(m) ** 3 + float(n) ** 3 for m, n in mats)
+                mn = sum(float(m) * n * (m + n) for m, n in mats)
+                f = info["flops"]
+                assert f["whiten_gemm"] == pytest.approx((4 if moments else 6) * mn, rel=1e-12)
+                assert f["factor_gemm"] == pytest.approx(mn, rel=1e-12)
+                assert f["ns_gemm"] == pytest.approx(8 * cube, rel=1e-12)
+                assert f["eigensolver"] > 0
+    # every step refreshes: one plan
+    info = okls.plan_query(_soap_cfg(precond_freq=1), shapes[0])
+    assert info["launches_stale"] == info["launches"]
+
+
+def test_soap_config_validation():
+    """The direction's fp16 operand needs a bounded Adam ratio (beta1^2 <
+    beta2, or beta1 = 0); eps must be positive; the refresh period, the
+    sweep cap and the tolerance are range-checked."""
+    _lib()
+    g = [(1, 64, 80, 0)]
+    assert okls.workspace_size(_soap_cfg(), g) > 0
+    assert okls.workspace_size(_soap_cfg(beta1=0.0, beta2=0.0), g) > 0
+    with pytest.raises(okls.OKLSError, match="UNSUPPORTED"):
+        okls.plan_query(_soap_cfg(beta1=0.99, beta2=0.95), g)
+    for bad in (dict(eps=0.0), dict(precond_freq=0), dict(jacobi_sweeps=0), dict(jacobi_sweeps=65),
+                dict(jacobi_tol=0.0), dict(soap_moments=2), dict(bias_correction=3), dict(soap_beta=1.0),
+                dict(beta2=1.0)):
+        assert okls.workspace_size(_soap_cfg(**bad), g) == 0, bad
+        with pytest.raises(okls.OKLSError, match="INVALID_ARG"):
+            okls.plan_query(_soap_cfg(**bad), g)
+
+
 def test_plan_query_rejects_invalid_arguments():
     _lib()
     cfg = okls.precision_config("fp16")
