@@ -85,7 +85,7 @@ typedef enum {
                                 the Clean paper's Table 6: 5 iterations).  ns_steps and
                                 ns_floor are the iteration's (Muon setting: 5 and 1e-2);
                                 beta2, eps, ns_damping and root_period are not used */
-    OKLS_MODE_SOAP = 3       /* Adam in the factors' eigenbasis ("Clean: Second-order LLM
+    OKLS_MODE_SOAP = 3,      /* Adam in the factors' eigenbasis ("Clean: Second-order LLM
                                 Training at Linear Memory Cost via Nystrom Sketching",
                                 Appendix C, Algorithm 4 (SOAP); "KPOP Optimiser Explained",
                                 "Transforming the Gradient"): per matrix
@@ -102,6 +102,23 @@ typedef enum {
                                   ns_*, nesterov_var_corr, root_period, eps_convex,
                                   decay_after and shape_scale are not used; the GEMMs are
                                   split-fp16 (fp32-accurate) when factor_split is 1 */
+    OKLS_MODE_NYSTROM = 4    /* low-rank Nystrom factors ("Clean: Second-order LLM Training at
+                                Linear Memory Cost via Nystrom Sketching", section 2.2 eq. (4)-(5),
+                                section 3 eq. (6)-(10), Appendix A Algorithms 2-3): per side
+                                (S_a = L of G G^T, S_b = R of G^T G) only U (d x r', orthonormal
+                                columns) and Lambda (r') are stored, r' = min(nys_rank, d).  On
+                                steps t = 1, 1 + T, ... (T = root_period) both are refreshed by
+                                the warm-started randomized Nystrom approximation of
+                                beta2 U Lambda U^T + (1 - beta2) G G^T (the sketch formed through
+                                the stored factors, eq. (8)), with nys_oversample extra columns
+                                and nys_passes subspace-iteration passes; every step then
+                                preconditions the Nesterov momentum N of the OKLS mode,
+                                U = P_a^-1/2 N P_b^-1/2 with P^-1/2 = c U D U^T + (I - U U^T),
+                                D = (Lambda + eps)^-1/2, c = (lambda_r' + eps)^1/2 (eq. (9)), and
+                                updates W as the OKLS mode does.  Tensors: Pa / Pb hold U
+                                ((N, m, r'a) / (N, n, r'b)), Sa / Sb hold Lambda ((N, r'a) /
+                                (N, r'b)), PsiA / PsiB the refresh's Gaussian matrices.  All
+                                arithmetic is fp32 (the products are thin); r + p <= 128. */
 } okls_mode;
 
 typedef struct {
@@ -169,6 +186,10 @@ typedef struct {
                                   need 12 sweeps at d = 1024 and 13 at d = 2816) */
     float jacobi_tol;          /* a refresh stops once ||off(Q^T S Q)||_F <= tol ||diag||_F
                                   (default 2e-6) */
+    /* OKLS_MODE_NYSTROM only: */
+    int32_t nys_rank;          /* r >= 1: eigenpairs kept per factor (default 32) */
+    int32_t nys_oversample;    /* p >= 0: extra sketch columns, r + p <= 128 (default 8) */
+    int32_t nys_passes;        /* q, 0..8: subspace-iteration passes of a refresh (default 1) */
 } okls_config;
 
 typedef struct {
@@ -187,6 +208,10 @@ typedef struct {
     float* Pb;         /* (N, n, n) right preconditioner */
                        /* OKLS_MODE_MUON reads none of Sa, Sb, Pa, Pb: they may be NULL */
     float* V;          /* (N, m, n) second moment, OKLS_MODE_SOAP only (else NULL) */
+    const float* PsiA; /* OKLS_MODE_NYSTROM: (N, m, k_a) standard Gaussian matrix of the refresh,
+                          k_a = min(nys_rank + nys_oversample, m), read on refresh steps (the
+                          caller draws it: the method's random numbers are inputs); else NULL */
+    const float* PsiB; /* (N, n, k_b), likewise */
 } okls_group_tensors;
 
 typedef struct okls_handle okls_handle;

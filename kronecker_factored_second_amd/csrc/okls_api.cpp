@@ -14,6 +14,8 @@
 //   GEMM  U = P_a V with the fused update W <- decay W - lr c_shape U
 // The order is the "Online KL Shampoo" README's "How it works": factors
 // with the previous preconditioners, fresh roots, whitening, update.
+// The Nystrom mode (plan_nys) keeps low-rank factors refreshed by the Clean
+// paper's Algorithm 3 and preconditions the momentum with P^-1/2 (fp32).
 // The SOAP mode (plan_soap) runs the Clean paper's Algorithm 4 instead:
 // rotations into the eigenbasis, the Adam kernel, the rotation back with the
 // fused update, the factor EMAs, and on refresh steps Q^T S Q followed by
@@ -126,9 +128,17 @@ struct MatBufs {
   // SOAP: M' fp16, (G Q_b)^T and (M Q_b)^T fp16, G' and M' fp32, N' fp16, (N' Q_b^T)^T fp16
   size_t M16 = 0, XGT16 = 0, XMT16 = 0, Gr32 = 0, Mr32 = 0, NP16 = 0, ZT16 = 0;
   int s_m = 0, s_gx = 0, s_mx = 0;
+  // Nystrom: N (fp32, overwritten by the preconditioned U), N U_b, U_a^T N', U_a E_a, U_b E_b
+  size_t N32 = 0, X32 = 0, Z32 = 0, UtA = 0, UtB = 0;
+  struct NysSide {
+    int d = 0, k = 0, r = 0;           // side, sketch columns, kept eigenpairs
+    size_t Om = 0, Yb = 0, Fb = 0, T1 = 0, T2 = 0, gram = 0, cm = 0, zp = 0, kout = 0, scratch = 0;
+    int s_nu = 0, s_nuu = 0;
+  } ns[2];
 };
 
-enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4, L_SYM = 5, L_ADAM = 6, L_JAC = 7 };
+enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4, L_SYM = 5, L_ADAM = 6, L_JAC = 7,
+                  L_G32 = 8, L_NORTH = 9, L_NSMALL = 10, L_NELEM = 11 };
 
 struct LaunchRec {
   int type = L_STAT;
@@ -180,7 +190,7 @@ struct okls_handle {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_sym = 0, off_scal = 0, off_part = 0, off_flag = 0;
-  size_t off_adam = 0, off_jac = 0;
+  size_t off_adam = 0, off_jac = 0, off_g32 = 0, off_north = 0, off_nsmall = 0, off_nelem = 0;
   float s_np = 1.0f;                        // SOAP: static scale of the Adam direction
   std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
   std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them
@@ -217,7 +227,8 @@ namespace {
 // ---------------------------------------------------------------------------
 okls_status check_config(const okls_config* c) {
   if (c == nullptr) return OKLS_ERR_INVALID_ARG;
-  if (c->mode != OKLS_MODE_OKLS && c->mode != OKLS_MODE_SHAMPOO && c->mode != OKLS_MODE_MUON && c->mode != OKLS_MODE_SOAP)
+  if (c->mode != OKLS_MODE_OKLS && c->mode != OKLS_MODE_SHAMPOO && c->mode != OKLS_MODE_MUON && c->mode != OKLS_MODE_SOAP &&
+      c->mode != OKLS_MODE_NYSTROM)
     return OKLS_ERR_INVALID_ARG;
   if (c->ns_steps < 2 || c->ns_steps > 16) return OKLS_ERR_INVALID_ARG;
   if (c->ns_split_steps < 0 || c->ns_split_steps > c->ns_steps) return OKLS_ERR_INVALID_ARG;
@@ -243,6 +254,12 @@ okls_status check_config(const okls_config* c) {
     // the direction is bounded (and its fp16 operand can take a static scale)
     // only when beta1^2 < beta2, or beta1 = 0
     if (!(c->beta1 == 0.f || static_cast<double>(c->beta1) * c->beta1 < c->beta2)) return OKLS_ERR_UNSUPPORTED;
+  }
+  if (c->mode == OKLS_MODE_NYSTROM) {
+    if (!(c->beta2 >= 0.f && c->beta2 < 1.f)) return OKLS_ERR_INVALID_ARG;
+    if (!(c->eps > 0.f)) return OKLS_ERR_INVALID_ARG;      // P^-1/2 divides by lambda + eps
+    if (c->nys_rank < 1 || c->nys_oversample < 0 || c->nys_passes < 0 || c->nys_passes > 8) return OKLS_ERR_INVALID_ARG;
+    if (c->nys_rank + c->nys_oversample > kNysMaxK) return OKLS_ERR_UNSUPPORTED;
   }
   return OKLS_OK;
 }
@@ -288,6 +305,7 @@ struct Planner {
   bool okls_mode;
   bool muon_mode;
   bool soap_mode;
+  bool nys_mode;
   bool lo_layout;
   bool single_chain = false;   // never plan a second Newton-Schulz chain (no side stream)
   std::vector<double> na, nb;
@@ -301,6 +319,10 @@ struct Planner {
   std::vector<SymJob> sym_jobs;
   std::vector<AdamJob> adam_jobs;
   std::vector<JacJob> jac_jobs;
+  std::vector<Gemm32Prob> g32_jobs;
+  std::vector<NysOrthJob> north_jobs;
+  std::vector<NysSmallJob> nsmall_jobs;
+  std::vector<NysElemJob> nelem_jobs;
   float s_np = 1.0f;          // SOAP: static scale of the Adam direction's fp16 operand
   std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
   std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them (root_period > 1)
@@ -314,7 +336,8 @@ struct Planner {
 
   Planner(const okls_config& c, const std::vector<okls_group_desc>& g)
       : cfg(c), groups(g), okls_mode(c.mode == OKLS_MODE_OKLS), muon_mode(c.mode == OKLS_MODE_MUON),
-        soap_mode(c.mode == OKLS_MODE_SOAP), lo_layout(c.factor_split != 0 || c.ns_split_steps > 0) {
+        soap_mode(c.mode == OKLS_MODE_SOAP), nys_mode(c.mode == OKLS_MODE_NYSTROM),
+        lo_layout(c.factor_split != 0 || c.ns_split_steps > 0) {
     if (soap_mode) {
       first_dyn = n_slots = SL_FIRST_DYN_SOAP;
       s_np = pow2_for_bound(adam_ratio_bound(cfg));
@@ -351,6 +374,34 @@ struct Planner {
       pending.push_back({o, bytes});
       return o;
     };
+    if (nys_mode) {
+      for (MatBufs& mb : mats) {
+        const okls_group_desc& g = groups[mb.group];
+        mb.m = g.m; mb.n = g.n;
+        const size_t mn = static_cast<size_t>(g.m) * g.n * 4;
+        mb.N32 = take(mn);
+        const int ra = nys_r(g.m), rb = nys_r(g.n);
+        mb.X32 = take(static_cast<size_t>(g.m) * rb * 4);
+        mb.Z32 = take(static_cast<size_t>(ra) * g.n * 4);
+        mb.UtA = take(static_cast<size_t>(g.m) * ra * 4);
+        mb.UtB = take(static_cast<size_t>(g.n) * rb * 4);
+        for (int sd = 0; sd < 2; ++sd) {
+          MatBufs::NysSide& S = mb.ns[sd];
+          S.d = sd == 0 ? g.m : g.n;
+          S.k = nys_k(S.d);
+          S.r = nys_r(S.d);
+          const int other = sd == 0 ? g.n : g.m;
+          const size_t dk = static_cast<size_t>(S.d) * S.k * 4, kk = static_cast<size_t>(S.k) * S.k * 4,
+                       kr = static_cast<size_t>(S.k) * S.r * 4;
+          S.Om = take(dk); S.Yb = take(dk); S.Fb = take(dk);
+          S.T1 = take(static_cast<size_t>(S.r) * S.k * 4); S.T2 = take(static_cast<size_t>(other) * S.k * 4);
+          S.gram = take(kk); S.cm = take(kk); S.zp = take(kr); S.kout = take(kr);
+          S.scratch = take(static_cast<size_t>(S.k) * S.k * 8 * 2);
+          S.s_nu = slot++; S.s_nuu = slot++;
+        }
+      }
+      return off;
+    }
     if (soap_mode) {
       int parts = 0, flags = 0;
       auto sfac = [&](FacBufs& f, int d) {
@@ -1271,6 +1322,245 @@ struct Planner {
     add_gemm(L, pq, false, 1, 0);
   }
 
+  // ---- Nystrom mode (the Clean paper's low-rank factors, Algorithm 3, and
+  // the preconditioner of its eq. 9-10), fp32 throughout.
+  Gemm32Prob g32(Ref A, int lda, int ta, Ref B, int ldb, int tb, Ref C, int ldc, int M, int N, int K, float alpha,
+                 float beta) {
+    Gemm32Prob p{};
+    p.A = A; p.B = B; p.C = C; p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ta = ta; p.tb = tb;
+    p.M = M; p.N = N; p.K = K; p.alpha = alpha; p.beta = beta; p.alpha_slot = -1; p.rowscale = no_ref();
+    p.a_fmt = p.b_fmt = GF_F32;
+    return p;
+  }
+  void add_g32(std::vector<LaunchRec>& L, const std::vector<Gemm32Prob>& ps, int cat) {
+    if (ps.empty()) return;
+    LaunchRec r;
+    r.type = L_G32;
+    r.cat = cat;
+    r.first = static_cast<int>(g32_jobs.size());
+    int blk = 0;
+    for (Gemm32Prob p : ps) {
+      const int tm = (p.M + kG32Tile - 1) / kG32Tile, tn = (p.N + kG32Tile - 1) / kG32Tile;
+      p.tiles_n = tn;
+      p.blk_begin = blk;
+      blk += tm * tn;
+      step_flops[cat] += 2.0 * p.M * p.N * p.K;
+      step_bytes[cat] += 4.0 * (static_cast<double>(p.M) * p.K + static_cast<double>(p.K) * p.N +
+                                (p.beta != 0.0f ? 2.0 : 1.0) * p.M * p.N);
+      g32_jobs.push_back(p);
+    }
+    r.count = static_cast<int>(ps.size());
+    r.nblocks = blk;
+    L.push_back(r);
+  }
+  void add_north(std::vector<LaunchRec>& L, const std::vector<NysOrthJob>& js) {
+    LaunchRec r;
+    r.type = L_NORTH;
+    r.cat = CAT_EIG;
+    r.first = static_cast<int>(north_jobs.size());
+    for (const NysOrthJob& j : js) {
+      north_jobs.push_back(j);
+      step_flops[CAT_EIG] += 4.0 * j.d * static_cast<double>(j.k) * j.k;   // two Gram-Schmidt passes
+    }
+    r.count = static_cast<int>(js.size());
+    r.nblocks = r.count;
+    L.push_back(r);
+  }
+  void add_nelem(std::vector<LaunchRec>& L, std::vector<NysElemJob> js) {
+    LaunchRec r;
+    r.type = L_NELEM;
+    r.cat = CAT_CAST;
+    r.first = static_cast<int>(nelem_jobs.size());
+    int blk = 0;
+    for (NysElemJob& j : js) {
+      const size_t total = static_cast<size_t>(j.rows) * j.cols;
+      j.blocks = static_cast<int>(std::max<size_t>(1, std::min<size_t>((total + 255) / 256, 4096)));
+      j.blk_begin = blk;
+      blk += j.blocks;
+      const double per = j.kind == NE_MOMENTUM ? 16.0 : j.kind == NE_UPDATE ? 12.0 : 8.0;
+      step_bytes[CAT_CAST] += per * total;
+      nelem_jobs.push_back(j);
+    }
+    r.count = static_cast<int>(js.size());
+    r.nblocks = blk;
+    L.push_back(r);
+  }
+  NysElemJob nelem(int kind) {
+    NysElemJob j{};
+    j.kind = kind;
+    j.dst = j.src = j.src2 = j.lam = no_ref();
+    return j;
+  }
+
+  void plan_nys(std::vector<LaunchRec>& L, std::vector<MatBufs>& mats, bool refresh) {
+    auto gdt = [&](const MatBufs& mb) { return groups[mb.group].g_dtype; };
+    auto gfmt = [&](const MatBufs& mb) {
+      return gdt(mb) == OKLS_F32 ? GF_F32 : gdt(mb) == OKLS_BF16 ? GF_BF16 : GF_F16;
+    };
+    auto goff = [&](const MatBufs& mb) {
+      return static_cast<size_t>(mb.index) * mb.m * mb.n * (gdt(mb) == OKLS_F32 ? 4 : 2);
+    };
+    auto moff = [&](const MatBufs& mb) { return static_cast<size_t>(mb.index) * mb.m * mb.n * 4; };
+    // the caller's U (N, d, r), Lambda (N, r) and Psi (N, d, k) of a side
+    auto uref = [&](const MatBufs& mb, int sd) {
+      const MatBufs::NysSide& S = mb.ns[sd];
+      return user_ref(sd == 0 ? REF_PA : REF_PB, mb.group, static_cast<size_t>(mb.index) * S.d * S.r * 4);
+    };
+    auto lref = [&](const MatBufs& mb, int sd) {
+      const MatBufs::NysSide& S = mb.ns[sd];
+      return user_ref(sd == 0 ? REF_SA : REF_SB, mb.group, static_cast<size_t>(mb.index) * S.r * 4);
+    };
+    auto pref = [&](const MatBufs& mb, int sd) {
+      const MatBufs::NysSide& S = mb.ns[sd];
+      return user_ref(sd == 0 ? REF_PSA : REF_PSB, mb.group, static_cast<size_t>(mb.index) * S.d * S.k * 4);
+    };
+    const float b2 = cfg.beta2;
+    if (refresh) {
+      // Omega_0 = [U_prev | Psi's first k - r columns] (a first refresh has U = 0:
+      // those columns are dependent and take Psi's remaining columns instead)
+      std::vector<NysElemJob> ge;
+      std::vector<NysOrthJob> go;
+      for (const MatBufs& mb : mats)
+        for (int sd = 0; sd < 2; ++sd) {
+          const MatBufs::NysSide& S = mb.ns[sd];
+          NysElemJob j = nelem(NE_GATHER);
+          j.dst = ws_ref(S.Om); j.src = uref(mb, sd); j.src2 = pref(mb, sd);
+          j.rows = S.d; j.cols = S.k; j.ld_dst = S.k; j.ld_src = S.r; j.ld_src2 = S.k; j.cols1 = S.r;
+          ge.push_back(j);
+          go.push_back(NysOrthJob{ws_ref(S.Om), pref(mb, sd), S.d, S.k, S.k, S.k, S.k - S.r});
+        }
+      add_nelem(L, ge);
+      add_north(L, go);
+      // q passes of Y = A Omega, Omega = Q(Y); then the final sketch Y = A Omega.
+      // A Omega = beta2 U (Lambda U^T Omega) + (1 - beta2) G (G^T Omega) on the
+      // left, with G^T and G exchanged on the right (eq. 8).
+      for (int pass = 0; pass <= cfg.nys_passes; ++pass) {
+        std::vector<Gemm32Prob> p1, p2, p3;
+        std::vector<NysOrthJob> po;
+        for (const MatBufs& mb : mats)
+          for (int sd = 0; sd < 2; ++sd) {
+            const MatBufs::NysSide& S = mb.ns[sd];
+            const int other = sd == 0 ? mb.n : mb.m;
+            Gemm32Prob t1 = g32(uref(mb, sd), S.r, 1, ws_ref(S.Om), S.k, 0, ws_ref(S.T1), S.k, S.r, S.k, S.d, b2, 0.0f);
+            t1.rowscale = lref(mb, sd);
+            p1.push_back(t1);
+            // left: T2 = G^T Omega (n x k); right: T2 = G Omega (m x k)
+            Gemm32Prob t2 = g32(user_ref(REF_G, mb.group, goff(mb)), mb.n, sd == 0 ? 1 : 0, ws_ref(S.Om), S.k, 0,
+                                ws_ref(S.T2), S.k, other, S.k, S.d, 1.0f, 0.0f);
+            t2.a_fmt = gfmt(mb);
+            p1.push_back(t2);
+            // Y = (1 - beta2) G T2 (left) or G^T T2 (right)
+            Gemm32Prob y = g32(user_ref(REF_G, mb.group, goff(mb)), mb.n, sd == 0 ? 0 : 1, ws_ref(S.T2), S.k, 0,
+                               ws_ref(S.Yb), S.k, S.d, S.k, other, 1.0f - b2, 0.0f);
+            y.a_fmt = gfmt(mb);
+            p2.push_back(y);
+            // Y += U T1
+            p3.push_back(g32(uref(mb, sd), S.r, 0, ws_ref(S.T1), S.k, 0, ws_ref(S.Yb), S.k, S.d, S.k, S.r, 1.0f, 1.0f));
+            if (pass < cfg.nys_passes) po.push_back(NysOrthJob{ws_ref(S.Yb), pref(mb, sd), S.d, S.k, S.k, S.k, 0});
+          }
+        add_g32(L, p1, CAT_NS);
+        add_g32(L, p2, CAT_NS);
+        add_g32(L, p3, CAT_NS);
+        if (pass < cfg.nys_passes) {
+          add_north(L, po);
+          // the orthonormalised Y is the next Omega
+          for (MatBufs& mb : mats)
+            for (MatBufs::NysSide& S : mb.ns) std::swap(S.Om, S.Yb);
+        }
+      }
+      // G_Y = Y^T Y and C = Omega^T Y; phase 1 (shift, Cholesky, R^-1 over C);
+      // F = Y R^-1 + nu_u Omega R^-1; F^T F and F^T U_prev; phase 2
+      // (eigenpairs, signs, Lambda); U = F K into the caller's U (read above
+      // for the last time)
+      auto small = [&](int phase) {
+        LaunchRec r;
+        r.type = L_NSMALL;
+        r.cat = CAT_EIG;
+        r.round = phase;
+        r.first = static_cast<int>(nsmall_jobs.size());
+        for (const MatBufs& mb : mats)
+          for (int sd = 0; sd < 2; ++sd) {
+            const MatBufs::NysSide& S = mb.ns[sd];
+            NysSmallJob j{};
+            j.gram = ws_ref(S.gram); j.cmat = ws_ref(S.cm); j.ftu = ws_ref(S.zp); j.kout = ws_ref(S.kout);
+            j.lam = lref(mb, sd); j.scratch = ws_ref(S.scratch);
+            j.k = S.k; j.r = S.r; j.nu_slot = S.s_nu; j.nuu_slot = S.s_nuu;
+            nsmall_jobs.push_back(j);
+            step_flops[CAT_EIG] += 2.0 * std::pow(static_cast<double>(S.k), 3.0);
+            ++r.count;
+          }
+        r.nblocks = r.count;
+        L.push_back(r);
+      };
+      std::vector<Gemm32Prob> pg, pf1, pf2, pt, pu;
+      for (const MatBufs& mb : mats)
+        for (int sd = 0; sd < 2; ++sd) {
+          const MatBufs::NysSide& S = mb.ns[sd];
+          pg.push_back(g32(ws_ref(S.Yb), S.k, 1, ws_ref(S.Yb), S.k, 0, ws_ref(S.gram), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
+          pg.push_back(g32(ws_ref(S.Om), S.k, 1, ws_ref(S.Yb), S.k, 0, ws_ref(S.cm), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
+          pf1.push_back(g32(ws_ref(S.Yb), S.k, 0, ws_ref(S.cm), S.k, 0, ws_ref(S.Fb), S.k, S.d, S.k, S.k, 1.0f, 0.0f));
+          Gemm32Prob f2 = g32(ws_ref(S.Om), S.k, 0, ws_ref(S.cm), S.k, 0, ws_ref(S.Fb), S.k, S.d, S.k, S.k, 1.0f, 1.0f);
+          f2.alpha_slot = S.s_nuu;
+          pf2.push_back(f2);
+          pt.push_back(g32(ws_ref(S.Fb), S.k, 1, ws_ref(S.Fb), S.k, 0, ws_ref(S.gram), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
+          pt.push_back(g32(ws_ref(S.Fb), S.k, 1, uref(mb, sd), S.r, 0, ws_ref(S.zp), S.r, S.k, S.r, S.d, 1.0f, 0.0f));
+          pu.push_back(g32(ws_ref(S.Fb), S.k, 0, ws_ref(S.kout), S.r, 0, uref(mb, sd), S.r, S.d, S.r, S.k, 1.0f, 0.0f));
+        }
+      add_g32(L, pg, CAT_NS);
+      small(1);
+      add_g32(L, pf1, CAT_NS);
+      add_g32(L, pf2, CAT_NS);
+      add_g32(L, pt, CAT_NS);
+      small(2);
+      add_g32(L, pu, CAT_NS);
+      // the buffer roles are back where the layout put them for the next plan
+      if (cfg.nys_passes & 1)
+        for (MatBufs& mb : mats)
+          for (MatBufs::NysSide& S : mb.ns) std::swap(S.Om, S.Yb);
+    }
+    // every step: N, then U = P_a^-1/2 N P_b^-1/2 through thin products
+    // (P^-1/2 = I + U diag(e) U^T, e_j = sqrt((lambda_r + eps) / (lambda_j + eps)) - 1):
+    //   X = N U_b, N' = N + X (U_b E_b)^T, Z = U_a^T N', U = N' + (U_a E_a) Z
+    {
+      std::vector<NysElemJob> e1;
+      for (const MatBufs& mb : mats) {
+        NysElemJob j = nelem(NE_MOMENTUM);
+        j.dst = ws_ref(mb.N32); j.src = user_ref(REF_M, mb.group, moff(mb)); j.src2 = user_ref(REF_G, mb.group, goff(mb));
+        j.rows = mb.m; j.cols = mb.n; j.ld_dst = j.ld_src = j.ld_src2 = mb.n; j.g_fmt = gfmt(mb);
+        e1.push_back(j);
+        for (int sd = 0; sd < 2; ++sd) {
+          const MatBufs::NysSide& S = mb.ns[sd];
+          NysElemJob sc = nelem(NE_SCALE);
+          sc.dst = ws_ref(sd == 0 ? mb.UtA : mb.UtB); sc.src = uref(mb, sd); sc.lam = lref(mb, sd);
+          sc.rows = S.d; sc.cols = S.r; sc.ld_dst = sc.ld_src = S.r;
+          e1.push_back(sc);
+        }
+      }
+      add_nelem(L, e1);
+    }
+    std::vector<Gemm32Prob> q1, q2, q3, q4;
+    for (const MatBufs& mb : mats) {
+      const MatBufs::NysSide& A = mb.ns[0];
+      const MatBufs::NysSide& B = mb.ns[1];
+      q1.push_back(g32(ws_ref(mb.N32), mb.n, 0, uref(mb, 1), B.r, 0, ws_ref(mb.X32), B.r, mb.m, B.r, mb.n, 1.0f, 0.0f));
+      q2.push_back(g32(ws_ref(mb.X32), B.r, 0, ws_ref(mb.UtB), B.r, 1, ws_ref(mb.N32), mb.n, mb.m, mb.n, B.r, 1.0f, 1.0f));
+      q3.push_back(g32(uref(mb, 0), A.r, 1, ws_ref(mb.N32), mb.n, 0, ws_ref(mb.Z32), mb.n, A.r, mb.n, mb.m, 1.0f, 0.0f));
+      q4.push_back(g32(ws_ref(mb.UtA), A.r, 0, ws_ref(mb.Z32), mb.n, 0, ws_ref(mb.N32), mb.n, mb.m, mb.n, A.r, 1.0f, 1.0f));
+    }
+    add_g32(L, q1, CAT_WHITEN);
+    add_g32(L, q2, CAT_WHITEN);
+    add_g32(L, q3, CAT_WHITEN);
+    add_g32(L, q4, CAT_WHITEN);
+    std::vector<NysElemJob> e2;
+    for (const MatBufs& mb : mats) {
+      NysElemJob j = nelem(NE_UPDATE);
+      j.dst = user_ref(REF_W, mb.group, moff(mb)); j.src = ws_ref(mb.N32);
+      j.rows = mb.m; j.cols = mb.n; j.ld_dst = j.ld_src = mb.n; j.c0 = update_scale(mb);
+      e2.push_back(j);
+    }
+    add_nelem(L, e2);
+  }
+
   // Whether a second concurrent Newton-Schulz chain pays for this chunk.
   // It fills the CUs that the last, partly filled round of a launch leaves
   // idle; with a full last round, or many rounds, it only adds launches and
@@ -1310,8 +1600,13 @@ struct Planner {
       for (MatBufs& mb : mats) {
         size_t* offs[] = {&mb.G16, &mb.G16T, &mb.N16, &mb.Xa32, &mb.XbT32, &mb.Xa16, &mb.XbT16, &mb.VT32, &mb.VT16,
                           &mb.NT16, &mb.X[0], &mb.X[1], &mb.XT[0], &mb.XT[1], &mb.A32, &mb.A16,
-                          &mb.M16, &mb.XGT16, &mb.XMT16, &mb.Gr32, &mb.Mr32, &mb.NP16, &mb.ZT16};
+                          &mb.M16, &mb.XGT16, &mb.XMT16, &mb.Gr32, &mb.Mr32, &mb.NP16, &mb.ZT16,
+                          &mb.N32, &mb.X32, &mb.Z32, &mb.UtA, &mb.UtB};
         for (size_t* o : offs) *o += base;
+        for (MatBufs::NysSide& S : mb.ns) {
+          size_t* so[] = {&S.Om, &S.Yb, &S.Fb, &S.T1, &S.T2, &S.gram, &S.cm, &S.zp, &S.kout, &S.scratch};
+          for (size_t* o : so) *o += base;
+        }
         for (FacBufs* f : {&mb.fa, &mb.fb}) {
           f->Y[0] += base; f->Y[1] += base; f->Z[0] += base; f->Z[1] += base; f->T += base; f->R32 += base;
           f->YT[0] += base; f->YT[1] += base; f->ZT[0] += base; f->ZT[1] += base; f->TT += base;
@@ -1334,6 +1629,11 @@ struct Planner {
     }
     if (soap_mode) {
       plan_soap(L, mats, refresh);
+      (refresh ? chunks : chunks_stale).push_back(std::move(L));
+      return;
+    }
+    if (nys_mode) {
+      plan_nys(L, mats, refresh);
       (refresh ? chunks : chunks_stale).push_back(std::move(L));
       return;
     }
@@ -1594,6 +1894,17 @@ struct Planner {
   size_t user_bytes(int kind, int group) const {
     const okls_group_desc& g = groups[group];
     const size_t b = static_cast<size_t>(g.batch);
+    if (nys_mode) {   // U (N, d, r'), Lambda (N, r'), Psi (N, d, k) per side
+      switch (kind) {
+        case REF_SA: return b * nys_r(g.m) * 4;
+        case REF_SB: return b * nys_r(g.n) * 4;
+        case REF_PA: return b * g.m * nys_r(g.m) * 4;
+        case REF_PB: return b * g.n * nys_r(g.n) * 4;
+        case REF_PSA: return b * g.m * nys_k(g.m) * 4;
+        case REF_PSB: return b * g.n * nys_k(g.n) * 4;
+        default: break;
+      }
+    }
     switch (kind) {
       case REF_W: case REF_M: case REF_V: return b * g.m * g.n * 4;
       case REF_G: return b * g.m * g.n * (g.g_dtype == OKLS_F32 ? 4 : 2);
@@ -1604,14 +1915,18 @@ struct Planner {
   }
   bool fits(const Ref& r, size_t bytes) const {
     if (r.kind == REF_WS) return fits_ws(r, bytes);
-    if (r.kind < REF_W || r.kind > REF_V || r.group < 0 || r.group >= static_cast<int>(groups.size())) return false;
+    if (r.kind < REF_W || r.kind > REF_PSB || r.group < 0 || r.group >= static_cast<int>(groups.size())) return false;
     if (r.kind == REF_V && !soap_mode) return false;
+    if ((r.kind == REF_PSA || r.kind == REF_PSB) && !nys_mode) return false;
     return r.off >= 0 && static_cast<size_t>(r.off) + bytes <= user_bytes(r.kind, r.group);
   }
   bool slot_ok(int s) const { return s >= 0 && s < n_slots; }
 
   // whether some steps keep the roots (SOAP: the bases) and run their own plan
   bool has_stale() const { return soap_mode ? cfg.precond_freq > 1 : (cfg.root_period > 1 && !muon_mode); }
+  // Nystrom: (sketch columns, kept eigenpairs) of a side d
+  int nys_k(int d) const { return std::min(cfg.nys_rank + cfg.nys_oversample, d); }
+  int nys_r(int d) const { return std::min(cfg.nys_rank, nys_k(d)); }
   bool validate() {
     if (!validate_plan(chunks)) return false;
     return has_stale() ? validate_plan(chunks_stale) : chunks_stale.empty();
@@ -1681,6 +1996,64 @@ struct Planner {
               if (!fits(p.aux, (static_cast<size_t>(p.M - 1) * p.ldaux + p.N) * 4)) return false;
             }
           }
+        } else if (r.type == L_G32) {
+          if (r.first < 0 || r.first + r.count > static_cast<int>(g32_jobs.size())) return false;
+          int blk = 0;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const Gemm32Prob& q = g32_jobs[j];
+            if (q.M < 1 || q.N < 1 || q.K < 1 || q.blk_begin != blk || q.tiles_n != (q.N + kG32Tile - 1) / kG32Tile) return false;
+            blk += ((q.M + kG32Tile - 1) / kG32Tile) * q.tiles_n;
+            const int ar = q.ta ? q.K : q.M, ac = q.ta ? q.M : q.K, br = q.tb ? q.N : q.K, bc = q.tb ? q.K : q.N;
+            if (q.lda < ac || q.ldb < bc || q.ldc < q.N) return false;
+            const size_t ae = q.a_fmt == GF_F32 ? 4 : 2, be = q.b_fmt == GF_F32 ? 4 : 2;
+            if (!fits(q.A, (static_cast<size_t>(ar - 1) * q.lda + ac) * ae)) return false;
+            if (!fits(q.B, (static_cast<size_t>(br - 1) * q.ldb + bc) * be)) return false;
+            if (!fits(q.C, (static_cast<size_t>(q.M - 1) * q.ldc + q.N) * 4)) return false;
+            if (q.rowscale.kind != REF_NONE && !fits(q.rowscale, static_cast<size_t>(q.M) * 4)) return false;
+            if (q.alpha_slot >= 0 && !slot_ok(q.alpha_slot)) return false;
+          }
+          if (blk != r.nblocks) return false;
+        } else if (r.type == L_NORTH) {
+          if (r.first < 0 || r.first + r.count > static_cast<int>(north_jobs.size()) || r.nblocks != r.count) return false;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const NysOrthJob& q = north_jobs[j];
+            if (q.d < 1 || q.k < 1 || q.k > q.d || q.k > kNysMaxK || q.ld < q.k || q.ldf < q.k || q.fb_shift < 0) return false;
+            if (!fits(q.Y, (static_cast<size_t>(q.d - 1) * q.ld + q.k) * 4)) return false;
+            if (!fits(q.fb, (static_cast<size_t>(q.d - 1) * q.ldf + q.k) * 4)) return false;
+          }
+        } else if (r.type == L_NSMALL) {
+          if (r.first < 0 || r.first + r.count > static_cast<int>(nsmall_jobs.size()) || r.nblocks != r.count) return false;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const NysSmallJob& q = nsmall_jobs[j];
+            if (q.k < 1 || q.k > kNysMaxK || q.r < 1 || q.r > q.k || (r.round != 1 && r.round != 2)) return false;
+            const size_t kk = static_cast<size_t>(q.k) * q.k * 4, kr = static_cast<size_t>(q.k) * q.r * 4;
+            if (!fits(q.gram, kk) || !fits(q.cmat, kk) || !fits(q.ftu, kr) || !fits(q.kout, kr)) return false;
+            if (!fits(q.lam, static_cast<size_t>(q.r) * 4) || !fits(q.scratch, 2 * static_cast<size_t>(q.k) * q.k * 8)) return false;
+            if (!slot_ok(q.nu_slot) || !slot_ok(q.nuu_slot)) return false;
+          }
+        } else if (r.type == L_NELEM) {
+          if (r.first < 0 || r.first + r.count > static_cast<int>(nelem_jobs.size())) return false;
+          int blk = 0;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const NysElemJob& q = nelem_jobs[j];
+            if (q.kind < NE_GATHER || q.kind > NE_UPDATE || q.rows < 1 || q.cols < 1 || q.blk_begin != blk || q.blocks < 1) return false;
+            blk += q.blocks;
+            if (q.ld_dst < q.cols || !fits(q.dst, (static_cast<size_t>(q.rows - 1) * q.ld_dst + q.cols) * 4)) return false;
+            const int scols = q.kind == NE_GATHER ? q.cols1 : q.cols;
+            if (scols > 0 && (q.ld_src < scols || !fits(q.src, (static_cast<size_t>(q.rows - 1) * q.ld_src + scols) * 4)))
+              return false;
+            if (q.kind == NE_GATHER) {
+              const int c2 = q.cols - q.cols1;
+              if (q.cols1 < 0 || q.cols1 > q.cols) return false;
+              if (c2 > 0 && (q.ld_src2 < c2 || !fits(q.src2, (static_cast<size_t>(q.rows - 1) * q.ld_src2 + c2) * 4))) return false;
+            }
+            if (q.kind == NE_MOMENTUM &&
+                (q.ld_src2 < q.cols ||
+                 !fits(q.src2, (static_cast<size_t>(q.rows - 1) * q.ld_src2 + q.cols) * (q.g_fmt == GF_F32 ? 4 : 2))))
+              return false;
+            if (q.kind == NE_SCALE && !fits(q.lam, static_cast<size_t>(q.cols) * 4)) return false;
+          }
+          if (blk != r.nblocks) return false;
         } else if (r.type == L_ADAM) {
           int blk = 0;
           if (r.first < 0 || r.first + r.count > static_cast<int>(adam_jobs.size())) return false;
@@ -1836,8 +2209,8 @@ struct Planner {
 };
 
 struct WsLayout {
-  size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, adam = 0, jac = 0, scal = 0, part = 0, flag = 0, chunk = 0,
-         total = 0;
+  size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, adam = 0, jac = 0, g32 = 0, north = 0, nsmall = 0,
+         nelem = 0, scal = 0, part = 0, flag = 0, chunk = 0, total = 0;
 };
 
 WsLayout ws_layout(Planner& P) {
@@ -1853,6 +2226,10 @@ WsLayout ws_layout(Planner& P) {
   w.sym = take(P.sym_jobs.size() * sizeof(SymJob));
   w.adam = take(P.adam_jobs.size() * sizeof(AdamJob));
   w.jac = take(P.jac_jobs.size() * sizeof(JacJob));
+  w.g32 = take(P.g32_jobs.size() * sizeof(Gemm32Prob));
+  w.north = take(P.north_jobs.size() * sizeof(NysOrthJob));
+  w.nsmall = take(P.nsmall_jobs.size() * sizeof(NysSmallJob));
+  w.nelem = take(P.nelem_jobs.size() * sizeof(NysElemJob));
   w.scal = take(static_cast<size_t>(P.n_slots) * sizeof(float));
   w.part = take(static_cast<size_t>(P.max_partials) * 2 * sizeof(float) * kNsStreams);   // one region per stream
   w.flag = take(sizeof(int));
@@ -1875,6 +2252,8 @@ UserPtrs user_ptrs(const okls_handle* h, const okls_group_tensors* t) {
     u.p[g][REF_PA] = t[g].Pa;
     u.p[g][REF_PB] = t[g].Pb;
     u.p[g][REF_V] = t[g].V;
+    u.p[g][REF_PSA] = const_cast<float*>(t[g].PsiA);
+    u.p[g][REF_PSB] = const_cast<float*>(t[g].PsiB);
   }
   return u;
 }
@@ -1916,6 +2295,9 @@ void okls_default_config(okls_config* c) {
   c->bias_correction = 1;
   c->jacobi_sweeps = 20;
   c->jacobi_tol = 2e-6f;
+  c->nys_rank = 32;
+  c->nys_oversample = 8;
+  c->nys_passes = 1;
 }
 
 size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups) {
@@ -1945,14 +2327,14 @@ okls_status okls_plan_query(const okls_config* cfg, int n_groups, const okls_gro
     for (const std::vector<LaunchRec>& L : cs)
       for (const LaunchRec& r : L)
         n += (r.type == L_STAT || r.type == L_CAST || r.type == L_GEMM || r.type == L_SYM || r.type == L_ADAM ||
-              r.type == L_JAC);
+              r.type == L_JAC || r.type == L_G32 || r.type == L_NORTH || r.type == L_NSMALL || r.type == L_NELEM);
     return n;
   };
   info.chunks = static_cast<int>(P.chunks.size());
   info.launches = kernels(P.chunks);
   info.launches_stale = P.chunks_stale.empty() ? info.launches : kernels(P.chunks_stale);
   info.ns_chains = 0;
-  if (!P.muon_mode && !P.soap_mode) {
+  if (!P.muon_mode && !P.soap_mode && !P.nys_mode) {
     for (const std::vector<LaunchRec>& L : P.chunks) {
       int streams = 1;
       for (const LaunchRec& r : L) streams = std::max(streams, r.stream + 1);
@@ -2001,7 +2383,8 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   P.single_chain = single_chain;
   P.plan(w.chunk);
   if (!P.validate() || P.probs.size() != sizing.probs.size() || P.chunk_bytes != sizing.chunk_bytes ||
-      P.adam_jobs.size() != sizing.adam_jobs.size() || P.jac_jobs.size() != sizing.jac_jobs.size())
+      P.adam_jobs.size() != sizing.adam_jobs.size() || P.jac_jobs.size() != sizing.jac_jobs.size() ||
+      P.g32_jobs.size() != sizing.g32_jobs.size() || P.nelem_jobs.size() != sizing.nelem_jobs.size())
     return OKLS_ERR_UNSUPPORTED;
   // the regions the tables and slots occupy must end before the chunk buffers
   if (w.flag + sizeof(int) > w.chunk) return OKLS_ERR_UNSUPPORTED;
@@ -2019,6 +2402,10 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_sym = w.sym;
   h->off_adam = w.adam;
   h->off_jac = w.jac;
+  h->off_g32 = w.g32;
+  h->off_north = w.north;
+  h->off_nsmall = w.nsmall;
+  h->off_nelem = w.nelem;
   h->s_np = P.s_np;
   h->off_scal = w.scal;
   h->off_part = w.part;
@@ -2076,6 +2463,10 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   up(w.sym, P.sym_jobs.data(), P.sym_jobs.size() * sizeof(SymJob));
   up(w.adam, P.adam_jobs.data(), P.adam_jobs.size() * sizeof(AdamJob));
   up(w.jac, P.jac_jobs.data(), P.jac_jobs.size() * sizeof(JacJob));
+  up(w.g32, P.g32_jobs.data(), P.g32_jobs.size() * sizeof(Gemm32Prob));
+  up(w.north, P.north_jobs.data(), P.north_jobs.size() * sizeof(NysOrthJob));
+  up(w.nsmall, P.nsmall_jobs.data(), P.nsmall_jobs.size() * sizeof(NysSmallJob));
+  up(w.nelem, P.nelem_jobs.data(), P.nelem_jobs.size() * sizeof(NysElemJob));
   up(w.scal, scal.data(), scal.size() * sizeof(float));
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
@@ -2120,6 +2511,9 @@ static okls_status check_tensors(const okls_handle* h, const okls_group_tensors*
       if (!aligned(x.Sa, 4) || !aligned(x.Sb, 4) || !aligned(x.Pa, 4) || !aligned(x.Pb, 4)) return OKLS_ERR_INVALID_ARG;
     }
     if (h->cfg.mode == OKLS_MODE_SOAP && (x.V == nullptr || !aligned(x.V, 4))) return OKLS_ERR_INVALID_ARG;
+    if (h->cfg.mode == OKLS_MODE_NYSTROM && need_wg &&
+        (x.PsiA == nullptr || x.PsiB == nullptr || !aligned(x.PsiA, 4) || !aligned(x.PsiB, 4)))
+      return OKLS_ERR_INVALID_ARG;
     if (need_wg) {
       if (x.W == nullptr || x.G == nullptr) return OKLS_ERR_INVALID_ARG;
       if (!aligned(x.W, 4) || !aligned(x.G, h->groups[g].g_dtype == OKLS_F32 ? 4 : 2)) return OKLS_ERR_INVALID_ARG;
@@ -2139,7 +2533,14 @@ okls_status okls_init_state(okls_handle* h, const okls_group_tensors* t, void* s
   int n = 0;
   for (size_t g = 0; g < h->groups.size(); ++g) {
     const okls_group_desc& d = h->groups[g];
-    if (h->cfg.mode != OKLS_MODE_MUON) {
+    if (h->cfg.mode == OKLS_MODE_NYSTROM) {   // no factors yet: U = 0, Lambda = 0 (a first refresh is a cold start)
+      const int ra = std::min(h->cfg.nys_rank, std::min(h->cfg.nys_rank + h->cfg.nys_oversample, d.m));
+      const int rb = std::min(h->cfg.nys_rank, std::min(h->cfg.nys_rank + h->cfg.nys_oversample, d.n));
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, 1, ra, 0.0f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, 1, rb, 0.0f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, ra, 0.0f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, rb, 0.0f};
+    } else if (h->cfg.mode != OKLS_MODE_MUON) {
       // SOAP: zero factors (the Clean paper's Algorithm 4 starts from none), identity bases
       const float s0 = h->cfg.mode == OKLS_MODE_SOAP ? 0.0f : h->cfg.eps;
       a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, s0};
@@ -2200,6 +2601,8 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
   float* part = reinterpret_cast<float*>(ws + h->off_part);
 
   // the roots are recomputed on steps 1, 1 + p, 1 + 2p, ... (p = root_period)
+  const bool nys = h->cfg.mode == OKLS_MODE_NYSTROM;
+  (void)nys;
   // SOAP: the bases are recomputed after steps t with t % precond_freq == 0
   const bool refresh = soap ? (h->cfg.precond_freq <= 1 || step % h->cfg.precond_freq == 0)
                             : (h->cfg.mode == OKLS_MODE_MUON || h->cfg.root_period <= 1 || (step - 1) % h->cfg.root_period == 0);
@@ -2300,6 +2703,42 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.ws = ws;
         a.user = user;
         e = launch_jacobi(a, r.jac_kind, r.nblocks, rs);
+      } else if (r.type == L_G32) {
+        Gemm32Args a;
+        a.jobs = reinterpret_cast<const Gemm32Prob*>(ws + h->off_g32) + r.first;
+        a.n_jobs = r.count;
+        a.scal = scal;
+        a.ws = ws;
+        a.user = user;
+        e = launch_gemm32(a, r.nblocks, rs);
+      } else if (r.type == L_NORTH) {
+        NysOrthArgs a;
+        a.jobs = reinterpret_cast<const NysOrthJob*>(ws + h->off_north) + r.first;
+        a.n_jobs = r.count;
+        a.ws = ws;
+        a.user = user;
+        e = launch_nys_orth(a, rs);
+      } else if (r.type == L_NSMALL) {
+        NysSmallArgs a;
+        a.jobs = reinterpret_cast<const NysSmallJob*>(ws + h->off_nsmall) + r.first;
+        a.n_jobs = r.count;
+        a.phase = r.round;
+        a.scal = scal;
+        a.ws = ws;
+        a.user = user;
+        e = launch_nys_small(a, rs);
+      } else if (r.type == L_NELEM) {
+        NysElemArgs a;
+        a.jobs = reinterpret_cast<const NysElemJob*>(ws + h->off_nelem) + r.first;
+        a.n_jobs = r.count;
+        a.beta1 = static_cast<float>(b1);
+        a.s_t = static_cast<float>(s_t);
+        a.mu = h->cfg.eps;
+        a.lr = lr_update;
+        a.decay = static_cast<float>(decay);
+        a.ws = ws;
+        a.user = user;
+        e = launch_nys_elem(a, r.nblocks, rs);
       } else {
         GemmArgs a;
         a.probs = reinterpret_cast<const GemmProb*>(ws + h->off_probs);
@@ -2337,7 +2776,14 @@ okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* t, void*
   int n = 0;
   for (size_t g = 0; g < h->groups.size(); ++g) {
     const okls_group_desc& d = h->groups[g];
-    if (h->cfg.mode != OKLS_MODE_MUON) {
+    if (h->cfg.mode == OKLS_MODE_NYSTROM) {
+      const int ra = std::min(h->cfg.nys_rank, std::min(h->cfg.nys_rank + h->cfg.nys_oversample, d.m));
+      const int rb = std::min(h->cfg.nys_rank, std::min(h->cfg.nys_rank + h->cfg.nys_oversample, d.n));
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, 1, ra, 0.f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, 1, rb, 0.f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, ra, 0.f};
+      a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PB, d.batch, d.n, rb, 0.f};
+    } else if (h->cfg.mode != OKLS_MODE_MUON) {
       a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SA, d.batch, d.m, d.m, 0.f};
       a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_SB, d.batch, d.n, d.n, 0.f};
       a.jobs[n++] = InitJob{static_cast<int32_t>(g), REF_PA, d.batch, d.m, d.m, 0.f};

@@ -6,7 +6,7 @@
 
 namespace okls {
 
-constexpr int kMaxInitJobs = 5 * kMaxGroups;
+constexpr int kMaxInitJobs = 6 * kMaxGroups;   // SOAP: S_a, S_b, P_a, P_b, M and V per group
 
 // One caller tensor of one group: batch x rows x cols fp32, filled with
 // `diag` on each matrix's diagonal and zero elsewhere (init), or scanned
@@ -32,6 +32,10 @@ enum JacKind { JAC_RESET = 0, JAC_SOLVE = 1, JAC_APPLY = 2, JAC_CHECK = 3 };
 // JAC_RESET ignores n_blocks (one block clears every job's flag); JAC_CHECK
 // takes one block per job
 hipError_t launch_jacobi(const JacArgs& a, int kind, int n_blocks, hipStream_t s);
+hipError_t launch_gemm32(const Gemm32Args& a, int n_blocks, hipStream_t s);
+hipError_t launch_nys_orth(const NysOrthArgs& a, hipStream_t s);     // one block per job
+hipError_t launch_nys_small(const NysSmallArgs& a, hipStream_t s);   // one block per job
+hipError_t launch_nys_elem(const NysElemArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_init_state(const InitArgs& a, int n_jobs, hipStream_t s);
 hipError_t launch_check_finite(const InitArgs& a, int n_jobs, int* flag_dev, hipStream_t s);
 // device address of the static scratch (kStaticScratchBytes) on the current

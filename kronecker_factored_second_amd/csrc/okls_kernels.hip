@@ -1566,6 +1566,397 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_check_kernel(JacArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Nystrom low-rank factors (Gemm32Prob, NysOrthJob, NysSmallJob, NysElemJob)
+// ---------------------------------------------------------------------------
+// C = alpha op(A) op(B) (row i times rowscale[i]) + beta C in fp32: 64 x 64
+// output tiles, K in steps of 16 through LDS, a 4 x 4 block per thread.
+__global__ __launch_bounds__(256) void gemm32_kernel(Gemm32Args a) {
+  __shared__ __attribute__((aligned(16))) float As[kG32K][kG32Tile + 4];   // As[kk][i] = op(A)[i0 + i][k0 + kk]
+  __shared__ __attribute__((aligned(16))) float Bs[kG32K][kG32Tile + 4];   // Bs[kk][j] = op(B)[k0 + kk][j0 + j]
+  const int gb = blockIdx.x;
+  const Gemm32Prob P = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
+  const int lb = gb - P.blk_begin;
+  const int ti = lb / P.tiles_n, tj = lb - ti * P.tiles_n;
+  const int i0 = ti * kG32Tile, j0 = tj * kG32Tile;
+  const char* A = resolve(P.A, a.ws, a.user);
+  const char* B = resolve(P.B, a.ws, a.user);
+  float* C = reinterpret_cast<float*>(resolve(P.C, a.ws, a.user));
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < P.K; k0 += kG32K) {
+    for (int e = threadIdx.x; e < kG32Tile * kG32K; e += 256) {
+      // the fastest-varying index walks the operand's contiguous dimension
+      const int i = P.ta ? e % kG32Tile : e / kG32K, kk = P.ta ? e / kG32Tile : e % kG32K;
+      const int gi = i0 + i, gk = k0 + kk;
+      float v = 0.0f;
+      if (gi < P.M && gk < P.K)
+        v = grad_elem(A, P.ta ? static_cast<size_t>(gk) * P.lda + gi : static_cast<size_t>(gi) * P.lda + gk, P.a_fmt);
+      As[kk][i] = v;
+      const int j = P.tb ? e / kG32K : e % kG32Tile, kb = P.tb ? e % kG32K : e / kG32Tile;
+      const int gj = j0 + j, gkb = k0 + kb;
+      float w = 0.0f;
+      if (gj < P.N && gkb < P.K)
+        w = grad_elem(B, P.tb ? static_cast<size_t>(gj) * P.ldb + gkb : static_cast<size_t>(gkb) * P.ldb + gj, P.b_fmt);
+      Bs[kb][j] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kG32K; ++kk) {
+      const float4 av = *reinterpret_cast<const float4*>(&As[kk][4 * ty]);
+      const float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][4 * tx]);
+      const float x[4] = {av.x, av.y, av.z, av.w}, y[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(x[i], y[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const float alpha = P.alpha * (P.alpha_slot >= 0 ? a.scal[P.alpha_slot] : 1.0f);
+  const float* rs = P.rowscale.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(P.rowscale, a.ws, a.user)) : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gi = i0 + 4 * ty + i;
+    if (gi >= P.M) continue;
+    const float ri = rs != nullptr ? alpha * rs[gi] : alpha;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gj = j0 + 4 * tx + j;
+      if (gj >= P.N) continue;
+      float* c = C + static_cast<size_t>(gi) * P.ldc + gj;
+      *c = P.beta != 0.0f ? __builtin_fmaf(P.beta, *c, ri * acc[i][j]) : ri * acc[i][j];
+    }
+  }
+}
+
+// Block sum of one float (all threads get the result).
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Thin QR's Q of Y (d x k) in place: column by column, classical
+// Gram-Schmidt against the finished columns, repeated while a pass removes
+// more than half the remaining norm (at most three passes), then
+// normalised.  A column that keeps less than 1e-6 of its norm (dependent,
+// or zero) is replaced by a column of the Gaussian fallback and
+// orthogonalised again.  One workgroup per job; the projections of a pass
+// are one wave per finished column, lanes over the rows.
+__global__ __launch_bounds__(256) void nys_orth_kernel(NysOrthArgs a) {
+  __shared__ float coef[kNysMaxK];
+  __shared__ float red[4];
+  const NysOrthJob J = a.jobs[blockIdx.x];
+  float* Y = reinterpret_cast<float*>(resolve(J.Y, a.ws, a.user));
+  const float* F = reinterpret_cast<const float*>(resolve(J.fb, a.ws, a.user));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto col_norm2 = [&](int j) {
+    float s = 0.0f;
+    for (int r = threadIdx.x; r < J.d; r += 256) {
+      const float v = Y[static_cast<size_t>(r) * J.ld + j];
+      s += v * v;
+    }
+    return block_sum256(s, red);
+  };
+  auto project_out = [&](int j) {       // y_j <- y_j - Q_{<j} (Q_{<j}^T y_j)
+    for (int c = wave; c < j; c += 4) {
+      float s = 0.0f;
+      for (int r = lane; r < J.d; r += 64)
+        s += Y[static_cast<size_t>(r) * J.ld + c] * Y[static_cast<size_t>(r) * J.ld + j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+      if (lane == 0) coef[c] = s;
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < J.d; r += 256) {
+      float* row = Y + static_cast<size_t>(r) * J.ld;
+      float v = row[j];
+      for (int c = 0; c < j; ++c) v -= row[c] * coef[c];
+      row[j] = v;
+    }
+    __syncthreads();
+  };
+  for (int j = 0; j < J.k; ++j) {
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      const float n0 = col_norm2(j);
+      float prev = n0, now = n0;
+      for (int pass = 0; pass < 3 && j > 0; ++pass) {
+        project_out(j);
+        now = col_norm2(j);
+        if (!(now < 0.25f * prev)) break;
+        prev = now;
+      }
+      if (now > 1e-12f * n0 && now > 0.0f) {
+        const float inv = 1.0f / sqrtf(now);
+        for (int r = threadIdx.x; r < J.d; r += 256) Y[static_cast<size_t>(r) * J.ld + j] *= inv;
+        __syncthreads();
+        break;
+      }
+      // dependent: take the fallback column and try once more
+      const int fc = (j + J.fb_shift) % J.k;
+      for (int r = threadIdx.x; r < J.d; r += 256)
+        Y[static_cast<size_t>(r) * J.ld + j] = attempt == 0 ? F[static_cast<size_t>(r) * J.ldf + fc] : (r == j ? 1.0f : 0.0f);
+      __syncthreads();
+    }
+  }
+}
+
+// Cyclic Jacobi eigendecomposition of the symmetric n x n matrix A (LDS,
+// row stride n + 1) accumulating V; round-robin order, rotations in fp64.
+__device__ void nys_jacobi(float* A, float* V, int n, int ld) {
+  __shared__ float rc[kNysMaxK / 2], rs[kNysMaxK / 2];
+  __shared__ int ru[kNysMaxK / 2], rw[kNysMaxK / 2], rot_any;
+  __shared__ float fro_sh;
+  const int np = n + (n & 1);                    // an odd size pairs one index with a dummy
+  float s2 = 0.0f;
+  for (int e = threadIdx.x; e < n * n; e += 256) {
+    const float x = A[(e / n) * ld + e % n];
+    s2 += x * x;
+  }
+  __shared__ float red[4];
+  s2 = block_sum256(s2, red);
+  const float floor_abs = 1e-9f * sqrtf(s2);
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    if (threadIdx.x == 0) rot_any = 0;
+    __syncthreads();
+    for (int rd = 0; rd < np - 1; ++rd) {
+      if (threadIdx.x < np / 2) {
+        const int t = threadIdx.x;
+        const int pa = t == 0 ? 0 : ((t - 1 + rd) % (np - 1)) + 1;
+        const int tb = np - 1 - t;
+        const int pb = tb == 0 ? 0 : ((tb - 1 + rd) % (np - 1)) + 1;
+        const int u = min(pa, pb), w = max(pa, pb);
+        float c = 1.0f, sn = 0.0f;
+        if (w < n) {
+          const float auu = A[u * ld + u], aww = A[w * ld + w], auw = A[u * ld + w];
+          if (fabsf(auw) > floor_abs && fabsf(auw) > 1e-7f * sqrtf(fabsf(auu * aww))) {
+            const double tau = (static_cast<double>(aww) - auu) / (2.0 * auw);
+            const double tt = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+            const double cd = 1.0 / sqrt(1.0 + tt * tt);
+            c = static_cast<float>(cd);
+            sn = static_cast<float>(tt * cd);
+            rot_any = 1;
+          }
+        }
+        ru[t] = u; rw[t] = w; rc[t] = c; rs[t] = sn;
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < (np / 2) * n; e += 256) {   // rows
+        const int t = e / n, col = e % n;
+        if (rs[t] != 0.0f) {
+          const int u = ru[t], w = rw[t];
+          const float xu = A[u * ld + col], xw = A[w * ld + col];
+          A[u * ld + col] = rc[t] * xu - rs[t] * xw;
+          A[w * ld + col] = rs[t] * xu + rc[t] * xw;
+        }
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < (np / 2) * n; e += 256) {   // columns of A and V
+        const int t = e / n, row = e % n;
+        if (rs[t] != 0.0f) {
+          const int u = ru[t], w = rw[t];
+          const float xu = A[row * ld + u], xw = A[row * ld + w];
+          A[row * ld + u] = rc[t] * xu - rs[t] * xw;
+          A[row * ld + w] = rs[t] * xu + rc[t] * xw;
+          const float vu = V[row * ld + u], vw = V[row * ld + w];
+          V[row * ld + u] = rc[t] * vu - rs[t] * vw;
+          V[row * ld + w] = rs[t] * vu + rc[t] * vw;
+        }
+      }
+      __syncthreads();
+    }
+    const bool more = rot_any != 0;
+    __syncthreads();
+    if (!more) break;
+  }
+  (void)fro_sh;
+}
+
+// The k x k ends of a refresh, in two phases around the products that form
+// F = Y_nu R^-1 and its Gram:
+//   phase 1, from G_Y = Y^T Y and C = Omega^T Y (Omega orthonormal, so
+//   B = Omega^T Y_nu = C + nu I for Y_nu = Y + nu Omega): nu = the fp32
+//   spacing at ||Y||_2 (power iteration on G_Y); B = sym(C) + nu I = R^T R
+//   (Cholesky, fp64, a pivot that rounding took below nu held at nu); R^-1
+//   (fp64), written over C as fp32.  The products then form F = Y R^-1 +
+//   nu Omega R^-1 and F^T F, F^T U_prev.
+//   phase 2: the eigenpairs (S, V) of F^T F by Jacobi (fp32), in decreasing
+//   order; U = F V_r S_r^-1/2 = F K, each column's sign set so that
+//   u_i^T u_prev,i >= 0 (= K_i^T (F^T u_prev,i)); Lambda = max(0, S_r - nu).
+// A zero sketch (phase 1 finds G_Y = 0) records nu = 0, nu_u = 1 and R^-1 = I,
+// so that F = Omega; phase 2 then keeps K = the first r columns of I and
+// Lambda = 0 (U = Omega's first columns).
+__global__ __launch_bounds__(256) void nys_small_kernel(NysSmallArgs a) {
+  constexpr int LD = kNysMaxK + 1;
+  __shared__ float A[kNysMaxK * LD];
+  __shared__ float V[kNysMaxK * LD];
+  __shared__ float S[kNysMaxK];
+  __shared__ int order[kNysMaxK];
+  __shared__ float red[4];
+  __shared__ float vec[kNysMaxK], vec2[kNysMaxK];
+  const NysSmallJob J = a.jobs[blockIdx.x];
+  const int k = J.k, r = J.r;
+  float* Gy = reinterpret_cast<float*>(resolve(J.gram, a.ws, a.user));
+  float* Cm = reinterpret_cast<float*>(resolve(J.cmat, a.ws, a.user));
+  if (a.phase == 1) {
+    double* R = reinterpret_cast<double*>(resolve(J.scratch, a.ws, a.user));   // R (k x k)
+    double* X = R + static_cast<size_t>(k) * k;                               // R^-1
+    float tr = 0.0f;
+    for (int i = threadIdx.x; i < k; i += 256) tr += Gy[i * k + i];
+    tr = block_sum256(tr, red);
+    if (!(tr > 0.0f)) {                            // a zero sketch: nothing to factor
+      for (int e = threadIdx.x; e < k * k; e += 256) Cm[e] = (e / k == e % k) ? 1.0f : 0.0f;
+      if (threadIdx.x == 0) {
+        a.scal[J.nu_slot] = 0.0f;
+        a.scal[J.nuu_slot] = 1.0f;
+      }
+      return;
+    }
+    for (int i = threadIdx.x; i < k; i += 256) vec[i] = 1.0f;
+    __syncthreads();
+    float lmax = 0.0f;
+    for (int it = 0; it < 60; ++it) {
+      for (int i = threadIdx.x; i < k; i += 256) {
+        float s = 0.0f;
+        for (int j = 0; j < k; ++j) s += Gy[i * k + j] * vec[j];
+        vec2[i] = s;
+      }
+      __syncthreads();
+      float n2 = 0.0f, dotv = 0.0f, vn = 0.0f;
+      for (int i = threadIdx.x; i < k; i += 256) {
+        n2 += vec2[i] * vec2[i];
+        dotv += vec2[i] * vec[i];
+        vn += vec[i] * vec[i];
+      }
+      n2 = block_sum256(n2, red);
+      dotv = block_sum256(dotv, red);
+      vn = block_sum256(vn, red);
+      lmax = dotv / vn;                            // Rayleigh quotient
+      const float inv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+      for (int i = threadIdx.x; i < k; i += 256) vec[i] = vec2[i] * inv;
+      __syncthreads();
+    }
+    int e2;
+    (void)frexpf(sqrtf(fmaxf(lmax, 0.0f)), &e2);   // ||Y||_2 = f 2^e2, f in [0.5, 1)
+    const float nu = ldexpf(1.0f, e2 - 1 - 23);
+    for (int e = threadIdx.x; e < k * k; e += 256) {
+      const int i = e / k, j = e % k;
+      R[e] = 0.5 * (static_cast<double>(Cm[i * k + j]) + Cm[j * k + i]) + (i == j ? static_cast<double>(nu) : 0.0);
+    }
+    __syncthreads();
+    for (int j = 0; j < k; ++j) {                  // upper R, R^T R = B, in place
+      if (threadIdx.x == 0) R[j * k + j] = sqrt(fmax(R[j * k + j], static_cast<double>(nu)));
+      __syncthreads();
+      const double djj = R[j * k + j];
+      for (int l = j + 1 + threadIdx.x; l < k; l += 256) R[j * k + l] /= djj;
+      __syncthreads();
+      for (int e = threadIdx.x; e < (k - j - 1) * (k - j - 1); e += 256) {
+        const int i = j + 1 + e / (k - j - 1), l = j + 1 + e % (k - j - 1);
+        if (l >= i) R[i * k + l] -= R[j * k + i] * R[j * k + l];
+      }
+      __syncthreads();
+    }
+    for (int j = threadIdx.x; j < k; j += 256) {   // R^-1 by back substitution, a column per thread
+      for (int i = j; i >= 0; --i) {
+        double s = (i == j) ? 1.0 : 0.0;
+        for (int l = i + 1; l <= j; ++l) s -= R[i * k + l] * X[l * k + j];
+        X[i * k + j] = s / R[i * k + i];
+      }
+      for (int i = j + 1; i < k; ++i) X[i * k + j] = 0.0;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < k * k; e += 256) Cm[e] = static_cast<float>(X[e]);
+    if (threadIdx.x == 0) {
+      a.scal[J.nu_slot] = nu;
+      a.scal[J.nuu_slot] = nu;
+    }
+    return;
+  }
+  // ---- phase 2
+  const float* Fu = reinterpret_cast<const float*>(resolve(J.ftu, a.ws, a.user));
+  float* K = reinterpret_cast<float*>(resolve(J.kout, a.ws, a.user));
+  float* lam = reinterpret_cast<float*>(resolve(J.lam, a.ws, a.user));
+  const float nu = a.scal[J.nu_slot];
+  if (nu == 0.0f) {                                // the zero sketch of phase 1: F = Omega
+    for (int e = threadIdx.x; e < k * r; e += 256) K[e] = (e / r == e % r) ? 1.0f : 0.0f;
+    for (int i = threadIdx.x; i < r; i += 256) lam[i] = 0.0f;
+    return;
+  }
+  for (int e = threadIdx.x; e < k * k; e += 256) {
+    const int i = e / k, j = e % k;
+    A[i * LD + j] = 0.5f * (Gy[i * k + j] + Gy[j * k + i]);
+    V[i * LD + j] = i == j ? 1.0f : 0.0f;
+  }
+  __syncthreads();
+  nys_jacobi(A, V, k, LD);
+  for (int i = threadIdx.x; i < k; i += 256) S[i] = A[i * LD + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += 256) {     // decreasing order (ties by index)
+    int rank = 0;
+    for (int j = 0; j < k; ++j) rank += (S[j] > S[i]) || (S[j] == S[i] && j < i);
+    order[rank] = i;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < k * r; e += 256) {
+    const int row = e / r, i = e % r;
+    const int c = order[i];
+    const float sv = S[c];
+    K[e] = sv > 0.0f ? V[row * LD + c] / sqrtf(sv) : 0.0f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < r; i += 256) {
+    float d = 0.0f;
+    for (int row = 0; row < k; ++row) d += K[row * r + i] * Fu[row * r + i];
+    const float sgn = d < 0.0f ? -1.0f : 1.0f;
+    for (int row = 0; row < k; ++row) K[row * r + i] *= sgn;
+    lam[i] = fmaxf(0.0f, S[order[i]] - nu);
+  }
+}
+
+// Element-wise jobs (NysElemJob): each job has its own run of blocks, and
+// its threads stride over the job's rows x cols elements.
+__global__ __launch_bounds__(256) void nys_elem_kernel(NysElemArgs a) {
+  const int gb = blockIdx.x;
+  const NysElemJob J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
+  const size_t total = static_cast<size_t>(J.rows) * J.cols;
+  const size_t stride = static_cast<size_t>(J.blocks) * 256;
+  float* dst = reinterpret_cast<float*>(resolve(J.dst, a.ws, a.user));
+  const char* src = resolve(J.src, a.ws, a.user);
+  const char* src2 = J.src2.kind != REF_NONE ? resolve(J.src2, a.ws, a.user) : nullptr;
+  const float* lam = J.lam.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(J.lam, a.ws, a.user)) : nullptr;
+  float lam_r = 0.0f;
+  if (J.kind == NE_SCALE) lam_r = lam[J.cols - 1];
+  for (size_t e = static_cast<size_t>(gb - J.blk_begin) * 256 + threadIdx.x; e < total; e += stride) {
+    const int r = static_cast<int>(e / J.cols), c = static_cast<int>(e % J.cols);
+    const size_t od = static_cast<size_t>(r) * J.ld_dst + c;
+    if (J.kind == NE_GATHER) {
+      dst[od] = c < J.cols1 ? reinterpret_cast<const float*>(src)[static_cast<size_t>(r) * J.ld_src + c]
+                            : reinterpret_cast<const float*>(src2)[static_cast<size_t>(r) * J.ld_src2 + (c - J.cols1)];
+    } else if (J.kind == NE_MOMENTUM) {
+      float* m = reinterpret_cast<float*>(const_cast<char*>(src));
+      const size_t om = static_cast<size_t>(r) * J.ld_src + c;
+      const float g = grad_elem(src2, static_cast<size_t>(r) * J.ld_src2 + c, J.g_fmt);
+      const float mn = a.beta1 * m[om] + (1.0f - a.beta1) * g;
+      m[om] = mn;
+      dst[od] = a.s_t * (a.beta1 * mn + (1.0f - a.beta1) * g);
+    } else if (J.kind == NE_SCALE) {
+      const float e_c = sqrtf((lam_r + a.mu) / (lam[c] + a.mu)) - 1.0f;
+      dst[od] = reinterpret_cast<const float*>(src)[static_cast<size_t>(r) * J.ld_src + c] * e_c;
+    } else {
+      const float v = reinterpret_cast<const float*>(src)[static_cast<size_t>(r) * J.ld_src + c];
+      dst[od] = __builtin_fmaf(a.decay, dst[od], -(a.lr * J.c0) * v);
+    }
+  }
+}
+
 // Clears the converged flags of every job (start of a refresh).
 __global__ void jacobi_reset_kernel(JacArgs a) {
   for (int j = threadIdx.x; j < a.n_jobs; j += blockDim.x) a.flags[a.jobs[j].flag] = 0;
@@ -1665,6 +2056,30 @@ hipError_t launch_jacobi(const JacArgs& a, int kind, int n_blocks, hipStream_t s
   if (kind == JAC_SOLVE) jacobi_solve_kernel<<<dim3(n_blocks), dim3(kJacThreads), 0, s>>>(a);
   else if (kind == JAC_APPLY) jacobi_apply_kernel<<<dim3(n_blocks), dim3(kJacThreads), 0, s>>>(a);
   else jacobi_check_kernel<<<dim3(n_blocks), dim3(kJacThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm32(const Gemm32Args& a, int n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  gemm32_kernel<<<dim3(n_blocks), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_nys_orth(const NysOrthArgs& a, hipStream_t s) {
+  if (a.n_jobs <= 0) return hipSuccess;
+  nys_orth_kernel<<<dim3(a.n_jobs), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_nys_small(const NysSmallArgs& a, hipStream_t s) {
+  if (a.n_jobs <= 0) return hipSuccess;
+  nys_small_kernel<<<dim3(a.n_jobs), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_nys_elem(const NysElemArgs& a, int n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  nys_elem_kernel<<<dim3(n_blocks), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

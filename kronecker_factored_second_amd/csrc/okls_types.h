@@ -23,7 +23,7 @@ constexpr int kScaleExp = 14;        // dynamic casts put max |x| in (2^13, 2^14
 // caller tensor of one group (byte offset from that tensor's base).
 enum RefKind : int32_t {
   REF_NONE = -1, REF_WS = 0, REF_W = 1, REF_G = 2, REF_M = 3,
-  REF_SA = 4, REF_SB = 5, REF_PA = 6, REF_PB = 7, REF_V = 8
+  REF_SA = 4, REF_SB = 5, REF_PA = 6, REF_PB = 7, REF_V = 8, REF_PSA = 9, REF_PSB = 10
 };
 struct Ref {
   int32_t kind;
@@ -40,7 +40,7 @@ struct TileRef {
 
 // Caller pointers of one okls_step, passed by value to every launch.
 struct UserPtrs {
-  void* p[kMaxGroups][9];
+  void* p[kMaxGroups][11];
 };
 
 // ---------------------------------------------------------------------------
@@ -286,6 +286,102 @@ struct JacArgs {
   float tol;               // converged when ||off(B)||_F <= tol ||diag(B)||_F
   float* partials;         // float2 (off^2, diag^2) per B tile
   int32_t* flags;
+  char* ws;
+  UserPtrs user;
+};
+
+// ---------------------------------------------------------------------------
+// Nystrom low-rank factors.  All arithmetic is fp32 (the sketches are thin:
+// k = r + p <= kNysMaxK columns), in four kernels:
+//  - gemm32: batched fp32 products C = alpha op(A) op(B) (rows scaled by an
+//    optional vector) + beta C, 64 x 64 tiles from LDS;
+//  - nys_orth: thin QR's Q of a d x k matrix in place by classical
+//    Gram-Schmidt with reorthogonalisation, a dependent column replaced by a
+//    column of the refresh's Gaussian matrix;
+//  - nys_small: the k x k end of a refresh (shift, Cholesky, triangular
+//    inverse, the Gram of the triangular solve and its eigendecomposition,
+//    ordering, sign alignment), one workgroup per factor;
+//  - nys_elem: element-wise gather, momentum, column scaling and update.
+// ---------------------------------------------------------------------------
+constexpr int kNysMaxK = 128;
+constexpr int kG32Tile = 64;
+constexpr int kG32K = 16;
+
+struct Gemm32Prob {
+  Ref A, B, C;
+  int32_t M, N, K;
+  int32_t lda, ldb, ldc;   // row strides in elements
+  int32_t ta, tb;          // op(A) = A^T (A stored K x M) / op(B) = B^T (B stored N x K)
+  int32_t a_fmt, b_fmt;    // GradFmt of the operands (fp32 except a gradient)
+  float alpha;
+  int32_t alpha_slot;      // >= 0: alpha is multiplied by scal[alpha_slot]
+  float beta;              // 0: C is written without being read
+  Ref rowscale;            // REF_NONE, or M floats: row i of the product times rowscale[i]
+  int32_t tiles_n;
+  int32_t blk_begin;
+};
+
+struct Gemm32Args {
+  const Gemm32Prob* jobs;
+  int32_t n_jobs;
+  const float* scal;
+  char* ws;
+  UserPtrs user;
+};
+
+struct NysOrthJob {
+  Ref Y;                   // d x k fp32, row stride ld: replaced by Q
+  Ref fb;                  // d x k fp32, row stride ldf: column (j + fb_shift) % k replaces a dependent column j
+  int32_t d, k, ld, ldf, fb_shift;
+};
+
+struct NysOrthArgs {
+  const NysOrthJob* jobs;
+  int32_t n_jobs;
+  char* ws;
+  UserPtrs user;
+};
+
+struct NysSmallJob {
+  Ref gram;                // k x k: phase 1 Y^T Y; phase 2 F^T F (fp32)
+  Ref cmat;                // k x k: phase 1 Omega^T Y in, R^-1 out (fp32)
+  Ref ftu;                 // k x r: phase 2 F^T U_prev (fp32)
+  Ref kout;                // k x r: phase 2 U = F K (fp32)
+  Ref lam;                 // r floats: phase 2 the eigenvalues (the caller's factor)
+  Ref scratch;             // 2 k x k doubles (phase 1)
+  int32_t k, r;
+  int32_t nu_slot, nuu_slot;   // scal slots: the shift nu, and the multiplier nu_u of Omega in Y_nu
+};
+
+struct NysSmallArgs {
+  const NysSmallJob* jobs;
+  int32_t n_jobs;
+  int32_t phase;           // 1: shift, Cholesky, R^-1; 2: eigenpairs of F^T F, K, Lambda
+  float* scal;
+  char* ws;
+  UserPtrs user;
+};
+
+enum NysElemKind : int32_t {
+  NE_GATHER = 0,           // dst (rows x cols) = [src (cols1 columns) | src2 (the rest)]
+  NE_MOMENTUM = 1,         // src (M) <- beta1 M + (1 - beta1) G (src2, g_fmt); dst = s_t (beta1 M' + (1 - beta1) G)
+  NE_SCALE = 2,            // dst = src * e_j by column, e_j = sqrt((lam_{r-1} + mu) / (lam_j + mu)) - 1
+  NE_UPDATE = 3            // dst (W) = decay W - lr c0 src
+};
+
+struct NysElemJob {
+  int32_t kind;
+  Ref dst, src, src2, lam;
+  int32_t rows, cols, ld_dst, ld_src, ld_src2, cols1;
+  int32_t g_fmt;
+  float c0;
+  int32_t blk_begin, blocks;
+};
+
+struct NysElemArgs {
+  const NysElemJob* jobs;
+  int32_t n_jobs;
+  float beta1, s_t, mu, lr, decay;
   char* ws;
   UserPtrs user;
 };

@@ -17,7 +17,7 @@ OKLS_OK = 0
 STATUS = {0: "OKLS_OK", -1: "OKLS_ERR_INVALID_ARG", -2: "OKLS_ERR_SHAPE", -3: "OKLS_ERR_DTYPE",
           -4: "OKLS_ERR_WORKSPACE", -5: "OKLS_ERR_HIP", -6: "OKLS_ERR_NONFINITE", -7: "OKLS_ERR_UNSUPPORTED"}
 OKLS_F32, OKLS_BF16, OKLS_F16 = 0, 1, 2
-MODE = {"okls": 0, "shampoo": 1, "muon": 2, "soap": 3}
+MODE = {"okls": 0, "shampoo": 1, "muon": 2, "soap": 3, "nystrom": 4}
 # the Muon setting of the polar iteration: 5 steps (Clean, Table 6) on [1e-2, 1]
 MUON_DEFAULTS = dict(ns_steps=5, ns_floor=1e-2)
 # optimizer hyperparameters per mode: the README's "Hyperparameters" table, and
@@ -40,7 +40,8 @@ class Config(ctypes.Structure):
                 ("eps_convex", ctypes.c_int32), ("decay_after", ctypes.c_int32), ("shape_scale", ctypes.c_int32),
                 ("ns_classical", ctypes.c_int32), ("whiten_split", ctypes.c_int32),
                 ("soap_beta", ctypes.c_float), ("precond_freq", ctypes.c_int32), ("soap_moments", ctypes.c_int32),
-                ("bias_correction", ctypes.c_int32), ("jacobi_sweeps", ctypes.c_int32), ("jacobi_tol", ctypes.c_float)]
+                ("bias_correction", ctypes.c_int32), ("jacobi_sweeps", ctypes.c_int32), ("jacobi_tol", ctypes.c_float),
+                ("nys_rank", ctypes.c_int32), ("nys_oversample", ctypes.c_int32), ("nys_passes", ctypes.c_int32)]
 
 
 class GroupDesc(ctypes.Structure):
@@ -50,7 +51,8 @@ class GroupDesc(ctypes.Structure):
 
 class GroupTensors(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("M", ctypes.c_void_p), ("Sa", ctypes.c_void_p),
-                ("Sb", ctypes.c_void_p), ("Pa", ctypes.c_void_p), ("Pb", ctypes.c_void_p), ("V", ctypes.c_void_p)]
+                ("Sb", ctypes.c_void_p), ("Pa", ctypes.c_void_p), ("Pb", ctypes.c_void_p), ("V", ctypes.c_void_p),
+                ("PsiA", ctypes.c_void_p), ("PsiB", ctypes.c_void_p)]
 
 
 class ProfileStats(ctypes.Structure):
@@ -217,11 +219,12 @@ def _ptr(t):
 
 
 def tensors_array(per_group):
-    """per_group: list of dicts with torch tensors W, G, M, Sa, Sb, Pa, Pb (and V in SOAP mode)."""
+    """per_group: list of dicts with torch tensors W, G, M, Sa, Sb, Pa, Pb (and V in SOAP mode,
+    PsiA and PsiB in Nystrom mode)."""
     arr = (GroupTensors * len(per_group))()
     for i, d in enumerate(per_group):
         arr[i] = GroupTensors(*[(d[k].data_ptr() if d.get(k) is not None else None)
-                                for k in ("W", "G", "M", "Sa", "Sb", "Pa", "Pb", "V")])
+                                for k in ("W", "G", "M", "Sa", "Sb", "Pa", "Pb", "V", "PsiA", "PsiB")])
     return arr
 
 
@@ -293,7 +296,7 @@ class OKLS:
 
     def __init__(self, params, lr=None, beta1=None, beta2=None, eps=None, weight_decay=None,
                  mode="okls", precision="fp16", grad_dtype=None, chunk_matrices=0, workspace_limit=None,
-                 **cfg_overrides):
+                 psi_seed=0, **cfg_overrides):
         import torch
         self.torch = torch
         self.params = list(params)
@@ -328,6 +331,14 @@ class OKLS:
             self.groups.append((b, m, n, gdt))
             if mode == "muon":     # no factors or roots
                 self.state.append(dict(M=torch.zeros(b, m, n, device=dev)))
+            elif mode == "nystrom":   # low-rank factors U (d x r') and Lambda (r') per side
+                r = self.cfg.nys_rank
+                ka, kb = min(r + self.cfg.nys_oversample, m), min(r + self.cfg.nys_oversample, n)
+                ra, rb = min(r, ka), min(r, kb)
+                self.state.append(dict(M=torch.zeros(b, m, n, device=dev), Sa=torch.empty(b, ra, device=dev),
+                                       Sb=torch.empty(b, rb, device=dev), Pa=torch.empty(b, m, ra, device=dev),
+                                       Pb=torch.empty(b, n, rb, device=dev),
+                                       PsiA=torch.zeros(b, m, ka, device=dev), PsiB=torch.zeros(b, n, kb, device=dev)))
             elif mode == "soap":   # factors, bases and both moments
                 self.state.append(dict(M=torch.zeros(b, m, n, device=dev), V=torch.zeros(b, m, n, device=dev),
                                        Sa=torch.empty(b, m, m, device=dev), Sb=torch.empty(b, n, n, device=dev),
@@ -345,6 +356,8 @@ class OKLS:
         self.stream = torch.cuda.current_stream(dev).cuda_stream
         self.handle = init(self.cfg, self.groups, self.workspace, self.stream)
         self.t = 0
+        self.psi_seed = int(psi_seed)
+        self._psi_gen = None
         init_state(self.handle, self._tensors(grads=None), self.stream)
 
     _GRAD_DTYPES = {OKLS_F32: "float32", OKLS_BF16: "bfloat16", OKLS_F16: "float16"}
@@ -378,9 +391,21 @@ class OKLS:
         self._keep = per
         return tensors_array(per)
 
+    def _draw_sketches(self, t):
+        """Nystrom mode: the Gaussian matrices of a refresh step (t = 1, 1 + T, ...)
+        are the method's random numbers, drawn here and passed to the library."""
+        if self.mode != "nystrom" or (t - 1) % max(self.cfg.root_period, 1) != 0:
+            return
+        if self._psi_gen is None:
+            self._psi_gen = self.torch.Generator(device=self.params[0].device).manual_seed(self.psi_seed)
+        for s in self.state:
+            for k in ("PsiA", "PsiB"):
+                s[k].normal_(generator=self._psi_gen)
+
     def step(self, grads=None, lr=None):
         lr = self.lr if lr is None else float(lr)
         self.stream = self.torch.cuda.current_stream(self.params[0].device).cuda_stream
+        self._draw_sketches(self.t + 1)
         tensors = self._tensors(grads, check=True)
         # the counter and the learning rate change only once the library has
         # accepted the step

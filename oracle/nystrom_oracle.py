@@ -30,7 +30,7 @@ via Nystrom Sketching"; short name [CLEAN]):
           with U_prev).
 
 Readings where the pages leave a step open (listed with the design notes as
-N1..N6):
+N1..N9):
   N1  eps(x) is the spacing of IEEE single precision at x, 2^(floor(log2 x)
       - 23): the shift is meant at the working precision's rounding level,
       and the library works in fp32.
@@ -52,6 +52,12 @@ N1..N6):
       min(r, d) of them.
   N8  A sketch Y = 0 (a zero factor) gives Lambda = 0 and U = the first
       columns of the orthonormalised test matrix (nothing to factor).
+  N9  With r above the factor's rank the tail eigenvalues are zero here
+      (fp64: ~1e-17 of ||A||) but sit at the sketch's rounding level in any
+      fp32 computation (~nu), and c = (lambda_r + mu)^1/2 follows that
+      rounding unless mu is far above nu: P^-1/2 is then defined by the
+      arithmetic, not by the method.  Comparisons keep r at or below the
+      factors' rank.
 
 Parity status (what pins each function in the CPU test-suite):
   nystrom (Alg. 2/3) ... an exactly rank-r PSD matrix is reproduced to
