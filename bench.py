@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "preconditioned matrices/sec + step latency (ms); % fp16 MFMA peak on NS chain"
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector (the Nystrom mode's SIMT products)
 
 
 # the GEMM's traffic depends on its kernel and on the planner's launch shapes
@@ -60,10 +61,13 @@ def parse():
     p.add_argument("--device-grads", action="store_true",
                    help="gradients of the workload's recipe drawn on the GPU (the default for "
                         "workloads above 1e9 parameters, whose host recipes would take minutes per step)")
-    p.add_argument("--mode", choices=["okls", "shampoo", "muon", "soap"], default=None,
+    p.add_argument("--mode", choices=["okls", "shampoo", "muon", "soap", "nystrom"], default=None,
                    help="optimizer mode (default: the workload's); muon runs the polar iteration of the momentum "
                         "on the same matrices, the pages' throughput comparison; soap runs Adam in the factors' "
                         "eigenbasis (bases refreshed every --precond-freq steps)")
+    p.add_argument("--nys-rank", type=int, default=32, help="nystrom mode: eigenpairs kept per factor")
+    p.add_argument("--nys-oversample", type=int, default=8, help="nystrom mode: extra sketch columns")
+    p.add_argument("--nys-passes", type=int, default=1, help="nystrom mode: subspace-iteration passes")
     p.add_argument("--precond-freq", type=int, default=10,
                    help="soap mode: refresh the eigenbases after every this many steps (the Clean paper's Table 6: 10)")
     p.add_argument("--root-period", type=int, default=1,
@@ -238,6 +242,44 @@ def progress(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_baseline_nys(w, budget_s, args):
+    """The fp64 Nystrom oracle on the same bounded sample as cpu_baseline:
+    per shape class one step that refreshes the factors and one that keeps
+    them, averaged over one period and scaled to the workload's counts."""
+    from oracle import nystrom_oracle as Y
+    from kronecker_factored_second_amd import workloads as WL
+    T = max(args.root_period, 1)
+    hp = Y.NysHyper(rank=args.nys_rank, oversample=args.nys_oversample, passes=args.nys_passes, period=T)
+    rng = np.random.default_rng(0)
+    total_s, step_s, sampled, timed = 0.0, 0.0, [], {}
+    for gi, (m, n, b) in enumerate(w.groups):
+        key = (min(m, n), max(m, n))
+        if key in timed:
+            sampled.append(f"{m}x{n}: as {timed[key][0]}")
+            step_s += timed[key][1] * b
+            continue
+        G = WL.gradient(w, gi, 0, 1).astype(np.float64)
+        k = args.nys_rank + args.nys_oversample
+        psa, psb = rng.standard_normal((m, min(k, m))), rng.standard_normal((n, min(k, n)))
+        t0 = time.perf_counter()
+        r = Y.nys_step(Y.init_state(np.zeros((m, n))), G, hp, 1, psa, psb)
+        dt_ref = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        Y.nys_step(r.state, G, hp, 2 if T > 1 else 1, psa, psb)
+        dt_keep = time.perf_counter() - t0 if T > 1 else dt_ref
+        total_s += dt_ref + dt_keep
+        dt = (dt_ref + (T - 1) * dt_keep) / T
+        sampled.append(f"{m}x{n}:{dt:.3f}s")
+        timed[key] = (f"{m}x{n}", dt)
+        step_s += dt * b
+        if total_s > budget_s:
+            return None
+    return {"value": w.n_matrices / step_s, "unit": "matrices/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"per shape class one fp64 oracle step refreshing the factors and one keeping them, averaged "
+                      f"over {T} steps ({', '.join(sampled)}), scaled to the {w.n_matrices}-matrix workload: "
+                      f"{step_s:.3f} s/step"}
+
+
 def cpu_baseline_soap(w, budget_s, freq):
     """The fp64 eigenbasis-Adam oracle on the same bounded sample as
     cpu_baseline: per shape class one step that keeps the bases and one that
@@ -388,6 +430,8 @@ def main():
         limit = torch.cuda.mem_get_info(0)[0] - sum(b * (m * n + 2 * m * m + 2 * n * n) * 4 for m, n, b in w.groups) \
             - (8 << 30)
     extra = dict(precond_freq=args.precond_freq) if mode == "soap" else dict(root_period=args.root_period)
+    if mode == "nystrom":
+        extra.update(nys_rank=args.nys_rank, nys_oversample=args.nys_oversample, nys_passes=args.nys_passes)
     opt = okls.OKLS(params, mode=mode, precision=args.precision,
                     grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit, **extra)
     progress(f"{w.name}: optimizer ready (workspace {opt.workspace.numel() / 2**30:.1f} GiB)")
@@ -446,7 +490,7 @@ def main():
     g_fl = sum(prof[k]["flops"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     g_n = sum(prof[k]["launches"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     g_b = sum(prof[k]["bytes"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
-    achieved = g_fl / (g_busy * 1e-3) / 1e12
+    achieved = g_fl / (g_busy * 1e-3) / 1e12 if g_busy > 0 else 0.0
     per_launch = g_fl / (g_ms * 1e-3) / 1e12
     ns = prof["ns_gemm"]
     ns_tflops = ns["flops"] / (ns["busy_ms"] * 1e-3) / 1e12
@@ -469,7 +513,9 @@ def main():
                                                    " (device Gaussian)") if device_grads else "") +
                    f", precision {args.precision}" +
                    (f", chunks of {opt.cfg.chunk_matrices} matrices" if opt.cfg.chunk_matrices else "") +
-                   (f", roots every {args.root_period} steps" if args.root_period > 1 and mode != "soap" else "") +
+                   (f", roots every {args.root_period} steps" if args.root_period > 1 and mode not in ("soap", "nystrom") else "") +
+                   (f", Nystrom rank {args.nys_rank} + {args.nys_oversample}, {args.nys_passes} pass(es), factors "
+                    f"refreshed every {args.root_period} steps" if mode == "nystrom" else "") +
                    (f", eigenbases refreshed every {args.precond_freq} steps" if mode == "soap" else ""),
                    "matrices": w.n_matrices, "parallelism": "single GPU"},
         "step_latency_ms": ms_step,
@@ -478,10 +524,12 @@ def main():
         "ms_per_step_with_launch_events": ms_step_profiled,
         "ns_chain": {"tflops": ns_tflops, "frac_fp16_peak": ns_tflops / PEAK_FP16_TFLOPS,
                      "ms_per_step": ns["busy_ms"] / max(prof["steps"], 1), "launches_per_step": ns["launches"] / max(prof["steps"], 1)},
-        "roofline": {"kernel": "gemm_nt_kernel", "bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS,
+        "roofline": {"kernel": "gemm32_kernel" if mode == "nystrom" else "gemm_nt_kernel",
+                     "bound": "alu" if mode == "nystrom" else "mfma", "achieved": achieved,
+                     "peak": PEAK_FP32_TFLOPS if mode == "nystrom" else PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / (PEAK_FP32_TFLOPS if mode == "nystrom" else PEAK_FP16_TFLOPS),
                      "traffic": measured_traffic(args.workload) if (args.precision == "fp16" and mode == w.mode and
-                                                                    args.root_period == 1) else None,
+                                                                    args.root_period == 1 and mode != "nystrom") else None,
                      "method": "algorithmic FLOPs of every gemm_nt_kernel launch over the union of their intervals, "
                                "from HIP events on the launch streams in a second pass of the same steps (the timed "
                                "pass runs without them); where the plan runs two Newton-Schulz chains their launches overlap",
@@ -501,6 +549,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = (cpu_baseline_soap(w, args.cpu_sample_seconds, args.precond_freq) if mode == "soap"
+                                else cpu_baseline_nys(w, args.cpu_sample_seconds, args) if mode == "nystrom"
                                 else cpu_baseline(w, args.cpu_sample_seconds, args.root_period, mode))
     print(json.dumps(line), flush=True)
 

@@ -20,7 +20,7 @@ int main(int argc, char** argv) {
   for (int r = 0; r < rounds; ++r) {
     okls_config c;
     okls_default_config(&c);
-    c.mode = uni(0, 3);
+    c.mode = uni(0, 4);
     c.ns_steps = uni(2, 16);
     c.ns_split_steps = uni(0, 1) ? 0 : uni(0, c.ns_steps);
     c.factor_split = uni(0, 1);
@@ -36,6 +36,9 @@ int main(int argc, char** argv) {
     c.soap_moments = uni(0, 1);
     c.bias_correction = uni(0, 1);
     c.jacobi_sweeps = uni(1, 3);
+    c.nys_rank = uni(1, 40);
+    c.nys_oversample = uni(0, 12);
+    c.nys_passes = uni(0, 3);
     const int ng = uni(1, 16);
     std::vector<okls_group_desc> g(ng);
     for (okls_group_desc& d : g) {

@@ -286,6 +286,47 @@ def test_soap_config_validation():
             okls.plan_query(_soap_cfg(**bad), g)
 
 
+def _nys_cfg(**kw):
+    base = dict(mode=okls.MODE["nystrom"], nys_rank=16, nys_oversample=8, nys_passes=1, root_period=3)
+    base.update(kw)
+    return okls.precision_config("fp16", **base)
+
+
+def test_nystrom_plans_validate_and_flops_are_the_closed_forms():
+    """Nystrom mode plans and validates for ragged, tiny (a side below
+    r + p), transformer-block and bf16 shapes; a step that keeps the factors
+    launches fewer kernels; the per-step preconditioning FLOPs are the thin
+    products 8 m n r' (N U_b, the rank-r' correction of N, U_a^T N', the
+    second correction; r' per side), and a refresh adds the sketch products."""
+    _lib()
+    for groups in ([(2, 96, 160, 0), (1, 200, 72, 0)], [(1, 5, 7, 1), (3, 33, 40, 2)],
+                   [(4, 1024, 1024, 1), (2, 2816, 1024, 1), (1, 1024, 2816, 1)]):
+        for passes in (0, 1, 2):
+            cfg = _nys_cfg(nys_passes=passes)
+            assert okls.workspace_size(cfg, groups) > 0, (groups, passes)
+            info = okls.plan_query(cfg, groups)
+            assert info["launches_stale"] < info["launches"] and info["ns_chains"] == 0
+            want = 0.0
+            for b, m, n, _ in groups:
+                ra, rb = min(16, min(24, m)), min(16, min(24, n))
+                want += b * (2.0 * m * n * rb * 2 + 2.0 * m * n * ra * 2)
+            assert info["flops"]["whiten_gemm"] == pytest.approx(want, rel=1e-12)
+            assert info["flops"]["ns_gemm"] > 0 and info["flops"]["eigensolver"] > 0
+
+
+def test_nystrom_config_validation():
+    """eps must be positive (P^-1/2 divides by lambda + eps), r + p fits the
+    k x k workgroup kernel (at most 128), and the counts are range-checked."""
+    _lib()
+    g = [(1, 64, 80, 0)]
+    assert okls.workspace_size(_nys_cfg(), g) > 0
+    assert okls.workspace_size(_nys_cfg(nys_rank=120, nys_oversample=8), g) > 0
+    with pytest.raises(okls.OKLSError, match="UNSUPPORTED"):
+        okls.plan_query(_nys_cfg(nys_rank=120, nys_oversample=9), g)
+    for bad in (dict(eps=0.0), dict(nys_rank=0), dict(nys_oversample=-1), dict(nys_passes=9), dict(beta2=1.0)):
+        assert okls.workspace_size(_nys_cfg(**bad), g) == 0, bad
+
+
 def test_plan_query_rejects_invalid_arguments():
     _lib()
     cfg = okls.precision_config("fp16")
