@@ -547,6 +547,12 @@ def main():
         "state_finite": finite,
         "host_wall_s": wall,
     }
+    if mode in ("okls", "shampoo"):
+        # convergence of the roots: ||Z_{K-1} Y_{K-1} - I||_F of every chain of the last step
+        r = np.array([x for g in opt.ns_residuals() for mat in g for side in mat for x in side], dtype=np.float64)
+        r = r[np.isfinite(r)]
+        if r.size:
+            line["ns_residual"] = {"chains": int(r.size), "median": float(np.median(r)), "max": float(r.max())}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = (cpu_baseline_soap(w, args.cpu_sample_seconds, args.precond_freq) if mode == "soap"
                                 else cpu_baseline_nys(w, args.cpu_sample_seconds, args) if mode == "nystrom"

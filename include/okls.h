@@ -297,6 +297,24 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* tensors, int64_t
  * synchronises `stream`.  Returns OKLS_OK or OKLS_ERR_NONFINITE. */
 okls_status okls_check_finite(okls_handle* h, const okls_group_tensors* tensors, void* stream);
 
+/* Convergence diagnostic of the coupled Newton-Schulz roots ("Online KL
+ * Shampoo" README, "How it works": the roots come from the coupled
+ * iteration).  The last step's T = a I + b Z Y is formed from the product
+ * Z_{K-1} Y_{K-1}, which converges to I; that launch's epilogue also sums
+ * (Z_{K-1} Y_{K-1} - I)^2 over the factor, in fp32 per wave and tile, and
+ * this call reads the partials back (synchronising `stream`) and returns
+ * ||Z_{K-1} Y_{K-1} - I||_F summed in double, in the same order every call.
+ * Y and Z are the iteration's own scaled fp16 (split: hi + lo) iterates, so
+ * the value includes their rounding.
+ * out: host array of `count` >= 4 * (matrices over all groups) doubles,
+ * out[(mat * 2 + side) * 2 + chain] with mat the matrix index in group order,
+ * side 0 for S_a and 1 for S_b, chain 0 for the inverse root and, in the
+ * Shampoo mode, chain 1 for the square root of that result (its fourth root).
+ * Values are those of the most recent step that recomputed the roots; NaN
+ * where none has yet, and for the OKLS mode's chain 1.  OKLS and Shampoo
+ * modes only (else OKLS_ERR_UNSUPPORTED); needs ns_steps >= 2 (else NaN). */
+okls_status okls_ns_residuals(okls_handle* h, double* out, int64_t count, void* stream);
+
 /* The Newton-Schulz coefficient table the handle uses: a[k], b[k] for
  * k < ns_steps (T_k = a_k I + b_k Z_k Y_k; in Muon mode X <- a_k X +
  * b_k (X X^T) X), written to caller host arrays of length >= max_steps.

@@ -27,6 +27,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <functional>
+#include <limits>
 #include <map>
 #include <new>
 #include <string>
@@ -113,6 +114,7 @@ struct FacBufs {
   size_t Q16 = 0, Q16T = 0, L16 = 0, HT16 = 0, B32 = 0, jbuf = 0;
   int ldq = 0;   // row stride of those four: [hi | lo] always (the refresh's last products are split)
   int s_l = 0, s_lx = 0;
+  int mat = -1, side = 0;   // the matrix (in group order) and side this factor belongs to
 };
 
 struct MatBufs {
@@ -191,6 +193,10 @@ struct okls_handle {
   size_t ws_bytes = 0;
   size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_sym = 0, off_scal = 0, off_part = 0, off_flag = 0;
   size_t off_adam = 0, off_jac = 0, off_g32 = 0, off_north = 0, off_nsmall = 0, off_nelem = 0;
+  size_t off_resid = 0, resid_floats = 0;   // Newton-Schulz residual partials
+  struct Resid { int mat, side, chain, first, count; };
+  std::vector<Resid> resid;
+  int n_mats = 0;
   float s_np = 1.0f;                        // SOAP: static scale of the Adam direction
   std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
   std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them
@@ -333,6 +339,12 @@ struct Planner {
   int n_slots = SL_FIRST_DYN; // max over chunks
   int first_dyn = SL_FIRST_DYN;
   int max_partials = 1;
+  // Newton-Schulz residual partials: per (matrix, side, chain) a range of
+  // floats in the residual region, of which the last T launch writes count
+  struct ResidSlot { int mat, side, chain, first, count; };
+  std::vector<ResidSlot> resid_slots;
+  int resid_floats = 0;
+  std::vector<int> mat_base;   // first matrix of each group (group order)
 
   Planner(const okls_config& c, const std::vector<okls_group_desc>& g)
       : cfg(c), groups(g), okls_mode(c.mode == OKLS_MODE_OKLS), muon_mode(c.mode == OKLS_MODE_MUON),
@@ -343,6 +355,8 @@ struct Planner {
       s_np = pow2_for_bound(adam_ratio_bound(cfg));
     }
     coeff_table(cfg, na, nb);
+    int nm = 0;
+    for (const okls_group_desc& gd : groups) { mat_base.push_back(nm); nm += gd.batch; }
     double prod = 1.0, amax = 0.0;
     for (int k = 0; k < cfg.ns_steps; ++k) {
       prod *= std::max(std::fabs(na[k]), std::fabs(na[k] + nb[k]));
@@ -583,7 +597,7 @@ struct Planner {
       const long tm = p.Mp / kBigTile, tn = p.Np / kBigTile;
       big_tiles += upper ? tm * (tm + 1) / 2 : tm * tn;
     }
-    const bool f16_out = r.epi == EPI_NS_T || r.epi == EPI_NS_Y1 || r.epi == EPI_STORE16 || r.epi == EPI_NS_FINAL ||
+    const bool f16_out = r.epi == EPI_NS_T || r.epi == EPI_NS_T_RES || r.epi == EPI_NS_Y1 || r.epi == EPI_STORE16 || r.epi == EPI_NS_FINAL ||
                          r.epi == EPI_POLAR;
     // a Muon launch has no concurrent chain to fill a partly idle round: the
     // 256 tile only from one full round of it
@@ -741,6 +755,7 @@ struct Planner {
     p.ld16T = -1;
     p.aux_lo = -1;
     p.s_aux = -1;
+    p.resid = -1;
     return p;
   }
 
@@ -811,6 +826,7 @@ struct Planner {
       const float ka = static_cast<float>(na[k]), kb = static_cast<float>(nb[k]);
       // T_k = a_k I + b_k Z_k Y_k
       std::vector<GemmProb> pt;
+      const size_t first_slot = resid_slots.size();
       for (size_t f = 0; f < nf; ++f) {
         FacBufs& F = *facs[f];
         GemmProb p = prob();
@@ -819,9 +835,25 @@ struct Planner {
         p.Mp = p.Np = F.dp; p.epi = EPI_NS_T; p.out16 = ws_ref(F.T); p.out16T = ws_ref(F.TT); p.ld16 = F.ld;
         p.lo16 = F.dp;
         p.s_out = SL_T; p.sA = SL_Z; p.sB = SL_Y;
+        if (k == K - 1 && F.mat >= 0) {
+          // the last T's epilogue leaves the partials of ||Z_{K-1} Y_{K-1} - I||_F:
+          // room for the small tile's count (one per wave and tile), the larger
+          p.epi = EPI_NS_T_RES;
+          p.resid = resid_floats;
+          const int tt = F.dp / kTile;
+          resid_slots.push_back(ResidSlot{F.mat, F.side, chain, resid_floats, 0});
+          resid_floats += tt * tt * 4;
+        }
         pt.push_back(p);
       }
       add_gemm(L, pt, false, k < ks, k < ks, ka, kb);
+      // partials written: one per wave of every tile of the class the launch took
+      const int bt = L.back().tile;
+      for (size_t q = first_slot, f = 0; f < nf; ++f) {
+        if (k != K - 1 || facs[f]->mat < 0) continue;
+        const int n = facs[f]->dp / bt;
+        resid_slots[q++].count = n * n * (bt == kBigTile ? 8 : 4);
+      }
       std::vector<GemmProb> pu;
       if (k < K - 1) {
         for (size_t f = 0; f < nf; ++f) {   // Y_{k+1} = Y_k T_k
@@ -1782,6 +1814,9 @@ struct Planner {
       std::vector<FacBufs*> facs;
       std::vector<Ref> src, pdst;
       for (MatBufs& mb : mats) {
+        mb.fa.mat = mb.fb.mat = mat_base[mb.group] + mb.index;
+        mb.fa.side = 0;
+        mb.fb.side = 1;
         facs.push_back(&mb.fa);
         src.push_back(user_ref(REF_SA, mb.group, aoff(mb)));
         pdst.push_back(user_ref(REF_PA, mb.group, aoff(mb)));
@@ -1946,7 +1981,7 @@ struct Planner {
         if (r.type == L_GEMM) {
           if (r.first < 0 || r.first + r.count > static_cast<int>(tiles.size())) return false;
           if (r.tile != kTile && r.tile != kBigTile) return false;
-          if (r.epi < EPI_STORE32 || r.epi > EPI_POLAR_UPDATE) return false;
+          if (r.epi < EPI_STORE32 || r.epi > EPI_NS_T_RES) return false;
           const int segs = r.split_in ? 2 : 1;
           for (int t = r.first; t < r.first + r.count; ++t) {
             const TileRef tr = tiles[t];
@@ -1971,7 +2006,7 @@ struct Planner {
               if (!fits(p.out32, (static_cast<size_t>(p.M - 1) * p.ld32 + p.N) * 4)) return false;
               if (p.epi == EPI_SYRK && p.M != p.N) return false;
             }
-            const bool need16 = p.epi == EPI_NS_T || p.epi == EPI_NS_Y1 || p.epi == EPI_STORE16 ||
+            const bool need16 = p.epi == EPI_NS_T || p.epi == EPI_NS_T_RES || p.epi == EPI_NS_Y1 || p.epi == EPI_STORE16 ||
                                 p.epi == EPI_POLAR || (p.epi == EPI_NS_FINAL && p.out16.kind != REF_NONE);
             if (need16) {
               if (p.out16.kind == REF_NONE || !slot_ok(p.s_out)) return false;
@@ -1990,6 +2025,11 @@ struct Planner {
               if (p.ldaux < need_lda || (p.aux_lo >= 0 && p.aux_lo < p.Np) || (p.ldaux & 3) || (p.aux_lo > 0 && (p.aux_lo & 3)))
                 return false;
               if (!fits(p.aux, static_cast<size_t>(p.Mp) * p.ldaux * 2)) return false;
+            }
+            if (p.epi == EPI_NS_T_RES) {   // one partial per wave and tile: the small tile's count at most
+              if (p.resid < 0 || p.Mp % kTile || p.Np % kTile) return false;
+              const long need = static_cast<long>(p.Mp / kTile) * (p.Np / kTile) * 4;
+              if (p.resid + need > resid_floats) return false;
             }
             if (p.epi == EPI_NS_Y1) {
               if (p.aux.kind == REF_NONE || p.ldaux < p.N || !slot_ok(p.cslot)) return false;
@@ -2172,6 +2212,8 @@ struct Planner {
 
   // Plans every chunk; chunk buffers start at `base` (identical across chunks).
   void plan(size_t base) {
+    resid_slots.clear();
+    resid_floats = 0;
     std::vector<std::vector<MatBufs>> all;
     std::vector<MatBufs> cur;
     const int cap = cfg.chunk_matrices > 0 ? cfg.chunk_matrices : (1 << 30);
@@ -2210,7 +2252,7 @@ struct Planner {
 
 struct WsLayout {
   size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, adam = 0, jac = 0, g32 = 0, north = 0, nsmall = 0,
-         nelem = 0, scal = 0, part = 0, flag = 0, chunk = 0, total = 0;
+         nelem = 0, scal = 0, part = 0, flag = 0, resid = 0, chunk = 0, total = 0;
 };
 
 WsLayout ws_layout(Planner& P) {
@@ -2233,6 +2275,7 @@ WsLayout ws_layout(Planner& P) {
   w.scal = take(static_cast<size_t>(P.n_slots) * sizeof(float));
   w.part = take(static_cast<size_t>(P.max_partials) * 2 * sizeof(float) * kNsStreams);   // one region per stream
   w.flag = take(sizeof(int));
+  w.resid = take(static_cast<size_t>(P.resid_floats) * sizeof(float));
   w.chunk = off;
   w.total = off + P.chunk_bytes;
   return w;
@@ -2410,6 +2453,10 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_scal = w.scal;
   h->off_part = w.part;
   h->off_flag = w.flag;
+  h->off_resid = w.resid;
+  h->resid_floats = static_cast<size_t>(P.resid_floats);
+  for (const Planner::ResidSlot& q : P.resid_slots) h->resid.push_back({q.mat, q.side, q.chain, q.first, q.count});
+  for (const okls_group_desc& gd : g) h->n_mats += gd.batch;
   h->chunks = P.chunks;
   h->chunks_stale = P.chunks_stale;
   h->part_stride = static_cast<size_t>(P.max_partials) * 2;
@@ -2468,6 +2515,9 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   up(w.nsmall, P.nsmall_jobs.data(), P.nsmall_jobs.size() * sizeof(NysSmallJob));
   up(w.nelem, P.nelem_jobs.data(), P.nelem_jobs.size() * sizeof(NysElemJob));
   up(w.scal, scal.data(), scal.size() * sizeof(float));
+  // residual partials start as NaN: no root computed yet
+  const std::vector<float> nan_fill(h->resid_floats, std::numeric_limits<float>::quiet_NaN());
+  up(w.resid, nan_fill.data(), nan_fill.size() * sizeof(float));
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete h;
@@ -2753,6 +2803,7 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.decay = static_cast<float>(decay);
         a.ws = ws;
         a.scal = scal;
+        a.resid = reinterpret_cast<float*>(ws + h->off_resid);
         a.user = user;
         e = launch_gemm(a, r.count, r.tile, r.epi, rs);
       }
@@ -2762,6 +2813,25 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         h->pending.push_back({r.cat, static_cast<int>(ev)});
       }
     }
+  }
+  return OKLS_OK;
+}
+
+okls_status okls_ns_residuals(okls_handle* h, double* out, int64_t count, void* stream) {
+  if (h == nullptr || out == nullptr) return OKLS_ERR_INVALID_ARG;
+  if (h->cfg.mode != OKLS_MODE_OKLS && h->cfg.mode != OKLS_MODE_SHAMPOO) return OKLS_ERR_UNSUPPORTED;
+  if (count < 4 * static_cast<int64_t>(h->n_mats)) return OKLS_ERR_INVALID_ARG;
+  std::vector<float> part(h->resid_floats);
+  hipStream_t s = as_stream(stream);
+  if (!part.empty() && hipMemcpyAsync(part.data(), h->ws + h->off_resid, part.size() * sizeof(float),
+                                      hipMemcpyDeviceToHost, s) != hipSuccess)
+    return OKLS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return OKLS_ERR_HIP;
+  for (int64_t i = 0; i < 4 * static_cast<int64_t>(h->n_mats); ++i) out[i] = std::numeric_limits<double>::quiet_NaN();
+  for (const okls_handle::Resid& q : h->resid) {
+    double sum = 0.0;   // in the partials' order: a fixed order, so repeatable
+    for (int k = 0; k < q.count; ++k) sum += static_cast<double>(part[static_cast<size_t>(q.first) + k]);
+    out[(static_cast<int64_t>(q.mat) * 2 + q.side) * 2 + q.chain] = std::sqrt(sum);
   }
   return OKLS_OK;
 }

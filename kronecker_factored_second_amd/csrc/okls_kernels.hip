@@ -119,6 +119,7 @@ struct EpiCtx {
   int ld32, ld16, lo16, ld16T, lo16T, ldaux, aux_sym, aux_lo;
   bool aux_vec, out32_vec;  // fp32 aux rows / fp32 output rows are 16-byte aligned
   float c0, c1, c2, ka, kb, lr, decay;
+  float* resid;             // EPI_NS_T_RES: this wave's residual partial
 };
 
 // K advances in stages of 32 through a 4-deep LDS ring filled by
@@ -442,6 +443,34 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
   Stage<C>::flush(x, PART == 0 ? 0 : x.lo16, PART == 0 ? 0 : x.lo16T);
 }
 
+// The Newton-Schulz residual's partial: the sum of (Z Y - I)^2 over this
+// wave's entries of the logical region (v = Z Y is the accumulator times
+// alpha), reduced over the wave in a fixed butterfly order; lane 0 writes it.
+template <class C>
+__device__ __forceinline__ void resid_partial(const floatx16 (&acc)[C::GI][C::GJ], const EpiCtx& x) {
+  float rsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < C::GI; ++i) {
+    const int r = x.rbase + i * 32;
+#pragma unroll
+    for (int jg = 0; jg < 4 * C::GJ; ++jg) {
+      const int j = jg >> 2, g = jg & 3;
+      const int c0 = x.cbase + j * 32 + g * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = c0 + e;
+        if (r < x.M && c < x.N) {
+          const float q = acc[i][j][4 * g + e] * x.alpha - (r == c ? 1.0f : 0.0f);
+          rsum = fmaf(q, q, rsum);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) rsum += __shfl_xor(rsum, off, 64);
+  if ((threadIdx.x & 63) == 0) *x.resid = rsum;
+}
+
 template <class C, int EPI, bool WL>
 __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_nt_kernel(GemmArgs args) {
   constexpr int BT = C::BT, GI = C::GI, GJ = C::GJ, LPW = C::LPW, NW = C::NW;
@@ -649,11 +678,18 @@ __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_nt_kernel(G
   ctx.kb = args.kb;
   ctx.lr = args.lr;
   ctx.decay = args.decay;
+  ctx.resid = nullptr;
+  if constexpr (EPI == EPI_NS_T_RES)
+    ctx.resid = args.resid + P.resid + (static_cast<size_t>(ti) * (P.Np / BT) + tj) * NW + wave;
   if constexpr (EPI == EPI_STORE32 || EPI == EPI_UPDATE || EPI == EPI_SYRK || EPI == EPI_POLAR_UPDATE) {
     epilogue_f32<C, EPI>(acc, ctx);
   } else {
-    epilogue_pass<C, EPI, 0>(acc, ctx);
-    if constexpr (WL) epilogue_pass<C, EPI, 1>(acc, ctx);
+    // the residual variant of the T product has its own instantiation, so
+    // the other T launches keep their register allocation
+    constexpr int EPO = EPI == EPI_NS_T_RES ? EPI_NS_T : EPI;
+    if constexpr (EPI == EPI_NS_T_RES) resid_partial<C>(acc, ctx);
+    epilogue_pass<C, EPO, 0>(acc, ctx);
+    if constexpr (WL) epilogue_pass<C, EPO, 1>(acc, ctx);
   }
 }
 
@@ -1977,6 +2013,7 @@ hipError_t launch_gemm_cfg(const GemmArgs& a, int n_tiles, int epi, hipStream_t 
     case EPI_SYRK: OKLS_GEMM(EPI_SYRK, false); break;
     case EPI_UPDATE: OKLS_GEMM(EPI_UPDATE, false); break;
     case EPI_NS_T: if (wl) OKLS_GEMM(EPI_NS_T, true); else OKLS_GEMM(EPI_NS_T, false); break;
+    case EPI_NS_T_RES: if (wl) OKLS_GEMM(EPI_NS_T_RES, true); else OKLS_GEMM(EPI_NS_T_RES, false); break;
     case EPI_NS_Y1: if (wl) OKLS_GEMM(EPI_NS_Y1, true); else OKLS_GEMM(EPI_NS_Y1, false); break;
     case EPI_STORE16: if (wl) OKLS_GEMM(EPI_STORE16, true); else OKLS_GEMM(EPI_STORE16, false); break;
     case EPI_NS_FINAL: if (wl) OKLS_GEMM(EPI_NS_FINAL, true); else OKLS_GEMM(EPI_NS_FINAL, false); break;

@@ -57,7 +57,8 @@ enum Epi : int32_t {
   EPI_NS_FINAL = 5,  // out32 = v * scal[cslot] (fp32 root), out16 = v * scal[s_out]
   EPI_UPDATE = 6,    // W = decay*W - lr*c0*v
   EPI_POLAR = 7,     // X' = scal[cslot] * (ka*X + kb*v) -> out16 (+ out16T), X = fp16 aux
-  EPI_POLAR_UPDATE = 8   // W = decay*W - lr*c0*scal[cslot]*(ka*X + kb*v), X = fp16 aux
+  EPI_POLAR_UPDATE = 8,  // W = decay*W - lr*c0*scal[cslot]*(ka*X + kb*v), X = fp16 aux
+  EPI_NS_T_RES = 9   // EPI_NS_T, and the partials of ||v - I||_F^2 (one per wave and tile) into resid
 };
 
 struct GemmProb {
@@ -79,6 +80,8 @@ struct GemmProb {
   int32_t cslot;           // per-problem device scalar used by the epilogue
   float c0, c1, c2;        // per-problem constants
   int32_t Mp, Np;          // padded output dims
+  int32_t resid;           // EPI_NS_T: first float of this problem's residual partials
+                           // (one per wave and tile), or -1
 };
 
 struct GemmArgs {
@@ -92,6 +95,7 @@ struct GemmArgs {
   float lr, decay;         // update epilogue
   char* ws;
   float* scal;             // device scalar slots
+  float* resid;            // residual partials (problems with resid >= 0)
   UserPtrs user;
 };
 

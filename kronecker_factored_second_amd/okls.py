@@ -26,7 +26,7 @@ HYPER_DEFAULTS = {"okls": dict(lr=0.09434, beta1=0.9684, beta2=0.9482, eps=1e-9,
                   "soap": dict(lr=2.8e-3, beta1=0.95, beta2=0.95, eps=1e-8, weight_decay=0.1)}
 EXPORTED = ("okls_default_config", "okls_workspace_size", "okls_init", "okls_init_state", "okls_step",
             "okls_check_finite", "okls_ns_coefficients", "okls_profile_enable", "okls_profile_read",
-            "okls_destroy", "okls_status_string", "okls_plan_query", "okls_init_static")
+            "okls_destroy", "okls_status_string", "okls_plan_query", "okls_init_static", "okls_ns_residuals")
 STATIC_SCRATCH_BYTES = 128 << 20
 PROFILE_CATEGORIES = ("ns_gemm", "factor_gemm", "whiten_gemm", "stats", "cast", "eigensolver")
 
@@ -100,6 +100,8 @@ def load(path: str = LIB_PATH):
     lib.okls_step.restype = ctypes.c_int
     lib.okls_check_finite.argtypes = [vp, ctypes.POINTER(GroupTensors), vp]
     lib.okls_check_finite.restype = ctypes.c_int
+    lib.okls_ns_residuals.argtypes = [vp, ctypes.POINTER(ctypes.c_double), i64, vp]
+    lib.okls_ns_residuals.restype = ctypes.c_int
     lib.okls_ns_coefficients.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(ctypes.c_double), ctypes.c_int]
     lib.okls_ns_coefficients.restype = ctypes.c_int
@@ -263,6 +265,14 @@ def check_finite(h, tensors, stream) -> bool:
     return True
 
 
+def ns_residuals(h, n_mats: int, stream):
+    """||Z_{K-1} Y_{K-1} - I||_F per (matrix, side, chain): a list of
+    n_mats entries [[a0, a1], [b0, b1]] (NaN where not computed)."""
+    buf = (ctypes.c_double * (4 * n_mats))()
+    _check("okls_ns_residuals", load().okls_ns_residuals(h, buf, 4 * n_mats, ctypes.c_void_p(stream)))
+    return [[[buf[(i * 2 + s) * 2 + c] for c in range(2)] for s in range(2)] for i in range(n_mats)]
+
+
 def profile_enable(h, enable: bool):
     _check("okls_profile_enable", load().okls_profile_enable(h, 1 if enable else 0))
 
@@ -420,6 +430,17 @@ class OKLS:
     def check_finite(self) -> bool:
         # G is not read by the scan; W stands in for its pointer
         return check_finite(self.handle, self._tensors(grads=list(self.params)), self.stream)
+
+    def ns_residuals(self):
+        """The Newton-Schulz residual of each root of the last step that
+        recomputed them, per parameter: a list over the parameters of lists
+        over the batch of [[a chain 0, a chain 1], [b chain 0, b chain 1]]."""
+        flat = ns_residuals(self.handle, sum(g[0] for g in self.groups), self.stream)
+        out, k = [], 0
+        for (b, _, _, _) in self.groups:
+            out.append(flat[k:k + b])
+            k += b
+        return out
 
     def state_dict(self):
         return {"t": self.t, "lr": self.lr, "lr_peak": self.cfg.lr_peak,

@@ -41,6 +41,9 @@ Parity status of each function (what pins it in the CPU test-suite):
   ns_spectral / closed form .... matrix iterations (damped, p = 2 and 4) on random SPD
                                  factors; output within the coefficient bound of
                                  (lambda + delta c)^{-1/2} on the design interval
+  ns_residual .................. hand-computed classical values on a scalar matrix
+                                 (K = 1 and 2); equals the per-eigenvalue recurrence
+                                 (eigh) on random SPD factors
   ns_inv_sqrt / ns_inv_quarter . diagonal S reduces to scalar recurrences,
                                  eigen closed form, worked example through NS,
                                  damped isotropic closed form, damped root within
@@ -299,6 +302,39 @@ def ns_inv_sqrt(S: np.ndarray, coeffs, nu: float = 0.0):
         T = a * eye + b * (Z @ Y)
         Y, Z = Y @ T, T @ Z
     return Z / math.sqrt(c), Y * math.sqrt(c)
+
+
+def ns_residual(S: np.ndarray, coeffs, nu: float = 0.0) -> float:
+    """Convergence diagnostic of the iteration above: ||Z_{K-1} Y_{K-1} - I||_F,
+    the product the last step's T_{K-1} = a I + b Z_{K-1} Y_{K-1} is formed
+    from (K = len(coeffs); for K = 1 that is Z_0 Y_0 = Y_0).  Z_k Y_k -> I as
+    the iteration converges."""
+    d = S.shape[0]
+    eye = np.eye(d)
+    delta = nu / math.sqrt(d)
+    c = float(np.linalg.norm(S)) * (1.0 + delta)
+    Y = (S + (delta * c / (1.0 + delta)) * eye) / c
+    Z = eye.copy()
+    ZY = Z @ Y
+    for a, b in coeffs:
+        ZY = Z @ Y
+        T = a * eye + b * ZY
+        Y, Z = Y @ T, T @ Z
+    return float(np.linalg.norm(ZY - eye))
+
+
+def ns_residual_spectral(lam: np.ndarray, coeffs, nu: float = 0.0) -> float:
+    """ns_residual through the eigenvalues (the per-direction recurrence of
+    ns_spectral): in each eigen-direction Z_k Y_k = sigma_k^2, so the residual
+    is (sum over directions of (sigma_{K-1}^2 - 1)^2)^1/2."""
+    lam = np.asarray(lam, dtype=np.float64)
+    d = lam.size
+    delta = nu / math.sqrt(d)
+    c = float(np.linalg.norm(lam))
+    s = np.sqrt((lam + delta * c) / (c * (1.0 + delta)))
+    for a, b in coeffs[:-1]:
+        s = s * (a + b * s * s)
+    return float(np.sqrt(np.sum((s * s - 1.0) ** 2)))
 
 
 def ns_inv_quarter(S: np.ndarray, coeffs, nu: float = 0.0):

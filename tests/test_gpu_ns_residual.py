@@ -1,0 +1,118 @@
+"""GPU check of the Newton-Schulz convergence diagnostic: the residual
+||Z_{K-1} Y_{K-1} - I||_F that the last T product of each root's coupled
+iteration leaves ("Online KL Shampoo" README, "How it works": the roots come
+from the coupled iteration), read back through okls_ns_residuals, against
+the oracle's fp64 run of the same damped iteration on the same factor
+(teacher forced: the oracle's factor is the update of the GPU's state before
+the step).
+
+The GPU's iterates are the rounded (fp16, or split hi + lo) copies the
+products read, so its residual carries their rounding on top of the exact
+iteration's.  For a factor within the condition-number gate of the root
+comparisons (the directions the iteration resolves in that arithmetic),
+|r_gpu - r_oracle| stays within a rounding floor that grows like sqrt(d)
+times the rounding unit of the iterates (fp16 2^-11; split ~2^-21), times a
+margin for the nine steps' accumulation.  Beyond the gate (the
+rank-deficient first steps) each unresolved direction leaves |sigma^2 - 1|
+of order 1, which rounding moves: there the value is only bounded.  Values
+are NaN before the first root and unchanged on a step that keeps the roots.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from kronecker_factored_second_amd import workloads as WL
+from oracle import okls_oracle as O
+
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+UNIT = {"fp16": 2.0 ** -11, "fp32": 2.0 ** -21}
+MARGIN = 8.0
+
+
+def _floor(precision, d):
+    return MARGIN * UNIT[precision] * math.sqrt(d)
+
+
+def _run(name, groups, grad_fn, steps, precision, mode="okls", **cfg):
+    torch = pytest.importorskip("torch")
+    opt, params = H.make(groups, precision=precision, mode=mode, **cfg)
+    hp = H.hyper_of(opt)
+    coeffs = hp.coeffs()
+    rep = H.Report(name)
+    r0 = opt.ns_residuals()
+    assert all(math.isnan(x) for g in r0 for mat in g for side in mat for x in side), "residual before any root"
+    worst = 0.0
+    prev = None
+    for t in range(1, steps + 1):
+        host = {gi: [grad_fn(gi, i, t) for i in range(b)] for gi, (m, n, b) in enumerate(groups)}
+        before = {(gi, i): H.snapshot(opt, gi, i) for gi, (m, n, b) in enumerate(groups) for i in range(b)}
+        opt.step(grads=[H.to_device_grad(np.stack(host[gi]), "f32") for gi in range(len(groups))])
+        torch.cuda.synchronize()
+        res = opt.ns_residuals()
+        if not hp.refresh(t):
+            flat = lambda r: np.array([x for g in r for mat in g for side in mat for x in side])
+            assert np.array_equal(flat(res), flat(prev), equal_nan=True), \
+                f"t={t}: the residuals changed on a step that keeps the roots"
+            continue
+        for gi, (m, n, b) in enumerate(groups):
+            for i in range(b):
+                ref = O.step(before[(gi, i)], host[gi][i], hp, t, mode, root="ns")
+                for side, S, d in ((0, ref.state.Sa, m), (1, ref.state.Sb, n)):
+                    want = [O.ns_residual(S, coeffs, hp.ns_damping)]
+                    if mode == "shampoo":   # the second chain roots sym(S^-1/2)
+                        P1, _ = O.ns_inv_sqrt(S, coeffs, hp.ns_damping)
+                        want.append(O.ns_residual(0.5 * (P1 + P1.T), coeffs, hp.ns_damping))
+                    got = res[gi][i][side]
+                    lam = np.linalg.eigvalsh(0.5 * (S + S.T))
+                    kappa = float(lam[-1] / lam[0]) if lam[0] > 0 else float("inf")
+                    gated = kappa <= H.kappa_gate(precision, d)
+                    for c, w in enumerate(want):
+                        err = abs(got[c] - w)
+                        rep.add(t=t, g=gi, i=i, side=side, chain=c, d=d, kappa=kappa, gpu=got[c], oracle=w, err=err,
+                                floor=_floor(precision, d))
+                        assert math.isfinite(got[c]), (t, gi, i, side, c)
+                        if not gated:
+                            # directions the iteration does not resolve in this arithmetic
+                            # (rank-deficient early factors) leave |sigma^2 - 1| up to about
+                            # 1 each, and rounding decides how close: only bounded
+                            assert got[c] <= 2.0 * math.sqrt(d), (t, gi, i, side, c, got[c])
+                            continue
+                        assert err <= _floor(precision, d), \
+                            f"t={t} group {gi} matrix {i} side {side} chain {c}: residual {got[c]:.3e} vs {w:.3e}"
+                        worst = max(worst, err / _floor(precision, d))
+                    if mode != "shampoo":
+                        assert math.isnan(got[1])
+        prev = res
+    print(f"[{name}] worst error / floor {worst:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("precision", ["fp16", "fp32"])
+def test_residual_c1(precision):
+    """The 128 x 256 matrix with N(0,1) gradients (seed 0), 20 steps: the
+    residual of both sides' roots at every step."""
+    w = WL.workload("c1")
+    WL.reset_caches()
+    _run(f"resid-c1-{precision}", [(128, 256, 1)], lambda g, i, t: WL.gradient(w, 0, 0, t), 20, precision)
+
+
+@pytest.mark.parametrize("precision", ["fp16", "fp32"])
+def test_residual_ragged_shampoo_and_kept_roots(precision):
+    """Ragged sides in two groups, the Shampoo mode's two chains, and roots
+    refreshed every other step (the kept steps leave the residuals as they
+    were)."""
+    rng = np.random.default_rng(7)
+    cache = {}
+
+    def grad(gi, i, t):
+        key = (gi, i, t)
+        if key not in cache:
+            m, n = [(200, 72), (33, 130)][gi]
+            cache[key] = rng.standard_normal((m, n))
+        return cache[key]
+
+    _run(f"resid-ragged-{precision}", [(200, 72, 2), (33, 130, 1)], grad, 4, precision, mode="shampoo",
+         root_period=2)

@@ -692,3 +692,31 @@ def test_classical_coefficients_converge_to_the_exact_root():
     np.testing.assert_allclose(O.ns_eigen_closed_form(S, coeffs, 2, 0.0), P, rtol=1e-10, atol=1e-12)
     hp = O.Hyper(ns_classical=True, ns_steps=7)
     assert hp.coeffs() == [(1.5, -0.5)] * 7
+
+
+def test_ns_residual_hand_computed():
+    """Classical Newton-Schulz (a, b) = (3/2, -1/2) on S = 3 I of side 4:
+    c = ||S||_F = 6, Y_0 = I / 2, so Z_0 Y_0 = I / 2 and the residual with
+    K = 1 is ||-I / 2||_F = 1.  One step gives sigma^2 = (1/2)(3/2 - 1/4)^2 =
+    25 / 32, so with K = 2 the residual (of Z_1 Y_1) is 2 (1 - 25/32) = 7/16."""
+    S = 3.0 * np.eye(4)
+    assert O.ns_residual(S, [(1.5, -0.5)]) == pytest.approx(1.0, abs=1e-15)
+    assert O.ns_residual(S, [(1.5, -0.5)] * 2) == pytest.approx(7.0 / 16.0, abs=1e-15)
+
+
+@pytest.mark.parametrize("nu", [0.0, 5e-3])
+def test_ns_residual_matches_the_eigenvalue_recurrence(nu):
+    """The matrix iteration's ||Z_{K-1} Y_{K-1} - I||_F equals the residual of
+    the scalar recurrence over S's eigenvalues (LAPACK eigh), and falls as
+    classical steps are added on a well-conditioned factor (there 1 - sigma^2
+    shrinks at every step in every direction)."""
+    rng = np.random.default_rng(41)
+    coeffs, _ = O.ns_coefficients(1e-3, 10)
+    for d, kappa in ((30, 1e2), (64, 1e4)):
+        S = _spd(rng, d, kappa) * 0.7
+        r = O.ns_residual(S, coeffs, nu)
+        lam = np.linalg.eigvalsh(S)
+        assert r == pytest.approx(O.ns_residual_spectral(lam, coeffs, nu), rel=1e-9, abs=1e-12)
+    S = _spd(rng, 40, 10.0)
+    seq = [O.ns_residual(S, [(1.5, -0.5)] * k, nu) for k in range(1, 11)]
+    assert all(b < a for a, b in zip(seq, seq[1:])) and seq[-1] < 1e-12
