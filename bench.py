@@ -30,7 +30,6 @@ sys.path.insert(0, ROOT)
 METRIC = "preconditioned matrices/sec + step latency (ms); % fp16 MFMA peak on NS chain"
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0
-PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector (the Nystrom mode's SIMT products)
 
 
 # the GEMM's traffic depends on its kernel and on the planner's launch shapes
@@ -53,7 +52,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps before the timed ones (default 5; soap mode: --precond-freq, so that the "
+                        "first eigenbasis refresh, a cold start from the identity, is not timed)")
     p.add_argument("--workload", default="c3")
     p.add_argument("--precision", default="fp16", choices=["fp16", "fp32"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,8 +71,9 @@ def parse():
     p.add_argument("--nys-passes", type=int, default=1, help="nystrom mode: subspace-iteration passes")
     p.add_argument("--precond-freq", type=int, default=10,
                    help="soap mode: refresh the eigenbases after every this many steps (the Clean paper's Table 6: 10)")
-    p.add_argument("--root-period", type=int, default=1,
-                   help="recompute the roots every this many steps (1: every step)")
+    p.add_argument("--root-period", type=int, default=None,
+                   help="recompute the roots every this many steps (default 1: every step); nystrom mode: "
+                        "refresh the low-rank factors every this many steps (default 10, the Clean paper's T)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 10 times (HBM counter calibration)")
     p.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV_DIR", "WRITE_CSV_DIR", "COMMANDS"),
@@ -398,6 +400,10 @@ def main():
 
     w = WL.workload(args.workload)
     mode = args.mode or w.mode
+    if args.root_period is None:
+        args.root_period = 10 if mode == "nystrom" else 1
+    if args.warmup is None:
+        args.warmup = args.precond_freq if mode == "soap" else 5
     dev = torch.device("cuda:0")
     bf16 = w.grad_dtype == "bf16"
     big = w.n_params > 1e9
@@ -491,9 +497,25 @@ def main():
     g_n = sum(prof[k]["launches"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     g_b = sum(prof[k]["bytes"] for k in ("ns_gemm", "factor_gemm", "whiten_gemm"))
     achieved = g_fl / (g_busy * 1e-3) / 1e12 if g_busy > 0 else 0.0
-    per_launch = g_fl / (g_ms * 1e-3) / 1e12
+    per_launch = g_fl / (g_ms * 1e-3) / 1e12 if g_ms > 0 else 0.0
     ns = prof["ns_gemm"]
-    ns_tflops = ns["flops"] / (ns["busy_ms"] * 1e-3) / 1e12
+    ns_tflops = ns["flops"] / (ns["busy_ms"] * 1e-3) / 1e12 if ns["busy_ms"] > 0 else 0.0
+    nys_roofline = None
+    if mode == "nystrom":
+        # every step's preconditioning (thin_kernel launches and the weight
+        # update's gemm32_kernel) streams the m x n data three times: bound by HBM
+        wb = prof["whiten_gemm"]
+        ach = wb["bytes"] / (wb["busy_ms"] * 1e-3) / 1e9 if wb["busy_ms"] > 0 else 0.0
+        nys_roofline = {"kernel": "thin_kernel + gemm32_kernel (per-step preconditioning)", "bound": "hbm",
+                        "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                        "traffic": None,
+                        "method": "algorithmic bytes of the per-step preconditioning launches (the momentum read and "
+                                  "written once, N read twice more, W read and written) over their busy time from HIP "
+                                  "events on the launch stream, in a second pass of the same steps",
+                        "avg_launch_us": wb["ms"] * 1e3 / max(wb["launches"], 1),
+                        "launches_per_step": wb["launches"] / max(prof["steps"], 1),
+                        "algorithmic_bytes_per_step": wb["bytes"] / max(prof["steps"], 1),
+                        "algorithmic_flops_per_step": wb["flops"] / max(prof["steps"], 1)}
     line = {
         "metric": METRIC,
         "value": w.n_matrices / (ms_step * 1e-3),
@@ -524,10 +546,10 @@ def main():
         "ms_per_step_with_launch_events": ms_step_profiled,
         "ns_chain": {"tflops": ns_tflops, "frac_fp16_peak": ns_tflops / PEAK_FP16_TFLOPS,
                      "ms_per_step": ns["busy_ms"] / max(prof["steps"], 1), "launches_per_step": ns["launches"] / max(prof["steps"], 1)},
-        "roofline": {"kernel": "gemm32_kernel" if mode == "nystrom" else "gemm_nt_kernel",
-                     "bound": "alu" if mode == "nystrom" else "mfma", "achieved": achieved,
-                     "peak": PEAK_FP32_TFLOPS if mode == "nystrom" else PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / (PEAK_FP32_TFLOPS if mode == "nystrom" else PEAK_FP16_TFLOPS),
+        "roofline": nys_roofline if mode == "nystrom" else {"kernel": "gemm_nt_kernel",
+                     "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP16_TFLOPS,
                      "traffic": measured_traffic(args.workload) if (args.precision == "fp16" and mode == w.mode and
                                                                     args.root_period == 1 and mode != "nystrom") else None,
                      "method": "algorithmic FLOPs of every gemm_nt_kernel launch over the union of their intervals, "
@@ -543,10 +565,22 @@ def main():
                                "frac": prof[cat]["bytes"] / (prof[cat]["busy_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                "bytes_per_step": prof[cat]["bytes"] / max(prof["steps"], 1),
                                "launches_per_step": prof[cat]["launches"] / max(prof["steps"], 1)}
-                        for kern, cat in (("stats_kernel", "stats"), ("cast_kernel", "cast")) if prof[cat]["ms"] > 0},
+                        for kern, cat in (("stats_kernel", "stats"), ("cast_kernel", "cast")) if prof[cat]["busy_ms"] > 0},
         "state_finite": finite,
         "host_wall_s": wall,
     }
+    if mode in ("okls", "shampoo") and prof["stats"]["busy_ms"] + prof["cast"]["busy_ms"] > 0:
+        # the statistics and cast launches against the method's own bytes, not
+        # the staging copies the GEMMs read: the momentum reads G and M and
+        # writes M and the fp16 N (bytes_G + 10 per element), and the root's
+        # start reads each factor and writes its fp16 Y_0 (6 per entry)
+        gb = 2 if bf16 else 4
+        mb = sum(b * (m * n * (gb + 10) + 6 * (m * m + n * n)) for m, n, b in w.groups)
+        sc_ms = (prof["stats"]["busy_ms"] + prof["cast"]["busy_ms"]) / max(prof["steps"], 1)
+        line["hbm_kernels_method_bytes"] = {"kernels": "stats_kernel + cast_kernel", "bytes_per_step": mb,
+                                            "ms_per_step": sc_ms, "achieved": mb / (sc_ms * 1e-3) / 1e9,
+                                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                            "frac": mb / (sc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if mode in ("okls", "shampoo"):
         # convergence of the roots: ||Z_{K-1} Y_{K-1} - I||_F of every chain of the last step
         r = np.array([x for g in opt.ns_residuals() for mat in g for side in mat for x in side], dtype=np.float64)

@@ -185,7 +185,9 @@ typedef struct {
                                   stops once converged: measured cold starts from the identity
                                   need 12 sweeps at d = 1024 and 13 at d = 2816) */
     float jacobi_tol;          /* a refresh stops once ||off(Q^T S Q)||_F <= tol ||diag||_F
-                                  (default 2e-6) */
+                                  (default 2e-6), tol raised per factor of side d to
+                                  2^-23 sqrt(d), where the fp32 basis' own rounding sets
+                                  its accuracy */
     /* OKLS_MODE_NYSTROM only: */
     int32_t nys_rank;          /* r >= 1: eigenpairs kept per factor (default 32) */
     int32_t nys_oversample;    /* p >= 0: extra sketch columns, r + p <= 128 (default 8) */

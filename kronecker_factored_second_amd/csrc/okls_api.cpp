@@ -130,8 +130,10 @@ struct MatBufs {
   // SOAP: M' fp16, (G Q_b)^T and (M Q_b)^T fp16, G' and M' fp32, N' fp16, (N' Q_b^T)^T fp16
   size_t M16 = 0, XGT16 = 0, XMT16 = 0, Gr32 = 0, Mr32 = 0, NP16 = 0, ZT16 = 0;
   int s_m = 0, s_gx = 0, s_mx = 0;
-  // Nystrom: N (fp32, overwritten by the preconditioned U), N U_b, U_a^T N', U_a E_a, U_b E_b
-  size_t N32 = 0, X32 = 0, Z32 = 0, UtA = 0, UtB = 0;
+  // Nystrom: the momentum N (fp32); XU = [X | U_a E_a] (m x (r_b + r_a)) with X = N U_b;
+  // ZB = [(U_b E_b)^T ; Z] ((r_b + r_a) x n) with Z = U_a^T N + (U_a^T X) (U_b E_b)^T;
+  // Ct = (U_a^T X)^T (r_b x r_a)
+  size_t N32 = 0, XU = 0, ZB = 0, Ct = 0;
   struct NysSide {
     int d = 0, k = 0, r = 0;           // side, sketch columns, kept eigenpairs
     size_t Om = 0, Yb = 0, Fb = 0, T1 = 0, T2 = 0, gram = 0, cm = 0, zp = 0, kout = 0, scratch = 0;
@@ -140,7 +142,7 @@ struct MatBufs {
 };
 
 enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4, L_SYM = 5, L_ADAM = 6, L_JAC = 7,
-                  L_G32 = 8, L_NORTH = 9, L_NSMALL = 10, L_NELEM = 11 };
+                  L_G32 = 8, L_NORTH = 9, L_NSMALL = 10, L_NELEM = 11, L_THIN = 12 };
 
 struct LaunchRec {
   int type = L_STAT;
@@ -156,6 +158,7 @@ struct LaunchRec {
   int stream = 0;               // 0: the caller's stream; 1: the library's side stream (between a fork and a join)
   int jac_kind = 0, round = 0;  // L_JAC: JacKind and tournament round
   size_t jac_part = 0, jac_flag = 0;   // L_JAC: workspace offsets of the chunk's partials and flags
+  int thin_ta = 0, thin_mom = 0;       // L_THIN: the launch's operand form
 };
 
 enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4, CAT_EIG = 5 };
@@ -192,7 +195,7 @@ struct okls_handle {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_sym = 0, off_scal = 0, off_part = 0, off_flag = 0;
-  size_t off_adam = 0, off_jac = 0, off_g32 = 0, off_north = 0, off_nsmall = 0, off_nelem = 0;
+  size_t off_adam = 0, off_jac = 0, off_g32 = 0, off_north = 0, off_nsmall = 0, off_nelem = 0, off_thin = 0;
   size_t off_resid = 0, resid_floats = 0;   // Newton-Schulz residual partials
   struct Resid { int mat, side, chain, first, count; };
   std::vector<Resid> resid;
@@ -329,6 +332,7 @@ struct Planner {
   std::vector<NysOrthJob> north_jobs;
   std::vector<NysSmallJob> nsmall_jobs;
   std::vector<NysElemJob> nelem_jobs;
+  std::vector<ThinJob> thin_jobs;
   float s_np = 1.0f;          // SOAP: static scale of the Adam direction's fp16 operand
   std::vector<std::vector<LaunchRec>> chunks;        // steps that recompute the roots
   std::vector<std::vector<LaunchRec>> chunks_stale;  // steps that keep them (root_period > 1)
@@ -395,10 +399,9 @@ struct Planner {
         const size_t mn = static_cast<size_t>(g.m) * g.n * 4;
         mb.N32 = take(mn);
         const int ra = nys_r(g.m), rb = nys_r(g.n);
-        mb.X32 = take(static_cast<size_t>(g.m) * rb * 4);
-        mb.Z32 = take(static_cast<size_t>(ra) * g.n * 4);
-        mb.UtA = take(static_cast<size_t>(g.m) * ra * 4);
-        mb.UtB = take(static_cast<size_t>(g.n) * rb * 4);
+        mb.XU = take(static_cast<size_t>(g.m) * (rb + ra) * 4);
+        mb.ZB = take(static_cast<size_t>(rb + ra) * g.n * 4);
+        mb.Ct = take(static_cast<size_t>(rb) * ra * 4);
         for (int sd = 0; sd < 2; ++sd) {
           MatBufs::NysSide& S = mb.ns[sd];
           S.d = sd == 0 ? g.m : g.n;
@@ -1284,6 +1287,12 @@ struct Planner {
       j.btiles = j.npairs * (j.npairs + 1) / 2; j.vrows = (F.d + kJp - 1) / kJp;
       j.jbuf = static_cast<int64_t>(F.jbuf); j.part = part; j.flag = static_cast<int32_t>(f);
       j.solve_begin = solve_blk; j.apply_begin = apply_blk;
+      // the rotations and the basis are fp32: the basis' own residual stops
+      // near u sqrt(d) (measured at d = 2816: 8e-6 of ||L|| from the eighth
+      // sweep of a cold start on), so the stop is the larger of jacobi_tol
+      // and 2^-23 sqrt(d) (6.3e-6 at d = 2816); sweeps below it only shrink
+      // B's off-diagonal, not the basis' error
+      j.tol = std::max(cfg.jacobi_tol, static_cast<float>(std::ldexp(std::sqrt(static_cast<double>(F.d)), -23)));
       solve_blk += j.npairs;
       apply_blk += j.btiles + j.vrows * j.npairs;
       part += j.btiles;
@@ -1362,6 +1371,7 @@ struct Planner {
     p.A = A; p.B = B; p.C = C; p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ta = ta; p.tb = tb;
     p.M = M; p.N = N; p.K = K; p.alpha = alpha; p.beta = beta; p.alpha_slot = -1; p.rowscale = no_ref();
     p.a_fmt = p.b_fmt = GF_F32;
+    p.wupd = 0; p.aux = no_ref(); p.c0 = 0.0f;
     return p;
   }
   void add_g32(std::vector<LaunchRec>& L, const std::vector<Gemm32Prob>& ps, int cat) {
@@ -1377,11 +1387,61 @@ struct Planner {
       p.blk_begin = blk;
       blk += tm * tn;
       step_flops[cat] += 2.0 * p.M * p.N * p.K;
+      // operands once; C written (and read when beta != 0); the weight
+      // update reads W and the added matrix and writes W
       step_bytes[cat] += 4.0 * (static_cast<double>(p.M) * p.K + static_cast<double>(p.K) * p.N +
-                                (p.beta != 0.0f ? 2.0 : 1.0) * p.M * p.N);
+                                (p.wupd ? 3.0 : p.beta != 0.0f ? 2.0 : 1.0) * p.M * p.N);
       g32_jobs.push_back(p);
     }
     r.count = static_cast<int>(ps.size());
+    r.nblocks = blk;
+    L.push_back(r);
+  }
+  // C = alpha op(A) B + beta C with op(A) Mo x K (ta: A stored K x Mo), B K x R, C Mo x R (ot: R x Mo)
+  ThinJob thin(Ref A, int lda, int ta, Ref B, int ldb, Ref C, int ldc, int ot, int Mo, int K, int R, float alpha,
+               float beta) {
+    ThinJob j{};
+    j.A = A; j.B = B; j.C = C; j.M = j.Nout = no_ref();
+    j.lda = lda; j.ldb = ldb; j.ldc = ldc; j.ldn = 0; j.ta = ta; j.ot = ot; j.a_fmt = GF_F32; j.mom = 0;
+    j.Mo = Mo; j.K = K; j.R = R; j.alpha = alpha; j.beta = beta; j.alpha_slot = -1; j.rowscale = no_ref();
+    return j;
+  }
+  // a thin product written in the gemm32 form (op(B) = B, N <= kThinMaxR)
+  ThinJob thin_of(const Gemm32Prob& p) {
+    ThinJob j = thin(p.A, p.lda, p.ta, p.B, p.ldb, p.C, p.ldc, 0, p.M, p.K, p.N, p.alpha, p.beta);
+    j.a_fmt = p.a_fmt; j.alpha_slot = p.alpha_slot; j.rowscale = p.rowscale;
+    return j;
+  }
+  // products of both operand forms: one launch per form
+  void add_thin_any(std::vector<LaunchRec>& L, const std::vector<Gemm32Prob>& ps, int cat) {
+    std::vector<ThinJob> by_ta[2];
+    for (const Gemm32Prob& p : ps) by_ta[p.ta ? 1 : 0].push_back(thin_of(p));
+    add_thin(L, by_ta[0], cat);
+    add_thin(L, by_ta[1], cat);
+  }
+  // one launch per (ta, mom) kind
+  void add_thin(std::vector<LaunchRec>& L, const std::vector<ThinJob>& js, int cat) {
+    if (js.empty()) return;
+    LaunchRec r;
+    r.type = L_THIN;
+    r.cat = cat;
+    r.first = static_cast<int>(thin_jobs.size());
+    r.thin_ta = js.front().ta;
+    r.thin_mom = js.front().mom;
+    int blk = 0;
+    for (ThinJob j : js) {
+      j.blk_begin = blk;
+      blk += (j.Mo + kThinTile - 1) / kThinTile;
+      step_flops[cat] += 2.0 * j.Mo * static_cast<double>(j.K) * j.R;
+      // op(A) once (gradient bytes as stored), B once, C once (twice when read)
+      const double ae = j.a_fmt == GF_F32 ? 4.0 : 2.0;
+      double b = ae * j.Mo * static_cast<double>(j.K) + 4.0 * j.K * static_cast<double>(j.R) +
+                 4.0 * (j.beta != 0.0f ? 2.0 : 1.0) * j.Mo * static_cast<double>(j.R);
+      if (j.mom) b += 12.0 * j.Mo * static_cast<double>(j.K);   // M read and written, N written
+      step_bytes[cat] += b;
+      thin_jobs.push_back(j);
+    }
+    r.count = static_cast<int>(js.size());
     r.nblocks = blk;
     L.push_back(r);
   }
@@ -1409,8 +1469,7 @@ struct Planner {
       j.blocks = static_cast<int>(std::max<size_t>(1, std::min<size_t>((total + 255) / 256, 4096)));
       j.blk_begin = blk;
       blk += j.blocks;
-      const double per = j.kind == NE_MOMENTUM ? 16.0 : j.kind == NE_UPDATE ? 12.0 : 8.0;
-      step_bytes[CAT_CAST] += per * total;
+      step_bytes[CAT_CAST] += 8.0 * total;   // one fp32 read and one write per element
       nelem_jobs.push_back(j);
     }
     r.count = static_cast<int>(js.size());
@@ -1490,9 +1549,9 @@ struct Planner {
             p3.push_back(g32(uref(mb, sd), S.r, 0, ws_ref(S.T1), S.k, 0, ws_ref(S.Yb), S.k, S.d, S.k, S.r, 1.0f, 1.0f));
             if (pass < cfg.nys_passes) po.push_back(NysOrthJob{ws_ref(S.Yb), pref(mb, sd), S.d, S.k, S.k, S.k, 0});
           }
-        add_g32(L, p1, CAT_NS);
-        add_g32(L, p2, CAT_NS);
-        add_g32(L, p3, CAT_NS);
+        add_thin_any(L, p1, CAT_NS);
+        add_thin_any(L, p2, CAT_NS);
+        add_thin_any(L, p3, CAT_NS);
         if (pass < cfg.nys_passes) {
           add_north(L, po);
           // the orthonormalised Y is the next Omega
@@ -1538,59 +1597,68 @@ struct Planner {
           pt.push_back(g32(ws_ref(S.Fb), S.k, 1, uref(mb, sd), S.r, 0, ws_ref(S.zp), S.r, S.k, S.r, S.d, 1.0f, 0.0f));
           pu.push_back(g32(ws_ref(S.Fb), S.k, 0, ws_ref(S.kout), S.r, 0, uref(mb, sd), S.r, S.d, S.r, S.k, 1.0f, 0.0f));
         }
-      add_g32(L, pg, CAT_NS);
+      add_thin_any(L, pg, CAT_NS);
       small(1);
-      add_g32(L, pf1, CAT_NS);
-      add_g32(L, pf2, CAT_NS);
-      add_g32(L, pt, CAT_NS);
+      add_thin_any(L, pf1, CAT_NS);
+      add_thin_any(L, pf2, CAT_NS);
+      add_thin_any(L, pt, CAT_NS);
       small(2);
-      add_g32(L, pu, CAT_NS);
+      add_thin_any(L, pu, CAT_NS);
       // the buffer roles are back where the layout put them for the next plan
       if (cfg.nys_passes & 1)
         for (MatBufs& mb : mats)
           for (MatBufs::NysSide& S : mb.ns) std::swap(S.Om, S.Yb);
     }
-    // every step: N, then U = P_a^-1/2 N P_b^-1/2 through thin products
-    // (P^-1/2 = I + U diag(e) U^T, e_j = sqrt((lambda_r + eps) / (lambda_j + eps)) - 1):
-    //   X = N U_b, N' = N + X (U_b E_b)^T, Z = U_a^T N', U = N' + (U_a E_a) Z
+    // every step: the preconditioned U = P_a^-1/2 N P_b^-1/2 with
+    // P^-1/2 = I + U diag(e) U^T, e_j = sqrt((lambda_r + eps) / (lambda_j + eps)) - 1,
+    // expanded so that the m x n data is read three times:
+    //   X = N U_b (N computed from G and M on the fly, M and N written),
+    //   Z = U_a^T N + (U_a^T X) (U_b E_b)^T,
+    //   U = N + X (U_b E_b)^T + (U_a E_a) Z  (= P_a^-1/2 N' with N' = N + X (U_b E_b)^T),
+    // the last product in the weight update's epilogue.
     {
       std::vector<NysElemJob> e1;
       for (const MatBufs& mb : mats) {
-        NysElemJob j = nelem(NE_MOMENTUM);
-        j.dst = ws_ref(mb.N32); j.src = user_ref(REF_M, mb.group, moff(mb)); j.src2 = user_ref(REF_G, mb.group, goff(mb));
-        j.rows = mb.m; j.cols = mb.n; j.ld_dst = j.ld_src = j.ld_src2 = mb.n; j.g_fmt = gfmt(mb);
-        e1.push_back(j);
-        for (int sd = 0; sd < 2; ++sd) {
-          const MatBufs::NysSide& S = mb.ns[sd];
-          NysElemJob sc = nelem(NE_SCALE);
-          sc.dst = ws_ref(sd == 0 ? mb.UtA : mb.UtB); sc.src = uref(mb, sd); sc.lam = lref(mb, sd);
-          sc.rows = S.d; sc.cols = S.r; sc.ld_dst = sc.ld_src = S.r;
-          e1.push_back(sc);
-        }
+        const int ra = mb.ns[0].r, rb = mb.ns[1].r;
+        NysElemJob sa = nelem(NE_SCALE);      // U_a E_a into XU's last r_a columns
+        sa.dst = ws_ref(mb.XU + static_cast<size_t>(rb) * 4); sa.src = uref(mb, 0); sa.lam = lref(mb, 0);
+        sa.rows = mb.m; sa.cols = ra; sa.ld_dst = rb + ra; sa.ld_src = ra;
+        e1.push_back(sa);
+        NysElemJob sb = nelem(NE_SCALE);      // (U_b E_b)^T into ZB's first r_b rows
+        sb.dst = ws_ref(mb.ZB); sb.src = uref(mb, 1); sb.lam = lref(mb, 1);
+        sb.rows = mb.n; sb.cols = rb; sb.ld_dst = mb.n; sb.ld_src = rb; sb.trans = 1;
+        e1.push_back(sb);
       }
       add_nelem(L, e1);
     }
-    std::vector<Gemm32Prob> q1, q2, q3, q4;
+    std::vector<ThinJob> t1, t2, t3, t4;
+    std::vector<Gemm32Prob> fin;
     for (const MatBufs& mb : mats) {
-      const MatBufs::NysSide& A = mb.ns[0];
-      const MatBufs::NysSide& B = mb.ns[1];
-      q1.push_back(g32(ws_ref(mb.N32), mb.n, 0, uref(mb, 1), B.r, 0, ws_ref(mb.X32), B.r, mb.m, B.r, mb.n, 1.0f, 0.0f));
-      q2.push_back(g32(ws_ref(mb.X32), B.r, 0, ws_ref(mb.UtB), B.r, 1, ws_ref(mb.N32), mb.n, mb.m, mb.n, B.r, 1.0f, 1.0f));
-      q3.push_back(g32(uref(mb, 0), A.r, 1, ws_ref(mb.N32), mb.n, 0, ws_ref(mb.Z32), mb.n, A.r, mb.n, mb.m, 1.0f, 0.0f));
-      q4.push_back(g32(ws_ref(mb.UtA), A.r, 0, ws_ref(mb.Z32), mb.n, 0, ws_ref(mb.N32), mb.n, mb.m, mb.n, A.r, 1.0f, 1.0f));
+      const int ra = mb.ns[0].r, rb = mb.ns[1].r, ld = rb + ra;
+      // X = N U_b with N = momentum(G, M)
+      ThinJob x = thin(user_ref(REF_G, mb.group, goff(mb)), mb.n, 0, uref(mb, 1), rb, ws_ref(mb.XU), ld, 0,
+                       mb.m, mb.n, rb, 1.0f, 0.0f);
+      x.a_fmt = gfmt(mb); x.mom = 1; x.M = user_ref(REF_M, mb.group, moff(mb)); x.Nout = ws_ref(mb.N32); x.ldn = mb.n;
+      t1.push_back(x);
+      // Z = U_a^T N (written as r_a x n below ZB's first r_b rows): op(A) = N^T
+      t2.push_back(thin(ws_ref(mb.N32), mb.n, 1, uref(mb, 0), ra, ws_ref(mb.ZB + static_cast<size_t>(rb) * mb.n * 4),
+                        mb.n, 1, mb.n, mb.m, ra, 1.0f, 0.0f));
+      // Ct = X^T U_a (r_b x r_a): op(A) = X^T, X the first r_b columns of XU
+      t3.push_back(thin(ws_ref(mb.XU), ld, 1, uref(mb, 0), ra, ws_ref(mb.Ct), ra, 0, rb, mb.m, ra, 1.0f, 0.0f));
+      // Z += (U_a^T X) (U_b E_b)^T, as Z^T += (U_b E_b) Ct: op(A) = ((U_b E_b)^T)^T from ZB's first rows
+      t4.push_back(thin(ws_ref(mb.ZB), mb.n, 1, ws_ref(mb.Ct), ra, ws_ref(mb.ZB + static_cast<size_t>(rb) * mb.n * 4),
+                        mb.n, 1, mb.n, rb, ra, 1.0f, 1.0f));
+      // W <- decay W - lr c_shape (N + [X | U_a E_a] [(U_b E_b)^T ; Z])
+      Gemm32Prob f = g32(ws_ref(mb.XU), ld, 0, ws_ref(mb.ZB), mb.n, 0, user_ref(REF_W, mb.group, moff(mb)), mb.n,
+                         mb.m, mb.n, ld, 1.0f, 0.0f);
+      f.wupd = 1; f.aux = ws_ref(mb.N32); f.c0 = update_scale(mb);
+      fin.push_back(f);
     }
-    add_g32(L, q1, CAT_WHITEN);
-    add_g32(L, q2, CAT_WHITEN);
-    add_g32(L, q3, CAT_WHITEN);
-    add_g32(L, q4, CAT_WHITEN);
-    std::vector<NysElemJob> e2;
-    for (const MatBufs& mb : mats) {
-      NysElemJob j = nelem(NE_UPDATE);
-      j.dst = user_ref(REF_W, mb.group, moff(mb)); j.src = ws_ref(mb.N32);
-      j.rows = mb.m; j.cols = mb.n; j.ld_dst = j.ld_src = mb.n; j.c0 = update_scale(mb);
-      e2.push_back(j);
-    }
-    add_nelem(L, e2);
+    add_thin(L, t1, CAT_WHITEN);
+    add_thin(L, t2, CAT_WHITEN);
+    add_thin(L, t3, CAT_WHITEN);
+    add_thin(L, t4, CAT_WHITEN);
+    add_g32(L, fin, CAT_WHITEN);
   }
 
   // Whether a second concurrent Newton-Schulz chain pays for this chunk.
@@ -1633,7 +1701,7 @@ struct Planner {
         size_t* offs[] = {&mb.G16, &mb.G16T, &mb.N16, &mb.Xa32, &mb.XbT32, &mb.Xa16, &mb.XbT16, &mb.VT32, &mb.VT16,
                           &mb.NT16, &mb.X[0], &mb.X[1], &mb.XT[0], &mb.XT[1], &mb.A32, &mb.A16,
                           &mb.M16, &mb.XGT16, &mb.XMT16, &mb.Gr32, &mb.Mr32, &mb.NP16, &mb.ZT16,
-                          &mb.N32, &mb.X32, &mb.Z32, &mb.UtA, &mb.UtB};
+                          &mb.N32, &mb.XU, &mb.ZB, &mb.Ct};
         for (size_t* o : offs) *o += base;
         for (MatBufs::NysSide& S : mb.ns) {
           size_t* so[] = {&S.Om, &S.Yb, &S.Fb, &S.T1, &S.T2, &S.gram, &S.cm, &S.zp, &S.kout, &S.scratch};
@@ -2051,6 +2119,31 @@ struct Planner {
             if (!fits(q.C, (static_cast<size_t>(q.M - 1) * q.ldc + q.N) * 4)) return false;
             if (q.rowscale.kind != REF_NONE && !fits(q.rowscale, static_cast<size_t>(q.M) * 4)) return false;
             if (q.alpha_slot >= 0 && !slot_ok(q.alpha_slot)) return false;
+            if (q.wupd && (q.C.kind != REF_W || !fits(q.aux, (static_cast<size_t>(q.M - 1) * q.ldc + q.N) * 4))) return false;
+          }
+          if (blk != r.nblocks) return false;
+        } else if (r.type == L_THIN) {
+          if (r.first < 0 || r.first + r.count > static_cast<int>(thin_jobs.size())) return false;
+          if (r.thin_ta < 0 || r.thin_ta > 1 || r.thin_mom < 0 || r.thin_mom > 1 || (r.thin_ta && r.thin_mom)) return false;
+          int blk = 0;
+          for (int j = r.first; j < r.first + r.count; ++j) {
+            const ThinJob& q = thin_jobs[j];
+            if (q.ta != r.thin_ta || q.mom != r.thin_mom || q.ot < 0 || q.ot > 1) return false;
+            if (q.Mo < 1 || q.K < 1 || q.R < 1 || q.R > kThinMaxR || q.blk_begin != blk) return false;
+            blk += (q.Mo + kThinTile - 1) / kThinTile;
+            const int ar = q.ta ? q.K : q.Mo, ac = q.ta ? q.Mo : q.K;
+            const int cr = q.ot ? q.R : q.Mo, cc = q.ot ? q.Mo : q.R;
+            if (q.lda < ac || q.ldb < q.R || q.ldc < cc) return false;
+            if (!fits(q.A, (static_cast<size_t>(ar - 1) * q.lda + ac) * (q.a_fmt == GF_F32 ? 4 : 2))) return false;
+            if (!fits(q.B, (static_cast<size_t>(q.K - 1) * q.ldb + q.R) * 4)) return false;
+            if (!fits(q.C, (static_cast<size_t>(cr - 1) * q.ldc + cc) * 4)) return false;
+            if (q.mom) {   // M: the gradient's shape and stride; N: Mo x K, stride ldn
+              if (q.ldn < q.K || !fits(q.M, (static_cast<size_t>(ar - 1) * q.lda + ac) * 4) ||
+                  !fits(q.Nout, (static_cast<size_t>(q.Mo - 1) * q.ldn + q.K) * 4))
+                return false;
+            }
+            if (q.alpha_slot >= 0 && !slot_ok(q.alpha_slot)) return false;
+            if (q.rowscale.kind != REF_NONE && (q.ot != 0 || !fits(q.rowscale, static_cast<size_t>(q.Mo) * 4))) return false;
           }
           if (blk != r.nblocks) return false;
         } else if (r.type == L_NORTH) {
@@ -2076,9 +2169,11 @@ struct Planner {
           int blk = 0;
           for (int j = r.first; j < r.first + r.count; ++j) {
             const NysElemJob& q = nelem_jobs[j];
-            if (q.kind < NE_GATHER || q.kind > NE_UPDATE || q.rows < 1 || q.cols < 1 || q.blk_begin != blk || q.blocks < 1) return false;
+            if (q.kind < NE_GATHER || q.kind > NE_SCALE || q.rows < 1 || q.cols < 1 || q.blk_begin != blk || q.blocks < 1) return false;
             blk += q.blocks;
-            if (q.ld_dst < q.cols || !fits(q.dst, (static_cast<size_t>(q.rows - 1) * q.ld_dst + q.cols) * 4)) return false;
+            if (q.trans && q.kind != NE_SCALE) return false;
+            const int dr = q.trans ? q.cols : q.rows, dc = q.trans ? q.rows : q.cols;
+            if (q.ld_dst < dc || !fits(q.dst, (static_cast<size_t>(dr - 1) * q.ld_dst + dc) * 4)) return false;
             const int scols = q.kind == NE_GATHER ? q.cols1 : q.cols;
             if (scols > 0 && (q.ld_src < scols || !fits(q.src, (static_cast<size_t>(q.rows - 1) * q.ld_src + scols) * 4)))
               return false;
@@ -2087,10 +2182,6 @@ struct Planner {
               if (q.cols1 < 0 || q.cols1 > q.cols) return false;
               if (c2 > 0 && (q.ld_src2 < c2 || !fits(q.src2, (static_cast<size_t>(q.rows - 1) * q.ld_src2 + c2) * 4))) return false;
             }
-            if (q.kind == NE_MOMENTUM &&
-                (q.ld_src2 < q.cols ||
-                 !fits(q.src2, (static_cast<size_t>(q.rows - 1) * q.ld_src2 + q.cols) * (q.g_fmt == GF_F32 ? 4 : 2))))
-              return false;
             if (q.kind == NE_SCALE && !fits(q.lam, static_cast<size_t>(q.cols) * 4)) return false;
           }
           if (blk != r.nblocks) return false;
@@ -2252,7 +2343,7 @@ struct Planner {
 
 struct WsLayout {
   size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, adam = 0, jac = 0, g32 = 0, north = 0, nsmall = 0,
-         nelem = 0, scal = 0, part = 0, flag = 0, resid = 0, chunk = 0, total = 0;
+         nelem = 0, thin = 0, scal = 0, part = 0, flag = 0, resid = 0, chunk = 0, total = 0;
 };
 
 WsLayout ws_layout(Planner& P) {
@@ -2272,6 +2363,7 @@ WsLayout ws_layout(Planner& P) {
   w.north = take(P.north_jobs.size() * sizeof(NysOrthJob));
   w.nsmall = take(P.nsmall_jobs.size() * sizeof(NysSmallJob));
   w.nelem = take(P.nelem_jobs.size() * sizeof(NysElemJob));
+  w.thin = take(P.thin_jobs.size() * sizeof(ThinJob));
   w.scal = take(static_cast<size_t>(P.n_slots) * sizeof(float));
   w.part = take(static_cast<size_t>(P.max_partials) * 2 * sizeof(float) * kNsStreams);   // one region per stream
   w.flag = take(sizeof(int));
@@ -2370,7 +2462,8 @@ okls_status okls_plan_query(const okls_config* cfg, int n_groups, const okls_gro
     for (const std::vector<LaunchRec>& L : cs)
       for (const LaunchRec& r : L)
         n += (r.type == L_STAT || r.type == L_CAST || r.type == L_GEMM || r.type == L_SYM || r.type == L_ADAM ||
-              r.type == L_JAC || r.type == L_G32 || r.type == L_NORTH || r.type == L_NSMALL || r.type == L_NELEM);
+              r.type == L_JAC || r.type == L_G32 || r.type == L_NORTH || r.type == L_NSMALL || r.type == L_NELEM ||
+              r.type == L_THIN);
     return n;
   };
   info.chunks = static_cast<int>(P.chunks.size());
@@ -2427,7 +2520,8 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   P.plan(w.chunk);
   if (!P.validate() || P.probs.size() != sizing.probs.size() || P.chunk_bytes != sizing.chunk_bytes ||
       P.adam_jobs.size() != sizing.adam_jobs.size() || P.jac_jobs.size() != sizing.jac_jobs.size() ||
-      P.g32_jobs.size() != sizing.g32_jobs.size() || P.nelem_jobs.size() != sizing.nelem_jobs.size())
+      P.g32_jobs.size() != sizing.g32_jobs.size() || P.nelem_jobs.size() != sizing.nelem_jobs.size() ||
+      P.thin_jobs.size() != sizing.thin_jobs.size())
     return OKLS_ERR_UNSUPPORTED;
   // the regions the tables and slots occupy must end before the chunk buffers
   if (w.flag + sizeof(int) > w.chunk) return OKLS_ERR_UNSUPPORTED;
@@ -2449,6 +2543,7 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_north = w.north;
   h->off_nsmall = w.nsmall;
   h->off_nelem = w.nelem;
+  h->off_thin = w.thin;
   h->s_np = P.s_np;
   h->off_scal = w.scal;
   h->off_part = w.part;
@@ -2514,6 +2609,7 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   up(w.north, P.north_jobs.data(), P.north_jobs.size() * sizeof(NysOrthJob));
   up(w.nsmall, P.nsmall_jobs.data(), P.nsmall_jobs.size() * sizeof(NysSmallJob));
   up(w.nelem, P.nelem_jobs.data(), P.nelem_jobs.size() * sizeof(NysElemJob));
+  up(w.thin, P.thin_jobs.data(), P.thin_jobs.size() * sizeof(ThinJob));
   up(w.scal, scal.data(), scal.size() * sizeof(float));
   // residual partials start as NaN: no root computed yet
   const std::vector<float> nan_fill(h->resid_floats, std::numeric_limits<float>::quiet_NaN());
@@ -2747,7 +2843,6 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.jobs = reinterpret_cast<const JacJob*>(ws + h->off_jac) + r.first;
         a.n_jobs = r.count;
         a.round = r.round;
-        a.tol = h->cfg.jacobi_tol;
         a.partials = reinterpret_cast<float*>(ws + r.jac_part);
         a.flags = reinterpret_cast<int32_t*>(ws + r.jac_flag);
         a.ws = ws;
@@ -2758,9 +2853,21 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.jobs = reinterpret_cast<const Gemm32Prob*>(ws + h->off_g32) + r.first;
         a.n_jobs = r.count;
         a.scal = scal;
+        a.lr = lr_update;
+        a.decay = static_cast<float>(decay);
         a.ws = ws;
         a.user = user;
         e = launch_gemm32(a, r.nblocks, rs);
+      } else if (r.type == L_THIN) {
+        ThinArgs a;
+        a.jobs = reinterpret_cast<const ThinJob*>(ws + h->off_thin) + r.first;
+        a.n_jobs = r.count;
+        a.scal = scal;
+        a.beta1 = static_cast<float>(b1);
+        a.s_t = static_cast<float>(s_t);
+        a.ws = ws;
+        a.user = user;
+        e = launch_thin(a, r.thin_ta, r.thin_mom, r.nblocks, rs);
       } else if (r.type == L_NORTH) {
         NysOrthArgs a;
         a.jobs = reinterpret_cast<const NysOrthJob*>(ws + h->off_north) + r.first;
@@ -2781,11 +2888,7 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         NysElemArgs a;
         a.jobs = reinterpret_cast<const NysElemJob*>(ws + h->off_nelem) + r.first;
         a.n_jobs = r.count;
-        a.beta1 = static_cast<float>(b1);
-        a.s_t = static_cast<float>(s_t);
         a.mu = h->cfg.eps;
-        a.lr = lr_update;
-        a.decay = static_cast<float>(decay);
         a.ws = ws;
         a.user = user;
         e = launch_nys_elem(a, r.nblocks, rs);

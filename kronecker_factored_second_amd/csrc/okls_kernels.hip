@@ -1598,7 +1598,7 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_check_kernel(JacArgs a) {
       so += red[2 * w];
       sd += red[2 * w + 1];
     }
-    a.flags[J.flag] = (so <= a.tol * a.tol * sd) ? 1 : 0;
+    a.flags[J.flag] = (so <= J.tol * J.tol * sd) ? 1 : 0;
   }
 }
 
@@ -1655,6 +1655,34 @@ __global__ __launch_bounds__(256) void gemm32_kernel(Gemm32Args a) {
   }
   const float alpha = P.alpha * (P.alpha_slot >= 0 ? a.scal[P.alpha_slot] : 1.0f);
   const float* rs = P.rowscale.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(P.rowscale, a.ws, a.user)) : nullptr;
+  if (P.wupd) {
+    // W <- decay W - lr c0 (alpha acc + X), X the unpreconditioned part of the
+    // update (same layout as W); a row's four entries as one 16-byte access
+    const float* X = reinterpret_cast<const float*>(resolve(P.aux, a.ws, a.user));
+    const float s = -(a.lr * P.c0);
+    const bool vec = (P.ldc & 3) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(X)) & 15) == 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gi = i0 + 4 * ty + i;
+      if (gi >= P.M) continue;
+      const int gj = j0 + 4 * tx;
+      const size_t o = static_cast<size_t>(gi) * P.ldc + gj;
+      if (vec && gj + 3 < P.N) {
+        const float4 x = *reinterpret_cast<const float4*>(X + o);
+        float4 w = *reinterpret_cast<const float4*>(C + o);
+        w.x = __builtin_fmaf(a.decay, w.x, s * __builtin_fmaf(alpha, acc[i][0], x.x));
+        w.y = __builtin_fmaf(a.decay, w.y, s * __builtin_fmaf(alpha, acc[i][1], x.y));
+        w.z = __builtin_fmaf(a.decay, w.z, s * __builtin_fmaf(alpha, acc[i][2], x.z));
+        w.w = __builtin_fmaf(a.decay, w.w, s * __builtin_fmaf(alpha, acc[i][3], x.w));
+        *reinterpret_cast<float4*>(C + o) = w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (gj + j < P.N) C[o + j] = __builtin_fmaf(a.decay, C[o + j], s * __builtin_fmaf(alpha, acc[i][j], X[o + j]));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int gi = i0 + 4 * ty + i;
@@ -1666,6 +1694,219 @@ __global__ __launch_bounds__(256) void gemm32_kernel(Gemm32Args a) {
       if (gj >= P.N) continue;
       float* c = C + static_cast<size_t>(gi) * P.ldc + gj;
       *c = P.beta != 0.0f ? __builtin_fmaf(P.beta, *c, ri * acc[i][j]) : ri * acc[i][j];
+    }
+  }
+}
+
+// Thin fp32 products (ThinJob): kThinTile rows of op(A) per block, K in
+// stages of kThinK through LDS, the next stage's global loads in registers
+// during the current stage's FMAs, every thread a 4 x 4 block of each
+// 32-column block of C.  The stage of op(A) is held k-major (As[k][i]); the
+// 4-row group index of row i is XOR-swizzled by k / 4, so that the
+// transposing stores of a row-major A (eight quads of one row per eight
+// lanes) fall in distinct banks while the FMA loop's 16-byte reads stay
+// contiguous per group.
+__device__ __forceinline__ int thin_sw(int k, int i) { return ((((i >> 2) ^ (k >> 2)) & 31) << 2) | (i & 3); }
+
+__device__ __forceinline__ float4 quad_any(const char* p, size_t o, int fmt) {
+  return fmt == GF_F32 ? grad_quad<GF_F32>(p, o) : fmt == GF_BF16 ? grad_quad<GF_BF16>(p, o) : grad_quad<GF_F16>(p, o);
+}
+__device__ __forceinline__ float& f4_at(float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+
+template <int TA, bool MOM>
+__global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
+  constexpr int TM = kThinTile, KC = kThinK, LA = TM + 4, LB = kThinMaxR + 4;
+  static_assert(TM == 128 && KC == 32 && kThinMaxR == 128, "the load and FMA maps below assume these sizes");
+  static_assert(!MOM || TA == 0, "the momentum operand is row-major");
+  __shared__ __attribute__((aligned(16))) float As[KC][LA];
+  __shared__ __attribute__((aligned(16))) float Bs[KC][LB];
+  const int gb = blockIdx.x;
+  const ThinJob J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
+  const int i0 = (gb - J.blk_begin) * TM;
+  const char* A = resolve(J.A, a.ws, a.user);
+  const float* B = reinterpret_cast<const float*>(resolve(J.B, a.ws, a.user));
+  float* C = reinterpret_cast<float*>(resolve(J.C, a.ws, a.user));
+  float* Mp = nullptr;
+  float* Np = nullptr;
+  if constexpr (MOM) {
+    Mp = reinterpret_cast<float*>(resolve(J.M, a.ws, a.user));
+    Np = reinterpret_cast<float*>(resolve(J.Nout, a.ws, a.user));
+  }
+  const int t = threadIdx.x, rg = t & 31, cg = t >> 5;
+  const int CB = (J.R + 31) >> 5;
+  const uintptr_t amask = J.a_fmt == GF_F32 ? 15 : 7;
+  bool avec = (J.lda & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & amask) == 0;
+  if constexpr (MOM)
+    avec = avec && (J.ldn & 3) == 0 && ((reinterpret_cast<uintptr_t>(Mp) | reinterpret_cast<uintptr_t>(Np)) & 15) == 0;
+  const bool bvec = (J.ldb & 3) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
+  const bool cvec = (J.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
+  const float b1 = a.beta1, b1c = 1.0f - a.beta1, st = a.s_t;
+
+  float4 ra[4], rb[4];
+  float acc[4][4][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[c][i][j] = 0.0f;
+
+  // stage k0 into registers: op(A) as 1024 quads (TA 0: 128 rows x 8 quads
+  // along k; TA 1: 32 k-rows x 32 quads along i), B as 32 k-rows x 32 quads
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = t + 256 * j;
+      float4 v = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (TA == 0) {
+        const int row = q >> 3, gk = k0 + (q & 7) * 4, gi = i0 + row;
+        if (gi < J.Mo && gk < J.K) {
+          const size_t o = static_cast<size_t>(gi) * J.lda + gk;
+          if (avec && gk + 3 < J.K) {
+            v = quad_any(A, o, J.a_fmt);
+            if constexpr (MOM) {
+              float4 m = *reinterpret_cast<const float4*>(Mp + o);
+              float4 mn, nv;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                f4_at(mn, e) = b1 * f4_at(m, e) + b1c * f4_at(v, e);
+                f4_at(nv, e) = st * (b1 * f4_at(mn, e) + b1c * f4_at(v, e));
+              }
+              *reinterpret_cast<float4*>(Mp + o) = mn;
+              *reinterpret_cast<float4*>(Np + static_cast<size_t>(gi) * J.ldn + gk) = nv;
+              v = nv;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (gk + e >= J.K) break;
+              float g = grad_elem(A, o + e, J.a_fmt);
+              if constexpr (MOM) {
+                const float mn = b1 * Mp[o + e] + b1c * g;
+                Mp[o + e] = mn;
+                g = st * (b1 * mn + b1c * g);
+                Np[static_cast<size_t>(gi) * J.ldn + gk + e] = g;
+              }
+              f4_at(v, e) = g;
+            }
+          }
+        }
+      } else {
+        const int gk = k0 + (q >> 5), gi = i0 + (q & 31) * 4;
+        if (gk < J.K && gi < J.Mo) {
+          const size_t o = static_cast<size_t>(gk) * J.lda + gi;
+          if (avec && gi + 3 < J.Mo) {
+            v = quad_any(A, o, J.a_fmt);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gi + e < J.Mo) f4_at(v, e) = grad_elem(A, o + e, J.a_fmt);
+          }
+        }
+      }
+      ra[j] = v;
+      float4 w = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int bk = k0 + (q >> 5), bc = (q & 31) * 4;
+      if (bk < J.K && bc < J.R) {
+        const float* bp = B + static_cast<size_t>(bk) * J.ldb + bc;
+        if (bvec && bc + 3 < J.R) {
+          w = *reinterpret_cast<const float4*>(bp);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (bc + e < J.R) f4_at(w, e) = bp[e];
+        }
+      }
+      rb[j] = w;
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = t + 256 * j;
+      if constexpr (TA == 0) {
+        const int row = q >> 3, kq = (q & 7) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[kq + e][thin_sw(kq + e, row)] = f4_at(ra[j], e);
+      } else {
+        const int kr = q >> 5, c4 = (q & 31) * 4;
+        *reinterpret_cast<float4*>(&As[kr][thin_sw(kr, c4)]) = ra[j];
+      }
+      *reinterpret_cast<float4*>(&Bs[q >> 5][(q & 31) * 4]) = rb[j];
+    }
+  };
+
+  const int nk = (J.K + KC - 1) / KC;
+  gload(0);
+  for (int sidx = 0; sidx < nk; ++sidx) {
+    __syncthreads();                  // the previous stage's reads are done
+    lstore();
+    __syncthreads();
+    if (sidx + 1 < nk) gload((sidx + 1) * KC);
+#pragma unroll 4
+    for (int kk = 0; kk < KC; ++kk) {
+      float4 av = *reinterpret_cast<const float4*>(&As[kk][thin_sw(kk, 4 * rg)]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c >= CB) break;
+        float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][32 * c + 4 * cg]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[c][i][j] = __builtin_fmaf(f4_at(av, i), f4_at(bv, j), acc[c][i][j]);
+      }
+    }
+  }
+
+  const float alpha0 = J.alpha * (J.alpha_slot >= 0 ? a.scal[J.alpha_slot] : 1.0f);
+  const float* rsc = J.rowscale.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(J.rowscale, a.ws, a.user)) : nullptr;
+  const float beta = J.beta;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c >= CB) break;
+    const int c0 = 32 * c + 4 * cg;
+    if (J.ot == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gi = i0 + 4 * rg + i;
+        if (gi >= J.Mo) break;
+        const float alpha = rsc != nullptr ? alpha0 * rsc[gi] : alpha0;
+        float* cp = C + static_cast<size_t>(gi) * J.ldc + c0;
+        if (cvec && c0 + 3 < J.R) {
+          float4 o = float4{alpha * acc[c][i][0], alpha * acc[c][i][1], alpha * acc[c][i][2], alpha * acc[c][i][3]};
+          if (beta != 0.0f) {
+            const float4 old = *reinterpret_cast<const float4*>(cp);
+            o.x = __builtin_fmaf(beta, old.x, o.x); o.y = __builtin_fmaf(beta, old.y, o.y);
+            o.z = __builtin_fmaf(beta, old.z, o.z); o.w = __builtin_fmaf(beta, old.w, o.w);
+          }
+          *reinterpret_cast<float4*>(cp) = o;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (c0 + j < J.R) cp[j] = beta != 0.0f ? __builtin_fmaf(beta, cp[j], alpha * acc[c][i][j]) : alpha * acc[c][i][j];
+        }
+      }
+    } else {
+      const float alpha = alpha0;
+      const int r0 = i0 + 4 * rg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c0 + j >= J.R) break;
+        float* cp = C + static_cast<size_t>(c0 + j) * J.ldc + r0;
+        if (cvec && r0 + 3 < J.Mo) {
+          float4 o = float4{alpha * acc[c][0][j], alpha * acc[c][1][j], alpha * acc[c][2][j], alpha * acc[c][3][j]};
+          if (beta != 0.0f) {
+            const float4 old = *reinterpret_cast<const float4*>(cp);
+            o.x = __builtin_fmaf(beta, old.x, o.x); o.y = __builtin_fmaf(beta, old.y, o.y);
+            o.z = __builtin_fmaf(beta, old.z, o.z); o.w = __builtin_fmaf(beta, old.w, o.w);
+          }
+          *reinterpret_cast<float4*>(cp) = o;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (r0 + i < J.Mo) cp[i] = beta != 0.0f ? __builtin_fmaf(beta, cp[i], alpha * acc[c][i][j]) : alpha * acc[c][i][j];
+        }
+      }
     }
   }
 }
@@ -1689,6 +1930,7 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // are one wave per finished column, lanes over the rows.
 __global__ __launch_bounds__(256) void nys_orth_kernel(NysOrthArgs a) {
   __shared__ float coef[kNysMaxK];
+  __shared__ float part[4][16];
   __shared__ float red[4];
   const NysOrthJob J = a.jobs[blockIdx.x];
   float* Y = reinterpret_cast<float*>(resolve(J.Y, a.ws, a.user));
@@ -1703,15 +1945,34 @@ __global__ __launch_bounds__(256) void nys_orth_kernel(NysOrthArgs a) {
     return block_sum256(s, red);
   };
   auto project_out = [&](int j) {       // y_j <- y_j - Q_{<j} (Q_{<j}^T y_j)
-    for (int c = wave; c < j; c += 4) {
-      float s = 0.0f;
-      for (int r = lane; r < J.d; r += 64)
-        s += Y[static_cast<size_t>(r) * J.ld + c] * Y[static_cast<size_t>(r) * J.ld + j];
+    // the coefficients 16 at a time: every thread walks its rows, reading
+    // each row's 16 entries as one contiguous run, then a fixed-order
+    // reduction over the wave and the four waves
+    for (int c0 = 0; c0 < j; c0 += 16) {
+      float s[16];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-      if (lane == 0) coef[c] = s;
+      for (int c = 0; c < 16; ++c) s[c] = 0.0f;
+      for (int r = threadIdx.x; r < J.d; r += 256) {
+        const float* row = Y + static_cast<size_t>(r) * J.ld;
+        const float yj = row[j];
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (c0 + c < j) s[c] = __builtin_fmaf(row[c0 + c], yj, s[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s[c] += __shfl_xor(s[c], o, 64);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) part[wave][c] = s[c];
+      }
+      __syncthreads();
+      if (threadIdx.x < 16 && c0 + static_cast<int>(threadIdx.x) < j)
+        coef[c0 + threadIdx.x] = (part[0][threadIdx.x] + part[1][threadIdx.x]) + (part[2][threadIdx.x] + part[3][threadIdx.x]);
+      __syncthreads();
     }
-    __syncthreads();
     for (int r = threadIdx.x; r < J.d; r += 256) {
       float* row = Y + static_cast<size_t>(r) * J.ld;
       float v = row[j];
@@ -1972,23 +2233,13 @@ __global__ __launch_bounds__(256) void nys_elem_kernel(NysElemArgs a) {
   if (J.kind == NE_SCALE) lam_r = lam[J.cols - 1];
   for (size_t e = static_cast<size_t>(gb - J.blk_begin) * 256 + threadIdx.x; e < total; e += stride) {
     const int r = static_cast<int>(e / J.cols), c = static_cast<int>(e % J.cols);
-    const size_t od = static_cast<size_t>(r) * J.ld_dst + c;
+    const size_t od = J.trans ? static_cast<size_t>(c) * J.ld_dst + r : static_cast<size_t>(r) * J.ld_dst + c;
     if (J.kind == NE_GATHER) {
       dst[od] = c < J.cols1 ? reinterpret_cast<const float*>(src)[static_cast<size_t>(r) * J.ld_src + c]
                             : reinterpret_cast<const float*>(src2)[static_cast<size_t>(r) * J.ld_src2 + (c - J.cols1)];
-    } else if (J.kind == NE_MOMENTUM) {
-      float* m = reinterpret_cast<float*>(const_cast<char*>(src));
-      const size_t om = static_cast<size_t>(r) * J.ld_src + c;
-      const float g = grad_elem(src2, static_cast<size_t>(r) * J.ld_src2 + c, J.g_fmt);
-      const float mn = a.beta1 * m[om] + (1.0f - a.beta1) * g;
-      m[om] = mn;
-      dst[od] = a.s_t * (a.beta1 * mn + (1.0f - a.beta1) * g);
-    } else if (J.kind == NE_SCALE) {
+    } else {   // NE_SCALE
       const float e_c = sqrtf((lam_r + a.mu) / (lam[c] + a.mu)) - 1.0f;
       dst[od] = reinterpret_cast<const float*>(src)[static_cast<size_t>(r) * J.ld_src + c] * e_c;
-    } else {
-      const float v = reinterpret_cast<const float*>(src)[static_cast<size_t>(r) * J.ld_src + c];
-      dst[od] = __builtin_fmaf(a.decay, dst[od], -(a.lr * J.c0) * v);
     }
   }
 }
@@ -2099,6 +2350,15 @@ hipError_t launch_jacobi(const JacArgs& a, int kind, int n_blocks, hipStream_t s
 hipError_t launch_gemm32(const Gemm32Args& a, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   gemm32_kernel<<<dim3(n_blocks), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_thin(const ThinArgs& a, int ta, int mom, int n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  if (mom && ta) return hipErrorInvalidValue;
+  if (mom) thin_kernel<0, true><<<dim3(n_blocks), dim3(256), 0, s>>>(a);
+  else if (ta) thin_kernel<1, false><<<dim3(n_blocks), dim3(256), 0, s>>>(a);
+  else thin_kernel<0, false><<<dim3(n_blocks), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

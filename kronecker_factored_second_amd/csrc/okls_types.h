@@ -281,13 +281,13 @@ struct JacJob {
   int32_t flag;            // index of the converged flag
   int32_t solve_begin;     // first block of the job in a solve launch
   int32_t apply_begin;     // first block of the job in an apply launch
+  float tol;               // converged when ||off(B)||_F <= tol ||diag(B)||_F
 };
 
 struct JacArgs {
   const JacJob* jobs;
   int32_t n_jobs;
   int32_t round;           // 0 .. nb - 2 (jobs with fewer rounds skip the rest)
-  float tol;               // converged when ||off(B)||_F <= tol ||diag(B)||_F
   float* partials;         // float2 (off^2, diag^2) per B tile
   int32_t* flags;
   char* ws;
@@ -321,6 +321,9 @@ struct Gemm32Prob {
   int32_t alpha_slot;      // >= 0: alpha is multiplied by scal[alpha_slot]
   float beta;              // 0: C is written without being read
   Ref rowscale;            // REF_NONE, or M floats: row i of the product times rowscale[i]
+  int32_t wupd;            // 1: C is the weights W, updated as W <- decay W - lr c0 (alpha op(A) op(B) + aux)
+  Ref aux;                 // wupd: M x N fp32, row stride ldc
+  float c0;
   int32_t tiles_n;
   int32_t blk_begin;
 };
@@ -329,6 +332,37 @@ struct Gemm32Args {
   const Gemm32Prob* jobs;
   int32_t n_jobs;
   const float* scal;
+  float lr, decay;         // wupd problems
+  char* ws;
+  UserPtrs user;
+};
+
+// Thin fp32 products C = alpha op(A) B (+ beta C) where op(A) is Mo x K (the
+// large operand, streamed once) and B is K x R with R <= kThinMaxR: the sketch
+// products and the per-step preconditioning.  TA: op(A) = A^T (A stored
+// K x Mo).  OT: C stored transposed (R x Mo).  Momentum mode (TA = 0 only):
+// op(A) is the Nesterov momentum N computed from the gradient (A, a_fmt) and
+// M (same shape, row stride lda), which is updated in place; N is written to
+// Nout (row stride ldn).
+constexpr int kThinTile = 128;     // rows of op(A) per block
+constexpr int kThinK = 32;         // K per LDS stage
+constexpr int kThinMaxR = 128;     // columns of B and C
+struct ThinJob {
+  Ref A, B, C, M, Nout;
+  int32_t Mo, K, R;
+  int32_t lda, ldb, ldc, ldn;
+  int32_t ta, ot, a_fmt, mom;
+  float alpha, beta;
+  int32_t alpha_slot;      // >= 0: alpha is multiplied by scal[alpha_slot]
+  Ref rowscale;            // REF_NONE, or Mo floats: row i of op(A) B times rowscale[i] (ot = 0 only)
+  int32_t blk_begin;
+};
+
+struct ThinArgs {
+  const ThinJob* jobs;
+  int32_t n_jobs;
+  const float* scal;
+  float beta1, s_t;        // momentum mode
   char* ws;
   UserPtrs user;
 };
@@ -368,24 +402,21 @@ struct NysSmallArgs {
 
 enum NysElemKind : int32_t {
   NE_GATHER = 0,           // dst (rows x cols) = [src (cols1 columns) | src2 (the rest)]
-  NE_MOMENTUM = 1,         // src (M) <- beta1 M + (1 - beta1) G (src2, g_fmt); dst = s_t (beta1 M' + (1 - beta1) G)
-  NE_SCALE = 2,            // dst = src * e_j by column, e_j = sqrt((lam_{r-1} + mu) / (lam_j + mu)) - 1
-  NE_UPDATE = 3            // dst (W) = decay W - lr c0 src
+  NE_SCALE = 1             // dst = src * e_j by column, e_j = sqrt((lam_{r-1} + mu) / (lam_j + mu)) - 1
 };
 
 struct NysElemJob {
   int32_t kind;
   Ref dst, src, src2, lam;
   int32_t rows, cols, ld_dst, ld_src, ld_src2, cols1;
-  int32_t g_fmt;
-  float c0;
+  int32_t trans;           // NE_SCALE: dst holds the transpose (cols x rows, row stride ld_dst)
   int32_t blk_begin, blocks;
 };
 
 struct NysElemArgs {
   const NysElemJob* jobs;
   int32_t n_jobs;
-  float beta1, s_t, mu, lr, decay;
+  float mu;                // NE_SCALE: the eps of eq. (5)
   char* ws;
   UserPtrs user;
 };

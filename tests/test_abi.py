@@ -295,9 +295,11 @@ def _nys_cfg(**kw):
 def test_nystrom_plans_validate_and_flops_are_the_closed_forms():
     """Nystrom mode plans and validates for ragged, tiny (a side below
     r + p), transformer-block and bf16 shapes; a step that keeps the factors
-    launches fewer kernels; the per-step preconditioning FLOPs are the thin
-    products 8 m n r' (N U_b, the rank-r' correction of N, U_a^T N', the
-    second correction; r' per side), and a refresh adds the sketch products."""
+    launches fewer kernels; the per-step preconditioning FLOPs are those of
+    its thin products: X = N U_b (2 m n r_b), U_a^T N (2 m n r_a), X^T U_a
+    (2 m r_a r_b), the correction of Z (2 n r_a r_b) and the final
+    [X | U_a E_a] [(U_b E_b)^T ; Z] (2 m n (r_a + r_b)); a refresh adds the
+    sketch products."""
     _lib()
     for groups in ([(2, 96, 160, 0), (1, 200, 72, 0)], [(1, 5, 7, 1), (3, 33, 40, 2)],
                    [(4, 1024, 1024, 1), (2, 2816, 1024, 1), (1, 1024, 2816, 1)]):
@@ -309,7 +311,7 @@ def test_nystrom_plans_validate_and_flops_are_the_closed_forms():
             want = 0.0
             for b, m, n, _ in groups:
                 ra, rb = min(16, min(24, m)), min(16, min(24, n))
-                want += b * (2.0 * m * n * rb * 2 + 2.0 * m * n * ra * 2)
+                want += b * (4.0 * m * n * (ra + rb) + 2.0 * ra * rb * (m + n))
             assert info["flops"]["whiten_gemm"] == pytest.approx(want, rel=1e-12)
             assert info["flops"]["ns_gemm"] > 0 and info["flops"]["eigensolver"] > 0
 

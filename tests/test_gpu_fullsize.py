@@ -92,11 +92,11 @@ def _free_gpu():
     torch.cuda.empty_cache()
 
 
-def _build(name, precision, mode=None):
+def _build(name, precision, mode=None, **cfg):
     """Full workload: parameters (sampled ones from the spectral-muP init,
     the rest filler of the same scale) and the optimizer, its workspace
     limited so that one step's gradients still fit.  mode overrides the
-    workload's optimizer mode."""
+    workload's optimizer mode; cfg goes to the optimizer."""
     torch = pytest.importorskip("torch")
     w = WL.workload(name)
     WL.reset_caches()
@@ -107,13 +107,13 @@ def _build(name, precision, mode=None):
     for gi, i in _sampled(w, name):
         params[gi][i].copy_(torch.from_numpy(WL.initial_weights(w, gi, i)))
     bf16 = w.grad_dtype == "bf16"
-    opt_bytes = sum(b * (m * n + 2 * m * m + 2 * n * n) * 4 for m, n, b in w.groups)
+    opt_bytes = sum(b * ((2 if mode == "soap" else 1) * m * n + 2 * m * m + 2 * n * n) * 4 for m, n, b in w.groups)
     grad_bytes = sum(b * m * n * (2 if bf16 else 4) for m, n, b in w.groups)
     free = torch.cuda.mem_get_info(0)[0]
     limit = free - opt_bytes - 2 * grad_bytes - (8 << 30)
     from kronecker_factored_second_amd import okls
     opt = okls.OKLS(params, mode=mode or w.mode, precision=precision,
-                    grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit)
+                    grad_dtype=torch.bfloat16 if bf16 else torch.float32, workspace_limit=limit, **cfg)
     _log(f"{name}-{precision}: {w.n_matrices} matrices, chunk_matrices={opt.cfg.chunk_matrices}, "
          f"workspace {opt.workspace.numel() / 2**30:.1f} GiB")
     return w, opt, params
@@ -451,4 +451,143 @@ def test_max_side_rotated_diagonal(precision, kappa):
     decay = 1.0 - hp.lr * hp.weight_decay * (hp.lr / hp.peak())
     assert float(W.abs().max()) == 0.0 and decay < 1.0     # zero weights stay zero: U = 0
     del opt, W, S1, P1, Sa
+    _free_gpu()
+
+
+# Eigenbasis Adam (SOAP) at full size, bases refreshed after every second
+# step (t = 2 from the identity, a cold start): each checked matrix
+# teacher-forced on the GPU's own bases, as in tests/test_gpu_soap.py (whose
+# tolerances these are), the bases checked by orthogonality and by the
+# off-diagonal residual of Q^T S Q, and below side 4096 also by S's
+# eigenvalues (LAPACK eigvalsh).
+SOAP_CHECK = {"c2": None, "c3": [(0, 0), (1, 0), (2, 0)]}
+SOAP_TOL = {"fp32": dict(W=2e-4, M=1e-6, V=2e-5, F=2e-5, orth=2e-5, res=2e-5, eig=2e-5),
+            "fp16": dict(W=3e-2, M=1e-6, V=1e-2, F=5e-3, orth=2e-5, res=5e-3, eig=5e-3)}
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name,precision", [("c2", "fp32"), ("c2", "fp16"), ("c3", "fp16")])
+def test_fullsize_soap(name, precision):
+    torch = pytest.importorskip("torch")
+    from oracle import soap_oracle as S
+    _free_gpu()
+    w, opt, params = _build(name, precision, mode="soap", precond_freq=2)
+    c = opt.cfg
+    hp = S.SoapHyper(lr=opt.lr, beta1=float(np.float32(c.beta1)), beta2=float(np.float32(c.beta2)),
+                     shampoo_beta=float(np.float32(c.soap_beta)), eps=float(np.float32(c.eps)),
+                     weight_decay=float(np.float32(c.weight_decay)), freq=int(c.precond_freq),
+                     bias_correction=bool(c.bias_correction), moments="eigen" if c.soap_moments else "param")
+    tol = SOAP_TOL[precision]
+    checked = SOAP_CHECK[name] or _sampled(w, name)
+    rep = H.Report(f"full-soap-{name}-{precision}")
+
+    def snap(gi, i):
+        s = opt.state[gi]
+        return S.SoapState(W=_f64(params[gi][i]), M=_f64(s["M"][i]), V=_f64(s["V"][i]), L=_f64(s["Sa"][i]),
+                           R=_f64(s["Sb"][i]), QL=_f64(s["Pa"][i]), QR=_f64(s["Pb"][i]))
+
+    rel = lambda x, ref: float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
+    for t in (1, 2, 3):
+        grads, host = _grads(w, name, t)
+        before = {k: snap(*k) for k in checked}
+        _log(f"soap {name} t={t}: step")
+        opt.step(grads=grads)
+        torch.cuda.synchronize()
+        assert opt.check_finite(), f"non-finite state after step {t}"
+        for gi, i in checked:
+            got = snap(gi, i)
+            b4 = before[(gi, i)]
+            _log(f"soap {name} t={t} ({gi},{i}): oracle step")
+            r = S.soap_step(b4, host[(gi, i)], hp, t, bases=(got.QL, got.QR))
+            e = dict(t=t, g=gi, i=i, W=rel(got.W - b4.W, r.state.W - b4.W), M=rel(got.M, r.state.M),
+                     V=rel(got.V, r.state.V), F=max(rel(got.L, r.state.L), rel(got.R, r.state.R)))
+            if r.refreshed:
+                e["orth"] = max(S.orthogonality(got.QL), S.orthogonality(got.QR))
+                e["res"] = max(S.offdiag_residual(got.QL, r.state.L), S.offdiag_residual(got.QR, r.state.R))
+                eig = []
+                for Q, A in ((got.QL, r.state.L), (got.QR, r.state.R)):
+                    if A.shape[0] < 4096:
+                        dg = np.sort(np.diag(Q.T @ A @ Q))
+                        lam = np.linalg.eigvalsh(0.5 * (A + A.T))
+                        eig.append(float(np.max(np.abs(dg - lam)) / max(np.linalg.norm(A), 1e-300)))
+                if eig:
+                    e["eig"] = max(eig)
+            else:
+                assert np.array_equal(got.QL, b4.QL) and np.array_equal(got.QR, b4.QR), f"t={t}: bases changed"
+            rep.add(**e)
+            for k, v in e.items():
+                if k in tol:
+                    assert v <= tol[k], f"t={t} group {gi} matrix {i}: {k} error {v:.3e} > {tol[k]:.1e}"
+        del grads, host, before
+    del opt, params
+    _free_gpu()
+
+
+# Nystrom low-rank factors at full size, refreshed on steps 1 and 3 (the
+# first a cold start): each checked matrix teacher-forced with the GPU's own
+# Gaussian sketch matrices, as in tests/test_gpu_nystrom.py; U compared
+# column by column (up to sign after the cold start), Lambda relative to its
+# largest entry.  The sketch products' fp32 rounding grows like the square
+# root of their inner dimension (the other side, up to 5632 here, against
+# at most 200 in tests/test_gpu_nystrom.py): U and Lambda take that test's
+# bounds times sqrt(5632 / 200) ~ 5.
+NYS_CHECK = {"c2": None, "c3": [(0, 0), (1, 0), (2, 0)]}
+NYS_TOL = dict(W=2e-4, M=1e-6, U=1e-3, lam=1e-5)
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_fullsize_nystrom(name):
+    torch = pytest.importorskip("torch")
+    from oracle import nystrom_oracle as Y
+    _free_gpu()
+    w, opt, params = _build(name, "fp32", mode="nystrom", root_period=2)
+    c = opt.cfg
+    f = lambda x: float(np.float32(x))
+    hp = Y.NysHyper(lr=opt.lr, beta1=f(c.beta1), beta2=f(c.beta2), eps=f(c.eps), weight_decay=f(c.weight_decay),
+                    lr_peak=f(c.lr_peak), nesterov_var_corr=bool(c.nesterov_var_corr),
+                    shape_scale=bool(c.shape_scale), rank=int(c.nys_rank), oversample=int(c.nys_oversample),
+                    passes=int(c.nys_passes), period=int(c.root_period))
+    checked = NYS_CHECK[name] or _sampled(w, name)
+    rep = H.Report(f"full-nys-{name}")
+
+    def snap(gi, i, t):
+        s = opt.state[gi]
+        st = Y.NysState(W=_f64(params[gi][i]), M=_f64(s["M"][i]))
+        if t > 1:
+            st.UL, st.lamL, st.UR, st.lamR = _f64(s["Pa"][i]), _f64(s["Sa"][i]), _f64(s["Pb"][i]), _f64(s["Sb"][i])
+        return st
+
+    rel = lambda x, ref: float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
+
+    def u_err(got, ref, signed):
+        if not signed:
+            got = got * np.where(np.sum(got * ref, axis=0) < 0, -1.0, 1.0)
+        return rel(got, ref)
+
+    for t in (1, 2, 3):
+        grads, host = _grads(w, name, t)
+        before = {k: snap(*k, t) for k in checked}
+        _log(f"nystrom {name} t={t}: step")
+        opt.step(grads=grads)
+        torch.cuda.synchronize()
+        assert opt.check_finite(), f"non-finite state after step {t}"
+        for gi, i in checked:
+            got = snap(gi, i, 2)
+            b4 = before[(gi, i)]
+            s = opt.state[gi]
+            r = Y.nys_step(b4, host[(gi, i)], hp, t, _f64(s["PsiA"][i]), _f64(s["PsiB"][i]))
+            e = dict(t=t, g=gi, i=i, W=rel(got.W - b4.W, r.state.W - b4.W), M=rel(got.M, r.state.M))
+            if hp.refresh(t):
+                e["U"] = max(u_err(got.UL, r.state.UL, t > 1), u_err(got.UR, r.state.UR, t > 1))
+                e["lam"] = max(float(np.max(np.abs(got.lamL - r.state.lamL)) / r.state.lamL[0]),
+                               float(np.max(np.abs(got.lamR - r.state.lamR)) / r.state.lamR[0]))
+            else:
+                assert np.array_equal(got.UL, b4.UL) and np.array_equal(got.lamR, b4.lamR), f"t={t}: factors changed"
+            rep.add(**e)
+            for k, v in e.items():
+                if k in NYS_TOL:
+                    assert v <= NYS_TOL[k], f"t={t} group {gi} matrix {i}: {k} error {v:.3e} > {NYS_TOL[k]:.1e}"
+        del grads, host, before
+    del opt, params
     _free_gpu()
