@@ -155,7 +155,7 @@ def summarize_counters(fetch_dir, write_dir, commands, workload):
     print("\n".join(lines))
 
 
-EPI_NAMES = ["STORE32", "SYRK", "NS_T", "NS_Y1", "STORE16", "NS_FINAL", "UPDATE", "POLAR", "POLAR_UPDATE"]
+EPI_NAMES = ["STORE32", "SYRK", "NS_T", "NS_Y1", "STORE16", "NS_FINAL", "UPDATE", "POLAR", "POLAR_UPDATE", "NS_T_RES"]
 SQ_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16",
                "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES"]
 

@@ -116,3 +116,22 @@ def test_residual_ragged_shampoo_and_kept_roots(precision):
 
     _run(f"resid-ragged-{precision}", [(200, 72, 2), (33, 130, 1)], grad, 4, precision, mode="shampoo",
          root_period=2)
+
+
+def test_residual_entry_point_errors():
+    """The diagnostic is refused for modes without Newton-Schulz roots and for
+    an output array shorter than 4 doubles per matrix, and a chunked plan
+    reports every matrix."""
+    import ctypes
+    torch = pytest.importorskip("torch")
+    from kronecker_factored_second_amd import okls
+    opt, _ = H.make([(64, 80, 2)], mode="soap")
+    with pytest.raises(okls.OKLSError, match="UNSUPPORTED"):
+        opt.ns_residuals()
+    opt, _ = H.make([(64, 80, 3)], chunk_matrices=1)
+    buf = (ctypes.c_double * 11)()
+    assert okls.load().okls_ns_residuals(opt.handle, buf, 11, ctypes.c_void_p(opt.stream)) == -1
+    opt.step(grads=[torch.randn(3, 64, 80, device="cuda:0")])
+    torch.cuda.synchronize()
+    res = opt.ns_residuals()[0]
+    assert all(math.isfinite(mat[s][0]) and math.isnan(mat[s][1]) for mat in res for s in (0, 1))

@@ -281,6 +281,31 @@ def test_chunked_steps_are_bitwise_unchunked(mode, gdt, period, precision):
                 assert np.array_equal(a[k], b[k]), (mode, gdt, period, precision, k)
 
 
+@pytest.mark.parametrize("mode,cfg", [("soap", dict(precond_freq=2)), ("nystrom", dict(root_period=2)),
+                                      ("nystrom", dict(root_period=1, nys_passes=2))])
+def test_chunked_steps_are_bitwise_unchunked_soap_nystrom(mode, cfg):
+    """The eigenbasis-Adam and Nystrom modes under chunk_matrices = 1 and 2:
+    bit-identical to one chunk over steps that refresh (the bases, the
+    low-rank factors) and steps that keep them."""
+    torch = pytest.importorskip("torch")
+    groups = [(96, 160, 2), (130, 72, 1), (33, 40, 2)]
+    runs = []
+    for chunk in (0, 1, 2):
+        opt, params = H.make(groups, precision="fp32", mode=mode, chunk_matrices=chunk, **cfg)
+        for t in (1, 2, 3):
+            grads = [H.to_device_grad((0.02 * np.random.default_rng([gi, t, 19]).standard_normal((b, m, n)))
+                                      .astype(np.float32), "f32") for gi, (m, n, b) in enumerate(groups)]
+            opt.step(grads=grads)
+        torch.cuda.synchronize()
+        runs.append([{k: v.cpu().numpy().copy() for k, v in st.items()} | {"W": params[gi].cpu().numpy().copy()}
+                     for gi, st in enumerate(opt.state)])
+        del opt, params
+    for other in runs[1:]:
+        for a, b in zip(runs[0], other):
+            for k in a:
+                assert np.array_equal(a[k], b[k]), (mode, cfg, k)
+
+
 @pytest.mark.parametrize("mode", ["okls", "muon"])
 def test_step_replays_bitwise_from_a_hip_graph(mode):
     """okls_step captured into a HIP graph (its side-stream fork and join
