@@ -1276,55 +1276,101 @@ struct Planner {
       add_gemm(L, ph, false, 1, 1);
       add_gemm(L, pb, false, 1, 0);
     }
-    // 8. Jacobi sweeps: reset, then per sweep every round's solve and apply, and a check
-    const int first = static_cast<int>(jac_jobs.size());
-    int solve_blk = 0, apply_blk = 0, part = 0, max_rounds = 0;
+    // 8. Jacobi sweeps: reset, then per sweep every round's solve and apply, and a check.
+    // The factors are independent: with more than one, they form two sets of
+    // near-equal cost (d^3, largest first) whose launches run on two streams,
+    // so one set's solve (a few hundred latency-bound workgroups) overlaps the
+    // other set's apply.
+    const int nset = (!single_chain && facs.size() > 1) ? 2 : 1;
+    std::vector<std::vector<size_t>> sets(nset);
+    {
+      std::vector<size_t> order(facs.size());
+      for (size_t f = 0; f < order.size(); ++f) order[f] = f;
+      std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return facs[x]->d > facs[y]->d; });
+      std::vector<double> load(nset, 0.0);
+      for (size_t f : order) {
+        const int b = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+        sets[b].push_back(f);
+        load[b] += std::pow(static_cast<double>(facs[f]->d), 3.0);
+      }
+    }
     double sweep_flops = 0.0, sweep_bytes = 0.0;
-    for (size_t f = 0; f < facs.size(); ++f) {
-      const FacBufs& F = *facs[f];
-      JacJob j{};
-      j.B = ws_ref(F.B32); j.V = fbasis[f]; j.d = F.d; j.nb = jac_blocks(F.d); j.npairs = j.nb / 2;
-      j.btiles = j.npairs * (j.npairs + 1) / 2; j.vrows = (F.d + kJp - 1) / kJp;
-      j.jbuf = static_cast<int64_t>(F.jbuf); j.part = part; j.flag = static_cast<int32_t>(f);
-      j.solve_begin = solve_blk; j.apply_begin = apply_blk;
-      // the rotations and the basis are fp32: the basis' own residual stops
-      // near u sqrt(d) (measured at d = 2816: 8e-6 of ||L|| from the eighth
-      // sweep of a cold start on), so the stop is the larger of jacobi_tol
-      // and 2^-23 sqrt(d) (6.3e-6 at d = 2816); sweeps below it only shrink
-      // B's off-diagonal, not the basis' error
-      j.tol = std::max(cfg.jacobi_tol, static_cast<float>(std::ldexp(std::sqrt(static_cast<double>(F.d)), -23)));
-      solve_blk += j.npairs;
-      apply_blk += j.btiles + j.vrows * j.npairs;
-      part += j.btiles;
-      max_rounds = std::max(max_rounds, j.nb - 1);
-      const double tile = static_cast<double>(kJp) * kJp * kJp;   // one 64^3 product
-      sweep_flops += (j.nb - 1) * (2.0 * tile * 2.0 * j.btiles + 2.0 * tile * j.vrows * j.npairs);
-      // per round: B and V read and written once, the rotations written and read
-      sweep_bytes += (j.nb - 1) * (16.0 * F.d * F.d + 8.0 * j.npairs * kJp * kJp);
-      jac_jobs.push_back(j);
+    std::vector<std::vector<LaunchRec>> jl(nset);
+    int part_base = 0, flag_base = 0;
+    for (int st = 0; st < nset; ++st) {
+      std::sort(sets[st].begin(), sets[st].end());
+      const int first = static_cast<int>(jac_jobs.size());
+      int solve_blk = 0, apply_blk = 0, part = 0, max_rounds = 0;
+      for (size_t q = 0; q < sets[st].size(); ++q) {
+        const size_t f = sets[st][q];
+        const FacBufs& F = *facs[f];
+        JacJob j{};
+        j.B = ws_ref(F.B32); j.V = fbasis[f]; j.d = F.d; j.nb = jac_blocks(F.d); j.npairs = j.nb / 2;
+        j.btiles = j.npairs * (j.npairs + 1) / 2; j.vrows = (F.d + kJp - 1) / kJp;
+        j.jbuf = static_cast<int64_t>(F.jbuf); j.part = part; j.flag = static_cast<int32_t>(q);
+        j.solve_begin = solve_blk; j.apply_begin = apply_blk;
+        // the rotations and the basis are fp32: the basis' own residual stops
+        // near u sqrt(d) (measured at d = 2816: 8e-6 of ||L|| from the eighth
+        // sweep of a cold start on), so the stop is the larger of jacobi_tol
+        // and 2^-23 sqrt(d) (6.3e-6 at d = 2816); sweeps below it only shrink
+        // B's off-diagonal, not the basis' error
+        j.tol = std::max(cfg.jacobi_tol, static_cast<float>(std::ldexp(std::sqrt(static_cast<double>(F.d)), -23)));
+        solve_blk += j.npairs;
+        apply_blk += j.btiles + j.vrows * j.npairs;
+        part += j.btiles;
+        max_rounds = std::max(max_rounds, j.nb - 1);
+        const double tile = static_cast<double>(kJp) * kJp * kJp;   // one 64^3 product
+        sweep_flops += (j.nb - 1) * (2.0 * tile * 2.0 * j.btiles + 2.0 * tile * j.vrows * j.npairs);
+        // per round: B and V read and written once, the rotations written and read
+        sweep_bytes += (j.nb - 1) * (16.0 * F.d * F.d + 8.0 * j.npairs * kJp * kJp);
+        jac_jobs.push_back(j);
+      }
+      const int count = static_cast<int>(sets[st].size());
+      const size_t part_off = jac_part_rel + static_cast<size_t>(part_base) * 2 * sizeof(float);
+      const size_t flag_off = jac_flag_rel + static_cast<size_t>(flag_base) * sizeof(int32_t);
+      auto jac = [&](int kind, int round, int nblocks) {
+        LaunchRec r;
+        r.type = L_JAC;
+        r.cat = CAT_EIG;
+        r.first = first;
+        r.count = count;
+        r.jac_kind = kind;
+        r.round = round;
+        r.nblocks = nblocks;
+        r.jac_part = part_off;
+        r.jac_flag = flag_off;
+        r.stream = st;
+        jl[st].push_back(r);
+      };
+      jac(JAC_RESET, 0, 1);
+      for (int sw = 0; sw < cfg.jacobi_sweeps; ++sw) {
+        for (int rd = 0; rd < max_rounds; ++rd) {
+          jac(JAC_SOLVE, rd, solve_blk);
+          jac(JAC_APPLY, rd, apply_blk);
+        }
+        jac(JAC_CHECK, 0, count);
+      }
+      part_base += part;
+      flag_base += count;
     }
     step_flops[CAT_EIG] += cfg.jacobi_sweeps * sweep_flops;
     step_bytes[CAT_EIG] += cfg.jacobi_sweeps * sweep_bytes;
-    auto jac = [&](int kind, int round, int nblocks) {
-      LaunchRec r;
-      r.type = L_JAC;
-      r.cat = CAT_EIG;
-      r.first = first;
-      r.count = static_cast<int>(facs.size());
-      r.jac_kind = kind;
-      r.round = round;
-      r.nblocks = nblocks;
-      r.jac_part = jac_part_rel;
-      r.jac_flag = jac_flag_rel;
-      L.push_back(r);
-    };
-    jac(JAC_RESET, 0, 1);
-    for (int sw = 0; sw < cfg.jacobi_sweeps; ++sw) {
-      for (int rd = 0; rd < max_rounds; ++rd) {
-        jac(JAC_SOLVE, rd, solve_blk);
-        jac(JAC_APPLY, rd, apply_blk);
-      }
-      jac(JAC_CHECK, 0, static_cast<int>(facs.size()));
+    if (nset > 1) {
+      LaunchRec fork;
+      fork.type = L_FORK;
+      L.push_back(fork);
+    }
+    // issue the sets' launches interleaved, so both streams have work queued
+    for (size_t i = 0;; ++i) {
+      bool any = false;
+      for (int st = 0; st < nset; ++st)
+        if (i < jl[st].size()) { L.push_back(jl[st][i]); any = true; }
+      if (!any) break;
+    }
+    if (nset > 1) {
+      LaunchRec join;
+      join.type = L_JOIN;
+      L.push_back(join);
     }
     // 9. one Newton-Schulz step towards the nearest orthogonal matrix,
     // Q <- Q (3 I - Q^T Q) / 2, split-fp16 (fp32-accurate) whatever the
