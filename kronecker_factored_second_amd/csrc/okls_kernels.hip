@@ -1169,14 +1169,31 @@ __global__ __launch_bounds__(kSymThreads) void sym_kernel(SymArgs a) {
   float* P = reinterpret_cast<float*>(resolve(J.p, a.ws, a.user));
   const size_t d = static_cast<size_t>(J.d);
   const int r0 = ti * kSymTile, c0 = tj * kSymTile;
-  for (int k = threadIdx.x; k < kSymTile * kSymTile; k += kSymThreads) {
-    const int r = k / kSymTile, c = k % kSymTile;
-    const bool in_a = r0 + r < J.d && c0 + c < J.d, in_b = c0 + r < J.d && r0 + c < J.d;
-    tA[r][c] = in_a ? P[(r0 + r) * d + c0 + c] : 0.0f;
-    tB[r][c] = in_b ? P[(c0 + r) * d + r0 + c] : 0.0f;
+  half_t* dst = J.dst16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(J.dst16, a.ws, a.user)) : nullptr;
+  // rows of four: 16-byte fp32 and 8-byte fp16 accesses when every row
+  // start is aligned (d, the copy's stride and lo offset multiples of 4)
+  const bool vec = (d & 3) == 0 && (reinterpret_cast<uintptr_t>(P) & 15) == 0 &&
+                   (dst == nullptr || ((J.ld16 & 3) == 0 && (J.lo16 & 3) == 0 && (reinterpret_cast<uintptr_t>(dst) & 7) == 0));
+  constexpr int Q = kSymTile / 4;              // quads per tile row
+  if (vec) {
+    for (int k = threadIdx.x; k < kSymTile * Q; k += kSymThreads) {
+      const int r = k / Q, c = (k % Q) * 4;
+      float4 x = float4{0.0f, 0.0f, 0.0f, 0.0f}, y = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      // d is a multiple of 4, so a quad is wholly inside or wholly outside
+      if (r0 + r < J.d && c0 + c < J.d) x = *reinterpret_cast<const float4*>(P + (r0 + r) * d + c0 + c);
+      if (c0 + r < J.d && r0 + c < J.d) y = *reinterpret_cast<const float4*>(P + (c0 + r) * d + r0 + c);
+      tA[r][c] = x.x; tA[r][c + 1] = x.y; tA[r][c + 2] = x.z; tA[r][c + 3] = x.w;
+      tB[r][c] = y.x; tB[r][c + 1] = y.y; tB[r][c + 2] = y.z; tB[r][c + 3] = y.w;
+    }
+  } else {
+    for (int k = threadIdx.x; k < kSymTile * kSymTile; k += kSymThreads) {
+      const int r = k / kSymTile, c = k % kSymTile;
+      const bool in_a = r0 + r < J.d && c0 + c < J.d, in_b = c0 + r < J.d && r0 + c < J.d;
+      tA[r][c] = in_a ? P[(r0 + r) * d + c0 + c] : 0.0f;
+      tB[r][c] = in_b ? P[(c0 + r) * d + r0 + c] : 0.0f;
+    }
   }
   __syncthreads();
-  half_t* dst = J.dst16.kind != REF_NONE ? reinterpret_cast<half_t*>(resolve(J.dst16, a.ws, a.user)) : nullptr;
   const float sc = dst != nullptr ? a.scal[J.scale_slot] : 1.0f;
   auto put = [&](size_t gr, size_t gc, float v) {
     if (gr < d && gc < d) P[gr * d + gc] = v;
@@ -1188,15 +1205,41 @@ __global__ __launch_bounds__(kSymThreads) void sym_kernel(SymArgs a) {
       if (J.write_lo) q[J.lo16] = static_cast<half_t>(y - static_cast<float>(h));
     }
   };
-  // positions beyond d (the copy's padding) get zeros: the tiles hold zeros there
-  for (int k = threadIdx.x; k < kSymTile * kSymTile; k += kSymThreads) {
-    const int r = k / kSymTile, c = k % kSymTile;
-    put(r0 + r, c0 + c, 0.5f * (tA[r][c] + tB[c][r]));
-  }
-  if (ti == tj) return;
-  for (int k = threadIdx.x; k < kSymTile * kSymTile; k += kSymThreads) {
-    const int r = k / kSymTile, c = k % kSymTile;
-    put(c0 + r, r0 + c, 0.5f * (tB[r][c] + tA[c][r]));
+  // (gr, gc .. gc + 3) from the symmetrised values v; the copy's padding
+  // (positions beyond d) gets the zeros the tiles hold there
+  auto put4 = [&](size_t gr, size_t gc, const float (&v)[4]) {
+    if (gr < d && gc < d) *reinterpret_cast<float4*>(P + gr * d + gc) = float4{v[0], v[1], v[2], v[3]};
+    if (dst != nullptr) {
+      half4_t h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y = v[e] * sc;
+        h[e] = static_cast<half_t>(y);
+        l[e] = static_cast<half_t>(y - static_cast<float>(h[e]));
+      }
+      half_t* q = dst + gr * J.ld16 + gc;
+      *reinterpret_cast<half4_t*>(q) = h;
+      if (J.write_lo) *reinterpret_cast<half4_t*>(q + J.lo16) = l;
+    }
+  };
+  for (int half_pass = 0; half_pass < (ti == tj ? 1 : 2); ++half_pass) {
+    // pass 0: tile (ti, tj) = (A + B^T) / 2; pass 1: its mirror (tj, ti)
+    const int gr0 = half_pass == 0 ? r0 : c0, gc0 = half_pass == 0 ? c0 : r0;
+    if (vec) {
+      for (int k = threadIdx.x; k < kSymTile * Q; k += kSymThreads) {
+        const int r = k / Q, c = (k % Q) * 4;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = half_pass == 0 ? 0.5f * (tA[r][c + e] + tB[c + e][r]) : 0.5f * (tB[r][c + e] + tA[c + e][r]);
+        put4(gr0 + r, gc0 + c, v);
+      }
+    } else {
+      for (int k = threadIdx.x; k < kSymTile * kSymTile; k += kSymThreads) {
+        const int r = k / kSymTile, c = k % kSymTile;
+        put(gr0 + r, gc0 + c, half_pass == 0 ? 0.5f * (tA[r][c] + tB[c][r]) : 0.5f * (tB[r][c] + tA[c][r]));
+      }
+    }
   }
 }
 
@@ -1911,6 +1954,12 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
   }
 }
 
+// threads of a Gram-Schmidt block (a sketch is one block).  1024 threads
+// measured slower than 256 (17.8 against 13.7 ms per launch on the
+// 1.2B-class workload): the wider block reductions and barriers of every
+// column cost more than the shorter row walks save
+constexpr int kOrthThreads = 256;
+
 // Block sum of one float (all threads get the result).
 __device__ __forceinline__ float block_sum256(float v, float* red) {
 #pragma unroll
@@ -1928,31 +1977,44 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // or zero) is replaced by a column of the Gaussian fallback and
 // orthogonalised again.  One workgroup per job; the projections of a pass
 // are one wave per finished column, lanes over the rows.
-__global__ __launch_bounds__(256) void nys_orth_kernel(NysOrthArgs a) {
+__global__ __launch_bounds__(kOrthThreads) void nys_orth_kernel(NysOrthArgs a) {
+  constexpr int NWV = kOrthThreads / 64;
   __shared__ float coef[kNysMaxK];
-  __shared__ float part[4][16];
-  __shared__ float red[4];
+  __shared__ float part[NWV][16];
+  __shared__ float red[NWV];
+  // the block's sum of one float, fixed order (all threads get it)
+  auto bsum = [&](float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) t += red[w];
+    return t;
+  };
   const NysOrthJob J = a.jobs[blockIdx.x];
   float* Y = reinterpret_cast<float*>(resolve(J.Y, a.ws, a.user));
   const float* F = reinterpret_cast<const float*>(resolve(J.fb, a.ws, a.user));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   auto col_norm2 = [&](int j) {
     float s = 0.0f;
-    for (int r = threadIdx.x; r < J.d; r += 256) {
+    for (int r = threadIdx.x; r < J.d; r += kOrthThreads) {
       const float v = Y[static_cast<size_t>(r) * J.ld + j];
       s += v * v;
     }
-    return block_sum256(s, red);
+    return bsum(s);
   };
   auto project_out = [&](int j) {       // y_j <- y_j - Q_{<j} (Q_{<j}^T y_j)
     // the coefficients 16 at a time: every thread walks its rows, reading
     // each row's 16 entries as one contiguous run, then a fixed-order
-    // reduction over the wave and the four waves
+    // reduction over the wave and the waves of the block
     for (int c0 = 0; c0 < j; c0 += 16) {
       float s[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) s[c] = 0.0f;
-      for (int r = threadIdx.x; r < J.d; r += 256) {
+      for (int r = threadIdx.x; r < J.d; r += kOrthThreads) {
         const float* row = Y + static_cast<size_t>(r) * J.ld;
         const float yj = row[j];
 #pragma unroll
@@ -1969,11 +2031,15 @@ __global__ __launch_bounds__(256) void nys_orth_kernel(NysOrthArgs a) {
         for (int c = 0; c < 16; ++c) part[wave][c] = s[c];
       }
       __syncthreads();
-      if (threadIdx.x < 16 && c0 + static_cast<int>(threadIdx.x) < j)
-        coef[c0 + threadIdx.x] = (part[0][threadIdx.x] + part[1][threadIdx.x]) + (part[2][threadIdx.x] + part[3][threadIdx.x]);
+      if (threadIdx.x < 16 && c0 + static_cast<int>(threadIdx.x) < j) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) t += part[w][threadIdx.x];
+        coef[c0 + threadIdx.x] = t;
+      }
       __syncthreads();
     }
-    for (int r = threadIdx.x; r < J.d; r += 256) {
+    for (int r = threadIdx.x; r < J.d; r += kOrthThreads) {
       float* row = Y + static_cast<size_t>(r) * J.ld;
       float v = row[j];
       for (int c = 0; c < j; ++c) v -= row[c] * coef[c];
@@ -1993,13 +2059,13 @@ __global__ __launch_bounds__(256) void nys_orth_kernel(NysOrthArgs a) {
       }
       if (now > 1e-12f * n0 && now > 0.0f) {
         const float inv = 1.0f / sqrtf(now);
-        for (int r = threadIdx.x; r < J.d; r += 256) Y[static_cast<size_t>(r) * J.ld + j] *= inv;
+        for (int r = threadIdx.x; r < J.d; r += kOrthThreads) Y[static_cast<size_t>(r) * J.ld + j] *= inv;
         __syncthreads();
         break;
       }
       // dependent: take the fallback column and try once more
       const int fc = (j + J.fb_shift) % J.k;
-      for (int r = threadIdx.x; r < J.d; r += 256)
+      for (int r = threadIdx.x; r < J.d; r += kOrthThreads)
         Y[static_cast<size_t>(r) * J.ld + j] = attempt == 0 ? F[static_cast<size_t>(r) * J.ldf + fc] : (r == j ? 1.0f : 0.0f);
       __syncthreads();
     }
@@ -2364,7 +2430,7 @@ hipError_t launch_thin(const ThinArgs& a, int ta, int mom, int n_blocks, hipStre
 
 hipError_t launch_nys_orth(const NysOrthArgs& a, hipStream_t s) {
   if (a.n_jobs <= 0) return hipSuccess;
-  nys_orth_kernel<<<dim3(a.n_jobs), dim3(256), 0, s>>>(a);
+  nys_orth_kernel<<<dim3(a.n_jobs), dim3(kOrthThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
