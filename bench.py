@@ -502,11 +502,12 @@ def main():
     ns_tflops = ns["flops"] / (ns["busy_ms"] * 1e-3) / 1e12 if ns["busy_ms"] > 0 else 0.0
     nys_roofline = None
     if mode == "nystrom":
-        # every step's preconditioning (thin_kernel launches and the weight
-        # update's gemm32_kernel) streams the m x n data three times: bound by HBM
+        # every step's preconditioning (thin_kernel launches: the momentum
+        # with X = N U_b, U_a^T N, the weight update) streams the m x n data
+        # three times: bound by HBM
         wb = prof["whiten_gemm"]
         ach = wb["bytes"] / (wb["busy_ms"] * 1e-3) / 1e9 if wb["busy_ms"] > 0 else 0.0
-        nys_roofline = {"kernel": "thin_kernel + gemm32_kernel (per-step preconditioning)", "bound": "hbm",
+        nys_roofline = {"kernel": "thin_kernel (per-step preconditioning)", "bound": "hbm",
                         "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                         "traffic": None,
                         "method": "algorithmic bytes of the per-step preconditioning launches (the momentum read and "

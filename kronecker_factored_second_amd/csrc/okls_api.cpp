@@ -142,7 +142,7 @@ struct MatBufs {
 };
 
 enum LaunchType { L_STAT = 0, L_CAST = 1, L_GEMM = 2, L_FORK = 3, L_JOIN = 4, L_SYM = 5, L_ADAM = 6, L_JAC = 7,
-                  L_G32 = 8, L_NORTH = 9, L_NSMALL = 10, L_NELEM = 11, L_THIN = 12 };
+                  L_NORTH = 9, L_NSMALL = 10, L_NELEM = 11, L_THIN = 12 };
 
 struct LaunchRec {
   int type = L_STAT;
@@ -159,6 +159,7 @@ struct LaunchRec {
   int jac_kind = 0, round = 0;  // L_JAC: JacKind and tournament round
   size_t jac_part = 0, jac_flag = 0;   // L_JAC: workspace offsets of the chunk's partials and flags
   int thin_ta = 0, thin_mom = 0;       // L_THIN: the launch's operand form
+  int thin_cbm = 1;                    // L_THIN: 32-column blocks of C the kernel holds (1, 2 or 4)
 };
 
 enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4, CAT_EIG = 5 };
@@ -195,7 +196,7 @@ struct okls_handle {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   size_t off_probs = 0, off_tiles = 0, off_stat = 0, off_cast = 0, off_sym = 0, off_scal = 0, off_part = 0, off_flag = 0;
-  size_t off_adam = 0, off_jac = 0, off_g32 = 0, off_north = 0, off_nsmall = 0, off_nelem = 0, off_thin = 0;
+  size_t off_adam = 0, off_jac = 0, off_north = 0, off_nsmall = 0, off_nelem = 0, off_thin = 0;
   size_t off_resid = 0, resid_floats = 0;   // Newton-Schulz residual partials
   struct Resid { int mat, side, chain, first, count; };
   std::vector<Resid> resid;
@@ -308,6 +309,21 @@ okls_status check_groups(int n_groups, const okls_group_desc* g) {
 // ---------------------------------------------------------------------------
 // Planner
 // ---------------------------------------------------------------------------
+// The planner's description of a product C = alpha op(A) B (+ beta C),
+// op(A) M x K (A stored K x M when ta), rows of C scaled by an optional
+// vector; every such product runs as a ThinJob (N <= kThinMaxR).
+struct ProdDesc {
+  Ref A, B, C;
+  int32_t M, N, K;
+  int32_t lda, ldb, ldc;   // row strides in elements
+  int32_t ta;              // op(A) = A^T (A stored K x M)
+  int32_t a_fmt;           // GradFmt of A (fp32 except a gradient)
+  float alpha;
+  int32_t alpha_slot;      // >= 0: alpha is multiplied by scal[alpha_slot]
+  float beta;              // 0: C is written without being read
+  Ref rowscale;            // REF_NONE, or M floats: row i of the product times rowscale[i]
+};
+
 struct Planner {
   const okls_config& cfg;
   const std::vector<okls_group_desc>& groups;
@@ -328,7 +344,6 @@ struct Planner {
   std::vector<SymJob> sym_jobs;
   std::vector<AdamJob> adam_jobs;
   std::vector<JacJob> jac_jobs;
-  std::vector<Gemm32Prob> g32_jobs;
   std::vector<NysOrthJob> north_jobs;
   std::vector<NysSmallJob> nsmall_jobs;
   std::vector<NysElemJob> nelem_jobs;
@@ -1411,57 +1426,33 @@ struct Planner {
 
   // ---- Nystrom mode (the Clean paper's low-rank factors, Algorithm 3, and
   // the preconditioner of its eq. 9-10), fp32 throughout.
-  Gemm32Prob g32(Ref A, int lda, int ta, Ref B, int ldb, int tb, Ref C, int ldc, int M, int N, int K, float alpha,
-                 float beta) {
-    Gemm32Prob p{};
-    p.A = A; p.B = B; p.C = C; p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ta = ta; p.tb = tb;
+  ProdDesc prod(Ref A, int lda, int ta, Ref B, int ldb, Ref C, int ldc, int M, int N, int K, float alpha,
+                float beta) {
+    ProdDesc p{};
+    p.A = A; p.B = B; p.C = C; p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ta = ta;
     p.M = M; p.N = N; p.K = K; p.alpha = alpha; p.beta = beta; p.alpha_slot = -1; p.rowscale = no_ref();
-    p.a_fmt = p.b_fmt = GF_F32;
-    p.wupd = 0; p.aux = no_ref(); p.c0 = 0.0f;
+    p.a_fmt = GF_F32;
     return p;
-  }
-  void add_g32(std::vector<LaunchRec>& L, const std::vector<Gemm32Prob>& ps, int cat) {
-    if (ps.empty()) return;
-    LaunchRec r;
-    r.type = L_G32;
-    r.cat = cat;
-    r.first = static_cast<int>(g32_jobs.size());
-    int blk = 0;
-    for (Gemm32Prob p : ps) {
-      const int tm = (p.M + kG32Tile - 1) / kG32Tile, tn = (p.N + kG32Tile - 1) / kG32Tile;
-      p.tiles_n = tn;
-      p.blk_begin = blk;
-      blk += tm * tn;
-      step_flops[cat] += 2.0 * p.M * p.N * p.K;
-      // operands once; C written (and read when beta != 0); the weight
-      // update reads W and the added matrix and writes W
-      step_bytes[cat] += 4.0 * (static_cast<double>(p.M) * p.K + static_cast<double>(p.K) * p.N +
-                                (p.wupd ? 3.0 : p.beta != 0.0f ? 2.0 : 1.0) * p.M * p.N);
-      g32_jobs.push_back(p);
-    }
-    r.count = static_cast<int>(ps.size());
-    r.nblocks = blk;
-    L.push_back(r);
   }
   // C = alpha op(A) B + beta C with op(A) Mo x K (ta: A stored K x Mo), B K x R, C Mo x R (ot: R x Mo)
   ThinJob thin(Ref A, int lda, int ta, Ref B, int ldb, Ref C, int ldc, int ot, int Mo, int K, int R, float alpha,
                float beta) {
     ThinJob j{};
-    j.A = A; j.B = B; j.C = C; j.M = j.Nout = no_ref();
+    j.A = A; j.B = B; j.C = C; j.M = j.Nout = no_ref(); j.wupd = 0; j.aux = no_ref(); j.c0 = 0.0f;
     j.lda = lda; j.ldb = ldb; j.ldc = ldc; j.ldn = 0; j.ta = ta; j.ot = ot; j.a_fmt = GF_F32; j.mom = 0;
     j.Mo = Mo; j.K = K; j.R = R; j.alpha = alpha; j.beta = beta; j.alpha_slot = -1; j.rowscale = no_ref();
     return j;
   }
-  // a thin product written in the gemm32 form (op(B) = B, N <= kThinMaxR)
-  ThinJob thin_of(const Gemm32Prob& p) {
+  // a product description as a thin job (N <= kThinMaxR)
+  ThinJob thin_of(const ProdDesc& p) {
     ThinJob j = thin(p.A, p.lda, p.ta, p.B, p.ldb, p.C, p.ldc, 0, p.M, p.K, p.N, p.alpha, p.beta);
     j.a_fmt = p.a_fmt; j.alpha_slot = p.alpha_slot; j.rowscale = p.rowscale;
     return j;
   }
   // products of both operand forms: one launch per form
-  void add_thin_any(std::vector<LaunchRec>& L, const std::vector<Gemm32Prob>& ps, int cat) {
+  void add_thin_any(std::vector<LaunchRec>& L, const std::vector<ProdDesc>& ps, int cat) {
     std::vector<ThinJob> by_ta[2];
-    for (const Gemm32Prob& p : ps) by_ta[p.ta ? 1 : 0].push_back(thin_of(p));
+    for (const ProdDesc& p : ps) by_ta[p.ta ? 1 : 0].push_back(thin_of(p));
     add_thin(L, by_ta[0], cat);
     add_thin(L, by_ta[1], cat);
   }
@@ -1474,6 +1465,7 @@ struct Planner {
     r.first = static_cast<int>(thin_jobs.size());
     r.thin_ta = js.front().ta;
     r.thin_mom = js.front().mom;
+    for (const ThinJob& j : js) r.thin_cbm = std::max(r.thin_cbm, j.R <= 32 ? 1 : j.R <= 64 ? 2 : 4);
     int blk = 0;
     for (ThinJob j : js) {
       j.blk_begin = blk;
@@ -1482,7 +1474,7 @@ struct Planner {
       // op(A) once (gradient bytes as stored), B once, C once (twice when read)
       const double ae = j.a_fmt == GF_F32 ? 4.0 : 2.0;
       double b = ae * j.Mo * static_cast<double>(j.K) + 4.0 * j.K * static_cast<double>(j.R) +
-                 4.0 * (j.beta != 0.0f ? 2.0 : 1.0) * j.Mo * static_cast<double>(j.R);
+                 4.0 * (j.wupd ? 3.0 : j.beta != 0.0f ? 2.0 : 1.0) * j.Mo * static_cast<double>(j.R);
       if (j.mom) b += 12.0 * j.Mo * static_cast<double>(j.K);   // M read and written, N written
       step_bytes[cat] += b;
       thin_jobs.push_back(j);
@@ -1572,27 +1564,25 @@ struct Planner {
       // A Omega = beta2 U (Lambda U^T Omega) + (1 - beta2) G (G^T Omega) on the
       // left, with G^T and G exchanged on the right (eq. 8).
       for (int pass = 0; pass <= cfg.nys_passes; ++pass) {
-        std::vector<Gemm32Prob> p1, p2, p3;
+        std::vector<ProdDesc> p1, p2, p3;
         std::vector<NysOrthJob> po;
         for (const MatBufs& mb : mats)
           for (int sd = 0; sd < 2; ++sd) {
             const MatBufs::NysSide& S = mb.ns[sd];
             const int other = sd == 0 ? mb.n : mb.m;
-            Gemm32Prob t1 = g32(uref(mb, sd), S.r, 1, ws_ref(S.Om), S.k, 0, ws_ref(S.T1), S.k, S.r, S.k, S.d, b2, 0.0f);
+            ProdDesc t1 = prod(uref(mb, sd), S.r, 1, ws_ref(S.Om), S.k, ws_ref(S.T1), S.k, S.r, S.k, S.d, b2, 0.0f);
             t1.rowscale = lref(mb, sd);
             p1.push_back(t1);
             // left: T2 = G^T Omega (n x k); right: T2 = G Omega (m x k)
-            Gemm32Prob t2 = g32(user_ref(REF_G, mb.group, goff(mb)), mb.n, sd == 0 ? 1 : 0, ws_ref(S.Om), S.k, 0,
-                                ws_ref(S.T2), S.k, other, S.k, S.d, 1.0f, 0.0f);
+            ProdDesc t2 = prod(user_ref(REF_G, mb.group, goff(mb)), mb.n, sd == 0 ? 1 : 0, ws_ref(S.Om), S.k, ws_ref(S.T2), S.k, other, S.k, S.d, 1.0f, 0.0f);
             t2.a_fmt = gfmt(mb);
             p1.push_back(t2);
             // Y = (1 - beta2) G T2 (left) or G^T T2 (right)
-            Gemm32Prob y = g32(user_ref(REF_G, mb.group, goff(mb)), mb.n, sd == 0 ? 0 : 1, ws_ref(S.T2), S.k, 0,
-                               ws_ref(S.Yb), S.k, S.d, S.k, other, 1.0f - b2, 0.0f);
+            ProdDesc y = prod(user_ref(REF_G, mb.group, goff(mb)), mb.n, sd == 0 ? 0 : 1, ws_ref(S.T2), S.k, ws_ref(S.Yb), S.k, S.d, S.k, other, 1.0f - b2, 0.0f);
             y.a_fmt = gfmt(mb);
             p2.push_back(y);
             // Y += U T1
-            p3.push_back(g32(uref(mb, sd), S.r, 0, ws_ref(S.T1), S.k, 0, ws_ref(S.Yb), S.k, S.d, S.k, S.r, 1.0f, 1.0f));
+            p3.push_back(prod(uref(mb, sd), S.r, 0, ws_ref(S.T1), S.k, ws_ref(S.Yb), S.k, S.d, S.k, S.r, 1.0f, 1.0f));
             if (pass < cfg.nys_passes) po.push_back(NysOrthJob{ws_ref(S.Yb), pref(mb, sd), S.d, S.k, S.k, S.k, 0});
           }
         add_thin_any(L, p1, CAT_NS);
@@ -1629,19 +1619,19 @@ struct Planner {
         r.nblocks = r.count;
         L.push_back(r);
       };
-      std::vector<Gemm32Prob> pg, pf1, pf2, pt, pu;
+      std::vector<ProdDesc> pg, pf1, pf2, pt, pu;
       for (const MatBufs& mb : mats)
         for (int sd = 0; sd < 2; ++sd) {
           const MatBufs::NysSide& S = mb.ns[sd];
-          pg.push_back(g32(ws_ref(S.Yb), S.k, 1, ws_ref(S.Yb), S.k, 0, ws_ref(S.gram), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
-          pg.push_back(g32(ws_ref(S.Om), S.k, 1, ws_ref(S.Yb), S.k, 0, ws_ref(S.cm), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
-          pf1.push_back(g32(ws_ref(S.Yb), S.k, 0, ws_ref(S.cm), S.k, 0, ws_ref(S.Fb), S.k, S.d, S.k, S.k, 1.0f, 0.0f));
-          Gemm32Prob f2 = g32(ws_ref(S.Om), S.k, 0, ws_ref(S.cm), S.k, 0, ws_ref(S.Fb), S.k, S.d, S.k, S.k, 1.0f, 1.0f);
+          pg.push_back(prod(ws_ref(S.Yb), S.k, 1, ws_ref(S.Yb), S.k, ws_ref(S.gram), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
+          pg.push_back(prod(ws_ref(S.Om), S.k, 1, ws_ref(S.Yb), S.k, ws_ref(S.cm), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
+          pf1.push_back(prod(ws_ref(S.Yb), S.k, 0, ws_ref(S.cm), S.k, ws_ref(S.Fb), S.k, S.d, S.k, S.k, 1.0f, 0.0f));
+          ProdDesc f2 = prod(ws_ref(S.Om), S.k, 0, ws_ref(S.cm), S.k, ws_ref(S.Fb), S.k, S.d, S.k, S.k, 1.0f, 1.0f);
           f2.alpha_slot = S.s_nuu;
           pf2.push_back(f2);
-          pt.push_back(g32(ws_ref(S.Fb), S.k, 1, ws_ref(S.Fb), S.k, 0, ws_ref(S.gram), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
-          pt.push_back(g32(ws_ref(S.Fb), S.k, 1, uref(mb, sd), S.r, 0, ws_ref(S.zp), S.r, S.k, S.r, S.d, 1.0f, 0.0f));
-          pu.push_back(g32(ws_ref(S.Fb), S.k, 0, ws_ref(S.kout), S.r, 0, uref(mb, sd), S.r, S.d, S.r, S.k, 1.0f, 0.0f));
+          pt.push_back(prod(ws_ref(S.Fb), S.k, 1, ws_ref(S.Fb), S.k, ws_ref(S.gram), S.k, S.k, S.k, S.d, 1.0f, 0.0f));
+          pt.push_back(prod(ws_ref(S.Fb), S.k, 1, uref(mb, sd), S.r, ws_ref(S.zp), S.r, S.k, S.r, S.d, 1.0f, 0.0f));
+          pu.push_back(prod(ws_ref(S.Fb), S.k, 0, ws_ref(S.kout), S.r, uref(mb, sd), S.r, S.d, S.r, S.k, 1.0f, 0.0f));
         }
       add_thin_any(L, pg, CAT_NS);
       small(1);
@@ -1677,8 +1667,13 @@ struct Planner {
       }
       add_nelem(L, e1);
     }
-    std::vector<ThinJob> t1, t2, t3, t4;
-    std::vector<Gemm32Prob> fin;
+    std::vector<ThinJob> t1, t2, t3, t4, fin;
+    double wupd_a_bytes = 0.0;
+    // the weight update's column chunk: two 32-column blocks per thin block
+    // (its two-block kernel holds fewer registers than the four-block one,
+    // so more blocks share a CU; the m x (r_a + r_b) operand is re-read per
+    // chunk from L2)
+    constexpr int kWupdCols = 64;
     for (const MatBufs& mb : mats) {
       const int ra = mb.ns[0].r, rb = mb.ns[1].r, ld = rb + ra;
       // X = N U_b with N = momentum(G, M)
@@ -1694,17 +1689,25 @@ struct Planner {
       // Z += (U_a^T X) (U_b E_b)^T, as Z^T += (U_b E_b) Ct: op(A) = ((U_b E_b)^T)^T from ZB's first rows
       t4.push_back(thin(ws_ref(mb.ZB), mb.n, 1, ws_ref(mb.Ct), ra, ws_ref(mb.ZB + static_cast<size_t>(rb) * mb.n * 4),
                         mb.n, 1, mb.n, rb, ra, 1.0f, 1.0f));
-      // W <- decay W - lr c_shape (N + [X | U_a E_a] [(U_b E_b)^T ; Z])
-      Gemm32Prob f = g32(ws_ref(mb.XU), ld, 0, ws_ref(mb.ZB), mb.n, 0, user_ref(REF_W, mb.group, moff(mb)), mb.n,
-                         mb.m, mb.n, ld, 1.0f, 0.0f);
-      f.wupd = 1; f.aux = ws_ref(mb.N32); f.c0 = update_scale(mb);
-      fin.push_back(f);
+      // W <- decay W - lr c_shape (N + [X | U_a E_a] [(U_b E_b)^T ; Z]): a
+      // thin product per kWupdCols columns of W (op(A) = [X | U_a E_a],
+      // m x (r_a + r_b)), the update fused into its epilogue
+      for (int j0 = 0; j0 < mb.n; j0 += kWupdCols) {
+        const size_t cb = static_cast<size_t>(j0) * 4;
+        ThinJob f = thin(ws_ref(mb.XU), ld, 0, ws_ref(mb.ZB + cb), mb.n, user_ref(REF_W, mb.group, moff(mb) + cb),
+                         mb.n, 0, mb.m, ld, std::min(kWupdCols, mb.n - j0), 1.0f, 0.0f);
+        f.wupd = 1; f.aux = ws_ref(mb.N32 + cb); f.c0 = update_scale(mb);
+        fin.push_back(f);
+      }
+      wupd_a_bytes += 4.0 * mb.m * ld * (((mb.n + kWupdCols - 1) / kWupdCols) - 1);
     }
     add_thin(L, t1, CAT_WHITEN);
     add_thin(L, t2, CAT_WHITEN);
     add_thin(L, t3, CAT_WHITEN);
     add_thin(L, t4, CAT_WHITEN);
-    add_g32(L, fin, CAT_WHITEN);
+    add_thin(L, fin, CAT_WHITEN);
+    // algorithmic bytes: [X | U_a E_a] once per matrix, not once per chunk
+    step_bytes[CAT_WHITEN] -= wupd_a_bytes;
   }
 
   // Whether a second concurrent Newton-Schulz chain pays for this chunk.
@@ -2150,32 +2153,15 @@ struct Planner {
               if (!fits(p.aux, (static_cast<size_t>(p.M - 1) * p.ldaux + p.N) * 4)) return false;
             }
           }
-        } else if (r.type == L_G32) {
-          if (r.first < 0 || r.first + r.count > static_cast<int>(g32_jobs.size())) return false;
-          int blk = 0;
-          for (int j = r.first; j < r.first + r.count; ++j) {
-            const Gemm32Prob& q = g32_jobs[j];
-            if (q.M < 1 || q.N < 1 || q.K < 1 || q.blk_begin != blk || q.tiles_n != (q.N + kG32Tile - 1) / kG32Tile) return false;
-            blk += ((q.M + kG32Tile - 1) / kG32Tile) * q.tiles_n;
-            const int ar = q.ta ? q.K : q.M, ac = q.ta ? q.M : q.K, br = q.tb ? q.N : q.K, bc = q.tb ? q.K : q.N;
-            if (q.lda < ac || q.ldb < bc || q.ldc < q.N) return false;
-            const size_t ae = q.a_fmt == GF_F32 ? 4 : 2, be = q.b_fmt == GF_F32 ? 4 : 2;
-            if (!fits(q.A, (static_cast<size_t>(ar - 1) * q.lda + ac) * ae)) return false;
-            if (!fits(q.B, (static_cast<size_t>(br - 1) * q.ldb + bc) * be)) return false;
-            if (!fits(q.C, (static_cast<size_t>(q.M - 1) * q.ldc + q.N) * 4)) return false;
-            if (q.rowscale.kind != REF_NONE && !fits(q.rowscale, static_cast<size_t>(q.M) * 4)) return false;
-            if (q.alpha_slot >= 0 && !slot_ok(q.alpha_slot)) return false;
-            if (q.wupd && (q.C.kind != REF_W || !fits(q.aux, (static_cast<size_t>(q.M - 1) * q.ldc + q.N) * 4))) return false;
-          }
-          if (blk != r.nblocks) return false;
         } else if (r.type == L_THIN) {
           if (r.first < 0 || r.first + r.count > static_cast<int>(thin_jobs.size())) return false;
           if (r.thin_ta < 0 || r.thin_ta > 1 || r.thin_mom < 0 || r.thin_mom > 1 || (r.thin_ta && r.thin_mom)) return false;
+          if (r.thin_cbm != 1 && r.thin_cbm != 2 && r.thin_cbm != 4) return false;
           int blk = 0;
           for (int j = r.first; j < r.first + r.count; ++j) {
             const ThinJob& q = thin_jobs[j];
             if (q.ta != r.thin_ta || q.mom != r.thin_mom || q.ot < 0 || q.ot > 1) return false;
-            if (q.Mo < 1 || q.K < 1 || q.R < 1 || q.R > kThinMaxR || q.blk_begin != blk) return false;
+            if (q.Mo < 1 || q.K < 1 || q.R < 1 || q.R > 32 * r.thin_cbm || q.blk_begin != blk) return false;
             blk += (q.Mo + kThinTile - 1) / kThinTile;
             const int ar = q.ta ? q.K : q.Mo, ac = q.ta ? q.Mo : q.K;
             const int cr = q.ot ? q.R : q.Mo, cc = q.ot ? q.Mo : q.R;
@@ -2190,6 +2176,10 @@ struct Planner {
             }
             if (q.alpha_slot >= 0 && !slot_ok(q.alpha_slot)) return false;
             if (q.rowscale.kind != REF_NONE && (q.ot != 0 || !fits(q.rowscale, static_cast<size_t>(q.Mo) * 4))) return false;
+            if (q.wupd != 0 && q.wupd != 1) return false;
+            if (q.wupd && (q.ot != 0 || q.ta != 0 || q.mom != 0 || q.C.kind != REF_W || q.rowscale.kind != REF_NONE ||
+                           !fits(q.aux, (static_cast<size_t>(q.Mo - 1) * q.ldc + q.R) * 4)))
+              return false;
           }
           if (blk != r.nblocks) return false;
         } else if (r.type == L_NORTH) {
@@ -2388,7 +2378,7 @@ struct Planner {
 };
 
 struct WsLayout {
-  size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, adam = 0, jac = 0, g32 = 0, north = 0, nsmall = 0,
+  size_t probs = 0, tiles = 0, stat = 0, cast = 0, sym = 0, adam = 0, jac = 0, north = 0, nsmall = 0,
          nelem = 0, thin = 0, scal = 0, part = 0, flag = 0, resid = 0, chunk = 0, total = 0;
 };
 
@@ -2405,7 +2395,6 @@ WsLayout ws_layout(Planner& P) {
   w.sym = take(P.sym_jobs.size() * sizeof(SymJob));
   w.adam = take(P.adam_jobs.size() * sizeof(AdamJob));
   w.jac = take(P.jac_jobs.size() * sizeof(JacJob));
-  w.g32 = take(P.g32_jobs.size() * sizeof(Gemm32Prob));
   w.north = take(P.north_jobs.size() * sizeof(NysOrthJob));
   w.nsmall = take(P.nsmall_jobs.size() * sizeof(NysSmallJob));
   w.nelem = take(P.nelem_jobs.size() * sizeof(NysElemJob));
@@ -2508,7 +2497,7 @@ okls_status okls_plan_query(const okls_config* cfg, int n_groups, const okls_gro
     for (const std::vector<LaunchRec>& L : cs)
       for (const LaunchRec& r : L)
         n += (r.type == L_STAT || r.type == L_CAST || r.type == L_GEMM || r.type == L_SYM || r.type == L_ADAM ||
-              r.type == L_JAC || r.type == L_G32 || r.type == L_NORTH || r.type == L_NSMALL || r.type == L_NELEM ||
+              r.type == L_JAC || r.type == L_NORTH || r.type == L_NSMALL || r.type == L_NELEM ||
               r.type == L_THIN);
     return n;
   };
@@ -2566,7 +2555,7 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   P.plan(w.chunk);
   if (!P.validate() || P.probs.size() != sizing.probs.size() || P.chunk_bytes != sizing.chunk_bytes ||
       P.adam_jobs.size() != sizing.adam_jobs.size() || P.jac_jobs.size() != sizing.jac_jobs.size() ||
-      P.g32_jobs.size() != sizing.g32_jobs.size() || P.nelem_jobs.size() != sizing.nelem_jobs.size() ||
+      P.nelem_jobs.size() != sizing.nelem_jobs.size() ||
       P.thin_jobs.size() != sizing.thin_jobs.size())
     return OKLS_ERR_UNSUPPORTED;
   // the regions the tables and slots occupy must end before the chunk buffers
@@ -2585,7 +2574,6 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   h->off_sym = w.sym;
   h->off_adam = w.adam;
   h->off_jac = w.jac;
-  h->off_g32 = w.g32;
   h->off_north = w.north;
   h->off_nsmall = w.nsmall;
   h->off_nelem = w.nelem;
@@ -2651,7 +2639,6 @@ okls_status init_impl(okls_handle** out, const okls_config* cfg, int n_groups, c
   up(w.sym, P.sym_jobs.data(), P.sym_jobs.size() * sizeof(SymJob));
   up(w.adam, P.adam_jobs.data(), P.adam_jobs.size() * sizeof(AdamJob));
   up(w.jac, P.jac_jobs.data(), P.jac_jobs.size() * sizeof(JacJob));
-  up(w.g32, P.g32_jobs.data(), P.g32_jobs.size() * sizeof(Gemm32Prob));
   up(w.north, P.north_jobs.data(), P.north_jobs.size() * sizeof(NysOrthJob));
   up(w.nsmall, P.nsmall_jobs.data(), P.nsmall_jobs.size() * sizeof(NysSmallJob));
   up(w.nelem, P.nelem_jobs.data(), P.nelem_jobs.size() * sizeof(NysElemJob));
@@ -2894,16 +2881,6 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.ws = ws;
         a.user = user;
         e = launch_jacobi(a, r.jac_kind, r.nblocks, rs);
-      } else if (r.type == L_G32) {
-        Gemm32Args a;
-        a.jobs = reinterpret_cast<const Gemm32Prob*>(ws + h->off_g32) + r.first;
-        a.n_jobs = r.count;
-        a.scal = scal;
-        a.lr = lr_update;
-        a.decay = static_cast<float>(decay);
-        a.ws = ws;
-        a.user = user;
-        e = launch_gemm32(a, r.nblocks, rs);
       } else if (r.type == L_THIN) {
         ThinArgs a;
         a.jobs = reinterpret_cast<const ThinJob*>(ws + h->off_thin) + r.first;
@@ -2911,9 +2888,11 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.scal = scal;
         a.beta1 = static_cast<float>(b1);
         a.s_t = static_cast<float>(s_t);
+        a.lr = lr_update;
+        a.decay = static_cast<float>(decay);
         a.ws = ws;
         a.user = user;
-        e = launch_thin(a, r.thin_ta, r.thin_mom, r.nblocks, rs);
+        e = launch_thin(a, r.thin_ta, r.thin_mom, r.thin_cbm, r.nblocks, rs);
       } else if (r.type == L_NORTH) {
         NysOrthArgs a;
         a.jobs = reinterpret_cast<const NysOrthJob*>(ws + h->off_north) + r.first;

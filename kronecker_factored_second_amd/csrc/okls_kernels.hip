@@ -1646,123 +1646,41 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_check_kernel(JacArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Nystrom low-rank factors (Gemm32Prob, NysOrthJob, NysSmallJob, NysElemJob)
+// Nystrom low-rank factors (ThinJob, NysOrthJob, NysSmallJob, NysElemJob)
 // ---------------------------------------------------------------------------
-// C = alpha op(A) op(B) (row i times rowscale[i]) + beta C in fp32: 64 x 64
-// output tiles, K in steps of 16 through LDS, a 4 x 4 block per thread.
-__global__ __launch_bounds__(256) void gemm32_kernel(Gemm32Args a) {
-  __shared__ __attribute__((aligned(16))) float As[kG32K][kG32Tile + 4];   // As[kk][i] = op(A)[i0 + i][k0 + kk]
-  __shared__ __attribute__((aligned(16))) float Bs[kG32K][kG32Tile + 4];   // Bs[kk][j] = op(B)[k0 + kk][j0 + j]
-  const int gb = blockIdx.x;
-  const Gemm32Prob P = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
-  const int lb = gb - P.blk_begin;
-  const int ti = lb / P.tiles_n, tj = lb - ti * P.tiles_n;
-  const int i0 = ti * kG32Tile, j0 = tj * kG32Tile;
-  const char* A = resolve(P.A, a.ws, a.user);
-  const char* B = resolve(P.B, a.ws, a.user);
-  float* C = reinterpret_cast<float*>(resolve(P.C, a.ws, a.user));
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int k0 = 0; k0 < P.K; k0 += kG32K) {
-    for (int e = threadIdx.x; e < kG32Tile * kG32K; e += 256) {
-      // the fastest-varying index walks the operand's contiguous dimension
-      const int i = P.ta ? e % kG32Tile : e / kG32K, kk = P.ta ? e / kG32Tile : e % kG32K;
-      const int gi = i0 + i, gk = k0 + kk;
-      float v = 0.0f;
-      if (gi < P.M && gk < P.K)
-        v = grad_elem(A, P.ta ? static_cast<size_t>(gk) * P.lda + gi : static_cast<size_t>(gi) * P.lda + gk, P.a_fmt);
-      As[kk][i] = v;
-      const int j = P.tb ? e / kG32K : e % kG32Tile, kb = P.tb ? e % kG32K : e / kG32Tile;
-      const int gj = j0 + j, gkb = k0 + kb;
-      float w = 0.0f;
-      if (gj < P.N && gkb < P.K)
-        w = grad_elem(B, P.tb ? static_cast<size_t>(gj) * P.ldb + gkb : static_cast<size_t>(gkb) * P.ldb + gj, P.b_fmt);
-      Bs[kb][j] = w;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kG32K; ++kk) {
-      const float4 av = *reinterpret_cast<const float4*>(&As[kk][4 * ty]);
-      const float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][4 * tx]);
-      const float x[4] = {av.x, av.y, av.z, av.w}, y[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(x[i], y[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-  const float alpha = P.alpha * (P.alpha_slot >= 0 ? a.scal[P.alpha_slot] : 1.0f);
-  const float* rs = P.rowscale.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(P.rowscale, a.ws, a.user)) : nullptr;
-  if (P.wupd) {
-    // W <- decay W - lr c0 (alpha acc + X), X the unpreconditioned part of the
-    // update (same layout as W); a row's four entries as one 16-byte access
-    const float* X = reinterpret_cast<const float*>(resolve(P.aux, a.ws, a.user));
-    const float s = -(a.lr * P.c0);
-    const bool vec = (P.ldc & 3) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(X)) & 15) == 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gi = i0 + 4 * ty + i;
-      if (gi >= P.M) continue;
-      const int gj = j0 + 4 * tx;
-      const size_t o = static_cast<size_t>(gi) * P.ldc + gj;
-      if (vec && gj + 3 < P.N) {
-        const float4 x = *reinterpret_cast<const float4*>(X + o);
-        float4 w = *reinterpret_cast<const float4*>(C + o);
-        w.x = __builtin_fmaf(a.decay, w.x, s * __builtin_fmaf(alpha, acc[i][0], x.x));
-        w.y = __builtin_fmaf(a.decay, w.y, s * __builtin_fmaf(alpha, acc[i][1], x.y));
-        w.z = __builtin_fmaf(a.decay, w.z, s * __builtin_fmaf(alpha, acc[i][2], x.z));
-        w.w = __builtin_fmaf(a.decay, w.w, s * __builtin_fmaf(alpha, acc[i][3], x.w));
-        *reinterpret_cast<float4*>(C + o) = w;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (gj + j < P.N) C[o + j] = __builtin_fmaf(a.decay, C[o + j], s * __builtin_fmaf(alpha, acc[i][j], X[o + j]));
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gi = i0 + 4 * ty + i;
-    if (gi >= P.M) continue;
-    const float ri = rs != nullptr ? alpha * rs[gi] : alpha;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gj = j0 + 4 * tx + j;
-      if (gj >= P.N) continue;
-      float* c = C + static_cast<size_t>(gi) * P.ldc + gj;
-      *c = P.beta != 0.0f ? __builtin_fmaf(P.beta, *c, ri * acc[i][j]) : ri * acc[i][j];
-    }
-  }
-}
-
 // Thin fp32 products (ThinJob): kThinTile rows of op(A) per block, K in
 // stages of kThinK through LDS, the next stage's global loads in registers
-// during the current stage's FMAs, every thread a 4 x 4 block of each
-// 32-column block of C.  The stage of op(A) is held k-major (As[k][i]); the
-// 4-row group index of row i is XOR-swizzled by k / 4, so that the
-// transposing stores of a row-major A (eight quads of one row per eight
-// lanes) fall in distinct banks while the FMA loop's 16-byte reads stay
-// contiguous per group.
-__device__ __forceinline__ int thin_sw(int k, int i) { return ((((i >> 2) ^ (k >> 2)) & 31) << 2) | (i & 3); }
+// during the current stage's matrix-core products.  Each of the four waves
+// owns 32 rows of the block and runs v_mfma_f32_32x32x2_f32 per 32-column
+// block of C (fp32 operands, fp32 accumulation: the plain fp32 products,
+// at twice the rate of the unpacked fp32 FMA).  op(A) and B are held in LDS
+// with k contiguous per row (rows of op(A), columns of B), LK floats per
+// row, and the 4-wide k groups of row i XOR-swizzled by i / 8: the 16-byte
+// fragment reads are then free of bank conflicts and the transposing
+// stores two-way at most.  An MFMA's two k slots take, for the lanes of
+// half h, k = 8 p + 4 h + e of group p and element e, the same map on both
+// operands, so each 16-byte read feeds four MFMAs.
+constexpr int kThinLK = 40;
+__device__ __forceinline__ int thin_at(int i, int k) {
+  return i * kThinLK + ((((k >> 2) ^ (i >> 3)) & 7) << 2) + (k & 3);
+}
 
 __device__ __forceinline__ float4 quad_any(const char* p, size_t o, int fmt) {
   return fmt == GF_F32 ? grad_quad<GF_F32>(p, o) : fmt == GF_BF16 ? grad_quad<GF_BF16>(p, o) : grad_quad<GF_F16>(p, o);
 }
 __device__ __forceinline__ float& f4_at(float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
-template <int TA, bool MOM>
+// CBM: the most 32-column blocks of C a job of the launch has (1, 2 or 4);
+// the narrower forms hold fewer accumulators and less of B's stage, so more
+// blocks fit on a CU.
+template <int TA, bool MOM, int CBM>
 __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
-  constexpr int TM = kThinTile, KC = kThinK, LA = TM + 4, LB = kThinMaxR + 4;
-  static_assert(TM == 128 && KC == 32 && kThinMaxR == 128, "the load and FMA maps below assume these sizes");
+  constexpr int TM = kThinTile, KC = kThinK, LK = kThinLK;
+  static_assert(TM == 128 && KC == 32 && kThinMaxR == 128, "the load and fragment maps below assume these sizes");
   static_assert(!MOM || TA == 0, "the momentum operand is row-major");
-  __shared__ __attribute__((aligned(16))) float As[KC][LA];
-  __shared__ __attribute__((aligned(16))) float Bs[KC][LB];
+  static_assert(CBM == 1 || CBM == 2 || CBM == 4, "one, two or four column blocks");
+  __shared__ __attribute__((aligned(16))) float As[TM * LK];
+  __shared__ __attribute__((aligned(16))) float Bs[32 * CBM * LK];
   const int gb = blockIdx.x;
   const ThinJob J = a.jobs[find_job(a.jobs, a.n_jobs, gb)];
   const int i0 = (gb - J.blk_begin) * TM;
@@ -1775,8 +1693,8 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
     Mp = reinterpret_cast<float*>(resolve(J.M, a.ws, a.user));
     Np = reinterpret_cast<float*>(resolve(J.Nout, a.ws, a.user));
   }
-  const int t = threadIdx.x, rg = t & 31, cg = t >> 5;
-  const int CB = (J.R + 31) >> 5;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, hl = lane >> 5, ln = lane & 31;
+  const int CB = min((J.R + 31) >> 5, CBM);
   const uintptr_t amask = J.a_fmt == GF_F32 ? 15 : 7;
   bool avec = (J.lda & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & amask) == 0;
   if constexpr (MOM)
@@ -1785,52 +1703,38 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
   const bool cvec = (J.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
   const float b1 = a.beta1, b1c = 1.0f - a.beta1, st = a.s_t;
 
-  float4 ra[4], rb[4];
-  float acc[4][4][4];
+  float4 ra[4], rb[CBM];
+  float4 rm[MOM ? 4 : 1];
+  floatx16 acc[CBM];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < CBM; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[c][i][j] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
 
   // stage k0 into registers: op(A) as 1024 quads (TA 0: 128 rows x 8 quads
-  // along k; TA 1: 32 k-rows x 32 quads along i), B as 32 k-rows x 32 quads
+  // along k; TA 1: 32 k-rows x 32 quads along i), B as 32 k-rows x 32 quads.
+  // In the momentum form ra takes G and rm takes M; the momentum update and
+  // its stores wait for lstore, so that these loads stay in flight during
+  // the current stage's products.
   auto gload = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int q = t + 256 * j;
       float4 v = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      float4 m = float4{0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (TA == 0) {
         const int row = q >> 3, gk = k0 + (q & 7) * 4, gi = i0 + row;
         if (gi < J.Mo && gk < J.K) {
           const size_t o = static_cast<size_t>(gi) * J.lda + gk;
           if (avec && gk + 3 < J.K) {
             v = quad_any(A, o, J.a_fmt);
-            if constexpr (MOM) {
-              float4 m = *reinterpret_cast<const float4*>(Mp + o);
-              float4 mn, nv;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                f4_at(mn, e) = b1 * f4_at(m, e) + b1c * f4_at(v, e);
-                f4_at(nv, e) = st * (b1 * f4_at(mn, e) + b1c * f4_at(v, e));
-              }
-              *reinterpret_cast<float4*>(Mp + o) = mn;
-              *reinterpret_cast<float4*>(Np + static_cast<size_t>(gi) * J.ldn + gk) = nv;
-              v = nv;
-            }
+            if constexpr (MOM) m = *reinterpret_cast<const float4*>(Mp + o);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if (gk + e >= J.K) break;
-              float g = grad_elem(A, o + e, J.a_fmt);
-              if constexpr (MOM) {
-                const float mn = b1 * Mp[o + e] + b1c * g;
-                Mp[o + e] = mn;
-                g = st * (b1 * mn + b1c * g);
-                Np[static_cast<size_t>(gi) * J.ldn + gk + e] = g;
-              }
-              f4_at(v, e) = g;
+              f4_at(v, e) = grad_elem(A, o + e, J.a_fmt);
+              if constexpr (MOM) f4_at(m, e) = Mp[o + e];
             }
           }
         }
@@ -1848,8 +1752,14 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
         }
       }
       ra[j] = v;
+      if constexpr (MOM) rm[j] = m;
+    }
+    // B: 32 k-rows x 8 CBM quads, CBM per thread
+#pragma unroll
+    for (int j = 0; j < CBM; ++j) {
+      const int q = t + 256 * j;
       float4 w = float4{0.0f, 0.0f, 0.0f, 0.0f};
-      const int bk = k0 + (q >> 5), bc = (q & 31) * 4;
+      const int bk = k0 + q / (8 * CBM), bc = (q % (8 * CBM)) * 4;
       if (bk < J.K && bc < J.R) {
         const float* bp = B + static_cast<size_t>(bk) * J.ldb + bc;
         if (bvec && bc + 3 < J.R) {
@@ -1863,81 +1773,180 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
       rb[j] = w;
     }
   };
+  // the momentum form: M' = beta1 M + (1 - beta1) G and N = s_t (beta1 M' +
+  // (1 - beta1) G) for the staged quads of stage k0, M' and N stored, N
+  // left in ra (zeros outside the matrix stay zeros)
+  auto momentum = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = t + 256 * j;
+      const int row = q >> 3, gk = k0 + (q & 7) * 4, gi = i0 + row;
+      float4 mn, nv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f4_at(mn, e) = b1 * f4_at(rm[j], e) + b1c * f4_at(ra[j], e);
+        f4_at(nv, e) = st * (b1 * f4_at(mn, e) + b1c * f4_at(ra[j], e));
+      }
+      if (gi < J.Mo && gk < J.K) {
+        const size_t o = static_cast<size_t>(gi) * J.lda + gk;
+        const size_t on = static_cast<size_t>(gi) * J.ldn + gk;
+        if (avec && gk + 3 < J.K) {
+          *reinterpret_cast<float4*>(Mp + o) = mn;
+          *reinterpret_cast<float4*>(Np + on) = nv;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (gk + e >= J.K) break;
+            Mp[o + e] = f4_at(mn, e);
+            Np[on + e] = f4_at(nv, e);
+          }
+        }
+      }
+      ra[j] = nv;
+    }
+  };
   auto lstore = [&]() {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int q = t + 256 * j;
       if constexpr (TA == 0) {
         const int row = q >> 3, kq = (q & 7) * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) As[kq + e][thin_sw(kq + e, row)] = f4_at(ra[j], e);
+        *reinterpret_cast<float4*>(&As[thin_at(row, kq)]) = ra[j];
       } else {
         const int kr = q >> 5, c4 = (q & 31) * 4;
-        *reinterpret_cast<float4*>(&As[kr][thin_sw(kr, c4)]) = ra[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[thin_at(c4 + e, kr)] = f4_at(ra[j], e);
       }
-      *reinterpret_cast<float4*>(&Bs[q >> 5][(q & 31) * 4]) = rb[j];
+    }
+    // B's columns as rows
+#pragma unroll
+    for (int j = 0; j < CBM; ++j) {
+      const int q = t + 256 * j;
+      const int bk = q / (8 * CBM), bc = (q % (8 * CBM)) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Bs[thin_at(bc + e, bk)] = f4_at(rb[j], e);
     }
   };
 
   const int nk = (J.K + KC - 1) / KC;
+  const int arow = 32 * wave + ln;
   gload(0);
   for (int sidx = 0; sidx < nk; ++sidx) {
+    if constexpr (MOM) momentum(sidx * KC);
     __syncthreads();                  // the previous stage's reads are done
     lstore();
     __syncthreads();
     if (sidx + 1 < nk) gload((sidx + 1) * KC);
-#pragma unroll 4
-    for (int kk = 0; kk < KC; ++kk) {
-      float4 av = *reinterpret_cast<const float4*>(&As[kk][thin_sw(kk, 4 * rg)]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+    for (int p = 0; p < KC / 8; ++p) {
+      const int kg = 8 * p + 4 * hl;
+      const float4 av = *reinterpret_cast<const float4*>(&As[thin_at(arow, kg)]);
+#pragma unroll
+      for (int c = 0; c < CBM; ++c) {
         if (c >= CB) break;
-        float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][32 * c + 4 * cg]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[c][i][j] = __builtin_fmaf(f4_at(av, i), f4_at(bv, j), acc[c][i][j]);
+        const float4 bv = *reinterpret_cast<const float4*>(&Bs[thin_at(32 * c + ln, kg)]);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc[c], 0, 0, 0);
       }
     }
   }
 
+  // lane (h, n) holds column 32 c + n of C and, for element r of the
+  // accumulator, row 32 wave + 8 (r / 4) + 4 h + r % 4 of the block
   const float alpha0 = J.alpha * (J.alpha_slot >= 0 ? a.scal[J.alpha_slot] : 1.0f);
   const float* rsc = J.rowscale.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(J.rowscale, a.ws, a.user)) : nullptr;
   const float beta = J.beta;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (c >= CB) break;
-    const int c0 = 32 * c + 4 * cg;
-    if (J.ot == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gi = i0 + 4 * rg + i;
-        if (gi >= J.Mo) break;
-        const float alpha = rsc != nullptr ? alpha0 * rsc[gi] : alpha0;
-        float* cp = C + static_cast<size_t>(gi) * J.ldc + c0;
-        if (cvec && c0 + 3 < J.R) {
-          float4 o = float4{alpha * acc[c][i][0], alpha * acc[c][i][1], alpha * acc[c][i][2], alpha * acc[c][i][3]};
-          if (beta != 0.0f) {
-            const float4 old = *reinterpret_cast<const float4*>(cp);
-            o.x = __builtin_fmaf(beta, old.x, o.x); o.y = __builtin_fmaf(beta, old.y, o.y);
-            o.z = __builtin_fmaf(beta, old.z, o.z); o.w = __builtin_fmaf(beta, old.w, o.w);
+  // (weight-update jobs are plain row-major products: the planner's checks)
+  if constexpr (TA == 0 && !MOM) {
+    if (J.wupd) {
+      // W <- decay W - lr c0 (alpha acc + X), X the unpreconditioned part of
+      // the update (W's layout, stride ldc).  Per 32-column block the
+      // accumulators pass through LDS (As is free after the last stage), so
+      // that each thread then updates four 16-byte row quads of W, all eight
+      // W and X loads in flight before the first store.
+      const float* X = reinterpret_cast<const float*>(resolve(J.aux, a.ws, a.user));
+      const float sc = -(a.lr * J.c0);
+      constexpr int LS = 36;                 // staging row stride (floats)
+      static_assert(TM * LS <= TM * LK, "the staging fits As");
+      const bool wvec = (J.ldc & 3) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(X)) & 15) == 0;
+  #pragma unroll
+      for (int c = 0; c < CBM; ++c) {
+        if (c >= CB) break;
+        __syncthreads();                     // As is no longer read (products, or the previous block)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) As[(32 * wave + 8 * (r >> 2) + 4 * hl + (r & 3)) * LS + ln] = acc[c][r];
+        __syncthreads();
+        float4 w[4], x[4];
+  #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int qd = t + 256 * u, row = qd >> 3, cq = (qd & 7) * 4;
+          const int gi = i0 + row, gj = 32 * c + cq;
+          w[u] = x[u] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+          if (gi < J.Mo) {
+            const size_t o = static_cast<size_t>(gi) * J.ldc + gj;
+            if (wvec && gj + 3 < J.R) {
+              w[u] = *reinterpret_cast<const float4*>(C + o);
+              x[u] = *reinterpret_cast<const float4*>(X + o);
+            } else {
+  #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (gj + e < J.R) {
+                  f4_at(w[u], e) = C[o + e];
+                  f4_at(x[u], e) = X[o + e];
+                }
+            }
           }
-          *reinterpret_cast<float4*>(cp) = o;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (c0 + j < J.R) cp[j] = beta != 0.0f ? __builtin_fmaf(beta, cp[j], alpha * acc[c][i][j]) : alpha * acc[c][i][j];
+        }
+  #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int qd = t + 256 * u, row = qd >> 3, cq = (qd & 7) * 4;
+          const int gi = i0 + row, gj = 32 * c + cq;
+          if (gi >= J.Mo) continue;
+          float4 v = *reinterpret_cast<const float4*>(&As[row * LS + cq]);
+          float4 o4;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e)
+            f4_at(o4, e) = __builtin_fmaf(a.decay, f4_at(w[u], e), sc * __builtin_fmaf(alpha0, f4_at(v, e), f4_at(x[u], e)));
+          const size_t o = static_cast<size_t>(gi) * J.ldc + gj;
+          if (wvec && gj + 3 < J.R) {
+            *reinterpret_cast<float4*>(C + o) = o4;
+          } else {
+  #pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gj + e < J.R) C[o + e] = f4_at(o4, e);
+          }
         }
       }
-    } else {
-      const float alpha = alpha0;
-      const int r0 = i0 + 4 * rg;
+      return;
+    }
+  }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (c0 + j >= J.R) break;
-        float* cp = C + static_cast<size_t>(c0 + j) * J.ldc + r0;
+  for (int c = 0; c < CBM; ++c) {
+    if (c >= CB) break;
+    const int col = 32 * c + ln;
+    if (col >= J.R) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = i0 + 32 * wave + 8 * g + 4 * hl;
+      if (J.ot == 0) {
+        // lanes n = 0..31 write 32 consecutive columns of one row
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gi = r0 + e;
+          if (gi >= J.Mo) break;
+          const float alpha = rsc != nullptr ? alpha0 * rsc[gi] : alpha0;
+          float* cp = C + static_cast<size_t>(gi) * J.ldc + col;
+          const float v = alpha * acc[c][4 * g + e];
+          *cp = beta != 0.0f ? __builtin_fmaf(beta, *cp, v) : v;
+        }
+      } else {
+        // the transposed output: the lane's four rows are consecutive
+        float* cp = C + static_cast<size_t>(col) * J.ldc + r0;
         if (cvec && r0 + 3 < J.Mo) {
-          float4 o = float4{alpha * acc[c][0][j], alpha * acc[c][1][j], alpha * acc[c][2][j], alpha * acc[c][3][j]};
+          float4 o = float4{alpha0 * acc[c][4 * g], alpha0 * acc[c][4 * g + 1], alpha0 * acc[c][4 * g + 2],
+                            alpha0 * acc[c][4 * g + 3]};
           if (beta != 0.0f) {
             const float4 old = *reinterpret_cast<const float4*>(cp);
             o.x = __builtin_fmaf(beta, old.x, o.x); o.y = __builtin_fmaf(beta, old.y, o.y);
@@ -1946,8 +1955,11 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
           *reinterpret_cast<float4*>(cp) = o;
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (r0 + i < J.Mo) cp[i] = beta != 0.0f ? __builtin_fmaf(beta, cp[i], alpha * acc[c][i][j]) : alpha * acc[c][i][j];
+          for (int e = 0; e < 4; ++e)
+            if (r0 + e < J.Mo) {
+              const float v = alpha0 * acc[c][4 * g + e];
+              cp[e] = beta != 0.0f ? __builtin_fmaf(beta, cp[e], v) : v;
+            }
         }
       }
     }
@@ -2413,18 +2425,21 @@ hipError_t launch_jacobi(const JacArgs& a, int kind, int n_blocks, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_gemm32(const Gemm32Args& a, int n_blocks, hipStream_t s) {
-  if (n_blocks <= 0) return hipSuccess;
-  gemm32_kernel<<<dim3(n_blocks), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
+template <int CBM>
+void launch_thin_cbm(const ThinArgs& a, int ta, int mom, int n_blocks, hipStream_t s) {
+  const dim3 g(n_blocks), b(256);
+  if (mom) thin_kernel<0, true, CBM><<<g, b, 0, s>>>(a);
+  else if (ta) thin_kernel<1, false, CBM><<<g, b, 0, s>>>(a);
+  else thin_kernel<0, false, CBM><<<g, b, 0, s>>>(a);
 }
 
-hipError_t launch_thin(const ThinArgs& a, int ta, int mom, int n_blocks, hipStream_t s) {
+hipError_t launch_thin(const ThinArgs& a, int ta, int mom, int cbm, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   if (mom && ta) return hipErrorInvalidValue;
-  if (mom) thin_kernel<0, true><<<dim3(n_blocks), dim3(256), 0, s>>>(a);
-  else if (ta) thin_kernel<1, false><<<dim3(n_blocks), dim3(256), 0, s>>>(a);
-  else thin_kernel<0, false><<<dim3(n_blocks), dim3(256), 0, s>>>(a);
+  if (cbm == 1) launch_thin_cbm<1>(a, ta, mom, n_blocks, s);
+  else if (cbm == 2) launch_thin_cbm<2>(a, ta, mom, n_blocks, s);
+  else if (cbm == 4) launch_thin_cbm<4>(a, ta, mom, n_blocks, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -297,8 +297,8 @@ struct JacArgs {
 // ---------------------------------------------------------------------------
 // Nystrom low-rank factors.  All arithmetic is fp32 (the sketches are thin:
 // k = r + p <= kNysMaxK columns), in four kernels:
-//  - gemm32: batched fp32 products C = alpha op(A) op(B) (rows scaled by an
-//    optional vector) + beta C, 64 x 64 tiles from LDS;
+//  - thin: fp32 products with at most kThinMaxR columns on the matrix cores
+//    (ThinJob below), also the momentum with X = N U_b and the weight update;
 //  - nys_orth: thin QR's Q of a d x k matrix in place by classical
 //    Gram-Schmidt with reorthogonalisation, a dependent column replaced by a
 //    column of the refresh's Gaussian matrix;
@@ -308,34 +308,6 @@ struct JacArgs {
 //  - nys_elem: element-wise gather, momentum, column scaling and update.
 // ---------------------------------------------------------------------------
 constexpr int kNysMaxK = 128;
-constexpr int kG32Tile = 64;
-constexpr int kG32K = 16;
-
-struct Gemm32Prob {
-  Ref A, B, C;
-  int32_t M, N, K;
-  int32_t lda, ldb, ldc;   // row strides in elements
-  int32_t ta, tb;          // op(A) = A^T (A stored K x M) / op(B) = B^T (B stored N x K)
-  int32_t a_fmt, b_fmt;    // GradFmt of the operands (fp32 except a gradient)
-  float alpha;
-  int32_t alpha_slot;      // >= 0: alpha is multiplied by scal[alpha_slot]
-  float beta;              // 0: C is written without being read
-  Ref rowscale;            // REF_NONE, or M floats: row i of the product times rowscale[i]
-  int32_t wupd;            // 1: C is the weights W, updated as W <- decay W - lr c0 (alpha op(A) op(B) + aux)
-  Ref aux;                 // wupd: M x N fp32, row stride ldc
-  float c0;
-  int32_t tiles_n;
-  int32_t blk_begin;
-};
-
-struct Gemm32Args {
-  const Gemm32Prob* jobs;
-  int32_t n_jobs;
-  const float* scal;
-  float lr, decay;         // wupd problems
-  char* ws;
-  UserPtrs user;
-};
 
 // Thin fp32 products C = alpha op(A) B (+ beta C) where op(A) is Mo x K (the
 // large operand, streamed once) and B is K x R with R <= kThinMaxR: the sketch
@@ -355,6 +327,9 @@ struct ThinJob {
   float alpha, beta;
   int32_t alpha_slot;      // >= 0: alpha is multiplied by scal[alpha_slot]
   Ref rowscale;            // REF_NONE, or Mo floats: row i of op(A) B times rowscale[i] (ot = 0 only)
+  int32_t wupd;            // 1: C is W (Mo x R, stride ldc): W <- decay W - lr c0 (alpha op(A) B + aux)
+  Ref aux;                 // wupd: Mo x R fp32, stride ldc
+  float c0;                // wupd: the update's shape scale
   int32_t blk_begin;
 };
 
@@ -363,6 +338,7 @@ struct ThinArgs {
   int32_t n_jobs;
   const float* scal;
   float beta1, s_t;        // momentum mode
+  float lr, decay;         // weight-update mode
   char* ws;
   UserPtrs user;
 };
