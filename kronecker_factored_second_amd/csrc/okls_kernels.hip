@@ -1491,10 +1491,44 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_solve_kernel(JacArgs a) {
 // B <- R^T B R on the pair-block tiles (P, Q), P <= Q (the lower tile gets the
 // transpose), and V <- V R on kJp-row chunks of V; every B tile records the
 // squared Frobenius norms of its off-diagonal and diagonal entries (the
-// mirrored tile counted twice).  Each thread computes a 4 x 4 block of the
-// 64 x 64 products from LDS.
+// mirrored tile counted twice).  The 64 x 64 products run on the matrix
+// cores in fp32 (v_mfma_f32_32x32x2_f32): wave w computes the 32 x 32 block
+// (w / 2, w % 2) of each product from LDS operands stored k-major (row k
+// holds the 64 entries of index k), so every fragment read is 32 contiguous
+// floats.  Lane (h, n) of a product holds column n of its block and rows
+// 8 (r / 4) + 4 h + r % 4 for accumulator element r.
+__device__ __forceinline__ floatx16 jac_mfma64(const float (*L)[kJp + 4], const float (*R)[kJp + 4], int m0, int n0,
+                                               int h, int n) {
+  // sum over k of L[k][m0 + m] R[k][n0 + n]: lanes of half h take k = 2 kk + h
+  floatx16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll 8
+  for (int kk = 0; kk < kJp / 2; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(L[2 * kk + h][m0 + n], R[2 * kk + h][n0 + n], acc, 0, 0, 0);
+  return acc;
+}
+
+// Entries (r, c .. c + 3) of a d x d row-major matrix, zeros outside it; c
+// is a multiple of 4 inside one kJb block, so with d a multiple of 4 the
+// quad is wholly inside or wholly outside.
+__device__ __forceinline__ float4 jac_quad(const float* M, size_t r, size_t c, size_t d, bool vec) {
+  float4 v = float4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (r >= d) return v;
+  if (vec) {
+    if (c < d) v = *reinterpret_cast<const float4*>(M + r * d + c);
+  } else {
+    if (c < d) v.x = M[r * d + c];
+    if (c + 1 < d) v.y = M[r * d + c + 1];
+    if (c + 2 < d) v.z = M[r * d + c + 2];
+    if (c + 3 < d) v.w = M[r * d + c + 3];
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
   constexpr int LD = kJp + 4;                      // 16-byte aligned rows
+  static_assert(kJacThreads == 256 && kJp == 64, "four waves, each a 32 x 32 block of a 64 x 64 product");
   __shared__ __attribute__((aligned(16))) float X[kJp][LD];
   __shared__ __attribute__((aligned(16))) float JP[kJp][LD];
   __shared__ __attribute__((aligned(16))) float JQ[kJp][LD];
@@ -1505,23 +1539,8 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
   int t = gb - J.apply_begin;
   const float* jb = reinterpret_cast<const float*>(a.ws + J.jbuf);
   const size_t d = static_cast<size_t>(J.d);
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-  float acc[4][4];
-  auto product = [&](float (*L)[LD], float (*R)[LD]) {   // acc = sum_k L[k][4 tr + i] R[k][4 tc + j]
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-    for (int kk = 0; kk < kJp; ++kk) {
-      const float4 l = *reinterpret_cast<const float4*>(&L[kk][4 * tr]);
-      const float4 r = *reinterpret_cast<const float4*>(&R[kk][4 * tc]);
-      const float lv[4] = {l.x, l.y, l.z, l.w}, rv[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += lv[i] * rv[j];
-    }
-  };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
+  const int m0 = 32 * (wave >> 1), n0 = 32 * (wave & 1);
   if (t < J.btiles) {
     int P = 0, rem = t;
     while (rem >= J.npairs - P) {
@@ -1533,36 +1552,63 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
     circle_pair(a.round, P, J.nb, p1, p2);
     circle_pair(a.round, Q, J.nb, q1, q2);
     float* B = reinterpret_cast<float*>(resolve(J.B, a.ws, a.user));
+    // 16-byte accesses along rows of B: d a multiple of 4 and B 16-byte
+    // aligned (a block's 32 entries then start aligned)
+    const bool vec = (d & 3) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
     const float* jp = jb + static_cast<size_t>(P) * kJp * kJp;
     const float* jq = jb + static_cast<size_t>(Q) * kJp * kJp;
-    for (int e = threadIdx.x; e < kJp * kJp; e += kJacThreads) {
-      const int i = e / kJp, j = e % kJp;
+    // every load of the tile and of both rotations issued before the first
+    // LDS store: quad u is row u / 16, columns 4 (u % 16) .. + 3
+    float4 xv[4], pv[4], qv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
       const size_t gi = pair_index(p1, p2, i), gj = pair_index(q1, q2, j);
-      X[i][j] = (gi < d && gj < d) ? B[gi * d + gj] : 0.0f;
-      JP[i][j] = jp[e];
-      JQ[i][j] = jq[e];
+      xv[v] = jac_quad(B, gi, gj, d, vec);
+      pv[v] = *reinterpret_cast<const float4*>(jp + 4 * u);
+      qv[v] = *reinterpret_cast<const float4*>(jq + 4 * u);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
+      *reinterpret_cast<float4*>(&X[i][j]) = xv[v];
+      *reinterpret_cast<float4*>(&JP[i][j]) = pv[v];
+      *reinterpret_cast<float4*>(&JQ[i][j]) = qv[v];
     }
     __syncthreads();
-    product(JP, X);                                // T = J_P^T X
+    floatx16 acc = jac_mfma64(JP, X, m0, n0, h, n);   // T = J_P^T X
     __syncthreads();
+    // X <- T^T: row k of X holds column k of T (the lane's four rows at once)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)                    // X <- T^T (row c holds column c of T)
-      *reinterpret_cast<float4*>(&X[4 * tc + j][4 * tr]) = float4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(&X[n0 + n][m0 + 8 * g + 4 * h]) =
+          float4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
     __syncthreads();
-    product(X, JQ);                                // Y = T J_Q
+    acc = jac_mfma64(X, JQ, m0, n0, h, n);            // Y = T J_Q
     float off = 0.0f, dg = 0.0f;
     const float wgt = P == Q ? 1.0f : 2.0f;
+    const size_t gj = pair_index(q1, q2, n0 + n);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t gi = pair_index(p1, p2, 4 * tr + i);
+    for (int g = 0; g < 4; ++g) {
+      // rows m0 + 8 g + 4 h + e lie in one kJb block: consecutive in B
+      const size_t gi0 = pair_index(p1, p2, m0 + 8 * g + 4 * h);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const size_t gj = pair_index(q1, q2, 4 * tc + j);
+      for (int e = 0; e < 4; ++e) {
+        const size_t gi = gi0 + e;
         if (gi < d && gj < d) {
-          const float y = acc[i][j];
+          const float y = acc[4 * g + e];
           B[gi * d + gj] = y;
-          if (P != Q) B[gj * d + gi] = y;
           if (gi == gj) dg += y * y; else off += wgt * y * y;
+        }
+      }
+      if (P != Q && gj < d) {                      // the mirrored tile: four consecutive entries of row gj
+        float* row = B + gj * d + gi0;
+        if (vec && gi0 + 3 < d) {
+          *reinterpret_cast<float4*>(row) = float4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (gi0 + e < d) row[e] = acc[4 * g + e];
         }
       }
     }
@@ -1593,23 +1639,31 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
   int q1, q2;
   circle_pair(a.round, Q, J.nb, q1, q2);
   float* V = reinterpret_cast<float*>(resolve(J.V, a.ws, a.user));
+  const bool vec = (d & 3) == 0 && (reinterpret_cast<uintptr_t>(V) & 15) == 0;
   const float* jq = jb + static_cast<size_t>(Q) * kJp * kJp;
   const size_t r0 = static_cast<size_t>(chunk) * kJp;
-  for (int e = threadIdx.x; e < kJp * kJp; e += kJacThreads) {
-    const int i = e / kJp, j = e % kJp;            // X holds V's chunk transposed: X[j][i] = V[r0 + i][col j]
-    const size_t gj = pair_index(q1, q2, j);
-    X[j][i] = (r0 + i < d && gj < d) ? V[(r0 + i) * d + gj] : 0.0f;
-    JQ[i][j] = jq[e];
+  // X holds V's chunk transposed: X[j][i] = V[r0 + i][col j]
+  float4 xv[4], qv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
+    xv[v] = jac_quad(V, r0 + i, pair_index(q1, q2, j), d, vec);
+    qv[v] = *reinterpret_cast<const float4*>(jq + 4 * u);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
+    X[j][i] = xv[v].x; X[j + 1][i] = xv[v].y; X[j + 2][i] = xv[v].z; X[j + 3][i] = xv[v].w;
+    *reinterpret_cast<float4*>(&JQ[i][j]) = qv[v];
   }
   __syncthreads();
-  product(X, JQ);                                  // Y = V_chunk J_Q
+  const floatx16 acc = jac_mfma64(X, JQ, m0, n0, h, n);   // Y = V_chunk J_Q
+  const size_t gj = pair_index(q1, q2, n0 + n);
+  if (gj < d) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const size_t r = r0 + 4 * tr + i;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const size_t gj = pair_index(q1, q2, 4 * tc + j);
-      if (r < d && gj < d) V[r * d + gj] = acc[i][j];
+    for (int r = 0; r < 16; ++r) {
+      const size_t row = r0 + m0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < d) V[row * d + gj] = acc[r];
     }
   }
 }
