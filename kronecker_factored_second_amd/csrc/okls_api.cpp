@@ -1331,7 +1331,7 @@ struct Planner {
         // B's off-diagonal, not the basis' error
         j.tol = std::max(cfg.jacobi_tol, static_cast<float>(std::ldexp(std::sqrt(static_cast<double>(F.d)), -23)));
         solve_blk += j.npairs;
-        apply_blk += j.btiles + j.vrows * j.npairs;
+        apply_blk += (j.btiles + j.vrows * j.npairs + kJacApplyItems - 1) / kJacApplyItems;
         part += j.btiles;
         max_rounds = std::max(max_rounds, j.nb - 1);
         const double tile = static_cast<double>(kJp) * kJp * kJp;   // one 64^3 product
@@ -2250,7 +2250,7 @@ struct Planner {
             if (q.btiles != q.npairs * (q.npairs + 1) / 2 || q.vrows != (q.d + kJp - 1) / kJp) return false;
             if (q.solve_begin != solve || q.apply_begin != apply || q.part != part || q.flag != j - r.first) return false;
             solve += q.npairs;
-            apply += q.btiles + q.vrows * q.npairs;
+            apply += (q.btiles + q.vrows * q.npairs + kJacApplyItems - 1) / kJacApplyItems;
             part += q.btiles;
             const size_t dd = static_cast<size_t>(q.d) * q.d * 4;
             if (!fits(q.B, dd) || !fits(q.V, dd)) return false;

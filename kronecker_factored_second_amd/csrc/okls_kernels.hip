@@ -1491,8 +1491,9 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_solve_kernel(JacArgs a) {
 // B <- R^T B R on the pair-block tiles (P, Q), P <= Q (the lower tile gets the
 // transpose), and V <- V R on kJp-row chunks of V; every B tile records the
 // squared Frobenius norms of its off-diagonal and diagonal entries (the
-// mirrored tile counted twice).  The 64 x 64 products run on the matrix
-// cores in fp32 (v_mfma_f32_32x32x2_f32): wave w computes the 32 x 32 block
+// mirrored tile counted twice).  A block takes kJacApplyItems consecutive
+// tiles, the next one's loads in flight during the current one's products.
+// The 64 x 64 products run on the matrix cores in fp32 (v_mfma_f32_32x32x2_f32): wave w computes the 32 x 32 block
 // (w / 2, w % 2) of each product from LDS operands stored k-major (row k
 // holds the 64 entries of index k), so every fragment read is 32 contiguous
 // floats.  Lane (h, n) of a product holds column n of its block and rows
@@ -1536,46 +1537,108 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
   const int gb = blockIdx.x;
   const JacJob J = a.jobs[find_jac_job<true>(a.jobs, a.n_jobs, gb)];
   if (a.round >= J.nb - 1 || a.flags[J.flag] != 0) return;
-  int t = gb - J.apply_begin;
+  // the block's work items: B tiles 0 .. btiles - 1, then V tiles (chunk, Q)
+  const int n_items = J.btiles + J.vrows * J.npairs;
+  const int it0 = (gb - J.apply_begin) * kJacApplyItems;
+  const int it1 = min(it0 + kJacApplyItems, n_items);
   const float* jb = reinterpret_cast<const float*>(a.ws + J.jbuf);
   const size_t d = static_cast<size_t>(J.d);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
   const int m0 = 32 * (wave >> 1), n0 = 32 * (wave & 1);
-  if (t < J.btiles) {
-    int P = 0, rem = t;
-    while (rem >= J.npairs - P) {
-      rem -= J.npairs - P;
-      ++P;
+  float* B = reinterpret_cast<float*>(resolve(J.B, a.ws, a.user));
+  float* V = reinterpret_cast<float*>(resolve(J.V, a.ws, a.user));
+  // 16-byte accesses along rows: d a multiple of 4 and the matrix 16-byte
+  // aligned (a block's 32 entries then start aligned)
+  const bool bvec = (d & 3) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
+  const bool vvec = (d & 3) == 0 && (reinterpret_cast<uintptr_t>(V) & 15) == 0;
+
+  // item it: B tile (P, Q), P <= Q, row by row; or V chunk `chunk` of pair Q
+  struct Item { int P, Q, chunk; };
+  auto item = [&](int it) __attribute__((always_inline)) {
+    Item r;
+    if (it < J.btiles) {
+      int P = 0, rem = it;
+      while (rem >= J.npairs - P) {
+        rem -= J.npairs - P;
+        ++P;
+      }
+      r.P = P; r.Q = P + rem; r.chunk = -1;
+    } else {
+      const int v = it - J.btiles;
+      r.chunk = v / J.npairs; r.Q = v - r.chunk * J.npairs; r.P = -1;
     }
-    const int Q = P + rem;
-    int p1, p2, q1, q2;
-    circle_pair(a.round, P, J.nb, p1, p2);
-    circle_pair(a.round, Q, J.nb, q1, q2);
-    float* B = reinterpret_cast<float*>(resolve(J.B, a.ws, a.user));
-    // 16-byte accesses along rows of B: d a multiple of 4 and B 16-byte
-    // aligned (a block's 32 entries then start aligned)
-    const bool vec = (d & 3) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
-    const float* jp = jb + static_cast<size_t>(P) * kJp * kJp;
-    const float* jq = jb + static_cast<size_t>(Q) * kJp * kJp;
-    // every load of the tile and of both rotations issued before the first
-    // LDS store: quad u is row u / 16, columns 4 (u % 16) .. + 3
-    float4 xv[4], pv[4], qv[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
-      const size_t gi = pair_index(p1, p2, i), gj = pair_index(q1, q2, j);
-      xv[v] = jac_quad(B, gi, gj, d, vec);
-      pv[v] = *reinterpret_cast<const float4*>(jp + 4 * u);
-      qv[v] = *reinterpret_cast<const float4*>(jq + 4 * u);
+    return r;
+  };
+  // the item's operands into registers: quad u = threadIdx.x + 256 v is
+  // row u / 16, columns 4 (u % 16) .. + 3 (of the B tile, of V's chunk, of
+  // J_P and of J_Q); four named quads each, so that they stay in registers
+  float4 ox0, ox1, ox2, ox3, op0, op1, op2, op3, oq0, oq1, oq2, oq3;
+  auto fetch_quad = [&](const Item& w, int v, float4& x, float4& pq, float4& qq) __attribute__((always_inline)) {
+    const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
+    int c1, c2;
+    circle_pair(a.round, w.Q, J.nb, c1, c2);
+    qq = *reinterpret_cast<const float4*>(jb + static_cast<size_t>(w.Q) * kJp * kJp + 4 * u);
+    if (w.chunk < 0) {
+      int r1, r2;
+      circle_pair(a.round, w.P, J.nb, r1, r2);
+      x = jac_quad(B, pair_index(r1, r2, i), pair_index(c1, c2, j), d, bvec);
+      pq = *reinterpret_cast<const float4*>(jb + static_cast<size_t>(w.P) * kJp * kJp + 4 * u);
+    } else {
+      x = jac_quad(V, static_cast<size_t>(w.chunk) * kJp + i, pair_index(c1, c2, j), d, vvec);
+      pq = float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
-      *reinterpret_cast<float4*>(&X[i][j]) = xv[v];
-      *reinterpret_cast<float4*>(&JP[i][j]) = pv[v];
-      *reinterpret_cast<float4*>(&JQ[i][j]) = qv[v];
+  };
+  auto fetch = [&](const Item& w) __attribute__((always_inline)) {
+    fetch_quad(w, 0, ox0, op0, oq0);
+    fetch_quad(w, 1, ox1, op1, oq1);
+    fetch_quad(w, 2, ox2, op2, oq2);
+    fetch_quad(w, 3, ox3, op3, oq3);
+  };
+  auto stage_quad = [&](bool bt, int v, const float4& x, const float4& pq, const float4& qq) __attribute__((always_inline)) {
+    const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
+    if (bt) {
+      *reinterpret_cast<float4*>(&X[i][j]) = x;
+      *reinterpret_cast<float4*>(&JP[i][j]) = pq;
+    } else {
+      // X holds V's chunk transposed: X[j][i] = V[r0 + i][col j]
+      X[j][i] = x.x; X[j + 1][i] = x.y; X[j + 2][i] = x.z; X[j + 3][i] = x.w;
     }
+    *reinterpret_cast<float4*>(&JQ[i][j]) = qq;
+  };
+
+  if (it0 >= it1) return;
+  Item cur = item(it0);
+  fetch(cur);
+  for (int it = it0; it < it1; ++it) {
+    __syncthreads();                               // the previous item's LDS reads are done
+    const bool bt = cur.chunk < 0;
+    stage_quad(bt, 0, ox0, op0, oq0);
+    stage_quad(bt, 1, ox1, op1, oq1);
+    stage_quad(bt, 2, ox2, op2, oq2);
+    stage_quad(bt, 3, ox3, op3, oq3);
     __syncthreads();
+    const Item w = cur;
+    if (it + 1 < it1) {                            // the next item's loads, in flight during these products
+      cur = item(it + 1);
+      fetch(cur);
+    }
+    int q1, q2;
+    circle_pair(a.round, w.Q, J.nb, q1, q2);
+    const size_t gj = pair_index(q1, q2, n0 + n);
+    if (w.chunk >= 0) {
+      const floatx16 acc = jac_mfma64(X, JQ, m0, n0, h, n);   // Y = V_chunk J_Q
+      if (gj < d) {
+        const size_t r0 = static_cast<size_t>(w.chunk) * kJp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const size_t row = r0 + m0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row < d) V[row * d + gj] = acc[r];
+        }
+      }
+      continue;
+    }
+    int p1, p2;
+    circle_pair(a.round, w.P, J.nb, p1, p2);
     floatx16 acc = jac_mfma64(JP, X, m0, n0, h, n);   // T = J_P^T X
     __syncthreads();
     // X <- T^T: row k of X holds column k of T (the lane's four rows at once)
@@ -1586,8 +1649,7 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
     __syncthreads();
     acc = jac_mfma64(X, JQ, m0, n0, h, n);            // Y = T J_Q
     float off = 0.0f, dg = 0.0f;
-    const float wgt = P == Q ? 1.0f : 2.0f;
-    const size_t gj = pair_index(q1, q2, n0 + n);
+    const float wgt = w.P == w.Q ? 1.0f : 2.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // rows m0 + 8 g + 4 h + e lie in one kJb block: consecutive in B
@@ -1601,9 +1663,9 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
           if (gi == gj) dg += y * y; else off += wgt * y * y;
         }
       }
-      if (P != Q && gj < d) {                      // the mirrored tile: four consecutive entries of row gj
+      if (w.P != w.Q && gj < d) {                  // the mirrored tile: four consecutive entries of row gj
         float* row = B + gj * d + gi0;
-        if (vec && gi0 + 3 < d) {
+        if (bvec && gi0 + 3 < d) {
           *reinterpret_cast<float4*>(row) = float4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
         } else {
 #pragma unroll
@@ -1625,45 +1687,12 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
     if (threadIdx.x == 0) {
       float so = 0.0f, sd = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kJacThreads / 64; ++w) {
-        so += red[2 * w];
-        sd += red[2 * w + 1];
+      for (int q = 0; q < kJacThreads / 64; ++q) {
+        so += red[2 * q];
+        sd += red[2 * q + 1];
       }
-      a.partials[2 * (J.part + t)] = so;
-      a.partials[2 * (J.part + t) + 1] = sd;
-    }
-    return;
-  }
-  t -= J.btiles;
-  const int chunk = t / J.npairs, Q = t - chunk * J.npairs;
-  int q1, q2;
-  circle_pair(a.round, Q, J.nb, q1, q2);
-  float* V = reinterpret_cast<float*>(resolve(J.V, a.ws, a.user));
-  const bool vec = (d & 3) == 0 && (reinterpret_cast<uintptr_t>(V) & 15) == 0;
-  const float* jq = jb + static_cast<size_t>(Q) * kJp * kJp;
-  const size_t r0 = static_cast<size_t>(chunk) * kJp;
-  // X holds V's chunk transposed: X[j][i] = V[r0 + i][col j]
-  float4 xv[4], qv[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
-    xv[v] = jac_quad(V, r0 + i, pair_index(q1, q2, j), d, vec);
-    qv[v] = *reinterpret_cast<const float4*>(jq + 4 * u);
-  }
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int u = threadIdx.x + kJacThreads * v, i = u >> 4, j = (u & 15) * 4;
-    X[j][i] = xv[v].x; X[j + 1][i] = xv[v].y; X[j + 2][i] = xv[v].z; X[j + 3][i] = xv[v].w;
-    *reinterpret_cast<float4*>(&JQ[i][j]) = qv[v];
-  }
-  __syncthreads();
-  const floatx16 acc = jac_mfma64(X, JQ, m0, n0, h, n);   // Y = V_chunk J_Q
-  const size_t gj = pair_index(q1, q2, n0 + n);
-  if (gj < d) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const size_t row = r0 + m0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row < d) V[row * d + gj] = acc[r];
+      a.partials[2 * (J.part + it)] = so;
+      a.partials[2 * (J.part + it) + 1] = sd;
     }
   }
 }
