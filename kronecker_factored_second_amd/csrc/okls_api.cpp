@@ -1316,6 +1316,16 @@ struct Planner {
       std::sort(sets[st].begin(), sets[st].end());
       const int first = static_cast<int>(jac_jobs.size());
       int solve_blk = 0, apply_blk = 0, part = 0, max_rounds = 0;
+      // tiles per apply block: several, with the next one's loads in flight,
+      // where a round has many (measured on the 1.2B-class workload: warm
+      // refresh 6.7 -> 4.0 s); one on small rounds, whose blocks would
+      // otherwise leave CUs idle (d=1024 block: 141 against 147 ms)
+      long set_items = 0;
+      for (const size_t f : sets[st]) {
+        const long np = jac_blocks(facs[f]->d) / 2;
+        set_items += np * (np + 1) / 2 + static_cast<long>((facs[f]->d + kJp - 1) / kJp) * np;
+      }
+      const int items = set_items >= kJacManyItems ? kJacApplyItems : 1;
       for (size_t q = 0; q < sets[st].size(); ++q) {
         const size_t f = sets[st][q];
         const FacBufs& F = *facs[f];
@@ -1330,8 +1340,9 @@ struct Planner {
         // and 2^-23 sqrt(d) (6.3e-6 at d = 2816); sweeps below it only shrink
         // B's off-diagonal, not the basis' error
         j.tol = std::max(cfg.jacobi_tol, static_cast<float>(std::ldexp(std::sqrt(static_cast<double>(F.d)), -23)));
+        j.apply_items = items;
         solve_blk += j.npairs;
-        apply_blk += (j.btiles + j.vrows * j.npairs + kJacApplyItems - 1) / kJacApplyItems;
+        apply_blk += (j.btiles + j.vrows * j.npairs + items - 1) / items;
         part += j.btiles;
         max_rounds = std::max(max_rounds, j.nb - 1);
         const double tile = static_cast<double>(kJp) * kJp * kJp;   // one 64^3 product
@@ -2250,7 +2261,8 @@ struct Planner {
             if (q.btiles != q.npairs * (q.npairs + 1) / 2 || q.vrows != (q.d + kJp - 1) / kJp) return false;
             if (q.solve_begin != solve || q.apply_begin != apply || q.part != part || q.flag != j - r.first) return false;
             solve += q.npairs;
-            apply += (q.btiles + q.vrows * q.npairs + kJacApplyItems - 1) / kJacApplyItems;
+            if (q.apply_items != 1 && q.apply_items != kJacApplyItems) return false;
+            apply += (q.btiles + q.vrows * q.npairs + q.apply_items - 1) / q.apply_items;
             part += q.btiles;
             const size_t dd = static_cast<size_t>(q.d) * q.d * 4;
             if (!fits(q.B, dd) || !fits(q.V, dd)) return false;

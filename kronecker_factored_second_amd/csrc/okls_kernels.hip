@@ -1491,7 +1491,7 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_solve_kernel(JacArgs a) {
 // B <- R^T B R on the pair-block tiles (P, Q), P <= Q (the lower tile gets the
 // transpose), and V <- V R on kJp-row chunks of V; every B tile records the
 // squared Frobenius norms of its off-diagonal and diagonal entries (the
-// mirrored tile counted twice).  A block takes kJacApplyItems consecutive
+// mirrored tile counted twice).  A block takes apply_items consecutive
 // tiles, the next one's loads in flight during the current one's products.
 // The 64 x 64 products run on the matrix cores in fp32 (v_mfma_f32_32x32x2_f32): wave w computes the 32 x 32 block
 // (w / 2, w % 2) of each product from LDS operands stored k-major (row k
@@ -1539,8 +1539,8 @@ __global__ __launch_bounds__(kJacThreads) void jacobi_apply_kernel(JacArgs a) {
   if (a.round >= J.nb - 1 || a.flags[J.flag] != 0) return;
   // the block's work items: B tiles 0 .. btiles - 1, then V tiles (chunk, Q)
   const int n_items = J.btiles + J.vrows * J.npairs;
-  const int it0 = (gb - J.apply_begin) * kJacApplyItems;
-  const int it1 = min(it0 + kJacApplyItems, n_items);
+  const int it0 = (gb - J.apply_begin) * J.apply_items;
+  const int it1 = min(it0 + J.apply_items, n_items);
   const float* jb = reinterpret_cast<const float*>(a.ws + J.jbuf);
   const size_t d = static_cast<size_t>(J.d);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;

@@ -269,7 +269,8 @@ struct AdamArgs {
 constexpr int kJb = 32;
 constexpr int kJp = 2 * kJb;         // side of a pair block
 constexpr int kJacThreads = 256;
-constexpr int kJacApplyItems = 4;     // B and V tiles per apply block
+constexpr int kJacApplyItems = 4;     // B and V tiles per apply block on large rounds
+constexpr long kJacManyItems = 65536; // a set's tiles per round from which the rounds are large
 
 struct JacJob {
   Ref B;                   // d x d fp32 (row stride d): Q^T A Q on entry, rotated in place
@@ -281,7 +282,8 @@ struct JacJob {
   int32_t part;            // first partial (float2 per B tile)
   int32_t flag;            // index of the converged flag
   int32_t solve_begin;     // first block of the job in a solve launch
-  int32_t apply_begin;     // first block of the job in an apply launch (kJacApplyItems tiles a block)
+  int32_t apply_begin;     // first block of the job in an apply launch
+  int32_t apply_items;     // B and V tiles per apply block (1 or kJacApplyItems)
   float tol;               // converged when ||off(B)||_F <= tol ||diag(B)||_F
 };
 
