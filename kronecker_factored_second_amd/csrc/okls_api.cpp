@@ -160,6 +160,7 @@ struct LaunchRec {
   size_t jac_part = 0, jac_flag = 0;   // L_JAC: workspace offsets of the chunk's partials and flags
   int thin_ta = 0, thin_mom = 0;       // L_THIN: the launch's operand form
   int thin_cbm = 1;                    // L_THIN: 32-column blocks of C the kernel holds (1, 2 or 4)
+  int thin_wupd = 0;                   // L_THIN: the weight-update form (every job wupd)
 };
 
 enum { CAT_NS = 0, CAT_FACTOR = 1, CAT_WHITEN = 2, CAT_STAT = 3, CAT_CAST = 4, CAT_EIG = 5 };
@@ -1477,6 +1478,7 @@ struct Planner {
     r.thin_ta = js.front().ta;
     r.thin_mom = js.front().mom;
     for (const ThinJob& j : js) r.thin_cbm = std::max(r.thin_cbm, j.R <= 32 ? 1 : j.R <= 64 ? 2 : 4);
+    r.thin_wupd = js.front().wupd;
     int blk = 0;
     for (ThinJob j : js) {
       j.blk_begin = blk;
@@ -1680,11 +1682,11 @@ struct Planner {
     }
     std::vector<ThinJob> t1, t2, t3, t4, fin;
     double wupd_a_bytes = 0.0;
-    // the weight update's column chunk: two 32-column blocks per thin block
-    // (its two-block kernel holds fewer registers than the four-block one,
-    // so more blocks share a CU; the m x (r_a + r_b) operand is re-read per
-    // chunk from L2)
-    constexpr int kWupdCols = 64;
+    // the weight update's column chunk: one 32-column block per thin block
+    // (the one-block kernel's registers leave room for the block's W and X
+    // quads, loaded before the product; the m x (r_a + r_b) operand is
+    // re-read per chunk from L2)
+    constexpr int kWupdCols = 32;
     for (const MatBufs& mb : mats) {
       const int ra = mb.ns[0].r, rb = mb.ns[1].r, ld = rb + ra;
       // X = N U_b with N = momentum(G, M)
@@ -2168,6 +2170,7 @@ struct Planner {
           if (r.first < 0 || r.first + r.count > static_cast<int>(thin_jobs.size())) return false;
           if (r.thin_ta < 0 || r.thin_ta > 1 || r.thin_mom < 0 || r.thin_mom > 1 || (r.thin_ta && r.thin_mom)) return false;
           if (r.thin_cbm != 1 && r.thin_cbm != 2 && r.thin_cbm != 4) return false;
+          if (r.thin_wupd != 0 && (r.thin_wupd != 1 || r.thin_cbm != 1 || r.thin_ta || r.thin_mom)) return false;
           int blk = 0;
           for (int j = r.first; j < r.first + r.count; ++j) {
             const ThinJob& q = thin_jobs[j];
@@ -2187,7 +2190,7 @@ struct Planner {
             }
             if (q.alpha_slot >= 0 && !slot_ok(q.alpha_slot)) return false;
             if (q.rowscale.kind != REF_NONE && (q.ot != 0 || !fits(q.rowscale, static_cast<size_t>(q.Mo) * 4))) return false;
-            if (q.wupd != 0 && q.wupd != 1) return false;
+            if (q.wupd != r.thin_wupd) return false;
             if (q.wupd && (q.ot != 0 || q.ta != 0 || q.mom != 0 || q.C.kind != REF_W || q.rowscale.kind != REF_NONE ||
                            !fits(q.aux, (static_cast<size_t>(q.Mo - 1) * q.ldc + q.R) * 4)))
               return false;
@@ -2904,7 +2907,7 @@ okls_status okls_step(okls_handle* h, const okls_group_tensors* t, int64_t step,
         a.decay = static_cast<float>(decay);
         a.ws = ws;
         a.user = user;
-        e = launch_thin(a, r.thin_ta, r.thin_mom, r.thin_cbm, r.nblocks, rs);
+        e = launch_thin(a, r.thin_ta, r.thin_mom, r.thin_cbm, r.thin_wupd, r.nblocks, rs);
       } else if (r.type == L_NORTH) {
         NysOrthArgs a;
         a.jobs = reinterpret_cast<const NysOrthJob*>(ws + h->off_north) + r.first;

@@ -33,7 +33,7 @@ enum JacKind { JAC_RESET = 0, JAC_SOLVE = 1, JAC_APPLY = 2, JAC_CHECK = 3 };
 // takes one block per job
 hipError_t launch_jacobi(const JacArgs& a, int kind, int n_blocks, hipStream_t s);
 // Thin fp32 products; every job of one launch has the same ta and mom.
-hipError_t launch_thin(const ThinArgs& a, int ta, int mom, int cbm, int n_blocks, hipStream_t s);
+hipError_t launch_thin(const ThinArgs& a, int ta, int mom, int cbm, int wupd, int n_blocks, hipStream_t s);
 hipError_t launch_nys_orth(const NysOrthArgs& a, hipStream_t s);     // one block per job
 hipError_t launch_nys_small(const NysSmallArgs& a, hipStream_t s);   // one block per job
 hipError_t launch_nys_elem(const NysElemArgs& a, int n_blocks, hipStream_t s);

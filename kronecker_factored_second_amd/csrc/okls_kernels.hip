@@ -1755,13 +1755,14 @@ __device__ __forceinline__ float& f4_at(float4& v, int e) { return e == 0 ? v.x 
 
 // CBM: the most 32-column blocks of C a job of the launch has (1, 2 or 4);
 // the narrower forms hold fewer accumulators and less of B's stage, so more
-// blocks fit on a CU.
-template <int TA, bool MOM, int CBM>
+// blocks fit on a CU.  WU: the weight-update form (every job wupd, R <= 32).
+template <int TA, bool MOM, int CBM, bool WU>
 __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
   constexpr int TM = kThinTile, KC = kThinK, LK = kThinLK;
   static_assert(TM == 128 && KC == 32 && kThinMaxR == 128, "the load and fragment maps below assume these sizes");
   static_assert(!MOM || TA == 0, "the momentum operand is row-major");
   static_assert(CBM == 1 || CBM == 2 || CBM == 4, "one, two or four column blocks");
+  static_assert(!WU || (TA == 0 && !MOM && CBM == 1), "the weight update is a row-major product of 32 columns");
   __shared__ __attribute__((aligned(16))) float As[TM * LK];
   __shared__ __attribute__((aligned(16))) float Bs[32 * CBM * LK];
   const int gb = blockIdx.x;
@@ -1793,6 +1794,36 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
   for (int c = 0; c < CBM; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+
+  // the weight update: the block's W and X quads (128 rows x 32 columns,
+  // thread quads u = t + 256 v: row u / 8, columns 4 (u % 8) .. + 3) are
+  // loaded before the product, so their latency passes during it
+  float4 uw[WU ? 4 : 1], ux[WU ? 4 : 1];
+  const float* X = nullptr;
+  bool wvec = false;
+  if constexpr (WU) {
+    X = reinterpret_cast<const float*>(resolve(J.aux, a.ws, a.user));
+    wvec = (J.ldc & 3) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(X)) & 15) == 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int u = t + 256 * v, gi = i0 + (u >> 3), gj = (u & 7) * 4;
+      uw[v] = ux[v] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (gi < J.Mo) {
+        const size_t o = static_cast<size_t>(gi) * J.ldc + gj;
+        if (wvec && gj + 3 < J.R) {
+          uw[v] = *reinterpret_cast<const float4*>(C + o);
+          ux[v] = *reinterpret_cast<const float4*>(X + o);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (gj + e < J.R) {
+              f4_at(uw[v], e) = C[o + e];
+              f4_at(ux[v], e) = X[o + e];
+            }
+        }
+      }
+    }
+  }
 
   // stage k0 into registers: op(A) as 1024 quads (TA 0: 128 rows x 8 quads
   // along k; TA 1: 32 k-rows x 32 quads along i), B as 32 k-rows x 32 quads.
@@ -1941,69 +1972,37 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
   const float alpha0 = J.alpha * (J.alpha_slot >= 0 ? a.scal[J.alpha_slot] : 1.0f);
   const float* rsc = J.rowscale.kind != REF_NONE ? reinterpret_cast<const float*>(resolve(J.rowscale, a.ws, a.user)) : nullptr;
   const float beta = J.beta;
-  // (weight-update jobs are plain row-major products: the planner's checks)
-  if constexpr (TA == 0 && !MOM) {
-    if (J.wupd) {
-      // W <- decay W - lr c0 (alpha acc + X), X the unpreconditioned part of
-      // the update (W's layout, stride ldc).  Per 32-column block the
-      // accumulators pass through LDS (As is free after the last stage), so
-      // that each thread then updates four 16-byte row quads of W, all eight
-      // W and X loads in flight before the first store.
-      const float* X = reinterpret_cast<const float*>(resolve(J.aux, a.ws, a.user));
-      const float sc = -(a.lr * J.c0);
-      constexpr int LS = 36;                 // staging row stride (floats)
-      static_assert(TM * LS <= TM * LK, "the staging fits As");
-      const bool wvec = (J.ldc & 3) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(X)) & 15) == 0;
-  #pragma unroll
-      for (int c = 0; c < CBM; ++c) {
-        if (c >= CB) break;
-        __syncthreads();                     // As is no longer read (products, or the previous block)
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) As[(32 * wave + 8 * (r >> 2) + 4 * hl + (r & 3)) * LS + ln] = acc[c][r];
-        __syncthreads();
-        float4 w[4], x[4];
-  #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int qd = t + 256 * u, row = qd >> 3, cq = (qd & 7) * 4;
-          const int gi = i0 + row, gj = 32 * c + cq;
-          w[u] = x[u] = float4{0.0f, 0.0f, 0.0f, 0.0f};
-          if (gi < J.Mo) {
-            const size_t o = static_cast<size_t>(gi) * J.ldc + gj;
-            if (wvec && gj + 3 < J.R) {
-              w[u] = *reinterpret_cast<const float4*>(C + o);
-              x[u] = *reinterpret_cast<const float4*>(X + o);
-            } else {
-  #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (gj + e < J.R) {
-                  f4_at(w[u], e) = C[o + e];
-                  f4_at(x[u], e) = X[o + e];
-                }
-            }
-          }
-        }
-  #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int qd = t + 256 * u, row = qd >> 3, cq = (qd & 7) * 4;
-          const int gi = i0 + row, gj = 32 * c + cq;
-          if (gi >= J.Mo) continue;
-          float4 v = *reinterpret_cast<const float4*>(&As[row * LS + cq]);
-          float4 o4;
-  #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            f4_at(o4, e) = __builtin_fmaf(a.decay, f4_at(w[u], e), sc * __builtin_fmaf(alpha0, f4_at(v, e), f4_at(x[u], e)));
-          const size_t o = static_cast<size_t>(gi) * J.ldc + gj;
-          if (wvec && gj + 3 < J.R) {
-            *reinterpret_cast<float4*>(C + o) = o4;
-          } else {
-  #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gj + e < J.R) C[o + e] = f4_at(o4, e);
-          }
-        }
+  if constexpr (WU) {
+    // W <- decay W - lr c0 (alpha acc + X), X the unpreconditioned part of
+    // the update (W's layout, stride ldc).  The accumulators pass through
+    // LDS (As is free after the last stage), so that each thread updates its
+    // four prefetched 16-byte row quads.
+    constexpr int LS = 36;                 // staging row stride (floats)
+    static_assert(TM * LS <= TM * LK, "the staging fits As");
+    const float sc = -(a.lr * J.c0);
+    __syncthreads();                       // the products no longer read As
+#pragma unroll
+    for (int r = 0; r < 16; ++r) As[(32 * wave + 8 * (r >> 2) + 4 * hl + (r & 3)) * LS + ln] = acc[0][r];
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int u = t + 256 * v, row = u >> 3, gj = (u & 7) * 4, gi = i0 + row;
+      if (gi >= J.Mo) continue;
+      float4 pv = *reinterpret_cast<const float4*>(&As[row * LS + gj]);
+      float4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        f4_at(o4, e) = __builtin_fmaf(a.decay, f4_at(uw[v], e), sc * __builtin_fmaf(alpha0, f4_at(pv, e), f4_at(ux[v], e)));
+      const size_t o = static_cast<size_t>(gi) * J.ldc + gj;
+      if (wvec && gj + 3 < J.R) {
+        *reinterpret_cast<float4*>(C + o) = o4;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gj + e < J.R) C[o + e] = f4_at(o4, e);
       }
-      return;
     }
+    return;
   }
 #pragma unroll
   for (int c = 0; c < CBM; ++c) {
@@ -2511,15 +2510,18 @@ hipError_t launch_jacobi(const JacArgs& a, int kind, int n_blocks, hipStream_t s
 template <int CBM>
 void launch_thin_cbm(const ThinArgs& a, int ta, int mom, int n_blocks, hipStream_t s) {
   const dim3 g(n_blocks), b(256);
-  if (mom) thin_kernel<0, true, CBM><<<g, b, 0, s>>>(a);
-  else if (ta) thin_kernel<1, false, CBM><<<g, b, 0, s>>>(a);
-  else thin_kernel<0, false, CBM><<<g, b, 0, s>>>(a);
+  if (mom) thin_kernel<0, true, CBM, false><<<g, b, 0, s>>>(a);
+  else if (ta) thin_kernel<1, false, CBM, false><<<g, b, 0, s>>>(a);
+  else thin_kernel<0, false, CBM, false><<<g, b, 0, s>>>(a);
 }
 
-hipError_t launch_thin(const ThinArgs& a, int ta, int mom, int cbm, int n_blocks, hipStream_t s) {
+hipError_t launch_thin(const ThinArgs& a, int ta, int mom, int cbm, int wupd, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   if (mom && ta) return hipErrorInvalidValue;
-  if (cbm == 1) launch_thin_cbm<1>(a, ta, mom, n_blocks, s);
+  if (wupd) {
+    if (ta || mom || cbm != 1) return hipErrorInvalidValue;
+    thin_kernel<0, false, 1, true><<<dim3(n_blocks), dim3(256), 0, s>>>(a);
+  } else if (cbm == 1) launch_thin_cbm<1>(a, ta, mom, n_blocks, s);
   else if (cbm == 2) launch_thin_cbm<2>(a, ta, mom, n_blocks, s);
   else if (cbm == 4) launch_thin_cbm<4>(a, ta, mom, n_blocks, s);
   else return hipErrorInvalidValue;
