@@ -840,10 +840,12 @@ def test_well_conditioned_state_matches_exact_root(precision, tol):
         assert e["U_exact"] < max(tol, 1e-3), e
 
 
-def test_misaligned_weights_take_the_scalar_path():
+@pytest.mark.parametrize("mode,cfg", [("okls", {}), ("soap", dict(precond_freq=2)), ("nystrom", dict(root_period=2))])
+def test_misaligned_weights_take_the_scalar_path(mode, cfg):
     """W as a view one float into its buffer (4-byte aligned, not 16): the
     fp32 epilogues use their element-wise path and give bit-identically the
-    results of an aligned W over two steps (factor update, weight update)."""
+    results of an aligned W over three steps (factor update, weight update;
+    SOAP's and Nystrom's weight updates and refreshes)."""
     torch = pytest.importorskip("torch")
     from kronecker_factored_second_amd import okls
     m, n = 96, 160
@@ -854,13 +856,13 @@ def test_misaligned_weights_take_the_scalar_path():
     runs = []
     for W in (W0.clone(), Wodd):
         W.copy_(W0)
-        opt = okls.OKLS([W], precision="fp16")
-        for t in (1, 2):
+        opt = okls.OKLS([W], precision="fp16", mode=mode, **cfg)
+        for t in (1, 2, 3):
             g = torch.tensor((0.02 * np.random.default_rng([t, 72]).standard_normal((1, m, n))).astype(np.float32),
                              device="cuda:0")
             opt.step(grads=[g])
         torch.cuda.synchronize()
-        runs.append([W.clone()] + [opt.state[0][k].clone() for k in ("M", "Sa", "Sb", "Pa", "Pb")])
+        runs.append([W.clone()] + [opt.state[0][k].clone() for k in sorted(opt.state[0])])
     for a, b in zip(*runs):
         assert torch.equal(a, b)
 
