@@ -192,6 +192,11 @@ typedef struct {
     int32_t nys_rank;          /* r >= 1: eigenpairs kept per factor (default 32) */
     int32_t nys_oversample;    /* p >= 0: extra sketch columns, r + p <= 128 (default 8) */
     int32_t nys_passes;        /* q, 0..8: subspace-iteration passes of a refresh (default 1) */
+    /* OKLS_MODE_SOAP only: */
+    int32_t jacobi_apply_tiles; /* tiles per workgroup of the eigensolver's rotation apply:
+                                   0 (default) chooses by the size of a round (4 on rounds with
+                                   at least 65536 tiles, else 1); 1 or 4 forces it.  The results
+                                   are bitwise the same either way. */
 } okls_config;
 
 typedef struct {

@@ -262,6 +262,8 @@ okls_status check_config(const okls_config* c) {
     if (c->precond_freq < 1 || ((c->soap_moments | c->bias_correction) & ~1)) return OKLS_ERR_INVALID_ARG;
     if (c->jacobi_sweeps < 1 || c->jacobi_sweeps > 64 || !(c->jacobi_tol > 0.f && c->jacobi_tol < 1.f))
       return OKLS_ERR_INVALID_ARG;
+    if (c->jacobi_apply_tiles != 0 && c->jacobi_apply_tiles != 1 && c->jacobi_apply_tiles != kJacApplyItems)
+      return OKLS_ERR_INVALID_ARG;
     // the direction is bounded (and its fp16 operand can take a static scale)
     // only when beta1^2 < beta2, or beta1 = 0
     if (!(c->beta1 == 0.f || static_cast<double>(c->beta1) * c->beta1 < c->beta2)) return OKLS_ERR_UNSUPPORTED;
@@ -1326,7 +1328,8 @@ struct Planner {
         const long np = jac_blocks(facs[f]->d) / 2;
         set_items += np * (np + 1) / 2 + static_cast<long>((facs[f]->d + kJp - 1) / kJp) * np;
       }
-      const int items = set_items >= kJacManyItems ? kJacApplyItems : 1;
+      const int items = cfg.jacobi_apply_tiles != 0 ? cfg.jacobi_apply_tiles
+                        : set_items >= kJacManyItems ? kJacApplyItems : 1;
       for (size_t q = 0; q < sets[st].size(); ++q) {
         const size_t f = sets[st][q];
         const FacBufs& F = *facs[f];
@@ -2483,6 +2486,7 @@ void okls_default_config(okls_config* c) {
   c->nys_rank = 32;
   c->nys_oversample = 8;
   c->nys_passes = 1;
+  c->jacobi_apply_tiles = 0;
 }
 
 size_t okls_workspace_size(const okls_config* cfg, int n_groups, const okls_group_desc* groups) {

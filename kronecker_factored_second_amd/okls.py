@@ -41,7 +41,8 @@ class Config(ctypes.Structure):
                 ("ns_classical", ctypes.c_int32), ("whiten_split", ctypes.c_int32),
                 ("soap_beta", ctypes.c_float), ("precond_freq", ctypes.c_int32), ("soap_moments", ctypes.c_int32),
                 ("bias_correction", ctypes.c_int32), ("jacobi_sweeps", ctypes.c_int32), ("jacobi_tol", ctypes.c_float),
-                ("nys_rank", ctypes.c_int32), ("nys_oversample", ctypes.c_int32), ("nys_passes", ctypes.c_int32)]
+                ("nys_rank", ctypes.c_int32), ("nys_oversample", ctypes.c_int32), ("nys_passes", ctypes.c_int32),
+                ("jacobi_apply_tiles", ctypes.c_int32)]
 
 
 class GroupDesc(ctypes.Structure):

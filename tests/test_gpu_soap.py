@@ -171,3 +171,26 @@ def test_soap_refresh_recovers_a_known_spectrum(d):
         res, orth, eig = S.offdiag_residual(Q, Lout), S.orthogonality(Q), _eig_err(Q, Lout)
         print(f"d={d} refresh {t}: residual {res:.2e} orthogonality {orth:.2e} eigenvalues {eig:.2e}", flush=True)
         assert res < 2e-5 and orth < 2e-5 and eig < 2e-5
+
+
+@pytest.mark.parametrize("precision", ["fp32", "fp16"])
+def test_soap_apply_tile_walk_is_bitwise_one_tile_per_block(precision):
+    """The rotation apply run with four tiles per workgroup (the next tile's
+    loads in flight during the current products; the form large rounds
+    take) gives bitwise the state of one tile per workgroup.  Ragged sides
+    (96, 160, 200, 72 and 513) put the walk across the boundary between B
+    and V tiles and over partial edge tiles; refreshes after steps 2 and 4,
+    the first from the identity."""
+    torch = _torch()
+    groups = [(96, 160, 2), (200, 72, 1), (513, 40, 1)]
+    states = []
+    for tiles in (1, 4):
+        opt, params = _make(groups, precision, precond_freq=2, jacobi_apply_tiles=tiles)
+        for t in range(1, 5):
+            grads = [torch.tensor((0.02 * np.random.default_rng([gi, t, 91]).standard_normal((b, m, n))).astype(np.float32),
+                                  device="cuda:0") for gi, (m, n, b) in enumerate(groups)]
+            opt.step(grads=grads)
+        torch.cuda.synchronize()
+        states.append([p.clone() for p in params] + [s[k].clone() for s in opt.state for k in sorted(s)])
+    for a, b in zip(*states):
+        assert torch.equal(a, b)
