@@ -2051,7 +2051,9 @@ __global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
 // threads of a Gram-Schmidt block (a sketch is one block).  1024 threads
 // measured slower than 256 (17.8 against 13.7 ms per launch on the
 // 1.2B-class workload): the wider block reductions and barriers of every
-// column cost more than the shorter row walks save
+// column cost more than the shorter row walks save.  The row walks are
+// unrolled by two, so a thread has two rows' loads in flight (by four
+// measured the same).
 constexpr int kOrthThreads = 256;
 
 // Block sum of one float (all threads get the result).
@@ -2094,6 +2096,7 @@ __global__ __launch_bounds__(kOrthThreads) void nys_orth_kernel(NysOrthArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   auto col_norm2 = [&](int j) {
     float s = 0.0f;
+#pragma unroll 4
     for (int r = threadIdx.x; r < J.d; r += kOrthThreads) {
       const float v = Y[static_cast<size_t>(r) * J.ld + j];
       s += v * v;
@@ -2108,6 +2111,7 @@ __global__ __launch_bounds__(kOrthThreads) void nys_orth_kernel(NysOrthArgs a) {
       float s[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) s[c] = 0.0f;
+#pragma unroll 2
       for (int r = threadIdx.x; r < J.d; r += kOrthThreads) {
         const float* row = Y + static_cast<size_t>(r) * J.ld;
         const float yj = row[j];
@@ -2133,9 +2137,11 @@ __global__ __launch_bounds__(kOrthThreads) void nys_orth_kernel(NysOrthArgs a) {
       }
       __syncthreads();
     }
+#pragma unroll 2
     for (int r = threadIdx.x; r < J.d; r += kOrthThreads) {
       float* row = Y + static_cast<size_t>(r) * J.ld;
       float v = row[j];
+#pragma unroll 8
       for (int c = 0; c < j; ++c) v -= row[c] * coef[c];
       row[j] = v;
     }
