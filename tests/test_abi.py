@@ -276,11 +276,17 @@ def test_soap_config_validation():
     g = [(1, 64, 80, 0)]
     assert okls.workspace_size(_soap_cfg(), g) > 0
     assert okls.workspace_size(_soap_cfg(beta1=0.0, beta2=0.0), g) > 0
+    # the apply's tiles per workgroup: automatic, or forced to 1 or 4 (fewer
+    # apply workgroups with 4, the same plan otherwise)
+    big = [(2, 1024, 1024, 0)]
+    one, four = (okls.plan_query(_soap_cfg(jacobi_apply_tiles=k), big) for k in (1, 4))
+    assert okls.plan_query(_soap_cfg(jacobi_apply_tiles=0), big)["launches"] == one["launches"] == four["launches"]
+    assert one["flops"] == four["flops"]
     with pytest.raises(okls.OKLSError, match="UNSUPPORTED"):
         okls.plan_query(_soap_cfg(beta1=0.99, beta2=0.95), g)
     for bad in (dict(eps=0.0), dict(precond_freq=0), dict(jacobi_sweeps=0), dict(jacobi_sweeps=65),
                 dict(jacobi_tol=0.0), dict(soap_moments=2), dict(bias_correction=3), dict(soap_beta=1.0),
-                dict(beta2=1.0)):
+                dict(beta2=1.0), dict(jacobi_apply_tiles=2), dict(jacobi_apply_tiles=-1)):
         assert okls.workspace_size(_soap_cfg(**bad), g) == 0, bad
         with pytest.raises(okls.OKLSError, match="INVALID_ARG"):
             okls.plan_query(_soap_cfg(**bad), g)
