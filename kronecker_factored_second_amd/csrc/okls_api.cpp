@@ -838,9 +838,15 @@ struct Planner {
         p.aux_sym = chain == 1;
         p.out16 = ws_ref(F.Y[1]); p.out16T = ws_ref(F.YT[1]); p.ld16 = F.ld; p.lo16 = F.dp; p.s_out = SL_Y;
         p.sA = p.sB = SL_Y;
+        // Y_0 Y_0 with plain fp16 operands is symmetric bit for bit (entry
+        // (i, j) and (j, i) sum the same products in the same order): its
+        // upper tiles, each written with its transpose.  The split product
+        // sums the hi-lo and lo-hi parts in the other order for (j, i), so it
+        // stays whole.
+        p.sym_out = ks == 0 ? 1 : 0;
         ps.push_back(p);
       }
-      add_gemm(L, ps, false, 0 < ks, 1 < ks, static_cast<float>(na[0]), static_cast<float>(nb[0]));
+      add_gemm(L, ps, ks == 0, 0 < ks, 1 < ks, static_cast<float>(na[0]), static_cast<float>(nb[0]));
     }
     for (int k = 1; k < K; ++k) {
       const int cb = k & 1, nbuf = (k + 1) & 1;
@@ -1871,9 +1877,11 @@ struct Planner {
       const double m = mb.m, n = mb.n;
       step_flops[CAT_FACTOR] += (okls_mode ? 3.0 : 1.0) * m * n * (m + n);
       step_flops[CAT_WHITEN] += 2.0 * m * n * (m + n);
-      // 3K - 3 GEMMs per inverse square root (27 at K = 10); two chains for the fourth root
+      // 3K - 3 GEMMs per inverse square root (27 at K = 10), the first (Y_0
+      // Y_0) on its upper half on the unsplit path; two chains for the fourth root
       if (refresh)
-        step_flops[CAT_NS] += (okls_mode ? 1.0 : 2.0) * (3.0 * cfg.ns_steps - 3.0) * 2.0 * (m * m * m + n * n * n);
+        step_flops[CAT_NS] += (okls_mode ? 1.0 : 2.0) * (3.0 * cfg.ns_steps - 3.0 - (cfg.ns_split_steps == 0 ? 0.5 : 0.0)) *
+                              2.0 * (m * m * m + n * n * n);
     }
     gemm_cat = CAT_FACTOR;
     if (okls_mode) {
@@ -2126,6 +2134,14 @@ struct Planner {
             if (p.Mp % r.tile || p.Np % r.tile || p.Kp % kTile || p.Kp <= 0) return false;
             if (ti < 0 || tj < 0 || ti >= p.Mp / r.tile || tj >= p.Np / r.tile) return false;
             if (p.M > p.Mp || p.N > p.Np || p.M < 1 || p.N < 1) return false;
+            if (p.sym_out != 0 && p.sym_out != 1) return false;
+            // a symmetric product on its upper tiles: one unsplit square operand
+            // and two fp16 copies of one layout
+            if (p.sym_out && (p.epi != EPI_NS_Y1 || r.split_in || ti > tj || p.M != p.N || p.Mp != p.Np ||
+                              p.A.kind != p.B.kind || p.A.group != p.B.group || p.A.off != p.B.off || p.lda != p.ldb ||
+                              p.out16.kind == REF_NONE || p.out16T.kind == REF_NONE || p.ld16T != p.ld16 ||
+                              p.lo16T != p.lo16))
+              return false;
             if (p.lda < segs * p.Kp || p.ldb < segs * p.Kp) return false;
             if (!fits(p.A, static_cast<size_t>(p.Mp) * p.lda * 2) || !fits(p.B, static_cast<size_t>(p.Np) * p.ldb * 2))
               return false;

@@ -82,6 +82,9 @@ struct GemmProb {
   int32_t Mp, Np;          // padded output dims
   int32_t resid;           // EPI_NS_T: first float of this problem's residual partials
                            // (one per wave and tile), or -1
+  int32_t sym_out;         // EPI_NS_Y1: 1 = the product is symmetric bit for bit (A = B,
+                           // unsplit): upper tiles only, each written with its transpose
+                           // into both fp16 copies
 };
 
 struct GemmArgs {
