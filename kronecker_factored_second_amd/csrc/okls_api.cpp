@@ -965,7 +965,11 @@ struct Planner {
     gemm_cat = CAT_NS;
     for (const MatBufs& mb : mats) {
       const double p = mb.pd, q = std::max(mb.m, mb.n);
-      step_flops[CAT_NS] += 4.0 * K * p * p * q;     // a Gram and an update product per step
+      // a Gram and an update product per step; the unsplit Grams after the
+      // first run on their upper half
+      step_flops[CAT_NS] += 4.0 * K * p * p * q;
+      for (int k = 1; k < K; ++k)
+        if (!sp(k)) step_flops[CAT_NS] -= p * p * q;
     }
     // 3. Gram of the smaller side in fp32: A_0 = N N^T (wide) or N^T N (tall)
     {
@@ -1009,9 +1013,12 @@ struct Planner {
           g.A = g.B = ws_ref(w ? mb.X[cur] : mb.XT[cur]); g.lda = g.ldb = w ? mb.ldn : mb.ldm;
           g.M = g.N = mb.pd; g.Kp = w ? mb.np : mb.mp; g.Mp = g.Np = mb.pdp; g.epi = EPI_STORE16;
           g.out16 = ws_ref(mb.A16); g.ld16 = mb.ldp; g.lo16 = mb.pdp; g.s_out = SL_Y; g.sA = g.sB = SL_Y;
+          // X X^T with plain fp16 operands is symmetric bit for bit: its
+          // upper tiles, each also written transposed
+          g.sym_out = sp(k) ? 0 : 1;
           pg.push_back(g);
         }
-        add_gemm(L, pg, false, sp(k), sp(k));
+        add_gemm(L, pg, !sp(k), sp(k), sp(k));
       }
       // update: X_{k+1} = c (a_k X_k + b_k A_k X_k), c = ||A_0||_F^{-1/2} at k = 0 (X_0 = N c), else 1
       std::vector<GemmProb> pu;
@@ -2137,10 +2144,10 @@ struct Planner {
             if (p.sym_out != 0 && p.sym_out != 1) return false;
             // a symmetric product on its upper tiles: one unsplit square operand
             // and two fp16 copies of one layout
-            if (p.sym_out && (p.epi != EPI_NS_Y1 || r.split_in || ti > tj || p.M != p.N || p.Mp != p.Np ||
-                              p.A.kind != p.B.kind || p.A.group != p.B.group || p.A.off != p.B.off || p.lda != p.ldb ||
-                              p.out16.kind == REF_NONE || p.out16T.kind == REF_NONE || p.ld16T != p.ld16 ||
-                              p.lo16T != p.lo16))
+            if (p.sym_out && ((p.epi != EPI_NS_Y1 && p.epi != EPI_STORE16) || r.split_in || r.write_lo || ti > tj ||
+                              p.M != p.N || p.Mp != p.Np || p.A.kind != p.B.kind || p.A.group != p.B.group ||
+                              p.A.off != p.B.off || p.lda != p.ldb || p.out16.kind == REF_NONE ||
+                              (p.out16T.kind != REF_NONE && (p.ld16T != p.ld16 || p.lo16T != p.lo16))))
               return false;
             if (p.lda < segs * p.Kp || p.ldb < segs * p.Kp) return false;
             if (!fits(p.A, static_cast<size_t>(p.Mp) * p.lda * 2) || !fits(p.B, static_cast<size_t>(p.Np) * p.ldb * 2))

@@ -120,7 +120,7 @@ struct EpiCtx {
   bool aux_vec, out32_vec;  // fp32 aux rows / fp32 output rows are 16-byte aligned
   float c0, c1, c2, ka, kb, lr, decay;
   float* resid;             // EPI_NS_T_RES: this wave's residual partial
-  int sym_out;              // EPI_NS_Y1: also write the transposed tile into both copies
+  int sym_out;              // EPI_NS_Y1, EPI_STORE16: also write the transposed tile into the copies
 };
 
 // K advances in stages of 32 through a 4-deep LDS ring filled by
@@ -442,15 +442,16 @@ __device__ __forceinline__ void epilogue_pass(const floatx16 (&acc)[C::GI][C::GJ
     }
   }
   Stage<C>::flush(x, PART == 0 ? 0 : x.lo16, PART == 0 ? 0 : x.lo16T);
-  if constexpr (EPI == EPI_NS_Y1) {
+  if constexpr (EPI == EPI_NS_Y1 || EPI == EPI_STORE16) {
     // a symmetric product computed on its upper tiles: the tile's transpose
-    // is the lower tile, so the copies swap roles for a second write (on a
+    // is the lower tile, so the copies swap roles for a second write (with
+    // no transposed copy, only the transpose into the one copy; on a
     // diagonal tile the two writes of an entry carry the same value)
     if (x.sym_out) {
       EpiCtx y = x;
       y.out16 = x.out16T; y.out16T = x.out16;
-      y.ld16 = x.ld16T; y.ld16T = x.ld16;
-      y.lo16 = x.lo16T; y.lo16T = x.lo16;
+      y.ld16 = x.out16T != nullptr ? x.ld16T : x.ld16; y.ld16T = x.ld16;
+      y.lo16 = x.out16T != nullptr ? x.lo16T : x.lo16; y.lo16T = x.lo16;
       Stage<C>::flush(y, PART == 0 ? 0 : y.lo16, PART == 0 ? 0 : y.lo16T);
     }
   }
@@ -692,7 +693,7 @@ __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_nt_kernel(G
   ctx.lr = args.lr;
   ctx.decay = args.decay;
   ctx.resid = nullptr;
-  ctx.sym_out = P.sym_out;
+  ctx.sym_out = WL ? 0 : P.sym_out;   // symmetric products are unsplit, with no lo halves
   if constexpr (EPI == EPI_NS_T_RES)
     ctx.resid = args.resid + P.resid + (static_cast<size_t>(ti) * (P.Np / BT) + tj) * NW + wave;
   if constexpr (EPI == EPI_STORE32 || EPI == EPI_UPDATE || EPI == EPI_SYRK || EPI == EPI_POLAR_UPDATE) {

@@ -214,7 +214,8 @@ def test_plan_query_flops_are_the_closed_forms():
     the Shampoo fourth root; on the fp16 path the first of them, symmetric, on
     its upper half: 26.5) over d = m and d = n, 3 m n (m + n) for the OKLS
     factor products (m n (m + n) for the Shampoo sums), 2 m n (m + n) for the
-    whitening; Muon: 4 K p^2 q with p, q the smaller and larger side."""
+    whitening; Muon: 4 K p^2 q with p, q the smaller and larger side (on the
+    fp16 path the K - 1 Grams after the first on their upper half)."""
     groups = [(4, 1024, 1024, 0), (2, 2816, 1024, 0), (1, 1024, 2816, 0), (3, 200, 72, 0)]
     mats = [(m, n) for b, m, n, _ in groups for _ in range(b)]
     cube = sum(float(m) ** 3 + float(n) ** 3 for m, n in mats)
@@ -231,7 +232,10 @@ def test_plan_query_flops_are_the_closed_forms():
         assert f["factor_gemm"] == pytest.approx(mn, rel=1e-12)
         f = _plan(groups, prec, mode=okls.MODE["muon"], **okls.MUON_DEFAULTS)["flops"]
         k = okls.MUON_DEFAULTS["ns_steps"]
-        assert f["ns_gemm"] == pytest.approx(sum(4 * k * float(min(m, n)) ** 2 * max(m, n) for m, n in mats), rel=1e-12)
+        # a Gram and an update product per step; on the fp16 path the Grams
+        # after the first (symmetric, unsplit) run on their upper half
+        grams = 4 * k if prec == "fp32" else 4 * k - (k - 1)
+        assert f["ns_gemm"] == pytest.approx(sum(grams * float(min(m, n)) ** 2 * max(m, n) for m, n in mats), rel=1e-12)
 
 
 def _soap_cfg(precision="fp32", **kw):
