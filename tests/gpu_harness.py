@@ -68,13 +68,13 @@ class Report:
 
 
 # Condition numbers up to which the exact root is asserted, per path and
-# factor side.  The survey's attainability table for 10 minimax steps
-# (d = 256, log-spaced spectra): all-fp16 6.9e-3 at kappa 1e3 and 5.0e-2 at
-# 1e4; split-fp16 4.4e-5 at 1e4 and 3.5e-4 at 1e5.  The relative Frobenius
-# error of P is carried by its few largest entries (the smallest
-# eigenvalues), so on small factors it is not averaged down: on the fp16
-# path an 8-side factor reaches 2e-2 at kappa ~ 7e2 (measured), hence the
-# lower gate below 32.  A factor beyond its gate (the rank-deficient first
+# factor side.  Emulated attainability of 10 minimax steps (d = 256,
+# log-spaced spectra, relative Frobenius error of P): all-fp16 6.9e-3 at
+# kappa 1e3 and 5.0e-2 at 1e4; split-fp16 4.4e-5 at 1e4 and 3.5e-4 at 1e5.
+# The relative Frobenius error of P is carried by its few largest entries
+# (the smallest eigenvalues), so on small factors it is not averaged down: on
+# the fp16 path an 8-side factor reaches 2e-2 at kappa ~ 7e2 (measured), hence
+# the lower gate below 32.  A factor beyond its gate (the rank-deficient first
 # steps, the eps-level null spaces, the 1e6-conditioned stress layer) is what
 # ten Newton-Schulz steps in that arithmetic cannot resolve; its errors are
 # logged, and the whitened update is then checked against the GPU's own roots.
