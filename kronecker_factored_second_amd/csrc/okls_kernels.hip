@@ -1771,8 +1771,12 @@ __device__ __forceinline__ float& f4_at(float4& v, int e) { return e == 0 ? v.x 
 // CBM: the most 32-column blocks of C a job of the launch has (1, 2 or 4);
 // the narrower forms hold fewer accumulators and less of B's stage, so more
 // blocks fit on a CU.  WU: the weight-update form (every job wupd, R <= 32).
+// The weight-update form is held to four waves per SIMD (128 registers, no
+// spills): its blocks are short and mostly stream W and X, so a fourth block
+// per CU keeps more of that stream in flight than the three that its
+// unconstrained allocation (132 registers) allows.
 template <int TA, bool MOM, int CBM, bool WU>
-__global__ __launch_bounds__(256) void thin_kernel(ThinArgs a) {
+__global__ __launch_bounds__(256, WU ? 4 : 1) void thin_kernel(ThinArgs a) {
   constexpr int TM = kThinTile, KC = kThinK, LK = kThinLK;
   static_assert(TM == 128 && KC == 32 && kThinMaxR == 128, "the load and fragment maps below assume these sizes");
   static_assert(!MOM || TA == 0, "the momentum operand is row-major");
