@@ -359,19 +359,29 @@ def ns_spectral(lam: np.ndarray, coeffs, nu: float = 0.0, p: int = 2, out: str =
         P = Z_K / sqrt(c') = sigma_K / sqrt(lam + delta c)    (out='inv')
         R = Y_K sqrt(c')  = sigma_K sqrt(lam + delta c)      (out='sqrt').
     p = 2 returns that chain's output; p = 4 (R8) runs a second chain on
-    the first chain's P eigenvalues and returns its R."""
+    the first chain's P eigenvalues and returns its R.
+
+    The factor is positive semidefinite (outer products plus eps I), so an
+    eigenvalue below zero is the eigensolver's rounding and is taken as zero.
+    The ratio t_k = sigma_k / sigma_0 runs through the same recurrence:
+    P = t_K / sqrt(c') equals sigma_K / sqrt(lam + delta c) wherever that is
+    defined, and is the iteration's limit on a zero eigenvalue."""
     lam = np.asarray(lam, dtype=np.float64)
     d = lam.size
     delta = nu / math.sqrt(d)
     c = float(np.linalg.norm(lam))
-    shifted = lam + delta * c
-    s = np.sqrt(shifted / (c * (1.0 + delta)))
+    cp = c * (1.0 + delta)
+    shifted = np.maximum(lam + delta * c, 0.0)
+    s = np.sqrt(shifted / cp)
+    t = np.ones_like(s)
     for a, b in coeffs:
-        s = s * (a + b * s * s)
+        g = a + b * s * s
+        s = s * g
+        t = t * g
     if p == 2:
-        return s / np.sqrt(shifted) if out == "inv" else s * np.sqrt(shifted)
+        return t / math.sqrt(cp) if out == "inv" else s * np.sqrt(shifted)
     if p == 4:
-        return ns_spectral(s / np.sqrt(shifted), coeffs, nu, 2, "sqrt")
+        return ns_spectral(t / math.sqrt(cp), coeffs, nu, 2, "sqrt")
     raise ValueError("p must be 2 or 4")
 
 

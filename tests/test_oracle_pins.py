@@ -336,6 +336,24 @@ def test_ns_spectral_within_coefficient_bound_of_shifted_root():
     np.testing.assert_array_less(np.abs(f4 / np.sqrt(r + shift2) - 1.0), 2.5 * efin)
 
 
+def test_ns_spectral_zero_eigenvalue_is_the_iteration_limit():
+    """A rank-deficient factor: in a zero eigen-direction Z Y stays 0, so each
+    T_k acts there as a_k and P = prod(a_k) / sqrt(c').  The closed form gives
+    that value, also for an eigenvalue rounded below zero, and matches the
+    matrix iteration on a singular PSD matrix."""
+    coeffs, _ = O.ns_coefficients(1e-3, 10)
+    lam = np.array([-1e-18, 0.0, 0.25, 1.0])
+    f = O.ns_spectral(lam, coeffs, 0.0, 2)
+    want0 = np.prod([a for a, _ in coeffs]) / math.sqrt(np.linalg.norm(lam))
+    np.testing.assert_allclose(f[:2], want0, rtol=1e-12)
+    assert np.all(np.isfinite(O.ns_spectral(lam, coeffs, 0.0, 4)))
+    rng = np.random.default_rng(11)
+    V, _ = np.linalg.qr(rng.standard_normal((6, 6)))
+    S = (V * np.array([0.0, 0.0, 1e-2, 0.1, 0.5, 1.0])) @ V.T
+    P, _ = O.ns_inv_sqrt(S, coeffs)
+    np.testing.assert_allclose(O.ns_eigen_closed_form(S, coeffs), P, rtol=1e-9, atol=1e-9)
+
+
 def test_ns_damped_isotropic():
     """S = s I: ||S||_F = s sqrt(d), so the shifted matrix is s (1 + nu) I."""
     coeffs, efin = O.ns_coefficients(1e-3, 10)
